@@ -1,0 +1,117 @@
+"""ctypes wrapper around libttt_oracle.so (plain C, fp64) — TEST INFRASTRUCTURE ONLY."""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ttt_oracle.c")
+_LIB = os.path.join(_HERE, "libttt_oracle.so")
+_lib = None
+
+
+def lib_path() -> str:
+    return _LIB
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O3, no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O3", "-std=c11", "-D_GNU_SOURCE", "-ffp-contract=off",
+                               "-fno-fast-math", "-Wall", "-shared", "-fPIC", _SRC, "-o", tmp,
+                               "-lm", "-lpthread"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.POINTER(ctypes.c_double)
+        lib.ttt_oracle_linear.argtypes = [P, P, P, P, ctypes.c_double, P, P, P,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, ctypes.c_int]
+        lib.ttt_oracle_linear.restype = ctypes.c_int
+        lib.ttt_oracle_mlp.argtypes = [P, P, P, P, ctypes.c_double, P, P, P, P,
+                                       P, P, P, P, P,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.ttt_oracle_mlp.restype = ctypes.c_int
+        lib.ttt_oracle_gelu.argtypes = [ctypes.c_double]
+        lib.ttt_oracle_gelu.restype = ctypes.c_double
+        lib.ttt_oracle_gelu_prime.argtypes = [ctypes.c_double]
+        lib.ttt_oracle_gelu_prime.restype = ctypes.c_double
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def linear(K, Q, V, eta, eta_scalar: float, W0, chunk: int,
+           nthreads: int = 0, return_threads: bool = False):
+    """TTT-Linear scan.  K, Q, V: [n, T, d]; eta: [n, T] or None; W0: [n, d, d].
+    Returns (Z [n, T, d], W_T [n, d, d]) in fp64 (and the thread count if asked)."""
+    K, Q, V, W0 = _f64(K), _f64(Q), _f64(V), _f64(W0)
+    eta = _f64(eta)
+    n, T, d = K.shape
+    assert Q.shape == K.shape == V.shape and W0.shape == (n, d, d)
+    if eta is not None:
+        assert eta.shape == (n, T)
+    Z = np.empty((n, T, d), np.float64)
+    W = np.empty((n, d, d), np.float64)
+    rc = _load().ttt_oracle_linear(_ptr(K), _ptr(Q), _ptr(V), _ptr(eta), float(eta_scalar),
+                                   _ptr(W0), _ptr(Z), _ptr(W), n, T, d, int(chunk),
+                                   int(nthreads))
+    if rc <= 0:
+        raise ValueError("ttt_oracle_linear rejected its arguments")
+    return (Z, W, rc) if return_threads else (Z, W)
+
+
+def mlp(K, Q, V, eta, eta_scalar: float, W1, b1, W2, b2, chunk: int,
+        nthreads: int = 0, return_threads: bool = False):
+    """TTT-MLP scan.  W1: [n, hd, d], b1: [n, hd] or None, W2: [n, d, hd],
+    b2: [n, d] or None.  Returns (Z, W1_T, b1_T, W2_T, b2_T) in fp64."""
+    K, Q, V, W1, W2 = _f64(K), _f64(Q), _f64(V), _f64(W1), _f64(W2)
+    eta, b1, b2 = _f64(eta), _f64(b1), _f64(b2)
+    n, T, d = K.shape
+    hd = W1.shape[1]
+    assert W1.shape == (n, hd, d) and W2.shape == (n, d, hd)
+    Z = np.empty((n, T, d), np.float64)
+    W1o = np.empty_like(W1)
+    W2o = np.empty_like(W2)
+    b1o = np.empty((n, hd), np.float64) if b1 is not None else None
+    b2o = np.empty((n, d), np.float64) if b2 is not None else None
+    rc = _load().ttt_oracle_mlp(_ptr(K), _ptr(Q), _ptr(V), _ptr(eta), float(eta_scalar),
+                                _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2),
+                                _ptr(Z), _ptr(W1o), _ptr(b1o), _ptr(W2o), _ptr(b2o),
+                                n, T, d, hd, int(chunk), int(nthreads))
+    if rc <= 0:
+        raise ValueError("ttt_oracle_mlp rejected its arguments")
+    res = (Z, W1o, b1o, W2o, b2o)
+    return res + (rc,) if return_threads else res
+
+
+def gelu(x: float) -> float:
+    return _load().ttt_oracle_gelu(float(x))
+
+
+def gelu_prime(x: float) -> float:
+    return _load().ttt_oracle_gelu_prime(float(x))

@@ -1,0 +1,290 @@
+/*
+ * ttt_oracle.c — TEST INFRASTRUCTURE ONLY (see ttt_oracle.h).
+ *
+ * Per-token primal form of the chunked TTT scan, in fp64, written straight from
+ * the definition: for every token the gradient of 1/2||f(k_t) - v_t||^2 is taken
+ * at the chunk-start parameters, accumulated with its own eta, and the token's
+ * output is read from (chunk-start parameters - accumulated update).  No dual
+ * form, no blocking, no fusion.  Threads only split the independent
+ * (batch, head) slices.
+ */
+#include "ttt_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ------------------------------------------------------------------------ */
+/* TTT-Linear, one (batch, head) slice.                                      */
+/* PaperTrace "5 · TestingTime 训练与长上下文" §1.1 (chunked update, gradient at */
+/* the chunk start, read with the updated model), §2.1 (write/read rules),   */
+/* §2.3 (f_W(k) = W k, l = 1/2||W k - v||^2, gradient (W k - v) k^T).        */
+/* ------------------------------------------------------------------------ */
+static void linear_slice(const double* K, const double* Q, const double* V,
+                         const double* eta, double eta_scalar, const double* W0,
+                         double* Z, double* W_out, int T, int d, int chunk)
+{
+    double* W  = (double*)malloc(sizeof(double) * d * d);  /* running state      */
+    double* Ws = (double*)malloc(sizeof(double) * d * d);  /* chunk-start state  */
+    double* G  = (double*)malloc(sizeof(double) * d * d);  /* sum eta_s e_s k_s^T */
+    double* e  = (double*)malloc(sizeof(double) * d);
+    memcpy(W, W0, sizeof(double) * d * d);
+
+    for (int c0 = 0; c0 < T; c0 += chunk) {
+        int c1 = c0 + chunk < T ? c0 + chunk : T;
+        memcpy(Ws, W, sizeof(double) * d * d);
+        memset(G, 0, sizeof(double) * d * d);
+        for (int t = c0; t < c1; ++t) {
+            const double* k = K + (size_t)t * d;
+            const double* q = Q + (size_t)t * d;
+            const double* v = V + (size_t)t * d;
+            double et = eta ? eta[t] : eta_scalar;
+            /* e_t = Ws k_t - v_t : the loss gradient is e_t k_t^T at Ws */
+            for (int i = 0; i < d; ++i) {
+                double s = 0.0;
+                for (int j = 0; j < d; ++j) s += Ws[i * d + j] * k[j];
+                e[i] = s - v[i];
+            }
+            /* G += eta_t e_t k_t^T  (eta of the writing token) */
+            for (int i = 0; i < d; ++i)
+                for (int j = 0; j < d; ++j) G[i * d + j] += et * e[i] * k[j];
+            /* z_t = (Ws - G) q_t : own update included */
+            double* z = Z + (size_t)t * d;
+            for (int i = 0; i < d; ++i) {
+                double s = 0.0;
+                for (int j = 0; j < d; ++j) s += (Ws[i * d + j] - G[i * d + j]) * q[j];
+                z[i] = s;
+            }
+        }
+        for (int i = 0; i < d * d; ++i) W[i] = Ws[i] - G[i];
+    }
+    memcpy(W_out, W, sizeof(double) * d * d);
+    free(W); free(Ws); free(G); free(e);
+}
+
+/* ------------------------------------------------------------------------ */
+/* GELU, exact erf form: gelu(x) = x * Phi(x), Phi the standard normal CDF.  */
+/* diosapp "Test-Time Training (TTT) guide" §3 names GELU; the erf form is   */
+/* the reading taken here.                                                   */
+/* ------------------------------------------------------------------------ */
+double ttt_oracle_gelu(double x)
+{
+    return 0.5 * x * (1.0 + erf(x / sqrt(2.0)));
+}
+
+/* d/dx [x Phi(x)] = Phi(x) + x phi(x), phi the standard normal density. */
+double ttt_oracle_gelu_prime(double x)
+{
+    const double inv_sqrt_2pi = 0.39894228040143267794;
+    return 0.5 * (1.0 + erf(x / sqrt(2.0))) + x * inv_sqrt_2pi * exp(-0.5 * x * x);
+}
+
+/* ------------------------------------------------------------------------ */
+/* TTT-MLP, one (batch, head) slice.                                         */
+/* f(x) = W2 gelu(W1 x + b1) + b2, hidden width `hidden` (4d on the page,    */
+/* diosapp guide §3).  Per token, explicit backprop of 1/2||f(k) - v||^2 at  */
+/* the chunk-start parameters Ps:                                            */
+/*   h = W1 k + b1, a = gelu(h), e = W2 a + b2 - v                           */
+/*   dW2 = e a^T, db2 = e, delta = (W2^T e) * gelu'(h), dW1 = delta k^T,     */
+/*   db1 = delta;   G += eta_t * grad;   z_t = f_{Ps - G}(q_t).              */
+/* A NULL bias is absent: it stays zero and receives no update.             */
+/* ------------------------------------------------------------------------ */
+static void mlp_slice(const double* K, const double* Q, const double* V,
+                      const double* eta, double eta_scalar,
+                      const double* W1_0, const double* b1_0,
+                      const double* W2_0, const double* b2_0,
+                      double* Z, double* W1_o, double* b1_o,
+                      double* W2_o, double* b2_o,
+                      int T, int d, int hd, int chunk)
+{
+    size_t n1 = (size_t)hd * d, n2 = (size_t)d * hd;
+    double* W1  = (double*)calloc(n1, sizeof(double));
+    double* W2  = (double*)calloc(n2, sizeof(double));
+    double* b1  = (double*)calloc(hd, sizeof(double));
+    double* b2  = (double*)calloc(d, sizeof(double));
+    double* W1s = (double*)calloc(n1, sizeof(double));
+    double* W2s = (double*)calloc(n2, sizeof(double));
+    double* b1s = (double*)calloc(hd, sizeof(double));
+    double* b2s = (double*)calloc(d, sizeof(double));
+    double* G1  = (double*)calloc(n1, sizeof(double));
+    double* G2  = (double*)calloc(n2, sizeof(double));
+    double* g1  = (double*)calloc(hd, sizeof(double));
+    double* g2  = (double*)calloc(d, sizeof(double));
+    double* h   = (double*)calloc(hd, sizeof(double));
+    double* a   = (double*)calloc(hd, sizeof(double));
+    double* dl  = (double*)calloc(hd, sizeof(double));
+    double* e   = (double*)calloc(d, sizeof(double));
+    double* hr  = (double*)calloc(hd, sizeof(double));
+
+    memcpy(W1, W1_0, sizeof(double) * n1);
+    memcpy(W2, W2_0, sizeof(double) * n2);
+    if (b1_0) memcpy(b1, b1_0, sizeof(double) * hd);
+    if (b2_0) memcpy(b2, b2_0, sizeof(double) * d);
+
+    for (int c0 = 0; c0 < T; c0 += chunk) {
+        int c1 = c0 + chunk < T ? c0 + chunk : T;
+        memcpy(W1s, W1, sizeof(double) * n1);
+        memcpy(W2s, W2, sizeof(double) * n2);
+        memcpy(b1s, b1, sizeof(double) * hd);
+        memcpy(b2s, b2, sizeof(double) * d);
+        memset(G1, 0, sizeof(double) * n1);
+        memset(G2, 0, sizeof(double) * n2);
+        memset(g1, 0, sizeof(double) * hd);
+        memset(g2, 0, sizeof(double) * d);
+        for (int t = c0; t < c1; ++t) {
+            const double* k = K + (size_t)t * d;
+            const double* q = Q + (size_t)t * d;
+            const double* v = V + (size_t)t * d;
+            double et = eta ? eta[t] : eta_scalar;
+            /* forward at the chunk-start parameters */
+            for (int u = 0; u < hd; ++u) {
+                double s = b1s[u];
+                for (int j = 0; j < d; ++j) s += W1s[(size_t)u * d + j] * k[j];
+                h[u] = s;
+                a[u] = ttt_oracle_gelu(s);
+            }
+            for (int i = 0; i < d; ++i) {
+                double s = b2s[i];
+                for (int u = 0; u < hd; ++u) s += W2s[(size_t)i * hd + u] * a[u];
+                e[i] = s - v[i];
+            }
+            /* backward */
+            for (int u = 0; u < hd; ++u) {
+                double s = 0.0;
+                for (int i = 0; i < d; ++i) s += W2s[(size_t)i * hd + u] * e[i];
+                dl[u] = s * ttt_oracle_gelu_prime(h[u]);
+            }
+            /* accumulate eta_t * gradient */
+            for (int i = 0; i < d; ++i)
+                for (int u = 0; u < hd; ++u) G2[(size_t)i * hd + u] += et * e[i] * a[u];
+            for (int u = 0; u < hd; ++u)
+                for (int j = 0; j < d; ++j) G1[(size_t)u * d + j] += et * dl[u] * k[j];
+            if (b2_0) for (int i = 0; i < d; ++i) g2[i] += et * e[i];
+            if (b1_0) for (int u = 0; u < hd; ++u) g1[u] += et * dl[u];
+            /* read with the updated parameters Ps - G */
+            for (int u = 0; u < hd; ++u) {
+                double s = b1s[u] - g1[u];
+                for (int j = 0; j < d; ++j)
+                    s += (W1s[(size_t)u * d + j] - G1[(size_t)u * d + j]) * q[j];
+                hr[u] = ttt_oracle_gelu(s);
+            }
+            double* z = Z + (size_t)t * d;
+            for (int i = 0; i < d; ++i) {
+                double s = b2s[i] - g2[i];
+                for (int u = 0; u < hd; ++u)
+                    s += (W2s[(size_t)i * hd + u] - G2[(size_t)i * hd + u]) * hr[u];
+                z[i] = s;
+            }
+        }
+        for (size_t i = 0; i < n1; ++i) W1[i] = W1s[i] - G1[i];
+        for (size_t i = 0; i < n2; ++i) W2[i] = W2s[i] - G2[i];
+        for (int u = 0; u < hd; ++u) b1[u] = b1s[u] - g1[u];
+        for (int i = 0; i < d; ++i) b2[i] = b2s[i] - g2[i];
+    }
+    memcpy(W1_o, W1, sizeof(double) * n1);
+    memcpy(W2_o, W2, sizeof(double) * n2);
+    if (b1_o) memcpy(b1_o, b1, sizeof(double) * hd);
+    if (b2_o) memcpy(b2_o, b2, sizeof(double) * d);
+
+    free(W1); free(W2); free(b1); free(b2); free(W1s); free(W2s); free(b1s); free(b2s);
+    free(G1); free(G2); free(g1); free(g2); free(h); free(a); free(dl); free(e); free(hr);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Thread pool over (batch, head) slices.                                    */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int is_mlp;
+    const double *K, *Q, *V, *eta, *W0, *W1, *b1, *W2, *b2;
+    double eta_scalar;
+    double *Z, *W_out, *W1_o, *b1_o, *W2_o, *b2_o;
+    int BH, T, d, hd, chunk, nthreads, tid;
+} job_t;
+
+static void* worker(void* arg)
+{
+    const job_t* j = (const job_t*)arg;
+    size_t td = (size_t)j->T * j->d;
+    for (int s = j->tid; s < j->BH; s += j->nthreads) {
+        const double* eta = j->eta ? j->eta + (size_t)s * j->T : NULL;
+        if (!j->is_mlp) {
+            size_t dd = (size_t)j->d * j->d;
+            linear_slice(j->K + s * td, j->Q + s * td, j->V + s * td, eta, j->eta_scalar,
+                         j->W0 + s * dd, j->Z + s * td, j->W_out + s * dd,
+                         j->T, j->d, j->chunk);
+        } else {
+            size_t n1 = (size_t)j->hd * j->d;
+            mlp_slice(j->K + s * td, j->Q + s * td, j->V + s * td, eta, j->eta_scalar,
+                      j->W1 + s * n1, j->b1 ? j->b1 + (size_t)s * j->hd : NULL,
+                      j->W2 + s * n1, j->b2 ? j->b2 + (size_t)s * j->d : NULL,
+                      j->Z + s * td, j->W1_o + s * n1,
+                      j->b1_o ? j->b1_o + (size_t)s * j->hd : NULL,
+                      j->W2_o + s * n1,
+                      j->b2_o ? j->b2_o + (size_t)s * j->d : NULL,
+                      j->T, j->d, j->hd, j->chunk);
+        }
+    }
+    return NULL;
+}
+
+static int run_pool(job_t* proto)
+{
+    int nt = proto->nthreads;
+    if (nt <= 0) {
+        long n = sysconf(_SC_NPROCESSORS_ONLN);
+        nt = n > 0 ? (int)n : 1;
+    }
+    if (nt > proto->BH) nt = proto->BH;
+    if (nt < 1) nt = 1;
+    job_t* jobs = (job_t*)malloc(sizeof(job_t) * nt);
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * nt);
+    for (int i = 0; i < nt; ++i) {
+        jobs[i] = *proto;
+        jobs[i].nthreads = nt;
+        jobs[i].tid = i;
+    }
+    for (int i = 1; i < nt; ++i) pthread_create(&th[i], NULL, worker, &jobs[i]);
+    worker(&jobs[0]);
+    for (int i = 1; i < nt; ++i) pthread_join(th[i], NULL);
+    free(jobs); free(th);
+    return nt;
+}
+
+int ttt_oracle_linear(const double* K, const double* Q, const double* V,
+                      const double* eta, double eta_scalar, const double* W0,
+                      double* Z, double* W_out,
+                      int BH, int T, int d, int chunk, int nthreads)
+{
+    if (!K || !Q || !V || !W0 || !Z || !W_out) return -1;
+    if (BH <= 0 || T <= 0 || d <= 0 || chunk <= 0) return -1;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.K = K; j.Q = Q; j.V = V; j.eta = eta; j.eta_scalar = eta_scalar; j.W0 = W0;
+    j.Z = Z; j.W_out = W_out; j.BH = BH; j.T = T; j.d = d; j.chunk = chunk;
+    j.nthreads = nthreads;
+    return run_pool(&j);
+}
+
+int ttt_oracle_mlp(const double* K, const double* Q, const double* V,
+                   const double* eta, double eta_scalar,
+                   const double* W1, const double* b1,
+                   const double* W2, const double* b2,
+                   double* Z, double* W1_out, double* b1_out,
+                   double* W2_out, double* b2_out,
+                   int BH, int T, int d, int hidden, int chunk, int nthreads)
+{
+    if (!K || !Q || !V || !W1 || !W2 || !Z || !W1_out || !W2_out) return -1;
+    if ((b1 == NULL) != (b1_out == NULL) || (b2 == NULL) != (b2_out == NULL)) return -1;
+    if (BH <= 0 || T <= 0 || d <= 0 || hidden <= 0 || chunk <= 0) return -1;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.is_mlp = 1;
+    j.K = K; j.Q = Q; j.V = V; j.eta = eta; j.eta_scalar = eta_scalar;
+    j.W1 = W1; j.b1 = b1; j.W2 = W2; j.b2 = b2;
+    j.Z = Z; j.W1_o = W1_out; j.b1_o = b1_out; j.W2_o = W2_out; j.b2_o = b2_out;
+    j.BH = BH; j.T = T; j.d = d; j.hd = hidden; j.chunk = chunk;
+    j.nthreads = nthreads;
+    return run_pool(&j);
+}

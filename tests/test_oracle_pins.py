@@ -1,0 +1,347 @@
+"""Pins for the fp64 oracle: checks against what the pages and the mathematics fix.
+
+The pages print no worked example, so each test pins the oracle to a closed
+form, an identity or an independent derivation:
+
+  delta rule (b=1)            PaperTrace "5 · TestingTime 训练与长上下文" §2.1, §2.3
+  causal linear attention     same page §1.1 (Theorem 1), §2.1; diosapp TTT guide §4
+  dual form == primal         diosapp TTT guide §3; PaperTrace §1.1
+  exact write (orthonormal)   PaperTrace §2.3 (erase along k, write the new value)
+  resume / slice isolation    PaperTrace §2.2 (state lives for one sequence)
+  MLP gradient                finite differences of the loss (no formula shared)
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from ref_dual import linear_dual, mlp_dual
+from test_sequence_layers_ttt_amd.inputs import round_to_bf16, make_inputs, workload
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def rand_linear(rng, n, T, d, per_token=True, w0=True, normalize=True):
+    K = rng.standard_normal((n, T, d))
+    Q = rng.standard_normal((n, T, d))
+    V = rng.standard_normal((n, T, d))
+    if normalize:
+        K /= np.linalg.norm(K, axis=-1, keepdims=True)
+        Q /= np.linalg.norm(Q, axis=-1, keepdims=True)
+    eta = rng.uniform(0.01, 0.2, (n, T)) if per_token else None
+    W0 = rng.standard_normal((n, d, d)) * 0.3 if w0 else np.zeros((n, d, d))
+    return K, Q, V, eta, W0
+
+
+# ---------------------------------------------------------------- TTT-Linear
+@pytest.mark.parametrize("d,T", [(4, 9), (8, 33)])
+def test_delta_rule_b1(d, T):
+    """b=1: W_t = W_{t-1}(I - eta_t k_t k_t^T) + eta_t v_t k_t^T, z_t = W_t q_t (DeltaNet
+    write with beta = eta on the writing token)."""
+    rng = np.random.default_rng(1)
+    K, Q, V, eta, W0 = rand_linear(rng, 2, T, d)
+    Z, WT = oracle.linear(K, Q, V, eta, 0.0, W0, chunk=1)
+    for s in range(2):
+        W = W0[s].copy()
+        I = np.eye(d)
+        for t in range(T):
+            k, v, q, b = K[s, t], V[s, t], Q[s, t], eta[s, t]
+            W = W @ (I - b * np.outer(k, k)) + b * np.outer(v, k)
+            np.testing.assert_allclose(Z[s, t], W @ q, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(WT[s], W, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("T,chunk", [(12, 12), (12, 40), (1, 1)])
+def test_linear_attention_equivalence(T, chunk):
+    """W0 = 0, one chunk over the whole sequence, scalar eta -> causal linear attention:
+    z_t = eta sum_{s<=t} (k_s . q_t) v_s and W_T = eta sum_s v_s k_s^T."""
+    rng = np.random.default_rng(2)
+    d = 5
+    K, Q, V, _, _ = rand_linear(rng, 1, T, d, normalize=False)
+    eta = 0.37
+    Z, WT = oracle.linear(K, Q, V, None, eta, np.zeros((1, d, d)), chunk=chunk)
+    for t in range(T):
+        ref = sum(eta * float(K[0, s] @ Q[0, t]) * V[0, s] for s in range(t + 1))
+        np.testing.assert_allclose(Z[0, t], ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(WT[0], eta * V[0].T @ K[0], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 3, 8, 16, 23, 64])
+@pytest.mark.parametrize("per_token", [True, False])
+def test_dual_equals_primal(chunk, per_token):
+    rng = np.random.default_rng(3 + chunk)
+    T, d = 50, 8          # 50 is not a multiple of most chunks: ragged last chunk
+    K, Q, V, eta, W0 = rand_linear(rng, 2, T, d, per_token=per_token)
+    Z, WT = oracle.linear(K, Q, V, eta, 0.11, W0, chunk=chunk)
+    for s in range(2):
+        Zd, Wd = linear_dual(K[s], Q[s], V[s], None if eta is None else eta[s], 0.11,
+                             W0[s], chunk)
+        np.testing.assert_allclose(Z[s], Zd, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(WT[s], Wd, rtol=0, atol=1e-12)
+
+
+def test_eta_zero_is_identity_read():
+    rng = np.random.default_rng(4)
+    K, Q, V, _, W0 = rand_linear(rng, 2, 20, 6)
+    Z, WT = oracle.linear(K, Q, V, None, 0.0, W0, chunk=4)
+    np.testing.assert_array_equal(WT, W0)
+    for s in range(2):
+        np.testing.assert_allclose(Z[s], Q[s] @ W0[s].T, rtol=0, atol=1e-13)
+
+
+def test_exact_write_orthonormal_keys():
+    """eta = 1 and orthonormal keys in a chunk: after the chunk W k_s = v_s exactly."""
+    rng = np.random.default_rng(5)
+    d, chunk = 8, 5
+    Qm, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    K = Qm[:, :chunk].T[None]             # 5 orthonormal keys
+    V = rng.standard_normal((1, chunk, d))
+    Q = rng.standard_normal((1, chunk, d))
+    W0 = rng.standard_normal((1, d, d))
+    _, WT = oracle.linear(K, Q, V, None, 1.0, W0, chunk=chunk)
+    np.testing.assert_allclose(K[0] @ WT[0].T, V[0], rtol=0, atol=1e-12)
+    # directions orthogonal to every key are left untouched
+    P = np.eye(d) - K[0].T @ K[0]
+    np.testing.assert_allclose(WT[0] @ P, W0[0] @ P, rtol=0, atol=1e-12)
+
+
+def test_last_token_reads_next_chunk_state():
+    """The last token of a chunk reads with the whole chunk's update, i.e. with the
+    state the next chunk starts from (per-token eta scales the writer's gradient)."""
+    rng = np.random.default_rng(6)
+    d, chunk, T = 6, 7, 21
+    K, Q, V, eta, W0 = rand_linear(rng, 1, T, d)
+    Z, _ = oracle.linear(K, Q, V, eta, 0.0, W0, chunk=chunk)
+    for m in (1, 2, 3):
+        _, Wm = oracle.linear(K[:, :m * chunk], Q[:, :m * chunk], V[:, :m * chunk],
+                              eta[:, :m * chunk], 0.0, W0, chunk=chunk)
+        np.testing.assert_allclose(Z[0, m * chunk - 1], Wm[0] @ Q[0, m * chunk - 1],
+                                   rtol=0, atol=1e-12)
+
+
+def test_linearity_in_w0_and_v():
+    rng = np.random.default_rng(7)
+    K, Q, Va, eta, W0a = rand_linear(rng, 1, 30, 6)
+    Vb = rng.standard_normal(Va.shape)
+    W0b = rng.standard_normal(W0a.shape)
+    a, b = 0.7, -1.9
+    Za, Wa = oracle.linear(K, Q, Va, eta, 0, W0a, chunk=4)
+    Zb, Wb = oracle.linear(K, Q, Vb, eta, 0, W0b, chunk=4)
+    Zc, Wc = oracle.linear(K, Q, a * Va + b * Vb, eta, 0, a * W0a + b * W0b, chunk=4)
+    np.testing.assert_allclose(Zc, a * Za + b * Zb, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(Wc, a * Wa + b * Wb, rtol=0, atol=1e-11)
+
+
+def test_row_permutation_equivariance():
+    """Output feature i depends only on row i of W0 and feature i of V."""
+    rng = np.random.default_rng(8)
+    d = 7
+    K, Q, V, eta, W0 = rand_linear(rng, 1, 25, d)
+    perm = rng.permutation(d)
+    Z, W = oracle.linear(K, Q, V, eta, 0, W0, chunk=3)
+    Zp, Wp = oracle.linear(K, Q, V[:, :, perm], eta, 0, W0[:, perm, :], chunk=3)
+    np.testing.assert_allclose(Zp, Z[:, :, perm], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(Wp, W[:, perm, :], rtol=0, atol=1e-13)
+
+
+def test_chunk_aligned_resume():
+    rng = np.random.default_rng(9)
+    K, Q, V, eta, W0 = rand_linear(rng, 2, 48, 6)
+    Z, W = oracle.linear(K, Q, V, eta, 0, W0, chunk=8)
+    Z1, W1 = oracle.linear(K[:, :24], Q[:, :24], V[:, :24], eta[:, :24], 0, W0, chunk=8)
+    Z2, W2 = oracle.linear(K[:, 24:], Q[:, 24:], V[:, 24:], eta[:, 24:], 0, W1, chunk=8)
+    np.testing.assert_array_equal(np.concatenate([Z1, Z2], axis=1), Z)
+    np.testing.assert_array_equal(W2, W)
+
+
+def test_slices_are_isolated():
+    rng = np.random.default_rng(10)
+    K, Q, V, eta, W0 = rand_linear(rng, 3, 16, 4)
+    V[1, 5, 2] = np.nan
+    Z, W = oracle.linear(K, Q, V, eta, 0, W0, chunk=4)
+    assert np.isfinite(Z[[0, 2]]).all() and np.isfinite(W[[0, 2]]).all()
+    assert np.isnan(Z[1, 5:]).any()
+    Zc, Wc = oracle.linear(K[[0, 2]], Q[[0, 2]], V[[0, 2]], eta[[0, 2]], 0, W0[[0, 2]], chunk=4)
+    np.testing.assert_array_equal(Z[[0, 2]], Zc)
+    np.testing.assert_array_equal(W[[0, 2]], Wc)
+
+
+def test_thread_count_does_not_change_results():
+    rng = np.random.default_rng(11)
+    K, Q, V, eta, W0 = rand_linear(rng, 5, 20, 4)
+    Z1, W1 = oracle.linear(K, Q, V, eta, 0, W0, chunk=4, nthreads=1)
+    Z3, W3 = oracle.linear(K, Q, V, eta, 0, W0, chunk=4, nthreads=3)
+    np.testing.assert_array_equal(Z1, Z3)
+    np.testing.assert_array_equal(W1, W3)
+
+
+# ---------------------------------------------------------------- GELU
+def test_gelu_values():
+    # Phi(1) and Phi(2) from the standard normal table
+    assert oracle.gelu(0.0) == 0.0
+    assert abs(oracle.gelu(1.0) - 0.8413447460685429) < 1e-15
+    assert abs(oracle.gelu(-1.0) - (-(1 - 0.8413447460685429))) < 1e-15
+    assert abs(oracle.gelu(2.0) - 2 * 0.9772498680518208) < 1e-15
+    assert abs(oracle.gelu(12.0) - 12.0) < 1e-15
+    assert abs(oracle.gelu(-12.0)) < 1e-30
+    assert abs(oracle.gelu_prime(0.0) - 0.5) < 1e-16
+    for x in (-3.0, -0.7, 0.0, 0.4, 1.3, 4.0):
+        h = 1e-5
+        fd = (oracle.gelu(x + h) - oracle.gelu(x - h)) / (2 * h)
+        assert abs(fd - oracle.gelu_prime(x)) < 1e-9
+
+
+# ---------------------------------------------------------------- TTT-MLP
+def _gelu_np(x):
+    return np.array([0.5 * v * (1 + math.erf(v / math.sqrt(2))) for v in np.ravel(x)]).reshape(
+        np.shape(x))
+
+
+def _mlp_forward(P, x):
+    W1, b1, W2, b2 = P
+    return W2 @ _gelu_np(W1 @ x + b1) + b2
+
+
+def _fd_grad(P, k, v, h=1e-6):
+    """Central differences of 1/2||f_P(k) - v||^2 over every parameter."""
+    def loss(P_):
+        r = _mlp_forward(P_, k) - v
+        return 0.5 * float(r @ r)
+    grads = []
+    for i, p in enumerate(P):
+        g = np.zeros_like(p)
+        it = np.nditer(p, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            Pp = [q.copy() for q in P]
+            Pm = [q.copy() for q in P]
+            Pp[i][idx] += h
+            Pm[i][idx] -= h
+            g[idx] = (loss(Pp) - loss(Pm)) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+def _rand_mlp(rng, d, hd, scale=0.5):
+    return [rng.standard_normal((hd, d)) * scale, rng.standard_normal(hd) * 0.3,
+            rng.standard_normal((d, hd)) * scale, rng.standard_normal(d) * 0.3]
+
+
+def test_mlp_single_step_matches_finite_differences():
+    """One token, one chunk: P_out = P - eta * grad, grad from central differences."""
+    rng = np.random.default_rng(12)
+    d, hd, eta = 3, 5, 0.3
+    P = _rand_mlp(rng, d, hd)
+    k, q, v = rng.standard_normal(d), rng.standard_normal(d), rng.standard_normal(d)
+    Z, W1o, b1o, W2o, b2o = oracle.mlp(k[None, None], q[None, None], v[None, None], None, eta,
+                                       P[0][None], P[1][None], P[2][None], P[3][None], chunk=1)
+    grads = _fd_grad(P, k, v)
+    for po, p, g in zip((W1o[0], b1o[0], W2o[0], b2o[0]), P, grads):
+        np.testing.assert_allclose((p - po) / eta, g, rtol=0, atol=1e-7)
+    Pn = [p - eta * g for p, g in zip(P, grads)]
+    np.testing.assert_allclose(Z[0, 0], _mlp_forward(Pn, q), rtol=0, atol=1e-7)
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 3])
+def test_mlp_chunked_scan_with_fd_gradients(chunk):
+    """Chunk semantics with gradients from finite differences only."""
+    rng = np.random.default_rng(13 + chunk)
+    d, hd, T = 2, 4, 5
+    P = _rand_mlp(rng, d, hd)
+    K, Q, V = (rng.standard_normal((T, d)) for _ in range(3))
+    eta = rng.uniform(0.05, 0.4, T)
+    Z, W1o, b1o, W2o, b2o = oracle.mlp(K[None], Q[None], V[None], eta[None], 0.0,
+                                       P[0][None], P[1][None], P[2][None], P[3][None],
+                                       chunk=chunk)
+    cur = [p.copy() for p in P]
+    for c0 in range(0, T, chunk):
+        start = [p.copy() for p in cur]
+        acc = [np.zeros_like(p) for p in P]
+        for t in range(c0, min(T, c0 + chunk)):
+            g = _fd_grad(start, K[t], V[t])
+            acc = [a + eta[t] * gi for a, gi in zip(acc, g)]
+            read = [s - a for s, a in zip(start, acc)]
+            np.testing.assert_allclose(Z[0, t], _mlp_forward(read, Q[t]), rtol=0, atol=1e-7)
+        cur = [s - a for s, a in zip(start, acc)]
+    for po, p in zip((W1o[0], b1o[0], W2o[0], b2o[0]), cur):
+        np.testing.assert_allclose(po, p, rtol=0, atol=1e-7)
+
+
+@pytest.mark.parametrize("chunk", [1, 4, 16, 7])
+@pytest.mark.parametrize("bias", [True, False])
+def test_mlp_dual_equals_primal(chunk, bias):
+    rng = np.random.default_rng(20 + chunk)
+    d, hd, T = 4, 16, 37
+    W1, b1, W2, b2 = _rand_mlp(rng, d, hd, 0.3)
+    if not bias:
+        b1 = b2 = None
+    K, Q, V = (rng.standard_normal((T, d)) for _ in range(3))
+    K /= np.linalg.norm(K, axis=-1, keepdims=True)
+    eta = rng.uniform(0.01, 0.1, T)
+    o = oracle.mlp(K[None], Q[None], V[None], eta[None], 0.0, W1[None],
+                   None if b1 is None else b1[None], W2[None],
+                   None if b2 is None else b2[None], chunk=chunk)
+    r = mlp_dual(K, Q, V, eta, 0.0, W1, b1, W2, b2, chunk)
+    np.testing.assert_allclose(o[0][0], r[0], rtol=0, atol=1e-12)
+    for a, b in zip(o[1:], r[1:]):
+        if b is None:
+            assert a is None
+        else:
+            np.testing.assert_allclose(a[0], b, rtol=0, atol=1e-12)
+
+
+def test_mlp_bias_free_keeps_zero_bias_semantics():
+    """NULL biases = the model without biases: equals running with zero biases and
+    freezing them, i.e. the bias-free dual form."""
+    rng = np.random.default_rng(30)
+    d, hd, T = 3, 6, 10
+    W1, _, W2, _ = _rand_mlp(rng, d, hd)
+    K, Q, V = (rng.standard_normal((1, T, d)) for _ in range(3))
+    o = oracle.mlp(K, Q, V, None, 0.2, W1[None], None, W2[None], None, chunk=3)
+    r = mlp_dual(K[0], Q[0], V[0], None, 0.2, W1, None, W2, None, 3)
+    np.testing.assert_allclose(o[0][0], r[0], rtol=0, atol=1e-12)
+    assert o[2] is None and o[4] is None
+
+
+# ---------------------------------------------------------------- inputs / golden
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(40)
+    x = rng.standard_normal(100000).astype(np.float32) * 3
+    # exact ties: a value halfway between two bf16 numbers rounds to the even one
+    x[:4] = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8, 0.0], np.float32)
+    ours = round_to_bf16(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_inputs_are_deterministic_per_slice():
+    wl = workload("linear_b16_8x12", T=64)
+    full = make_inputs(wl, 1)
+    part = make_inputs(wl, 1, slices=[(3, 7)])
+    i = 3 * wl.H + 7
+    np.testing.assert_array_equal(full["K"][i], part["K"][0])
+    np.testing.assert_array_equal(full["eta"][i], part["eta"][0])
+    np.testing.assert_allclose(np.linalg.norm(full["K"], axis=-1), 1.0, atol=1e-2)
+    assert (full["eta"] > 0).all() and (full["eta"] < 0.1).all()
+
+
+def test_golden_fixtures_unchanged():
+    """Regression fixtures written by tests/golden/make_golden.py (oracle only)."""
+    with open(os.path.join(HERE, "golden", "oracle_tiny.json")) as f:
+        gold = json.load(f)
+    for case in gold["cases"]:
+        a = {k: (None if v is None else np.array(v, np.float64)) for k, v in case["inputs"].items()}
+        if case["model"] == "linear":
+            Z, W = oracle.linear(a["K"], a["Q"], a["V"], a["eta"], case["eta_scalar"], a["W0"],
+                                 chunk=case["chunk"])
+            outs = {"Z": Z, "W": W}
+        else:
+            Z, W1, b1, W2, b2 = oracle.mlp(a["K"], a["Q"], a["V"], a["eta"], case["eta_scalar"],
+                                           a["W1"], a["b1"], a["W2"], a["b2"], chunk=case["chunk"])
+            outs = {"Z": Z, "W1": W1, "b1": b1, "W2": W2, "b2": b2}
+        for k, v in case["outputs"].items():
+            np.testing.assert_allclose(outs[k], np.array(v), rtol=0, atol=1e-13)
