@@ -1,0 +1,153 @@
+/*
+ * ttt.h — C ABI of libttt_amd.so: forward scan of a test-time-training (TTT)
+ * layer on an AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ * -------------------------
+ * A TTT layer carries, per (batch, head), a fast-weight state that is itself a
+ * small model; reading the sequence trains that model one gradient step at a
+ * time (PaperTrace "5 · TestingTime 训练与长上下文" §1.1 and §2.1: an initial
+ * state W0, an update rule W_t = W_{t-1} - eta * grad l(W_{t-1}; x_t) and an
+ * output rule y_t = f(q_t; W_t); keys, queries and values arrive already
+ * projected).  The loss is the key-to-value reconstruction
+ * l = 1/2 ||f(k_t) - v_t||^2 (same page §2.3).  Tokens are taken in chunks of
+ * `chunk` tokens (same page §1.1, "b = 16"); every gradient in a chunk is taken
+ * at the chunk-start state, token t reads with the chunk's updates up to and
+ * including its own, and the state then advances by the eta-weighted sum of the
+ * chunk's gradients.  eta_s scales the gradient of token s (the writer).
+ *
+ *   TTT-Linear  f_W(k) = W k,               W  : d x d            (§2.3)
+ *   TTT-MLP     f(k) = W2 gelu(W1 k + b1) + b2, W1 : 4d x d, b1 : 4d,
+ *               W2 : d x 4d, b2 : d; GELU in its exact erf form
+ *               (diosapp "Test-Time Training (TTT) guide" §3: two layers,
+ *               hidden width 4x, GELU)
+ *
+ * Inside a chunk the kernels use the dual form (diosapp guide §3; PaperTrace
+ * §1.1): for TTT-Linear, with the chunk's keys/queries/values as columns,
+ *   E = W K - V,   Z = W Q - E diag(eta) triu(K^T Q),   W <- W - E diag(eta) K^T.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - All tensor pointers are DEVICE pointers, row-major and contiguous.
+ *    K, Q, V, Z, W0/W_out, W1/W2 and their outputs must be 16-byte aligned;
+ *    eta and the bias vectors 4-byte aligned.
+ *  - K, Q, V  : [B, H, T, d] in `io_dtype` (one row of d features per token).
+ *    Z        : [B, H, T, d] in `io_dtype` (fp32 -> bf16 rounds to nearest even).
+ *    eta      : [B, H, T] fp32 per-token learning rate, or NULL to use
+ *               `eta_scalar` for every token.
+ *    states   : always fp32; row index = output feature.
+ *  - Any T >= 1; a last chunk shorter than `chunk` is processed with the
+ *    tokens it has.
+ *  - Ownership: the caller allocates every buffer, including the workspace.
+ *    The library allocates no device memory, keeps no state between calls and
+ *    may be called from several host threads at once.
+ *  - Streams: all work is enqueued on `stream` (a hipStream_t; NULL = the
+ *    default stream).  The call returns before the work completes; outputs are
+ *    valid once the stream has been synchronised.  The library never
+ *    synchronises.
+ *  - Aliasing: the final-state outputs may alias the matching initial-state
+ *    inputs (W_out == W0 updates in place).  Z must not overlap any input.
+ *  - Errors: arguments are checked on the host before any HIP call; a failed
+ *    check returns a negative ttt_status and enqueues nothing.  A kernel
+ *    launch failure returns TTT_ERR_LAUNCH.  Non-finite values inside tensors
+ *    are not checked: they propagate (IEEE) within their own (batch, head)
+ *    slice only.
+ */
+#ifndef TTT_H
+#define TTT_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TTT_OK = 0,
+    TTT_ERR_INVALID_ARG = -1,   /* null/misaligned pointer, non-positive size, bad enum,
+                                   non-finite eta_scalar with eta == NULL */
+    TTT_ERR_UNSUPPORTED = -2,   /* valid arguments outside what the kernels implement */
+    TTT_ERR_WORKSPACE = -3,     /* workspace missing or smaller than required */
+    TTT_ERR_LAUNCH = -4         /* the HIP runtime rejected a kernel launch */
+} ttt_status;
+
+typedef enum {
+    TTT_DTYPE_F32 = 0,          /* K, Q, V, Z in fp32 */
+    TTT_DTYPE_BF16 = 1          /* K, Q, V, Z in bf16; arithmetic accumulates in fp32 */
+} ttt_dtype;
+
+/* Kernel plans.  AUTO picks the fastest plan that supports the shape; the others
+ * force one (TTT_ERR_UNSUPPORTED if it cannot run the shape) so that tests can
+ * compare plans on the same inputs. */
+typedef enum {
+    TTT_PLAN_AUTO = 0,
+    TTT_PLAN_GENERIC = 1,       /* fp32 vector ALU, any chunk, fp32 or bf16 I/O */
+    TTT_PLAN_MFMA = 2,          /* bf16 matrix cores, chunk <= 16 or a multiple of 16 <= 64 */
+    TTT_PLAN_BIGCHUNK = 3       /* bf16 matrix cores, three stages, chunk a multiple of 64 >= 128 */
+} ttt_plan;
+
+/* ------------------------------------------------------------------------ */
+/* TTT-Linear                                                                */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace ttt_linear_fwd needs for this shape and plan (0 when none).
+ * Returns 0 as well for shapes the plan cannot run. */
+size_t ttt_linear_workspace_bytes(int B, int H, int T, int d, int chunk,
+                                  int io_dtype, int plan);
+
+/* Plan that ttt_linear_fwd would run for this shape (never TTT_PLAN_AUTO), or a
+ * negative ttt_status if no plan supports it. */
+int ttt_linear_select_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan);
+
+/* Forward scan of TTT-Linear.
+ *   W0    : [B, H, d, d] fp32 initial state.
+ *   W_out : [B, H, d, d] fp32 state after the last token (may alias W0).
+ *   d     : 16, 32, 64 or 128.   chunk : >= 1.
+ *   workspace / workspace_bytes : device scratch of at least
+ *           ttt_linear_workspace_bytes(...) bytes, 256-byte aligned (may be NULL
+ *           when that is 0).
+ * The state update follows PaperTrace "5 · TestingTime 训练与长上下文" §1.1/§2.3;
+ * with chunk == 1 it is the delta rule of the same page §2.1. */
+int ttt_linear_fwd(const void* K, const void* Q, const void* V,
+                   const float* eta, float eta_scalar,
+                   const float* W0,
+                   void* Z, float* W_out,
+                   int B, int H, int T, int d, int chunk, int io_dtype,
+                   void* workspace, size_t workspace_bytes,
+                   void* stream, int plan);
+
+/* ------------------------------------------------------------------------ */
+/* TTT-MLP (hidden width 4d)                                                 */
+/* ------------------------------------------------------------------------ */
+
+size_t ttt_mlp_workspace_bytes(int B, int H, int T, int d, int chunk, int io_dtype, int plan);
+
+int ttt_mlp_select_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan);
+
+/* Forward scan of TTT-MLP, f(k) = W2 gelu(W1 k + b1) + b2.
+ *   W1_0 : [B, H, 4d, d]   b1_0 : [B, H, 4d] or NULL (model without b1)
+ *   W2_0 : [B, H, d, 4d]   b2_0 : [B, H, d]  or NULL (model without b2)
+ *   W1_out, W2_out : final states (may alias W1_0, W2_0);
+ *   b1_out / b2_out: final biases, NULL exactly when b1_0 / b2_0 is NULL.
+ *   d : 64 (hidden 256).  chunk : >= 1.
+ * A present bias is part of the state and takes the same gradient step; an
+ * absent one is a model without that bias. */
+int ttt_mlp_fwd(const void* K, const void* Q, const void* V,
+                const float* eta, float eta_scalar,
+                const float* W1_0, const float* b1_0,
+                const float* W2_0, const float* b2_0,
+                void* Z, float* W1_out, float* b1_out, float* W2_out, float* b2_out,
+                int B, int H, int T, int d, int chunk, int io_dtype,
+                void* workspace, size_t workspace_bytes,
+                void* stream, int plan);
+
+/* Static string for a ttt_status value (or "unknown status"). */
+const char* ttt_status_string(int status);
+
+/* Static string naming a plan ("generic", "mfma", "bigchunk", ...). */
+const char* ttt_plan_name(int plan);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TTT_H */

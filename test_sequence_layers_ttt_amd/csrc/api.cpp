@@ -1,0 +1,183 @@
+// C ABI of libttt_amd.so (declared in include/ttt.h).
+//
+// Every argument is validated here, on the host, before any HIP call; a failed
+// check returns a negative status and enqueues nothing.  Plan selection picks a
+// kernel for the shape; the launchers in the kernel files only size grids.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/ttt.h"
+#include "launch.h"
+
+using namespace ttt;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool dims_ok(int B, int H, int T, int d, int chunk)
+{
+    if (B <= 0 || H <= 0 || T <= 0 || d <= 0 || chunk <= 0) return false;
+    // keep every element index inside 2^62 and the grid inside 2^31 workgroups
+    long double n = (long double)B * H * T * d;
+    return n < 4.0e18L && (long double)B * H * 64 < 2.0e9L;
+}
+
+int linear_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
+{
+    if (!dims_ok(B, H, T, d, chunk)) return TTT_ERR_INVALID_ARG;
+    if (io_dtype != TTT_DTYPE_F32 && io_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARG;
+    if (plan < TTT_PLAN_AUTO || plan > TTT_PLAN_BIGCHUNK) return TTT_ERR_INVALID_ARG;
+    if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
+    const int bf16 = io_dtype == TTT_DTYPE_BF16;
+    const bool mfma = linear_mfma_supported(d, chunk, bf16);
+    const bool big = linear_bigchunk_supported(d, chunk, bf16);
+    switch (plan) {
+    case TTT_PLAN_GENERIC: return TTT_PLAN_GENERIC;
+    case TTT_PLAN_MFMA: return mfma ? TTT_PLAN_MFMA : TTT_ERR_UNSUPPORTED;
+    case TTT_PLAN_BIGCHUNK: return big ? TTT_PLAN_BIGCHUNK : TTT_ERR_UNSUPPORTED;
+    default: break;
+    }
+    if (mfma) return TTT_PLAN_MFMA;
+    if (big) return TTT_PLAN_BIGCHUNK;
+    return TTT_PLAN_GENERIC;
+}
+
+int mlp_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
+{
+    if (!dims_ok(B, H, T, d, chunk)) return TTT_ERR_INVALID_ARG;
+    if (io_dtype != TTT_DTYPE_F32 && io_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARG;
+    if (plan < TTT_PLAN_AUTO || plan > TTT_PLAN_BIGCHUNK) return TTT_ERR_INVALID_ARG;
+    if (d != 16 && d != 32 && d != 64) return TTT_ERR_UNSUPPORTED;
+    const bool mfma = mlp_mfma_supported(d, chunk, io_dtype == TTT_DTYPE_BF16);
+    switch (plan) {
+    case TTT_PLAN_GENERIC: return TTT_PLAN_GENERIC;
+    case TTT_PLAN_MFMA: return mfma ? TTT_PLAN_MFMA : TTT_ERR_UNSUPPORTED;
+    case TTT_PLAN_BIGCHUNK: return TTT_ERR_UNSUPPORTED;
+    default: break;
+    }
+    return mfma ? TTT_PLAN_MFMA : TTT_PLAN_GENERIC;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* ttt_status_string(int status)
+{
+    switch (status) {
+    case TTT_OK: return "ok";
+    case TTT_ERR_INVALID_ARG: return "invalid argument";
+    case TTT_ERR_UNSUPPORTED: return "unsupported shape, dtype or plan";
+    case TTT_ERR_WORKSPACE: return "workspace missing or too small";
+    case TTT_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+const char* ttt_plan_name(int plan)
+{
+    switch (plan) {
+    case TTT_PLAN_AUTO: return "auto";
+    case TTT_PLAN_GENERIC: return "generic";
+    case TTT_PLAN_MFMA: return "mfma";
+    case TTT_PLAN_BIGCHUNK: return "bigchunk";
+    default: return "unknown plan";
+    }
+}
+
+int ttt_linear_select_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
+{
+    return linear_plan(B, H, T, d, chunk, io_dtype, plan);
+}
+
+size_t ttt_linear_workspace_bytes(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
+{
+    int p = linear_plan(B, H, T, d, chunk, io_dtype, plan);
+    if (p == TTT_PLAN_BIGCHUNK) return linear_bigchunk_workspace(B * H, T, d, chunk);
+    return 0;
+}
+
+int ttt_linear_fwd(const void* K, const void* Q, const void* V,
+                   const float* eta, float eta_scalar, const float* W0,
+                   void* Z, float* W_out,
+                   int B, int H, int T, int d, int chunk, int io_dtype,
+                   void* workspace, size_t workspace_bytes, void* stream, int plan)
+{
+    if (!K || !Q || !V || !W0 || !Z || !W_out) return TTT_ERR_INVALID_ARG;
+    if (!aligned(K, 16) || !aligned(Q, 16) || !aligned(V, 16) || !aligned(Z, 16) ||
+        !aligned(W0, 16) || !aligned(W_out, 16))
+        return TTT_ERR_INVALID_ARG;
+    if (eta ? !aligned(eta, 4) : !std::isfinite(eta_scalar)) return TTT_ERR_INVALID_ARG;
+    const int p = linear_plan(B, H, T, d, chunk, io_dtype, plan);
+    if (p < 0) return p;
+    const size_t need = ttt_linear_workspace_bytes(B, H, T, d, chunk, io_dtype, p);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return TTT_ERR_WORKSPACE;
+
+    LinearArgs a;
+    a.K = K; a.Q = Q; a.V = V; a.eta = eta; a.eta_scalar = eta_scalar; a.W0 = W0;
+    a.Z = Z; a.W_out = W_out; a.BH = B * H; a.T = T; a.d = d; a.chunk = chunk;
+    a.bf16 = io_dtype == TTT_DTYPE_BF16;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    switch (p) {
+    case TTT_PLAN_MFMA: return launch_status(launch_linear_mfma(a, s));
+    case TTT_PLAN_BIGCHUNK: return launch_status(launch_linear_bigchunk(a, s));
+    default: return launch_status(launch_linear_generic(a, s));
+    }
+}
+
+int ttt_mlp_select_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
+{
+    return mlp_plan(B, H, T, d, chunk, io_dtype, plan);
+}
+
+size_t ttt_mlp_workspace_bytes(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
+{
+    int p = mlp_plan(B, H, T, d, chunk, io_dtype, plan);
+    if (p == TTT_PLAN_GENERIC) return mlp_generic_workspace(B * H, T, d, chunk);
+    return 0;
+}
+
+int ttt_mlp_fwd(const void* K, const void* Q, const void* V,
+                const float* eta, float eta_scalar,
+                const float* W1_0, const float* b1_0, const float* W2_0, const float* b2_0,
+                void* Z, float* W1_out, float* b1_out, float* W2_out, float* b2_out,
+                int B, int H, int T, int d, int chunk, int io_dtype,
+                void* workspace, size_t workspace_bytes, void* stream, int plan)
+{
+    if (!K || !Q || !V || !W1_0 || !W2_0 || !Z || !W1_out || !W2_out) return TTT_ERR_INVALID_ARG;
+    if ((b1_0 == nullptr) != (b1_out == nullptr) || (b2_0 == nullptr) != (b2_out == nullptr))
+        return TTT_ERR_INVALID_ARG;
+    if (!aligned(K, 16) || !aligned(Q, 16) || !aligned(V, 16) || !aligned(Z, 16) ||
+        !aligned(W1_0, 16) || !aligned(W2_0, 16) || !aligned(W1_out, 16) ||
+        !aligned(W2_out, 16))
+        return TTT_ERR_INVALID_ARG;
+    if ((b1_0 && (!aligned(b1_0, 4) || !aligned(b1_out, 4))) ||
+        (b2_0 && (!aligned(b2_0, 4) || !aligned(b2_out, 4))))
+        return TTT_ERR_INVALID_ARG;
+    if (eta ? !aligned(eta, 4) : !std::isfinite(eta_scalar)) return TTT_ERR_INVALID_ARG;
+    const int p = mlp_plan(B, H, T, d, chunk, io_dtype, plan);
+    if (p < 0) return p;
+    const size_t need = ttt_mlp_workspace_bytes(B, H, T, d, chunk, io_dtype, p);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return TTT_ERR_WORKSPACE;
+
+    MlpArgs a;
+    a.K = K; a.Q = Q; a.V = V; a.eta = eta; a.eta_scalar = eta_scalar;
+    a.W1 = W1_0; a.b1 = b1_0; a.W2 = W2_0; a.b2 = b2_0;
+    a.Z = Z; a.W1_out = W1_out; a.b1_out = b1_out; a.W2_out = W2_out; a.b2_out = b2_out;
+    a.BH = B * H; a.T = T; a.d = d; a.chunk = chunk;
+    a.bf16 = io_dtype == TTT_DTYPE_BF16;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (p == TTT_PLAN_MFMA) return launch_status(launch_mlp_mfma(a, s));
+    return launch_status(launch_mlp_generic(a, s));
+}
+
+}  // extern "C"

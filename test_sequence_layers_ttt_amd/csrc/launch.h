@@ -1,0 +1,63 @@
+// Internal launchers, one per kernel plan.  The C ABI (api.cpp) validates every
+// argument before calling these; they only size the grid and launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace ttt {
+
+struct LinearArgs {
+    const void* K;
+    const void* Q;
+    const void* V;
+    const float* eta;      // [BH, T] or nullptr
+    float eta_scalar;
+    const float* W0;       // [BH, d, d]
+    void* Z;
+    float* W_out;
+    int BH, T, d, chunk;
+    int bf16;              // 1: K/Q/V/Z are bf16, 0: fp32
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+struct MlpArgs {
+    const void* K;
+    const void* Q;
+    const void* V;
+    const float* eta;
+    float eta_scalar;
+    const float* W1;       // [BH, 4d, d]
+    const float* b1;       // [BH, 4d] or nullptr
+    const float* W2;       // [BH, d, 4d]
+    const float* b2;       // [BH, d] or nullptr
+    void* Z;
+    float* W1_out;
+    float* b1_out;
+    float* W2_out;
+    float* b2_out;
+    int BH, T, d, chunk;
+    int bf16;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+// fp32 vector-ALU dual form, any chunk, d <= 128.
+hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
+
+// bf16 MFMA path for chunk <= 16 or chunk in {32, 48, 64}; d in {32, 64, 128}.
+bool linear_mfma_supported(int d, int chunk, int bf16);
+hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
+
+// three-stage large-chunk path; chunk a multiple of 64, >= 128; d in {64, 128}; bf16.
+bool linear_bigchunk_supported(int d, int chunk, int bf16);
+size_t linear_bigchunk_workspace(int BH, int T, int d, int chunk);
+hipError_t launch_linear_bigchunk(const LinearArgs& a, hipStream_t s);
+
+// TTT-MLP: generic fp32 path (d <= 64) and the bf16 MFMA path (d == 64, chunk <= 16).
+size_t mlp_generic_workspace(int BH, int T, int d, int chunk);
+hipError_t launch_mlp_generic(const MlpArgs& a, hipStream_t s);
+bool mlp_mfma_supported(int d, int chunk, int bf16);
+hipError_t launch_mlp_mfma(const MlpArgs& a, hipStream_t s);
+
+}  // namespace ttt

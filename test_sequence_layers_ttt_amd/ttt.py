@@ -1,0 +1,199 @@
+"""Python binding of libttt_amd.so (the C ABI in include/ttt.h).
+
+Argument marshalling only: torch provides device memory and the stream; every
+step of the scan runs in the library's HIP kernels.  There is no fallback: if
+the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libttt_amd.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3, -4
+DTYPE_F32, DTYPE_BF16 = 0, 1
+PLAN_AUTO, PLAN_GENERIC, PLAN_MFMA, PLAN_BIGCHUNK = 0, 1, 2, 3
+
+# every symbol include/ttt.h declares
+EXPORTS = ("ttt_linear_workspace_bytes", "ttt_linear_select_plan", "ttt_linear_fwd",
+           "ttt_mlp_workspace_bytes", "ttt_mlp_select_plan", "ttt_mlp_fwd",
+           "ttt_status_string", "ttt_plan_name")
+
+
+class TTTError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__("%s: %s (status %d)" % (what, status_string(status), status))
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libttt_amd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libttt_amd.so is not built (run __graft_entry__.build()); "
+                               "the TTT scan has no CPU fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        L.ttt_linear_workspace_bytes.argtypes = [i] * 7
+        L.ttt_linear_workspace_bytes.restype = sz
+        L.ttt_linear_select_plan.argtypes = [i] * 7
+        L.ttt_linear_select_plan.restype = i
+        L.ttt_linear_fwd.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp, i]
+        L.ttt_linear_fwd.restype = i
+        L.ttt_mlp_workspace_bytes.argtypes = [i] * 7
+        L.ttt_mlp_workspace_bytes.restype = sz
+        L.ttt_mlp_select_plan.argtypes = [i] * 7
+        L.ttt_mlp_select_plan.restype = i
+        L.ttt_mlp_fwd.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  i, i, i, i, i, i, vp, sz, vp, i]
+        L.ttt_mlp_fwd.restype = i
+        L.ttt_status_string.argtypes = [i]
+        L.ttt_status_string.restype = ctypes.c_char_p
+        L.ttt_plan_name.argtypes = [i]
+        L.ttt_plan_name.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().ttt_status_string(int(status)).decode()
+
+
+def plan_name(plan: int) -> str:
+    return lib().ttt_plan_name(int(plan)).decode()
+
+
+def _io_dtype(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError("K/Q/V must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device, stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _check(t, name, shape, dtype=None):
+    import torch
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s" % (name, dtype))
+
+
+def linear_workspace_bytes(B, H, T, d, chunk, io_dtype, plan=PLAN_AUTO) -> int:
+    return int(lib().ttt_linear_workspace_bytes(B, H, T, d, chunk, io_dtype, plan))
+
+
+def linear_select_plan(B, H, T, d, chunk, io_dtype, plan=PLAN_AUTO) -> int:
+    return int(lib().ttt_linear_select_plan(B, H, T, d, chunk, io_dtype, plan))
+
+
+def mlp_workspace_bytes(B, H, T, d, chunk, io_dtype, plan=PLAN_AUTO) -> int:
+    return int(lib().ttt_mlp_workspace_bytes(B, H, T, d, chunk, io_dtype, plan))
+
+
+def mlp_select_plan(B, H, T, d, chunk, io_dtype, plan=PLAN_AUTO) -> int:
+    return int(lib().ttt_mlp_select_plan(B, H, T, d, chunk, io_dtype, plan))
+
+
+def _workspace(nbytes, device, workspace):
+    import torch
+    if nbytes == 0:
+        return None
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return workspace
+
+
+def linear_fwd(K, Q, V, eta, W0, chunk: int, eta_scalar: float = 0.0, *, Z=None, W_out=None,
+               workspace=None, plan: int = PLAN_AUTO, stream=None) -> Tuple:
+    """TTT-Linear forward scan.  K, Q, V: [B, H, T, d] fp32 or bf16; eta: [B, H, T]
+    fp32 or None (then eta_scalar); W0: [B, H, d, d] fp32.  Returns (Z, W_out)."""
+    import torch
+    B, H, T, d = K.shape
+    _check(K, "K", (B, H, T, d))
+    _check(Q, "Q", (B, H, T, d), K.dtype)
+    _check(V, "V", (B, H, T, d), K.dtype)
+    _check(W0, "W0", (B, H, d, d), torch.float32)
+    if eta is not None:
+        _check(eta, "eta", (B, H, T), torch.float32)
+    if Z is None:
+        Z = torch.empty_like(K)
+    if W_out is None:
+        W_out = torch.empty_like(W0)
+    _check(Z, "Z", (B, H, T, d), K.dtype)
+    _check(W_out, "W_out", (B, H, d, d), torch.float32)
+    io = _io_dtype(K)
+    nbytes = linear_workspace_bytes(B, H, T, d, chunk, io, plan)
+    ws = _workspace(nbytes, K.device, workspace)
+    rc = lib().ttt_linear_fwd(K.data_ptr(), Q.data_ptr(), V.data_ptr(), _ptr(eta),
+                              float(eta_scalar), W0.data_ptr(), Z.data_ptr(), W_out.data_ptr(),
+                              B, H, T, d, int(chunk), io, _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream(K.device, stream),
+                              int(plan))
+    if rc != OK:
+        raise TTTError(rc, "ttt_linear_fwd")
+    return Z, W_out
+
+
+def mlp_fwd(K, Q, V, eta, W1, b1, W2, b2, chunk: int, eta_scalar: float = 0.0, *, Z=None,
+            W1_out=None, b1_out=None, W2_out=None, b2_out=None, workspace=None,
+            plan: int = PLAN_AUTO, stream=None) -> Tuple:
+    """TTT-MLP forward scan (hidden 4d).  W1: [B, H, 4d, d], b1: [B, H, 4d] or None,
+    W2: [B, H, d, 4d], b2: [B, H, d] or None.  Returns (Z, W1, b1, W2, b2) final."""
+    import torch
+    B, H, T, d = K.shape
+    hd = 4 * d
+    _check(K, "K", (B, H, T, d))
+    _check(Q, "Q", (B, H, T, d), K.dtype)
+    _check(V, "V", (B, H, T, d), K.dtype)
+    _check(W1, "W1", (B, H, hd, d), torch.float32)
+    _check(W2, "W2", (B, H, d, hd), torch.float32)
+    if b1 is not None:
+        _check(b1, "b1", (B, H, hd), torch.float32)
+    if b2 is not None:
+        _check(b2, "b2", (B, H, d), torch.float32)
+    if eta is not None:
+        _check(eta, "eta", (B, H, T), torch.float32)
+    Z = torch.empty_like(K) if Z is None else Z
+    W1_out = torch.empty_like(W1) if W1_out is None else W1_out
+    W2_out = torch.empty_like(W2) if W2_out is None else W2_out
+    if b1 is not None and b1_out is None:
+        b1_out = torch.empty_like(b1)
+    if b2 is not None and b2_out is None:
+        b2_out = torch.empty_like(b2)
+    io = _io_dtype(K)
+    nbytes = mlp_workspace_bytes(B, H, T, d, chunk, io, plan)
+    ws = _workspace(nbytes, K.device, workspace)
+    rc = lib().ttt_mlp_fwd(K.data_ptr(), Q.data_ptr(), V.data_ptr(), _ptr(eta), float(eta_scalar),
+                           W1.data_ptr(), _ptr(b1), W2.data_ptr(), _ptr(b2),
+                           Z.data_ptr(), W1_out.data_ptr(), _ptr(b1_out), W2_out.data_ptr(),
+                           _ptr(b2_out), B, H, T, d, int(chunk), io, _ptr(ws),
+                           0 if ws is None else ws.numel(), _stream(K.device, stream), int(plan))
+    if rc != OK:
+        raise TTTError(rc, "ttt_mlp_fwd")
+    return Z, W1_out, b1_out, W2_out, b2_out

@@ -1,0 +1,136 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, and rejects bad arguments before any HIP call (no GPU needed; every call
+here carries at least one argument the host validation refuses, so nothing is
+ever launched)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from test_sequence_layers_ttt_amd import ttt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttt.h")
+
+FAKE = 0x10000000          # aligned, never dereferenced: validation fails first
+MISALIGNED = FAKE + 2
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ttt_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_what_the_binding_lists():
+    assert declared_functions() == sorted(ttt.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ttt.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", ttt.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in declared_functions():
+        assert name in exported, name
+
+
+def test_status_and_plan_strings():
+    assert ttt.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert ttt.status_string(s) not in ("ok", "unknown status")
+    assert ttt.status_string(17) == "unknown status"
+    assert [ttt.plan_name(p) for p in range(4)] == ["auto", "generic", "mfma", "bigchunk"]
+
+
+def _linear(**kw):
+    a = dict(K=FAKE, Q=FAKE, V=FAKE, eta=FAKE, eta_scalar=0.1, W0=FAKE, Z=FAKE, W=FAKE,
+             B=1, H=1, T=16, d=16, chunk=16, io=0, ws=None, wsb=0, stream=None, plan=0)
+    a.update(kw)
+    return ttt.lib().ttt_linear_fwd(a["K"], a["Q"], a["V"], a["eta"], a["eta_scalar"], a["W0"],
+                                    a["Z"], a["W"], a["B"], a["H"], a["T"], a["d"], a["chunk"],
+                                    a["io"], a["ws"], a["wsb"], a["stream"], a["plan"])
+
+
+def _mlp(**kw):
+    a = dict(K=FAKE, Q=FAKE, V=FAKE, eta=None, eta_scalar=0.05, W1=FAKE, b1=FAKE, W2=FAKE,
+             b2=FAKE, Z=FAKE, W1o=FAKE, b1o=FAKE, W2o=FAKE, b2o=FAKE, B=1, H=1, T=16, d=64,
+             chunk=16, io=1, ws=None, wsb=0, stream=None, plan=0)
+    a.update(kw)
+    return ttt.lib().ttt_mlp_fwd(a["K"], a["Q"], a["V"], a["eta"], a["eta_scalar"], a["W1"],
+                                 a["b1"], a["W2"], a["b2"], a["Z"], a["W1o"], a["b1o"], a["W2o"],
+                                 a["b2o"], a["B"], a["H"], a["T"], a["d"], a["chunk"], a["io"],
+                                 a["ws"], a["wsb"], a["stream"], a["plan"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=None), ttt.ERR_INVALID_ARG),
+    (dict(Q=None), ttt.ERR_INVALID_ARG),
+    (dict(V=None), ttt.ERR_INVALID_ARG),
+    (dict(W0=None), ttt.ERR_INVALID_ARG),
+    (dict(Z=None), ttt.ERR_INVALID_ARG),
+    (dict(W=None), ttt.ERR_INVALID_ARG),
+    (dict(K=MISALIGNED), ttt.ERR_INVALID_ARG),
+    (dict(Z=MISALIGNED), ttt.ERR_INVALID_ARG),
+    (dict(W0=FAKE + 8), ttt.ERR_INVALID_ARG),
+    (dict(eta=FAKE + 1), ttt.ERR_INVALID_ARG),
+    (dict(eta=None, eta_scalar=math.nan), ttt.ERR_INVALID_ARG),
+    (dict(eta=None, eta_scalar=math.inf), ttt.ERR_INVALID_ARG),
+    (dict(B=0), ttt.ERR_INVALID_ARG),
+    (dict(H=-1), ttt.ERR_INVALID_ARG),
+    (dict(T=0), ttt.ERR_INVALID_ARG),
+    (dict(chunk=0), ttt.ERR_INVALID_ARG),
+    (dict(d=0), ttt.ERR_INVALID_ARG),
+    (dict(io=2), ttt.ERR_INVALID_ARG),
+    (dict(plan=7), ttt.ERR_INVALID_ARG),
+    (dict(d=48), ttt.ERR_UNSUPPORTED),
+    (dict(d=256), ttt.ERR_UNSUPPORTED),
+    (dict(d=16, io=1, plan=ttt.PLAN_MFMA), ttt.ERR_UNSUPPORTED),
+    (dict(io=0, d=64, plan=ttt.PLAN_BIGCHUNK), ttt.ERR_UNSUPPORTED),
+    (dict(B=1 << 20, H=1 << 20, T=1 << 20), ttt.ERR_INVALID_ARG),
+])
+def test_linear_rejects_bad_arguments(kw, status):
+    assert _linear(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=None), ttt.ERR_INVALID_ARG),
+    (dict(W1=None), ttt.ERR_INVALID_ARG),
+    (dict(W2o=None), ttt.ERR_INVALID_ARG),
+    (dict(b1o=None), ttt.ERR_INVALID_ARG),          # b1 given, b1_out missing
+    (dict(b2=None), ttt.ERR_INVALID_ARG),           # b2_out given, b2 missing
+    (dict(b1=FAKE + 2), ttt.ERR_INVALID_ARG),
+    (dict(W2=FAKE + 4), ttt.ERR_INVALID_ARG),
+    (dict(eta_scalar=math.nan), ttt.ERR_INVALID_ARG),
+    (dict(d=128), ttt.ERR_UNSUPPORTED),
+    (dict(d=48), ttt.ERR_UNSUPPORTED),
+    (dict(io=5), ttt.ERR_INVALID_ARG),
+    (dict(T=-3), ttt.ERR_INVALID_ARG),
+    (dict(plan=ttt.PLAN_BIGCHUNK), ttt.ERR_UNSUPPORTED),
+    (dict(chunk=32, plan=ttt.PLAN_GENERIC), ttt.ERR_WORKSPACE),   # needs a workspace
+    (dict(chunk=32, plan=ttt.PLAN_GENERIC, ws=FAKE, wsb=16), ttt.ERR_WORKSPACE),
+])
+def test_mlp_rejects_bad_arguments(kw, status):
+    assert _mlp(**kw) == status
+
+
+def test_plan_selection_and_workspace_are_host_only():
+    assert ttt.linear_select_plan(1, 1, 256, 16, 16, ttt.DTYPE_F32) == ttt.PLAN_GENERIC
+    assert ttt.linear_select_plan(1, 1, 256, 16, 16, 0, ttt.PLAN_GENERIC) == ttt.PLAN_GENERIC
+    assert ttt.linear_select_plan(1, 1, 256, 24, 16, 0) == ttt.ERR_UNSUPPORTED
+    assert ttt.linear_workspace_bytes(8, 12, 2048, 64, 16, ttt.DTYPE_BF16) == 0
+    assert ttt.mlp_workspace_bytes(1, 2, 64, 64, 16, 1, ttt.PLAN_GENERIC) == 0
+    assert ttt.mlp_workspace_bytes(1, 2, 64, 64, 32, 1, ttt.PLAN_GENERIC) == \
+        2 * (2 * 256 * 64 + 256 + 64) * 4
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    K = torch.zeros(1, 1, 16, 16)
+    with pytest.raises(ValueError):
+        ttt.linear_fwd(K, K, K, None, torch.zeros(1, 1, 16, 16), 16, 0.1)

@@ -1,0 +1,136 @@
+"""GPU parity of ttt_linear_fwd against the fp64 oracle (element by element).
+
+Tolerance: max relative error per (batch, head) slice, max|gpu - oracle| /
+max|oracle|, 1e-4 for fp32 I/O and 2e-2 for bf16 I/O with fp32 state."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import TOL, rel_err, run_linear, say, take
+from test_sequence_layers_ttt_amd import inputs, ttt
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ttt.lib()
+    return torch.device("cuda:0")
+
+
+def small(d, chunk, io, per_token, T=77, B=2, H=3, seed=101):
+    base = inputs.workload("linear_b16_8x12")
+    return base.with_(B=B, H=H, T=T, d=d, chunk=chunk, io=io,
+                      eta_mode="token" if per_token else "scalar",
+                      eta_value=0.1 if per_token else 0.07), seed
+
+
+def check_linear(wl, seed, dev, plan, slices=None):
+    x = inputs.make_inputs(wl, seed)
+    p = ttt.linear_select_plan(wl.B, wl.H, wl.T, wl.d, wl.chunk, 1 if wl.io == "bf16" else 0, plan)
+    if p < 0:
+        pytest.skip("plan %d does not run this shape" % plan)
+    say("case", wl, "seed", seed, "plan", ttt.plan_name(p))
+    Z, W = run_linear(wl, x, dev, plan=plan)
+    idx = np.arange(wl.BH) if slices is None else np.asarray(slices)
+    xo = take(x, idx)
+    Zo, Wo = oracle.linear(xo["K"], xo["Q"], xo["V"], xo["eta"], xo["eta_scalar"], xo["W0"],
+                           wl.chunk)
+    ez, ew = rel_err(Z[idx], Zo), rel_err(W[idx], Wo)
+    say("  max rel err Z %.3e  W %.3e" % (ez, ew))
+    tol = TOL[wl.io]
+    assert ez < tol and ew < tol, (ez, ew)
+    return ez, ew
+
+
+@pytest.mark.parametrize("plan", [ttt.PLAN_GENERIC, ttt.PLAN_AUTO])
+@pytest.mark.parametrize("d", [16, 32, 64, 128])
+@pytest.mark.parametrize("chunk", [1, 3, 16, 40])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_small_shapes(dev, plan, d, chunk, io):
+    wl, seed = small(d, chunk, io, per_token=(chunk % 2 == 0))
+    check_linear(wl, seed, dev, plan)
+
+
+@pytest.mark.parametrize("T,chunk", [(1, 16), (5, 16), (16, 16), (17, 16), (300, 64), (130, 128)])
+def test_edge_lengths(dev, T, chunk):
+    wl, seed = small(64, chunk, "bf16", per_token=True, T=T)
+    check_linear(wl, seed, dev, ttt.PLAN_AUTO)
+
+
+def test_linear_d16_t256_fp32(dev):
+    wl = inputs.WORKLOADS["linear_d16_t256"]
+    check_linear(wl, inputs.WORKLOAD_SEEDS[wl.name], dev, ttt.PLAN_AUTO)
+
+
+def test_linear_b16_8x12_full(dev):
+    wl = inputs.WORKLOADS["linear_b16_8x12"]
+    check_linear(wl, inputs.WORKLOAD_SEEDS[wl.name], dev, ttt.PLAN_AUTO)
+
+
+def test_linear_b16_1x32_full(dev):
+    wl = inputs.WORKLOADS["linear_b16_1x32"]
+    check_linear(wl, inputs.WORKLOAD_SEEDS[wl.name], dev, ttt.PLAN_AUTO,
+                 slices=[0, 5, 17, 31])
+
+
+def test_linear_b2048_1x16_full(dev):
+    wl = inputs.WORKLOADS["linear_b2048_1x16"]
+    check_linear(wl, inputs.WORKLOAD_SEEDS[wl.name], dev, ttt.PLAN_AUTO, slices=[3, 12])
+
+
+def test_state_may_alias_initial_state(dev):
+    import torch
+    from gpu_helpers import device_inputs
+    wl, seed = small(64, 16, "bf16", per_token=True)
+    x = inputs.make_inputs(wl, seed)
+    a = device_inputs(wl, x, dev)
+    Z1, W1 = ttt.linear_fwd(a["K"], a["Q"], a["V"], a["eta"], a["W0"], wl.chunk)
+    W = a["W0"].clone()
+    Z2, W2 = ttt.linear_fwd(a["K"], a["Q"], a["V"], a["eta"], W, wl.chunk, W_out=W)
+    torch.cuda.synchronize()
+    assert W2.data_ptr() == W.data_ptr()
+    assert torch.equal(W1, W2) and torch.equal(Z1, Z2)
+
+
+def test_bitwise_deterministic_and_stream(dev):
+    import torch
+    from gpu_helpers import device_inputs
+    wl, seed = small(64, 16, "bf16", per_token=True, T=500)
+    x = inputs.make_inputs(wl, seed)
+    a = device_inputs(wl, x, dev)
+    Z1, W1 = ttt.linear_fwd(a["K"], a["Q"], a["V"], a["eta"], a["W0"], wl.chunk)
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        Z2, W2 = ttt.linear_fwd(a["K"], a["Q"], a["V"], a["eta"], a["W0"], wl.chunk)
+    s.synchronize()
+    assert torch.equal(Z1, Z2) and torch.equal(W1, W2)
+
+
+def test_nan_stays_in_its_slice(dev):
+    import torch
+    from gpu_helpers import device_inputs
+    wl, seed = small(64, 16, "bf16", per_token=True, T=64)
+    x = inputs.make_inputs(wl, seed)
+    a = device_inputs(wl, x, dev)
+    a["V"][1, 2, 10, 5] = float("nan")
+    Z, W = ttt.linear_fwd(a["K"], a["Q"], a["V"], a["eta"], a["W0"], wl.chunk)
+    torch.cuda.synchronize()
+    bad = torch.isnan(Z.float()).flatten(2).any(-1) | torch.isnan(W).flatten(2).any(-1)
+    assert bad[1, 2] and int(bad.sum()) == 1
+
+
+def test_eta_zero_reads_initial_state(dev):
+    import torch
+    from gpu_helpers import device_inputs
+    wl, seed = small(32, 16, "f32", per_token=False, T=40)
+    x = inputs.make_inputs(wl, seed)
+    a = device_inputs(wl, x, dev)
+    Z, W = ttt.linear_fwd(a["K"], a["Q"], a["V"], None, a["W0"], wl.chunk, eta_scalar=0.0)
+    torch.cuda.synchronize()
+    assert torch.equal(W, a["W0"])
+    ref = a["Q"].double().cpu() @ a["W0"].double().cpu().transpose(-1, -2)
+    assert float((Z.double().cpu() - ref).abs().max()) < 1e-5

@@ -1,0 +1,75 @@
+"""GPU parity of ttt_mlp_fwd against the fp64 oracle (element by element).
+
+Tolerance as for TTT-Linear: max relative error per (batch, head) slice, 1e-4 for
+fp32 I/O and 2e-2 for bf16 I/O; each of Z, W1, b1, W2, b2 is checked (biases that
+start at zero use a floor of 1e-6 for the denominator)."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import TOL, rel_err, run_mlp, say, take
+from test_sequence_layers_ttt_amd import inputs, ttt
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ttt.lib()
+    return torch.device("cuda:0")
+
+
+def check_mlp(wl, seed, dev, plan, slices=None, bias_init=None):
+    x = inputs.make_inputs(wl, seed)
+    if bias_init is not None and wl.mlp_bias:
+        rng = np.random.default_rng(seed + 999)
+        x["b1"] = (rng.standard_normal(x["b1"].shape) * bias_init).astype(np.float32)
+        x["b2"] = (rng.standard_normal(x["b2"].shape) * bias_init).astype(np.float32)
+    p = ttt.mlp_select_plan(wl.B, wl.H, wl.T, wl.d, wl.chunk, 1 if wl.io == "bf16" else 0, plan)
+    if p < 0:
+        pytest.skip("plan %d does not run this shape" % plan)
+    say("case", wl, "seed", seed, "plan", ttt.plan_name(p))
+    got = run_mlp(wl, x, dev, plan=plan)
+    idx = np.arange(wl.BH) if slices is None else np.asarray(slices)
+    xo = take(x, idx)
+    ref = oracle.mlp(xo["K"], xo["Q"], xo["V"], xo["eta"], xo["eta_scalar"], xo["W1"], xo["b1"],
+                     xo["W2"], xo["b2"], wl.chunk)
+    errs = {}
+    for name, g, r in zip(("Z", "W1", "b1", "W2", "b2"), got, ref):
+        if r is None:
+            assert g is None
+            continue
+        errs[name] = rel_err(g[idx], r)
+    say("  max rel err", " ".join("%s %.3e" % kv for kv in errs.items()))
+    tol = TOL[wl.io]
+    assert all(e < tol for e in errs.values()), errs
+    return errs
+
+
+def small(d, chunk, io, per_token, bias=True, T=45, B=1, H=3):
+    base = inputs.workload("mlp_b16_4x16")
+    return base.with_(B=B, H=H, T=T, d=d, chunk=chunk, io=io, mlp_bias=bias,
+                      eta_mode="token" if per_token else "scalar",
+                      eta_value=0.1 if per_token else 0.05)
+
+
+@pytest.mark.parametrize("plan", [ttt.PLAN_GENERIC, ttt.PLAN_AUTO])
+@pytest.mark.parametrize("d", [16, 64])
+@pytest.mark.parametrize("chunk", [1, 16, 20])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("bias", [True, False])
+def test_small_shapes(dev, plan, d, chunk, io, bias):
+    wl = small(d, chunk, io, per_token=(chunk != 16), bias=bias)
+    check_mlp(wl, 200 + d + chunk, dev, plan, bias_init=0.1)
+
+
+@pytest.mark.parametrize("T", [1, 7, 33])
+def test_edge_lengths(dev, T):
+    check_mlp(small(64, 16, "bf16", per_token=True, T=T), 300 + T, dev, ttt.PLAN_AUTO)
+
+
+def test_mlp_b16_4x16_full(dev):
+    wl = inputs.WORKLOADS["mlp_b16_4x16"]
+    check_mlp(wl, inputs.WORKLOAD_SEEDS[wl.name], dev, ttt.PLAN_AUTO, slices=[0, 21, 42, 63])
