@@ -1,0 +1,307 @@
+"""Benchmark of the TTT forward scan on one MI355X.
+
+One step = one ttt_linear_fwd (or ttt_mlp_fwd) call over the whole batch: every
+(batch, head) scans its T tokens.  Inputs are resident in HBM before the timed
+region; successive steps rotate over enough input/output copies (>= 1 GiB) that
+the 256 MB last-level cache cannot serve them.
+
+Default workload: TTT-Linear, 8 x 12 heads, d = 64, T = 2048, chunk b = 16, bf16
+K/Q/V, per-token eta, fp32 state.  Prints ONE JSON line on stdout; diagnostics go
+to stderr.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--plan auto|generic|mfma|bigchunk]
+                  [--no-cpu-baseline] [--copy-calibration BYTES]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TTT scan tokens/sec (all heads) + % of HBM/MFMA roofline, b=16 d=64"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFS = 2500.0           # MI355X dense bf16 MFMA
+PLANS = {"auto": 0, "generic": 1, "mfma": 2, "bigchunk": 3}
+KERNEL_SOURCES = {"linear": ["linear_mfma.hip", "linear_generic.hip", "linear_bigchunk.hip",
+                             "mfma_common.h"],
+                  "mlp": ["mlp_mfma.hip", "mlp_generic.hip", "mfma_common.h"]}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl) -> float:
+    """Bytes the scan must move once: K, Q, V read, Z written (io dtype), eta read
+    (fp32, per-token mode), initial state read and final state written (fp32)."""
+    esz = 2 if wl.io == "bf16" else 4
+    per_tok = 4 * wl.d * esz + (4 if wl.eta_mode == "token" else 0)
+    if wl.model == "linear":
+        state = wl.d * wl.d * 4
+    else:
+        state = (2 * wl.hidden * wl.d + wl.hidden + wl.d) * 4
+    return float(wl.BH) * (wl.T * per_tok + 2 * state)
+
+
+def algorithmic_flops(wl) -> float:
+    """Flops of the dual form as stated for the method: per chunk of n tokens,
+    TTT-Linear 3*2*d^2*n (W K, W Q, E K^T) + 2*d*n*(n+1) (causal half of the
+    K^T Q and E S products); TTT-MLP 7*2*h*d*n + 2*(d+h)*n*(n+1)."""
+    total = 0.0
+    for c0 in range(0, wl.T, wl.chunk):
+        n = min(wl.chunk, wl.T - c0)
+        if wl.model == "linear":
+            total += 6.0 * wl.d * wl.d * n + 2.0 * wl.d * n * (n + 1)
+        else:
+            h = wl.hidden
+            total += 14.0 * h * wl.d * n + 2.0 * (wl.d + h) * n * (n + 1)
+    return total * wl.BH
+
+
+def kernel_hash(model: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[model]:
+        p = os.path.join(ROOT, "test_sequence_layers_ttt_amd", "csrc", name)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(wl, plan_name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none for this workload or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (wl.name, plan_name))
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    if rec.get("kernel_hash") != kernel_hash(wl.model):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(nbytes: int, steps: int):
+    """A plain device copy of known size, for scaling the FETCH_SIZE/WRITE_SIZE
+    counters (run under rocprofv3 --pmc)."""
+    import torch
+    n = nbytes // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "steps": steps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="linear_b16_8x12")
+    ap.add_argument("--plan", default="auto", choices=sorted(PLANS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-slices", type=int, default=0,
+                    help="slices the oracle times (0 = pick a bounded sample)")
+    ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
+    ap.add_argument("--copy-calibration", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(requested --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from test_sequence_layers_ttt_amd import inputs, ttt
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, args.steps)
+        return
+
+    wl = inputs.WORKLOADS[args.workload]
+    seed = inputs.WORKLOAD_SEEDS[wl.name]
+    dev = torch.device("cuda:0")
+    plan_req = PLANS[args.plan]
+    io_code = ttt.DTYPE_BF16 if wl.io == "bf16" else ttt.DTYPE_F32
+    sel = ttt.linear_select_plan if wl.model == "linear" else ttt.mlp_select_plan
+    plan = sel(wl.B, wl.H, wl.T, wl.d, wl.chunk, io_code, plan_req)
+    if plan < 0:
+        raise SystemExit("plan %s cannot run %s" % (args.plan, wl.name))
+    plan_name = ttt.plan_name(plan)
+    log("workload %s plan %s" % (wl.name, plan_name))
+
+    t0 = time.time()
+    x = inputs.make_inputs(wl, seed)
+    log("inputs generated in %.1f s" % (time.time() - t0))
+
+    io = torch.bfloat16 if wl.io == "bf16" else torch.float32
+    B, H, T, d = wl.B, wl.H, wl.T, wl.d
+
+    def dev_t(a, shape, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).reshape(shape).to(dt).contiguous()
+
+    base = {k: dev_t(x[k], (B, H, T, d), io) for k in ("K", "Q", "V")}
+    base["eta"] = None if x["eta"] is None else dev_t(x["eta"], (B, H, T))
+    if wl.model == "linear":
+        base["W0"] = dev_t(x["W0"], (B, H, d, d))
+    else:
+        base["W1"] = dev_t(x["W1"], (B, H, wl.hidden, d))
+        base["W2"] = dev_t(x["W2"], (B, H, d, wl.hidden))
+        base["b1"] = None if x["b1"] is None else dev_t(x["b1"], (B, H, wl.hidden))
+        base["b2"] = None if x["b2"] is None else dev_t(x["b2"], (B, H, d))
+
+    def out_set():
+        o = {"Z": torch.empty((B, H, T, d), dtype=io, device=dev)}
+        if wl.model == "linear":
+            o["W"] = torch.empty_like(base["W0"])
+        else:
+            o["W1"] = torch.empty_like(base["W1"])
+            o["W2"] = torch.empty_like(base["W2"])
+            o["b1"] = None if base["b1"] is None else torch.empty_like(base["b1"])
+            o["b2"] = None if base["b2"] is None else torch.empty_like(base["b2"])
+        return o
+
+    set_bytes = sum(t.numel() * t.element_size() for t in base.values() if t is not None)
+    set_bytes += sum(t.numel() * t.element_size() for t in out_set().values() if t is not None)
+    ncopies = max(1, min(64, int(math.ceil(args.rotate_bytes / set_bytes))))
+    sets = [({k: (None if v is None else v.clone()) for k, v in base.items()}, out_set())
+            for _ in range(ncopies)]
+    nbytes_ws = (ttt.linear_workspace_bytes if wl.model == "linear" else ttt.mlp_workspace_bytes)(
+        B, H, T, d, wl.chunk, io_code, plan)
+    ws = torch.empty(max(nbytes_ws, 1), dtype=torch.uint8, device=dev) if nbytes_ws else None
+    log("rotating over %d copies of %.1f MB (workspace %.1f MB)" % (
+        ncopies, set_bytes / 1e6, nbytes_ws / 1e6))
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        a, o = sets[i % ncopies]
+        if wl.model == "linear":
+            ttt.linear_fwd(a["K"], a["Q"], a["V"], a["eta"], a["W0"], wl.chunk,
+                           eta_scalar=x["eta_scalar"], Z=o["Z"], W_out=o["W"], workspace=ws,
+                           plan=plan_req, stream=stream)
+        else:
+            ttt.mlp_fwd(a["K"], a["Q"], a["V"], a["eta"], a["W1"], a["b1"], a["W2"], a["b2"],
+                        wl.chunk, eta_scalar=x["eta_scalar"], Z=o["Z"], W1_out=o["W1"],
+                        b1_out=o["b1"], W2_out=o["W2"], b2_out=o["b2"], workspace=ws,
+                        plan=plan_req, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_event = ev0.elapsed_time(ev1) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    log("timed %d steps: %.4f ms/step (events), %.4f ms/step (wall)" % (
+        args.steps, ms_event, ms_step))
+
+    tokens = B * T
+    value = tokens / (ms_step * 1e-3)
+    abytes = algorithmic_bytes(wl)
+    aflops = algorithmic_flops(wl)
+    achieved_gbs = abytes / (ms_event * 1e-3) / 1e9
+    achieved_tfs = aflops / (ms_event * 1e-3) / 1e12
+    traffic = traffic_from_profiles(wl, plan_name)
+    hbm_bound = wl.model == "linear" and plan_name != "bigchunk"
+    if hbm_bound:
+        roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                "traffic": traffic}
+    else:
+        roof = {"bound": "mfma", "achieved": round(achieved_tfs, 2), "peak": BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(achieved_tfs / BF16_PEAK_TFS, 4),
+                "traffic": traffic}
+    roof["kernel_ms"] = round(ms_event, 5)
+    roof["algorithmic_bytes"] = abytes
+    roof["algorithmic_flops"] = aflops
+
+    # parity of the first output set against the oracle, and the CPU baseline
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nsl = args.cpu_sample_slices or wl.BH
+        # bound the oracle's work to roughly 10-30 s of host time
+        per_slice_fma = wl.T * (3 * wl.d * wl.d if wl.model == "linear"
+                                else 7 * wl.hidden * wl.d)
+        ncores = os.cpu_count() or 1
+        budget = 2.0e10 * max(1, min(ncores, 16))
+        if not args.cpu_sample_slices:
+            nsl = int(max(1, min(wl.BH, budget // per_slice_fma)))
+        idx = np.linspace(0, wl.BH - 1, nsl).round().astype(int)
+        idx = np.unique(idx)
+        xo = {k: (v[idx] if isinstance(v, np.ndarray) else v) for k, v in x.items()}
+        t1 = time.perf_counter()
+        if wl.model == "linear":
+            Zo, Wo, nth = oracle.linear(xo["K"], xo["Q"], xo["V"], xo["eta"], xo["eta_scalar"],
+                                        xo["W0"], wl.chunk, return_threads=True)
+            refs = {"Z": Zo, "W": Wo}
+        else:
+            r = oracle.mlp(xo["K"], xo["Q"], xo["V"], xo["eta"], xo["eta_scalar"], xo["W1"],
+                           xo["b1"], xo["W2"], xo["b2"], wl.chunk, return_threads=True)
+            refs = {"Z": r[0], "W1": r[1], "W2": r[3]}
+            nth = r[5]
+        tcpu = time.perf_counter() - t1
+        cpu_tok_s = (len(idx) * wl.T / wl.H) / tcpu if wl.H > 0 else 0.0
+        # tokens/s counts a token when all H heads are done: sample heads / H
+        cpu = {"value": round(cpu_tok_s, 1), "unit": "tokens/s", "cores": int(nth),
+               "kind": "oracle",
+               "sample": "%d of %d (batch, head) slices, full T=%d, fp64 per-token primal "
+                         "loop, %.2f s" % (len(idx), wl.BH, wl.T, tcpu)}
+        o = sets[0][1]
+        errs = {}
+        for k, ref in refs.items():
+            g = o[k].float().cpu().numpy().reshape(wl.BH, -1)[idx]
+            r2 = ref.reshape(len(idx), -1)
+            den = np.maximum(np.abs(r2).max(axis=1), 1e-6)
+            errs[k] = float((np.abs(g - r2).max(axis=1) / den).max())
+        parity = {"max_rel_err": {k: float("%.3e" % v) for k, v in errs.items()},
+                  "slices_checked": int(len(idx))}
+        log("oracle: %d slices in %.2f s on %d threads; parity %s" % (
+            len(idx), tcpu, nth, parity))
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.io == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "scan": "ttt_" + wl.model, "batch": B, "heads": H,
+                   "seq_len": T, "head_dim": d, "chunk": wl.chunk, "plan": plan_name,
+                   "state_dtype": "f32", "parallelism": "single_gpu"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "head_tokens_per_s": round(B * H * T / (ms_step * 1e-3), 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

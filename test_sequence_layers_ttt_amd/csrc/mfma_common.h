@@ -1,0 +1,94 @@
+// gfx950 matrix-core helpers shared by the MFMA kernels.
+//
+// Register layouts of the 16x16 MFMA forms used here (wave64, lane l, lane
+// group g = l / 16, c = l % 16):
+//   A operand (16 x K): lane l holds row c, K-slots of group g;
+//   B operand (K x 16): lane l holds column c, K-slots of group g;
+//   C/D       (16x16) : lane l holds rows 4g + i (i = 0..3) of column c.
+// Only the pairing of A-slot (g, j) with B-slot (g, j) matters for a product,
+// so each kernel is free to choose which contraction index sits in which slot,
+// as long as both operands use the same choice.  In particular a C/D tile,
+// rounded to bf16, is directly a B operand (or, read as its transpose, an A
+// operand) of a 16x16x16 product whose contraction index is the tile's row.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+
+// D = A(16x16) B(16x16) + C, bf16 operands (4 per lane), fp32 accumulate.
+__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// D = A(16x32) B(32x16) + C, bf16 operands (8 per lane), fp32 accumulate.
+__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// two fp32 -> packed bf16x2 (hardware convert, round to nearest even)
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi)
+{
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ u32x2 pack_bf16x4(f32x4 v)
+{
+    u32x2 r;
+    r.x = pack_bf16x2(v.x, v.y);
+    r.y = pack_bf16x2(v.z, v.w);
+    return r;
+}
+
+// 8 bf16: slots 0..3 from `lo`, 4..7 from `hi`
+__device__ __forceinline__ u32x4 pack_bf16x8(f32x4 lo, f32x4 hi)
+{
+    u32x4 r;
+    r.x = pack_bf16x2(lo.x, lo.y);
+    r.y = pack_bf16x2(lo.z, lo.w);
+    r.z = pack_bf16x2(hi.x, hi.y);
+    r.w = pack_bf16x2(hi.z, hi.w);
+    return r;
+}
+
+__device__ __forceinline__ u32x2 lo_half(u32x4 v) { return u32x2{v.x, v.y}; }
+__device__ __forceinline__ u32x2 hi_half(u32x4 v) { return u32x2{v.z, v.w}; }
+
+// B operand of the 16x16 identity for a 16x16x16 product (slot (g, j) is
+// contraction index 4g + j): multiplying a bf16 A operand by it moves the
+// operand's 16x16 tile into C/D layout exactly (products by 1 and 0).
+__device__ __forceinline__ u32x2 identity_b16(int lane)
+{
+    const int c = lane & 15, g = lane >> 4;
+    const unsigned one = 0x3F80u;   // bf16 1.0
+    unsigned e0 = (4 * g + 0 == c) ? one : 0u;
+    unsigned e1 = (4 * g + 1 == c) ? one : 0u;
+    unsigned e2 = (4 * g + 2 == c) ? one : 0u;
+    unsigned e3 = (4 * g + 3 == c) ? one : 0u;
+    return u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+}
+
+// Workgroup index -> (unit, part) so that the `parts` workgroups of one unit run
+// on the same XCD (workgroups are handed to the 8 XCDs round-robin), sharing
+// that XCD's L2 for the unit's common inputs.  Grid = round_up(units, 8) * parts.
+__device__ __forceinline__ void xcd_unit_part(int bid, int parts, int& unit, int& part)
+{
+    const int xcd = bid & 7, rest = bid >> 3;
+    part = rest % parts;
+    unit = (rest / parts) * 8 + xcd;
+}
+
+}  // namespace ttt
