@@ -8,7 +8,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/ttt.h"
+#include "ttt.h"
 #include "launch.h"
 
 using namespace ttt;

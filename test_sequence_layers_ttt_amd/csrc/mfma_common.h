@@ -25,10 +25,15 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 // D = A(16x16) B(16x16) + C, bf16 operands (4 per lane), fp32 accumulate.
+// Issued as the 16x16x32 form with the upper four slots of both operands zero:
+// with this toolchain the 16x16x16 bf16 form returned stale accumulator values
+// under some instruction schedules (seen with d = 128 kernels), while the
+// 16x16x32 form was exact in every schedule tested.  The zero slots add nothing.
 __device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c)
 {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                    __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+    const u32x4 a8 = {a.x, a.y, 0u, 0u}, b8 = {b.x, b.y, 0u, 0u};
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a8),
+                                                  __builtin_bit_cast(bf16x8, b8), c, 0, 0, 0);
 }
 
 // D = A(16x32) B(32x16) + C, bf16 operands (8 per lane), fp32 accumulate.

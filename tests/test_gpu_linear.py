@@ -54,9 +54,10 @@ def test_small_shapes(dev, plan, d, chunk, io):
     check_linear(wl, seed, dev, plan)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("T,chunk", [(1, 16), (5, 16), (16, 16), (17, 16), (300, 64), (130, 128)])
-def test_edge_lengths(dev, T, chunk):
-    wl, seed = small(64, chunk, "bf16", per_token=True, T=T)
+def test_edge_lengths(dev, T, chunk, d):
+    wl, seed = small(d, chunk, "bf16", per_token=True, T=T)
     check_linear(wl, seed, dev, ttt.PLAN_AUTO)
 
 
