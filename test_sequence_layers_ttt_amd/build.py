@@ -20,8 +20,11 @@ INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
+# -amdgpu-mfma-vgpr-form: matrix-core results land in ordinary VGPRs, so no
+# accumulator-register copies are needed between products and vector ALU work.
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-x", "hip",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wall", "-Wno-unused-function", "-I", CSRC, "-I", INCLUDE]
 
 

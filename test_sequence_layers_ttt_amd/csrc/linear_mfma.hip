@@ -29,6 +29,8 @@
 //   Z^T    = W Q^T + F^T... :  A = W rows, B = Q rows, then A = F read as
 //            (E diag(-eta)) rows, B = S^T; lane (t, g) ends with Z[t][4g..4g+3].
 // No LDS, no barriers, no atomics.
+#include <stdint.h>
+
 #include "device_common.h"
 #include "launch.h"
 #include "mfma_common.h"
@@ -38,46 +40,77 @@ namespace {
 
 constexpr int kStep = 16;
 
+// eta modes: none (scalar for every token), per-token scalar loads, per-token
+// 16-byte loads (every sub-tile full and the eta rows 16-byte aligned)
+enum { kEtaScalar = 0, kEtaToken = 1, kEtaToken4 = 2 };
+
 template <int D>
 struct Tile {
     u32x4 k[D / 32];   // K row (lane = token), 16-byte pieces at 32m + 8g
     u32x4 q[D / 32];   // Q row, same pieces
     u32x2 v;           // V[token][out0 + 4g .. +3]
-    f32x4 eta;         // eta of tokens 4g .. 4g+3 (C/D rows)
+    f32x4 eta;         // eta of tokens 4g .. 4g+3 (C/D rows), raw
     int n;             // valid tokens (0 = past the end)
 };
 
-template <int D>
+// Loads a sub-tile exactly as stored.  Rows past the sub-tile's last valid token
+// re-read a valid row of the same slice (addresses stay in bounds); they are
+// neutralised later by giving them eta = 0, so no select ever touches the
+// loaded registers here (a select on load results would force the wait for the
+// load at the point of the select and stall the prefetch pipeline).
+template <int D, int ETA, bool FULL>
 __device__ __forceinline__ void load_tile(Tile<D>& t, const uint16_t* __restrict__ K,
                                           const uint16_t* __restrict__ Q,
                                           const uint16_t* __restrict__ V,
-                                          const float* __restrict__ eta, float eta_scalar,
+                                          const float* __restrict__ eta,
                                           size_t tok0, int s0, int n, int out0, int lane)
 {
     const int c = lane & 15, g = lane >> 4;
     t.n = n;
-    const bool live = c < n;
-    const size_t row = (tok0 + s0 + (live ? c : 0)) * D;
+    const size_t row = (tok0 + s0 + (FULL || c < n ? c : 0)) * D;
 #pragma unroll
     for (int m = 0; m < D / 32; ++m) {
-        u32x4 kk = *(const u32x4*)(K + row + 32 * m + 8 * g);
-        u32x4 qq = *(const u32x4*)(Q + row + 32 * m + 8 * g);
-        t.k[m] = live ? kk : u32x4{0, 0, 0, 0};
-        t.q[m] = live ? qq : u32x4{0, 0, 0, 0};
+        t.k[m] = *(const u32x4*)(K + row + 32 * m + 8 * g);
+        t.q[m] = *(const u32x4*)(Q + row + 32 * m + 8 * g);
     }
-    u32x2 vv = *(const u32x2*)(V + row + out0 + 4 * g);
-    t.v = live ? vv : u32x2{0, 0};
-    float e[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int s = 4 * g + i;
-        float x = eta ? eta[tok0 + s0 + (s < n ? s : 0)] : eta_scalar;
-        e[i] = s < n ? x : 0.f;
+    t.v = *(const u32x2*)(V + row + out0 + 4 * g);
+    if (ETA == kEtaToken4) {
+        t.eta = *(const f32x4*)(eta + tok0 + s0 + 4 * g);
+    } else if (ETA == kEtaToken) {
+        const float* e = eta + tok0 + s0;
+        t.eta.x = e[FULL || 4 * g + 0 < n ? 4 * g + 0 : 0];
+        t.eta.y = e[FULL || 4 * g + 1 < n ? 4 * g + 1 : 0];
+        t.eta.z = e[FULL || 4 * g + 2 < n ? 4 * g + 2 : 0];
+        t.eta.w = e[FULL || 4 * g + 3 < n ? 4 * g + 3 : 0];
     }
-    t.eta = f32x4{e[0], e[1], e[2], e[3]};
 }
 
-template <int D, int PF>
+// K of one sub-tile, re-laid out in LDS as d/16 row-major 16 x 16 bf16 blocks
+// (block jb holds K[token][pi(jb, 0..15)], 512 bytes), then read back with the
+// gfx950 transpose read: in each 16-lane group, lanes 4r..4r+3 supply row r
+// (4 elements each) and lane i receives element i of rows 0..3.  Reading block
+// jb at (8 * lane) therefore gives lane (i, g) the four tokens 4g..4g+3 of input
+// feature pi(jb, i): the A operand of the state update, already in bf16.
+template <int D>
+__device__ __forceinline__ void transpose_k(u32x2 (&kt)[D / 16], const Tile<D>& t, u32x2* lds,
+                                            int lane)
+{
+    const int c = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+        lds[(2 * m) * 64 + 4 * c + g] = lo_half(t.k[m]);
+        lds[(2 * m + 1) * 64 + 4 * c + g] = hi_half(t.k[m]);
+    }
+    asm volatile("" ::: "memory");   // keep the reads after the writes (one wave: LDS is in order)
+#pragma unroll
+    for (int jb = 0; jb < D / 16; ++jb) {
+        auto p = (__attribute__((address_space(3))) s16x4*)(lds + jb * 64 + lane);
+        kt[jb] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+    }
+    asm volatile("" ::: "memory");
+}
+
+template <int D, int PF, int ETA, bool FULL, bool MULTI>
 __global__ __launch_bounds__(64) void linear_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
@@ -85,6 +118,8 @@ __global__ __launch_bounds__(64) void linear_mfma_kernel(
 {
     constexpr int NB = D / 16;
     constexpr int NM = D / 32;
+    __shared__ u32x2 lds_kt[NB * 64];
+
     const int lane = threadIdx.x;
     const int c = lane & 15, g = lane >> 4;
     int slice, ob;
@@ -107,16 +142,20 @@ __global__ __launch_bounds__(64) void linear_mfma_kernel(
 
     const int step = chunk < kStep ? chunk : kStep;
     const int ntiles = (T + step - 1) / step;
+    const int tiles_per_chunk = chunk / step;   // 1 when chunk <= 16
 
     Tile<D> buf[PF];
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
         const int s0 = p * step;
         const int n = s0 < T ? min(step, T - s0) : 0;
-        load_tile<D>(buf[p], K, Q, V, eta, eta_scalar, tok0, n > 0 ? s0 : 0, n, out0, lane);
+        load_tile<D, ETA, FULL>(buf[p], K, Q, V, eta, tok0, n > 0 ? s0 : 0, n, out0, lane);
     }
+    u32x2 kt[NB];   // transposed K of the current sub-tile
+    transpose_k<D>(kt, buf[0], lds_kt, lane);
 
     u32x4 Wc[NM];   // bf16 chunk-start state (operand of E)
+    int in_chunk = 0;
     for (int tau0 = 0; tau0 < ntiles; tau0 += PF) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
@@ -126,25 +165,39 @@ __global__ __launch_bounds__(64) void linear_mfma_kernel(
             {
                 const int s0 = (tau + PF) * step;
                 const int n = s0 < T ? min(step, T - s0) : 0;
-                load_tile<D>(buf[p], K, Q, V, eta, eta_scalar, tok0, n > 0 ? s0 : 0, n, out0,
-                             lane);
+                load_tile<D, ETA, FULL>(buf[p], K, Q, V, eta, tok0, n > 0 ? s0 : 0, n, out0,
+                                        lane);
             }
             const int s0 = tau * step;
+            // eta of padding tokens (4g + i >= n) is zero: they then add nothing
+            // to E diag(eta) K^T or to the E diag(eta) S term of Z
+            f32x4 et = ETA == kEtaScalar ? f32x4{eta_scalar, eta_scalar, eta_scalar, eta_scalar}
+                                         : cur.eta;
+            if (!FULL) {
+                et.x = (4 * g + 0 < cur.n) ? et.x : 0.f;
+                et.y = (4 * g + 1 < cur.n) ? et.y : 0.f;
+                et.z = (4 * g + 2 < cur.n) ? et.z : 0.f;
+                et.w = (4 * g + 3 < cur.n) ? et.w : 0.f;
+            }
             // running state in bf16 (operand of W Q, and of E at a chunk start)
             u32x4 Mf[NM];
 #pragma unroll
             for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
-            if (s0 % chunk == 0) {
+            if (!MULTI || in_chunk == 0) {
 #pragma unroll
                 for (int m = 0; m < NM; ++m) Wc[m] = Mf[m];
             }
+            if (MULTI) in_chunk = (in_chunk + 1 == tiles_per_chunk) ? 0 : in_chunk + 1;
             // E^T = K^T W_c^T - V^T
-            u32x2 vneg = cur.v ^ u32x2{0x80008000u, 0x80008000u};
+            const u32x2 vneg = cur.v ^ u32x2{0x80008000u, 0x80008000u};
             f32x4 Et = mfma16(vneg, I16, f32x4{0, 0, 0, 0});
 #pragma unroll
             for (int m = 0; m < NM; ++m) Et = mfma32(cur.k[m], Wc[m], Et);
             // F = -diag(eta) E^T  (bf16)
-            const u32x2 F = pack_bf16x4(-cur.eta * Et);
+            const u32x2 F = pack_bf16x4(-et * Et);
+            // M += K F, block by block (contraction over the sub-tile's tokens)
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) M[jb] = mfma16(kt[jb], F, M[jb]);
             // S^T = K^T Q with the inclusive causal mask s <= t
             f32x4 St = {0, 0, 0, 0};
 #pragma unroll
@@ -155,23 +208,17 @@ __global__ __launch_bounds__(64) void linear_mfma_kernel(
             Sm.z = (4 * g + 2 <= c) ? St.z : 0.f;
             Sm.w = (4 * g + 3 <= c) ? St.w : 0.f;
             const u32x2 Sb = pack_bf16x4(Sm);
-            // Z^T = M Q^T - (E diag(eta)) S
+            // Z^T = M Q^T - (E diag(eta)) S   (M as it was at the sub-tile start)
             f32x4 Zt = {0, 0, 0, 0};
 #pragma unroll
             for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[m], cur.q[m], Zt);
             Zt = mfma16(F, Sb, Zt);
-            if (c < cur.n) {
-                u32x2 zb = pack_bf16x4(Zt);
+            if (FULL || c < cur.n) {
+                const u32x2 zb = pack_bf16x4(Zt);
                 *(u32x2*)(Z + (tok0 + s0 + c) * D + out0 + 4 * g) = zb;
             }
-            // M += K F  (tile by tile; K transposed by the identity product)
-#pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                f32x4 t0 = mfma16(lo_half(cur.k[m]), I16, f32x4{0, 0, 0, 0});
-                f32x4 t1 = mfma16(hi_half(cur.k[m]), I16, f32x4{0, 0, 0, 0});
-                M[2 * m] = mfma16(pack_bf16x4(t0), F, M[2 * m]);
-                M[2 * m + 1] = mfma16(pack_bf16x4(t1), F, M[2 * m + 1]);
-            }
+            // transposed K of the next sub-tile (its loads were issued PF-1 sub-tiles ago)
+            if (tau + 1 < ntiles) transpose_k<D>(kt, buf[(p + 1) % PF], lds_kt, lane);
         }
     }
 
@@ -183,15 +230,40 @@ __global__ __launch_bounds__(64) void linear_mfma_kernel(
     }
 }
 
-template <int D>
-hipError_t launch_d(const LinearArgs& a, hipStream_t s)
+template <int D, int ETA, bool FULL>
+void launch_cfg(const LinearArgs& a, hipStream_t s)
 {
     constexpr int PF = 4;
     const int units = (a.BH + 7) / 8 * 8;
     dim3 grid((unsigned)(units * (D / 16))), block(64);
-    hipLaunchKernelGGL((linear_mfma_kernel<D, PF>), grid, block, 0, s, (const uint16_t*)a.K,
-                       (const uint16_t*)a.Q, (const uint16_t*)a.V, a.eta, a.eta_scalar, a.W0,
-                       (uint16_t*)a.Z, a.W_out, a.BH, a.T, a.chunk);
+    // MULTI: a chunk spans several 16-token sub-tiles (E keeps the frozen W_c)
+    if (a.chunk > kStep)
+        hipLaunchKernelGGL((linear_mfma_kernel<D, PF, ETA, FULL, true>), grid, block, 0, s,
+                           (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V,
+                           a.eta, a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.BH, a.T,
+                           a.chunk);
+    else
+        hipLaunchKernelGGL((linear_mfma_kernel<D, PF, ETA, FULL, false>), grid, block, 0, s,
+                           (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V,
+                           a.eta, a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.BH, a.T,
+                           a.chunk);
+}
+
+template <int D>
+hipError_t launch_d(const LinearArgs& a, hipStream_t s)
+{
+    // every sub-tile holds 16 tokens: no padding logic at all
+    const bool full = a.chunk % kStep == 0 && a.T % kStep == 0;
+    const bool eta4 = a.eta && full && (reinterpret_cast<uintptr_t>(a.eta) % 16 == 0) &&
+                      a.T % 4 == 0;
+    if (full) {
+        if (!a.eta) launch_cfg<D, kEtaScalar, true>(a, s);
+        else if (eta4) launch_cfg<D, kEtaToken4, true>(a, s);
+        else launch_cfg<D, kEtaToken, true>(a, s);
+    } else {
+        if (!a.eta) launch_cfg<D, kEtaScalar, false>(a, s);
+        else launch_cfg<D, kEtaToken, false>(a, s);
+    }
     return hipGetLastError();
 }
 
