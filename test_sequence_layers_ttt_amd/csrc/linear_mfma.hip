@@ -110,20 +110,25 @@ __device__ __forceinline__ void transpose_k(u32x2 (&kt)[D / 16], const Tile<D>& 
     asm volatile("" ::: "memory");
 }
 
-template <int D, int PF, int ETA, bool FULL, bool MULTI>
-__global__ __launch_bounds__(64) void linear_mfma_kernel(
+template <int D, int PF, int WPB, int ETA, bool FULL, bool MULTI>
+__global__ __launch_bounds__(64 * WPB) void linear_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
     const float* W0, uint16_t* __restrict__ Z, float* W_out, int BH, int T, int chunk)
 {
     constexpr int NB = D / 16;
     constexpr int NM = D / 32;
-    __shared__ u32x2 lds_kt[NB * 64];
+    __shared__ u32x2 lds_all[WPB * NB * 64];
 
-    const int lane = threadIdx.x;
+    // WPB waves per workgroup own WPB consecutive 16-row slices of one head
+    // (a workgroup's waves sit on distinct SIMDs of one CU and share its L1)
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int c = lane & 15, g = lane >> 4;
-    int slice, ob;
-    xcd_unit_part(blockIdx.x, NB, slice, ob);
+    u32x2* lds_kt = lds_all + wave * NB * 64;
+    int slice, bpart;
+    xcd_unit_part(blockIdx.x, NB / WPB, slice, bpart);
+    const int ob = bpart * WPB + wave;
     if (slice >= BH) return;
     const int out0 = ob * 16;
     const size_t tok0 = (size_t)slice * T;
@@ -230,23 +235,182 @@ __global__ __launch_bounds__(64) void linear_mfma_kernel(
     }
 }
 
-template <int D, int ETA, bool FULL>
+// Chunks of at most 16 tokens: every sub-tile is a chunk and the state feeds the
+// next chunk's error directly.  The serial dependency W_c -> E_c -> W_{c+1} is cut
+// short with
+//     E_{c+1} = K_{c+1} W_{c+1}^T - V_{c+1}
+//             = [K_{c+1} W_c^T - V_{c+1}] + (K_{c+1} K_c^T) F_c,   F_c = -diag(eta_c) E_c,
+// (token-row layout; W_{c+1} = W_c + F_c^T K_c).  The bracket needs only the older
+// state and the Gram matrix K_{c+1} K_c^T needs no state at all, so after F_c only
+// one product stands between two chunks; the state update itself runs beside it.
+template <int D, int PF, int WPB, int ETA, bool FULL>
+__global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
+    const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
+    const float* W0, uint16_t* __restrict__ Z, float* W_out, int BH, int T, int chunk)
+{
+    constexpr int NB = D / 16;
+    constexpr int NM = D / 32;
+    static_assert(PF >= 2, "the next tile must be resident");
+    __shared__ u32x2 lds_all[WPB * NB * 64];
+
+    // WPB waves per workgroup own WPB consecutive 16-row slices of one head
+    // (a workgroup's waves sit on distinct SIMDs of one CU and share its L1)
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 15, g = lane >> 4;
+    u32x2* lds_kt = lds_all + wave * NB * 64;
+    int slice, bpart;
+    xcd_unit_part(blockIdx.x, NB / WPB, slice, bpart);
+    const int ob = bpart * WPB + wave;
+    if (slice >= BH) return;
+    const int out0 = ob * 16;
+    const size_t tok0 = (size_t)slice * T;
+    const int step = chunk;                    // <= 16
+    const int ntiles = (T + step - 1) / step;
+
+    f32x4 M[NB];
+    {
+        const float* w = W0 + (size_t)slice * D * D + (size_t)(out0 + c) * D;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            M[2 * m] = *(const f32x4*)(w + 32 * m + 8 * g);
+            M[2 * m + 1] = *(const f32x4*)(w + 32 * m + 8 * g + 4);
+        }
+    }
+    const u32x2 I16 = identity_b16(lane);
+
+    Tile<D> buf[PF];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        const int s0 = p * step;
+        const int n = s0 < T ? min(step, T - s0) : 0;
+        load_tile<D, ETA, FULL>(buf[p], K, Q, V, eta, tok0, n > 0 ? s0 : 0, n, out0, lane);
+    }
+
+    // prologue: E_0 = K_0 W_0^T - V_0 directly
+    u32x4 Mf[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
+    f32x4 Et;
+    {
+        const u32x2 vneg = buf[0].v ^ u32x2{0x80008000u, 0x80008000u};
+        Et = mfma16(vneg, I16, f32x4{0, 0, 0, 0});
+#pragma unroll
+        for (int m = 0; m < NM; ++m) Et = mfma32(buf[0].k[m], Mf[m], Et);
+    }
+    u32x2 kt[NB];
+    transpose_k<D>(kt, buf[0], lds_kt, lane);
+
+    // One chunk.  Work for the next chunk (Gram term, bracket, transposed K, bf16
+    // state) is done unconditionally: after the last chunk the next tile is a
+    // valid re-read of this slice and its results are simply unused, so the
+    // steady-state body has no branches for the scheduler to stop at.
+    auto chunk_step = [&](const Tile<D>& cur, const Tile<D>& nxt, int tau) {
+        const int s0 = tau * step;
+        f32x4 et = ETA == kEtaScalar ? f32x4{eta_scalar, eta_scalar, eta_scalar, eta_scalar}
+                                     : cur.eta;
+        if (!FULL) {
+            et.x = (4 * g + 0 < cur.n) ? et.x : 0.f;
+            et.y = (4 * g + 1 < cur.n) ? et.y : 0.f;
+            et.z = (4 * g + 2 < cur.n) ? et.z : 0.f;
+            et.w = (4 * g + 3 < cur.n) ? et.w : 0.f;
+        }
+        // F_c = -diag(eta) E_c (bf16): the only value the next chunk waits for
+        const u32x2 F = pack_bf16x4(-et * Et);
+        // E_{c+1} = K_{c+1} W_c^T + [-V_{c+1} | G_c] [I ; F_c]
+        {
+            f32x4 Gt = {0, 0, 0, 0};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) Gt = mfma32(cur.k[m], nxt.k[m], Gt);
+            const u32x2 G = pack_bf16x4(Gt);   // A operand of K_{c+1} K_c^T
+            f32x4 P = {0, 0, 0, 0};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) P = mfma32(nxt.k[m], Mf[m], P);
+            const u32x2 vneg = nxt.v ^ u32x2{0x80008000u, 0x80008000u};
+            Et = mfma32(u32x4{vneg.x, vneg.y, G.x, G.y}, u32x4{I16.x, I16.y, F.x, F.y}, P);
+        }
+        // W_{c+1} = W_c + F_c^T K_c, block by block
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) M[jb] = mfma16(kt[jb], F, M[jb]);
+        // Z_c = Q_c W_c^T - causal (eta-weighted) scores times E_c
+        f32x4 St = {0, 0, 0, 0};
+#pragma unroll
+        for (int m = 0; m < NM; ++m) St = mfma32(cur.k[m], cur.q[m], St);
+        f32x4 Sm;
+        Sm.x = (4 * g + 0 <= c) ? St.x : 0.f;
+        Sm.y = (4 * g + 1 <= c) ? St.y : 0.f;
+        Sm.z = (4 * g + 2 <= c) ? St.z : 0.f;
+        Sm.w = (4 * g + 3 <= c) ? St.w : 0.f;
+        const u32x2 Sb = pack_bf16x4(Sm);
+        f32x4 Zt = {0, 0, 0, 0};
+#pragma unroll
+        for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[m], cur.q[m], Zt);
+        Zt = mfma16(F, Sb, Zt);
+        if (FULL || c < cur.n) {
+            const u32x2 zb = pack_bf16x4(Zt);
+            *(u32x2*)(Z + (tok0 + s0 + c) * D + out0 + 4 * g) = zb;
+        }
+        transpose_k<D>(kt, nxt, lds_kt, lane);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
+    };
+    auto refill = [&](Tile<D>& slot, int tau) {
+        const int s1 = tau * step;
+        const int n = s1 < T ? min(step, T - s1) : 0;
+        load_tile<D, ETA, FULL>(slot, K, Q, V, eta, tok0, n > 0 ? s1 : 0, n, out0, lane);
+    };
+
+    int tau0 = 0;
+    for (; tau0 + PF <= ntiles; tau0 += PF) {
+#pragma unroll
+        for (int p = 0; p < PF; ++p) {
+            chunk_step(buf[p], buf[(p + 1) % PF], tau0 + p);
+            refill(buf[p], tau0 + p + PF);
+        }
+    }
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+        if (tau0 + p >= ntiles) break;
+        chunk_step(buf[p], buf[(p + 1) % PF], tau0 + p);
+    }
+
+    float* w = W_out + (size_t)slice * D * D + (size_t)(out0 + c) * D;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        *(f32x4*)(w + 32 * m + 8 * g) = M[2 * m];
+        *(f32x4*)(w + 32 * m + 8 * g + 4) = M[2 * m + 1];
+    }
+}
+
+template <int D, int WPB, int ETA, bool FULL>
 void launch_cfg(const LinearArgs& a, hipStream_t s)
 {
     constexpr int PF = 4;
     const int units = (a.BH + 7) / 8 * 8;
-    dim3 grid((unsigned)(units * (D / 16))), block(64);
+    dim3 grid((unsigned)(units * (D / 16) / WPB)), block(64 * WPB);
     // MULTI: a chunk spans several 16-token sub-tiles (E keeps the frozen W_c)
     if (a.chunk > kStep)
-        hipLaunchKernelGGL((linear_mfma_kernel<D, PF, ETA, FULL, true>), grid, block, 0, s,
+        hipLaunchKernelGGL((linear_mfma_kernel<D, PF, WPB, ETA, FULL, true>), grid, block, 0, s,
                            (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V,
                            a.eta, a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.BH, a.T,
                            a.chunk);
     else
-        hipLaunchKernelGGL((linear_mfma_kernel<D, PF, ETA, FULL, false>), grid, block, 0, s,
+        hipLaunchKernelGGL((linear_mfma_chain_kernel<D, PF, WPB, ETA, FULL>), grid, block, 0, s,
                            (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V,
                            a.eta, a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.BH, a.T,
                            a.chunk);
+}
+
+template <int D, int ETA, bool FULL>
+void launch_wpb(const LinearArgs& a, hipStream_t s)
+{
+    // Two slices per workgroup when that still leaves at least 128 workgroups
+    // (measured on MI355X: 8x12 heads at d = 64 run 6% faster; 1x32 heads would
+    // leave half the CUs idle and run 14% slower), else one.
+    const long blocks2 = (long)a.BH * (D / 16) / 2;
+    if (blocks2 >= 128) launch_cfg<D, 2, ETA, FULL>(a, s);
+    else launch_cfg<D, 1, ETA, FULL>(a, s);
 }
 
 template <int D>
@@ -257,12 +421,12 @@ hipError_t launch_d(const LinearArgs& a, hipStream_t s)
     const bool eta4 = a.eta && full && (reinterpret_cast<uintptr_t>(a.eta) % 16 == 0) &&
                       a.T % 4 == 0;
     if (full) {
-        if (!a.eta) launch_cfg<D, kEtaScalar, true>(a, s);
-        else if (eta4) launch_cfg<D, kEtaToken4, true>(a, s);
-        else launch_cfg<D, kEtaToken, true>(a, s);
+        if (!a.eta) launch_wpb<D, kEtaScalar, true>(a, s);
+        else if (eta4) launch_wpb<D, kEtaToken4, true>(a, s);
+        else launch_wpb<D, kEtaToken, true>(a, s);
     } else {
-        if (!a.eta) launch_cfg<D, kEtaScalar, false>(a, s);
-        else launch_cfg<D, kEtaToken, false>(a, s);
+        if (!a.eta) launch_wpb<D, kEtaScalar, false>(a, s);
+        else launch_wpb<D, kEtaToken, false>(a, s);
     }
     return hipGetLastError();
 }
