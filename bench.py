@@ -290,7 +290,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if wl.io == "bf16" else "f32",
+        # arithmetic type of the products (accumulation and state are fp32)
+        "dtype": ("f32" if wl.io == "f32" or plan_name == "generic"
+                  else ("f16" if wl.model == "mlp" else "bf16")),
         "data": "synthetic",
         "config": {"workload": wl.name, "scan": "ttt_" + wl.model, "batch": B, "heads": H,
                    "seq_len": T, "head_dim": d, "chunk": wl.chunk, "plan": plan_name,

@@ -21,6 +21,9 @@ typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
@@ -41,6 +44,51 @@ __device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// fp16 forms of the same products (same rate as bf16; 11-bit significands)
+__device__ __forceinline__ f32x4 mfma32h(u32x4 a, u32x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                 __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16h(u32x2 a, u32x2 b, f32x4 c)
+{
+    const u32x4 a8 = {a.x, a.y, 0u, 0u}, b8 = {b.x, b.y, 0u, 0u};
+    return mfma32h(a8, b8, c);
+}
+
+__device__ __forceinline__ unsigned pack_f16x2(float lo, float hi)
+{
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, f16x2));
+}
+
+__device__ __forceinline__ u32x2 pack_f16x4(f32x4 v)
+{
+    return u32x2{pack_f16x2(v.x, v.y), pack_f16x2(v.z, v.w)};
+}
+
+__device__ __forceinline__ u32x4 pack_f16x8(f32x4 lo, f32x4 hi)
+{
+    return u32x4{pack_f16x2(lo.x, lo.y), pack_f16x2(lo.z, lo.w), pack_f16x2(hi.x, hi.y),
+                 pack_f16x2(hi.z, hi.w)};
+}
+
+__device__ __forceinline__ f32x4 f16x4_to_f32(u32x2 v)
+{
+    return __builtin_convertvector(__builtin_bit_cast(f16x4, v), f32x4);
+}
+
+// 8 bf16 -> 8 fp16 (exact for magnitudes inside the fp16 normal range)
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v)
+{
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r[i] = pack_f16x2(__uint_as_float(v[i] << 16), __uint_as_float(v[i] & 0xffff0000u));
+    return r;
 }
 
 // two fp32 -> packed bf16x2 (hardware convert, round to nearest even)
@@ -84,6 +132,23 @@ __device__ __forceinline__ u32x2 identity_b16(int lane)
     unsigned e2 = (4 * g + 2 == c) ? one : 0u;
     unsigned e3 = (4 * g + 3 == c) ? one : 0u;
     return u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
+}
+
+// LDS 16x16 bf16 transpose through the gfx950 transpose read.  `x` is a tile
+// in C/D layout converted to bf16 (lane (c, g) holds X[4g..4g+3][c]); it is
+// stored as row c of a 512-byte block, and the transpose read (in each 16-lane
+// group, lanes 4r..4r+3 supply row r and lane i receives element i of rows
+// 0..3) returns lane (i, g) holding X[i][4g..4g+3]: the row index moves into the
+// lane and the column index into the slots.  One wave; the caller keeps other
+// waves off `block`.
+__device__ __forceinline__ u32x2 lds_transpose16(u32x2* block, u32x2 x, int lane)
+{
+    block[4 * (lane & 15) + (lane >> 4)] = x;
+    asm volatile("" ::: "memory");   // LDS is in order for one wave: read after the write
+    auto p = (__attribute__((address_space(3))) s16x4*)(block + lane);
+    u32x2 r = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+    asm volatile("" ::: "memory");
+    return r;
 }
 
 // Workgroup index -> (unit, part) so that the `parts` workgroups of one unit run

@@ -72,4 +72,4 @@ def test_edge_lengths(dev, T):
 
 def test_mlp_b16_4x16_full(dev):
     wl = inputs.WORKLOADS["mlp_b16_4x16"]
-    check_mlp(wl, inputs.WORKLOAD_SEEDS[wl.name], dev, ttt.PLAN_AUTO, slices=[0, 21, 42, 63])
+    check_mlp(wl, inputs.WORKLOAD_SEEDS[wl.name], dev, ttt.PLAN_AUTO)   # all 64 slices
