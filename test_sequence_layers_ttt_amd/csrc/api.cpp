@@ -40,8 +40,9 @@ int linear_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
     case TTT_PLAN_BIGCHUNK: return big ? TTT_PLAN_BIGCHUNK : TTT_ERR_UNSUPPORTED;
     default: break;
     }
-    if (mfma) return TTT_PLAN_MFMA;
+    // chunks of 128+ tokens: the three-stage path spreads the chunks over the GPU
     if (big) return TTT_PLAN_BIGCHUNK;
+    if (mfma) return TTT_PLAN_MFMA;
     return TTT_PLAN_GENERIC;
 }
 

@@ -45,11 +45,16 @@ struct MlpArgs {
 // fp32 vector-ALU dual form, any chunk, d <= 128.
 hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
 
-// bf16 MFMA path for chunk <= 16 or chunk in {32, 48, 64}; d in {32, 64, 128}.
+// bf16 MFMA path for chunk <= 16 or a multiple of 16; d in {32, 64, 128}.
 bool linear_mfma_supported(int d, int chunk, int bf16);
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
 
-// three-stage large-chunk path; chunk a multiple of 64, >= 128; d in {64, 128}; bf16.
+// The multi-sub-tile MFMA kernel run once per (batch*head, chunk) unit, each from
+// its own chunk-start state in Wstart ([BH * nseg, d, d] fp32); writes Z only.
+hipError_t launch_linear_mfma_segments(const LinearArgs& a, const float* Wstart, int nseg,
+                                       hipStream_t s);
+
+// three-stage large-chunk path; chunk a multiple of 32, >= 128; d in {64, 128}; bf16.
 bool linear_bigchunk_supported(int d, int chunk, int bf16);
 size_t linear_bigchunk_workspace(int BH, int T, int d, int chunk);
 hipError_t launch_linear_bigchunk(const LinearArgs& a, hipStream_t s);

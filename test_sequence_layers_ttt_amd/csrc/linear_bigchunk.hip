@@ -1,7 +1,277 @@
-// placeholder until the large-chunk plan lands
+// TTT-Linear forward scan for large chunks (hundreds to thousands of tokens, the
+// LaCT regime of PaperTrace "5 · TestingTime 训练与长上下文" §1.1 and §2.4), bf16
+// I/O, fp32 state, d in {64, 128}.
+//
+// With E_c = W_c K_c - V_c (tokens as columns) the chunk update
+//     W_{c+1} = W_c - E_c diag(eta) K_c^T = W_c - W_c P_c + B_c,
+//     P_c = K_c diag(eta) K_c^T,   B_c = V_c diag(eta) K_c^T,
+// is affine in W_c, and P_c, B_c (d x d) need no state.  Three kernels:
+//   A  (parallel over every chunk): P_c and B_c on the matrix cores;
+//   B  (one chain per (batch, head), split by 16 output rows): W_{c+1} from W_c,
+//      storing every chunk-start state W_c;
+//   C  (parallel over chunk x row slice): the 16-token sub-tile dual form of the
+//      chunk from its stored W_c, writing Z (launch_linear_mfma_segments).
+// Only the short d x d chain of kernel B is sequential; the long per-chunk work
+// is spread over all chunks at once.
+//
+// Workspace, in this order: P (bf16, [BH*nchunks, d, d]), B (fp32, same shape),
+// chunk-start states W_c (fp32, same shape).
+#include <stdint.h>
+
+#include "device_common.h"
 #include "launch.h"
+#include "mfma_common.h"
+
 namespace ttt {
-bool linear_bigchunk_supported(int, int, int) { return false; }
-size_t linear_bigchunk_workspace(int, int, int, int) { return 0; }
-hipError_t launch_linear_bigchunk(const LinearArgs&, hipStream_t) { return hipErrorInvalidValue; }
+namespace {
+
+constexpr int kKStep = 32;   // tokens per contraction step of kernel A
+
+// ---------------------------------------------------------------------------
+// Kernel A.  One workgroup (d/16 waves) per (batch*head, chunk).  Per 32-token
+// step the K and V rows are staged in LDS as row-major 16 x 16 bf16 blocks
+// (block (token group, feature block)); the transpose read then yields operands
+// with features in the lanes and tokens in the slots.  Wave w owns input block
+// i = w: P tiles (w, j) for all j and B tiles (w, o) for all o.
+//   P tile:  D[i][j] = sum_s (eta K)[s][i] K[s][j]   -> lane j, rows i
+//   B tile:  D[i][o] = sum_s K[s][i] (eta V)[s][o]   -> lane o, rows i
+// P is symmetric, so the tile's lane-j column is stored as row j of P; B's
+// lane-o column is row o of B = V diag(eta) K^T.
+// ---------------------------------------------------------------------------
+template <int D, bool ETA_TOKEN>
+__global__ __launch_bounds__(64 * (D / 16)) void bigchunk_gram_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const float* __restrict__ eta, float eta_scalar, uint16_t* __restrict__ Pout,
+    float* __restrict__ Bout, int T, int chunk, int nchunks)
+{
+    constexpr int NB = D / 16;
+    constexpr int NT = 64 * NB;                 // threads
+    constexpr int BLK = 64;                     // u32x2 per 16 x 16 block
+    constexpr int TILE = 2 * NB * BLK;          // u32x2 per 32-token tile
+    // [buffer][K, eta*K, eta*V][tile]
+    __shared__ u32x2 lds[2][3][TILE];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const int unit = blockIdx.x;
+    const int slice = unit / nchunks, ci = unit % nchunks;
+    const size_t t0 = (size_t)slice * T + (size_t)ci * chunk;
+    const int n = min(chunk, T - ci * chunk);
+    const int nsteps = (n + kKStep - 1) / kKStep;
+
+    // loader role: thread -> (token, 8-feature group) of the 32-token step
+    const int lt = tid / (D / 8), lq = tid % (D / 8);
+    const int lblk = ((lt >> 4) * NB + (lq >> 1)) * BLK;   // block of (token group, feature block)
+    const int loff = lblk + (lt & 15) * 4 + (lq & 1) * 2;  // row (token), half (8 features)
+
+    auto load = [&](int st, u32x4& kv, u32x4& vv, float& e) {
+        const int tok = st * kKStep + lt;
+        const bool live = tok < n;
+        const size_t r = (t0 + (live ? tok : 0)) * D + 8 * lq;
+        kv = *(const u32x4*)(K + r);
+        vv = *(const u32x4*)(V + r);
+        e = ETA_TOKEN ? eta[t0 + (live ? tok : 0)] : eta_scalar;
+        if (!live) e = 0.f;   // padding tokens contribute nothing
+        if (!live) kv = u32x4{0, 0, 0, 0};
+    };
+    auto scale = [&](u32x4 x, float e) {
+        u32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            r[i] = pack_bf16x2(__uint_as_float(x[i] << 16) * e, __uint_as_float(x[i] & 0xffff0000u) * e);
+        return r;
+    };
+    auto store = [&](int buf, u32x4 kv, u32x4 vv, float e) {
+        lds[buf][0][loff] = lo_half(kv);
+        lds[buf][0][loff + 1] = hi_half(kv);
+        const u32x4 ek = ETA_TOKEN ? scale(kv, e) : kv;
+        const u32x4 ev = ETA_TOKEN ? scale(vv, e) : vv;
+        lds[buf][1][loff] = lo_half(ek);
+        lds[buf][1][loff + 1] = hi_half(ek);
+        lds[buf][2][loff] = lo_half(ev);
+        lds[buf][2][loff + 1] = hi_half(ev);
+    };
+    // x32 operand of feature block `fb` from tile `which`: slots 0..3 = tokens
+    // 4g..4g+3, slots 4..7 = tokens 16+4g..16+4g+3
+    auto operand = [&](int buf, int which, int fb) {
+        auto p0 = (__attribute__((address_space(3))) s16x4*)(&lds[buf][which][fb * BLK] + lane);
+        auto p1 = (__attribute__((address_space(3))) s16x4*)(&lds[buf][which][(NB + fb) * BLK] + lane);
+        const u32x2 a = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0));
+        const u32x2 b = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1));
+        return u32x4{a.x, a.y, b.x, b.y};
+    };
+
+    f32x4 Pacc[NB], Bacc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) Pacc[j] = Bacc[j] = f32x4{0, 0, 0, 0};
+
+    u32x4 kv, vv;
+    float e;
+    load(0, kv, vv, e);
+    store(0, kv, vv, e);
+    __syncthreads();
+    for (int st = 0; st < nsteps; ++st) {
+        const int buf = st & 1;
+        const bool next = st + 1 < nsteps;
+        if (next) load(st + 1, kv, vv, e);
+        const u32x4 aK = operand(buf, 1, w);    // (eta K)^T, input block w
+        const u32x4 aKp = operand(buf, 0, w);   // K^T, input block w
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const u32x4 bK = operand(buf, 0, j);
+            const u32x4 bV = operand(buf, 2, j);
+            Pacc[j] = mfma32(aK, bK, Pacc[j]);
+            Bacc[j] = mfma32(aKp, bV, Bacc[j]);
+        }
+        if (next) store(buf ^ 1, kv, vv, e);
+        __syncthreads();
+    }
+
+    const float sc = ETA_TOKEN ? 1.f : eta_scalar;
+    uint16_t* P = Pout + (size_t)unit * D * D;
+    float* B = Bout + (size_t)unit * D * D;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        // lane (j', g): rows i = 16w + 4g + r of column 16j + j'
+        *(u32x2*)(P + (size_t)(16 * j + c) * D + 16 * w + 4 * g) = pack_bf16x4(Pacc[j] * sc);
+        *(f32x4*)(B + (size_t)(16 * j + c) * D + 16 * w + 4 * g) = Bacc[j] * sc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel B.  One wave per (batch*head, 16 output rows): the state rows live in
+// fp32 C/D tiles as in the sub-tile kernels (lane = output row o, values = input
+// features pi(jb, 4g + r)).  Per chunk: store W_c, then
+//   W_{c+1}^T tile jb = W_c^T tile jb + B_c^T tile jb + (-P_c)(rows pi(jb, .)) W_c^T,
+// with -P_c as the A operand (rows of P, 16-byte loads) and W_c in bf16 as B.
+// The next chunk's P and B are loaded while the current one is applied.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void bigchunk_chain_kernel(
+    const float* W0, const uint16_t* __restrict__ P, const float* __restrict__ Bm,
+    float* __restrict__ Wc, float* W_out, int BH, int nchunks)
+{
+    constexpr int NB = D / 16;
+    constexpr int NM = D / 32;
+    const int lane = threadIdx.x;
+    const int c = lane & 15, g = lane >> 4;
+    int slice, ob;
+    xcd_unit_part(blockIdx.x, NB, slice, ob);
+    if (slice >= BH) return;
+    const int out0 = 16 * ob;
+
+    f32x4 M[NB];
+    {
+        const float* w = W0 + (size_t)slice * D * D + (size_t)(out0 + c) * D;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            M[2 * m] = *(const f32x4*)(w + 32 * m + 8 * g);
+            M[2 * m + 1] = *(const f32x4*)(w + 32 * m + 8 * g + 4);
+        }
+    }
+    // operands of chunk cc: rows pi(jb, c) of P_cc, and B_cc^T tiles
+    auto loadP = [&](int cc, u32x4 (&pf)[NB][NM], f32x4 (&bt)[NB]) {
+        const uint16_t* Pc = P + ((size_t)slice * nchunks + cc) * D * D;
+        const float* Bc = Bm + ((size_t)slice * nchunks + cc) * D * D + (size_t)(out0 + c) * D;
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+            const int prow = 32 * (jb >> 1) + 8 * (c >> 2) + 4 * (jb & 1) + (c & 3);   // pi(jb, c)
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+                pf[jb][m] = *(const u32x4*)(Pc + (size_t)prow * D + 32 * m + 8 * g);
+            bt[jb] = *(const f32x4*)(Bc + 32 * (jb >> 1) + 8 * g + 4 * (jb & 1));
+        }
+    };
+    u32x4 pf[NB][NM];
+    f32x4 bt[NB];
+    loadP(0, pf, bt);
+    for (int cc = 0; cc < nchunks; ++cc) {
+        float* wc = Wc + ((size_t)slice * nchunks + cc) * D * D + (size_t)(out0 + c) * D;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            *(f32x4*)(wc + 32 * m + 8 * g) = M[2 * m];
+            *(f32x4*)(wc + 32 * m + 8 * g + 4) = M[2 * m + 1];
+        }
+        u32x4 Mf[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
+        u32x4 pcur[NB][NM];
+        f32x4 bcur[NB];
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+            bcur[jb] = bt[jb];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) pcur[jb][m] = pf[jb][m] ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+        }
+        if (cc + 1 < nchunks) loadP(cc + 1, pf, bt);
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+            f32x4 acc = M[jb] + bcur[jb];
+#pragma unroll
+            for (int m = 0; m < NM; ++m) acc = mfma32(pcur[jb][m], Mf[m], acc);
+            M[jb] = acc;
+        }
+    }
+    float* w = W_out + (size_t)slice * D * D + (size_t)(out0 + c) * D;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        *(f32x4*)(w + 32 * m + 8 * g) = M[2 * m];
+        *(f32x4*)(w + 32 * m + 8 * g + 4) = M[2 * m + 1];
+    }
+}
+
+template <int D>
+hipError_t launch_d(const LinearArgs& a, hipStream_t s)
+{
+    const int nchunks = (a.T + a.chunk - 1) / a.chunk;
+    const size_t mats = (size_t)a.BH * nchunks * D * D;
+    uint16_t* P = (uint16_t*)a.workspace;
+    float* Bm = (float*)((char*)a.workspace + mats * sizeof(uint16_t));
+    float* Wc = Bm + mats;
+
+    if (a.eta)
+        hipLaunchKernelGGL((bigchunk_gram_kernel<D, true>), dim3((unsigned)(a.BH * nchunks)),
+                           dim3(64 * (D / 16)), 0, s, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                           a.eta, a.eta_scalar, P, Bm, a.T, a.chunk, nchunks);
+    else
+        hipLaunchKernelGGL((bigchunk_gram_kernel<D, false>), dim3((unsigned)(a.BH * nchunks)),
+                           dim3(64 * (D / 16)), 0, s, (const uint16_t*)a.K, (const uint16_t*)a.V,
+                           a.eta, a.eta_scalar, P, Bm, a.T, a.chunk, nchunks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    const int units = (a.BH + 7) / 8 * 8;
+    hipLaunchKernelGGL((bigchunk_chain_kernel<D>), dim3((unsigned)(units * (D / 16))), dim3(64), 0,
+                       s, a.W0, P, Bm, Wc, a.W_out, a.BH, nchunks);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    return launch_linear_mfma_segments(a, Wc, nchunks, s);
+}
+
+}  // namespace
+
+bool linear_bigchunk_supported(int d, int chunk, int bf16)
+{
+    return bf16 && (d == 64 || d == 128) && chunk >= 128 && chunk % kKStep == 0;
+}
+
+size_t linear_bigchunk_workspace(int BH, int T, int d, int chunk)
+{
+    const size_t nchunks = ((size_t)T + chunk - 1) / chunk;
+    const size_t mats = (size_t)BH * nchunks * d * d;
+    return mats * (sizeof(uint16_t) + 2 * sizeof(float));
+}
+
+hipError_t launch_linear_bigchunk(const LinearArgs& a, hipStream_t s)
+{
+    switch (a.d) {
+    case 64: return launch_d<64>(a, s);
+    case 128: return launch_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace ttt

@@ -134,3 +134,14 @@ def test_eta_zero_reads_initial_state(dev):
     assert torch.equal(W, a["W0"])
     ref = a["Q"].double().cpu() @ a["W0"].double().cpu().transpose(-1, -2)
     assert float((Z.double().cpu() - ref).abs().max()) < 1e-5
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T,chunk", [(256, 128), (300, 128), (1000, 256), (4096, 2048), (96, 160)])
+@pytest.mark.parametrize("per_token", [True, False])
+def test_large_chunk_plan(dev, d, T, chunk, per_token):
+    """Three-stage large-chunk path (per-chunk Gram products, state chain, per-chunk
+    sub-tile pass), including a ragged last chunk and a sequence shorter than a chunk."""
+    wl, seed = small(d, chunk, "bf16", per_token=per_token, T=T, B=1, H=3)
+    wl = wl.with_(eta_value=(0.1 if per_token else 1.0 / chunk))
+    check_linear(wl, seed, dev, ttt.PLAN_BIGCHUNK)
