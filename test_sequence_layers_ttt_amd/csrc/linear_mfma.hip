@@ -44,11 +44,11 @@ constexpr int kStep = 16;
 // 16-byte loads (every sub-tile full and the eta rows 16-byte aligned)
 enum { kEtaScalar = 0, kEtaToken = 1, kEtaToken4 = 2 };
 
-template <int D>
+template <int D, int RB = 1>
 struct Tile {
     u32x4 k[D / 32];   // K row (lane = token), 16-byte pieces at 32m + 8g
     u32x4 q[D / 32];   // Q row, same pieces
-    u32x2 v;           // V[token][out0 + 4g .. +3]
+    u32x2 v[RB];       // V[token][out0 + 16r + 4g .. +3] for the wave's RB row blocks
     f32x4 eta;         // eta of tokens 4g .. 4g+3 (C/D rows), raw
     int n;             // valid tokens (0 = past the end)
 };
@@ -58,8 +58,8 @@ struct Tile {
 // neutralised later by giving them eta = 0, so no select ever touches the
 // loaded registers here (a select on load results would force the wait for the
 // load at the point of the select and stall the prefetch pipeline).
-template <int D, int ETA, bool FULL>
-__device__ __forceinline__ void load_tile(Tile<D>& t, const uint16_t* __restrict__ K,
+template <int D, int ETA, bool FULL, int RB = 1>
+__device__ __forceinline__ void load_tile(Tile<D, RB>& t, const uint16_t* __restrict__ K,
                                           const uint16_t* __restrict__ Q,
                                           const uint16_t* __restrict__ V,
                                           const float* __restrict__ eta,
@@ -73,7 +73,8 @@ __device__ __forceinline__ void load_tile(Tile<D>& t, const uint16_t* __restrict
         t.k[m] = *(const u32x4*)(K + row + 32 * m + 8 * g);
         t.q[m] = *(const u32x4*)(Q + row + 32 * m + 8 * g);
     }
-    t.v = *(const u32x2*)(V + row + out0 + 4 * g);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) t.v[r] = *(const u32x2*)(V + row + out0 + 16 * r + 4 * g);
     if (ETA == kEtaToken4) {
         t.eta = *(const f32x4*)(eta + tok0 + s0 + 4 * g);
     } else if (ETA == kEtaToken) {
@@ -91,8 +92,8 @@ __device__ __forceinline__ void load_tile(Tile<D>& t, const uint16_t* __restrict
 // (4 elements each) and lane i receives element i of rows 0..3.  Reading block
 // jb at (8 * lane) therefore gives lane (i, g) the four tokens 4g..4g+3 of input
 // feature pi(jb, i): the A operand of the state update, already in bf16.
-template <int D>
-__device__ __forceinline__ void transpose_k(u32x2 (&kt)[D / 16], const Tile<D>& t, u32x2* lds,
+template <int D, int RB>
+__device__ __forceinline__ void transpose_k(u32x2 (&kt)[D / 16], const Tile<D, RB>& t, u32x2* lds,
                                             int lane)
 {
     const int c = lane & 15, g = lane >> 4;
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_kernel(
             }
             if (MULTI) in_chunk = (in_chunk + 1 == tiles_per_chunk) ? 0 : in_chunk + 1;
             // E^T = K^T W_c^T - V^T
-            const u32x2 vneg = cur.v ^ u32x2{0x80008000u, 0x80008000u};
+            const u32x2 vneg = cur.v[0] ^ u32x2{0x80008000u, 0x80008000u};
             f32x4 Et = mfma16(vneg, I16, f32x4{0, 0, 0, 0});
 #pragma unroll
             for (int m = 0; m < NM; ++m) Et = mfma32(cur.k[m], Wc[m], Et);
@@ -252,7 +253,12 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_kernel(
 // (token-row layout; W_{c+1} = W_c + F_c^T K_c).  The bracket needs only the older
 // state and the Gram matrix K_{c+1} K_c^T needs no state at all, so after F_c only
 // one product stands between two chunks; the state update itself runs beside it.
-template <int D, int PF, int WPB, int ETA, bool FULL>
+//
+// A wave owns RB consecutive 16-row blocks of the state (RB independent chains).
+// They share the K/Q loads, the K transpose, the Gram matrix and the causal
+// scores, and their chains interleave in one instruction stream, which measures
+// faster than the same chains on separate waves of one compute unit.
+template <int D, int PF, int WPB, int RB, int ETA, bool FULL>
 __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
@@ -261,52 +267,54 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
     constexpr int NB = D / 16;
     constexpr int NM = D / 32;
     static_assert(PF >= 2, "the next tile must be resident");
+    static_assert(NB % (WPB * RB) == 0, "row blocks must tile the state");
     __shared__ u32x2 lds_all[WPB * NB * 64];
 
-    // WPB waves per workgroup own WPB consecutive 16-row slices of one head
+    // WPB waves per workgroup own WPB * RB consecutive 16-row blocks of one head
     // (a workgroup's waves sit on distinct SIMDs of one CU and share its L1)
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int c = lane & 15, g = lane >> 4;
     u32x2* lds_kt = lds_all + wave * NB * 64;
     int slice, bpart;
-    xcd_unit_part(blockIdx.x, NB / WPB, slice, bpart);
-    const int ob = bpart * WPB + wave;
+    xcd_unit_part(blockIdx.x, NB / (WPB * RB), slice, bpart);
     if (slice >= BH) return;
-    const int out0 = ob * 16;
+    const int out0 = (bpart * WPB + wave) * RB * 16;
     const size_t tok0 = (size_t)slice * T;
     const int step = chunk;                    // <= 16
     const int ntiles = (T + step - 1) / step;
 
-    f32x4 M[NB];
-    {
-        const float* w = W0 + (size_t)slice * D * D + (size_t)(out0 + c) * D;
+    f32x4 M[RB][NB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const float* w = W0 + (size_t)slice * D * D + (size_t)(out0 + 16 * r + c) * D;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            M[2 * m] = *(const f32x4*)(w + 32 * m + 8 * g);
-            M[2 * m + 1] = *(const f32x4*)(w + 32 * m + 8 * g + 4);
+            M[r][2 * m] = *(const f32x4*)(w + 32 * m + 8 * g);
+            M[r][2 * m + 1] = *(const f32x4*)(w + 32 * m + 8 * g + 4);
         }
     }
     const u32x2 I16 = identity_b16(lane);
 
-    Tile<D> buf[PF];
+    Tile<D, RB> buf[PF];
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
         const int s0 = p * step;
         const int n = s0 < T ? min(step, T - s0) : 0;
-        load_tile<D, ETA, FULL>(buf[p], K, Q, V, eta, tok0, n > 0 ? s0 : 0, n, out0, lane);
+        load_tile<D, ETA, FULL, RB>(buf[p], K, Q, V, eta, tok0, n > 0 ? s0 : 0, n, out0, lane);
     }
 
     // prologue: E_0 = K_0 W_0^T - V_0 directly
-    u32x4 Mf[NM];
+    u32x4 Mf[RB][NM];
+    f32x4 Et[RB];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
-    f32x4 Et;
-    {
-        const u32x2 vneg = buf[0].v ^ u32x2{0x80008000u, 0x80008000u};
-        Et = mfma16(vneg, I16, f32x4{0, 0, 0, 0});
+    for (int r = 0; r < RB; ++r) {
 #pragma unroll
-        for (int m = 0; m < NM; ++m) Et = mfma32(buf[0].k[m], Mf[m], Et);
+        for (int m = 0; m < NM; ++m) Mf[r][m] = pack_bf16x8(M[r][2 * m], M[r][2 * m + 1]);
+        const u32x2 vneg = buf[0].v[r] ^ u32x2{0x80008000u, 0x80008000u};
+        Et[r] = mfma16(vneg, I16, f32x4{0, 0, 0, 0});
+#pragma unroll
+        for (int m = 0; m < NM; ++m) Et[r] = mfma32(buf[0].k[m], Mf[r][m], Et[r]);
     }
     u32x2 kt[NB];
     transpose_k<D>(kt, buf[0], lds_kt, lane);
@@ -315,7 +323,7 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
     // state) is done unconditionally: after the last chunk the next tile is a
     // valid re-read of this slice and its results are simply unused, so the
     // steady-state body has no branches for the scheduler to stop at.
-    auto chunk_step = [&](const Tile<D>& cur, const Tile<D>& nxt, int tau) {
+    auto chunk_step = [&](const Tile<D, RB>& cur, const Tile<D, RB>& nxt, int tau) {
         const int s0 = tau * step;
         f32x4 et = ETA == kEtaScalar ? f32x4{eta_scalar, eta_scalar, eta_scalar, eta_scalar}
                                      : cur.eta;
@@ -326,22 +334,30 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
             et.w = (4 * g + 3 < cur.n) ? et.w : 0.f;
         }
         // F_c = -diag(eta) E_c (bf16): the only value the next chunk waits for
-        const u32x2 F = pack_bf16x4(-et * Et);
+        u32x2 F[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) F[r] = pack_bf16x4(-et * Et[r]);
         // E_{c+1} = K_{c+1} W_c^T + [-V_{c+1} | G_c] [I ; F_c]
         {
             f32x4 Gt = {0, 0, 0, 0};
 #pragma unroll
             for (int m = 0; m < NM; ++m) Gt = mfma32(cur.k[m], nxt.k[m], Gt);
             const u32x2 G = pack_bf16x4(Gt);   // A operand of K_{c+1} K_c^T
-            f32x4 P = {0, 0, 0, 0};
 #pragma unroll
-            for (int m = 0; m < NM; ++m) P = mfma32(nxt.k[m], Mf[m], P);
-            const u32x2 vneg = nxt.v ^ u32x2{0x80008000u, 0x80008000u};
-            Et = mfma32(u32x4{vneg.x, vneg.y, G.x, G.y}, u32x4{I16.x, I16.y, F.x, F.y}, P);
+            for (int r = 0; r < RB; ++r) {
+                f32x4 P = {0, 0, 0, 0};
+#pragma unroll
+                for (int m = 0; m < NM; ++m) P = mfma32(nxt.k[m], Mf[r][m], P);
+                const u32x2 vneg = nxt.v[r] ^ u32x2{0x80008000u, 0x80008000u};
+                Et[r] = mfma32(u32x4{vneg.x, vneg.y, G.x, G.y}, u32x4{I16.x, I16.y, F[r].x, F[r].y},
+                               P);
+            }
         }
         // W_{c+1} = W_c + F_c^T K_c, block by block
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) M[jb] = mfma16(kt[jb], F, M[jb]);
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) M[r][jb] = mfma16(kt[jb], F[r], M[r][jb]);
         // Z_c = Q_c W_c^T - causal (eta-weighted) scores times E_c
         f32x4 St = {0, 0, 0, 0};
 #pragma unroll
@@ -352,22 +368,27 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
         Sm.z = (4 * g + 2 <= c) ? St.z : 0.f;
         Sm.w = (4 * g + 3 <= c) ? St.w : 0.f;
         const u32x2 Sb = pack_bf16x4(Sm);
-        f32x4 Zt = {0, 0, 0, 0};
 #pragma unroll
-        for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[m], cur.q[m], Zt);
-        Zt = mfma16(F, Sb, Zt);
-        if (FULL || c < cur.n) {
-            const u32x2 zb = pack_bf16x4(Zt);
-            *(u32x2*)(Z + (tok0 + s0 + c) * D + out0 + 4 * g) = zb;
+        for (int r = 0; r < RB; ++r) {
+            f32x4 Zt = {0, 0, 0, 0};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[r][m], cur.q[m], Zt);
+            Zt = mfma16(F[r], Sb, Zt);
+            if (FULL || c < cur.n) {
+                const u32x2 zb = pack_bf16x4(Zt);
+                *(u32x2*)(Z + (tok0 + s0 + c) * D + out0 + 16 * r + 4 * g) = zb;
+            }
         }
         transpose_k<D>(kt, nxt, lds_kt, lane);
 #pragma unroll
-        for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int m = 0; m < NM; ++m) Mf[r][m] = pack_bf16x8(M[r][2 * m], M[r][2 * m + 1]);
     };
-    auto refill = [&](Tile<D>& slot, int tau) {
+    auto refill = [&](Tile<D, RB>& slot, int tau) {
         const int s1 = tau * step;
         const int n = s1 < T ? min(step, T - s1) : 0;
-        load_tile<D, ETA, FULL>(slot, K, Q, V, eta, tok0, n > 0 ? s1 : 0, n, out0, lane);
+        load_tile<D, ETA, FULL, RB>(slot, K, Q, V, eta, tok0, n > 0 ? s1 : 0, n, out0, lane);
     };
 
     int tau0 = 0;
@@ -384,42 +405,71 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
         chunk_step(buf[p], buf[(p + 1) % PF], tau0 + p);
     }
 
-    float* w = W_out + (size_t)slice * D * D + (size_t)(out0 + c) * D;
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-        *(f32x4*)(w + 32 * m + 8 * g) = M[2 * m];
-        *(f32x4*)(w + 32 * m + 8 * g + 4) = M[2 * m + 1];
+    for (int r = 0; r < RB; ++r) {
+        float* w = W_out + (size_t)slice * D * D + (size_t)(out0 + 16 * r + c) * D;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            *(f32x4*)(w + 32 * m + 8 * g) = M[r][2 * m];
+            *(f32x4*)(w + 32 * m + 8 * g + 4) = M[r][2 * m + 1];
+        }
     }
 }
 
+#ifndef CHAIN_PF
+#define CHAIN_PF 8
+#endif
+#ifndef CHAIN_PF_WIDE
+#define CHAIN_PF_WIDE 4
+#endif
+#ifndef CHAIN_RB2_UNITS
+#define CHAIN_RB2_UNITS 256
+#endif
+
+// Chunks of several 16-token sub-tiles (E keeps the frozen chunk-start state).
 template <int D, int WPB, int ETA, bool FULL>
-void launch_cfg(const LinearArgs& a, hipStream_t s)
+void launch_multi(const LinearArgs& a, hipStream_t s)
 {
     constexpr int PF = 4;
     const int units = (a.BH + 7) / 8 * 8;
     dim3 grid((unsigned)(units * (D / 16) / WPB)), block(64 * WPB);
-    // MULTI: a chunk spans several 16-token sub-tiles (E keeps the frozen W_c)
-    if (a.chunk > kStep)
-        hipLaunchKernelGGL((linear_mfma_kernel<D, PF, WPB, ETA, FULL, true>), grid, block, 0, s,
-                           (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V,
-                           a.eta, a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.BH, a.T,
-                           a.chunk);
-    else
-        hipLaunchKernelGGL((linear_mfma_chain_kernel<D, PF, WPB, ETA, FULL>), grid, block, 0, s,
-                           (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V,
-                           a.eta, a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.BH, a.T,
-                           a.chunk);
+    hipLaunchKernelGGL((linear_mfma_kernel<D, PF, WPB, ETA, FULL, true>), grid, block, 0, s,
+                       (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V, a.eta,
+                       a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.BH, a.T, a.chunk);
+}
+
+template <int D, int RB, int ETA, bool FULL>
+void launch_chain(const LinearArgs& a, hipStream_t s)
+{
+    // prefetch depth: 8 chunks where the registers allow it (d = 128 keeps 4)
+    constexpr int PF = D * RB <= 64 ? CHAIN_PF : CHAIN_PF_WIDE;
+    const int units = (a.BH + 7) / 8 * 8;
+    dim3 grid((unsigned)(units * (D / 16) / RB)), block(64);
+    hipLaunchKernelGGL((linear_mfma_chain_kernel<D, PF, 1, RB, ETA, FULL>), grid, block, 0, s,
+                       (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V, a.eta,
+                       a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.BH, a.T, a.chunk);
 }
 
 template <int D, int ETA, bool FULL>
 void launch_wpb(const LinearArgs& a, hipStream_t s)
 {
-    // Two slices per workgroup when that still leaves at least 128 workgroups
-    // (measured on MI355X: 8x12 heads at d = 64 run 6% faster; 1x32 heads would
-    // leave half the CUs idle and run 14% slower), else one.
-    const long blocks2 = (long)a.BH * (D / 16) / 2;
-    if (blocks2 >= 128) launch_cfg<D, 2, ETA, FULL>(a, s);
-    else launch_cfg<D, 1, ETA, FULL>(a, s);
+    const long units = (long)a.BH * (D / 16);   // (batch*head, 16-row block) pairs
+    if (a.chunk <= kStep) {
+        // One wave per workgroup.  Measured on MI355X, a second wave on the same
+        // compute unit slows both by 1.5-2x, so once the 16-row units outnumber
+        // the 256 compute units a wave takes two of them (d <= 64).
+        if constexpr (D <= 64) {
+            if (units > CHAIN_RB2_UNITS) {
+                launch_chain<D, 2, ETA, FULL>(a, s);
+                return;
+            }
+        }
+        launch_chain<D, 1, ETA, FULL>(a, s);
+        return;
+    }
+    // Two slices per workgroup when that still leaves at least 128 workgroups.
+    if (units / 2 >= 128) launch_multi<D, 2, ETA, FULL>(a, s);
+    else launch_multi<D, 1, ETA, FULL>(a, s);
 }
 
 template <int D>
