@@ -22,12 +22,13 @@
 // One workgroup of four waves per (batch, head); wave w owns hidden units
 // 64w .. 64w+63, i.e. rows of W1 and columns of W2.  Each product keeps one
 // index in the lanes and the contracted one in the register slots (see
-// mfma_common.h), so W2, contracted over the hidden units for E and Z but over
-// the output features for D, is kept in both orientations (W2o: lanes = output
-// feature, W2u: lanes = hidden unit), and both copies take the same update.
-// Sums over all 256 hidden units (E, A^T A', W2 A') are formed as per-wave
-// partials and added through LDS; two barriers per chunk.  A, A' and E change
-// orientation through the LDS transpose read.
+// mfma_common.h).  W2 is contracted over the hidden units for E and Z but over
+// the output features for D: the fp32 state keeps it with the output feature in
+// the lanes, and D takes the LDS transpose of its fp16 tiles each chunk.  Sums
+// over all 256 hidden units (E, A^T A', W2 A') are formed as per-wave partials
+// and added through LDS; two barriers per chunk.  A, A' and E change orientation
+// through the LDS transpose read as well.  The next chunk's inputs are loaded
+// while the current one is processed.
 //
 // GELU: gelu(x) = x Phi(x), gelu'(x) = Phi(x) + x phi(x), with erf from
 // Abramowitz & Stegun, Handbook of Mathematical Functions, eq. 7.1.26
@@ -97,11 +98,20 @@ struct Lds {
     u32x2 tA2[kWaves][kUB * 64];    // A'
     u32x2 tE[kWaves][kNB * 64];     // -eta E
     u32x2 tK[kWaves][kNB * 64];     // K tile for the W1 update operand
+    u32x2 tW2[kWaves][kUB * kNB * 64];  // fp16 W2 tiles for the transpose to (u, o)
     float b2d[kWaves][kD];          // b2 update staging
     // shared partial sums (fp32, C/D layout, one f32x4 per lane)
     f32x4 Ep[kWaves][kNB][64];
     f32x4 S2p[kWaves][64];
     f32x4 Zp[kWaves][kNB][64];
+};
+
+// One chunk's inputs as loaded (bf16), one chunk ahead of their use.
+struct ChunkIn {
+    u32x4 k[kNB / 2], q[kNB / 2];   // K, Q rows (lane = token), pieces at 32m + 8g
+    u32x2 v[kNB];                   // V[token][16ob + 4g ..], loaded by wave 0 only
+    f32x4 er;                       // eta of tokens 4g + r
+    float ec;                       // eta of token c
 };
 
 template <bool FULL, bool ETA_TOKEN, bool HAS_B1, bool HAS_B2>
@@ -115,7 +125,7 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
     extern __shared__ __align__(16) unsigned char lds_raw[];
     Lds& L = *reinterpret_cast<Lds*>(lds_raw);
 
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int c = lane & 15, g = lane >> 4;
     const int slice = blockIdx.x;
@@ -127,8 +137,9 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
     // ---- state in C/D tiles ----
     // W1t[ub][ib]: lane (u, g), value r = W1[u][pi(ib, 4g + r)], u = ubase + 16ub + c
     // W2o[ob][ub]: lane (o, g), value r = W2[o][ubase + 16ub + 4g + r], o = 16ob + c
-    // W2u[ub][ob]: lane (u, g), value r = W2[16ob + 4g + r][u]
-    f32x4 W1t[kUB][kNB], W2o[kNB][kUB], W2u[kUB][kNB];
+    // (W2 with the hidden unit in the lanes, needed for D, is the LDS transpose of
+    // W2o's fp16 tiles, formed per chunk)
+    f32x4 W1t[kUB][kNB], W2o[kNB][kUB];
     f32x4 b1r;      // b1[ubase + 16ub + c] for ub = 0..3
     f32x4 b2r[kNB]; // b2[16ob + 4g + r]
 #pragma unroll
@@ -140,13 +151,8 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
             W1t[ub][2 * m + 1] = *(const f32x4*)(row + 32 * m + 8 * g + 4);
         }
 #pragma unroll
-        for (int ob = 0; ob < kNB; ++ob) {
+        for (int ob = 0; ob < kNB; ++ob)
             W2o[ob][ub] = *(const f32x4*)(W2s + (size_t)(16 * ob + c) * kH + ubase + 16 * ub + 4 * g);
-            f32x4 t;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) t[r] = W2s[(size_t)(16 * ob + 4 * g + r) * kH + ubase + 16 * ub + c];
-            W2u[ub][ob] = t;
-        }
         b1r[ub] = HAS_B1 ? b1_0[(size_t)slice * kH + ubase + 16 * ub + c] : 0.f;
     }
 #pragma unroll
@@ -156,32 +162,51 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
 
     const int step = chunk;   // <= 16
     const int nchunks = (T + step - 1) / step;
-    for (int ci = 0; ci < nchunks; ++ci) {
-        const int s0 = ci * step;
+    // Loads one chunk's inputs; chunks past the end re-read the last one (their
+    // values are never used).  Rows past a short chunk's end re-read row 0 of it;
+    // their tokens are neutralised with eta = 0 where the chunk is used.
+    auto load_in = [&](ChunkIn& t, int ci) {
+        const int cc = ci < nchunks ? ci : nchunks - 1;
+        const int s0 = cc * step;
         const int n = FULL ? 16 : min(step, T - s0);
-        const int crow = (FULL || c < n) ? c : 0;
-        const size_t row = (tok0 + s0 + crow) * kD;
-        // ---- loads: K, Q rows (lane = token), V of the output layout, eta ----
-        u32x4 Kf[kNB / 2], Qf[kNB / 2];
+        const size_t row = (tok0 + s0 + ((FULL || c < n) ? c : 0)) * kD;
 #pragma unroll
         for (int m = 0; m < kNB / 2; ++m) {
-            Kf[m] = bf16x8_to_f16x8(*(const u32x4*)(K + row + 32 * m + 8 * g));
-            Qf[m] = bf16x8_to_f16x8(*(const u32x4*)(Q + row + 32 * m + 8 * g));
+            t.k[m] = *(const u32x4*)(K + row + 32 * m + 8 * g);
+            t.q[m] = *(const u32x4*)(Q + row + 32 * m + 8 * g);
         }
-        u32x2 Vr[kNB];
+        if (w == 0) {
 #pragma unroll
-        for (int ob = 0; ob < kNB; ++ob) Vr[ob] = *(const u32x2*)(V + row + 16 * ob + 4 * g);
-        f32x4 er;    // eta of tokens 4g + r (C/D rows), zero for padding tokens
-        float ec;    // eta of this lane's token c
+            for (int ob = 0; ob < kNB; ++ob) t.v[ob] = *(const u32x2*)(V + row + 16 * ob + 4 * g);
+        } else {
+#pragma unroll
+            for (int ob = 0; ob < kNB; ++ob) t.v[ob] = u32x2{0u, 0u};
+        }
         if (ETA_TOKEN) {
             const float* e = eta + tok0 + s0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) er[r] = e[(FULL || 4 * g + r < n) ? 4 * g + r : 0];
-            ec = e[crow];
+            for (int r = 0; r < 4; ++r) t.er[r] = e[(FULL || 4 * g + r < n) ? 4 * g + r : 0];
+            t.ec = e[(FULL || c < n) ? c : 0];
         } else {
-            er = f32x4{eta_scalar, eta_scalar, eta_scalar, eta_scalar};
-            ec = eta_scalar;
+            t.er = f32x4{eta_scalar, eta_scalar, eta_scalar, eta_scalar};
+            t.ec = eta_scalar;
         }
+    };
+    ChunkIn nxt;
+    load_in(nxt, 0);
+    for (int ci = 0; ci < nchunks; ++ci) {
+        const int s0 = ci * step;
+        const int n = FULL ? 16 : min(step, T - s0);
+        const ChunkIn cur = nxt;
+        load_in(nxt, ci + 1);
+        u32x4 Kf[kNB / 2], Qf[kNB / 2];
+#pragma unroll
+        for (int m = 0; m < kNB / 2; ++m) {
+            Kf[m] = bf16x8_to_f16x8(cur.k[m]);
+            Qf[m] = bf16x8_to_f16x8(cur.q[m]);
+        }
+        f32x4 er = cur.er;   // zero for padding tokens
+        float ec = cur.ec;
         if (!FULL) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) er[r] = (4 * g + r < n) ? er[r] : 0.f;
@@ -194,6 +219,15 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
         for (int ub = 0; ub < kUB; ++ub)
 #pragma unroll
             for (int m = 0; m < kNB / 2; ++m) W1f[ub][m] = pack_f16x8(W1t[ub][2 * m], W1t[ub][2 * m + 1]);
+        u32x2 W2f[kNB][kUB];   // W2o tiles in fp16 (A operand over u, two tiles per x32)
+#pragma unroll
+        for (int ob = 0; ob < kNB; ++ob)
+#pragma unroll
+            for (int ub = 0; ub < kUB; ++ub) W2f[ob][ub] = pack_f16x4(W2o[ob][ub]);
+        auto w2pair = [&](int ob, int m) {
+            return u32x4{W2f[ob][2 * m].x, W2f[ob][2 * m].y, W2f[ob][2 * m + 1].x,
+                         W2f[ob][2 * m + 1].y};
+        };
 
         // ---- H^T (t x u) = K W1^T + b1; A = gelu(H), G = gelu'(H) ----
         f32x4 A[kUB], G[kUB];
@@ -221,10 +255,9 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
 #pragma unroll
         for (int ob = 0; ob < kNB; ++ob) {
             f32x4 e = {0, 0, 0, 0};
-            if (w == 0) e = b2r[ob] - bf16x4_to_f32(Vr[ob]);
+            if (w == 0) e = b2r[ob] - bf16x4_to_f32(cur.v[ob]);
 #pragma unroll
-            for (int m = 0; m < kUB / 2; ++m)
-                e = mfma32h(pack_f16x8(W2o[ob][2 * m], W2o[ob][2 * m + 1]), tAf[m], e);
+            for (int m = 0; m < kUB / 2; ++m) e = mfma32h(w2pair(ob, m), tAf[m], e);
             L.Ep[w][ob][lane] = e;
         }
         // ---- S1 (s x t) = K Q^T (+1), causal, scaled by -eta_s (A operand of H') ----
@@ -264,10 +297,16 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
         f32x4 db1 = {0, 0, 0, 0};
 #pragma unroll
         for (int ub = 0; ub < kUB; ++ub) {
+            // W2 with lanes = hidden unit u, slots = output features (transpose read)
+            u32x2 w2t[kNB];
+#pragma unroll
+            for (int ob = 0; ob < kNB; ++ob)
+                w2t[ob] = lds_transpose16(&L.tW2[w][(ub * kNB + ob) * 64], W2f[ob][ub], lane);
             f32x4 d = {0, 0, 0, 0};
 #pragma unroll
             for (int m = 0; m < kNB / 2; ++m)
-                d = mfma32h(Ef[m], pack_f16x8(W2u[ub][2 * m], W2u[ub][2 * m + 1]), d);
+                d = mfma32h(Ef[m], u32x4{w2t[2 * m].x, w2t[2 * m].y, w2t[2 * m + 1].x,
+                                         w2t[2 * m + 1].y}, d);
             d = d * G[ub];
             Db[ub] = pack_f16x4(d);
             const f32x4 ds = -er * d;
@@ -301,8 +340,7 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
             for (int ob = 0; ob < kNB; ++ob) {
                 f32x4 z = (w == 0) ? b2r[ob] : f32x4{0, 0, 0, 0};
 #pragma unroll
-                for (int m = 0; m < kUB / 2; ++m)
-                    z = mfma32h(pack_f16x8(W2o[ob][2 * m], W2o[ob][2 * m + 1]), tA2f[m], z);
+                for (int m = 0; m < kUB / 2; ++m) z = mfma32h(w2pair(ob, m), tA2f[m], z);
                 L.Zp[w][ob][lane] = z;
             }
         }
@@ -347,10 +385,7 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
 #pragma unroll
             for (int ob = 0; ob < kNB; ++ob)
 #pragma unroll
-                for (int ub = 0; ub < kUB; ++ub) {
-                    W2o[ob][ub] = mfma16h(Ab[ub], tE[ob], W2o[ob][ub]);
-                    W2u[ub][ob] = mfma16h(tE[ob], Ab[ub], W2u[ub][ob]);
-                }
+                for (int ub = 0; ub < kUB; ++ub) W2o[ob][ub] = mfma16h(Ab[ub], tE[ob], W2o[ob][ub]);
             if (HAS_B1) {
 #pragma unroll
                 for (int ub = 0; ub < kUB; ++ub) {
