@@ -49,11 +49,6 @@ hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
 bool linear_mfma_supported(int d, int chunk, int bf16);
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
 
-// The multi-sub-tile MFMA kernel run once per (batch*head, chunk) unit, each from
-// its own chunk-start state in Wstart ([BH * nseg, d, d] fp32); writes Z only.
-hipError_t launch_linear_mfma_segments(const LinearArgs& a, const float* Wstart, int nseg,
-                                       hipStream_t s);
-
 // three-stage large-chunk path; chunk a multiple of 32, >= 128; d in {64, 128}; bf16.
 bool linear_bigchunk_supported(int d, int chunk, int bf16);
 size_t linear_bigchunk_workspace(int BH, int T, int d, int chunk);

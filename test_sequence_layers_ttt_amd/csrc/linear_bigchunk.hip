@@ -9,14 +9,16 @@
 //   A  (parallel over every chunk): P_c and B_c on the matrix cores;
 //   B  (one chain per (batch, head), split by 16 output rows): W_{c+1} from W_c,
 //      storing every chunk-start state W_c;
-//   C  (parallel over chunk x row slice): the 16-token sub-tile dual form of the
-//      chunk from its stored W_c, writing Z (launch_linear_mfma_segments).
+//   C  (parallel over every chunk): the 16-token sub-tile dual form of the chunk
+//      from its stored W_c, writing Z.
 // Only the short d x d chain of kernel B is sequential; the long per-chunk work
 // is spread over all chunks at once.
 //
 // Workspace, in this order: P (bf16, [BH*nchunks, d, d]), B (fp32, same shape),
 // chunk-start states W_c (fp32, same shape).
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -222,6 +224,226 @@ __global__ __launch_bounds__(64) void bigchunk_chain_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel C.  One workgroup of d/16 waves per (batch*head, chunk), started from
+// the chunk's stored state W_c; wave w owns output rows 16w .. 16w+15.  The chunk
+// is walked in 16-token sub-tiles tau with the running matrix
+//     M_tau = W_c - sum_{tau' < tau} E_tau' diag(eta) K_tau'^T :
+//     E_tau = K_tau W_c^T - V_tau          (frozen chunk-start state),
+//     F_tau = -diag(eta) E_tau,
+//     Z_tau = Q_tau M_tau^T + (causal, inclusive Q_tau K_tau^T) F_tau,
+//     M_tau+1 = M_tau + F_tau^T K_tau,
+// which is the chunk's dual form with only 16 x 16 masks formed.
+//
+// Every wave needs the whole K and Q sub-tile.  They are loaded once per
+// workgroup -- each thread fetches one 16-byte granule (coalesced, through a
+// register ring eight sub-tiles deep) and stores it to a double-buffered LDS
+// tile -- and every wave reads its matrix-core operands from there: row reads
+// for K and Q (lane = token) and the gfx950 transpose read for K with the
+// feature in the lanes.  Granules are XOR-swizzled per row so that both read
+// patterns are free of bank conflicts.  One barrier per sub-tile.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int seg_swizzle(int row)
+{
+    if constexpr (D == 128) return ((row & 3) << 2) | (row >> 2);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 1) | (((row >> 3) & 1) << 1);
+}
+
+template <int D>
+struct SegTile {
+    u32x4 g[2][16 * (D / 8)];   // [K, Q][row * (D / 8) + swizzled granule]
+};
+
+// eta modes of kernel C: scalar, per-token single loads, per-token 16-byte loads
+enum { kSegEtaScalar = 0, kSegEtaToken = 1, kSegEtaToken4 = 2 };
+
+template <int D, int ETA, bool FULL>
+__global__ __launch_bounds__(4 * D) void bigchunk_seg_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
+    const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
+    const float* __restrict__ Wstart, uint16_t* __restrict__ Z, int T, int chunk, int nseg)
+{
+    constexpr int NB = D / 16;
+    constexpr int NM = D / 32;
+    constexpr int G = D / 8;    // 16-byte granules per row
+    constexpr int P = 8;        // sub-tiles in flight per thread
+    __shared__ SegTile<D> L[2];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const int slice = blockIdx.x / nseg, seg = blockIdx.x % nseg;
+    const int t0 = seg * chunk;
+    const int nc = min(chunk, T - t0);          // tokens in this chunk
+    const int ntile = (nc + 15) / 16;
+    const size_t tok0 = (size_t)slice * T + t0;
+    const int out0 = 16 * wave;
+    // token of row r of sub-tile tau, clamped into the chunk (clamped rows are
+    // re-reads whose tokens get eta = 0 and no store)
+    auto tok = [&](int tau, int r) {
+        const int tt = tau < ntile ? tau : ntile - 1;
+        const int t = 16 * tt + r;
+        return FULL ? t : (t < nc ? t : nc - 1);
+    };
+
+    // this thread's granule of each staged sub-tile: K for the first half of
+    // the workgroup, Q for the second
+    const int which = tid / (16 * G);
+    const int grow = (tid / G) & 15, ggr = tid % G;
+    const uint16_t* src = which ? Q : K;
+    const int lpos = grow * G + (ggr ^ seg_swizzle<D>(grow));
+    auto gload = [&](int tau) {
+        return *(const u32x4*)(src + (tok0 + tok(tau, grow)) * D + 8 * ggr);
+    };
+    // this lane's V (tokens c, features out0 + 4g ..) and eta (tokens 4g .. 4g+3)
+    auto vload = [&](int tau) {
+        return *(const u32x2*)(V + (tok0 + tok(tau, c)) * D + out0 + 4 * g);
+    };
+    auto eload = [&](int tau) {
+        if (ETA == kSegEtaToken4) {
+            const int tt = tau < ntile ? tau : ntile - 1;
+            return *(const f32x4*)(eta + tok0 + 16 * tt + 4 * g);
+        } else if (ETA == kSegEtaToken) {
+            f32x4 e;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) e[r] = eta[tok0 + tok(tau, 4 * g + r)];
+            return e;
+        } else {
+            return f32x4{eta_scalar, eta_scalar, eta_scalar, eta_scalar};
+        }
+    };
+
+    // chunk-start state rows of this wave: fp32 running M and bf16 copies
+    f32x4 M[NB];
+    {
+        const float* w = Wstart + ((size_t)slice * nseg + seg) * D * D + (size_t)(out0 + c) * D;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            M[2 * m] = *(const f32x4*)(w + 32 * m + 8 * g);
+            M[2 * m + 1] = *(const f32x4*)(w + 32 * m + 8 * g + 4);
+        }
+    }
+    u32x4 Wf[NM], Mf[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) Wf[m] = Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
+    const u32x2 I16 = identity_b16(lane);
+
+    u32x4 rg[P];
+    u32x2 rv[P];
+    f32x4 re[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        rg[p] = gload(p);
+        rv[p] = vload(p);
+        re[p] = eload(p);
+    }
+    L[0].g[which][lpos] = rg[0];
+    rg[0] = gload(P);
+    __syncthreads();
+
+    // one sub-tile; p = tau % P is a compile-time ring position
+    auto step = [&](int tau, auto pc) {
+        constexpr int p = decltype(pc)::value;
+        constexpr int p1 = (p + 1) % P;
+        const int sl = tau & 1;
+        // stage the next sub-tile, refill its register slot
+        if (tau + 1 < ntile) L[sl ^ 1].g[which][lpos] = rg[p1];
+        rg[p1] = gload(tau + 1 + P);
+
+        const u32x4* Kt = L[sl].g[0];
+        const u32x4* Qt = L[sl].g[1];
+        u32x4 kop[NM], qop[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            const int gi = c * G + ((4 * m + g) ^ seg_swizzle<D>(c));
+            kop[m] = Kt[gi];
+            qop[m] = Qt[gi];
+        }
+        // K with the feature in the lanes: supplying lane (r, q) of group g reads
+        // the 8 bytes K[4g + r][32m + 8q + 4h .. +3] of block jb = 2m + h
+        u32x2 kt[NB];
+        {
+            const int r = (lane >> 2) & 3, q = lane & 3;
+            const int row = 4 * g + r;
+            const u32x2* base = reinterpret_cast<const u32x2*>(Kt) + row * (2 * G);
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                const int m = jb >> 1, h = jb & 1;
+                auto pt = (__attribute__((address_space(3))) s16x4*)(
+                    base + 2 * ((4 * m + q) ^ seg_swizzle<D>(row)) + h);
+                kt[jb] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(pt));
+            }
+        }
+        const int n = FULL ? 16 : min(16, nc - 16 * tau);
+        f32x4 et = re[p];
+        if (!FULL) {
+            et.x = (4 * g + 0 < n) ? et.x : 0.f;
+            et.y = (4 * g + 1 < n) ? et.y : 0.f;
+            et.z = (4 * g + 2 < n) ? et.z : 0.f;
+            et.w = (4 * g + 3 < n) ? et.w : 0.f;
+        }
+        // E = K W_c^T - V (tokens in the rows, this wave's outputs in the lanes)
+        f32x4 Et = mfma16(rv[p] ^ u32x2{0x80008000u, 0x80008000u}, I16, f32x4{0, 0, 0, 0});
+#pragma unroll
+        for (int m = 0; m < NM; ++m) Et = mfma32(kop[m], Wf[m], Et);
+        const u32x2 F = pack_bf16x4(-et * Et);
+        // causal scores S[s][t] = k_s . q_t for s <= t
+        f32x4 St = {0, 0, 0, 0};
+#pragma unroll
+        for (int m = 0; m < NM; ++m) St = mfma32(kop[m], qop[m], St);
+        f32x4 Sm;
+        Sm.x = (4 * g + 0 <= c) ? St.x : 0.f;
+        Sm.y = (4 * g + 1 <= c) ? St.y : 0.f;
+        Sm.z = (4 * g + 2 <= c) ? St.z : 0.f;
+        Sm.w = (4 * g + 3 <= c) ? St.w : 0.f;
+        // Z = Q M^T + S^T-weighted F (outputs in the rows, tokens in the lanes)
+        f32x4 Zt = {0, 0, 0, 0};
+#pragma unroll
+        for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[m], qop[m], Zt);
+        Zt = mfma16(F, pack_bf16x4(Sm), Zt);
+        if (FULL || c < n)
+            *(u32x2*)(Z + (tok0 + 16 * tau + c) * D + out0 + 4 * g) = pack_bf16x4(Zt);
+        // M += F^T K
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) M[jb] = mfma16(kt[jb], F, M[jb]);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
+        rv[p] = vload(tau + P);
+        re[p] = eload(tau + P);
+        __syncthreads();
+    };
+
+    int tau0 = 0;
+    for (; tau0 + P <= ntile; tau0 += P) {
+        step(tau0 + 0, std::integral_constant<int, 0>{});
+        step(tau0 + 1, std::integral_constant<int, 1>{});
+        step(tau0 + 2, std::integral_constant<int, 2>{});
+        step(tau0 + 3, std::integral_constant<int, 3>{});
+        step(tau0 + 4, std::integral_constant<int, 4>{});
+        step(tau0 + 5, std::integral_constant<int, 5>{});
+        step(tau0 + 6, std::integral_constant<int, 6>{});
+        step(tau0 + 7, std::integral_constant<int, 7>{});
+    }
+    if (tau0 + 0 < ntile) step(tau0 + 0, std::integral_constant<int, 0>{});
+    if (tau0 + 1 < ntile) step(tau0 + 1, std::integral_constant<int, 1>{});
+    if (tau0 + 2 < ntile) step(tau0 + 2, std::integral_constant<int, 2>{});
+    if (tau0 + 3 < ntile) step(tau0 + 3, std::integral_constant<int, 3>{});
+    if (tau0 + 4 < ntile) step(tau0 + 4, std::integral_constant<int, 4>{});
+    if (tau0 + 5 < ntile) step(tau0 + 5, std::integral_constant<int, 5>{});
+    if (tau0 + 6 < ntile) step(tau0 + 6, std::integral_constant<int, 6>{});
+}
+
+template <int D, int ETA, bool FULL>
+void launch_seg(const LinearArgs& a, const float* Wc, int nchunks, hipStream_t s)
+{
+    hipLaunchKernelGGL((bigchunk_seg_kernel<D, ETA, FULL>), dim3((unsigned)(a.BH * nchunks)),
+                       dim3(4 * D), 0, s, (const uint16_t*)a.K, (const uint16_t*)a.Q,
+                       (const uint16_t*)a.V, a.eta, a.eta_scalar, Wc, (uint16_t*)a.Z, a.T, a.chunk,
+                       nchunks);
+}
+
 template <int D>
 hipError_t launch_d(const LinearArgs& a, hipStream_t s)
 {
@@ -248,7 +470,18 @@ hipError_t launch_d(const LinearArgs& a, hipStream_t s)
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    return launch_linear_mfma_segments(a, Wc, nchunks, s);
+    // every sub-tile full: T (and the chunk, a multiple of 32) divide into 16s
+    const bool full = a.T % 16 == 0;
+    const bool eta4 = a.eta && full && reinterpret_cast<uintptr_t>(a.eta) % 16 == 0;
+    if (full) {
+        if (!a.eta) launch_seg<D, kSegEtaScalar, true>(a, Wc, nchunks, s);
+        else if (eta4) launch_seg<D, kSegEtaToken4, true>(a, Wc, nchunks, s);
+        else launch_seg<D, kSegEtaToken, true>(a, Wc, nchunks, s);
+    } else {
+        if (!a.eta) launch_seg<D, kSegEtaScalar, false>(a, Wc, nchunks, s);
+        else launch_seg<D, kSegEtaToken, false>(a, Wc, nchunks, s);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace

@@ -111,16 +111,12 @@ __device__ __forceinline__ void transpose_k(u32x2 (&kt)[D / 16], const Tile<D, R
     asm volatile("" ::: "memory");
 }
 
-// SEG: the unit is one chunk of one (batch, head) -- tokens
-// [seg * chunk, min(T, (seg + 1) * chunk)) -- started from its own chunk-start
-// state W0 + unit * d * d (produced by the large-chunk state chain); only Z is
-// written.  Otherwise the unit is a whole (batch, head) sequence.
-template <int D, int PF, int WPB, int ETA, bool FULL, bool MULTI, bool SEG = false>
+// The unit is one (batch, head) sequence and one 16-row block of its state.
+template <int D, int PF, int WPB, int ETA, bool FULL, bool MULTI>
 __global__ __launch_bounds__(64 * WPB) void linear_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
-    const float* W0, uint16_t* __restrict__ Z, float* W_out, int BH, int T, int chunk,
-    int nseg = 1)
+    const float* W0, uint16_t* __restrict__ Z, float* W_out, int BH, int T, int chunk)
 {
     constexpr int NB = D / 16;
     constexpr int NM = D / 32;
@@ -132,20 +128,17 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_kernel(
     const int lane = threadIdx.x & 63;
     const int c = lane & 15, g = lane >> 4;
     u32x2* lds_kt = lds_all + wave * NB * 64;
-    int unit, bpart;
-    xcd_unit_part(blockIdx.x, NB / WPB, unit, bpart);
+    int slice, bpart;
+    xcd_unit_part(blockIdx.x, NB / WPB, slice, bpart);
     const int ob = bpart * WPB + wave;
-    if (unit >= BH * nseg) return;
-    const int slice = SEG ? unit / nseg : unit;
-    const int seg = SEG ? unit % nseg : 0;
+    if (slice >= BH) return;
     const int out0 = ob * 16;
-    const size_t tok0 = (size_t)slice * T + (size_t)seg * chunk;
-    if (SEG) T = min(chunk, T - seg * chunk);   // tokens of this unit
+    const size_t tok0 = (size_t)slice * T;
 
     // state rows out0 + c, columns pi(jb, 4g + i)
     f32x4 M[NB];
     {
-        const float* w = W0 + (size_t)unit * D * D + (size_t)(out0 + c) * D;
+        const float* w = W0 + (size_t)slice * D * D + (size_t)(out0 + c) * D;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             M[2 * m] = *(const f32x4*)(w + 32 * m + 8 * g);
@@ -236,7 +229,6 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_kernel(
         }
     }
 
-    if (SEG) return;
     float* w = W_out + (size_t)slice * D * D + (size_t)(out0 + c) * D;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
@@ -490,40 +482,7 @@ hipError_t launch_d(const LinearArgs& a, hipStream_t s)
     return hipGetLastError();
 }
 
-template <int D>
-hipError_t launch_seg_d(const LinearArgs& a, const float* Wstart, int nseg, hipStream_t s)
-{
-    constexpr int PF = 4, WPB = 2;
-    const int units = (a.BH * nseg + 7) / 8 * 8;
-    dim3 grid((unsigned)(units * (D / 16) / WPB)), block(64 * WPB);
-    const bool full = a.chunk % kStep == 0 && a.T % kStep == 0;
-#define TTT_SEG_LAUNCH(ETA_, FULL_)                                                            \
-    hipLaunchKernelGGL((linear_mfma_kernel<D, PF, WPB, ETA_, FULL_, true, true>), grid, block, 0, \
-                       s, (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V,      \
-                       a.eta, a.eta_scalar, Wstart, (uint16_t*)a.Z, a.W_out, a.BH, a.T, a.chunk, \
-                       nseg)
-    if (full) {
-        if (a.eta) TTT_SEG_LAUNCH(kEtaToken, true);
-        else TTT_SEG_LAUNCH(kEtaScalar, true);
-    } else {
-        if (a.eta) TTT_SEG_LAUNCH(kEtaToken, false);
-        else TTT_SEG_LAUNCH(kEtaScalar, false);
-    }
-#undef TTT_SEG_LAUNCH
-    return hipGetLastError();
-}
-
 }  // namespace
-
-hipError_t launch_linear_mfma_segments(const LinearArgs& a, const float* Wstart, int nseg,
-                                       hipStream_t s)
-{
-    switch (a.d) {
-    case 64: return launch_seg_d<64>(a, Wstart, nseg, s);
-    case 128: return launch_seg_d<128>(a, Wstart, nseg, s);
-    default: return hipErrorInvalidValue;
-    }
-}
 
 bool linear_mfma_supported(int d, int chunk, int bf16)
 {
