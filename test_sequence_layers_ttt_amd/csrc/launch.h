@@ -49,6 +49,11 @@ hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
 bool linear_mfma_supported(int d, int chunk, int bf16);
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
 
+// Chunks of exactly 16 tokens, one workgroup of d/16 waves per (batch, head)
+// sharing each chunk's K/Q tile through LDS; part of the MFMA plan.
+bool linear_coop_supported(int d, int chunk, int bf16);
+hipError_t launch_linear_coop(const LinearArgs& a, hipStream_t s);
+
 // three-stage large-chunk path; chunk a multiple of 32, >= 128; d in {64, 128}; bf16.
 bool linear_bigchunk_supported(int d, int chunk, int bf16);
 size_t linear_bigchunk_workspace(int BH, int T, int d, int chunk);

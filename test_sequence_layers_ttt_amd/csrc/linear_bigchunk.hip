@@ -243,17 +243,6 @@ __global__ __launch_bounds__(64) void bigchunk_chain_kernel(
 // feature in the lanes.  Granules are XOR-swizzled per row so that both read
 // patterns are free of bank conflicts.  One barrier per sub-tile.
 // ---------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ int seg_swizzle(int row)
-{
-    if constexpr (D == 128) return ((row & 3) << 2) | (row >> 2);
-    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 1) | (((row >> 3) & 1) << 1);
-}
-
-template <int D>
-struct SegTile {
-    u32x4 g[2][16 * (D / 8)];   // [K, Q][row * (D / 8) + swizzled granule]
-};
 
 // eta modes of kernel C: scalar, per-token single loads, per-token 16-byte loads
 enum { kSegEtaScalar = 0, kSegEtaToken = 1, kSegEtaToken4 = 2 };
@@ -268,7 +257,7 @@ __global__ __launch_bounds__(4 * D) void bigchunk_seg_kernel(
     constexpr int NM = D / 32;
     constexpr int G = D / 8;    // 16-byte granules per row
     constexpr int P = 8;        // sub-tiles in flight per thread
-    __shared__ SegTile<D> L[2];
+    __shared__ KQTile16<D> L[2];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -293,7 +282,7 @@ __global__ __launch_bounds__(4 * D) void bigchunk_seg_kernel(
     const int which = tid / (16 * G);
     const int grow = (tid / G) & 15, ggr = tid % G;
     const uint16_t* src = which ? Q : K;
-    const int lpos = grow * G + (ggr ^ seg_swizzle<D>(grow));
+    const int lpos = grow * G + (ggr ^ tile16_swizzle<D>(grow));
     auto gload = [&](int tau) {
         return *(const u32x4*)(src + (tok0 + tok(tau, grow)) * D + 8 * ggr);
     };
@@ -357,7 +346,7 @@ __global__ __launch_bounds__(4 * D) void bigchunk_seg_kernel(
         u32x4 kop[NM], qop[NM];
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            const int gi = c * G + ((4 * m + g) ^ seg_swizzle<D>(c));
+            const int gi = c * G + ((4 * m + g) ^ tile16_swizzle<D>(c));
             kop[m] = Kt[gi];
             qop[m] = Qt[gi];
         }
@@ -372,7 +361,7 @@ __global__ __launch_bounds__(4 * D) void bigchunk_seg_kernel(
             for (int jb = 0; jb < NB; ++jb) {
                 const int m = jb >> 1, h = jb & 1;
                 auto pt = (__attribute__((address_space(3))) s16x4*)(
-                    base + 2 * ((4 * m + q) ^ seg_swizzle<D>(row)) + h);
+                    base + 2 * ((4 * m + q) ^ tile16_swizzle<D>(row)) + h);
                 kt[jb] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(pt));
             }
         }

@@ -1,0 +1,269 @@
+// TTT-Linear forward scan, chunks of exactly 16 tokens, one workgroup per
+// (batch, head): d/16 waves, wave w owning state rows 16w .. 16w+15.
+//
+// Same chunk arithmetic as the single-wave chunk kernel (linear_mfma.hip): with
+// F_c = -diag(eta) E_c (token-row layout, PaperTrace "5 · TestingTime 训练与长上下文"
+// §1.1/§2.3, dual form of diosapp "Test-Time Training (TTT) guide" §3)
+//     Z_c     = Q_c W_c^T + (causal, inclusive Q_c K_c^T) F_c,
+//     W_{c+1} = W_c + F_c^T K_c,
+//     E_{c+1} = [K_{c+1} W_c^T - V_{c+1}] + (K_{c+1} K_c^T) F_c   (Gram lookahead).
+//
+// Every wave of a head needs the whole K and Q tile of each chunk.  Instead of
+// each wave fetching them (d/16 copies through the compute unit's vector-memory
+// path, which saturates once several waves share a compute unit), the workgroup
+// fetches each tile once -- one coalesced 16-byte granule per thread, through a
+// register ring eight chunks deep -- into a ring of four swizzled LDS tiles, and
+// every wave reads its operands from there (row reads; the transpose read gives K
+// with the feature in the lanes for the state update).  V and eta are loaded per
+// wave.  One barrier per chunk.
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+#include "mfma_common.h"
+
+namespace ttt {
+namespace {
+
+enum { kCoopEtaScalar = 0, kCoopEtaToken = 1, kCoopEtaToken4 = 2 };
+
+template <int D, int ETA, bool FULL>
+__global__ __launch_bounds__(4 * D) void linear_coop_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
+    const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
+    const float* W0, uint16_t* __restrict__ Z, float* W_out, int T)
+{
+    constexpr int NB = D / 16;
+    constexpr int NM = D / 32;
+    constexpr int G = D / 8;     // 16-byte granules per row
+    constexpr int P = 8;         // chunks in flight per thread
+    __shared__ KQTile16<D> L[4];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const int slice = blockIdx.x;
+    const size_t tok0 = (size_t)slice * T;
+    const int nch = (T + 15) / 16;
+    const int out0 = 16 * wave;
+    // token of row r of chunk ch, clamped into the sequence (a clamped row is a
+    // re-read; its token gets eta = 0 and no store)
+    auto tok = [&](int ch, int r) {
+        const int cc = ch < nch ? ch : nch - 1;
+        const int t = 16 * cc + r;
+        return FULL ? t : (t < T ? t : T - 1);
+    };
+
+    // this thread's granule of each staged tile: K for the first half of the
+    // workgroup, Q for the second
+    const int which = tid / (16 * G);
+    const int grow = (tid / G) & 15, ggr = tid % G;
+    const uint16_t* src = which ? Q : K;
+    const int lpos = grow * G + (ggr ^ tile16_swizzle<D>(grow));
+    auto gload = [&](int ch) {
+        return *(const u32x4*)(src + (tok0 + tok(ch, grow)) * D + 8 * ggr);
+    };
+    auto vload = [&](int ch) {
+        return *(const u32x2*)(V + (tok0 + tok(ch, c)) * D + out0 + 4 * g);
+    };
+    auto eload = [&](int ch) {
+        if (ETA == kCoopEtaToken4) {
+            const int cc = ch < nch ? ch : nch - 1;
+            return *(const f32x4*)(eta + tok0 + 16 * cc + 4 * g);
+        } else if (ETA == kCoopEtaToken) {
+            f32x4 e;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) e[r] = eta[tok0 + tok(ch, 4 * g + r)];
+            return e;
+        } else {
+            return f32x4{eta_scalar, eta_scalar, eta_scalar, eta_scalar};
+        }
+    };
+    // row operand of a staged tile: lane (c, g) gets granules 4m + g of row c
+    auto row_operand = [&](const u32x4* t, u32x4 (&op)[NM]) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) op[m] = t[c * G + ((4 * m + g) ^ tile16_swizzle<D>(c))];
+    };
+
+    f32x4 M[NB];
+    {
+        const float* w = W0 + (size_t)slice * D * D + (size_t)(out0 + c) * D;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            M[2 * m] = *(const f32x4*)(w + 32 * m + 8 * g);
+            M[2 * m + 1] = *(const f32x4*)(w + 32 * m + 8 * g + 4);
+        }
+    }
+    u32x4 Mf[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
+    const u32x2 I16 = identity_b16(lane);
+
+    u32x4 rg[P];
+    u32x2 rv[P];
+    f32x4 re[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        rg[p] = gload(p);
+        rv[p] = vload(p);
+        re[p] = eload(p);
+    }
+    L[0].g[which][lpos] = rg[0];
+    L[1].g[which][lpos] = rg[1];
+    rg[0] = gload(P);
+    rg[1] = gload(P + 1);
+    __syncthreads();
+
+    // E_0 = K_0 W_0^T - V_0 directly
+    u32x4 kc[NM];
+    row_operand(L[0].g[0], kc);
+    f32x4 Et = mfma16(rv[0] ^ u32x2{0x80008000u, 0x80008000u}, I16, f32x4{0, 0, 0, 0});
+#pragma unroll
+    for (int m = 0; m < NM; ++m) Et = mfma32(kc[m], Mf[m], Et);
+
+    // one chunk; p = ch % P is a compile-time ring position
+    auto step = [&](int ch, auto pc) {
+        constexpr int p = decltype(pc)::value;
+        // stage chunk ch + 2, refill its register slot
+        if (ch + 2 < nch) L[(ch + 2) & 3].g[which][lpos] = rg[(p + 2) % P];
+        rg[(p + 2) % P] = gload(ch + 2 + P);
+
+        const u32x4* Kc = L[ch & 3].g[0];
+        const u32x4* Qc = L[ch & 3].g[1];
+        u32x4 kn[NM], qc[NM];
+        row_operand(L[(ch + 1) & 3].g[0], kn);   // stale (unused) after the last chunk
+        row_operand(Qc, qc);
+        // K_c with the feature in the lanes (A operand of the state update)
+        u32x2 kt[NB];
+        {
+            const int r = (lane >> 2) & 3, q = lane & 3;
+            const int row = 4 * g + r;
+            const u32x2* base = reinterpret_cast<const u32x2*>(Kc) + row * (2 * G);
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                auto pt = (__attribute__((address_space(3))) s16x4*)(
+                    base + 2 * ((4 * (jb >> 1) + q) ^ tile16_swizzle<D>(row)) + (jb & 1));
+                kt[jb] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(pt));
+            }
+        }
+        f32x4 et = re[p];
+        if (!FULL) {
+            const int n = min(16, T - 16 * ch);
+            et.x = (4 * g + 0 < n) ? et.x : 0.f;
+            et.y = (4 * g + 1 < n) ? et.y : 0.f;
+            et.z = (4 * g + 2 < n) ? et.z : 0.f;
+            et.w = (4 * g + 3 < n) ? et.w : 0.f;
+        }
+        // F_c = -diag(eta) E_c: the only value the next chunk waits for
+        const u32x2 F = pack_bf16x4(-et * Et);
+        // E_{c+1} = K_{c+1} W_c^T + [-V_{c+1} | G_c] [I ; F_c]
+        {
+            f32x4 Gt = {0, 0, 0, 0};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) Gt = mfma32(kc[m], kn[m], Gt);
+            const u32x2 Gb = pack_bf16x4(Gt);
+            f32x4 Pt = {0, 0, 0, 0};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) Pt = mfma32(kn[m], Mf[m], Pt);
+            const u32x2 vneg = rv[(p + 1) % P] ^ u32x2{0x80008000u, 0x80008000u};
+            Et = mfma32(u32x4{vneg.x, vneg.y, Gb.x, Gb.y}, u32x4{I16.x, I16.y, F.x, F.y}, Pt);
+        }
+        // W_{c+1} = W_c + F_c^T K_c
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) M[jb] = mfma16(kt[jb], F, M[jb]);
+        // Z_c = Q_c W_c^T + causal scores times F_c
+        f32x4 St = {0, 0, 0, 0};
+#pragma unroll
+        for (int m = 0; m < NM; ++m) St = mfma32(kc[m], qc[m], St);
+        f32x4 Sm;
+        Sm.x = (4 * g + 0 <= c) ? St.x : 0.f;
+        Sm.y = (4 * g + 1 <= c) ? St.y : 0.f;
+        Sm.z = (4 * g + 2 <= c) ? St.z : 0.f;
+        Sm.w = (4 * g + 3 <= c) ? St.w : 0.f;
+        f32x4 Zt = {0, 0, 0, 0};
+#pragma unroll
+        for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[m], qc[m], Zt);
+        Zt = mfma16(F, pack_bf16x4(Sm), Zt);
+        if (FULL || 16 * ch + c < T)
+            *(u32x2*)(Z + (tok0 + 16 * ch + c) * D + out0 + 4 * g) = pack_bf16x4(Zt);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
+            kc[m] = kn[m];
+        }
+        rv[p] = vload(ch + P);
+        re[p] = eload(ch + P);
+        __syncthreads();
+    };
+
+    int c0 = 0;
+    for (; c0 + P <= nch; c0 += P) {
+        step(c0 + 0, std::integral_constant<int, 0>{});
+        step(c0 + 1, std::integral_constant<int, 1>{});
+        step(c0 + 2, std::integral_constant<int, 2>{});
+        step(c0 + 3, std::integral_constant<int, 3>{});
+        step(c0 + 4, std::integral_constant<int, 4>{});
+        step(c0 + 5, std::integral_constant<int, 5>{});
+        step(c0 + 6, std::integral_constant<int, 6>{});
+        step(c0 + 7, std::integral_constant<int, 7>{});
+    }
+    if (c0 + 0 < nch) step(c0 + 0, std::integral_constant<int, 0>{});
+    if (c0 + 1 < nch) step(c0 + 1, std::integral_constant<int, 1>{});
+    if (c0 + 2 < nch) step(c0 + 2, std::integral_constant<int, 2>{});
+    if (c0 + 3 < nch) step(c0 + 3, std::integral_constant<int, 3>{});
+    if (c0 + 4 < nch) step(c0 + 4, std::integral_constant<int, 4>{});
+    if (c0 + 5 < nch) step(c0 + 5, std::integral_constant<int, 5>{});
+    if (c0 + 6 < nch) step(c0 + 6, std::integral_constant<int, 6>{});
+
+    float* w = W_out + (size_t)slice * D * D + (size_t)(out0 + c) * D;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+        *(f32x4*)(w + 32 * m + 8 * g) = M[2 * m];
+        *(f32x4*)(w + 32 * m + 8 * g + 4) = M[2 * m + 1];
+    }
+}
+
+template <int D, int ETA, bool FULL>
+void launch_cfg(const LinearArgs& a, hipStream_t s)
+{
+    hipLaunchKernelGGL((linear_coop_kernel<D, ETA, FULL>), dim3((unsigned)a.BH), dim3(4 * D), 0,
+                       s, (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V, a.eta,
+                       a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.T);
+}
+
+template <int D>
+hipError_t launch_d(const LinearArgs& a, hipStream_t s)
+{
+    const bool full = a.T % 16 == 0;
+    const bool eta4 = a.eta && full && reinterpret_cast<uintptr_t>(a.eta) % 16 == 0;
+    if (full) {
+        if (!a.eta) launch_cfg<D, kCoopEtaScalar, true>(a, s);
+        else if (eta4) launch_cfg<D, kCoopEtaToken4, true>(a, s);
+        else launch_cfg<D, kCoopEtaToken, true>(a, s);
+    } else {
+        if (!a.eta) launch_cfg<D, kCoopEtaScalar, false>(a, s);
+        else launch_cfg<D, kCoopEtaToken, false>(a, s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool linear_coop_supported(int d, int chunk, int bf16)
+{
+    return bf16 && (d == 64 || d == 128) && chunk == 16;
+}
+
+hipError_t launch_linear_coop(const LinearArgs& a, hipStream_t s)
+{
+    switch (a.d) {
+    case 64: return launch_d<64>(a, s);
+    case 128: return launch_d<128>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ttt

@@ -411,6 +411,9 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
 #ifndef CHAIN_PF
 #define CHAIN_PF 8
 #endif
+#ifndef COOP_MIN_UNITS
+#define COOP_MIN_UNITS 256
+#endif
 #ifndef CHAIN_PF_WIDE
 #define CHAIN_PF_WIDE 4
 #endif
@@ -491,6 +494,12 @@ bool linear_mfma_supported(int d, int chunk, int bf16)
 
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s)
 {
+    // Once the 16-row units outnumber the compute units, chunk-16 heads at d = 64
+    // and 128 go to one workgroup per head that fetches K and Q once for all of
+    // its waves (8x12 heads at d = 64: 49 us vs 52 us; at 32 heads, where every
+    // unit has a compute unit to itself, the single-wave kernel is faster).
+    if ((long)a.BH * (a.d / 16) > COOP_MIN_UNITS && linear_coop_supported(a.d, a.chunk, a.bf16))
+        return launch_linear_coop(a, s);
     switch (a.d) {
     case 32: return launch_d<32>(a, s);
     case 64: return launch_d<64>(a, s);

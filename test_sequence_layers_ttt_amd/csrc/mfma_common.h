@@ -151,6 +151,25 @@ __device__ __forceinline__ u32x2 lds_transpose16(u32x2* block, u32x2 x, int lane
     return r;
 }
 
+// 16-token K and Q tiles staged in LDS (bf16, rows of d/8 16-byte granules).
+// Granule gr of row r is stored at position gr ^ tile16_swizzle<D>(r), which
+// keeps both reads of the tile free of bank conflicts (checked exhaustively for
+// d = 64 and 128): the row read, lane (c, g) taking granule 4m + g of row c, and
+// the transpose read, lane 4r + q of group g supplying 8 bytes of granule 4m + q
+// of row 4g + r.
+template <int D>
+__device__ __forceinline__ int tile16_swizzle(int row)
+{
+    static_assert(D == 64 || D == 128, "swizzle defined for d = 64 and 128");
+    if constexpr (D == 128) return ((row & 3) << 2) | (row >> 2);
+    else return (((row >> 1) & 1) << 2) | ((row >> 2) & 1) | (((row >> 3) & 1) << 1);
+}
+
+template <int D>
+struct KQTile16 {
+    u32x4 g[2][16 * (D / 8)];   // [K, Q][row * (D / 8) + swizzled granule]
+};
+
 // Workgroup index -> (unit, part) so that the `parts` workgroups of one unit run
 // on the same XCD (workgroups are handed to the 8 XCDs round-robin), sharing
 // that XCD's L2 for the unit's common inputs.  Grid = round_up(units, 8) * parts.

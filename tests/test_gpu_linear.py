@@ -61,6 +61,21 @@ def test_edge_lengths(dev, T, chunk, d):
     check_linear(wl, seed, dev, ttt.PLAN_AUTO)
 
 
+# Many (batch, head) slices: shapes past the 256-unit threshold (units = B*H*d/16)
+# where chunk-16 heads share their K/Q tiles per workgroup, and the two-block
+# single-wave kernel for the shapes that cannot.
+@pytest.mark.parametrize("d,B,H,T,chunk,per_token", [
+    (64, 9, 8, 100, 16, True),     # shared-tile kernel, ragged last chunk
+    (64, 5, 16, 64, 16, False),    # shared-tile kernel, scalar eta
+    (128, 3, 11, 48, 16, True),    # shared-tile kernel at d = 128
+    (32, 9, 15, 40, 16, True),     # two 16-row blocks per wave at d = 32
+    (64, 2, 40, 56, 8, True),      # two blocks per wave, chunk 8
+])
+def test_many_slices(dev, d, B, H, T, chunk, per_token):
+    wl, seed = small(d, chunk, "bf16", per_token=per_token, T=T, B=B, H=H, seed=107)
+    check_linear(wl, seed, dev, ttt.PLAN_AUTO)
+
+
 def test_linear_d16_t256_fp32(dev):
     wl = inputs.WORKLOADS["linear_d16_t256"]
     check_linear(wl, inputs.WORKLOAD_SEEDS[wl.name], dev, ttt.PLAN_AUTO)
