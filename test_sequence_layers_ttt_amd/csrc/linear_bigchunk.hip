@@ -146,9 +146,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void bigchunk_gram_kernel(
 // Kernel B.  One wave per (batch*head, 16 output rows): the state rows live in
 // fp32 C/D tiles as in the sub-tile kernels (lane = output row o, values = input
 // features pi(jb, 4g + r)).  Per chunk: store W_c, then
-//   W_{c+1}^T tile jb = W_c^T tile jb + B_c^T tile jb + (-P_c)(rows pi(jb, .)) W_c^T,
-// with -P_c as the A operand (rows of P, 16-byte loads) and W_c in bf16 as B.
-// The next chunk's P and B are loaded while the current one is applied.
+//   W_{c+1}^T tile jb = W_c^T tile jb + B_c^T tile jb + P_c(rows pi(jb, .)) (-W_c)^T,
+// with P_c as the A operand (rows of P, 16-byte loads) and -W_c in bf16 as B.
+// The operands of the next two chunks are in flight while one is applied.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(64) void bigchunk_chain_kernel(
@@ -186,36 +186,41 @@ __global__ __launch_bounds__(64) void bigchunk_chain_kernel(
             bt[jb] = *(const f32x4*)(Bc + 32 * (jb >> 1) + 8 * g + 4 * (jb & 1));
         }
     };
-    u32x4 pf[NB][NM];
-    f32x4 bt[NB];
-    loadP(0, pf, bt);
-    for (int cc = 0; cc < nchunks; ++cc) {
+    // two chunks of operands in flight: ring position cc & 1, static per half of
+    // the unrolled loop body
+    u32x4 pf[2][NB][NM];
+    f32x4 bt[2][NB];
+    loadP(0, pf[0], bt[0]);
+    if (nchunks > 1) loadP(1, pf[1], bt[1]);
+    auto chunk_step = [&](int cc, auto rc) {
+        constexpr int r = decltype(rc)::value;
         float* wc = Wc + ((size_t)slice * nchunks + cc) * D * D + (size_t)(out0 + c) * D;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             *(f32x4*)(wc + 32 * m + 8 * g) = M[2 * m];
             *(f32x4*)(wc + 32 * m + 8 * g + 4) = M[2 * m + 1];
         }
-        u32x4 Mf[NM];
+        // -W_c in bf16 (the sign goes on the state, not on the 8x larger P operand)
+        u32x4 Mn[NM];
 #pragma unroll
-        for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
-        u32x4 pcur[NB][NM];
-        f32x4 bcur[NB];
-#pragma unroll
-        for (int jb = 0; jb < NB; ++jb) {
-            bcur[jb] = bt[jb];
-#pragma unroll
-            for (int m = 0; m < NM; ++m) pcur[jb][m] = pf[jb][m] ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-        }
-        if (cc + 1 < nchunks) loadP(cc + 1, pf, bt);
+        for (int m = 0; m < NM; ++m)
+            Mn[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]) ^
+                    u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) {
-            f32x4 acc = M[jb] + bcur[jb];
+            f32x4 acc = M[jb] + bt[r][jb];
 #pragma unroll
-            for (int m = 0; m < NM; ++m) acc = mfma32(pcur[jb][m], Mf[m], acc);
+            for (int m = 0; m < NM; ++m) acc = mfma32(pf[r][jb][m], Mn[m], acc);
             M[jb] = acc;
         }
+        if (cc + 2 < nchunks) loadP(cc + 2, pf[r], bt[r]);
+    };
+    int cc = 0;
+    for (; cc + 2 <= nchunks; cc += 2) {
+        chunk_step(cc, std::integral_constant<int, 0>{});
+        chunk_step(cc + 1, std::integral_constant<int, 1>{});
     }
+    if (cc < nchunks) chunk_step(cc, std::integral_constant<int, 0>{});
     float* w = W_out + (size_t)slice * D * D + (size_t)(out0 + c) * D;
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
