@@ -100,10 +100,13 @@ struct Lds {
     u32x2 tK[kWaves][kNB * 64];     // K tile for the W1 update operand
     u32x2 tW2[kWaves][kUB * kNB * 64];  // fp16 W2 tiles for the transpose to (u, o)
     float b2d[kWaves][kD];          // b2 update staging
-    // shared partial sums (fp32, C/D layout, one f32x4 per lane)
-    f32x4 Ep[kWaves][kNB][64];
-    f32x4 S2p[kWaves][64];
-    f32x4 Zp[kWaves][kNB][64];
+    // shared partial sums (fp32, C/D layout, one f32x4 per lane), double-buffered
+    // by chunk parity: a wave may write chunk c+1's partials while another still
+    // reads chunk c's
+    f32x4 Ep[2][kWaves][kNB][64];   // W2 A_{c+1}  (+ b2 - V_{c+1} from wave 0)
+    f32x4 S3p[2][kWaves][64];       // A_c^T A_{c+1}
+    f32x4 Zp[2][kWaves][kNB][64];   // W2 A'_c     (+ b2 from wave 0)
+    f32x4 S2p[2][kWaves][64];       // A_c^T A'_c
 };
 
 // One chunk's inputs as loaded (bf16), one chunk ahead of their use.
@@ -192,19 +195,96 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
             t.ec = eta_scalar;
         }
     };
-    ChunkIn nxt;
-    load_in(nxt, 0);
+    auto to_f16 = [&](const u32x4 (&x)[kNB / 2], u32x4 (&y)[kNB / 2]) {
+#pragma unroll
+        for (int m = 0; m < kNB / 2; ++m) y[m] = bf16x8_to_f16x8(x[m]);
+    };
+    // fp16 state operands: W1 rows (B operand over the input features) and W2o tiles
+    u32x4 W1f[kUB][kNB / 2];
+    u32x2 W2f[kNB][kUB];
+    auto pack_state = [&]() {
+#pragma unroll
+        for (int ub = 0; ub < kUB; ++ub)
+#pragma unroll
+            for (int m = 0; m < kNB / 2; ++m)
+                W1f[ub][m] = pack_f16x8(W1t[ub][2 * m], W1t[ub][2 * m + 1]);
+#pragma unroll
+        for (int ob = 0; ob < kNB; ++ob)
+#pragma unroll
+            for (int ub = 0; ub < kUB; ++ub) W2f[ob][ub] = pack_f16x4(W2o[ob][ub]);
+    };
+    auto w2pair = [&](int ob, int m) {
+        return u32x4{W2f[ob][2 * m].x, W2f[ob][2 * m].y, W2f[ob][2 * m + 1].x, W2f[ob][2 * m + 1].y};
+    };
+    // A (fp16, lane = hidden unit) -> tokens in the lanes, hidden units in the slots
+    auto transpose_a = [&](u32x2* buf, const u32x2 (&ab)[kUB], u32x4 (&ta)[kUB / 2]) {
+        u32x2 t[kUB];
+#pragma unroll
+        for (int ub = 0; ub < kUB; ++ub) t[ub] = lds_transpose16(buf + ub * 64, ab[ub], lane);
+#pragma unroll
+        for (int m = 0; m < kUB / 2; ++m) ta[m] = u32x4{t[2 * m].x, t[2 * m].y, t[2 * m + 1].x, t[2 * m + 1].y};
+    };
+    // partial of W2 X (o x t) over this wave's units, plus `base` on wave 0
+    auto w2_partial = [&](const u32x4 (&tx)[kUB / 2], int ob, f32x4 base) {
+        f32x4 e = (w == 0) ? base : f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int m = 0; m < kUB / 2; ++m) e = mfma32h(w2pair(ob, m), tx[m], e);
+        return e;
+    };
+
+    // ---- chunk 0's forward at the initial state: H, A, gelu'(H), E ----
+    ChunkIn cur, nx, nx2;
+    load_in(cur, 0);
+    load_in(nx, 1);
+    pack_state();
+    u32x4 Kc[kNB / 2];          // K of the current chunk (fp16, lane = token)
+    to_f16(cur.k, Kc);
+    f32x4 G[kUB];               // gelu'(H_c)
+    u32x2 Ab[kUB];              // A_c (fp16, lane = hidden unit, rows = tokens)
+    u32x4 tAf[kUB / 2];         // A_c with tokens in the lanes
+    f32x4 E[kNB];               // E_c (lanes = tokens, rows = output features)
+    {
+#pragma unroll
+        for (int ub = 0; ub < kUB; ++ub) {
+            f32x4 h = {b1r[ub], b1r[ub], b1r[ub], b1r[ub]};
+#pragma unroll
+            for (int m = 0; m < kNB / 2; ++m) h = mfma32h(Kc[m], W1f[ub][m], h);
+            f32x4 a;
+            gelu_pair(h, a, G[ub]);
+            Ab[ub] = pack_f16x4(a);
+        }
+        transpose_a(L.tA[w], Ab, tAf);
+#pragma unroll
+        for (int ob = 0; ob < kNB; ++ob)
+            L.Ep[1][w][ob][lane] = w2_partial(tAf, ob, b2r[ob] - bf16x4_to_f32(cur.v[ob]));
+        __syncthreads();
+#pragma unroll
+        for (int ob = 0; ob < kNB; ++ob) {
+            f32x4 e = L.Ep[1][0][ob][lane];
+#pragma unroll
+            for (int v = 1; v < kWaves; ++v) e += L.Ep[1][v][ob][lane];
+            E[ob] = e;
+        }
+    }
+
+    // Chunk c, from its start state and its forward (H_c, A_c, E_c): the backward
+    // D_c, then two reads of the chunk's updated model -- Q_c (the output, causal
+    // and inclusive) and K_{c+1} (the next chunk's forward; every token of chunk c
+    // precedes it) -- and one barrier for all the sums over hidden units:
+    //   H'      = W1 Q_c     + b1 - D_c diag(eta) (U * (K_c^T Q_c + 1))
+    //   H_{c+1} = W1 K_{c+1} + b1 - D_c diag(eta) (K_c^T K_{c+1} + 1)
+    //   Z_c     = W2 A'      + b2 - E_c diag(eta) (U * (A_c^T A' + 1))
+    //   E_{c+1} = W2 A_{c+1} + b2 - V_{c+1} - E_c diag(eta) (A_c^T A_{c+1} + 1)
+    // The state update itself is off the chain: only the next chunk's operands
+    // need it.
     for (int ci = 0; ci < nchunks; ++ci) {
         const int s0 = ci * step;
         const int n = FULL ? 16 : min(step, T - s0);
-        const ChunkIn cur = nxt;
-        load_in(nxt, ci + 1);
-        u32x4 Kf[kNB / 2], Qf[kNB / 2];
-#pragma unroll
-        for (int m = 0; m < kNB / 2; ++m) {
-            Kf[m] = bf16x8_to_f16x8(cur.k[m]);
-            Qf[m] = bf16x8_to_f16x8(cur.q[m]);
-        }
+        const int pb = ci & 1;
+        load_in(nx2, ci + 2);
+        u32x4 Qf[kNB / 2], Kn[kNB / 2];
+        to_f16(cur.q, Qf);
+        to_f16(nx.k, Kn);
         f32x4 er = cur.er;   // zero for padding tokens
         float ec = cur.ec;
         if (!FULL) {
@@ -213,82 +293,11 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
             ec = (c < n) ? ec : 0.f;
         }
 
-        // ---- fp16 operands of the chunk-start state ----
-        u32x4 W1f[kUB][kNB / 2];
-#pragma unroll
-        for (int ub = 0; ub < kUB; ++ub)
-#pragma unroll
-            for (int m = 0; m < kNB / 2; ++m) W1f[ub][m] = pack_f16x8(W1t[ub][2 * m], W1t[ub][2 * m + 1]);
-        u32x2 W2f[kNB][kUB];   // W2o tiles in fp16 (A operand over u, two tiles per x32)
-#pragma unroll
-        for (int ob = 0; ob < kNB; ++ob)
-#pragma unroll
-            for (int ub = 0; ub < kUB; ++ub) W2f[ob][ub] = pack_f16x4(W2o[ob][ub]);
-        auto w2pair = [&](int ob, int m) {
-            return u32x4{W2f[ob][2 * m].x, W2f[ob][2 * m].y, W2f[ob][2 * m + 1].x,
-                         W2f[ob][2 * m + 1].y};
-        };
-
-        // ---- H^T (t x u) = K W1^T + b1; A = gelu(H), G = gelu'(H) ----
-        f32x4 A[kUB], G[kUB];
-        u32x2 Ab[kUB];
-#pragma unroll
-        for (int ub = 0; ub < kUB; ++ub) {
-            f32x4 h = {b1r[ub], b1r[ub], b1r[ub], b1r[ub]};
-#pragma unroll
-            for (int m = 0; m < kNB / 2; ++m) h = mfma32h(Kf[m], W1f[ub][m], h);
-            gelu_pair(h, A[ub], G[ub]);
-            Ab[ub] = pack_f16x4(A[ub]);
-        }
-        // A with tokens in lanes and hidden units in slots (B operand over u)
-        u32x4 tAf[kUB / 2];
-        {
-            u32x2 t0[kUB];
-#pragma unroll
-            for (int ub = 0; ub < kUB; ++ub) t0[ub] = lds_transpose16(&L.tA[w][ub * 64], Ab[ub], lane);
-#pragma unroll
-            for (int m = 0; m < kUB / 2; ++m)
-                tAf[m] = u32x4{t0[2 * m].x, t0[2 * m].y, t0[2 * m + 1].x, t0[2 * m + 1].y};
-        }
-
-        // ---- E partial (o x t) over this wave's units; wave 0 adds b2 - V ----
-#pragma unroll
-        for (int ob = 0; ob < kNB; ++ob) {
-            f32x4 e = {0, 0, 0, 0};
-            if (w == 0) e = b2r[ob] - bf16x4_to_f32(cur.v[ob]);
-#pragma unroll
-            for (int m = 0; m < kUB / 2; ++m) e = mfma32h(w2pair(ob, m), tAf[m], e);
-            L.Ep[w][ob][lane] = e;
-        }
-        // ---- S1 (s x t) = K Q^T (+1), causal, scaled by -eta_s (A operand of H') ----
-        u32x2 S1b;
-        {
-            f32x4 s1 = {0, 0, 0, 0};
-#pragma unroll
-            for (int m = 0; m < kNB / 2; ++m) s1 = mfma32h(Kf[m], Qf[m], s1);
-            f32x4 sm;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sm[r] = (4 * g + r <= c) ? -er[r] * (s1[r] + (HAS_B1 ? 1.f : 0.f)) : 0.f;
-            S1b = pack_f16x4(sm);
-        }
-        __syncthreads();
-
-        // ---- E = sum of the partials (every wave; lanes = tokens, rows = o) ----
-        f32x4 E[kNB];
-#pragma unroll
-        for (int ob = 0; ob < kNB; ++ob) {
-            f32x4 e = L.Ep[0][ob][lane];
-#pragma unroll
-            for (int v = 1; v < kWaves; ++v) e += L.Ep[v][ob][lane];
-            E[ob] = e;
-        }
-        // -eta E with o in the lanes and tokens in the slots
+        // -eta E_c with o in the lanes and tokens in the slots
         u32x2 tE[kNB];
 #pragma unroll
         for (int ob = 0; ob < kNB; ++ob)
             tE[ob] = lds_transpose16(&L.tE[w][ob * 64], pack_f16x4(-ec * E[ob]), lane);
-
         // ---- D^T (t x u) = (E^T W2) * gelu'(H) ----
         u32x4 Ef[kNB / 2];
 #pragma unroll
@@ -313,63 +322,102 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
             DSb[ub] = pack_f16x4(ds);
             if (HAS_B1) db1[ub] = ds[0] + ds[1] + ds[2] + ds[3];
         }
-
-        // ---- H'^T = Q W1^T + b1 - S1^T diag(eta) D^T ;  A' = gelu(H') ----
-        u32x4 tA2f[kUB / 2];
+        // ---- scores of K_c against Q_c (causal) and K_{c+1} (all), scaled by -eta_s ----
+        u32x2 S1q, S1k;
         {
-            u32x2 t1[kUB];
+            f32x4 sq = {0, 0, 0, 0}, sk = {0, 0, 0, 0};
 #pragma unroll
-            for (int ub = 0; ub < kUB; ++ub) {
-                f32x4 h = {b1r[ub], b1r[ub], b1r[ub], b1r[ub]};
-#pragma unroll
-                for (int m = 0; m < kNB / 2; ++m) h = mfma32h(Qf[m], W1f[ub][m], h);
-                h = mfma16h(S1b, Db[ub], h);
-                t1[ub] = lds_transpose16(&L.tA2[w][ub * 64], pack_f16x4(gelu4(h)), lane);
+            for (int m = 0; m < kNB / 2; ++m) {
+                sq = mfma32h(Kc[m], Qf[m], sq);
+                sk = mfma32h(Kc[m], Kn[m], sk);
             }
+            f32x4 mq, mk;
 #pragma unroll
-            for (int m = 0; m < kUB / 2; ++m)
-                tA2f[m] = u32x4{t1[2 * m].x, t1[2 * m].y, t1[2 * m + 1].x, t1[2 * m + 1].y};
+            for (int r = 0; r < 4; ++r) {
+                mq[r] = (4 * g + r <= c) ? -er[r] * (sq[r] + (HAS_B1 ? 1.f : 0.f)) : 0.f;
+                mk[r] = -er[r] * (sk[r] + (HAS_B1 ? 1.f : 0.f));
+            }
+            S1q = pack_f16x4(mq);
+            S1k = pack_f16x4(mk);
         }
-        // ---- partials of S2 (s x t) = A^T A' and of W2 A' (o x t) ----
-        {
-            f32x4 s2 = {0, 0, 0, 0};
+        // ---- H' and H_{c+1}; A' = gelu(H'), A_{c+1} = gelu(H_{c+1}), G_{c+1} ----
+        u32x2 A2b[kUB], An[kUB];
+        f32x4 Gn[kUB];
 #pragma unroll
-            for (int m = 0; m < kUB / 2; ++m) s2 = mfma32h(tAf[m], tA2f[m], s2);
-            L.S2p[w][lane] = s2;
+        for (int ub = 0; ub < kUB; ++ub) {
+            f32x4 hq = {b1r[ub], b1r[ub], b1r[ub], b1r[ub]};
+            f32x4 hk = hq;
+#pragma unroll
+            for (int m = 0; m < kNB / 2; ++m) {
+                hq = mfma32h(Qf[m], W1f[ub][m], hq);
+                hk = mfma32h(Kn[m], W1f[ub][m], hk);
+            }
+            hq = mfma16h(S1q, Db[ub], hq);
+            hk = mfma16h(S1k, Db[ub], hk);
+            A2b[ub] = pack_f16x4(gelu4(hq));
+            f32x4 a;
+            gelu_pair(hk, a, Gn[ub]);
+            An[ub] = pack_f16x4(a);
+        }
+        u32x4 tA2f[kUB / 2], tAn[kUB / 2];
+        transpose_a(L.tA2[w], A2b, tA2f);
+        transpose_a(L.tA[w], An, tAn);
+        // ---- per-wave partials of Z_c and E_{c+1} ----
+        {
+            f32x4 s2 = {0, 0, 0, 0}, s3 = {0, 0, 0, 0};
+#pragma unroll
+            for (int m = 0; m < kUB / 2; ++m) {
+                s2 = mfma32h(tAf[m], tA2f[m], s2);
+                s3 = mfma32h(tAf[m], tAn[m], s3);
+            }
+            L.S2p[pb][w][lane] = s2;
+            L.S3p[pb][w][lane] = s3;
 #pragma unroll
             for (int ob = 0; ob < kNB; ++ob) {
-                f32x4 z = (w == 0) ? b2r[ob] : f32x4{0, 0, 0, 0};
-#pragma unroll
-                for (int m = 0; m < kUB / 2; ++m) z = mfma32h(w2pair(ob, m), tA2f[m], z);
-                L.Zp[w][ob][lane] = z;
+                L.Zp[pb][w][ob][lane] = w2_partial(tA2f, ob, b2r[ob]);
+                L.Ep[pb][w][ob][lane] = w2_partial(tAn, ob, b2r[ob] - bf16x4_to_f32(nx.v[ob]));
             }
         }
         __syncthreads();
 
-        // ---- wave w finishes Z for output block w ----
+        // ---- Z_c: wave w finishes output block w ----
         {
-            f32x4 s2 = L.S2p[0][lane];
+            f32x4 s2 = L.S2p[pb][0][lane];
 #pragma unroll
-            for (int v = 1; v < kWaves; ++v) s2 += L.S2p[v][lane];
+            for (int v = 1; v < kWaves; ++v) s2 += L.S2p[pb][v][lane];
             f32x4 sm;
 #pragma unroll
             for (int r = 0; r < 4; ++r) sm[r] = (4 * g + r <= c) ? s2[r] + (HAS_B2 ? 1.f : 0.f) : 0.f;
-            f32x4 z = L.Zp[0][w][lane];
+            f32x4 z = L.Zp[pb][0][w][lane];
 #pragma unroll
-            for (int v = 1; v < kWaves; ++v) z += L.Zp[v][w][lane];
+            for (int v = 1; v < kWaves; ++v) z += L.Zp[pb][v][w][lane];
             z = mfma16h(tE[w], pack_f16x4(sm), z);
             if (FULL || c < n) *(u32x2*)(Z + (tok0 + s0 + c) * kD + 16 * w + 4 * g) = pack_bf16x4(z);
         }
-
-        // ---- state updates ----
+        // ---- E_{c+1} (every wave, every output block) ----
         {
-            // K with input features in the lanes and tokens in the slots
+            f32x4 s3 = L.S3p[pb][0][lane];
+#pragma unroll
+            for (int v = 1; v < kWaves; ++v) s3 += L.S3p[pb][v][lane];
+            const u32x2 s3b = pack_f16x4(s3 + (HAS_B2 ? 1.f : 0.f));
+#pragma unroll
+            for (int ob = 0; ob < kNB; ++ob) {
+                f32x4 e = L.Ep[pb][0][ob][lane];
+#pragma unroll
+                for (int v = 1; v < kWaves; ++v) e += L.Ep[pb][v][ob][lane];
+                E[ob] = mfma16h(tE[ob], s3b, e);
+            }
+        }
+
+        // ---- state updates (needed from the next chunk's operands on) ----
+        {
+            // K_c with input features in the lanes and tokens in the slots
             // (block ib holds K[token][pi(ib, 0..15)] row by row, 512 bytes)
             u32x2 Kt[kNB];
 #pragma unroll
             for (int m = 0; m < kNB / 2; ++m) {
-                L.tK[w][(2 * m) * 64 + 4 * c + g] = lo_half(Kf[m]);
-                L.tK[w][(2 * m + 1) * 64 + 4 * c + g] = hi_half(Kf[m]);
+                L.tK[w][(2 * m) * 64 + 4 * c + g] = lo_half(Kc[m]);
+                L.tK[w][(2 * m + 1) * 64 + 4 * c + g] = hi_half(Kc[m]);
             }
             asm volatile("" ::: "memory");
 #pragma unroll
@@ -412,6 +460,19 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
                 asm volatile("" ::: "memory");
             }
         }
+        pack_state();
+        // ---- move to the next chunk ----
+#pragma unroll
+        for (int ub = 0; ub < kUB; ++ub) {
+            G[ub] = Gn[ub];
+            Ab[ub] = An[ub];
+        }
+#pragma unroll
+        for (int m = 0; m < kUB / 2; ++m) tAf[m] = tAn[m];
+#pragma unroll
+        for (int m = 0; m < kNB / 2; ++m) Kc[m] = Kn[m];
+        cur = nx;
+        nx = nx2;
     }
 
     // ---- final state ----
