@@ -63,11 +63,24 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
     const int grow = (tid / G) & 15, ggr = tid % G;
     const uint16_t* src = which ? Q : K;
     const int lpos = grow * G + (ggr ^ tile16_swizzle<D>(grow));
+    // first token of chunk ch (clamped), as a wave-uniform base; lanes add a
+    // 32-bit offset within the chunk
+    auto chunk_base = [&](int ch) {
+        const int cc = ch < nch ? ch : nch - 1;
+        return tok0 + (size_t)16 * cc;
+    };
+    auto row_in = [&](int ch, int r) {   // row r of chunk ch, clamped into the sequence
+        if (FULL) return r;
+        const int cc = ch < nch ? ch : nch - 1;
+        return 16 * cc + r < T ? r : T - 1 - 16 * cc;
+    };
     auto gload = [&](int ch) {
-        return *(const u32x4*)(src + (tok0 + tok(ch, grow)) * D + 8 * ggr);
+        const uint16_t* b = src + chunk_base(ch) * D;
+        return *(const u32x4*)(b + (row_in(ch, grow) * D + 8 * ggr));
     };
     auto vload = [&](int ch) {
-        return *(const u32x2*)(V + (tok0 + tok(ch, c)) * D + out0 + 4 * g);
+        const uint16_t* b = V + chunk_base(ch) * D;
+        return *(const u32x2*)(b + (row_in(ch, c) * D + out0 + 4 * g));
     };
     auto eload = [&](int ch) {
         if (ETA == kCoopEtaToken4) {
@@ -117,12 +130,12 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
     rg[1] = gload(P + 1);
     __syncthreads();
 
-    // E_0 = K_0 W_0^T - V_0 directly
-    u32x4 kc[NM];
-    row_operand(L[0].g[0], kc);
+    // E_0 = K_0 W_0^T - V_0 directly.  kb[ch & 1] holds K_ch as row operand.
+    u32x4 kb[2][NM];
+    row_operand(L[0].g[0], kb[0]);
     f32x4 Et = mfma16(rv[0] ^ u32x2{0x80008000u, 0x80008000u}, I16, f32x4{0, 0, 0, 0});
 #pragma unroll
-    for (int m = 0; m < NM; ++m) Et = mfma32(kc[m], Mf[m], Et);
+    for (int m = 0; m < NM; ++m) Et = mfma32(kb[0][m], Mf[m], Et);
 
     // one chunk; p = ch % P is a compile-time ring position
     auto step = [&](int ch, auto pc) {
@@ -133,7 +146,10 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
 
         const u32x4* Kc = L[ch & 3].g[0];
         const u32x4* Qc = L[ch & 3].g[1];
-        u32x4 kn[NM], qc[NM];
+        constexpr int pe = p & 1;   // ch & 1 (the ring length is even)
+        u32x4 (&kc)[NM] = kb[pe];
+        u32x4 (&kn)[NM] = kb[pe ^ 1];
+        u32x4 qc[NM];
         row_operand(L[(ch + 1) & 3].g[0], kn);   // stale (unused) after the last chunk
         row_operand(Qc, qc);
         // K_c with the feature in the lanes (A operand of the state update)
@@ -187,13 +203,12 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
 #pragma unroll
         for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[m], qc[m], Zt);
         Zt = mfma16(F, pack_bf16x4(Sm), Zt);
-        if (FULL || 16 * ch + c < T)
-            *(u32x2*)(Z + (tok0 + 16 * ch + c) * D + out0 + 4 * g) = pack_bf16x4(Zt);
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
-            kc[m] = kn[m];
+        if (FULL || 16 * ch + c < T) {
+            uint16_t* zb = Z + (tok0 + (size_t)16 * ch) * D;
+            *(u32x2*)(zb + (c * D + out0 + 4 * g)) = pack_bf16x4(Zt);
         }
+#pragma unroll
+        for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
         rv[p] = vload(ch + P);
         re[p] = eload(ch + P);
         __syncthreads();
