@@ -22,7 +22,9 @@ def rel_err(gpu, ref, floor=1e-6):
     return float((np.abs(g - r).max(axis=1) / den).max())
 
 
-def device_inputs(wl, x, dev):
+def device_inputs(wl, x, dev, eta_offset=0):
+    """Device copies of the inputs.  eta_offset > 0 places eta that many floats into
+    its allocation, so its pointer is 4-byte but not 16-byte aligned."""
     import torch
     io = torch.bfloat16 if wl.io == "bf16" else torch.float32
     B, H, T, d = wl.B, wl.H, wl.T, wl.d
@@ -31,7 +33,14 @@ def device_inputs(wl, x, dev):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev).reshape(shape).to(dt).contiguous()
 
     out = {k: t(x[k], (B, H, T, d), io) for k in ("K", "Q", "V")}
-    out["eta"] = None if x["eta"] is None else t(x["eta"], (B, H, T))
+    if x["eta"] is None:
+        out["eta"] = None
+    elif eta_offset:
+        buf = torch.zeros(B * H * T + eta_offset, dtype=torch.float32, device=dev)
+        buf[eta_offset:] = torch.from_numpy(np.ascontiguousarray(x["eta"]).reshape(-1)).to(dev)
+        out["eta"] = buf[eta_offset:].view(B, H, T)
+    else:
+        out["eta"] = t(x["eta"], (B, H, T))
     if wl.model == "linear":
         out["W0"] = t(x["W0"], (B, H, d, d))
     else:
@@ -47,20 +56,20 @@ def host(t, n):
     return t.float().cpu().numpy().reshape(n, *t.shape[2:])
 
 
-def run_linear(wl, x, dev, plan=0, **kw):
+def run_linear(wl, x, dev, plan=0, eta_offset=0, **kw):
     import torch
     from test_sequence_layers_ttt_amd import ttt
-    a = device_inputs(wl, x, dev)
+    a = device_inputs(wl, x, dev, eta_offset)
     Z, W = ttt.linear_fwd(a["K"], a["Q"], a["V"], a["eta"], a["W0"], wl.chunk,
                           eta_scalar=x["eta_scalar"], plan=plan, **kw)
     torch.cuda.synchronize()
     return host(Z, wl.BH), host(W, wl.BH)
 
 
-def run_mlp(wl, x, dev, plan=0, **kw):
+def run_mlp(wl, x, dev, plan=0, eta_offset=0, **kw):
     import torch
     from test_sequence_layers_ttt_amd import ttt
-    a = device_inputs(wl, x, dev)
+    a = device_inputs(wl, x, dev, eta_offset)
     res = ttt.mlp_fwd(a["K"], a["Q"], a["V"], a["eta"], a["W1"], a["b1"], a["W2"], a["b2"],
                       wl.chunk, eta_scalar=x["eta_scalar"], plan=plan, **kw)
     torch.cuda.synchronize()

@@ -27,13 +27,13 @@ def small(d, chunk, io, per_token, T=77, B=2, H=3, seed=101):
                       eta_value=0.1 if per_token else 0.07), seed
 
 
-def check_linear(wl, seed, dev, plan, slices=None):
+def check_linear(wl, seed, dev, plan, slices=None, eta_offset=0):
     x = inputs.make_inputs(wl, seed)
     p = ttt.linear_select_plan(wl.B, wl.H, wl.T, wl.d, wl.chunk, 1 if wl.io == "bf16" else 0, plan)
     if p < 0:
         pytest.skip("plan %d does not run this shape" % plan)
     say("case", wl, "seed", seed, "plan", ttt.plan_name(p))
-    Z, W = run_linear(wl, x, dev, plan=plan)
+    Z, W = run_linear(wl, x, dev, plan=plan, eta_offset=eta_offset)
     idx = np.arange(wl.BH) if slices is None else np.asarray(slices)
     xo = take(x, idx)
     Zo, Wo = oracle.linear(xo["K"], xo["Q"], xo["V"], xo["eta"], xo["eta_scalar"], xo["W0"],
@@ -74,6 +74,21 @@ def test_edge_lengths(dev, T, chunk, d):
 def test_many_slices(dev, d, B, H, T, chunk, per_token):
     wl, seed = small(d, chunk, "bf16", per_token=per_token, T=T, B=B, H=H, seed=107)
     check_linear(wl, seed, dev, ttt.PLAN_AUTO)
+
+
+# Per-token eta whose pointer is 4-byte but not 16-byte aligned: every kernel
+# family must take its per-element eta loads (T a multiple of 16 otherwise picks
+# the 16-byte loads).
+@pytest.mark.parametrize("d,B,H,T,chunk", [
+    (64, 9, 8, 64, 16),       # shared-tile kernel
+    (64, 2, 3, 64, 16),       # single-wave chunk kernel
+    (32, 9, 15, 32, 16),      # two blocks per wave
+    (64, 1, 3, 256, 128),     # large-chunk plan
+    (64, 2, 2, 96, 32),       # multi-sub-tile chunks
+])
+def test_unaligned_eta(dev, d, B, H, T, chunk):
+    wl, seed = small(d, chunk, "bf16", per_token=True, T=T, B=B, H=H, seed=113)
+    check_linear(wl, seed, dev, ttt.PLAN_AUTO, eta_offset=1)
 
 
 def test_linear_d16_t256_fp32(dev):

@@ -21,7 +21,7 @@ def dev():
     return torch.device("cuda:0")
 
 
-def check_mlp(wl, seed, dev, plan, slices=None, bias_init=None):
+def check_mlp(wl, seed, dev, plan, slices=None, bias_init=None, eta_offset=0):
     x = inputs.make_inputs(wl, seed)
     if bias_init is not None and wl.mlp_bias:
         rng = np.random.default_rng(seed + 999)
@@ -31,7 +31,7 @@ def check_mlp(wl, seed, dev, plan, slices=None, bias_init=None):
     if p < 0:
         pytest.skip("plan %d does not run this shape" % plan)
     say("case", wl, "seed", seed, "plan", ttt.plan_name(p))
-    got = run_mlp(wl, x, dev, plan=plan)
+    got = run_mlp(wl, x, dev, plan=plan, eta_offset=eta_offset)
     idx = np.arange(wl.BH) if slices is None else np.asarray(slices)
     xo = take(x, idx)
     ref = oracle.mlp(xo["K"], xo["Q"], xo["V"], xo["eta"], xo["eta_scalar"], xo["W1"], xo["b1"],
@@ -68,6 +68,11 @@ def test_small_shapes(dev, plan, d, chunk, io, bias):
 @pytest.mark.parametrize("T", [1, 7, 33])
 def test_edge_lengths(dev, T):
     check_mlp(small(64, 16, "bf16", per_token=True, T=T), 300 + T, dev, ttt.PLAN_AUTO)
+
+
+def test_unaligned_eta(dev):
+    # per-token eta at a 4-byte (not 16-byte) aligned address
+    check_mlp(small(64, 16, "bf16", per_token=True, T=48), 317, dev, ttt.PLAN_AUTO, eta_offset=1)
 
 
 def test_mlp_b16_4x16_full(dev):
