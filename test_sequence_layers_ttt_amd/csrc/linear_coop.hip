@@ -15,7 +15,12 @@
 // register ring eight chunks deep -- into a ring of four swizzled LDS tiles, and
 // every wave reads its operands from there (row reads; the transpose read gives K
 // with the feature in the lanes for the state update).  V and eta are loaded per
-// wave.  One barrier per chunk.
+// wave.
+//
+// Tiles are staged in groups of kGroup chunks into a ring three groups deep: a
+// chunk's tile is stored eight steps before it is needed, so one barrier per
+// group suffices, and the K rows of chunk c+2 are read into registers during
+// chunk c, keeping LDS latency off the chunk-to-chunk chain.
 #include <stdint.h>
 
 #include <type_traits>
@@ -38,8 +43,12 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
     constexpr int NB = D / 16;
     constexpr int NM = D / 32;
     constexpr int G = D / 8;     // 16-byte granules per row
-    constexpr int P = 8;         // chunks in flight per thread
-    __shared__ KQTile16<D> L[4];
+    // chunks per barrier (d = 128: eight waves per workgroup leave 256 registers
+    // per wave, so shorter rings)
+    constexpr int kGroup = D >= 128 ? 2 : 4;
+    constexpr int P = 2 * kGroup;   // chunks whose granule a thread holds in registers
+    constexpr int kSlots = 3 * kGroup;
+    __shared__ KQTile16<D> L[kSlots];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -115,6 +124,9 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
     for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
     const u32x2 I16 = identity_b16(lane);
 
+    // chunk X lives in LDS slot X % kSlots.  Tiles of chunks 0 .. 2*kGroup-1 are
+    // stored up front; during chunk ch the tile of chunk ch + P is stored and the
+    // granule of chunk ch + 2P loaded (into the register slot it came from).
     u32x4 rg[P];
     u32x2 rv[P];
     f32x4 re[P];
@@ -124,15 +136,18 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
         rv[p] = vload(p);
         re[p] = eload(p);
     }
-    L[0].g[which][lpos] = rg[0];
-    L[1].g[which][lpos] = rg[1];
-    rg[0] = gload(P);
-    rg[1] = gload(P + 1);
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        L[p].g[which][lpos] = rg[p];
+        rg[p] = gload(P + p);
+    }
     __syncthreads();
 
-    // E_0 = K_0 W_0^T - V_0 directly.  kb[ch & 1] holds K_ch as row operand.
+    // E_0 = K_0 W_0^T - V_0 directly.  kb[ch & 1] holds K_ch as row operand; the
+    // other set holds K_{ch+1}.
     u32x4 kb[2][NM];
     row_operand(L[0].g[0], kb[0]);
+    row_operand(L[1].g[0], kb[1]);
     f32x4 Et = mfma16(rv[0] ^ u32x2{0x80008000u, 0x80008000u}, I16, f32x4{0, 0, 0, 0});
 #pragma unroll
     for (int m = 0; m < NM; ++m) Et = mfma32(kb[0][m], Mf[m], Et);
@@ -140,17 +155,17 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
     // one chunk; p = ch % P is a compile-time ring position
     auto step = [&](int ch, auto pc) {
         constexpr int p = decltype(pc)::value;
-        // stage chunk ch + 2, refill its register slot
-        if (ch + 2 < nch) L[(ch + 2) & 3].g[which][lpos] = rg[(p + 2) % P];
-        rg[(p + 2) % P] = gload(ch + 2 + P);
+        // stage chunk ch + P, refill its register slot with chunk ch + 2P
+        if (ch + P < nch) L[(ch + P) % kSlots].g[which][lpos] = rg[p];
+        rg[p] = gload(ch + 2 * P);
 
-        const u32x4* Kc = L[ch & 3].g[0];
-        const u32x4* Qc = L[ch & 3].g[1];
+        const int sl = ch % kSlots;
+        const u32x4* Kc = L[sl].g[0];
+        const u32x4* Qc = L[sl].g[1];
         constexpr int pe = p & 1;   // ch & 1 (the ring length is even)
         u32x4 (&kc)[NM] = kb[pe];
         u32x4 (&kn)[NM] = kb[pe ^ 1];
         u32x4 qc[NM];
-        row_operand(L[(ch + 1) & 3].g[0], kn);   // stale (unused) after the last chunk
         row_operand(Qc, qc);
         // K_c with the feature in the lanes (A operand of the state update)
         u32x2 kt[NB];
@@ -209,9 +224,11 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
         }
 #pragma unroll
         for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
+        // K_{c+2} into the set K_c leaves (stale, unused, past the end)
+        row_operand(L[(ch + 2) % kSlots].g[0], kc);
         rv[p] = vload(ch + P);
         re[p] = eload(ch + P);
-        __syncthreads();
+        if (p % kGroup == kGroup - 1) __syncthreads();
     };
 
     int c0 = 0;
@@ -220,18 +237,22 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
         step(c0 + 1, std::integral_constant<int, 1>{});
         step(c0 + 2, std::integral_constant<int, 2>{});
         step(c0 + 3, std::integral_constant<int, 3>{});
-        step(c0 + 4, std::integral_constant<int, 4>{});
-        step(c0 + 5, std::integral_constant<int, 5>{});
-        step(c0 + 6, std::integral_constant<int, 6>{});
-        step(c0 + 7, std::integral_constant<int, 7>{});
+        if constexpr (P == 8) {
+            step(c0 + 4, std::integral_constant<int, 4 % P>{});
+            step(c0 + 5, std::integral_constant<int, 5 % P>{});
+            step(c0 + 6, std::integral_constant<int, 6 % P>{});
+            step(c0 + 7, std::integral_constant<int, 7 % P>{});
+        }
     }
     if (c0 + 0 < nch) step(c0 + 0, std::integral_constant<int, 0>{});
     if (c0 + 1 < nch) step(c0 + 1, std::integral_constant<int, 1>{});
     if (c0 + 2 < nch) step(c0 + 2, std::integral_constant<int, 2>{});
-    if (c0 + 3 < nch) step(c0 + 3, std::integral_constant<int, 3>{});
-    if (c0 + 4 < nch) step(c0 + 4, std::integral_constant<int, 4>{});
-    if (c0 + 5 < nch) step(c0 + 5, std::integral_constant<int, 5>{});
-    if (c0 + 6 < nch) step(c0 + 6, std::integral_constant<int, 6>{});
+    if constexpr (P == 8) {
+        if (c0 + 3 < nch) step(c0 + 3, std::integral_constant<int, 3>{});
+        if (c0 + 4 < nch) step(c0 + 4, std::integral_constant<int, 4 % P>{});
+        if (c0 + 5 < nch) step(c0 + 5, std::integral_constant<int, 5 % P>{});
+        if (c0 + 6 < nch) step(c0 + 6, std::integral_constant<int, 6 % P>{});
+    }
 
     float* w = W_out + (size_t)slice * D * D + (size_t)(out0 + c) * D;
 #pragma unroll
