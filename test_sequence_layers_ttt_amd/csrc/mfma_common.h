@@ -152,11 +152,14 @@ __device__ __forceinline__ u32x2 lds_transpose16(u32x2* block, u32x2 x, int lane
 }
 
 // 16-token K and Q tiles staged in LDS (bf16, rows of d/8 16-byte granules).
-// Granule gr of row r is stored at position gr ^ tile16_swizzle<D>(r), which
-// keeps both reads of the tile free of bank conflicts (checked exhaustively for
-// d = 64 and 128): the row read, lane (c, g) taking granule 4m + g of row c, and
-// the transpose read, lane 4r + q of group g supplying 8 bytes of granule 4m + q
-// of row 4g + r.
+// Granule gr of row r is stored at position gr ^ tile16_swizzle<D>(r).  Within
+// each 16-lane group this spreads both reads of the tile over distinct banks
+// (checked exhaustively for d = 64 and 128): the row read, lane (c, g) taking
+// granule 4m + g of row c, and the transpose read, lane 4r + q of group g
+// supplying 8 bytes of granule 4m + q of row 4g + r.  Lanes of different groups
+// served in the same cycle can still meet: every lane of a transpose read takes
+// the same 8-byte half of its granule, so 32 lanes reach only half the banks (a
+// 2-way conflict that no granule permutation removes).
 template <int D>
 __device__ __forceinline__ int tile16_swizzle(int row)
 {
