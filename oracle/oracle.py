@@ -11,6 +11,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ttt_oracle.c")
 _LIB = os.path.join(_HERE, "libttt_oracle.so")
+# a prebuilt oracle library to load instead (the mutation tests point this at
+# copies of the oracle with a planted mistake)
+_LIB_OVERRIDE = os.environ.get("TTT_ORACLE_LIB")
 _lib = None
 
 
@@ -32,9 +35,12 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        lib = ctypes.CDLL(_LIB)
+        if _LIB_OVERRIDE:
+            lib = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
         P = ctypes.POINTER(ctypes.c_double)
         lib.ttt_oracle_linear.argtypes = [P, P, P, P, ctypes.c_double, P, P, P,
                                           ctypes.c_int, ctypes.c_int, ctypes.c_int,
