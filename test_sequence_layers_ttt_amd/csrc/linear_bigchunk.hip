@@ -33,10 +33,14 @@ constexpr int kKStep = 32;   // tokens per contraction step of kernel A
 // Kernel A.  One workgroup (d/16 waves) per (batch*head, chunk).  Per 32-token
 // step the K and V rows are staged in LDS as row-major 16 x 16 bf16 blocks
 // (block (token group, feature block)); the transpose read then yields operands
-// with features in the lanes and tokens in the slots.  Wave w owns input block
-// i = w: P tiles (w, j) for all j and B tiles (w, o) for all o.
+// with features in the lanes and tokens in the slots.
 //   P tile:  D[i][j] = sum_s (eta K)[s][i] K[s][j]   -> lane j, rows i
 //   B tile:  D[i][o] = sum_s K[s][i] (eta V)[s][o]   -> lane o, rows i
+// Wave w owns input blocks i = 2 (w % (d/32)) + {0, 1} against output blocks
+// j = (d/32) (w / (d/32)) + {0 .. d/32 - 1}: eight tiles of P and eight of B at
+// d = 128, read through two A operands and d/16 B operands per step.  With a
+// scalar eta, K itself is the A operand of both products (eta is applied at
+// the end); per-token eta stages eta*K and eta*V as well.
 // P is symmetric, so the tile's lane-j column is stored as row j of P; B's
 // lane-o column is row o of B = V diag(eta) K^T.
 // ---------------------------------------------------------------------------
@@ -47,16 +51,18 @@ __global__ __launch_bounds__(64 * (D / 16)) void bigchunk_gram_kernel(
     float* __restrict__ Bout, int T, int chunk, int nchunks)
 {
     constexpr int NB = D / 16;
-    constexpr int NT = 64 * NB;                 // threads
+    constexpr int NH = NB / 2;                  // output blocks per wave
     constexpr int BLK = 64;                     // u32x2 per 16 x 16 block
     constexpr int TILE = 2 * NB * BLK;          // u32x2 per 32-token tile
-    // [buffer][K, eta*K, eta*V][tile]
-    __shared__ u32x2 lds[2][3][TILE];
+    constexpr int NT = ETA_TOKEN ? 3 : 2;       // staged tiles: K, (eta K,) V or eta V
+    constexpr int TK = 0, TEK = ETA_TOKEN ? 1 : 0, TV = NT - 1;
+    __shared__ u32x2 lds[2][NT][TILE];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
+    const int i0 = 2 * (w % NH), j0 = NH * (w / NH);   // input blocks i0, i0+1; outputs j0..
     const int unit = blockIdx.x;
     const int slice = unit / nchunks, ci = unit % nchunks;
     const size_t t0 = (size_t)slice * T + (size_t)ci * chunk;
@@ -86,14 +92,16 @@ __global__ __launch_bounds__(64 * (D / 16)) void bigchunk_gram_kernel(
         return r;
     };
     auto store = [&](int buf, u32x4 kv, u32x4 vv, float e) {
-        lds[buf][0][loff] = lo_half(kv);
-        lds[buf][0][loff + 1] = hi_half(kv);
-        const u32x4 ek = ETA_TOKEN ? scale(kv, e) : kv;
+        lds[buf][TK][loff] = lo_half(kv);
+        lds[buf][TK][loff + 1] = hi_half(kv);
+        if (ETA_TOKEN) {
+            const u32x4 ek = scale(kv, e);
+            lds[buf][TEK][loff] = lo_half(ek);
+            lds[buf][TEK][loff + 1] = hi_half(ek);
+        }
         const u32x4 ev = ETA_TOKEN ? scale(vv, e) : vv;
-        lds[buf][1][loff] = lo_half(ek);
-        lds[buf][1][loff + 1] = hi_half(ek);
-        lds[buf][2][loff] = lo_half(ev);
-        lds[buf][2][loff + 1] = hi_half(ev);
+        lds[buf][TV][loff] = lo_half(ev);
+        lds[buf][TV][loff + 1] = hi_half(ev);
     };
     // x32 operand of feature block `fb` from tile `which`: slots 0..3 = tokens
     // 4g..4g+3, slots 4..7 = tokens 16+4g..16+4g+3
@@ -105,9 +113,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void bigchunk_gram_kernel(
         return u32x4{a.x, a.y, b.x, b.y};
     };
 
-    f32x4 Pacc[NB], Bacc[NB];
+    f32x4 Pacc[2][NH], Bacc[2][NH];
 #pragma unroll
-    for (int j = 0; j < NB; ++j) Pacc[j] = Bacc[j] = f32x4{0, 0, 0, 0};
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < NH; ++jj) Pacc[ii][jj] = Bacc[ii][jj] = f32x4{0, 0, 0, 0};
 
     u32x4 kv, vv;
     float e;
@@ -118,14 +128,21 @@ __global__ __launch_bounds__(64 * (D / 16)) void bigchunk_gram_kernel(
         const int buf = st & 1;
         const bool next = st + 1 < nsteps;
         if (next) load(st + 1, kv, vv, e);
-        const u32x4 aK = operand(buf, 1, w);    // (eta K)^T, input block w
-        const u32x4 aKp = operand(buf, 0, w);   // K^T, input block w
+        u32x4 aK[2], aKp[2];   // (eta K)^T and K^T of input blocks i0, i0+1
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const u32x4 bK = operand(buf, 0, j);
-            const u32x4 bV = operand(buf, 2, j);
-            Pacc[j] = mfma32(aK, bK, Pacc[j]);
-            Bacc[j] = mfma32(aKp, bV, Bacc[j]);
+        for (int ii = 0; ii < 2; ++ii) {
+            aKp[ii] = operand(buf, TK, i0 + ii);
+            aK[ii] = ETA_TOKEN ? operand(buf, TEK, i0 + ii) : aKp[ii];
+        }
+#pragma unroll
+        for (int jj = 0; jj < NH; ++jj) {
+            const u32x4 bK = operand(buf, TK, j0 + jj);
+            const u32x4 bV = operand(buf, TV, j0 + jj);
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+                Pacc[ii][jj] = mfma32(aK[ii], bK, Pacc[ii][jj]);
+                Bacc[ii][jj] = mfma32(aKp[ii], bV, Bacc[ii][jj]);
+            }
         }
         if (next) store(buf ^ 1, kv, vv, e);
         __syncthreads();
@@ -135,11 +152,14 @@ __global__ __launch_bounds__(64 * (D / 16)) void bigchunk_gram_kernel(
     uint16_t* P = Pout + (size_t)unit * D * D;
     float* B = Bout + (size_t)unit * D * D;
 #pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        // lane (j', g): rows i = 16w + 4g + r of column 16j + j'
-        *(u32x2*)(P + (size_t)(16 * j + c) * D + 16 * w + 4 * g) = pack_bf16x4(Pacc[j] * sc);
-        *(f32x4*)(B + (size_t)(16 * j + c) * D + 16 * w + 4 * g) = Bacc[j] * sc;
-    }
+    for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+        for (int jj = 0; jj < NH; ++jj) {
+            // lane (j', g): rows i = 16 i + 4g + r of column 16 j + j'
+            const int i = i0 + ii, j = j0 + jj;
+            *(u32x2*)(P + (size_t)(16 * j + c) * D + 16 * i + 4 * g) = pack_bf16x4(Pacc[ii][jj] * sc);
+            *(f32x4*)(B + (size_t)(16 * j + c) * D + 16 * i + 4 * g) = Bacc[ii][jj] * sc;
+        }
 }
 
 // ---------------------------------------------------------------------------
