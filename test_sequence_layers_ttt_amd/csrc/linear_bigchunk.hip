@@ -272,16 +272,17 @@ __global__ __launch_bounds__(64) void bigchunk_chain_kernel(
 // eta modes of kernel C: scalar, per-token single loads, per-token 16-byte loads
 enum { kSegEtaScalar = 0, kSegEtaToken = 1, kSegEtaToken4 = 2 };
 
-template <int D, int ETA, bool FULL>
-__global__ __launch_bounds__(4 * D) void bigchunk_seg_kernel(
+template <int D, int ETA, bool FULL, int RB>
+__global__ __launch_bounds__(4 * D / RB) void bigchunk_seg_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
     const float* __restrict__ Wstart, uint16_t* __restrict__ Z, int T, int chunk, int nseg)
 {
     constexpr int NB = D / 16;
     constexpr int NM = D / 32;
-    constexpr int G = D / 8;    // 16-byte granules per row
-    constexpr int P = 8;        // sub-tiles in flight per thread
+    constexpr int G = D / 8;           // 16-byte granules per row
+    constexpr int NTH = 4 * D / RB;    // threads; each stages RB granules per sub-tile
+    constexpr int P = RB == 1 ? 8 : 4; // sub-tiles in flight per thread
     __shared__ KQTile16<D> L[2];
 
     const int tid = threadIdx.x;
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(4 * D) void bigchunk_seg_kernel(
     const int nc = min(chunk, T - t0);          // tokens in this chunk
     const int ntile = (nc + 15) / 16;
     const size_t tok0 = (size_t)slice * T + t0;
-    const int out0 = 16 * wave;
+    const int out0 = 16 * RB * wave;            // first state row of this wave
     // token of row r of sub-tile tau, clamped into the chunk (clamped rows are
     // re-reads whose tokens get eta = 0 and no store)
     auto tok = [&](int tau, int r) {
@@ -302,18 +303,23 @@ __global__ __launch_bounds__(4 * D) void bigchunk_seg_kernel(
         return FULL ? t : (t < nc ? t : nc - 1);
     };
 
-    // this thread's granule of each staged sub-tile: K for the first half of
-    // the workgroup, Q for the second
-    const int which = tid / (16 * G);
-    const int grow = (tid / G) & 15, ggr = tid % G;
-    const uint16_t* src = which ? Q : K;
-    const int lpos = grow * G + (ggr ^ tile16_swizzle<D>(grow));
-    auto gload = [&](int tau) {
-        return *(const u32x4*)(src + (tok0 + tok(tau, grow)) * D + 8 * ggr);
+    // this thread's granules of each staged sub-tile (K granules first, then Q)
+    int which[RB], grow[RB], ggr[RB], lpos[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const int gi = tid + r * NTH;
+        which[r] = gi / (16 * G);
+        grow[r] = (gi / G) & 15;
+        ggr[r] = gi % G;
+        lpos[r] = grow[r] * G + (ggr[r] ^ tile16_swizzle<D>(grow[r]));
+    }
+    auto gload = [&](int tau, int r) {
+        const uint16_t* src = which[r] ? Q : K;
+        return *(const u32x4*)(src + (tok0 + tok(tau, grow[r])) * D + 8 * ggr[r]);
     };
-    // this lane's V (tokens c, features out0 + 4g ..) and eta (tokens 4g .. 4g+3)
-    auto vload = [&](int tau) {
-        return *(const u32x2*)(V + (tok0 + tok(tau, c)) * D + out0 + 4 * g);
+    // this lane's V (token c, features out0 + 16 rb + 4g ..) and eta (tokens 4g ..)
+    auto vload = [&](int tau, int rb) {
+        return *(const u32x2*)(V + (tok0 + tok(tau, c)) * D + out0 + 16 * rb + 4 * g);
     };
     auto eload = [&](int tau) {
         if (ETA == kSegEtaToken4) {
@@ -330,31 +336,38 @@ __global__ __launch_bounds__(4 * D) void bigchunk_seg_kernel(
     };
 
     // chunk-start state rows of this wave: fp32 running M and bf16 copies
-    f32x4 M[NB];
-    {
-        const float* w = Wstart + ((size_t)slice * nseg + seg) * D * D + (size_t)(out0 + c) * D;
+    f32x4 M[RB][NB];
+    u32x4 Wf[RB][NM], Mf[RB][NM];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const float* w = Wstart + ((size_t)slice * nseg + seg) * D * D +
+                         (size_t)(out0 + 16 * rb + c) * D;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            M[2 * m] = *(const f32x4*)(w + 32 * m + 8 * g);
-            M[2 * m + 1] = *(const f32x4*)(w + 32 * m + 8 * g + 4);
+            M[rb][2 * m] = *(const f32x4*)(w + 32 * m + 8 * g);
+            M[rb][2 * m + 1] = *(const f32x4*)(w + 32 * m + 8 * g + 4);
+            Wf[rb][m] = Mf[rb][m] = pack_bf16x8(M[rb][2 * m], M[rb][2 * m + 1]);
         }
     }
-    u32x4 Wf[NM], Mf[NM];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) Wf[m] = Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
     const u32x2 I16 = identity_b16(lane);
 
-    u32x4 rg[P];
-    u32x2 rv[P];
+    u32x4 rg[P][RB];
+    u32x2 rv[P][RB];
     f32x4 re[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        rg[p] = gload(p);
-        rv[p] = vload(p);
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            rg[p][r] = gload(p, r);
+            rv[p][r] = vload(p, r);
+        }
         re[p] = eload(p);
     }
-    L[0].g[which][lpos] = rg[0];
-    rg[0] = gload(P);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        L[0].g[which[r]][lpos[r]] = rg[0][r];
+        rg[0][r] = gload(P, r);
+    }
     __syncthreads();
 
     // one sub-tile; p = tau % P is a compile-time ring position
@@ -362,9 +375,12 @@ __global__ __launch_bounds__(4 * D) void bigchunk_seg_kernel(
         constexpr int p = decltype(pc)::value;
         constexpr int p1 = (p + 1) % P;
         const int sl = tau & 1;
-        // stage the next sub-tile, refill its register slot
-        if (tau + 1 < ntile) L[sl ^ 1].g[which][lpos] = rg[p1];
-        rg[p1] = gload(tau + 1 + P);
+        // stage the next sub-tile, refill its register slots
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            if (tau + 1 < ntile) L[sl ^ 1].g[which[r]][lpos[r]] = rg[p1][r];
+            rg[p1][r] = gload(tau + 1 + P, r);
+        }
 
         const u32x4* Kt = L[sl].g[0];
         const u32x4* Qt = L[sl].g[1];
@@ -398,12 +414,7 @@ __global__ __launch_bounds__(4 * D) void bigchunk_seg_kernel(
             et.z = (4 * g + 2 < n) ? et.z : 0.f;
             et.w = (4 * g + 3 < n) ? et.w : 0.f;
         }
-        // E = K W_c^T - V (tokens in the rows, this wave's outputs in the lanes)
-        f32x4 Et = mfma16(rv[p] ^ u32x2{0x80008000u, 0x80008000u}, I16, f32x4{0, 0, 0, 0});
-#pragma unroll
-        for (int m = 0; m < NM; ++m) Et = mfma32(kop[m], Wf[m], Et);
-        const u32x2 F = pack_bf16x4(-et * Et);
-        // causal scores S[s][t] = k_s . q_t for s <= t
+        // causal scores S[s][t] = k_s . q_t for s <= t (shared by the row blocks)
         f32x4 St = {0, 0, 0, 0};
 #pragma unroll
         for (int m = 0; m < NM; ++m) St = mfma32(kop[m], qop[m], St);
@@ -412,19 +423,30 @@ __global__ __launch_bounds__(4 * D) void bigchunk_seg_kernel(
         Sm.y = (4 * g + 1 <= c) ? St.y : 0.f;
         Sm.z = (4 * g + 2 <= c) ? St.z : 0.f;
         Sm.w = (4 * g + 3 <= c) ? St.w : 0.f;
-        // Z = Q M^T + S^T-weighted F (outputs in the rows, tokens in the lanes)
-        f32x4 Zt = {0, 0, 0, 0};
+        const u32x2 Sb = pack_bf16x4(Sm);
 #pragma unroll
-        for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[m], qop[m], Zt);
-        Zt = mfma16(F, pack_bf16x4(Sm), Zt);
-        if (FULL || c < n)
-            *(u32x2*)(Z + (tok0 + 16 * tau + c) * D + out0 + 4 * g) = pack_bf16x4(Zt);
-        // M += F^T K
+        for (int rb = 0; rb < RB; ++rb) {
+            // E = K W_c^T - V (tokens in the rows, this block's outputs in the lanes)
+            f32x4 Et = mfma16(rv[p][rb] ^ u32x2{0x80008000u, 0x80008000u}, I16,
+                              f32x4{0, 0, 0, 0});
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) M[jb] = mfma16(kt[jb], F, M[jb]);
+            for (int m = 0; m < NM; ++m) Et = mfma32(kop[m], Wf[rb][m], Et);
+            const u32x2 F = pack_bf16x4(-et * Et);
+            // Z = Q M^T + S^T-weighted F (outputs in the rows, tokens in the lanes)
+            f32x4 Zt = {0, 0, 0, 0};
 #pragma unroll
-        for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
-        rv[p] = vload(tau + P);
+            for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[rb][m], qop[m], Zt);
+            Zt = mfma16(F, Sb, Zt);
+            if (FULL || c < n)
+                *(u32x2*)(Z + (tok0 + 16 * tau + c) * D + out0 + 16 * rb + 4 * g) =
+                    pack_bf16x4(Zt);
+            // M += F^T K
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) M[rb][jb] = mfma16(kt[jb], F, M[rb][jb]);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) Mf[rb][m] = pack_bf16x8(M[rb][2 * m], M[rb][2 * m + 1]);
+            rv[p][rb] = vload(tau + P, rb);
+        }
         re[p] = eload(tau + P);
         __syncthreads();
     };
@@ -435,25 +457,36 @@ __global__ __launch_bounds__(4 * D) void bigchunk_seg_kernel(
         step(tau0 + 1, std::integral_constant<int, 1>{});
         step(tau0 + 2, std::integral_constant<int, 2>{});
         step(tau0 + 3, std::integral_constant<int, 3>{});
-        step(tau0 + 4, std::integral_constant<int, 4>{});
-        step(tau0 + 5, std::integral_constant<int, 5>{});
-        step(tau0 + 6, std::integral_constant<int, 6>{});
-        step(tau0 + 7, std::integral_constant<int, 7>{});
+        if constexpr (P == 8) {
+            step(tau0 + 4, std::integral_constant<int, 4 % P>{});
+            step(tau0 + 5, std::integral_constant<int, 5 % P>{});
+            step(tau0 + 6, std::integral_constant<int, 6 % P>{});
+            step(tau0 + 7, std::integral_constant<int, 7 % P>{});
+        }
     }
     if (tau0 + 0 < ntile) step(tau0 + 0, std::integral_constant<int, 0>{});
     if (tau0 + 1 < ntile) step(tau0 + 1, std::integral_constant<int, 1>{});
     if (tau0 + 2 < ntile) step(tau0 + 2, std::integral_constant<int, 2>{});
-    if (tau0 + 3 < ntile) step(tau0 + 3, std::integral_constant<int, 3>{});
-    if (tau0 + 4 < ntile) step(tau0 + 4, std::integral_constant<int, 4>{});
-    if (tau0 + 5 < ntile) step(tau0 + 5, std::integral_constant<int, 5>{});
-    if (tau0 + 6 < ntile) step(tau0 + 6, std::integral_constant<int, 6>{});
+    if constexpr (P == 8) {
+        if (tau0 + 3 < ntile) step(tau0 + 3, std::integral_constant<int, 3>{});
+        if (tau0 + 4 < ntile) step(tau0 + 4, std::integral_constant<int, 4 % P>{});
+        if (tau0 + 5 < ntile) step(tau0 + 5, std::integral_constant<int, 5 % P>{});
+        if (tau0 + 6 < ntile) step(tau0 + 6, std::integral_constant<int, 6 % P>{});
+    }
 }
+
+#ifndef SEG_RB
+#define SEG_RB 2
+#endif
 
 template <int D, int ETA, bool FULL>
 void launch_seg(const LinearArgs& a, const float* Wc, int nchunks, hipStream_t s)
 {
-    hipLaunchKernelGGL((bigchunk_seg_kernel<D, ETA, FULL>), dim3((unsigned)(a.BH * nchunks)),
-                       dim3(4 * D), 0, s, (const uint16_t*)a.K, (const uint16_t*)a.Q,
+    // two 16-row state blocks per wave: one wave per SIMD, each K/Q operand and
+    // score serving both blocks
+    constexpr int RB = SEG_RB;
+    hipLaunchKernelGGL((bigchunk_seg_kernel<D, ETA, FULL, RB>), dim3((unsigned)(a.BH * nchunks)),
+                       dim3(4 * D / RB), 0, s, (const uint16_t*)a.K, (const uint16_t*)a.Q,
                        (const uint16_t*)a.V, a.eta, a.eta_scalar, Wc, (uint16_t*)a.Z, a.T, a.chunk,
                        nchunks);
 }
