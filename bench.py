@@ -31,9 +31,12 @@ METRIC = "TTT scan tokens/sec (all heads) + % of HBM/MFMA roofline, b=16 d=64"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFS = 2500.0           # MI355X dense bf16 MFMA
 PLANS = {"auto": 0, "generic": 1, "mfma": 2, "bigchunk": 3}
-KERNEL_SOURCES = {"linear": ["linear_mfma.hip", "linear_generic.hip", "linear_bigchunk.hip",
-                             "mfma_common.h"],
-                  "mlp": ["mlp_mfma.hip", "mlp_generic.hip", "mfma_common.h"]}
+# sources whose change invalidates a stored counter profile (kernels and dispatch)
+KERNEL_SOURCES = {"linear": ["linear_mfma.hip", "linear_coop.hip", "linear_generic.hip",
+                             "linear_bigchunk.hip", "mfma_common.h", "device_common.h",
+                             "launch.h", "api.cpp"],
+                  "mlp": ["mlp_mfma.hip", "mlp_generic.hip", "mfma_common.h", "device_common.h",
+                          "launch.h", "api.cpp"]}
 
 
 def log(*a):

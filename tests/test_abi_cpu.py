@@ -134,3 +134,15 @@ def test_binding_refuses_host_tensors():
     K = torch.zeros(1, 1, 16, 16)
     with pytest.raises(ValueError):
         ttt.linear_fwd(K, K, K, None, torch.zeros(1, 1, 16, 16), 16, 0.1)
+
+
+def test_profile_hash_covers_every_kernel_source():
+    """bench.py invalidates stored counter profiles through a hash of the kernel
+    sources; every file under csrc/ must be part of one of the hashed lists."""
+    import glob
+    import bench
+    csrc = os.path.join(ROOT, "test_sequence_layers_ttt_amd", "csrc")
+    files = {os.path.basename(p) for p in glob.glob(os.path.join(csrc, "*"))
+             if p.endswith((".hip", ".h", ".cpp"))}
+    hashed = set(bench.KERNEL_SOURCES["linear"]) | set(bench.KERNEL_SOURCES["mlp"])
+    assert files <= hashed, sorted(files - hashed)
