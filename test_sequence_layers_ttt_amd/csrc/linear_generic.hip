@@ -61,31 +61,54 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(
     }
     __syncthreads();
 
-    for (int c0 = 0; c0 < T; c0 += chunk) {
+    // Sub-tiles are walked in order (chunk by chunk); each thread holds its
+    // elements of the next sub-tile in registers, loaded while the current one
+    // is computed.
+    constexpr int kPer = kTile * kMaxD / 256;   // K/Q elements per thread (d <= 128)
+    auto next_tile = [&](int c0, int s0, int& nc0, int& ns0) {   // sub-tile after (c0, s0)
         const int c1 = min(T, c0 + chunk);
-        for (int s0 = c0; s0 < c1; s0 += kTile) {
-            const int n = min(kTile, c1 - s0);
-            // ---- stage the sub-tile (zeros past its last token) ----
-            for (int idx = tid; idx < kTile * d; idx += 256) {
-                int i = idx / d, j = idx % d;
-                float kv = 0.f, qv = 0.f;
-                if (i < n) {
-                    size_t off = (tok0 + s0 + i) * d + j;
-                    kv = io<TIO>::load(K, off);
-                    qv = io<TIO>::load(Q, off);
-                }
-                sK[i][j] = kv;
-                sQ[i][j] = qv;
+        if (s0 + kTile < c1) { nc0 = c0; ns0 = s0 + kTile; }
+        else { nc0 = c1; ns0 = c1; }
+    };
+    float rk[kPer], rq[kPer], rv, re;
+    auto load_tile = [&](int c0, int s0) {
+        const int n = s0 < T ? min(kTile, min(T, c0 + chunk) - s0) : 0;
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const int idx = tid + 256 * e;
+            const int i = idx / d, j = idx % d;
+            rk[e] = rq[e] = 0.f;
+            if (idx < kTile * d && i < n) {
+                const size_t off = (tok0 + s0 + i) * d + j;
+                rk[e] = io<TIO>::load(K, off);
+                rq[e] = io<TIO>::load(Q, off);
             }
-            {
-                int i = tid / kRows, r = tid % kRows;
-                float vv = 0.f;
-                if (i < n && r < R) vv = io<TIO>::load(V, (tok0 + s0 + i) * d + r0 + r);
-                sV[i][r] = vv;
+        }
+        const int i = tid / kRows, r = tid % kRows;
+        rv = (i < n && r < R) ? io<TIO>::load(V, (tok0 + s0 + i) * d + r0 + r) : 0.f;
+        re = (tid < n) ? (eta ? eta[tok0 + s0 + tid] : eta_scalar) : 0.f;
+    };
+    int c0 = 0, s0 = 0;
+    load_tile(0, 0);
+    while (s0 < T) {
+        const int c1 = min(T, c0 + chunk);
+        const int n = min(kTile, c1 - s0);
+        // ---- stage the sub-tile (zeros past its last token) ----
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const int idx = tid + 256 * e;
+            if (idx < kTile * d) {
+                sK[idx / d][idx % d] = rk[e];
+                sQ[idx / d][idx % d] = rq[e];
             }
-            if (tid < kTile) sEta[tid] = (tid < n) ? (eta ? eta[tok0 + s0 + tid] : eta_scalar) : 0.f;
-            __syncthreads();
-
+        }
+        sV[tid / kRows][tid % kRows] = rv;
+        if (tid < kTile) sEta[tid] = re;
+        __syncthreads();
+        int nc0, ns0;
+        next_tile(c0, s0, nc0, ns0);
+        load_tile(nc0, ns0);
+        {
             // ---- E = W_c K - V  and  S = triu(K^T Q) ----
             {
                 int r = tid / kTile, s = tid % kTile;
@@ -126,12 +149,16 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(
             }
             __syncthreads();
         }
-        // chunk end: the running state becomes the next chunk-start state
-        for (int idx = tid; idx < R * d; idx += 256) {
-            int r = idx / d, j = idx % d;
-            sWs[r][j] = sM[r][j];
+        if (s0 + kTile >= c1) {
+            // chunk end: the running state becomes the next chunk-start state
+            for (int idx = tid; idx < R * d; idx += 256) {
+                int r = idx / d, j = idx % d;
+                sWs[r][j] = sM[r][j];
+            }
+            __syncthreads();
         }
-        __syncthreads();
+        c0 = nc0;
+        s0 = ns0;
     }
 
     for (int idx = tid; idx < R * d; idx += 256) {
