@@ -475,16 +475,13 @@ __global__ __launch_bounds__(4 * D / RB) void bigchunk_seg_kernel(
     }
 }
 
-#ifndef SEG_RB
-#define SEG_RB 2
-#endif
 
 template <int D, int ETA, bool FULL>
 void launch_seg(const LinearArgs& a, const float* Wc, int nchunks, hipStream_t s)
 {
     // two 16-row state blocks per wave: one wave per SIMD, each K/Q operand and
     // score serving both blocks
-    constexpr int RB = SEG_RB;
+    constexpr int RB = 2;
     hipLaunchKernelGGL((bigchunk_seg_kernel<D, ETA, FULL, RB>), dim3((unsigned)(a.BH * nchunks)),
                        dim3(4 * D / RB), 0, s, (const uint16_t*)a.K, (const uint16_t*)a.Q,
                        (const uint16_t*)a.V, a.eta, a.eta_scalar, Wc, (uint16_t*)a.Z, a.T, a.chunk,

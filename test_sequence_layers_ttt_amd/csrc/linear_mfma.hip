@@ -408,18 +408,14 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
     }
 }
 
-#ifndef CHAIN_PF
-#define CHAIN_PF 8
-#endif
-#ifndef COOP_MIN_UNITS
-#define COOP_MIN_UNITS 256
-#endif
-#ifndef CHAIN_PF_WIDE
-#define CHAIN_PF_WIDE 4
-#endif
-#ifndef CHAIN_RB2_UNITS
-#define CHAIN_RB2_UNITS 256
-#endif
+// Launch choices, all measured on MI355X (256 compute units):
+//  - prefetch depth of the chunk-16 kernel: 8 chunks (1x32 heads x 32768 tokens:
+//    605 -> 438 us against 4), 4 where the registers do not allow 8;
+//  - past 256 (head, 16-row block) units, the shared-tile kernel (d = 64, 128)
+//    or two row blocks per wave take over from one wave per unit.
+constexpr int kChainPrefetch = 8;
+constexpr int kChainPrefetchWide = 4;
+constexpr long kComputeUnits = 256;
 
 // Chunks of several 16-token sub-tiles (E keeps the frozen chunk-start state).
 template <int D, int WPB, int ETA, bool FULL>
@@ -437,7 +433,7 @@ template <int D, int RB, int ETA, bool FULL>
 void launch_chain(const LinearArgs& a, hipStream_t s)
 {
     // prefetch depth: 8 chunks where the registers allow it (d = 128 keeps 4)
-    constexpr int PF = D * RB <= 64 ? CHAIN_PF : CHAIN_PF_WIDE;
+    constexpr int PF = D * RB <= 64 ? kChainPrefetch : kChainPrefetchWide;
     const int units = (a.BH + 7) / 8 * 8;
     dim3 grid((unsigned)(units * (D / 16) / RB)), block(64);
     hipLaunchKernelGGL((linear_mfma_chain_kernel<D, PF, 1, RB, ETA, FULL>), grid, block, 0, s,
@@ -454,7 +450,7 @@ void launch_wpb(const LinearArgs& a, hipStream_t s)
         // compute unit slows both by 1.5-2x, so once the 16-row units outnumber
         // the 256 compute units a wave takes two of them (d <= 64).
         if constexpr (D <= 64) {
-            if (units > CHAIN_RB2_UNITS) {
+            if (units > kComputeUnits) {
                 launch_chain<D, 2, ETA, FULL>(a, s);
                 return;
             }
@@ -498,7 +494,7 @@ hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s)
     // and 128 go to one workgroup per head that fetches K and Q once for all of
     // its waves (8x12 heads at d = 64: 49 us vs 52 us; at 32 heads, where every
     // unit has a compute unit to itself, the single-wave kernel is faster).
-    if ((long)a.BH * (a.d / 16) > COOP_MIN_UNITS && linear_coop_supported(a.d, a.chunk, a.bf16))
+    if ((long)a.BH * (a.d / 16) > kComputeUnits && linear_coop_supported(a.d, a.chunk, a.bf16))
         return launch_linear_coop(a, s);
     switch (a.d) {
     case 32: return launch_d<32>(a, s);
