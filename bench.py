@@ -11,6 +11,10 @@ to stderr.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--plan auto|generic|mfma|bigchunk]
                   [--no-cpu-baseline] [--copy-calibration BYTES]
+
+With --decode N one step is instead one ttt_linear_step call that continues
+every (batch, head) sequence of the workload by N tokens from its carried state
+(decode).  The states rotate over >= 1 GiB of copies, so they come from HBM.
 """
 from __future__ import annotations
 
@@ -36,7 +40,9 @@ KERNEL_SOURCES = {"linear": ["linear_mfma.hip", "linear_coop.hip", "linear_gener
                              "linear_bigchunk.hip", "mfma_common.h", "device_common.h",
                              "launch.h", "api.cpp"],
                   "mlp": ["mlp_mfma.hip", "mlp_generic.hip", "mfma_common.h", "device_common.h",
-                          "launch.h", "api.cpp"]}
+                          "launch.h", "api.cpp"],
+                  "step": ["linear_step.hip", "device_common.h", "launch.h", "api.cpp"]}
+DECODE_METRIC = "TTT-Linear decode tokens/sec (all heads) + % of HBM roofline"
 
 
 def log(*a):
@@ -94,6 +100,113 @@ def traffic_from_profiles(wl, plan_name):
     return rec.get("hbm_bytes_per_launch")
 
 
+def decode_bytes(wl, n: int) -> float:
+    """Bytes one decode call must move: the carried pair (W_chunk, G) read and G
+    written (fp32), W_chunk written by the calls in which a chunk completes (a
+    fraction min(1, n / chunk) of them), n tokens of K, Q, V read and Z written,
+    eta read."""
+    esz = 2 if wl.io == "bf16" else 4
+    per_tok = 4 * wl.d * esz + (4 if wl.eta_mode == "token" else 0)
+    state = wl.d * wl.d * 4
+    return float(wl.BH) * ((3.0 + min(1.0, n / wl.chunk)) * state + n * per_tok)
+
+
+def decode_main(args, wl, x):
+    """Decode: each call continues every sequence by n tokens.  The calls are
+    captured once in a HIP graph (one per state copy) and the graph is replayed,
+    so the events time the GPU rather than the host's launch rate."""
+    import torch
+    from test_sequence_layers_ttt_amd import ttt
+    dev = torch.device("cuda:0")
+    n = args.decode
+    B, H, T, d = wl.B, wl.H, wl.T, wl.d
+    io = torch.bfloat16 if wl.io == "bf16" else torch.float32
+
+    def dev_t(a, shape, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).reshape(shape).to(dt).contiguous()
+
+    seq = {k: dev_t(x[k], (B, H, T, d), io) for k in ("K", "Q", "V")}
+    seq["eta"] = None if x["eta"] is None else dev_t(x["eta"], (B, H, T))
+    # token groups [g*n, (g+1)*n) of the sequences, each a contiguous [B, H, n, d]
+    ngroups = max(1, min(64, T // n))
+    groups = []
+    for g in range(ngroups):
+        sl = slice(g * n, (g + 1) * n)
+        groups.append({k: (None if v is None else v[:, :, sl].contiguous())
+                       for k, v in seq.items()})
+    W0 = dev_t(x["W0"], (B, H, d, d))
+    state_bytes = 2 * W0.numel() * 4
+    ncopies = max(1, min(1024, int(math.ceil(args.rotate_bytes / state_bytes))))
+    states = [(W0.clone(), torch.zeros_like(W0)) for _ in range(ncopies)]
+    pos = [0] * ncopies
+    Z = torch.empty((B, H, n, d), dtype=io, device=dev)
+    log("decode: %d tokens per call, %d state copies of %.1f MB" % (
+        n, ncopies, state_bytes / 1e6))
+
+    def call(i, stream):
+        c = i % ncopies
+        g = groups[(i // ncopies) % ngroups]
+        Wc, G = states[c]
+        _, pos[c] = ttt.linear_step(g["K"], g["Q"], g["V"], g["eta"], Wc, G, pos[c], wl.chunk,
+                                    eta_scalar=x["eta_scalar"], Z=Z, stream=stream)
+
+    # eager calls first (they also advance every copy to a mid-chunk position)
+    stream = torch.cuda.current_stream(dev)
+    for i in range(max(args.warmup, ncopies)):
+        call(i, stream)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream(dev)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cap):
+        for c in range(ncopies):
+            call(c, cap)
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // ncopies)
+    graph.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    calls = reps * ncopies
+    ms_event = ev0.elapsed_time(ev1) / calls
+    ms_step = wall * 1e3 / calls
+    log("timed %d decode calls in %d graph replays: %.5f ms/call (events), %.5f ms/call "
+        "(wall)" % (calls, reps, ms_event, ms_step))
+    abytes = decode_bytes(wl, n)
+    gbs = abytes / (ms_event * 1e-3) / 1e9
+    rec = {
+        "metric": DECODE_METRIC,
+        "value": round(B * n / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": calls,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name + "_decode%d" % n, "scan": "ttt_linear_step",
+                   "batch": B, "heads": H, "tokens_per_call": n, "head_dim": d,
+                   "chunk": wl.chunk, "io": wl.io, "state_dtype": "f32",
+                   "launch": "hip_graph", "parallelism": "single_gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_ms": round(ms_event, 5), "algorithmic_bytes": abytes},
+        # the oracle's per-token cost is the scan's; its baseline is the scan line's
+        "cpu_baseline": None,
+        "parity": None,
+        "head_tokens_per_s": round(B * H * n / (ms_step * 1e-3), 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def copy_calibration(nbytes: int, steps: int):
     """A plain device copy of known size, for scaling the FETCH_SIZE/WRITE_SIZE
     counters (run under rocprofv3 --pmc)."""
@@ -119,6 +232,10 @@ def main():
                     help="slices the oracle times (0 = pick a bounded sample)")
     ap.add_argument("--rotate-bytes", type=float, default=float(1 << 30))
     ap.add_argument("--copy-calibration", type=int, default=0)
+    ap.add_argument("--decode", type=int, default=0,
+                    help="time ttt_linear_step continuing every sequence by N tokens")
+    ap.add_argument("--decode-batch", type=int, default=0,
+                    help="batch size of the decode line (default: the workload's)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -135,6 +252,13 @@ def main():
 
     wl = inputs.WORKLOADS[args.workload]
     seed = inputs.WORKLOAD_SEEDS[wl.name]
+    if args.decode:
+        if wl.model != "linear" or args.decode > wl.T:
+            raise SystemExit("--decode needs a TTT-Linear workload with T >= N")
+        # a decode call reads only its own n tokens: generate the first few groups
+        wl = wl.with_(T=min(wl.T, 64 * args.decode), B=args.decode_batch or wl.B)
+        decode_main(args, wl, inputs.make_inputs(wl, seed))
+        return
     dev = torch.device("cuda:0")
     plan_req = PLANS[args.plan]
     io_code = ttt.DTYPE_BF16 if wl.io == "bf16" else ttt.DTYPE_F32

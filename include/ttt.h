@@ -82,8 +82,10 @@ typedef enum {
 typedef enum {
     TTT_PLAN_AUTO = 0,
     TTT_PLAN_GENERIC = 1,       /* fp32 vector ALU, any chunk, fp32 or bf16 I/O */
-    TTT_PLAN_MFMA = 2,          /* bf16 matrix cores, chunk <= 16 or a multiple of 16 <= 64 */
-    TTT_PLAN_BIGCHUNK = 3       /* bf16 matrix cores, three stages, chunk a multiple of 64 >= 128 */
+    TTT_PLAN_MFMA = 2,          /* bf16 matrix cores, d in {32, 64, 128}, chunk <= 16 or a
+                                   multiple of 16 */
+    TTT_PLAN_BIGCHUNK = 3       /* bf16 matrix cores, three stages, d in {64, 128}, chunk a
+                                   multiple of 32 >= 128 */
 } ttt_plan;
 
 /* ------------------------------------------------------------------------ */
@@ -115,6 +117,33 @@ int ttt_linear_fwd(const void* K, const void* Q, const void* V,
                    int B, int H, int T, int d, int chunk, int io_dtype,
                    void* workspace, size_t workspace_bytes,
                    void* stream, int plan);
+
+/* Streaming continuation of the TTT-Linear scan: n more tokens of every
+ * (batch, head) sequence, from a carried state, with the same chunking as
+ * ttt_linear_fwd over the whole sequence (token i of the sequence belongs to
+ * chunk floor(i / chunk)).  Inside a chunk every gradient is taken at the
+ * chunk-start state and a token reads with the chunk's updates up to and
+ * including its own (PaperTrace "5 · TestingTime 训练与长上下文" §1.1, §2.1,
+ * §2.3), so the carried state is a pair:
+ *   W_chunk : [B, H, d, d] fp32, the state at the start of the current chunk;
+ *   G       : [B, H, d, d] fp32, the sum over the chunk's tokens so far of
+ *             eta_s (W_chunk k_s - v_s) k_s^T;
+ *   pos     : how many tokens of the current chunk came before this call,
+ *             0 <= pos < chunk (the caller tracks it: after the call it is
+ *             (pos + n) % chunk).
+ * The state after the last token read so far is W_chunk - G.  Both are updated
+ * in place; when a chunk completes W_chunk becomes W_chunk - G and G is zeroed.
+ * A stream starts from W_chunk = W0, G = 0, pos = 0; ttt_linear_fwd over a
+ * prefix whose length is a multiple of chunk hands over W_out with G = 0.
+ *   K, Q, V : [B, H, n, d] in io_dtype;  eta : [B, H, n] fp32 or NULL;
+ *   Z       : [B, H, n, d] in io_dtype;  d : 16, 32, 64 or 128;  n >= 1.
+ * W_chunk and G must not overlap each other or any other argument.  Arithmetic
+ * is fp32 on the vector ALUs; no workspace. */
+int ttt_linear_step(const void* K, const void* Q, const void* V,
+                    const float* eta, float eta_scalar,
+                    float* W_chunk, float* G, int pos,
+                    void* Z, int B, int H, int n, int d, int chunk, int io_dtype,
+                    void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* TTT-MLP (hidden width 4d)                                                 */

@@ -133,6 +133,32 @@ int ttt_linear_fwd(const void* K, const void* Q, const void* V,
     }
 }
 
+int ttt_linear_step(const void* K, const void* Q, const void* V,
+                    const float* eta, float eta_scalar, float* W_chunk, float* G, int pos,
+                    void* Z, int B, int H, int n, int d, int chunk, int io_dtype, void* stream)
+{
+    if (!K || !Q || !V || !W_chunk || !G || !Z) return TTT_ERR_INVALID_ARG;
+    if (!aligned(K, 16) || !aligned(Q, 16) || !aligned(V, 16) || !aligned(Z, 16) ||
+        !aligned(W_chunk, 16) || !aligned(G, 16))
+        return TTT_ERR_INVALID_ARG;
+    if (eta ? !aligned(eta, 4) : !std::isfinite(eta_scalar)) return TTT_ERR_INVALID_ARG;
+    if (!dims_ok(B, H, n, d, chunk)) return TTT_ERR_INVALID_ARG;
+    if (io_dtype != TTT_DTYPE_F32 && io_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARG;
+    if (pos < 0 || pos >= chunk) return TTT_ERR_INVALID_ARG;
+    if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
+    // the carried state and its in-chunk update must be disjoint
+    const uintptr_t wlo = reinterpret_cast<uintptr_t>(W_chunk), glo = reinterpret_cast<uintptr_t>(G);
+    const uintptr_t state_bytes = (uintptr_t)B * H * d * d * sizeof(float);
+    if (wlo < glo + state_bytes && glo < wlo + state_bytes) return TTT_ERR_INVALID_ARG;
+
+    LinearArgs a;
+    a.K = K; a.Q = Q; a.V = V; a.eta = eta; a.eta_scalar = eta_scalar; a.W0 = W_chunk;
+    a.Z = Z; a.W_out = W_chunk; a.BH = B * H; a.T = n; a.d = d; a.chunk = chunk;
+    a.bf16 = io_dtype == TTT_DTYPE_BF16;
+    a.workspace = nullptr; a.workspace_bytes = 0;
+    return launch_status(launch_linear_step(a, G, pos, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int ttt_mlp_select_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
 {
     return mlp_plan(B, H, T, d, chunk, io_dtype, plan);

@@ -59,6 +59,11 @@ bool linear_bigchunk_supported(int d, int chunk, int bf16);
 size_t linear_bigchunk_workspace(int BH, int T, int d, int chunk);
 hipError_t launch_linear_bigchunk(const LinearArgs& a, hipStream_t s);
 
+// Streaming continuation from a carried (chunk-start state, in-chunk update) pair;
+// fp32 vector ALU, d <= 128.  a.W_out is the chunk-start state, updated in place,
+// and a.T the number of new tokens.
+hipError_t launch_linear_step(const LinearArgs& a, float* G, int pos, hipStream_t s);
+
 // TTT-MLP: generic fp32 path (d <= 64) and the bf16 MFMA path (d == 64, chunk <= 16).
 size_t mlp_generic_workspace(int BH, int T, int d, int chunk);
 hipError_t launch_mlp_generic(const MlpArgs& a, hipStream_t s);

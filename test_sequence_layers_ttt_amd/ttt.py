@@ -19,6 +19,7 @@ PLAN_AUTO, PLAN_GENERIC, PLAN_MFMA, PLAN_BIGCHUNK = 0, 1, 2, 3
 
 # every symbol include/ttt.h declares
 EXPORTS = ("ttt_linear_workspace_bytes", "ttt_linear_select_plan", "ttt_linear_fwd",
+           "ttt_linear_step",
            "ttt_mlp_workspace_bytes", "ttt_mlp_select_plan", "ttt_mlp_fwd",
            "ttt_status_string", "ttt_plan_name")
 
@@ -47,6 +48,8 @@ def lib() -> ctypes.CDLL:
         L.ttt_linear_select_plan.restype = i
         L.ttt_linear_fwd.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp, i]
         L.ttt_linear_fwd.restype = i
+        L.ttt_linear_step.argtypes = [vp, vp, vp, vp, f, vp, vp, i, vp, i, i, i, i, i, i, vp]
+        L.ttt_linear_step.restype = i
         L.ttt_mlp_workspace_bytes.argtypes = [i] * 7
         L.ttt_mlp_workspace_bytes.restype = sz
         L.ttt_mlp_select_plan.argtypes = [i] * 7
@@ -158,6 +161,34 @@ def linear_fwd(K, Q, V, eta, W0, chunk: int, eta_scalar: float = 0.0, *, Z=None,
     if rc != OK:
         raise TTTError(rc, "ttt_linear_fwd")
     return Z, W_out
+
+
+def linear_step(K, Q, V, eta, W_chunk, G, pos: int, chunk: int, eta_scalar: float = 0.0, *,
+                Z=None, stream=None):
+    """Continue TTT-Linear scans by n tokens from a carried state, in place.
+    K, Q, V: [B, H, n, d] fp32 or bf16; eta: [B, H, n] fp32 or None; W_chunk (the
+    chunk-start state) and G (the chunk's update so far): [B, H, d, d] fp32, both
+    updated in place; pos: tokens of the current chunk already read.  Returns
+    (Z, new pos); the state after the last token is W_chunk - G."""
+    import torch
+    B, H, n, d = K.shape
+    _check(K, "K", (B, H, n, d))
+    _check(Q, "Q", (B, H, n, d), K.dtype)
+    _check(V, "V", (B, H, n, d), K.dtype)
+    _check(W_chunk, "W_chunk", (B, H, d, d), torch.float32)
+    _check(G, "G", (B, H, d, d), torch.float32)
+    if eta is not None:
+        _check(eta, "eta", (B, H, n), torch.float32)
+    if Z is None:
+        Z = torch.empty_like(K)
+    _check(Z, "Z", (B, H, n, d), K.dtype)
+    rc = lib().ttt_linear_step(K.data_ptr(), Q.data_ptr(), V.data_ptr(), _ptr(eta),
+                               float(eta_scalar), W_chunk.data_ptr(), G.data_ptr(), int(pos),
+                               Z.data_ptr(), B, H, n, d, int(chunk), _io_dtype(K),
+                               _stream(K.device, stream))
+    if rc != OK:
+        raise TTTError(rc, "ttt_linear_step")
+    return Z, (int(pos) + n) % int(chunk)
 
 
 def mlp_fwd(K, Q, V, eta, W1, b1, W2, b2, chunk: int, eta_scalar: float = 0.0, *, Z=None,

@@ -119,6 +119,39 @@ def test_mlp_rejects_bad_arguments(kw, status):
     assert _mlp(**kw) == status
 
 
+def _step(**kw):
+    a = dict(K=FAKE, Q=FAKE, V=FAKE, eta=None, eta_scalar=0.1, Wc=FAKE, G=FAKE + 65536, pos=0,
+             Z=FAKE, B=1, H=1, n=1, d=64, chunk=16, io=1, stream=None)
+    a.update(kw)
+    return ttt.lib().ttt_linear_step(a["K"], a["Q"], a["V"], a["eta"], a["eta_scalar"], a["Wc"],
+                                     a["G"], a["pos"], a["Z"], a["B"], a["H"], a["n"], a["d"],
+                                     a["chunk"], a["io"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=None), ttt.ERR_INVALID_ARG),
+    (dict(Wc=None), ttt.ERR_INVALID_ARG),
+    (dict(G=None), ttt.ERR_INVALID_ARG),
+    (dict(Z=None), ttt.ERR_INVALID_ARG),
+    (dict(G=FAKE), ttt.ERR_INVALID_ARG),            # state and update must not overlap
+    (dict(G=FAKE + 4096), ttt.ERR_INVALID_ARG),     # d = 64: 16 KiB of state per slice
+    (dict(Wc=FAKE + 65536, G=FAKE + 4096 * 13), ttt.ERR_INVALID_ARG),
+    (dict(G=FAKE + 65540), ttt.ERR_INVALID_ARG),    # misaligned
+    (dict(V=MISALIGNED), ttt.ERR_INVALID_ARG),
+    (dict(eta=FAKE + 2), ttt.ERR_INVALID_ARG),
+    (dict(eta_scalar=math.nan), ttt.ERR_INVALID_ARG),
+    (dict(pos=-1), ttt.ERR_INVALID_ARG),
+    (dict(pos=16), ttt.ERR_INVALID_ARG),
+    (dict(n=0), ttt.ERR_INVALID_ARG),
+    (dict(chunk=0, pos=0), ttt.ERR_INVALID_ARG),
+    (dict(io=3), ttt.ERR_INVALID_ARG),
+    (dict(d=48), ttt.ERR_UNSUPPORTED),
+    (dict(d=256), ttt.ERR_UNSUPPORTED),
+])
+def test_step_rejects_bad_arguments(kw, status):
+    assert _step(**kw) == status
+
+
 def test_plan_selection_and_workspace_are_host_only():
     assert ttt.linear_select_plan(1, 1, 256, 16, 16, ttt.DTYPE_F32) == ttt.PLAN_GENERIC
     assert ttt.linear_select_plan(1, 1, 256, 16, 16, 0, ttt.PLAN_GENERIC) == ttt.PLAN_GENERIC
@@ -144,5 +177,5 @@ def test_profile_hash_covers_every_kernel_source():
     csrc = os.path.join(ROOT, "test_sequence_layers_ttt_amd", "csrc")
     files = {os.path.basename(p) for p in glob.glob(os.path.join(csrc, "*"))
              if p.endswith((".hip", ".h", ".cpp"))}
-    hashed = set(bench.KERNEL_SOURCES["linear"]) | set(bench.KERNEL_SOURCES["mlp"])
+    hashed = set().union(*bench.KERNEL_SOURCES.values())
     assert files <= hashed, sorted(files - hashed)
