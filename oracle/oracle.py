@@ -1,4 +1,7 @@
-"""ctypes wrapper around libttt_oracle.so (plain C, fp64) — TEST INFRASTRUCTURE ONLY."""
+"""ctypes wrapper around libttt_oracle.so (plain C, fp64) — TEST INFRASTRUCTURE ONLY.
+
+Forward scans of TTT-Linear and TTT-MLP, and the vector-Jacobian product of the
+TTT-Linear scan."""
 from __future__ import annotations
 
 import ctypes
@@ -46,6 +49,11 @@ def _load():
                                           ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int]
         lib.ttt_oracle_linear.restype = ctypes.c_int
+        lib.ttt_oracle_linear_bwd.argtypes = [P, P, P, P, ctypes.c_double, P, P, P,
+                                              P, P, P, P, P,
+                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int, ctypes.c_int]
+        lib.ttt_oracle_linear_bwd.restype = ctypes.c_int
         lib.ttt_oracle_mlp.argtypes = [P, P, P, P, ctypes.c_double, P, P, P, P,
                                        P, P, P, P, P,
                                        ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -89,6 +97,34 @@ def linear(K, Q, V, eta, eta_scalar: float, W0, chunk: int,
     if rc <= 0:
         raise ValueError("ttt_oracle_linear rejected its arguments")
     return (Z, W, rc) if return_threads else (Z, W)
+
+
+def linear_bwd(K, Q, V, eta, eta_scalar: float, W0, chunk: int, dZ, dW_T=None,
+               nthreads: int = 0, return_threads: bool = False):
+    """Gradient of L = <dZ, Z> + <dW_T, W_T> through the TTT-Linear scan.
+    dZ: [n, T, d]; dW_T: [n, d, d] or None (zero).  Returns (dK, dQ, dV, deta [n, T],
+    dW0) in fp64; deta is per token also when eta is None (eta_scalar for all)."""
+    K, Q, V, W0, dZ = _f64(K), _f64(Q), _f64(V), _f64(W0), _f64(dZ)
+    eta, dW_T = _f64(eta), _f64(dW_T)
+    n, T, d = K.shape
+    assert Q.shape == K.shape == V.shape == dZ.shape and W0.shape == (n, d, d)
+    if eta is not None:
+        assert eta.shape == (n, T)
+    if dW_T is not None:
+        assert dW_T.shape == (n, d, d)
+    dK = np.empty((n, T, d), np.float64)
+    dQ = np.empty((n, T, d), np.float64)
+    dV = np.empty((n, T, d), np.float64)
+    deta = np.empty((n, T), np.float64)
+    dW0 = np.empty((n, d, d), np.float64)
+    rc = _load().ttt_oracle_linear_bwd(_ptr(K), _ptr(Q), _ptr(V), _ptr(eta), float(eta_scalar),
+                                       _ptr(W0), _ptr(dZ), _ptr(dW_T), _ptr(dK), _ptr(dQ),
+                                       _ptr(dV), _ptr(deta), _ptr(dW0), n, T, d, int(chunk),
+                                       int(nthreads))
+    if rc <= 0:
+        raise ValueError("ttt_oracle_linear_bwd rejected its arguments")
+    res = (dK, dQ, dV, deta, dW0)
+    return res + (rc,) if return_threads else res
 
 
 def mlp(K, Q, V, eta, eta_scalar: float, W1, b1, W2, b2, chunk: int,

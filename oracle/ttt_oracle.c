@@ -65,6 +65,142 @@ static void linear_slice(const double* K, const double* Q, const double* V,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Vector-Jacobian product of the TTT-Linear scan, one slice: the gradient of */
+/* L = <dZ, Z> + <dW_T, W_T> with respect to K, Q, V, every token's eta and W0. */
+/* Reverse mode through the same per-token loop as linear_slice (PaperTrace   */
+/* "5 · TestingTime 训练与长上下文" §1.1, §2.1, §2.3), one chunk at a time from */
+/* the last: with Wc the chunk-start state, G_t the chunk's accumulated update */
+/* after token t, and adjoints written dX,                                    */
+/*   W_next = Wc - G_last       : dWc = dW_next,  dG = -dW_next               */
+/*   z_t = (Wc - G_t) q_t       : dWc += dz q^T,  dG -= dz q^T,               */
+/*                                dq = (Wc - G_t)^T dz                         */
+/*   G_t = G_{t-1} + eta e k^T  : deta = e^T dG k, de = eta dG k,             */
+/*                                dk = eta dG^T e  (dG flows on to G_{t-1})    */
+/*   e_t = Wc k_t - v_t         : dWc += de k^T,  dk += Wc^T de,  dv = -de     */
+/* and dW_next of the previous chunk is this chunk's dWc.  The chunk-start    */
+/* states come from a forward pass kept whole; G_{t-1} is G_t minus token t's  */
+/* term.  deta_t is the gradient for token t's eta also when one scalar eta   */
+/* serves every token (the scalar's gradient is then the sum over tokens).    */
+/* ------------------------------------------------------------------------ */
+static void linear_bwd_slice(const double* K, const double* Q, const double* V,
+                             const double* eta, double eta_scalar, const double* W0,
+                             const double* dZ, const double* dWT,
+                             double* dK, double* dQ, double* dV, double* deta, double* dW0,
+                             int T, int d, int chunk)
+{
+    const size_t dd = (size_t)d * d;
+    const int nch = (T + chunk - 1) / chunk;
+    double* Wst = (double*)malloc(sizeof(double) * dd * nch);  /* chunk-start states */
+    double* W   = (double*)malloc(sizeof(double) * dd);
+    double* G   = (double*)malloc(sizeof(double) * dd);
+    double* dW  = (double*)malloc(sizeof(double) * dd);         /* adjoint of W_next  */
+    double* dWc = (double*)malloc(sizeof(double) * dd);
+    double* dG  = (double*)malloc(sizeof(double) * dd);
+    double* E   = (double*)malloc(sizeof(double) * (size_t)chunk * d);
+    double* de  = (double*)malloc(sizeof(double) * d);
+
+    /* forward pass: the chunk-start states */
+    memcpy(W, W0, sizeof(double) * dd);
+    for (int c = 0; c < nch; ++c) {
+        const int c0 = c * chunk, c1 = c0 + chunk < T ? c0 + chunk : T;
+        double* Wc = Wst + (size_t)c * dd;
+        memcpy(Wc, W, sizeof(double) * dd);
+        memset(G, 0, sizeof(double) * dd);
+        for (int t = c0; t < c1; ++t) {
+            const double* k = K + (size_t)t * d;
+            const double* v = V + (size_t)t * d;
+            const double et = eta ? eta[t] : eta_scalar;
+            for (int i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < d; ++j) acc += Wc[i * d + j] * k[j];
+                const double ei = acc - v[i];
+                for (int j = 0; j < d; ++j) G[i * d + j] += et * ei * k[j];
+            }
+        }
+        for (size_t i = 0; i < dd; ++i) W[i] = Wc[i] - G[i];
+    }
+
+    /* reverse pass */
+    if (dWT) memcpy(dW, dWT, sizeof(double) * dd);
+    else memset(dW, 0, sizeof(double) * dd);
+    for (int c = nch - 1; c >= 0; --c) {
+        const int c0 = c * chunk, c1 = c0 + chunk < T ? c0 + chunk : T;
+        const double* Wc = Wst + (size_t)c * dd;
+        /* e_t for the chunk's tokens and the chunk's whole update G */
+        memset(G, 0, sizeof(double) * dd);
+        for (int t = c0; t < c1; ++t) {
+            const double* k = K + (size_t)t * d;
+            const double* v = V + (size_t)t * d;
+            const double et = eta ? eta[t] : eta_scalar;
+            double* e = E + (size_t)(t - c0) * d;
+            for (int i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < d; ++j) acc += Wc[i * d + j] * k[j];
+                e[i] = acc - v[i];
+            }
+            for (int i = 0; i < d; ++i)
+                for (int j = 0; j < d; ++j) G[i * d + j] += (et * e[i]) * k[j];
+        }
+        /* W_next = Wc - G */
+        for (size_t i = 0; i < dd; ++i) {
+            dWc[i] = dW[i];
+            dG[i] = -dW[i];
+        }
+        for (int t = c1 - 1; t >= c0; --t) {
+            const double* k = K + (size_t)t * d;
+            const double* q = Q + (size_t)t * d;
+            const double* dz = dZ + (size_t)t * d;
+            const double et = eta ? eta[t] : eta_scalar;
+            const double* e = E + (size_t)(t - c0) * d;
+            double* dk = dK + (size_t)t * d;
+            double* dq = dQ + (size_t)t * d;
+            double* dv = dV + (size_t)t * d;
+            /* z_t = (Wc - G_t) q_t */
+            for (int j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < d; ++i) acc += (Wc[i * d + j] - G[i * d + j]) * dz[i];
+                dq[j] = acc;
+            }
+            for (int i = 0; i < d; ++i)
+                for (int j = 0; j < d; ++j) {
+                    dWc[i * d + j] += dz[i] * q[j];
+                    dG[i * d + j] -= dz[i] * q[j];
+                }
+            /* G_t = G_{t-1} + eta_t e_t k_t^T */
+            double sdeta = 0.0;
+            for (int i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < d; ++j) acc += dG[i * d + j] * k[j];
+                sdeta += e[i] * acc;
+                de[i] = et * acc;
+            }
+            deta[t] = sdeta;
+            for (int j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < d; ++i) acc += dG[i * d + j] * e[i];
+                dk[j] = et * acc;
+            }
+            /* e_t = Wc k_t - v_t */
+            for (int j = 0; j < d; ++j) {
+                double acc = 0.0;
+                for (int i = 0; i < d; ++i) acc += Wc[i * d + j] * de[i];
+                dk[j] += acc;
+            }
+            for (int i = 0; i < d; ++i) {
+                dv[i] = -de[i];
+                for (int j = 0; j < d; ++j) dWc[i * d + j] += de[i] * k[j];
+            }
+            /* back to G_{t-1} */
+            for (int i = 0; i < d; ++i)
+                for (int j = 0; j < d; ++j) G[i * d + j] -= et * e[i] * k[j];
+        }
+        memcpy(dW, dWc, sizeof(double) * dd);
+    }
+    memcpy(dW0, dW, sizeof(double) * dd);
+    free(Wst); free(W); free(G); free(dW); free(dWc); free(dG); free(E); free(de);
+}
+
+/* ------------------------------------------------------------------------ */
 /* GELU, exact erf form: gelu(x) = x * Phi(x), Phi the standard normal CDF.  */
 /* diosapp "Test-Time Training (TTT) guide" §3 names GELU; the erf form is   */
 /* the reading taken here.                                                   */
@@ -196,10 +332,10 @@ static void mlp_slice(const double* K, const double* Q, const double* V,
 /* Thread pool over (batch, head) slices.                                    */
 /* ------------------------------------------------------------------------ */
 typedef struct {
-    int is_mlp;
-    const double *K, *Q, *V, *eta, *W0, *W1, *b1, *W2, *b2;
+    int is_mlp, is_bwd;
+    const double *K, *Q, *V, *eta, *W0, *W1, *b1, *W2, *b2, *dZ, *dWT;
     double eta_scalar;
-    double *Z, *W_out, *W1_o, *b1_o, *W2_o, *b2_o;
+    double *Z, *W_out, *W1_o, *b1_o, *W2_o, *b2_o, *dK, *dQ, *dV, *deta, *dW0;
     int BH, T, d, hd, chunk, nthreads, tid;
 } job_t;
 
@@ -209,7 +345,14 @@ static void* worker(void* arg)
     size_t td = (size_t)j->T * j->d;
     for (int s = j->tid; s < j->BH; s += j->nthreads) {
         const double* eta = j->eta ? j->eta + (size_t)s * j->T : NULL;
-        if (!j->is_mlp) {
+        if (j->is_bwd) {
+            size_t dd = (size_t)j->d * j->d;
+            linear_bwd_slice(j->K + s * td, j->Q + s * td, j->V + s * td, eta, j->eta_scalar,
+                             j->W0 + s * dd, j->dZ + s * td, j->dWT ? j->dWT + s * dd : NULL,
+                             j->dK + s * td, j->dQ + s * td, j->dV + s * td,
+                             j->deta + (size_t)s * j->T, j->dW0 + s * dd,
+                             j->T, j->d, j->chunk);
+        } else if (!j->is_mlp) {
             size_t dd = (size_t)j->d * j->d;
             linear_slice(j->K + s * td, j->Q + s * td, j->V + s * td, eta, j->eta_scalar,
                          j->W0 + s * dd, j->Z + s * td, j->W_out + s * dd,
@@ -263,6 +406,24 @@ int ttt_oracle_linear(const double* K, const double* Q, const double* V,
     memset(&j, 0, sizeof j);
     j.K = K; j.Q = Q; j.V = V; j.eta = eta; j.eta_scalar = eta_scalar; j.W0 = W0;
     j.Z = Z; j.W_out = W_out; j.BH = BH; j.T = T; j.d = d; j.chunk = chunk;
+    j.nthreads = nthreads;
+    return run_pool(&j);
+}
+
+int ttt_oracle_linear_bwd(const double* K, const double* Q, const double* V,
+                          const double* eta, double eta_scalar, const double* W0,
+                          const double* dZ, const double* dW_T,
+                          double* dK, double* dQ, double* dV, double* deta, double* dW0,
+                          int BH, int T, int d, int chunk, int nthreads)
+{
+    if (!K || !Q || !V || !W0 || !dZ || !dK || !dQ || !dV || !deta || !dW0) return -1;
+    if (BH <= 0 || T <= 0 || d <= 0 || chunk <= 0) return -1;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.is_bwd = 1;
+    j.K = K; j.Q = Q; j.V = V; j.eta = eta; j.eta_scalar = eta_scalar; j.W0 = W0;
+    j.dZ = dZ; j.dWT = dW_T; j.dK = dK; j.dQ = dQ; j.dV = dV; j.deta = deta; j.dW0 = dW0;
+    j.BH = BH; j.T = T; j.d = d; j.chunk = chunk;
     j.nthreads = nthreads;
     return run_pool(&j);
 }

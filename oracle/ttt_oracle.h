@@ -2,7 +2,7 @@
  * ttt_oracle.h — TEST INFRASTRUCTURE ONLY.
  *
  * Plain, slow fp64 CPU reference for the forward scan of a test-time-training
- * (TTT) layer.  Only the test suite, the smoke check and the CPU-baseline leg of
+ * (TTT) layer, and for the gradient of the TTT-Linear scan.  Only the test suite, the smoke check and the CPU-baseline leg of
  * the benchmark may call it; the product library never links or loads it, and it
  * shares no code, header or constant with the HIP path.
  *
@@ -48,6 +48,16 @@ int ttt_oracle_linear(const double* K, const double* Q, const double* V,
                       const double* eta, double eta_scalar, const double* W0,
                       double* Z, double* W_out,
                       int BH, int T, int d, int chunk, int nthreads);
+
+/* Vector-Jacobian product of ttt_oracle_linear: for L = <dZ, Z> + <dW_T, W_T>
+ * (dW_T may be NULL for zero), writes dK, dQ, dV : [BH, T, d], deta : [BH, T]
+ * (the gradient for each token's eta, also when eta is NULL and eta_scalar
+ * serves every token) and dW0 : [BH, d, d]. */
+int ttt_oracle_linear_bwd(const double* K, const double* Q, const double* V,
+                          const double* eta, double eta_scalar, const double* W0,
+                          const double* dZ, const double* dW_T,
+                          double* dK, double* dQ, double* dV, double* deta, double* dW0,
+                          int BH, int T, int d, int chunk, int nthreads);
 
 int ttt_oracle_mlp(const double* K, const double* Q, const double* V,
                    const double* eta, double eta_scalar,

@@ -52,6 +52,24 @@ MUTANTS = {
         "s += W2s[(size_t)i * hd + u] * hr[u];"),
     "MLP backward skips gelu'": (
         "dl[u] = s * ttt_oracle_gelu_prime(h[u]);", "dl[u] = s;"),
+    # the vector-Jacobian product of the TTT-Linear scan
+    "VJP: dq read at the chunk-start state": (
+        "acc += (Wc[i * d + j] - G[i * d + j]) * dz[i];", "acc += Wc[i * d + j] * dz[i];"),
+    "VJP: state cotangent not sent into the update": (
+        "dG[i] = -dW[i];", "dG[i] = 0.0;"),
+    "VJP: dv sign": (
+        "dv[i] = -de[i];", "dv[i] = de[i];"),
+    "VJP: dk misses the error path": (
+        "dk[j] += acc;", "dk[j] += 0.0 * acc;"),
+    "VJP: update not unwound between tokens": (
+        "for (int j = 0; j < d; ++j) G[i * d + j] -= et * e[i] * k[j];", ";"),
+    "VJP: deta scaled by eta": (
+        "sdeta += e[i] * acc;", "sdeta += et * e[i] * acc;"),
+    "VJP: transposed update cotangent in dk": (
+        "for (int i = 0; i < d; ++i) acc += dG[i * d + j] * e[i];",
+        "for (int i = 0; i < d; ++i) acc += dG[j * d + i] * e[i];"),
+    "VJP: read cotangent skips the chunk-start state": (
+        "dWc[i * d + j] += dz[i] * q[j];", "dWc[i * d + j] += 0.0;"),
 }
 
 
@@ -75,6 +93,7 @@ def build_variant(tmp_path, name, old=None, new=None):
 def run_pins(lib):
     env = dict(os.environ, TTT_ORACLE_LIB=lib)
     return subprocess.run([sys.executable, "-m", "pytest", os.path.join(HERE, "test_oracle_pins.py"),
+                           os.path.join(HERE, "test_oracle_bwd_pins.py"),
                            "-x", "-q", "-p", "no:cacheprovider", "-k", NOT_PINS],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
 
