@@ -41,8 +41,12 @@ KERNEL_SOURCES = {"linear": ["linear_mfma.hip", "linear_coop.hip", "linear_gener
                              "launch.h", "api.cpp"],
                   "mlp": ["mlp_mfma.hip", "mlp_generic.hip", "mfma_common.h", "device_common.h",
                           "launch.h", "api.cpp"],
-                  "step": ["linear_step.hip", "device_common.h", "launch.h", "api.cpp"]}
+                  "step": ["linear_step.hip", "device_common.h", "launch.h", "api.cpp"],
+                  "bwd": ["linear_bwd.hip", "mfma_common.h", "device_common.h", "launch.h",
+                          "api.cpp"]}
 DECODE_METRIC = "TTT-Linear decode tokens/sec (all heads) + % of HBM roofline"
+BWD_METRIC = "TTT-Linear backward tokens/sec (all heads) + % of fp32 MFMA roofline"
+FP32_PEAK_TFS = 157.3            # MI355X dense fp32 matrix
 
 
 def log(*a):
@@ -109,6 +113,129 @@ def decode_bytes(wl, n: int) -> float:
     per_tok = 4 * wl.d * esz + (4 if wl.eta_mode == "token" else 0)
     state = wl.d * wl.d * 4
     return float(wl.BH) * ((3.0 + min(1.0, n / wl.chunk)) * state + n * per_tok)
+
+
+def bwd_flops(wl) -> float:
+    """Flops of the backward pass per (batch, head), in 16-token sub-tiles of m
+    tokens: forward recompute of the chunk-start states (E = W K, W -= F K^T:
+    4 d^2 m), then E, P K, dF's and dA's masked m x m products, dK (three
+    products), dQ (two), dW (two): 16 d^2 m + 5 m (m + 1) d, plus 2 d^2 m for the
+    running W - G when a chunk spans several sub-tiles."""
+    d, total = wl.d, 0.0
+    for c0 in range(0, wl.T, wl.chunk):
+        n = min(wl.chunk, wl.T - c0)
+        for s0 in range(0, n, 16):
+            m = min(16, n - s0)
+            total += 20.0 * d * d * m + 5.0 * m * (m + 1) * d
+            if wl.chunk > 16:
+                total += 2.0 * d * d * m
+    return total * wl.BH
+
+
+def bwd_main(args, wl, x, seed):
+    """One step = one ttt_linear_bwd call over the whole batch (dZ, dW_T seeded)."""
+    import torch
+    from test_sequence_layers_ttt_amd import inputs, ttt
+    dev = torch.device("cuda:0")
+    B, H, T, d = wl.B, wl.H, wl.T, wl.d
+    io = torch.bfloat16 if wl.io == "bf16" else torch.float32
+    rng = np.random.default_rng([seed, 77])
+    dZ = rng.standard_normal((wl.BH, T, d), dtype=np.float32)
+    if wl.io == "bf16":
+        dZ = inputs.round_to_bf16(dZ)
+    dWT = rng.standard_normal((wl.BH, d, d), dtype=np.float32)
+
+    def dev_t(a, shape, dt=torch.float32):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).reshape(shape).to(dt).contiguous()
+
+    base = {k: dev_t(x[k], (B, H, T, d), io) for k in ("K", "Q", "V")}
+    base["eta"] = None if x["eta"] is None else dev_t(x["eta"], (B, H, T))
+    base["W0"] = dev_t(x["W0"], (B, H, d, d))
+    base["dZ"] = dev_t(dZ, (B, H, T, d), io)
+    base["dWT"] = dev_t(dWT, (B, H, d, d))
+    outs = {k: torch.empty_like(base["K"]) for k in ("dK", "dQ", "dV")}
+    outs["deta"] = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    outs["dW0"] = torch.empty_like(base["W0"])
+    io_code = ttt.DTYPE_BF16 if wl.io == "bf16" else ttt.DTYPE_F32
+    nbytes = ttt.linear_bwd_workspace_bytes(B, H, T, d, wl.chunk, io_code)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    log("backward: workspace %.1f MB" % (nbytes / 1e6))
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ttt.linear_bwd(base["K"], base["Q"], base["V"], base["eta"], base["W0"], base["dZ"],
+                       wl.chunk, eta_scalar=x["eta_scalar"], dW_T=base["dWT"], dK=outs["dK"],
+                       dQ=outs["dQ"], dV=outs["dV"], deta=outs["deta"], dW0=outs["dW0"],
+                       workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_event = ev0.elapsed_time(ev1) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    log("timed %d backward calls: %.4f ms/call (events), %.4f ms/call (wall)" % (
+        args.steps, ms_event, ms_step))
+    flops = bwd_flops(wl)
+    tfs = flops / (ms_event * 1e-3) / 1e12
+
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        per_slice = 6.0 * wl.T * wl.d * wl.d * 4   # the oracle's fp64 work, roughly
+        nsl = args.cpu_sample_slices or int(max(1, min(wl.BH, 2.0e10 * 16 // per_slice)))
+        idx = np.unique(np.linspace(0, wl.BH - 1, nsl).round().astype(int))
+        t1 = time.perf_counter()
+        ref = oracle.linear_bwd(x["K"][idx], x["Q"][idx], x["V"][idx],
+                                None if x["eta"] is None else x["eta"][idx], x["eta_scalar"],
+                                x["W0"][idx], wl.chunk, dZ[idx], dWT[idx], return_threads=True)
+        tcpu = time.perf_counter() - t1
+        nth = ref[5]
+        cpu = {"value": round(len(idx) * wl.T / wl.H / tcpu, 1), "unit": "tokens/s",
+               "cores": int(nth), "kind": "oracle",
+               "sample": "%d of %d (batch, head) slices, full T=%d, fp64 per-token reverse "
+                         "loop, %.2f s" % (len(idx), wl.BH, wl.T, tcpu)}
+        got = [outs["dK"], outs["dQ"], outs["dV"], outs["deta"], outs["dW0"]]
+        errs = {}
+        for name, g, r in zip(("dK", "dQ", "dV", "deta", "dW0"), got, ref[:5]):
+            gg = g.float().cpu().numpy().reshape(wl.BH, -1)[idx]
+            rr = r.reshape(len(idx), -1)
+            den = np.maximum(np.abs(rr).max(axis=1), 1e-6)
+            errs[name] = float("%.3e" % (np.abs(gg - rr).max(axis=1) / den).max())
+        parity = {"max_rel_err": errs, "slices_checked": int(len(idx))}
+        log("oracle: %d slices in %.2f s on %d threads; parity %s" % (len(idx), tcpu, nth, parity))
+
+    rec = {
+        "metric": BWD_METRIC,
+        "value": round(B * T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name + "_bwd", "scan": "ttt_linear_bwd", "batch": B,
+                   "heads": H, "seq_len": T, "head_dim": d, "chunk": wl.chunk, "io": wl.io,
+                   "parallelism": "single_gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": FP32_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": round(tfs / FP32_PEAK_TFS, 4), "traffic": None,
+                     "kernel_ms": round(ms_event, 5), "algorithmic_flops": flops},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "head_tokens_per_s": round(B * H * T / (ms_step * 1e-3), 1),
+    }
+    print(json.dumps(rec), flush=True)
 
 
 def decode_main(args, wl, x):
@@ -234,6 +361,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0)
     ap.add_argument("--decode", type=int, default=0,
                     help="time ttt_linear_step continuing every sequence by N tokens")
+    ap.add_argument("--bwd", action="store_true",
+                    help="time ttt_linear_bwd (the backward pass) on the workload")
     ap.add_argument("--decode-batch", type=int, default=0,
                     help="batch size of the decode line (default: the workload's)")
     args = ap.parse_args()
@@ -252,6 +381,11 @@ def main():
 
     wl = inputs.WORKLOADS[args.workload]
     seed = inputs.WORKLOAD_SEEDS[wl.name]
+    if args.bwd:
+        if wl.model != "linear":
+            raise SystemExit("--bwd needs a TTT-Linear workload")
+        bwd_main(args, wl, inputs.make_inputs(wl, seed), seed)
+        return
     if args.decode:
         if wl.model != "linear" or args.decode > wl.T:
             raise SystemExit("--decode needs a TTT-Linear workload with T >= N")

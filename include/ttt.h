@@ -118,6 +118,37 @@ int ttt_linear_fwd(const void* K, const void* Q, const void* V,
                    void* workspace, size_t workspace_bytes,
                    void* stream, int plan);
 
+/* Bytes of workspace ttt_linear_bwd needs: the chunk-start states
+ * (B*H*(ceil(T/chunk)+1)*d*d fp32) and per-16-row-block partial sums of dK, dQ
+ * and deta.  0 for an unsupported shape. */
+size_t ttt_linear_bwd_workspace_bytes(int B, int H, int T, int d, int chunk, int io_dtype);
+
+/* Backward pass (vector-Jacobian product) of ttt_linear_fwd: for the scalar
+ * L = <dZ, Z> + <dW_T, W_out> it writes the gradients with respect to K, Q, V,
+ * each token's eta and W0.  The forward scan is recomputed from W0 (nothing is
+ * kept from a ttt_linear_fwd call).  Same chunking and semantics as
+ * ttt_linear_fwd (PaperTrace "5 · TestingTime 训练与长上下文" §1.1, §2.1, §2.3).
+ *   K, Q, V, dZ    : [B, H, T, d] in io_dtype (dZ: the cotangent of Z).
+ *   eta            : [B, H, T] fp32 or NULL (eta_scalar for every token).
+ *   W0             : [B, H, d, d] fp32.
+ *   dW_T           : [B, H, d, d] fp32 cotangent of W_out, or NULL for zero.
+ *   dK, dQ, dV     : [B, H, T, d] in io_dtype (outputs).
+ *   deta           : [B, H, T] fp32, the gradient for each token's eta (also
+ *                    when eta is NULL: the gradient of eta_scalar is then the
+ *                    sum of deta), or NULL to skip it.
+ *   dW0            : [B, H, d, d] fp32 (output).
+ *   d : 16, 32, 64 or 128;  chunk >= 1.
+ *   workspace      : at least ttt_linear_bwd_workspace_bytes(...) bytes,
+ *                    256-byte aligned.
+ * Arithmetic is fp32 (inputs in bf16 are widened exactly).  Outputs must not
+ * overlap inputs or each other. */
+int ttt_linear_bwd(const void* K, const void* Q, const void* V,
+                   const float* eta, float eta_scalar, const float* W0,
+                   const void* dZ, const float* dW_T,
+                   void* dK, void* dQ, void* dV, float* deta, float* dW0,
+                   int B, int H, int T, int d, int chunk, int io_dtype,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 /* Streaming continuation of the TTT-Linear scan: n more tokens of every
  * (batch, head) sequence, from a carried state, with the same chunking as
  * ttt_linear_fwd over the whole sequence (token i of the sequence belongs to

@@ -133,6 +133,43 @@ int ttt_linear_fwd(const void* K, const void* Q, const void* V,
     }
 }
 
+size_t ttt_linear_bwd_workspace_bytes(int B, int H, int T, int d, int chunk, int io_dtype)
+{
+    if (!dims_ok(B, H, T, d, chunk)) return 0;
+    if (io_dtype != TTT_DTYPE_F32 && io_dtype != TTT_DTYPE_BF16) return 0;
+    if (d != 16 && d != 32 && d != 64 && d != 128) return 0;
+    return linear_bwd_workspace(B * H, T, d, chunk);
+}
+
+int ttt_linear_bwd(const void* K, const void* Q, const void* V,
+                   const float* eta, float eta_scalar, const float* W0,
+                   const void* dZ, const float* dW_T,
+                   void* dK, void* dQ, void* dV, float* deta, float* dW0,
+                   int B, int H, int T, int d, int chunk, int io_dtype,
+                   void* workspace, size_t workspace_bytes, void* stream)
+{
+    if (!K || !Q || !V || !W0 || !dZ || !dK || !dQ || !dV || !dW0) return TTT_ERR_INVALID_ARG;
+    if (!aligned(K, 16) || !aligned(Q, 16) || !aligned(V, 16) || !aligned(dZ, 16) ||
+        !aligned(W0, 16) || !aligned(dK, 16) || !aligned(dQ, 16) || !aligned(dV, 16) ||
+        !aligned(dW0, 16) || (dW_T && !aligned(dW_T, 16)))
+        return TTT_ERR_INVALID_ARG;
+    if (eta ? !aligned(eta, 4) : !std::isfinite(eta_scalar)) return TTT_ERR_INVALID_ARG;
+    if (deta && !aligned(deta, 4)) return TTT_ERR_INVALID_ARG;
+    if (!dims_ok(B, H, T, d, chunk)) return TTT_ERR_INVALID_ARG;
+    if (io_dtype != TTT_DTYPE_F32 && io_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARG;
+    if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
+    const size_t need = linear_bwd_workspace(B * H, T, d, chunk);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return TTT_ERR_WORKSPACE;
+
+    LinearBwdArgs a;
+    a.K = K; a.Q = Q; a.V = V; a.eta = eta; a.eta_scalar = eta_scalar; a.W0 = W0;
+    a.dZ = dZ; a.dW_T = dW_T; a.dK = dK; a.dQ = dQ; a.dV = dV; a.deta = deta; a.dW0 = dW0;
+    a.BH = B * H; a.T = T; a.d = d; a.chunk = chunk;
+    a.bf16 = io_dtype == TTT_DTYPE_BF16;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    return launch_status(launch_linear_bwd(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int ttt_linear_step(const void* K, const void* Q, const void* V,
                     const float* eta, float eta_scalar, float* W_chunk, float* G, int pos,
                     void* Z, int B, int H, int n, int d, int chunk, int io_dtype, void* stream)

@@ -59,6 +59,32 @@ bool linear_bigchunk_supported(int d, int chunk, int bf16);
 size_t linear_bigchunk_workspace(int BH, int T, int d, int chunk);
 hipError_t launch_linear_bigchunk(const LinearArgs& a, hipStream_t s);
 
+struct LinearBwdArgs {
+    const void* K;
+    const void* Q;
+    const void* V;
+    const float* eta;      // [BH, T] or nullptr
+    float eta_scalar;
+    const float* W0;       // [BH, d, d]
+    const void* dZ;        // [BH, T, d] in the I/O type
+    const float* dW_T;     // [BH, d, d] or nullptr (zero)
+    void* dK;              // outputs [BH, T, d] in the I/O type
+    void* dQ;
+    void* dV;
+    float* deta;           // [BH, T] or nullptr (not written)
+    float* dW0;            // [BH, d, d]
+    int BH, T, d, chunk;
+    int bf16;
+    void* workspace;
+    size_t workspace_bytes;
+};
+
+// Backward pass of TTT-Linear (fp32 matrix cores), d in {16, 32, 64, 128}, any
+// chunk; the workspace holds the chunk-start states and the row-block partials.
+size_t linear_bwd_align(size_t bytes);
+size_t linear_bwd_workspace(int BH, int T, int d, int chunk);
+hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s);
+
 // Streaming continuation from a carried (chunk-start state, in-chunk update) pair;
 // fp32 vector ALU, d <= 128.  a.W_out is the chunk-start state, updated in place,
 // and a.T the number of new tokens.

@@ -1,0 +1,462 @@
+// Backward pass (vector-Jacobian product) of the TTT-Linear scan.
+//
+// Forward, per chunk of b tokens with chunk-start state W (PaperTrace "5 ·
+// TestingTime 训练与长上下文" §1.1, §2.1, §2.3): E = W K - V, F = E diag(eta),
+// Z = W Q - F (U o K^T Q), W_next = W - F K^T, with tokens as columns and U the
+// causal mask (s <= t).  Given the cotangents dZ and dW_next, the chunk's
+// gradients are, in 16-token sub-tiles sigma taken from the last
+// (P = dW_next + sum over later sub-tiles of dZ_tau Q_tau^T,
+//  H = W - G_{<sigma}, G_{<sigma} the chunk's update before sub-tile sigma):
+//   dF    = -dZ (U o K^T Q)^T - P K          (only the diagonal sub-tile masked)
+//   dE    = dF diag(eta),  deta_s = e_s . dF_s,  dV = -dE
+//   dA    = -(F^T dZ) o U
+//   dK    = -P^T F + Q dA^T + W^T dE          (tokens x dims: -F^T P + dA Q + dE^T W)
+//   dQ    = H^T dZ + K dA
+//   dW    = P_final + sum_sigma dE K^T        (= the previous chunk's dW_next)
+// Every product above except the sums behind dK, dQ and deta is separable by
+// state row: a wave owns 16 rows of one (batch, head) state, runs the forward
+// recurrence for them (saving each chunk-start state to the workspace), then
+// the reverse recurrence.  Its contributions to dK, dQ and deta (sums over the
+// rows) go to per-row-block partial buffers that a second kernel adds up.
+//
+// All products run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32), operands
+// staged through LDS in row-major fp32 tiles with padded rows.  Register forms
+// of a 16 x 16 tile X (lane l, c = l % 16, g = l / 16, slot v = 0..3):
+//   CL(X): lane holds X[4g + v][c]   (the MFMA result layout; a B operand whose
+//                                     contraction index is X's row)
+//   RL(X): lane holds X[c][4g + v]   (an A operand whose contraction index is
+//                                     X's column)
+// and RL(X) = CL(X^T).
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "launch.h"
+#include "mfma_common.h"
+
+namespace ttt {
+namespace {
+
+constexpr int kSub = 16;   // tokens per sub-tile
+
+// ---------------------------------------------------------------- LDS tiles
+// row-major fp32 with STRIDE floats per row (padding keeps the RL and CL reads
+// of 16 lanes on distinct banks)
+template <int STRIDE>
+__device__ __forceinline__ f32x4 rl(const float* X, int col0, int lane)
+{
+    const int c = lane & 15, g = lane >> 4;
+    return *reinterpret_cast<const f32x4*>(X + c * STRIDE + col0 + 4 * g);
+}
+
+template <int STRIDE>
+__device__ __forceinline__ f32x4 cl(const float* X, int col0, int lane)
+{
+    const int c = lane & 15, g = lane >> 4;
+    const float* p = X + (4 * g) * STRIDE + col0 + c;
+    return f32x4{p[0], p[STRIDE], p[2 * STRIDE], p[3 * STRIDE]};
+}
+
+// write a CL register tile into columns col0..col0+15 of a row-major tile
+template <int STRIDE>
+__device__ __forceinline__ void put_cl(float* X, int col0, int lane, f32x4 v)
+{
+    const int c = lane & 15, g = lane >> 4;
+    float* p = X + (4 * g) * STRIDE + col0 + c;
+    p[0] = v[0];
+    p[STRIDE] = v[1];
+    p[2 * STRIDE] = v[2];
+    p[3 * STRIDE] = v[3];
+}
+
+// keep the compiler from moving LDS accesses across this point (one wave: the
+// LDS unit executes its accesses in order)
+__device__ __forceinline__ void lds_order() { asm volatile("" ::: "memory"); }
+
+// D += A B over a 16-wide contraction: A in RL form, B in CL form
+__device__ __forceinline__ f32x4 mm16(f32x4 a, f32x4 b, f32x4 acc)
+{
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+    return acc;
+}
+
+// ---------------------------------------------------------------- global I/O
+// N consecutive elements (N a multiple of 4) widened to fp32
+template <int N>
+__device__ __forceinline__ void load_vec(const float* p, float* out)
+{
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(p + i);
+        out[i] = v.x; out[i + 1] = v.y; out[i + 2] = v.z; out[i + 3] = v.w;
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void load_vec(const uint16_t* p, float* out)
+{
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p + i);
+        out[i] = __uint_as_float(v.x << 16);
+        out[i + 1] = __uint_as_float(v.x & 0xffff0000u);
+        out[i + 2] = __uint_as_float(v.y << 16);
+        out[i + 3] = __uint_as_float(v.y & 0xffff0000u);
+    }
+}
+
+// Stage `rows` (<= 16) rows of D elements (row stride D in global memory) into
+// a [16][D + 4] fp32 LDS tile; rows past `rows` are zero.
+template <typename TIO, int D>
+__device__ __forceinline__ void stage_rows(float* lds, const TIO* src, int rows, int lane)
+{
+    constexpr int PER = D / 4;   // 16 rows x D elements over 64 lanes
+    const int row = lane >> 2, c0 = (lane & 3) * PER;
+    float v[PER];
+    if (row < rows) {
+        load_vec<PER>(src + (size_t)row * D + c0, v);
+    } else {
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v[i] = 0.f;
+    }
+    float* dst = lds + row * (D + 4) + c0;
+#pragma unroll
+    for (int i = 0; i < PER; i += 4)
+        *reinterpret_cast<f32x4*>(dst + i) = f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
+}
+
+// Stage columns col0..col0+15 of `rows` token rows (row stride D) into a
+// [16][20] fp32 LDS tile; rows past `rows` are zero.
+template <typename TIO, int D>
+__device__ __forceinline__ void stage_block(float* lds, const TIO* src, int col0, int rows, int lane)
+{
+    const int row = lane >> 2, c0 = (lane & 3) * 4;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (row < rows) load_vec<4>(src + (size_t)row * D + col0 + c0, v);
+    *reinterpret_cast<f32x4*>(lds + row * 20 + c0) = f32x4{v[0], v[1], v[2], v[3]};
+}
+
+template <int D>
+struct BwdLds {
+    static constexpr int S = D + 4;   // row stride of the d-wide tiles
+    float K[kSub * S];                // sub-tile keys    [token][dim]
+    float Q[kSub * S];                // sub-tile queries [token][dim]
+    float W[kSub * S];                // chunk-start state rows [row][dim]
+    float P[kSub * S];                // P rows            [row][dim]
+    float H[kSub * S];                // W - G_{<sigma} rows (chunks of several sub-tiles)
+    float dZ[kSub * 20];              // dZ of the block's dims [token][row]
+    float V[kSub * 20];               // V of the block's dims  [token][row]
+    float M[kSub * 20];               // masked K^T Q           [s][t]
+    float dA[kSub * 20];              // dA                     [s][t]
+    float dE[kSub * 20];              // dE                     [row][token]
+    float F[kSub * 20];               // F                      [row][token]
+};
+
+struct BwdArgs {
+    const void* K;
+    const void* Q;
+    const void* V;
+    const float* eta;
+    float eta_scalar;
+    const float* W0;
+    const void* dZ;
+    const float* dWT;     // may be null (zero)
+    void* dV;
+    float* dW0;
+    float* states;        // [BH, nch + 1, d, d]
+    float* dK_part;       // [d/16, BH, T, d]
+    float* dQ_part;       // [d/16, BH, T, d]
+    float* deta_part;     // [d/16, BH, T]
+    int BH, T, chunk;
+};
+
+template <typename TIO, int D>
+__global__ __launch_bounds__(64) void linear_bwd_kernel(BwdArgs a)
+{
+    constexpr int NB = D / 16, S = D + 4;
+    __shared__ BwdLds<D> L;
+    const int lane = threadIdx.x;
+    const int c = lane & 15, g = lane >> 4;
+    int slice, rb;
+    xcd_unit_part(blockIdx.x, NB, slice, rb);
+    if (slice >= a.BH) return;
+    const int r0 = 16 * rb;
+    const int T = a.T, chunk = a.chunk;
+    const int nch = (T + chunk - 1) / chunk;
+    const bool multi = chunk > kSub;
+    const TIO* Kg = static_cast<const TIO*>(a.K) + (size_t)slice * T * D;
+    const TIO* Qg = static_cast<const TIO*>(a.Q) + (size_t)slice * T * D;
+    const TIO* Vg = static_cast<const TIO*>(a.V) + (size_t)slice * T * D;
+    const TIO* dZg = static_cast<const TIO*>(a.dZ) + (size_t)slice * T * D;
+    const float* etag = a.eta ? a.eta + (size_t)slice * T : nullptr;
+    float* states = a.states + (size_t)slice * (nch + 1) * D * D;
+    const size_t part = ((size_t)rb * a.BH + slice) * T;
+
+    auto eta_at = [&](int tok, int len) {
+        return c < len ? (etag ? etag[tok + c] : a.eta_scalar) : 0.f;
+    };
+    auto store_state = [&](int slot, const f32x4* Wr) {
+        float* dst = states + (size_t)slot * D * D + (size_t)r0 * D;
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) dst[(4 * g + v) * D + 16 * b + c] = Wr[b][v];
+    };
+
+    // ------------------------------------------------ forward: chunk-start states
+    f32x4 Wr[NB];   // CL(W) per column block
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Wr[b][v] = a.W0[((size_t)slice * D + r0 + 4 * g + v) * D + 16 * b + c];
+    for (int ch = 0; ch < nch; ++ch) {
+        const int c0 = ch * chunk, c1 = min(c0 + chunk, T);
+        store_state(ch, Wr);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) put_cl<S>(L.W, 16 * b, lane, Wr[b]);
+        for (int t0 = c0; t0 < c1; t0 += kSub) {
+            const int len = min(kSub, c1 - t0);
+            lds_order();
+            stage_rows<TIO, D>(L.K, Kg + (size_t)t0 * D, len, lane);
+            stage_block<TIO, D>(L.V, Vg + (size_t)t0 * D, r0, len, lane);
+            lds_order();
+            // E = W K^T - V (CL: rows 4g + v, token c)
+            f32x4 E = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int b = 0; b < NB; ++b) E = mm16(rl<S>(L.W, 16 * b, lane), rl<S>(L.K, 16 * b, lane), E);
+            const f32x4 Vr = rl<20>(L.V, 0, lane);   // V[token c][row 4g + v], as E
+            const float et = eta_at(t0, len);
+            f32x4 Fm;   // -F
+#pragma unroll
+            for (int v = 0; v < 4; ++v) Fm[v] = -(E[v] - Vr[v]) * et;
+            put_cl<20>(L.F, 0, lane, Fm);
+            lds_order();
+            // W -= F K (contraction over the sub-tile's tokens)
+            const f32x4 Fa = rl<20>(L.F, 0, lane);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) Wr[b] = mm16(Fa, cl<S>(L.K, 16 * b, lane), Wr[b]);
+        }
+    }
+    if (multi) store_state(nch, Wr);
+    __threadfence();   // the states are read back below
+
+    // ------------------------------------------------ reverse
+    f32x4 P[NB], dWa[NB], Hr[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            P[b][v] = a.dWT ? a.dWT[((size_t)slice * D + r0 + 4 * g + v) * D + 16 * b + c] : 0.f;
+    for (int ch = nch - 1; ch >= 0; --ch) {
+        const int c0 = ch * chunk, c1 = min(c0 + chunk, T);
+        lds_order();
+        stage_rows<float, D>(L.W, states + (size_t)ch * D * D + (size_t)r0 * D, 16, lane);
+        if (multi) {
+            const float* src = states + (size_t)(ch + 1) * D * D + (size_t)r0 * D;
+#pragma unroll
+            for (int b = 0; b < NB; ++b)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) Hr[b][v] = src[(4 * g + v) * D + 16 * b + c];
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) dWa[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int nsub = (c1 - c0 + kSub - 1) / kSub;
+        for (int si = nsub - 1; si >= 0; --si) {
+            const int t0 = c0 + si * kSub;
+            const int len = min(kSub, c1 - t0);
+            lds_order();
+            stage_rows<TIO, D>(L.K, Kg + (size_t)t0 * D, len, lane);
+            stage_rows<TIO, D>(L.Q, Qg + (size_t)t0 * D, len, lane);
+            stage_block<TIO, D>(L.V, Vg + (size_t)t0 * D, r0, len, lane);
+            stage_block<TIO, D>(L.dZ, dZg + (size_t)t0 * D, r0, len, lane);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) put_cl<S>(L.P, 16 * b, lane, P[b]);
+            lds_order();
+            // E = W K^T - V, PK = P K^T, S = K Q^T (all CL)
+            f32x4 E = {0.f, 0.f, 0.f, 0.f}, PK = E, Sm = E;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const f32x4 kb = rl<S>(L.K, 16 * b, lane);
+                E = mm16(rl<S>(L.W, 16 * b, lane), kb, E);
+                PK = mm16(rl<S>(L.P, 16 * b, lane), kb, PK);
+                Sm = mm16(kb, rl<S>(L.Q, 16 * b, lane), Sm);
+            }
+            const float et = eta_at(t0, len);
+            const f32x4 Vr = rl<20>(L.V, 0, lane);
+            f32x4 F, Mk;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                E[v] -= Vr[v];
+                F[v] = E[v] * et;
+                Mk[v] = (4 * g + v <= c) ? Sm[v] : 0.f;   // s = 4g + v, t = c
+            }
+            put_cl<20>(L.M, 0, lane, Mk);
+            lds_order();
+            const f32x4 dZa = cl<20>(L.dZ, 0, lane);   // RL(dZ_blk): dZ[row c][token 4g + v]
+            const f32x4 dZb = rl<20>(L.dZ, 0, lane);   // CL(dZ_blk): dZ[row 4g + v][token c]
+            // dF = -dZ M^T - P K^T
+            f32x4 dF = mm16(dZa, rl<20>(L.M, 0, lane), f32x4{0.f, 0.f, 0.f, 0.f});
+            f32x4 dE;
+            float de = 0.f;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                dF[v] = -dF[v] - PK[v];
+                dE[v] = dF[v] * et;
+                de += E[v] * dF[v];
+            }
+            // deta: sum over the block's 16 rows (4 slots x 4 lane groups)
+            de += __shfl_xor(de, 16);
+            de += __shfl_xor(de, 32);
+            if (g == 0 && c < len) a.deta_part[part + t0 + c] = de;
+            // dV = -dE: lane holds dims r0 + 4g .. +3 of token c
+            if (c < len) {
+                TIO* dv = static_cast<TIO*>(a.dV) + ((size_t)slice * T + t0 + c) * D + r0 + 4 * g;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) io<TIO>::store(dv, v, -dE[v]);
+            }
+            // dA = -(F^T dZ) o U: A = RL(F^T) = CL(F) registers, B = CL(dZ_blk)
+            f32x4 dA = mm16(F, dZb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int v = 0; v < 4; ++v) dA[v] = (4 * g + v <= c) ? -dA[v] : 0.f;
+            put_cl<20>(L.dA, 0, lane, dA);
+            put_cl<20>(L.dE, 0, lane, dE);
+            if (multi) {
+                put_cl<20>(L.F, 0, lane, F);
+                lds_order();
+                // H = W - G_{<sigma}: add this sub-tile's update back
+                const f32x4 Fa = rl<20>(L.F, 0, lane);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    Hr[b] = mm16(Fa, cl<S>(L.K, 16 * b, lane), Hr[b]);
+                    put_cl<S>(L.H, 16 * b, lane, Hr[b]);
+                }
+            }
+            lds_order();
+            const f32x4 dAa = rl<20>(L.dA, 0, lane);   // RL(dA)
+            const f32x4 dEa = rl<20>(L.dE, 0, lane);   // RL(dE)
+            f32x4 Fn;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) Fn[v] = -F[v];
+            const float* Hs = multi ? L.H : L.W;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const f32x4 kc = cl<S>(L.K, 16 * b, lane);
+                const f32x4 qc = cl<S>(L.Q, 16 * b, lane);
+                // dK (tokens x dims) = -F^T P + dE^T W + dA Q
+                f32x4 dK = mm16(Fn, cl<S>(L.P, 16 * b, lane), f32x4{0.f, 0.f, 0.f, 0.f});
+                dK = mm16(dE, cl<S>(L.W, 16 * b, lane), dK);
+                dK = mm16(dAa, qc, dK);
+                // dQ (tokens x dims) = dZ^T H + dA^T K
+                f32x4 dQ = mm16(dZb, cl<S>(Hs, 16 * b, lane), f32x4{0.f, 0.f, 0.f, 0.f});
+                dQ = mm16(dA, kc, dQ);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    if (4 * g + v < len) {
+                        const size_t o = (part + t0 + 4 * g + v) * D + 16 * b + c;
+                        a.dK_part[o] = dK[v];
+                        a.dQ_part[o] = dQ[v];
+                    }
+                }
+                // P += dZ Q, dW += dE K
+                P[b] = mm16(dZa, qc, P[b]);
+                dWa[b] = mm16(dEa, kc, dWa[b]);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) P[b] += dWa[b];
+    }
+    float* dW0 = a.dW0 + ((size_t)slice * D + r0) * D;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dW0[(4 * g + v) * D + 16 * b + c] = P[b][v];
+}
+
+// dK, dQ = sum of the row blocks' partials (rounded to the I/O type), deta likewise
+template <typename TIO>
+__global__ __launch_bounds__(256) void linear_bwd_reduce_kernel(
+    const float* __restrict__ dK_part, const float* __restrict__ dQ_part,
+    const float* __restrict__ deta_part, TIO* __restrict__ dK, TIO* __restrict__ dQ,
+    float* __restrict__ deta, size_t n, size_t ntok, int nparts)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        float k = 0.f, q = 0.f;
+        for (int p = 0; p < nparts; ++p) {
+            k += dK_part[(size_t)p * n + i];
+            q += dQ_part[(size_t)p * n + i];
+        }
+        io<TIO>::store(dK, i, k);
+        io<TIO>::store(dQ, i, q);
+        if (deta && i < ntok) {
+            float e = 0.f;
+            for (int p = 0; p < nparts; ++p) e += deta_part[(size_t)p * ntok + i];
+            deta[i] = e;
+        }
+    }
+}
+
+template <typename TIO, int D>
+hipError_t launch_typed(const LinearBwdArgs& a, hipStream_t s)
+{
+    constexpr int NB = D / 16;
+    const int nch = (a.T + a.chunk - 1) / a.chunk;
+    const size_t n = (size_t)a.BH * a.T * D, ntok = (size_t)a.BH * a.T;
+    char* ws = static_cast<char*>(a.workspace);
+    BwdArgs k;
+    k.K = a.K; k.Q = a.Q; k.V = a.V; k.eta = a.eta; k.eta_scalar = a.eta_scalar;
+    k.W0 = a.W0; k.dZ = a.dZ; k.dWT = a.dW_T; k.dV = a.dV; k.dW0 = a.dW0;
+    k.states = reinterpret_cast<float*>(ws);
+    ws += linear_bwd_align((size_t)a.BH * (nch + 1) * D * D * sizeof(float));
+    k.dK_part = reinterpret_cast<float*>(ws);
+    ws += linear_bwd_align((size_t)NB * n * sizeof(float));
+    k.dQ_part = reinterpret_cast<float*>(ws);
+    ws += linear_bwd_align((size_t)NB * n * sizeof(float));
+    k.deta_part = reinterpret_cast<float*>(ws);
+    k.BH = a.BH; k.T = a.T; k.chunk = a.chunk;
+    const unsigned grid = (unsigned)(((a.BH + 7) / 8) * 8 * NB);
+    hipLaunchKernelGGL((linear_bwd_kernel<TIO, D>), dim3(grid), dim3(64), 0, s, k);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned rgrid = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(linear_bwd_reduce_kernel<TIO>, dim3(rgrid), dim3(256), 0, s,
+                       k.dK_part, k.dQ_part, k.deta_part, static_cast<TIO*>(a.dK),
+                       static_cast<TIO*>(a.dQ), a.deta, n, ntok, NB);
+    return hipGetLastError();
+}
+
+template <typename TIO>
+hipError_t launch_dtype(const LinearBwdArgs& a, hipStream_t s)
+{
+    switch (a.d) {
+    case 16: return launch_typed<TIO, 16>(a, s);
+    case 32: return launch_typed<TIO, 32>(a, s);
+    case 64: return launch_typed<TIO, 64>(a, s);
+    case 128: return launch_typed<TIO, 128>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+size_t linear_bwd_align(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
+
+size_t linear_bwd_workspace(int BH, int T, int d, int chunk)
+{
+    const size_t nch = (size_t)(T + chunk - 1) / chunk;
+    const size_t n = (size_t)BH * T * d, nb = (size_t)d / 16;
+    return linear_bwd_align((size_t)BH * (nch + 1) * d * d * sizeof(float)) +
+           2 * linear_bwd_align(nb * n * sizeof(float)) +
+           linear_bwd_align(nb * (size_t)BH * T * sizeof(float));
+}
+
+hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s)
+{
+    return a.bf16 ? launch_dtype<uint16_t>(a, s) : launch_dtype<float>(a, s);
+}
+
+}  // namespace ttt

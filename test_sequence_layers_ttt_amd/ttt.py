@@ -19,7 +19,7 @@ PLAN_AUTO, PLAN_GENERIC, PLAN_MFMA, PLAN_BIGCHUNK = 0, 1, 2, 3
 
 # every symbol include/ttt.h declares
 EXPORTS = ("ttt_linear_workspace_bytes", "ttt_linear_select_plan", "ttt_linear_fwd",
-           "ttt_linear_step",
+           "ttt_linear_step", "ttt_linear_bwd_workspace_bytes", "ttt_linear_bwd",
            "ttt_mlp_workspace_bytes", "ttt_mlp_select_plan", "ttt_mlp_fwd",
            "ttt_status_string", "ttt_plan_name")
 
@@ -48,6 +48,11 @@ def lib() -> ctypes.CDLL:
         L.ttt_linear_select_plan.restype = i
         L.ttt_linear_fwd.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp, i]
         L.ttt_linear_fwd.restype = i
+        L.ttt_linear_bwd_workspace_bytes.argtypes = [i] * 6
+        L.ttt_linear_bwd_workspace_bytes.restype = sz
+        L.ttt_linear_bwd.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     i, i, i, i, i, i, vp, sz, vp]
+        L.ttt_linear_bwd.restype = i
         L.ttt_linear_step.argtypes = [vp, vp, vp, vp, f, vp, vp, i, vp, i, i, i, i, i, i, vp]
         L.ttt_linear_step.restype = i
         L.ttt_mlp_workspace_bytes.argtypes = [i] * 7
@@ -161,6 +166,53 @@ def linear_fwd(K, Q, V, eta, W0, chunk: int, eta_scalar: float = 0.0, *, Z=None,
     if rc != OK:
         raise TTTError(rc, "ttt_linear_fwd")
     return Z, W_out
+
+
+def linear_bwd_workspace_bytes(B, H, T, d, chunk, io_dtype) -> int:
+    return int(lib().ttt_linear_bwd_workspace_bytes(B, H, T, d, chunk, io_dtype))
+
+
+def linear_bwd(K, Q, V, eta, W0, dZ, chunk: int, eta_scalar: float = 0.0, dW_T=None, *,
+               dK=None, dQ=None, dV=None, deta=None, dW0=None, want_deta: bool = True,
+               workspace=None, stream=None) -> Tuple:
+    """Gradients of <dZ, Z> + <dW_T, W_T> through linear_fwd(K, Q, V, eta, W0, chunk).
+    dZ: like K; dW_T: [B, H, d, d] fp32 or None.  Returns (dK, dQ, dV, deta, dW0);
+    deta [B, H, T] fp32 is per token (None when want_deta is False)."""
+    import torch
+    B, H, T, d = K.shape
+    _check(K, "K", (B, H, T, d))
+    _check(Q, "Q", (B, H, T, d), K.dtype)
+    _check(V, "V", (B, H, T, d), K.dtype)
+    _check(dZ, "dZ", (B, H, T, d), K.dtype)
+    _check(W0, "W0", (B, H, d, d), torch.float32)
+    if eta is not None:
+        _check(eta, "eta", (B, H, T), torch.float32)
+    if dW_T is not None:
+        _check(dW_T, "dW_T", (B, H, d, d), torch.float32)
+    dK = torch.empty_like(K) if dK is None else dK
+    dQ = torch.empty_like(K) if dQ is None else dQ
+    dV = torch.empty_like(K) if dV is None else dV
+    dW0 = torch.empty_like(W0) if dW0 is None else dW0
+    if want_deta and deta is None:
+        deta = torch.empty((B, H, T), dtype=torch.float32, device=K.device)
+    for t, name in ((dK, "dK"), (dQ, "dQ"), (dV, "dV")):
+        _check(t, name, (B, H, T, d), K.dtype)
+    _check(dW0, "dW0", (B, H, d, d), torch.float32)
+    if deta is not None:
+        _check(deta, "deta", (B, H, T), torch.float32)
+    io = _io_dtype(K)
+    nbytes = linear_bwd_workspace_bytes(B, H, T, d, chunk, io)
+    if nbytes == 0:
+        raise TTTError(ERR_UNSUPPORTED, "ttt_linear_bwd")
+    ws = _workspace(nbytes, K.device, workspace)
+    rc = lib().ttt_linear_bwd(K.data_ptr(), Q.data_ptr(), V.data_ptr(), _ptr(eta),
+                              float(eta_scalar), W0.data_ptr(), dZ.data_ptr(), _ptr(dW_T),
+                              dK.data_ptr(), dQ.data_ptr(), dV.data_ptr(), _ptr(deta),
+                              dW0.data_ptr(), B, H, T, d, int(chunk), io, _ptr(ws),
+                              ws.numel(), _stream(K.device, stream))
+    if rc != OK:
+        raise TTTError(rc, "ttt_linear_bwd")
+    return dK, dQ, dV, deta, dW0
 
 
 def linear_step(K, Q, V, eta, W_chunk, G, pos: int, chunk: int, eta_scalar: float = 0.0, *,

@@ -152,6 +152,49 @@ def test_step_rejects_bad_arguments(kw, status):
     assert _step(**kw) == status
 
 
+def _bwd(**kw):
+    a = dict(K=FAKE, Q=FAKE, V=FAKE, eta=None, eta_scalar=0.1, W0=FAKE, dZ=FAKE, dWT=None,
+             dK=FAKE, dQ=FAKE, dV=FAKE, deta=None, dW0=FAKE, B=1, H=2, T=40, d=64, chunk=16,
+             io=1, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return ttt.lib().ttt_linear_bwd(a["K"], a["Q"], a["V"], a["eta"], a["eta_scalar"], a["W0"],
+                                    a["dZ"], a["dWT"], a["dK"], a["dQ"], a["dV"], a["deta"],
+                                    a["dW0"], a["B"], a["H"], a["T"], a["d"], a["chunk"], a["io"],
+                                    a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=None), ttt.ERR_INVALID_ARG),
+    (dict(dZ=None), ttt.ERR_INVALID_ARG),
+    (dict(dK=None), ttt.ERR_INVALID_ARG),
+    (dict(dW0=None), ttt.ERR_INVALID_ARG),
+    (dict(dQ=MISALIGNED), ttt.ERR_INVALID_ARG),
+    (dict(dWT=FAKE + 8), ttt.ERR_INVALID_ARG),
+    (dict(deta=FAKE + 2), ttt.ERR_INVALID_ARG),
+    (dict(eta_scalar=math.inf), ttt.ERR_INVALID_ARG),
+    (dict(T=0), ttt.ERR_INVALID_ARG),
+    (dict(chunk=-1), ttt.ERR_INVALID_ARG),
+    (dict(io=4), ttt.ERR_INVALID_ARG),
+    (dict(d=48), ttt.ERR_UNSUPPORTED),
+    (dict(ws=None), ttt.ERR_WORKSPACE),
+    (dict(wsb=1024), ttt.ERR_WORKSPACE),
+    (dict(ws=FAKE + 64), ttt.ERR_WORKSPACE),
+])
+def test_bwd_rejects_bad_arguments(kw, status):
+    assert _bwd(**kw) == status
+
+
+def test_bwd_workspace_size():
+    # chunk-start states (ceil(T/b) + 1 per slice), then dK and dQ partials per
+    # 16-row block, then deta partials; each piece rounded up to 256 bytes
+    B, H, T, d, b = 1, 2, 40, 64, 16
+    up = lambda x: (x + 255) // 256 * 256
+    states = up(B * H * (3 + 1) * d * d * 4)
+    parts = 2 * up(4 * B * H * T * d * 4) + up(4 * B * H * T * 4)
+    assert ttt.linear_bwd_workspace_bytes(B, H, T, d, b, 1) == states + parts
+    assert ttt.linear_bwd_workspace_bytes(B, H, T, 48, b, 1) == 0
+
+
 def test_plan_selection_and_workspace_are_host_only():
     assert ttt.linear_select_plan(1, 1, 256, 16, 16, ttt.DTYPE_F32) == ttt.PLAN_GENERIC
     assert ttt.linear_select_plan(1, 1, 256, 16, 16, 0, ttt.PLAN_GENERIC) == ttt.PLAN_GENERIC
