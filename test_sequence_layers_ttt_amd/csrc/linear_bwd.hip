@@ -109,37 +109,6 @@ __device__ __forceinline__ void load_vec(const uint16_t* p, float* out)
     }
 }
 
-// Stage `rows` (<= 16) rows of D elements (row stride D in global memory) into
-// a [16][D + 4] fp32 LDS tile; rows past `rows` are zero.
-template <typename TIO, int D>
-__device__ __forceinline__ void stage_rows(float* lds, const TIO* src, int rows, int lane)
-{
-    constexpr int PER = D / 4;   // 16 rows x D elements over 64 lanes
-    const int row = lane >> 2, c0 = (lane & 3) * PER;
-    float v[PER];
-    if (row < rows) {
-        load_vec<PER>(src + (size_t)row * D + c0, v);
-    } else {
-#pragma unroll
-        for (int i = 0; i < PER; ++i) v[i] = 0.f;
-    }
-    float* dst = lds + row * (D + 4) + c0;
-#pragma unroll
-    for (int i = 0; i < PER; i += 4)
-        *reinterpret_cast<f32x4*>(dst + i) = f32x4{v[i], v[i + 1], v[i + 2], v[i + 3]};
-}
-
-// Stage columns col0..col0+15 of `rows` token rows (row stride D) into a
-// [16][20] fp32 LDS tile; rows past `rows` are zero.
-template <typename TIO, int D>
-__device__ __forceinline__ void stage_block(float* lds, const TIO* src, int col0, int rows, int lane)
-{
-    const int row = lane >> 2, c0 = (lane & 3) * 4;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (row < rows) load_vec<4>(src + (size_t)row * D + col0 + c0, v);
-    *reinterpret_cast<f32x4*>(lds + row * 20 + c0) = f32x4{v[0], v[1], v[2], v[3]};
-}
-
 template <int D>
 struct BwdLds {
     static constexpr int S = D + 4;   // row stride of the d-wide tiles
@@ -174,19 +143,33 @@ struct BwdArgs {
     int BH, T, chunk;
 };
 
+// One sub-tile's inputs, loaded into registers one sub-tile ahead: lane l holds
+// D/4 elements of row l/4 of K and Q, 4 elements of row l/4 of the block's V
+// and dZ columns, eta of token l % 16, and (when the sub-tile opens a chunk in
+// the reverse pass) D/4 elements of row l/4 of the chunk-start state.
+template <int D>
+struct SubTile {
+    static constexpr int PER = D / 4;
+    float k[PER], q[PER], w[PER], v[4], dz[4];
+    float eta;
+};
+
 template <typename TIO, int D>
 __global__ __launch_bounds__(64) void linear_bwd_kernel(BwdArgs a)
 {
-    constexpr int NB = D / 16, S = D + 4;
+    constexpr int NB = D / 16, S = D + 4, PER = D / 4;
     __shared__ BwdLds<D> L;
     const int lane = threadIdx.x;
     const int c = lane & 15, g = lane >> 4;
+    const int frow = lane >> 2, fcol = (lane & 3) * PER, fblk = (lane & 3) * 4;
     int slice, rb;
     xcd_unit_part(blockIdx.x, NB, slice, rb);
     if (slice >= a.BH) return;
     const int r0 = 16 * rb;
     const int T = a.T, chunk = a.chunk;
     const int nch = (T + chunk - 1) / chunk;
+    const int nsub = (chunk + kSub - 1) / kSub;            // sub-tiles of a full chunk
+    const int last = (T - 1) / chunk * nsub + ((T - 1) % chunk) / kSub;   // last sub-tile
     const bool multi = chunk > kSub;
     const TIO* Kg = static_cast<const TIO*>(a.K) + (size_t)slice * T * D;
     const TIO* Qg = static_cast<const TIO*>(a.Q) + (size_t)slice * T * D;
@@ -196,8 +179,57 @@ __global__ __launch_bounds__(64) void linear_bwd_kernel(BwdArgs a)
     float* states = a.states + (size_t)slice * (nch + 1) * D * D;
     const size_t part = ((size_t)rb * a.BH + slice) * T;
 
-    auto eta_at = [&](int tok, int len) {
-        return c < len ? (etag ? etag[tok + c] : a.eta_scalar) : 0.f;
+    // sub-tile j: chunk j / nsub, tokens [t0, t0 + len)
+    auto span = [&](int j, int& ch, int& si, int& t0, int& len) {
+        ch = j / nsub;
+        si = j - ch * nsub;
+        t0 = ch * chunk + si * kSub;
+        len = min(kSub, min(ch * chunk + chunk, T) - t0);
+    };
+    // registers <- sub-tile j (with Q and dZ in the reverse pass, and the
+    // chunk-start state rows when `state` is set)
+    auto fetch = [&](SubTile<D>& f, int j, bool rev, bool state) {
+        int ch, si, t0, len;
+        span(j, ch, si, t0, len);
+        if (frow < len) {
+            const size_t row = (size_t)(t0 + frow) * D;
+            load_vec<PER>(Kg + row + fcol, f.k);
+            load_vec<4>(Vg + row + r0 + fblk, f.v);
+            if (rev) {
+                load_vec<PER>(Qg + row + fcol, f.q);
+                load_vec<4>(dZg + row + r0 + fblk, f.dz);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < PER; ++i) f.k[i] = f.q[i] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f.v[i] = f.dz[i] = 0.f;
+        }
+        f.eta = c < len ? (etag ? etag[t0 + c] : a.eta_scalar) : 0.f;
+        if (state)
+            load_vec<PER>(states + (size_t)ch * D * D + (size_t)(r0 + frow) * D + fcol, f.w);
+    };
+    // LDS <- registers
+    auto put = [&](const SubTile<D>& f, bool rev, bool state) {
+        float* kd = L.K + frow * S + fcol;
+#pragma unroll
+        for (int i = 0; i < PER; i += 4)
+            *reinterpret_cast<f32x4*>(kd + i) = f32x4{f.k[i], f.k[i + 1], f.k[i + 2], f.k[i + 3]};
+        *reinterpret_cast<f32x4*>(L.V + frow * 20 + fblk) = f32x4{f.v[0], f.v[1], f.v[2], f.v[3]};
+        if (rev) {
+            float* qd = L.Q + frow * S + fcol;
+#pragma unroll
+            for (int i = 0; i < PER; i += 4)
+                *reinterpret_cast<f32x4*>(qd + i) = f32x4{f.q[i], f.q[i + 1], f.q[i + 2], f.q[i + 3]};
+            *reinterpret_cast<f32x4*>(L.dZ + frow * 20 + fblk) =
+                f32x4{f.dz[0], f.dz[1], f.dz[2], f.dz[3]};
+        }
+        if (state) {
+            float* wd = L.W + frow * S + fcol;
+#pragma unroll
+            for (int i = 0; i < PER; i += 4)
+                *reinterpret_cast<f32x4*>(wd + i) = f32x4{f.w[i], f.w[i + 1], f.w[i + 2], f.w[i + 3]};
+        }
     };
     auto store_state = [&](int slot, const f32x4* Wr) {
         float* dst = states + (size_t)slot * D * D + (size_t)r0 * D;
@@ -207,39 +239,48 @@ __global__ __launch_bounds__(64) void linear_bwd_kernel(BwdArgs a)
             for (int v = 0; v < 4; ++v) dst[(4 * g + v) * D + 16 * b + c] = Wr[b][v];
     };
 
+    SubTile<D> cur, nxt;
+
     // ------------------------------------------------ forward: chunk-start states
     f32x4 Wr[NB];   // CL(W) per column block
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) Wr[b][v] = a.W0[((size_t)slice * D + r0 + 4 * g + v) * D + 16 * b + c];
-    for (int ch = 0; ch < nch; ++ch) {
-        const int c0 = ch * chunk, c1 = min(c0 + chunk, T);
-        store_state(ch, Wr);
+        for (int v = 0; v < 4; ++v)
+            Wr[b][v] = a.W0[((size_t)slice * D + r0 + 4 * g + v) * D + 16 * b + c];
+    fetch(cur, 0, false, false);
+    for (int j = 0; j <= last; ++j) {
+        int ch, si, t0, len;
+        span(j, ch, si, t0, len);
+        lds_order();
+        if (si == 0) {
+            store_state(ch, Wr);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) put_cl<S>(L.W, 16 * b, lane, Wr[b]);
-        for (int t0 = c0; t0 < c1; t0 += kSub) {
-            const int len = min(kSub, c1 - t0);
-            lds_order();
-            stage_rows<TIO, D>(L.K, Kg + (size_t)t0 * D, len, lane);
-            stage_block<TIO, D>(L.V, Vg + (size_t)t0 * D, r0, len, lane);
-            lds_order();
-            // E = W K^T - V (CL: rows 4g + v, token c)
-            f32x4 E = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int b = 0; b < NB; ++b) E = mm16(rl<S>(L.W, 16 * b, lane), rl<S>(L.K, 16 * b, lane), E);
-            const f32x4 Vr = rl<20>(L.V, 0, lane);   // V[token c][row 4g + v], as E
-            const float et = eta_at(t0, len);
-            f32x4 Fm;   // -F
-#pragma unroll
-            for (int v = 0; v < 4; ++v) Fm[v] = -(E[v] - Vr[v]) * et;
-            put_cl<20>(L.F, 0, lane, Fm);
-            lds_order();
-            // W -= F K (contraction over the sub-tile's tokens)
-            const f32x4 Fa = rl<20>(L.F, 0, lane);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) Wr[b] = mm16(Fa, cl<S>(L.K, 16 * b, lane), Wr[b]);
+            for (int b = 0; b < NB; ++b) put_cl<S>(L.W, 16 * b, lane, Wr[b]);
         }
+        put(cur, false, false);
+        const float et = cur.eta;
+        if (j < last) fetch(nxt, j + 1, false, false);
+        lds_order();
+        // E = W K^T - V (CL: rows 4g + v, token c), two accumulation chains
+        f32x4 E0 = {0.f, 0.f, 0.f, 0.f}, E1 = E0;
+#pragma unroll
+        for (int b = 0; b < NB; b += 2) {
+            E0 = mm16(rl<S>(L.W, 16 * b, lane), rl<S>(L.K, 16 * b, lane), E0);
+            if (b + 1 < NB)
+                E1 = mm16(rl<S>(L.W, 16 * (b + 1), lane), rl<S>(L.K, 16 * (b + 1), lane), E1);
+        }
+        const f32x4 Vr = rl<20>(L.V, 0, lane);   // V[token c][row 4g + v], as E
+        f32x4 Fm;   // -F
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Fm[v] = -(E0[v] + E1[v] - Vr[v]) * et;
+        put_cl<20>(L.F, 0, lane, Fm);
+        lds_order();
+        // W -= F K (contraction over the sub-tile's tokens)
+        const f32x4 Fa = rl<20>(L.F, 0, lane);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) Wr[b] = mm16(Fa, cl<S>(L.K, 16 * b, lane), Wr[b]);
+        cur = nxt;
     }
     if (multi) store_state(nch, Wr);
     __threadfence();   // the states are read back below
@@ -247,127 +288,133 @@ __global__ __launch_bounds__(64) void linear_bwd_kernel(BwdArgs a)
     // ------------------------------------------------ reverse
     f32x4 P[NB], dWa[NB], Hr[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+    for (int b = 0; b < NB; ++b) {
+        dWa[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             P[b][v] = a.dWT ? a.dWT[((size_t)slice * D + r0 + 4 * g + v) * D + 16 * b + c] : 0.f;
-    for (int ch = nch - 1; ch >= 0; --ch) {
-        const int c0 = ch * chunk, c1 = min(c0 + chunk, T);
+    }
+    // a sub-tile opens its chunk in the reverse pass when it is the chunk's last
+    auto opens = [&](int j) {
+        int ch, si, t0, len;
+        span(j, ch, si, t0, len);
+        return j == last || si == nsub - 1;
+    };
+    fetch(cur, last, true, true);
+    for (int j = last; j >= 0; --j) {
+        int ch, si, t0, len;
+        span(j, ch, si, t0, len);
+        const bool first = opens(j);
         lds_order();
-        stage_rows<float, D>(L.W, states + (size_t)ch * D * D + (size_t)r0 * D, 16, lane);
-        if (multi) {
+        put(cur, true, first);
+        const float et = cur.eta;
+        if (first && multi) {
             const float* src = states + (size_t)(ch + 1) * D * D + (size_t)r0 * D;
 #pragma unroll
             for (int b = 0; b < NB; ++b)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) Hr[b][v] = src[(4 * g + v) * D + 16 * b + c];
         }
+        if (j > 0) fetch(nxt, j - 1, true, opens(j - 1));
 #pragma unroll
-        for (int b = 0; b < NB; ++b) dWa[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int nsub = (c1 - c0 + kSub - 1) / kSub;
-        for (int si = nsub - 1; si >= 0; --si) {
-            const int t0 = c0 + si * kSub;
-            const int len = min(kSub, c1 - t0);
-            lds_order();
-            stage_rows<TIO, D>(L.K, Kg + (size_t)t0 * D, len, lane);
-            stage_rows<TIO, D>(L.Q, Qg + (size_t)t0 * D, len, lane);
-            stage_block<TIO, D>(L.V, Vg + (size_t)t0 * D, r0, len, lane);
-            stage_block<TIO, D>(L.dZ, dZg + (size_t)t0 * D, r0, len, lane);
+        for (int b = 0; b < NB; ++b) put_cl<S>(L.P, 16 * b, lane, P[b]);
+        lds_order();
+        // E = W K^T - V, PK = P K^T, S = K Q^T (all CL)
+        f32x4 E = {0.f, 0.f, 0.f, 0.f}, PK = E, Sm = E;
 #pragma unroll
-            for (int b = 0; b < NB; ++b) put_cl<S>(L.P, 16 * b, lane, P[b]);
+        for (int b = 0; b < NB; ++b) {
+            const f32x4 kb = rl<S>(L.K, 16 * b, lane);
+            E = mm16(rl<S>(L.W, 16 * b, lane), kb, E);
+            PK = mm16(rl<S>(L.P, 16 * b, lane), kb, PK);
+            Sm = mm16(kb, rl<S>(L.Q, 16 * b, lane), Sm);
+        }
+        const f32x4 Vr = rl<20>(L.V, 0, lane);
+        f32x4 F, Mk;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            E[v] -= Vr[v];
+            F[v] = E[v] * et;
+            Mk[v] = (4 * g + v <= c) ? Sm[v] : 0.f;   // s = 4g + v, t = c
+        }
+        put_cl<20>(L.M, 0, lane, Mk);
+        lds_order();
+        const f32x4 dZa = cl<20>(L.dZ, 0, lane);   // RL(dZ_blk): dZ[row c][token 4g + v]
+        const f32x4 dZb = rl<20>(L.dZ, 0, lane);   // CL(dZ_blk): dZ[row 4g + v][token c]
+        // dF = -dZ M^T - P K^T
+        f32x4 dF = mm16(dZa, rl<20>(L.M, 0, lane), f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 dE;
+        float de = 0.f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            dF[v] = -dF[v] - PK[v];
+            dE[v] = dF[v] * et;
+            de += E[v] * dF[v];
+        }
+        // deta: sum over the block's 16 rows (4 slots x 4 lane groups)
+        de += __shfl_xor(de, 16);
+        de += __shfl_xor(de, 32);
+        if (g == 0 && c < len) a.deta_part[part + t0 + c] = de;
+        // dV = -dE: lane holds dims r0 + 4g .. +3 of token c
+        if (c < len) {
+            TIO* dv = static_cast<TIO*>(a.dV) + ((size_t)slice * T + t0 + c) * D + r0 + 4 * g;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) io<TIO>::store(dv, v, -dE[v]);
+        }
+        // dA = -(F^T dZ) o U: A = RL(F^T) = CL(F) registers, B = CL(dZ_blk)
+        f32x4 dA = mm16(F, dZb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dA[v] = (4 * g + v <= c) ? -dA[v] : 0.f;
+        put_cl<20>(L.dA, 0, lane, dA);
+        put_cl<20>(L.dE, 0, lane, dE);
+        if (multi) {
+            put_cl<20>(L.F, 0, lane, F);
             lds_order();
-            // E = W K^T - V, PK = P K^T, S = K Q^T (all CL)
-            f32x4 E = {0.f, 0.f, 0.f, 0.f}, PK = E, Sm = E;
+            // H = W - G_{<sigma}: add this sub-tile's update back
+            const f32x4 Fa = rl<20>(L.F, 0, lane);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const f32x4 kb = rl<S>(L.K, 16 * b, lane);
-                E = mm16(rl<S>(L.W, 16 * b, lane), kb, E);
-                PK = mm16(rl<S>(L.P, 16 * b, lane), kb, PK);
-                Sm = mm16(kb, rl<S>(L.Q, 16 * b, lane), Sm);
-            }
-            const float et = eta_at(t0, len);
-            const f32x4 Vr = rl<20>(L.V, 0, lane);
-            f32x4 F, Mk;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                E[v] -= Vr[v];
-                F[v] = E[v] * et;
-                Mk[v] = (4 * g + v <= c) ? Sm[v] : 0.f;   // s = 4g + v, t = c
-            }
-            put_cl<20>(L.M, 0, lane, Mk);
-            lds_order();
-            const f32x4 dZa = cl<20>(L.dZ, 0, lane);   // RL(dZ_blk): dZ[row c][token 4g + v]
-            const f32x4 dZb = rl<20>(L.dZ, 0, lane);   // CL(dZ_blk): dZ[row 4g + v][token c]
-            // dF = -dZ M^T - P K^T
-            f32x4 dF = mm16(dZa, rl<20>(L.M, 0, lane), f32x4{0.f, 0.f, 0.f, 0.f});
-            f32x4 dE;
-            float de = 0.f;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                dF[v] = -dF[v] - PK[v];
-                dE[v] = dF[v] * et;
-                de += E[v] * dF[v];
-            }
-            // deta: sum over the block's 16 rows (4 slots x 4 lane groups)
-            de += __shfl_xor(de, 16);
-            de += __shfl_xor(de, 32);
-            if (g == 0 && c < len) a.deta_part[part + t0 + c] = de;
-            // dV = -dE: lane holds dims r0 + 4g .. +3 of token c
-            if (c < len) {
-                TIO* dv = static_cast<TIO*>(a.dV) + ((size_t)slice * T + t0 + c) * D + r0 + 4 * g;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) io<TIO>::store(dv, v, -dE[v]);
-            }
-            // dA = -(F^T dZ) o U: A = RL(F^T) = CL(F) registers, B = CL(dZ_blk)
-            f32x4 dA = mm16(F, dZb, f32x4{0.f, 0.f, 0.f, 0.f});
-#pragma unroll
-            for (int v = 0; v < 4; ++v) dA[v] = (4 * g + v <= c) ? -dA[v] : 0.f;
-            put_cl<20>(L.dA, 0, lane, dA);
-            put_cl<20>(L.dE, 0, lane, dE);
-            if (multi) {
-                put_cl<20>(L.F, 0, lane, F);
-                lds_order();
-                // H = W - G_{<sigma}: add this sub-tile's update back
-                const f32x4 Fa = rl<20>(L.F, 0, lane);
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    Hr[b] = mm16(Fa, cl<S>(L.K, 16 * b, lane), Hr[b]);
-                    put_cl<S>(L.H, 16 * b, lane, Hr[b]);
-                }
-            }
-            lds_order();
-            const f32x4 dAa = rl<20>(L.dA, 0, lane);   // RL(dA)
-            const f32x4 dEa = rl<20>(L.dE, 0, lane);   // RL(dE)
-            f32x4 Fn;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) Fn[v] = -F[v];
-            const float* Hs = multi ? L.H : L.W;
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const f32x4 kc = cl<S>(L.K, 16 * b, lane);
-                const f32x4 qc = cl<S>(L.Q, 16 * b, lane);
-                // dK (tokens x dims) = -F^T P + dE^T W + dA Q
-                f32x4 dK = mm16(Fn, cl<S>(L.P, 16 * b, lane), f32x4{0.f, 0.f, 0.f, 0.f});
-                dK = mm16(dE, cl<S>(L.W, 16 * b, lane), dK);
-                dK = mm16(dAa, qc, dK);
-                // dQ (tokens x dims) = dZ^T H + dA^T K
-                f32x4 dQ = mm16(dZb, cl<S>(Hs, 16 * b, lane), f32x4{0.f, 0.f, 0.f, 0.f});
-                dQ = mm16(dA, kc, dQ);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    if (4 * g + v < len) {
-                        const size_t o = (part + t0 + 4 * g + v) * D + 16 * b + c;
-                        a.dK_part[o] = dK[v];
-                        a.dQ_part[o] = dQ[v];
-                    }
-                }
-                // P += dZ Q, dW += dE K
-                P[b] = mm16(dZa, qc, P[b]);
-                dWa[b] = mm16(dEa, kc, dWa[b]);
+                Hr[b] = mm16(Fa, cl<S>(L.K, 16 * b, lane), Hr[b]);
+                put_cl<S>(L.H, 16 * b, lane, Hr[b]);
             }
         }
+        lds_order();
+        const f32x4 dAa = rl<20>(L.dA, 0, lane);   // RL(dA)
+        const f32x4 dEa = rl<20>(L.dE, 0, lane);   // RL(dE)
+        f32x4 Fn;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) P[b] += dWa[b];
+        for (int v = 0; v < 4; ++v) Fn[v] = -F[v];
+        const float* Hs = multi ? L.H : L.W;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const f32x4 kc = cl<S>(L.K, 16 * b, lane);
+            const f32x4 qc = cl<S>(L.Q, 16 * b, lane);
+            // dK (tokens x dims) = -F^T P + dE^T W + dA Q
+            f32x4 dK = mm16(Fn, cl<S>(L.P, 16 * b, lane), f32x4{0.f, 0.f, 0.f, 0.f});
+            dK = mm16(dE, cl<S>(L.W, 16 * b, lane), dK);
+            dK = mm16(dAa, qc, dK);
+            // dQ (tokens x dims) = dZ^T H + dA^T K
+            f32x4 dQ = mm16(dZb, cl<S>(Hs, 16 * b, lane), f32x4{0.f, 0.f, 0.f, 0.f});
+            dQ = mm16(dA, kc, dQ);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                if (4 * g + v < len) {
+                    const size_t o = (part + t0 + 4 * g + v) * D + 16 * b + c;
+                    a.dK_part[o] = dK[v];
+                    a.dQ_part[o] = dQ[v];
+                }
+            }
+            // P += dZ Q, dW += dE K
+            P[b] = mm16(dZa, qc, P[b]);
+            dWa[b] = mm16(dEa, kc, dWa[b]);
+        }
+        if (si == 0) {   // the chunk is done: its dW is the previous chunk's dW_next
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                P[b] += dWa[b];
+                dWa[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        if (j > 0) cur = nxt;
     }
     float* dW0 = a.dW0 + ((size_t)slice * D + r0) * D;
 #pragma unroll
