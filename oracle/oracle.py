@@ -49,6 +49,10 @@ def _load():
                                           ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, ctypes.c_int]
         lib.ttt_oracle_linear.restype = ctypes.c_int
+        lib.ttt_oracle_linear_read.argtypes = [P, P, P, P, ctypes.c_double, P, P, P,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        lib.ttt_oracle_linear_read.restype = ctypes.c_int
         lib.ttt_oracle_linear_bwd.argtypes = [P, P, P, P, ctypes.c_double, P, P, P,
                                               P, P, P, P, P,
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -80,8 +84,10 @@ def _ptr(a):
 
 
 def linear(K, Q, V, eta, eta_scalar: float, W0, chunk: int,
-           nthreads: int = 0, return_threads: bool = False):
+           nthreads: int = 0, return_threads: bool = False, read_start: bool = False):
     """TTT-Linear scan.  K, Q, V: [n, T, d]; eta: [n, T] or None; W0: [n, d, d].
+    read_start: every token of a chunk reads with the chunk-start state (apply,
+    then update) instead of the inclusive read.
     Returns (Z [n, T, d], W_T [n, d, d]) in fp64 (and the thread count if asked)."""
     K, Q, V, W0 = _f64(K), _f64(Q), _f64(V), _f64(W0)
     eta = _f64(eta)
@@ -91,9 +97,9 @@ def linear(K, Q, V, eta, eta_scalar: float, W0, chunk: int,
         assert eta.shape == (n, T)
     Z = np.empty((n, T, d), np.float64)
     W = np.empty((n, d, d), np.float64)
-    rc = _load().ttt_oracle_linear(_ptr(K), _ptr(Q), _ptr(V), _ptr(eta), float(eta_scalar),
-                                   _ptr(W0), _ptr(Z), _ptr(W), n, T, d, int(chunk),
-                                   int(nthreads))
+    rc = _load().ttt_oracle_linear_read(_ptr(K), _ptr(Q), _ptr(V), _ptr(eta),
+                                        float(eta_scalar), _ptr(W0), _ptr(Z), _ptr(W), n, T, d,
+                                        int(chunk), int(bool(read_start)), int(nthreads))
     if rc <= 0:
         raise ValueError("ttt_oracle_linear rejected its arguments")
     return (Z, W, rc) if return_threads else (Z, W)

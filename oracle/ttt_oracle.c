@@ -24,7 +24,7 @@
 /* ------------------------------------------------------------------------ */
 static void linear_slice(const double* K, const double* Q, const double* V,
                          const double* eta, double eta_scalar, const double* W0,
-                         double* Z, double* W_out, int T, int d, int chunk)
+                         double* Z, double* W_out, int T, int d, int chunk, int read_start)
 {
     double* W  = (double*)malloc(sizeof(double) * d * d);  /* running state      */
     double* Ws = (double*)malloc(sizeof(double) * d * d);  /* chunk-start state  */
@@ -50,11 +50,16 @@ static void linear_slice(const double* K, const double* Q, const double* V,
             /* G += eta_t e_t k_t^T  (eta of the writing token) */
             for (int i = 0; i < d; ++i)
                 for (int j = 0; j < d; ++j) G[i * d + j] += et * e[i] * k[j];
-            /* z_t = (Ws - G) q_t : own update included */
+            /* z_t = (Ws - G) q_t : own update included.  The other read order
+             * reads every token of the chunk with the chunk-start state:
+             * z_t = Ws q_t (apply, then update). */
             double* z = Z + (size_t)t * d;
             for (int i = 0; i < d; ++i) {
                 double s = 0.0;
-                for (int j = 0; j < d; ++j) s += (Ws[i * d + j] - G[i * d + j]) * q[j];
+                if (read_start)
+                    for (int j = 0; j < d; ++j) s += Ws[i * d + j] * q[j];
+                else
+                    for (int j = 0; j < d; ++j) s += (Ws[i * d + j] - G[i * d + j]) * q[j];
                 z[i] = s;
             }
         }
@@ -332,7 +337,7 @@ static void mlp_slice(const double* K, const double* Q, const double* V,
 /* Thread pool over (batch, head) slices.                                    */
 /* ------------------------------------------------------------------------ */
 typedef struct {
-    int is_mlp, is_bwd;
+    int is_mlp, is_bwd, read_start;
     const double *K, *Q, *V, *eta, *W0, *W1, *b1, *W2, *b2, *dZ, *dWT;
     double eta_scalar;
     double *Z, *W_out, *W1_o, *b1_o, *W2_o, *b2_o, *dK, *dQ, *dV, *deta, *dW0;
@@ -356,7 +361,7 @@ static void* worker(void* arg)
             size_t dd = (size_t)j->d * j->d;
             linear_slice(j->K + s * td, j->Q + s * td, j->V + s * td, eta, j->eta_scalar,
                          j->W0 + s * dd, j->Z + s * td, j->W_out + s * dd,
-                         j->T, j->d, j->chunk);
+                         j->T, j->d, j->chunk, j->read_start);
         } else {
             size_t n1 = (size_t)j->hd * j->d;
             mlp_slice(j->K + s * td, j->Q + s * td, j->V + s * td, eta, j->eta_scalar,
@@ -400,10 +405,21 @@ int ttt_oracle_linear(const double* K, const double* Q, const double* V,
                       double* Z, double* W_out,
                       int BH, int T, int d, int chunk, int nthreads)
 {
+    return ttt_oracle_linear_read(K, Q, V, eta, eta_scalar, W0, Z, W_out, BH, T, d, chunk, 0,
+                                  nthreads);
+}
+
+int ttt_oracle_linear_read(const double* K, const double* Q, const double* V,
+                           const double* eta, double eta_scalar, const double* W0,
+                           double* Z, double* W_out,
+                           int BH, int T, int d, int chunk, int read_start, int nthreads)
+{
     if (!K || !Q || !V || !W0 || !Z || !W_out) return -1;
     if (BH <= 0 || T <= 0 || d <= 0 || chunk <= 0) return -1;
+    if (read_start != 0 && read_start != 1) return -1;
     job_t j;
     memset(&j, 0, sizeof j);
+    j.read_start = read_start;
     j.K = K; j.Q = Q; j.V = V; j.eta = eta; j.eta_scalar = eta_scalar; j.W0 = W0;
     j.Z = Z; j.W_out = W_out; j.BH = BH; j.T = T; j.d = d; j.chunk = chunk;
     j.nthreads = nthreads;

@@ -20,7 +20,10 @@
  * Readings where the pages leave a step open (each is listed in the design notes):
  *   - loss constant 1/2 (gradient e k^T, no factor 2);
  *   - the chunk update is the eta-weighted SUM of the per-token gradients;
- *   - token t reads with every in-chunk update up to and including its own;
+ *   - token t reads with every in-chunk update up to and including its own
+ *     (ttt_oracle_linear_read also offers the chunk-start read, the
+ *     apply-then-update order of large-chunk TTT: PaperTrace "5 · TestingTime
+ *     训练与长上下文" §1.1 and the read/write-order discussion after §3.1);
  *   - eta_t belongs to the writing token (it scales token t's gradient);
  *   - TTT-Linear has no bias; TTT-MLP biases b1, b2 are part of the state and
  *     are updated by the same step, or are absent (frozen zero) when NULL;
@@ -48,6 +51,15 @@ int ttt_oracle_linear(const double* K, const double* Q, const double* V,
                       const double* eta, double eta_scalar, const double* W0,
                       double* Z, double* W_out,
                       int BH, int T, int d, int chunk, int nthreads);
+
+/* The same scan with a choice of read order: read_start = 0 is the inclusive
+ * read above (z_t = (W_c - G_t) q_t); read_start = 1 reads every token of a
+ * chunk with the chunk-start state (z_t = W_c q_t: apply, then update).  The
+ * state update is the same in both. */
+int ttt_oracle_linear_read(const double* K, const double* Q, const double* V,
+                           const double* eta, double eta_scalar, const double* W0,
+                           double* Z, double* W_out,
+                           int BH, int T, int d, int chunk, int read_start, int nthreads);
 
 /* Vector-Jacobian product of ttt_oracle_linear: for L = <dZ, Z> + <dW_T, W_T>
  * (dW_T may be NULL for zero), writes dK, dQ, dV : [BH, T, d], deta : [BH, T]

@@ -52,6 +52,9 @@ MUTANTS = {
         "s += W2s[(size_t)i * hd + u] * hr[u];"),
     "MLP backward skips gelu'": (
         "dl[u] = s * ttt_oracle_gelu_prime(h[u]);", "dl[u] = s;"),
+    "chunk-start read includes the chunk's updates": (
+        "for (int j = 0; j < d; ++j) s += Ws[i * d + j] * q[j];",
+        "for (int j = 0; j < d; ++j) s += (Ws[i * d + j] - G[i * d + j]) * q[j];"),
     # the vector-Jacobian product of the TTT-Linear scan
     "VJP: dq read at the chunk-start state": (
         "acc += (Wc[i * d + j] - G[i * d + j]) * dz[i];", "acc += Wc[i * d + j] * dz[i];"),

@@ -345,3 +345,67 @@ def test_golden_fixtures_unchanged():
             outs = {"Z": Z, "W1": W1, "b1": b1, "W2": W2, "b2": b2}
         for k, v in case["outputs"].items():
             np.testing.assert_allclose(outs[k], np.array(v), rtol=0, atol=1e-13)
+
+
+# ------------------------------------------- TTT-Linear, chunk-start read order
+# Every token of a chunk reads with the chunk-start state (apply, then update):
+# the large-chunk ordering whose in-chunk dependencies are left to window
+# attention (PaperTrace "5 · TestingTime 训练与长上下文" §1.1, and the
+# read/write-order discussion after its §3.1).
+def test_read_start_keeps_the_state_update():
+    """The read order changes the outputs only: the final state is identical."""
+    rng = np.random.default_rng(41)
+    K, Q, V, eta, W0 = rand_linear(rng, 3, 37, 6)
+    for chunk in (1, 4, 16, 50):
+        _, Wa = oracle.linear(K, Q, V, eta, 0.0, W0, chunk)
+        _, Wb = oracle.linear(K, Q, V, eta, 0.0, W0, chunk, read_start=True)
+        np.testing.assert_array_equal(Wa, Wb)
+
+
+@pytest.mark.parametrize("d,T", [(4, 9), (8, 33)])
+def test_read_start_b1_is_read_before_write(d, T):
+    """b = 1: z_t = W_{t-1} q_t with the separately coded rank-1 recursion
+    W_t = W_{t-1}(I - eta_t k_t k_t^T) + eta_t v_t k_t^T."""
+    rng = np.random.default_rng(42)
+    K, Q, V, eta, W0 = rand_linear(rng, 2, T, d)
+    Z, WT = oracle.linear(K, Q, V, eta, 0.0, W0, chunk=1, read_start=True)
+    for s in range(2):
+        W = W0[s].copy()
+        I = np.eye(d)
+        for t in range(T):
+            np.testing.assert_allclose(Z[s, t], W @ Q[s, t], rtol=0, atol=1e-12)
+            k, v, b = K[s, t], V[s, t], eta[s, t]
+            W = W @ (I - b * np.outer(k, k)) + b * np.outer(v, k)
+        np.testing.assert_allclose(WT[s], W, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("chunk", [3, 8, 20])
+def test_read_start_differs_by_the_causal_term(chunk):
+    """z_incl_t - z_start_t = -sum_{s <= t in the chunk} eta_s (W_c k_s - v_s)(k_s . q_t),
+    with the chunk-start states W_c from the chunk update
+    W_{c+1} = W_c - sum_s eta_s (W_c k_s - v_s) k_s^T written out here."""
+    rng = np.random.default_rng(43)
+    n, T, d = 2, 29, 5
+    K, Q, V, eta, W0 = rand_linear(rng, n, T, d)
+    Zi, _ = oracle.linear(K, Q, V, eta, 0.0, W0, chunk)
+    Zs, _ = oracle.linear(K, Q, V, eta, 0.0, W0, chunk, read_start=True)
+    for s in range(n):
+        W = W0[s].copy()
+        for c0 in range(0, T, chunk):
+            c1 = min(T, c0 + chunk)
+            E = K[s, c0:c1] @ W.T - V[s, c0:c1]          # rows: e_s^T
+            for t in range(c0, c1):
+                corr = np.zeros(d)
+                for u in range(c0, t + 1):
+                    corr += eta[s, u] * E[u - c0] * (K[s, u] @ Q[s, t])
+                np.testing.assert_allclose(Zi[s, t] - Zs[s, t], -corr, rtol=0, atol=1e-11)
+                np.testing.assert_allclose(Zs[s, t], W @ Q[s, t], rtol=0, atol=1e-11)
+            W = W - (eta[s, c0:c1, None] * E).T @ K[s, c0:c1]
+
+
+def test_read_start_zero_state_reads_zero():
+    """W0 = 0 and one chunk over the whole sequence: every token reads W0 = 0."""
+    rng = np.random.default_rng(44)
+    K, Q, V, eta, _ = rand_linear(rng, 2, 12, 4)
+    Z, _ = oracle.linear(K, Q, V, eta, 0.0, np.zeros((2, 4, 4)), chunk=12, read_start=True)
+    assert np.all(Z == 0)
