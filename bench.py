@@ -65,15 +65,16 @@ def algorithmic_bytes(wl) -> float:
     return float(wl.BH) * (wl.T * per_tok + 2 * state)
 
 
-def algorithmic_flops(wl) -> float:
+def algorithmic_flops(wl, read_start: bool = False) -> float:
     """Flops of the dual form as stated for the method: per chunk of n tokens,
     TTT-Linear 3*2*d^2*n (W K, W Q, E K^T) + 2*d*n*(n+1) (causal half of the
-    K^T Q and E S products); TTT-MLP 7*2*h*d*n + 2*(d+h)*n*(n+1)."""
+    K^T Q and E S products; none with the chunk-start read order); TTT-MLP
+    7*2*h*d*n + 2*(d+h)*n*(n+1)."""
     total = 0.0
     for c0 in range(0, wl.T, wl.chunk):
         n = min(wl.chunk, wl.T - c0)
         if wl.model == "linear":
-            total += 6.0 * wl.d * wl.d * n + 2.0 * wl.d * n * (n + 1)
+            total += 6.0 * wl.d * wl.d * n + (0.0 if read_start else 2.0 * wl.d * n * (n + 1))
         else:
             h = wl.hidden
             total += 14.0 * h * wl.d * n + 2.0 * (wl.d + h) * n * (n + 1)
@@ -361,6 +362,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0)
     ap.add_argument("--decode", type=int, default=0,
                     help="time ttt_linear_step continuing every sequence by N tokens")
+    ap.add_argument("--read-start", action="store_true",
+                    help="TTT-Linear with the chunk-start read order")
     ap.add_argument("--bwd", action="store_true",
                     help="time ttt_linear_bwd (the backward pass) on the workload")
     ap.add_argument("--decode-batch", type=int, default=0,
@@ -396,8 +399,14 @@ def main():
     dev = torch.device("cuda:0")
     plan_req = PLANS[args.plan]
     io_code = ttt.DTYPE_BF16 if wl.io == "bf16" else ttt.DTYPE_F32
-    sel = ttt.linear_select_plan if wl.model == "linear" else ttt.mlp_select_plan
-    plan = sel(wl.B, wl.H, wl.T, wl.d, wl.chunk, io_code, plan_req)
+    read_mode = ttt.READ_CHUNK_START if args.read_start else ttt.READ_INCLUSIVE
+    if args.read_start and wl.model != "linear":
+        raise SystemExit("--read-start applies to TTT-Linear")
+    if wl.model == "linear":
+        plan = ttt.linear_select_plan(wl.B, wl.H, wl.T, wl.d, wl.chunk, io_code, plan_req,
+                                      read_mode)
+    else:
+        plan = ttt.mlp_select_plan(wl.B, wl.H, wl.T, wl.d, wl.chunk, io_code, plan_req)
     if plan < 0:
         raise SystemExit("plan %s cannot run %s" % (args.plan, wl.name))
     plan_name = ttt.plan_name(plan)
@@ -451,7 +460,7 @@ def main():
         if wl.model == "linear":
             ttt.linear_fwd(a["K"], a["Q"], a["V"], a["eta"], a["W0"], wl.chunk,
                            eta_scalar=x["eta_scalar"], Z=o["Z"], W_out=o["W"], workspace=ws,
-                           plan=plan_req, stream=stream)
+                           plan=plan_req, stream=stream, read_mode=read_mode)
         else:
             ttt.mlp_fwd(a["K"], a["Q"], a["V"], a["eta"], a["W1"], a["b1"], a["W2"], a["b2"],
                         wl.chunk, eta_scalar=x["eta_scalar"], Z=o["Z"], W1_out=o["W1"],
@@ -478,11 +487,13 @@ def main():
     tokens = B * T
     value = tokens / (ms_step * 1e-3)
     abytes = algorithmic_bytes(wl)
-    aflops = algorithmic_flops(wl)
+    aflops = algorithmic_flops(wl, args.read_start)
     achieved_gbs = abytes / (ms_event * 1e-3) / 1e9
     achieved_tfs = aflops / (ms_event * 1e-3) / 1e12
-    traffic = traffic_from_profiles(wl, plan_name)
-    hbm_bound = wl.model == "linear" and plan_name != "bigchunk"
+    traffic = None if args.read_start else traffic_from_profiles(wl, plan_name)
+    # the large-chunk plan is a matrix-core workload with the inclusive read; with the
+    # chunk-start read its Z pass is a plain W_c Q product and HBM bounds the call
+    hbm_bound = wl.model == "linear" and (plan_name != "bigchunk" or args.read_start)
     if hbm_bound:
         roof = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4),
@@ -514,7 +525,8 @@ def main():
         t1 = time.perf_counter()
         if wl.model == "linear":
             Zo, Wo, nth = oracle.linear(xo["K"], xo["Q"], xo["V"], xo["eta"], xo["eta_scalar"],
-                                        xo["W0"], wl.chunk, return_threads=True)
+                                        xo["W0"], wl.chunk, return_threads=True,
+                                        read_start=args.read_start)
             refs = {"Z": Zo, "W": Wo}
         else:
             r = oracle.mlp(xo["K"], xo["Q"], xo["V"], xo["eta"], xo["eta_scalar"], xo["W1"],
@@ -555,7 +567,8 @@ def main():
         "dtype": ("f32" if wl.io == "f32" or plan_name == "generic"
                   else ("f16" if wl.model == "mlp" else "bf16")),
         "data": "synthetic",
-        "config": {"workload": wl.name, "scan": "ttt_" + wl.model, "batch": B, "heads": H,
+        "config": {"workload": wl.name + ("_read_start" if args.read_start else ""),
+                   "scan": "ttt_" + wl.model, "batch": B, "heads": H,
                    "seq_len": T, "head_dim": d, "chunk": wl.chunk, "plan": plan_name,
                    "state_dtype": "f32", "parallelism": "single_gpu"},
         "roofline": roof,

@@ -88,6 +88,18 @@ typedef enum {
                                    multiple of 32 >= 128 */
 } ttt_plan;
 
+/* Read order of a chunk's tokens.  INCLUSIVE: token t reads with the chunk's
+ * updates up to and including its own (the dual form above).  CHUNK_START:
+ * every token of a chunk reads with the chunk-start state, z_t = W_c q_t (apply,
+ * then update: the large-chunk ordering that leaves in-chunk dependencies to
+ * window attention, PaperTrace "5 · TestingTime 训练与长上下文" §1.1 and the
+ * read/write-order discussion after its §3.1; with chunk == 1 the
+ * read-before-write delta rule).  The state update is the same in both. */
+typedef enum {
+    TTT_READ_INCLUSIVE = 0,
+    TTT_READ_CHUNK_START = 1
+} ttt_read_mode;
+
 /* ------------------------------------------------------------------------ */
 /* TTT-Linear                                                                */
 /* ------------------------------------------------------------------------ */
@@ -175,6 +187,23 @@ int ttt_linear_step(const void* K, const void* Q, const void* V,
                     float* W_chunk, float* G, int pos,
                     void* Z, int B, int H, int n, int d, int chunk, int io_dtype,
                     void* stream);
+
+/* ttt_linear_fwd with a choice of read order (ttt_read_mode); ttt_linear_fwd is
+ * this call with TTT_READ_INCLUSIVE.  CHUNK_START runs on the GENERIC and
+ * BIGCHUNK plans (MFMA: TTT_ERR_UNSUPPORTED); an unknown read_mode is
+ * TTT_ERR_INVALID_ARG.  Workspace sizes are those of ttt_linear_workspace_bytes
+ * for the plan that runs. */
+int ttt_linear_fwd_ex(const void* K, const void* Q, const void* V,
+                      const float* eta, float eta_scalar,
+                      const float* W0,
+                      void* Z, float* W_out,
+                      int B, int H, int T, int d, int chunk, int io_dtype,
+                      void* workspace, size_t workspace_bytes,
+                      void* stream, int plan, int read_mode);
+
+/* Plan that ttt_linear_fwd_ex would run for this shape and read order. */
+int ttt_linear_select_plan_ex(int B, int H, int T, int d, int chunk, int io_dtype, int plan,
+                              int read_mode);
 
 /* ------------------------------------------------------------------------ */
 /* TTT-MLP (hidden width 4d)                                                 */

@@ -25,14 +25,18 @@ bool dims_ok(int B, int H, int T, int d, int chunk)
     return n < 4.0e18L && (long double)B * H * 64 < 2.0e9L;
 }
 
-int linear_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
+int linear_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan,
+                int read_mode = TTT_READ_INCLUSIVE)
 {
     if (!dims_ok(B, H, T, d, chunk)) return TTT_ERR_INVALID_ARG;
     if (io_dtype != TTT_DTYPE_F32 && io_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARG;
     if (plan < TTT_PLAN_AUTO || plan > TTT_PLAN_BIGCHUNK) return TTT_ERR_INVALID_ARG;
+    if (read_mode != TTT_READ_INCLUSIVE && read_mode != TTT_READ_CHUNK_START)
+        return TTT_ERR_INVALID_ARG;
     if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
     const int bf16 = io_dtype == TTT_DTYPE_BF16;
-    const bool mfma = linear_mfma_supported(d, chunk, bf16);
+    // the small-chunk matrix-core kernels implement the inclusive read only
+    const bool mfma = read_mode == TTT_READ_INCLUSIVE && linear_mfma_supported(d, chunk, bf16);
     const bool big = linear_bigchunk_supported(d, chunk, bf16);
     switch (plan) {
     case TTT_PLAN_GENERIC: return TTT_PLAN_GENERIC;
@@ -96,6 +100,12 @@ int ttt_linear_select_plan(int B, int H, int T, int d, int chunk, int io_dtype, 
     return linear_plan(B, H, T, d, chunk, io_dtype, plan);
 }
 
+int ttt_linear_select_plan_ex(int B, int H, int T, int d, int chunk, int io_dtype, int plan,
+                              int read_mode)
+{
+    return linear_plan(B, H, T, d, chunk, io_dtype, plan, read_mode);
+}
+
 size_t ttt_linear_workspace_bytes(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
 {
     int p = linear_plan(B, H, T, d, chunk, io_dtype, plan);
@@ -109,12 +119,24 @@ int ttt_linear_fwd(const void* K, const void* Q, const void* V,
                    int B, int H, int T, int d, int chunk, int io_dtype,
                    void* workspace, size_t workspace_bytes, void* stream, int plan)
 {
+    return ttt_linear_fwd_ex(K, Q, V, eta, eta_scalar, W0, Z, W_out, B, H, T, d, chunk,
+                             io_dtype, workspace, workspace_bytes, stream, plan,
+                             TTT_READ_INCLUSIVE);
+}
+
+int ttt_linear_fwd_ex(const void* K, const void* Q, const void* V,
+                      const float* eta, float eta_scalar, const float* W0,
+                      void* Z, float* W_out,
+                      int B, int H, int T, int d, int chunk, int io_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream, int plan,
+                      int read_mode)
+{
     if (!K || !Q || !V || !W0 || !Z || !W_out) return TTT_ERR_INVALID_ARG;
     if (!aligned(K, 16) || !aligned(Q, 16) || !aligned(V, 16) || !aligned(Z, 16) ||
         !aligned(W0, 16) || !aligned(W_out, 16))
         return TTT_ERR_INVALID_ARG;
     if (eta ? !aligned(eta, 4) : !std::isfinite(eta_scalar)) return TTT_ERR_INVALID_ARG;
-    const int p = linear_plan(B, H, T, d, chunk, io_dtype, plan);
+    const int p = linear_plan(B, H, T, d, chunk, io_dtype, plan, read_mode);
     if (p < 0) return p;
     const size_t need = ttt_linear_workspace_bytes(B, H, T, d, chunk, io_dtype, p);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
@@ -124,6 +146,7 @@ int ttt_linear_fwd(const void* K, const void* Q, const void* V,
     a.K = K; a.Q = Q; a.V = V; a.eta = eta; a.eta_scalar = eta_scalar; a.W0 = W0;
     a.Z = Z; a.W_out = W_out; a.BH = B * H; a.T = T; a.d = d; a.chunk = chunk;
     a.bf16 = io_dtype == TTT_DTYPE_BF16;
+    a.read_start = read_mode == TTT_READ_CHUNK_START;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (p) {
@@ -192,6 +215,7 @@ int ttt_linear_step(const void* K, const void* Q, const void* V,
     a.K = K; a.Q = Q; a.V = V; a.eta = eta; a.eta_scalar = eta_scalar; a.W0 = W_chunk;
     a.Z = Z; a.W_out = W_chunk; a.BH = B * H; a.T = n; a.d = d; a.chunk = chunk;
     a.bf16 = io_dtype == TTT_DTYPE_BF16;
+    a.read_start = 0;
     a.workspace = nullptr; a.workspace_bytes = 0;
     return launch_status(launch_linear_step(a, G, pos, reinterpret_cast<hipStream_t>(stream)));
 }

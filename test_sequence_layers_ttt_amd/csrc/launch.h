@@ -17,6 +17,7 @@ struct LinearArgs {
     float* W_out;
     int BH, T, d, chunk;
     int bf16;              // 1: K/Q/V/Z are bf16, 0: fp32
+    int read_start;        // 1: every token reads with its chunk-start state
     void* workspace;
     size_t workspace_bytes;
 };
@@ -42,7 +43,7 @@ struct MlpArgs {
     size_t workspace_bytes;
 };
 
-// fp32 vector-ALU dual form, any chunk, d <= 128.
+// fp32 vector-ALU dual form, any chunk, d <= 128, either read order.
 hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
 
 // bf16 MFMA path for chunk <= 16 or a multiple of 16; d in {32, 64, 128}.
@@ -54,7 +55,8 @@ hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
 bool linear_coop_supported(int d, int chunk, int bf16);
 hipError_t launch_linear_coop(const LinearArgs& a, hipStream_t s);
 
-// three-stage large-chunk path; chunk a multiple of 32, >= 128; d in {64, 128}; bf16.
+// three-stage large-chunk path; chunk a multiple of 32, >= 128; d in {64, 128}; bf16;
+// either read order.
 bool linear_bigchunk_supported(int d, int chunk, int bf16);
 size_t linear_bigchunk_workspace(int BH, int T, int d, int chunk);
 hipError_t launch_linear_bigchunk(const LinearArgs& a, hipStream_t s);

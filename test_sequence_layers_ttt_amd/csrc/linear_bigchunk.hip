@@ -272,7 +272,9 @@ __global__ __launch_bounds__(64) void bigchunk_chain_kernel(
 // eta modes of kernel C: scalar, per-token single loads, per-token 16-byte loads
 enum { kSegEtaScalar = 0, kSegEtaToken = 1, kSegEtaToken4 = 2 };
 
-template <int D, int ETA, bool FULL, int RB>
+// START: the chunk-start read order, Z_tau = Q_tau W_c^T for every sub-tile (no E,
+// no running M, no causal term; K, V and eta are not read).
+template <int D, int ETA, bool FULL, int RB, bool START>
 __global__ __launch_bounds__(4 * D / RB) void bigchunk_seg_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
@@ -314,14 +316,19 @@ __global__ __launch_bounds__(4 * D / RB) void bigchunk_seg_kernel(
         lpos[r] = grow[r] * G + (ggr[r] ^ tile16_swizzle<D>(grow[r]));
     }
     auto gload = [&](int tau, int r) {
+        if constexpr (START) {
+            if (which[r] == 0) return u32x4{0u, 0u, 0u, 0u};
+        }
         const uint16_t* src = which[r] ? Q : K;
         return *(const u32x4*)(src + (tok0 + tok(tau, grow[r])) * D + 8 * ggr[r]);
     };
     // this lane's V (token c, features out0 + 16 rb + 4g ..) and eta (tokens 4g ..)
     auto vload = [&](int tau, int rb) {
+        if constexpr (START) return u32x2{0u, 0u};
         return *(const u32x2*)(V + (tok0 + tok(tau, c)) * D + out0 + 16 * rb + 4 * g);
     };
     auto eload = [&](int tau) {
+        if constexpr (START) return f32x4{0.f, 0.f, 0.f, 0.f};
         if (ETA == kSegEtaToken4) {
             const int tt = tau < ntile ? tau : ntile - 1;
             return *(const f32x4*)(eta + tok0 + 16 * tt + 4 * g);
@@ -388,8 +395,23 @@ __global__ __launch_bounds__(4 * D / RB) void bigchunk_seg_kernel(
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             const int gi = c * G + ((4 * m + g) ^ tile16_swizzle<D>(c));
-            kop[m] = Kt[gi];
+            if constexpr (!START) kop[m] = Kt[gi];
             qop[m] = Qt[gi];
+        }
+        if constexpr (START) {
+            // every token of the chunk reads the chunk-start state
+            const int n = FULL ? 16 : min(16, nc - 16 * tau);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                f32x4 Zt = {0, 0, 0, 0};
+#pragma unroll
+                for (int m = 0; m < NM; ++m) Zt = mfma32(Wf[rb][m], qop[m], Zt);
+                if (FULL || c < n)
+                    *(u32x2*)(Z + (tok0 + 16 * tau + c) * D + out0 + 16 * rb + 4 * g) =
+                        pack_bf16x4(Zt);
+            }
+            __syncthreads();
+            return;
         }
         // K with the feature in the lanes: supplying lane (r, q) of group g reads
         // the 8 bytes K[4g + r][32m + 8q + 4h .. +3] of block jb = 2m + h
@@ -476,13 +498,14 @@ __global__ __launch_bounds__(4 * D / RB) void bigchunk_seg_kernel(
 }
 
 
-template <int D, int ETA, bool FULL>
+template <int D, int ETA, bool FULL, bool START = false>
 void launch_seg(const LinearArgs& a, const float* Wc, int nchunks, hipStream_t s)
 {
     // two 16-row state blocks per wave: one wave per SIMD, each K/Q operand and
     // score serving both blocks
     constexpr int RB = 2;
-    hipLaunchKernelGGL((bigchunk_seg_kernel<D, ETA, FULL, RB>), dim3((unsigned)(a.BH * nchunks)),
+    hipLaunchKernelGGL((bigchunk_seg_kernel<D, ETA, FULL, RB, START>),
+                       dim3((unsigned)(a.BH * nchunks)),
                        dim3(4 * D / RB), 0, s, (const uint16_t*)a.K, (const uint16_t*)a.Q,
                        (const uint16_t*)a.V, a.eta, a.eta_scalar, Wc, (uint16_t*)a.Z, a.T, a.chunk,
                        nchunks);
@@ -517,7 +540,10 @@ hipError_t launch_d(const LinearArgs& a, hipStream_t s)
     // every sub-tile full: T (and the chunk, a multiple of 32) divide into 16s
     const bool full = a.T % 16 == 0;
     const bool eta4 = a.eta && full && reinterpret_cast<uintptr_t>(a.eta) % 16 == 0;
-    if (full) {
+    if (a.read_start) {
+        if (full) launch_seg<D, kSegEtaScalar, true, true>(a, Wc, nchunks, s);
+        else launch_seg<D, kSegEtaScalar, false, true>(a, Wc, nchunks, s);
+    } else if (full) {
         if (!a.eta) launch_seg<D, kSegEtaScalar, true>(a, Wc, nchunks, s);
         else if (eta4) launch_seg<D, kSegEtaToken4, true>(a, Wc, nchunks, s);
         else launch_seg<D, kSegEtaToken, true>(a, Wc, nchunks, s);

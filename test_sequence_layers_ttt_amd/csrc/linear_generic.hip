@@ -14,6 +14,9 @@
 // is ever formed: Z_tau = M Q_tau - E_tau diag(eta) triu(K_tau^T Q_tau),
 // M <- M - E_tau diag(eta) K_tau^T, and W_{c+1} = M at the chunk end.
 //
+// With the chunk-start read order every token of a chunk reads W_c: Z_tau = W_c Q_tau,
+// and the state moves exactly as above.
+//
 // Work split: one 256-thread workgroup per (batch*head, block of 16 output
 // rows).  Output row i of Z and of the state depends only on row i of W0 and
 // feature i of V (plus all of K, Q, eta), so row blocks never communicate.
@@ -32,7 +35,7 @@ template <typename TIO>
 __global__ __launch_bounds__(256) void linear_generic_kernel(
     const TIO* __restrict__ K, const TIO* __restrict__ Q, const TIO* __restrict__ V,
     const float* __restrict__ eta, float eta_scalar, const float* W0,
-    TIO* __restrict__ Z, float* W_out, int T, int d, int chunk)
+    TIO* __restrict__ Z, float* W_out, int T, int d, int chunk, int read_start)
 {
     __shared__ float sWs[kRows][kPad];   // chunk-start state rows
     __shared__ float sM[kRows][kPad];    // running state rows
@@ -127,14 +130,18 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(
             }
             __syncthreads();
 
-            // ---- Z = M Q - E diag(eta) S ----
+            // ---- Z = M Q - E diag(eta) S  (chunk-start read: Z = W_c Q) ----
             {
                 int t = tid / kRows, r = tid % kRows;
                 if (r < R && t < n) {
-                    float acc = 0.f;
-                    for (int j = 0; j < d; ++j) acc = fmaf(sM[r][j], sQ[t][j], acc);
-                    float corr = 0.f;
-                    for (int s = 0; s <= t; ++s) corr = fmaf(sEta[s] * sS[s][t], sE[r][s], corr);
+                    float acc = 0.f, corr = 0.f;
+                    if (read_start) {
+                        for (int j = 0; j < d; ++j) acc = fmaf(sWs[r][j], sQ[t][j], acc);
+                    } else {
+                        for (int j = 0; j < d; ++j) acc = fmaf(sM[r][j], sQ[t][j], acc);
+                        for (int s = 0; s <= t; ++s)
+                            corr = fmaf(sEta[s] * sS[s][t], sE[r][s], corr);
+                    }
                     io<TIO>::store(Z, (tok0 + s0 + t) * d + r0 + r, acc - corr);
                 }
             }
@@ -177,12 +184,12 @@ hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s)
         hipLaunchKernelGGL(linear_generic_kernel<uint16_t>, grid, block, 0, s,
                            (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V,
                            a.eta, a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.T, a.d,
-                           a.chunk);
+                           a.chunk, a.read_start);
     } else {
         hipLaunchKernelGGL(linear_generic_kernel<float>, grid, block, 0, s,
                            (const float*)a.K, (const float*)a.Q, (const float*)a.V,
                            a.eta, a.eta_scalar, a.W0, (float*)a.Z, a.W_out, a.T, a.d,
-                           a.chunk);
+                           a.chunk, a.read_start);
     }
     return hipGetLastError();
 }

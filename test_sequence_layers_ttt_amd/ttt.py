@@ -16,10 +16,12 @@ LIB_PATH = os.path.join(_PKG, "libttt_amd.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3, -4
 DTYPE_F32, DTYPE_BF16 = 0, 1
 PLAN_AUTO, PLAN_GENERIC, PLAN_MFMA, PLAN_BIGCHUNK = 0, 1, 2, 3
+READ_INCLUSIVE, READ_CHUNK_START = 0, 1
 
 # every symbol include/ttt.h declares
 EXPORTS = ("ttt_linear_workspace_bytes", "ttt_linear_select_plan", "ttt_linear_fwd",
            "ttt_linear_step", "ttt_linear_bwd_workspace_bytes", "ttt_linear_bwd",
+           "ttt_linear_fwd_ex", "ttt_linear_select_plan_ex",
            "ttt_mlp_workspace_bytes", "ttt_mlp_select_plan", "ttt_mlp_fwd",
            "ttt_status_string", "ttt_plan_name")
 
@@ -48,6 +50,11 @@ def lib() -> ctypes.CDLL:
         L.ttt_linear_select_plan.restype = i
         L.ttt_linear_fwd.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp, i]
         L.ttt_linear_fwd.restype = i
+        L.ttt_linear_fwd_ex.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, i, i, i, i, i, i, vp, sz,
+                                        vp, i, i]
+        L.ttt_linear_fwd_ex.restype = i
+        L.ttt_linear_select_plan_ex.argtypes = [i] * 8
+        L.ttt_linear_select_plan_ex.restype = i
         L.ttt_linear_bwd_workspace_bytes.argtypes = [i] * 6
         L.ttt_linear_bwd_workspace_bytes.restype = sz
         L.ttt_linear_bwd.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -116,8 +123,11 @@ def linear_workspace_bytes(B, H, T, d, chunk, io_dtype, plan=PLAN_AUTO) -> int:
     return int(lib().ttt_linear_workspace_bytes(B, H, T, d, chunk, io_dtype, plan))
 
 
-def linear_select_plan(B, H, T, d, chunk, io_dtype, plan=PLAN_AUTO) -> int:
-    return int(lib().ttt_linear_select_plan(B, H, T, d, chunk, io_dtype, plan))
+def linear_select_plan(B, H, T, d, chunk, io_dtype, plan=PLAN_AUTO,
+                       read_mode: int = READ_INCLUSIVE) -> int:
+    if read_mode == READ_INCLUSIVE:
+        return int(lib().ttt_linear_select_plan(B, H, T, d, chunk, io_dtype, plan))
+    return int(lib().ttt_linear_select_plan_ex(B, H, T, d, chunk, io_dtype, plan, read_mode))
 
 
 def mlp_workspace_bytes(B, H, T, d, chunk, io_dtype, plan=PLAN_AUTO) -> int:
@@ -138,9 +148,11 @@ def _workspace(nbytes, device, workspace):
 
 
 def linear_fwd(K, Q, V, eta, W0, chunk: int, eta_scalar: float = 0.0, *, Z=None, W_out=None,
-               workspace=None, plan: int = PLAN_AUTO, stream=None) -> Tuple:
+               workspace=None, plan: int = PLAN_AUTO, stream=None,
+               read_mode: int = READ_INCLUSIVE) -> Tuple:
     """TTT-Linear forward scan.  K, Q, V: [B, H, T, d] fp32 or bf16; eta: [B, H, T]
-    fp32 or None (then eta_scalar); W0: [B, H, d, d] fp32.  Returns (Z, W_out)."""
+    fp32 or None (then eta_scalar); W0: [B, H, d, d] fp32; read_mode: READ_INCLUSIVE
+    or READ_CHUNK_START.  Returns (Z, W_out)."""
     import torch
     B, H, T, d = K.shape
     _check(K, "K", (B, H, T, d))
@@ -156,13 +168,14 @@ def linear_fwd(K, Q, V, eta, W0, chunk: int, eta_scalar: float = 0.0, *, Z=None,
     _check(Z, "Z", (B, H, T, d), K.dtype)
     _check(W_out, "W_out", (B, H, d, d), torch.float32)
     io = _io_dtype(K)
-    nbytes = linear_workspace_bytes(B, H, T, d, chunk, io, plan)
+    p = linear_select_plan(B, H, T, d, chunk, io, plan, read_mode)
+    nbytes = linear_workspace_bytes(B, H, T, d, chunk, io, p) if p > 0 else 0
     ws = _workspace(nbytes, K.device, workspace)
-    rc = lib().ttt_linear_fwd(K.data_ptr(), Q.data_ptr(), V.data_ptr(), _ptr(eta),
-                              float(eta_scalar), W0.data_ptr(), Z.data_ptr(), W_out.data_ptr(),
-                              B, H, T, d, int(chunk), io, _ptr(ws),
-                              0 if ws is None else ws.numel(), _stream(K.device, stream),
-                              int(plan))
+    rc = lib().ttt_linear_fwd_ex(K.data_ptr(), Q.data_ptr(), V.data_ptr(), _ptr(eta),
+                                 float(eta_scalar), W0.data_ptr(), Z.data_ptr(),
+                                 W_out.data_ptr(), B, H, T, d, int(chunk), io, _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(K.device, stream),
+                                 int(plan), int(read_mode))
     if rc != OK:
         raise TTTError(rc, "ttt_linear_fwd")
     return Z, W_out

@@ -195,6 +195,39 @@ def test_bwd_workspace_size():
     assert ttt.linear_bwd_workspace_bytes(B, H, T, 48, b, 1) == 0
 
 
+def _linear_ex(read_mode, **kw):
+    a = dict(K=FAKE, Q=FAKE, V=FAKE, eta=FAKE, eta_scalar=0.1, W0=FAKE, Z=FAKE, W=FAKE,
+             B=1, H=1, T=16, d=16, chunk=16, io=0, ws=None, wsb=0, stream=None, plan=0)
+    a.update(kw)
+    return ttt.lib().ttt_linear_fwd_ex(a["K"], a["Q"], a["V"], a["eta"], a["eta_scalar"],
+                                       a["W0"], a["Z"], a["W"], a["B"], a["H"], a["T"], a["d"],
+                                       a["chunk"], a["io"], a["ws"], a["wsb"], a["stream"],
+                                       a["plan"], read_mode)
+
+
+@pytest.mark.parametrize("read_mode,kw,status", [
+    (2, dict(), ttt.ERR_INVALID_ARG),
+    (-1, dict(), ttt.ERR_INVALID_ARG),
+    (1, dict(K=None), ttt.ERR_INVALID_ARG),
+    (1, dict(d=64, io=1, plan=ttt.PLAN_MFMA), ttt.ERR_UNSUPPORTED),
+    (1, dict(d=24), ttt.ERR_UNSUPPORTED),
+    (1, dict(d=64, io=1, chunk=256, T=512, plan=ttt.PLAN_BIGCHUNK), ttt.ERR_WORKSPACE),
+])
+def test_linear_ex_rejects_bad_arguments(read_mode, kw, status):
+    assert _linear_ex(read_mode, **kw) == status
+
+
+def test_read_order_plan_selection():
+    R = ttt.READ_CHUNK_START
+    # small chunks: the matrix-core kernels read inclusively only
+    assert ttt.linear_select_plan(8, 12, 2048, 64, 16, 1) == ttt.PLAN_MFMA
+    assert ttt.linear_select_plan(8, 12, 2048, 64, 16, 1, read_mode=R) == ttt.PLAN_GENERIC
+    assert ttt.linear_select_plan(8, 12, 2048, 64, 16, 1, ttt.PLAN_MFMA, R) == ttt.ERR_UNSUPPORTED
+    # large chunks: the three-stage plan in both orders
+    assert ttt.linear_select_plan(1, 16, 4096, 128, 2048, 1, read_mode=R) == ttt.PLAN_BIGCHUNK
+    assert ttt.linear_select_plan(1, 1, 64, 64, 16, 1, 0, 7) == ttt.ERR_INVALID_ARG
+
+
 def test_plan_selection_and_workspace_are_host_only():
     assert ttt.linear_select_plan(1, 1, 256, 16, 16, ttt.DTYPE_F32) == ttt.PLAN_GENERIC
     assert ttt.linear_select_plan(1, 1, 256, 16, 16, 0, ttt.PLAN_GENERIC) == ttt.PLAN_GENERIC
