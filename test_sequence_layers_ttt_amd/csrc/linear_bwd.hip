@@ -14,10 +14,13 @@
 //   dQ    = H^T dZ + K dA
 //   dW    = P_final + sum_sigma dE K^T        (= the previous chunk's dW_next)
 // Every product above except the sums behind dK, dQ and deta is separable by
-// state row: a wave owns 16 rows of one (batch, head) state, runs the forward
-// recurrence for them (saving each chunk-start state to the workspace), then
-// the reverse recurrence.  Its contributions to dK, dQ and deta (sums over the
-// rows) go to per-row-block partial buffers that a second kernel adds up.
+// state row: a workgroup owns 16 rows of one (batch, head) state, runs the
+// forward recurrence for them (saving each chunk-start state to the workspace),
+// then the reverse recurrence.  Its waves split the state's column blocks: each
+// keeps its blocks of W, P, dW and H and computes its blocks of dK and dQ, and
+// the contractions over all columns (E, P K^T, K Q^T) are summed from per-wave
+// partial tiles in LDS.  Contributions to dK, dQ and deta (sums over the rows)
+// go to per-row-block partial buffers that a second kernel adds up.
 //
 // All products run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32), operands
 // staged through LDS in row-major fp32 tiles with padded rows.  Register forms
@@ -109,20 +112,27 @@ __device__ __forceinline__ void load_vec(const uint16_t* p, float* out)
     }
 }
 
+// Waves per workgroup: each owns NB / NW of the d/16 column blocks.
 template <int D>
+constexpr int bwd_waves()
+{
+    return D == 128 ? 2 : (D >= 32 ? D / 16 : 1);
+}
+
+template <int D, int NW>
 struct BwdLds {
     static constexpr int S = D + 4;   // row stride of the d-wide tiles
     float K[kSub * S];                // sub-tile keys    [token][dim]
     float Q[kSub * S];                // sub-tile queries [token][dim]
-    float W[kSub * S];                // chunk-start state rows [row][dim]
-    float P[kSub * S];                // P rows            [row][dim]
-    float H[kSub * S];                // W - G_{<sigma} rows (chunks of several sub-tiles)
-    float dZ[kSub * 20];              // dZ of the block's dims [token][row]
+    float W[kSub * S];                // chunk-start state rows [row][dim] (own blocks per wave)
+    float P[kSub * S];                // P rows [row][dim] (own blocks per wave)
     float V[kSub * 20];               // V of the block's dims  [token][row]
-    float M[kSub * 20];               // masked K^T Q           [s][t]
-    float dA[kSub * 20];              // dA                     [s][t]
-    float dE[kSub * 20];              // dE                     [row][token]
-    float F[kSub * 20];               // F                      [row][token]
+    float dZ[kSub * 20];              // dZ of the block's dims [token][row]
+    float part[NW][3][kSub * 20];     // per-wave partial E, P K^T, K Q^T
+    float M[NW][kSub * 20];           // masked K^T Q           [s][t]
+    float dA[NW][kSub * 20];          // dA                     [s][t]
+    float dE[NW][kSub * 20];          // dE                     [row][token]
+    float F[NW][kSub * 20];           // F                      [row][token]
 };
 
 struct BwdArgs {
@@ -143,25 +153,42 @@ struct BwdArgs {
     int BH, T, chunk;
 };
 
-// One sub-tile's inputs, loaded into registers one sub-tile ahead: lane l holds
-// D/4 elements of row l/4 of K and Q, 4 elements of row l/4 of the block's V
-// and dZ columns, eta of token l % 16, and (when the sub-tile opens a chunk in
-// the reverse pass) D/4 elements of row l/4 of the chunk-start state.
-template <int D>
+// N consecutive elements (N = 1, 2 or 4) widened to fp32
+template <int N, typename TIO>
+__device__ __forceinline__ void load_small(const TIO* p, float* out)
+{
+    if constexpr (N == 4) {
+        load_vec<4>(p, out);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) out[i] = io<TIO>::load(p, i);
+    }
+}
+
+// One sub-tile's inputs, loaded into registers one sub-tile ahead.  The 64*NW
+// threads share the K, Q (KP elements each) and V, dZ (VP elements each) tiles:
+// thread t takes row t / (4 NW); every lane holds eta of token l % 16, and each
+// wave the rows of its own column blocks of the chunk-start state (4 floats of
+// row l / 4 per block) when the sub-tile opens a chunk in the reverse pass.
+template <int D, int NW>
 struct SubTile {
-    static constexpr int PER = D / 4;
-    float k[PER], q[PER], w[PER], v[4], dz[4];
+    static constexpr int KP = D / (4 * NW), VP = 4 / NW, NBW = D / 16 / NW;
+    float k[KP], q[KP], v[VP], dz[VP], w[NBW][4];
     float eta;
 };
 
 template <typename TIO, int D>
-__global__ __launch_bounds__(64) void linear_bwd_kernel(BwdArgs a)
+__global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs a)
 {
-    constexpr int NB = D / 16, S = D + 4, PER = D / 4;
-    __shared__ BwdLds<D> L;
-    const int lane = threadIdx.x;
+    constexpr int NW = bwd_waves<D>(), NB = D / 16, NBW = NB / NW, S = D + 4;
+    constexpr int KP = SubTile<D, NW>::KP, VP = SubTile<D, NW>::VP;
+    __shared__ BwdLds<D, NW> L;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
-    const int frow = lane >> 2, fcol = (lane & 3) * PER, fblk = (lane & 3) * 4;
+    const int srow = tid / (4 * NW), kcol = (tid % (4 * NW)) * KP, vcol = (tid % (4 * NW)) * VP;
+    const int wrow = lane >> 2, wcol = (lane & 3) * 4;
     int slice, rb;
     xcd_unit_part(blockIdx.x, NB, slice, rb);
     if (slice >= a.BH) return;
@@ -178,6 +205,7 @@ __global__ __launch_bounds__(64) void linear_bwd_kernel(BwdArgs a)
     const float* etag = a.eta ? a.eta + (size_t)slice * T : nullptr;
     float* states = a.states + (size_t)slice * (nch + 1) * D * D;
     const size_t part = ((size_t)rb * a.BH + slice) * T;
+    auto blk = [&](int bb) { return wave + NW * bb; };   // column block of slot bb
 
     // sub-tile j: chunk j / nsub, tokens [t0, t0 + len)
     auto span = [&](int j, int& ch, int& si, int& t0, int& len) {
@@ -186,113 +214,123 @@ __global__ __launch_bounds__(64) void linear_bwd_kernel(BwdArgs a)
         t0 = ch * chunk + si * kSub;
         len = min(kSub, min(ch * chunk + chunk, T) - t0);
     };
-    // registers <- sub-tile j (with Q and dZ in the reverse pass, and the
-    // chunk-start state rows when `state` is set)
-    auto fetch = [&](SubTile<D>& f, int j, bool rev, bool state) {
+    auto fetch = [&](SubTile<D, NW>& f, int j, bool rev, bool state) {
         int ch, si, t0, len;
         span(j, ch, si, t0, len);
-        if (frow < len) {
-            const size_t row = (size_t)(t0 + frow) * D;
-            load_vec<PER>(Kg + row + fcol, f.k);
-            load_vec<4>(Vg + row + r0 + fblk, f.v);
+        if (srow < len) {
+            const size_t row = (size_t)(t0 + srow) * D;
+            load_vec<KP>(Kg + row + kcol, f.k);
+            load_small<VP>(Vg + row + r0 + vcol, f.v);
             if (rev) {
-                load_vec<PER>(Qg + row + fcol, f.q);
-                load_vec<4>(dZg + row + r0 + fblk, f.dz);
+                load_vec<KP>(Qg + row + kcol, f.q);
+                load_small<VP>(dZg + row + r0 + vcol, f.dz);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < PER; ++i) f.k[i] = f.q[i] = 0.f;
+            for (int i = 0; i < KP; ++i) f.k[i] = f.q[i] = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) f.v[i] = f.dz[i] = 0.f;
+            for (int i = 0; i < VP; ++i) f.v[i] = f.dz[i] = 0.f;
         }
         f.eta = c < len ? (etag ? etag[t0 + c] : a.eta_scalar) : 0.f;
-        if (state)
-            load_vec<PER>(states + (size_t)ch * D * D + (size_t)(r0 + frow) * D + fcol, f.w);
+        if (state) {
+            const float* src = states + (size_t)ch * D * D + (size_t)(r0 + wrow) * D + wcol;
+#pragma unroll
+            for (int bb = 0; bb < NBW; ++bb) load_vec<4>(src + 16 * blk(bb), f.w[bb]);
+        }
     };
-    // LDS <- registers
-    auto put = [&](const SubTile<D>& f, bool rev, bool state) {
-        float* kd = L.K + frow * S + fcol;
+    auto put = [&](const SubTile<D, NW>& f, bool rev, bool state) {
 #pragma unroll
-        for (int i = 0; i < PER; i += 4)
-            *reinterpret_cast<f32x4*>(kd + i) = f32x4{f.k[i], f.k[i + 1], f.k[i + 2], f.k[i + 3]};
-        *reinterpret_cast<f32x4*>(L.V + frow * 20 + fblk) = f32x4{f.v[0], f.v[1], f.v[2], f.v[3]};
+        for (int i = 0; i < KP; i += 4)
+            *reinterpret_cast<f32x4*>(L.K + srow * S + kcol + i) =
+                f32x4{f.k[i], f.k[i + 1], f.k[i + 2], f.k[i + 3]};
+#pragma unroll
+        for (int i = 0; i < VP; ++i) L.V[srow * 20 + vcol + i] = f.v[i];
         if (rev) {
-            float* qd = L.Q + frow * S + fcol;
 #pragma unroll
-            for (int i = 0; i < PER; i += 4)
-                *reinterpret_cast<f32x4*>(qd + i) = f32x4{f.q[i], f.q[i + 1], f.q[i + 2], f.q[i + 3]};
-            *reinterpret_cast<f32x4*>(L.dZ + frow * 20 + fblk) =
-                f32x4{f.dz[0], f.dz[1], f.dz[2], f.dz[3]};
+            for (int i = 0; i < KP; i += 4)
+                *reinterpret_cast<f32x4*>(L.Q + srow * S + kcol + i) =
+                    f32x4{f.q[i], f.q[i + 1], f.q[i + 2], f.q[i + 3]};
+#pragma unroll
+            for (int i = 0; i < VP; ++i) L.dZ[srow * 20 + vcol + i] = f.dz[i];
         }
         if (state) {
-            float* wd = L.W + frow * S + fcol;
 #pragma unroll
-            for (int i = 0; i < PER; i += 4)
-                *reinterpret_cast<f32x4*>(wd + i) = f32x4{f.w[i], f.w[i + 1], f.w[i + 2], f.w[i + 3]};
+            for (int bb = 0; bb < NBW; ++bb)
+                *reinterpret_cast<f32x4*>(L.W + wrow * S + 16 * blk(bb) + wcol) =
+                    f32x4{f.w[bb][0], f.w[bb][1], f.w[bb][2], f.w[bb][3]};
         }
     };
     auto store_state = [&](int slot, const f32x4* Wr) {
         float* dst = states + (size_t)slot * D * D + (size_t)r0 * D;
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int bb = 0; bb < NBW; ++bb)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) dst[(4 * g + v) * D + 16 * b + c] = Wr[b][v];
+            for (int v = 0; v < 4; ++v) dst[(4 * g + v) * D + 16 * blk(bb) + c] = Wr[bb][v];
+    };
+    // sum of the waves' partial tiles k (same order in every wave: identical sums)
+    auto reduce = [&](int k) {
+        f32x4 r = cl<20>(L.part[0][k], 0, lane);
+#pragma unroll
+        for (int w = 1; w < NW; ++w) r += cl<20>(L.part[w][k], 0, lane);
+        return r;
     };
 
-    SubTile<D> cur, nxt;
+    SubTile<D, NW> cur, nxt;
 
     // ------------------------------------------------ forward: chunk-start states
-    f32x4 Wr[NB];   // CL(W) per column block
+    f32x4 Wr[NBW];   // CL(W) of this wave's column blocks
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+    for (int bb = 0; bb < NBW; ++bb)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-            Wr[b][v] = a.W0[((size_t)slice * D + r0 + 4 * g + v) * D + 16 * b + c];
+            Wr[bb][v] = a.W0[((size_t)slice * D + r0 + 4 * g + v) * D + 16 * blk(bb) + c];
     fetch(cur, 0, false, false);
     for (int j = 0; j <= last; ++j) {
         int ch, si, t0, len;
         span(j, ch, si, t0, len);
-        lds_order();
+        __syncthreads();   // the previous sub-tile's tiles are consumed
         if (si == 0) {
             store_state(ch, Wr);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) put_cl<S>(L.W, 16 * b, lane, Wr[b]);
+            for (int bb = 0; bb < NBW; ++bb) put_cl<S>(L.W, 16 * blk(bb), lane, Wr[bb]);
         }
         put(cur, false, false);
         const float et = cur.eta;
+        __syncthreads();
         if (j < last) fetch(nxt, j + 1, false, false);
-        lds_order();
-        // E = W K^T - V (CL: rows 4g + v, token c), two accumulation chains
-        f32x4 E0 = {0.f, 0.f, 0.f, 0.f}, E1 = E0;
+        // E = W K^T - V: this wave's part of the contraction over the state columns
+        f32x4 Ew = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b = 0; b < NB; b += 2) {
-            E0 = mm16(rl<S>(L.W, 16 * b, lane), rl<S>(L.K, 16 * b, lane), E0);
-            if (b + 1 < NB)
-                E1 = mm16(rl<S>(L.W, 16 * (b + 1), lane), rl<S>(L.K, 16 * (b + 1), lane), E1);
-        }
+        for (int bb = 0; bb < NBW; ++bb)
+            Ew = mm16(rl<S>(L.W, 16 * blk(bb), lane), rl<S>(L.K, 16 * blk(bb), lane), Ew);
+        put_cl<20>(L.part[wave][0], 0, lane, Ew);
+        __syncthreads();
+        const f32x4 E = reduce(0);
         const f32x4 Vr = rl<20>(L.V, 0, lane);   // V[token c][row 4g + v], as E
         f32x4 Fm;   // -F
 #pragma unroll
-        for (int v = 0; v < 4; ++v) Fm[v] = -(E0[v] + E1[v] - Vr[v]) * et;
-        put_cl<20>(L.F, 0, lane, Fm);
+        for (int v = 0; v < 4; ++v) Fm[v] = -(E[v] - Vr[v]) * et;
+        put_cl<20>(L.F[wave], 0, lane, Fm);
         lds_order();
-        // W -= F K (contraction over the sub-tile's tokens)
-        const f32x4 Fa = rl<20>(L.F, 0, lane);
+        // W -= F K (contraction over the sub-tile's tokens), this wave's blocks
+        const f32x4 Fa = rl<20>(L.F[wave], 0, lane);
 #pragma unroll
-        for (int b = 0; b < NB; ++b) Wr[b] = mm16(Fa, cl<S>(L.K, 16 * b, lane), Wr[b]);
-        cur = nxt;
+        for (int bb = 0; bb < NBW; ++bb) Wr[bb] = mm16(Fa, cl<S>(L.K, 16 * blk(bb), lane), Wr[bb]);
+        if (j < last) cur = nxt;
     }
     if (multi) store_state(nch, Wr);
     __threadfence();   // the states are read back below
+    __syncthreads();
 
     // ------------------------------------------------ reverse
-    f32x4 P[NB], dWa[NB], Hr[NB];
+    f32x4 P[NBW], dWa[NBW], Hr[NBW];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        dWa[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int bb = 0; bb < NBW; ++bb) {
+        dWa[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-            P[b][v] = a.dWT ? a.dWT[((size_t)slice * D + r0 + 4 * g + v) * D + 16 * b + c] : 0.f;
+            P[bb][v] = a.dWT ? a.dWT[((size_t)slice * D + r0 + 4 * g + v) * D + 16 * blk(bb) + c]
+                             : 0.f;
     }
     // a sub-tile opens its chunk in the reverse pass when it is the chunk's last
     auto opens = [&](int j) {
@@ -305,29 +343,36 @@ __global__ __launch_bounds__(64) void linear_bwd_kernel(BwdArgs a)
         int ch, si, t0, len;
         span(j, ch, si, t0, len);
         const bool first = opens(j);
-        lds_order();
+        __syncthreads();   // the previous sub-tile's tiles are consumed
         put(cur, true, first);
         const float et = cur.eta;
         if (first && multi) {
             const float* src = states + (size_t)(ch + 1) * D * D + (size_t)r0 * D;
 #pragma unroll
-            for (int b = 0; b < NB; ++b)
+            for (int bb = 0; bb < NBW; ++bb)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) Hr[b][v] = src[(4 * g + v) * D + 16 * b + c];
+                for (int v = 0; v < 4; ++v) Hr[bb][v] = src[(4 * g + v) * D + 16 * blk(bb) + c];
         }
+#pragma unroll
+        for (int bb = 0; bb < NBW; ++bb) put_cl<S>(L.P, 16 * blk(bb), lane, P[bb]);
+        __syncthreads();
         if (j > 0) fetch(nxt, j - 1, true, opens(j - 1));
+        // partial E = W K^T, PK = P K^T, S = K Q^T over this wave's columns
+        f32x4 Ew = {0.f, 0.f, 0.f, 0.f}, PKw = Ew, Sw = Ew;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) put_cl<S>(L.P, 16 * b, lane, P[b]);
-        lds_order();
-        // E = W K^T - V, PK = P K^T, S = K Q^T (all CL)
-        f32x4 E = {0.f, 0.f, 0.f, 0.f}, PK = E, Sm = E;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        for (int bb = 0; bb < NBW; ++bb) {
+            const int b = blk(bb);
             const f32x4 kb = rl<S>(L.K, 16 * b, lane);
-            E = mm16(rl<S>(L.W, 16 * b, lane), kb, E);
-            PK = mm16(rl<S>(L.P, 16 * b, lane), kb, PK);
-            Sm = mm16(kb, rl<S>(L.Q, 16 * b, lane), Sm);
+            Ew = mm16(rl<S>(L.W, 16 * b, lane), kb, Ew);
+            PKw = mm16(rl<S>(L.P, 16 * b, lane), kb, PKw);
+            Sw = mm16(kb, rl<S>(L.Q, 16 * b, lane), Sw);
         }
+        put_cl<20>(L.part[wave][0], 0, lane, Ew);
+        put_cl<20>(L.part[wave][1], 0, lane, PKw);
+        put_cl<20>(L.part[wave][2], 0, lane, Sw);
+        __syncthreads();
+        f32x4 E = reduce(0);
+        const f32x4 PK = reduce(1), Sm = reduce(2);
         const f32x4 Vr = rl<20>(L.V, 0, lane);
         f32x4 F, Mk;
 #pragma unroll
@@ -336,12 +381,12 @@ __global__ __launch_bounds__(64) void linear_bwd_kernel(BwdArgs a)
             F[v] = E[v] * et;
             Mk[v] = (4 * g + v <= c) ? Sm[v] : 0.f;   // s = 4g + v, t = c
         }
-        put_cl<20>(L.M, 0, lane, Mk);
+        put_cl<20>(L.M[wave], 0, lane, Mk);
         lds_order();
         const f32x4 dZa = cl<20>(L.dZ, 0, lane);   // RL(dZ_blk): dZ[row c][token 4g + v]
         const f32x4 dZb = rl<20>(L.dZ, 0, lane);   // CL(dZ_blk): dZ[row 4g + v][token c]
         // dF = -dZ M^T - P K^T
-        f32x4 dF = mm16(dZa, rl<20>(L.M, 0, lane), f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 dF = mm16(dZa, rl<20>(L.M[wave], 0, lane), f32x4{0.f, 0.f, 0.f, 0.f});
         f32x4 dE;
         float de = 0.f;
 #pragma unroll
@@ -350,50 +395,50 @@ __global__ __launch_bounds__(64) void linear_bwd_kernel(BwdArgs a)
             dE[v] = dF[v] * et;
             de += E[v] * dF[v];
         }
-        // deta: sum over the block's 16 rows (4 slots x 4 lane groups)
+        // deta: sum over the block's 16 rows (4 slots x 4 lane groups); every wave
+        // holds the same values, wave 0 writes them and dV
         de += __shfl_xor(de, 16);
         de += __shfl_xor(de, 32);
-        if (g == 0 && c < len) a.deta_part[part + t0 + c] = de;
-        // dV = -dE: lane holds dims r0 + 4g .. +3 of token c
-        if (c < len) {
-            TIO* dv = static_cast<TIO*>(a.dV) + ((size_t)slice * T + t0 + c) * D + r0 + 4 * g;
+        if (wave == 0) {
+            if (g == 0 && c < len) a.deta_part[part + t0 + c] = de;
+            if (c < len) {
+                TIO* dv = static_cast<TIO*>(a.dV) + ((size_t)slice * T + t0 + c) * D + r0 + 4 * g;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) io<TIO>::store(dv, v, -dE[v]);
+                for (int v = 0; v < 4; ++v) io<TIO>::store(dv, v, -dE[v]);
+            }
         }
         // dA = -(F^T dZ) o U: A = RL(F^T) = CL(F) registers, B = CL(dZ_blk)
         f32x4 dA = mm16(F, dZb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int v = 0; v < 4; ++v) dA[v] = (4 * g + v <= c) ? -dA[v] : 0.f;
-        put_cl<20>(L.dA, 0, lane, dA);
-        put_cl<20>(L.dE, 0, lane, dE);
-        if (multi) {
-            put_cl<20>(L.F, 0, lane, F);
-            lds_order();
-            // H = W - G_{<sigma}: add this sub-tile's update back
-            const f32x4 Fa = rl<20>(L.F, 0, lane);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                Hr[b] = mm16(Fa, cl<S>(L.K, 16 * b, lane), Hr[b]);
-                put_cl<S>(L.H, 16 * b, lane, Hr[b]);
-            }
-        }
+        put_cl<20>(L.dA[wave], 0, lane, dA);
+        put_cl<20>(L.dE[wave], 0, lane, dE);
+        if (multi) put_cl<20>(L.F[wave], 0, lane, F);
         lds_order();
-        const f32x4 dAa = rl<20>(L.dA, 0, lane);   // RL(dA)
-        const f32x4 dEa = rl<20>(L.dE, 0, lane);   // RL(dE)
+        if (multi) {
+            // H = W - G_{<sigma}: add this sub-tile's update back
+            const f32x4 Fa = rl<20>(L.F[wave], 0, lane);
+#pragma unroll
+            for (int bb = 0; bb < NBW; ++bb)
+                Hr[bb] = mm16(Fa, cl<S>(L.K, 16 * blk(bb), lane), Hr[bb]);
+        }
+        const f32x4 dAa = rl<20>(L.dA[wave], 0, lane);   // RL(dA)
+        const f32x4 dEa = rl<20>(L.dE[wave], 0, lane);   // RL(dE)
         f32x4 Fn;
 #pragma unroll
         for (int v = 0; v < 4; ++v) Fn[v] = -F[v];
-        const float* Hs = multi ? L.H : L.W;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        for (int bb = 0; bb < NBW; ++bb) {
+            const int b = blk(bb);
             const f32x4 kc = cl<S>(L.K, 16 * b, lane);
             const f32x4 qc = cl<S>(L.Q, 16 * b, lane);
-            // dK (tokens x dims) = -F^T P + dE^T W + dA Q
-            f32x4 dK = mm16(Fn, cl<S>(L.P, 16 * b, lane), f32x4{0.f, 0.f, 0.f, 0.f});
-            dK = mm16(dE, cl<S>(L.W, 16 * b, lane), dK);
+            const f32x4 wc = cl<S>(L.W, 16 * b, lane);
+            // dK (tokens x dims) = -F^T P + dE^T W + dA Q   (P: this sub-tile's, CL)
+            f32x4 dK = mm16(Fn, P[bb], f32x4{0.f, 0.f, 0.f, 0.f});
+            dK = mm16(dE, wc, dK);
             dK = mm16(dAa, qc, dK);
             // dQ (tokens x dims) = dZ^T H + dA^T K
-            f32x4 dQ = mm16(dZb, cl<S>(Hs, 16 * b, lane), f32x4{0.f, 0.f, 0.f, 0.f});
+            f32x4 dQ = mm16(dZb, multi ? Hr[bb] : wc, f32x4{0.f, 0.f, 0.f, 0.f});
             dQ = mm16(dA, kc, dQ);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -404,23 +449,23 @@ __global__ __launch_bounds__(64) void linear_bwd_kernel(BwdArgs a)
                 }
             }
             // P += dZ Q, dW += dE K
-            P[b] = mm16(dZa, qc, P[b]);
-            dWa[b] = mm16(dEa, kc, dWa[b]);
+            P[bb] = mm16(dZa, qc, P[bb]);
+            dWa[bb] = mm16(dEa, kc, dWa[bb]);
         }
         if (si == 0) {   // the chunk is done: its dW is the previous chunk's dW_next
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                P[b] += dWa[b];
-                dWa[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int bb = 0; bb < NBW; ++bb) {
+                P[bb] += dWa[bb];
+                dWa[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
         if (j > 0) cur = nxt;
     }
     float* dW0 = a.dW0 + ((size_t)slice * D + r0) * D;
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
+    for (int bb = 0; bb < NBW; ++bb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) dW0[(4 * g + v) * D + 16 * b + c] = P[b][v];
+        for (int v = 0; v < 4; ++v) dW0[(4 * g + v) * D + 16 * blk(bb) + c] = P[bb][v];
 }
 
 // dK, dQ = sum of the row blocks' partials (rounded to the I/O type), deta likewise
@@ -466,7 +511,7 @@ hipError_t launch_typed(const LinearBwdArgs& a, hipStream_t s)
     k.deta_part = reinterpret_cast<float*>(ws);
     k.BH = a.BH; k.T = a.T; k.chunk = a.chunk;
     const unsigned grid = (unsigned)(((a.BH + 7) / 8) * 8 * NB);
-    hipLaunchKernelGGL((linear_bwd_kernel<TIO, D>), dim3(grid), dim3(64), 0, s, k);
+    hipLaunchKernelGGL((linear_bwd_kernel<TIO, D>), dim3(grid), dim3(64 * bwd_waves<D>()), 0, s, k);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned rgrid = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
