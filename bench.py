@@ -239,6 +239,88 @@ def bwd_main(args, wl, x, seed):
     print(json.dumps(rec), flush=True)
 
 
+def varlen_main(args, wl, x, seed):
+    """Packed documents with a reset at each: the workload's B x T tokens per head,
+    packed head-major and cut into documents of seeded lengths drawn uniformly
+    from [T/4, 7T/4] (the last one takes the rest), each with its own W0."""
+    import torch
+    from test_sequence_layers_ttt_amd import ttt
+    dev = torch.device("cuda:0")
+    B, H, T, d = wl.B, wl.H, wl.T, wl.d
+    total_T = B * T
+    rng = np.random.default_rng([seed, 99])
+    lengths = []
+    while sum(lengths) < total_T:
+        lengths.append(int(min(rng.integers(T // 4, 7 * T // 4 + 1), total_T - sum(lengths))))
+    n_docs = len(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    io = torch.bfloat16 if wl.io == "bf16" else torch.float32
+
+    def packed(a):   # [B*H, T, d] -> [H, B*T, d]
+        return np.ascontiguousarray(a.reshape(B, H, T, -1).transpose(1, 0, 2, 3).reshape(H, B * T, -1))
+
+    t = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    K, Q, V = (t(packed(x[k]), io) for k in ("K", "Q", "V"))
+    eta = None if x["eta"] is None else t(packed(x["eta"][..., None])[..., 0])
+    W0 = t(rng.standard_normal((n_docs, H, d, d), dtype=np.float32) * np.float32(wl.state_std))
+    cu_d = t(cu, torch.int32)
+    Z = torch.empty_like(K)
+    W_out = torch.empty_like(W0)
+    io_code = ttt.DTYPE_BF16 if wl.io == "bf16" else ttt.DTYPE_F32
+    plan = ttt.linear_select_plan_varlen(n_docs, H, total_T, d, wl.chunk, io_code)
+    log("varlen: %d documents (lengths %d..%d) x %d heads, plan %s" % (
+        n_docs, min(lengths), max(lengths), H, ttt.plan_name(plan)))
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ttt.linear_fwd_varlen(K, Q, V, eta, W0, cu_d, wl.chunk, eta_scalar=x["eta_scalar"],
+                              Z=Z, W_out=W_out, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_event = ev0.elapsed_time(ev1) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    log("timed %d varlen calls: %.4f ms/call (events), %.4f ms/call (wall)" % (
+        args.steps, ms_event, ms_step))
+    esz = 2 if wl.io == "bf16" else 4
+    abytes = float(H) * total_T * (4 * d * esz + (4 if eta is not None else 0)) + \
+        float(n_docs) * H * 2 * d * d * 4
+    gbs = abytes / (ms_event * 1e-3) / 1e9
+    rec = {
+        "metric": METRIC,
+        "value": round(total_T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.io == "bf16" and plan == ttt.PLAN_MFMA else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name + "_varlen", "scan": "ttt_linear_fwd_varlen",
+                   "documents": n_docs, "heads": H, "total_tokens": total_T, "head_dim": d,
+                   "chunk": wl.chunk, "plan": ttt.plan_name(plan), "parallelism": "single_gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_ms": round(ms_event, 5), "algorithmic_bytes": abytes},
+        "cpu_baseline": None,
+        "parity": None,
+        "head_tokens_per_s": round(H * total_T / (ms_step * 1e-3), 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def decode_main(args, wl, x):
     """Decode: each call continues every sequence by n tokens.  The calls are
     captured once in a HIP graph (one per state copy) and the graph is replayed,
@@ -362,6 +444,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0)
     ap.add_argument("--decode", type=int, default=0,
                     help="time ttt_linear_step continuing every sequence by N tokens")
+    ap.add_argument("--varlen", action="store_true",
+                    help="TTT-Linear over the workload's tokens packed as documents with resets")
     ap.add_argument("--read-start", action="store_true",
                     help="TTT-Linear with the chunk-start read order")
     ap.add_argument("--bwd", action="store_true",
@@ -384,6 +468,11 @@ def main():
 
     wl = inputs.WORKLOADS[args.workload]
     seed = inputs.WORKLOAD_SEEDS[wl.name]
+    if args.varlen:
+        if wl.model != "linear":
+            raise SystemExit("--varlen needs a TTT-Linear workload")
+        varlen_main(args, wl, inputs.make_inputs(wl, seed), seed)
+        return
     if args.bwd:
         if wl.model != "linear":
             raise SystemExit("--bwd needs a TTT-Linear workload")

@@ -130,6 +130,34 @@ int ttt_linear_fwd(const void* K, const void* Q, const void* V,
                    void* workspace, size_t workspace_bytes,
                    void* stream, int plan);
 
+/* Packed documents with a reset at every document (variable-length batches).
+ * Each document of every head is its own TTT-Linear scan from its own initial
+ * state: no state, gradient or output crosses a document boundary, and chunks
+ * are counted from the document's first token (PaperTrace "5 · TestingTime
+ * 训练与长上下文", the discussion of cross-sequence reset after §3.1: each
+ * independent document needs its own W0 and state).
+ *   K, Q, V, Z  : [H, total_T, d] in io_dtype, head-major: document n of head h is
+ *                 rows cu_seqlens[n] .. cu_seqlens[n+1]-1 of head h's block.
+ *   eta         : [H, total_T] fp32 or NULL (eta_scalar).
+ *   W0, W_out   : [n_docs, H, d, d] fp32 (W_out may alias W0).
+ *   cu_seqlens  : DEVICE int32 [n_docs + 1], non-decreasing offsets into
+ *                 [0, total_T] (read on the GPU; values outside are clamped, so a
+ *                 malformed table gives wrong documents, never an out-of-range
+ *                 access).  An empty document passes W0 through.  Rows that no
+ *                 document covers are not written in Z.
+ *   d : 16, 32, 64 or 128;  chunk >= 1;  plans: GENERIC, and MFMA for bf16 with
+ *   chunk <= 16 (AUTO picks it); no workspace. */
+int ttt_linear_fwd_varlen(const void* K, const void* Q, const void* V,
+                          const float* eta, float eta_scalar, const float* W0,
+                          void* Z, float* W_out, const int* cu_seqlens,
+                          int n_docs, int H, int total_T, int d, int chunk, int io_dtype,
+                          void* stream, int plan);
+
+/* Plan that ttt_linear_fwd_varlen would run (never TTT_PLAN_AUTO), or a negative
+ * ttt_status. */
+int ttt_linear_select_plan_varlen(int n_docs, int H, int total_T, int d, int chunk,
+                                  int io_dtype, int plan);
+
 /* Bytes of workspace ttt_linear_bwd needs: the chunk-start states
  * (B*H*(ceil(T/chunk)+1)*d*d fp32) and per-16-row-block partial sums of dK, dQ
  * and deta.  0 for an unsupported shape. */

@@ -148,6 +148,7 @@ int ttt_linear_fwd_ex(const void* K, const void* Q, const void* V,
     a.bf16 = io_dtype == TTT_DTYPE_BF16;
     a.read_start = read_mode == TTT_READ_CHUNK_START;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.cu = nullptr; a.H = H; a.total_T = T;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (p) {
     case TTT_PLAN_MFMA: return launch_status(launch_linear_mfma(a, s));
@@ -216,8 +217,54 @@ int ttt_linear_step(const void* K, const void* Q, const void* V,
     a.Z = Z; a.W_out = W_chunk; a.BH = B * H; a.T = n; a.d = d; a.chunk = chunk;
     a.bf16 = io_dtype == TTT_DTYPE_BF16;
     a.read_start = 0;
+    a.cu = nullptr; a.H = H; a.total_T = n;
     a.workspace = nullptr; a.workspace_bytes = 0;
     return launch_status(launch_linear_step(a, G, pos, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int ttt_linear_select_plan_varlen(int n_docs, int H, int total_T, int d, int chunk,
+                                  int io_dtype, int plan)
+{
+    if (n_docs <= 0 || H <= 0 || total_T < 0 || d <= 0 || chunk <= 0) return TTT_ERR_INVALID_ARG;
+    if ((long double)H * ((long double)total_T + 1) * d >= 4.0e18L ||
+        (long double)n_docs * H * 64 >= 2.0e9L)
+        return TTT_ERR_INVALID_ARG;
+    if (io_dtype != TTT_DTYPE_F32 && io_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARG;
+    if (plan < TTT_PLAN_AUTO || plan > TTT_PLAN_BIGCHUNK) return TTT_ERR_INVALID_ARG;
+    if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
+    const bool mfma = chunk <= 16 && linear_mfma_supported(d, chunk, io_dtype == TTT_DTYPE_BF16);
+    switch (plan) {
+    case TTT_PLAN_GENERIC: return TTT_PLAN_GENERIC;
+    case TTT_PLAN_MFMA: return mfma ? TTT_PLAN_MFMA : TTT_ERR_UNSUPPORTED;
+    case TTT_PLAN_BIGCHUNK: return TTT_ERR_UNSUPPORTED;
+    default: return mfma ? TTT_PLAN_MFMA : TTT_PLAN_GENERIC;
+    }
+}
+
+int ttt_linear_fwd_varlen(const void* K, const void* Q, const void* V,
+                          const float* eta, float eta_scalar, const float* W0,
+                          void* Z, float* W_out, const int* cu_seqlens,
+                          int n_docs, int H, int total_T, int d, int chunk, int io_dtype,
+                          void* stream, int plan)
+{
+    if (!K || !Q || !V || !W0 || !Z || !W_out || !cu_seqlens) return TTT_ERR_INVALID_ARG;
+    if (!aligned(K, 16) || !aligned(Q, 16) || !aligned(V, 16) || !aligned(Z, 16) ||
+        !aligned(W0, 16) || !aligned(W_out, 16) || !aligned(cu_seqlens, 4))
+        return TTT_ERR_INVALID_ARG;
+    if (eta ? !aligned(eta, 4) : !std::isfinite(eta_scalar)) return TTT_ERR_INVALID_ARG;
+    const int p = ttt_linear_select_plan_varlen(n_docs, H, total_T, d, chunk, io_dtype, plan);
+    if (p < 0) return p;
+
+    LinearArgs a;
+    a.K = K; a.Q = Q; a.V = V; a.eta = eta; a.eta_scalar = eta_scalar; a.W0 = W0;
+    a.Z = Z; a.W_out = W_out; a.BH = n_docs * H; a.T = 0; a.d = d; a.chunk = chunk;
+    a.bf16 = io_dtype == TTT_DTYPE_BF16;
+    a.read_start = 0;
+    a.workspace = nullptr; a.workspace_bytes = 0;
+    a.cu = cu_seqlens; a.H = H; a.total_T = total_T;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (p == TTT_PLAN_MFMA) return launch_status(launch_linear_mfma(a, s));
+    return launch_status(launch_linear_generic(a, s));
 }
 
 int ttt_mlp_select_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan)

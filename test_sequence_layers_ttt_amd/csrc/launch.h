@@ -20,7 +20,28 @@ struct LinearArgs {
     int read_start;        // 1: every token reads with its chunk-start state
     void* workspace;
     size_t workspace_bytes;
+    // packed documents: when cu is set, slice s = (document s / H, head s % H) reads
+    // tokens [cu[doc], cu[doc + 1]) of head h's rows of [H, total_T, d] (clamped to
+    // [0, total_T]); T is then unused
+    const int* cu;
+    int H, total_T;
 };
+
+// Token range of one slice: its first row in the packed arrays and its length.
+__device__ __forceinline__ void slice_span(const int* cu, int H, int total_T, int T, int slice,
+                                           size_t& tok0, int& len)
+{
+    if (!cu) {
+        tok0 = (size_t)slice * T;
+        len = T;
+        return;
+    }
+    const int doc = slice / H, h = slice - doc * H;
+    const int st = min(max(cu[doc], 0), total_T);
+    const int en = min(max(cu[doc + 1], st), total_T);
+    tok0 = (size_t)h * total_T + st;
+    len = en - st;
+}
 
 struct MlpArgs {
     const void* K;
@@ -46,7 +67,8 @@ struct MlpArgs {
 // fp32 vector-ALU dual form, any chunk, d <= 128, either read order.
 hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
 
-// bf16 MFMA path for chunk <= 16 or a multiple of 16; d in {32, 64, 128}.
+// bf16 MFMA path for chunk <= 16 or a multiple of 16; d in {32, 64, 128}.  Packed
+// documents: chunk <= 16 only.
 bool linear_mfma_supported(int d, int chunk, int bf16);
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
 

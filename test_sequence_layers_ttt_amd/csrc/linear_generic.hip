@@ -35,7 +35,8 @@ template <typename TIO>
 __global__ __launch_bounds__(256) void linear_generic_kernel(
     const TIO* __restrict__ K, const TIO* __restrict__ Q, const TIO* __restrict__ V,
     const float* __restrict__ eta, float eta_scalar, const float* W0,
-    TIO* __restrict__ Z, float* W_out, int T, int d, int chunk, int read_start)
+    TIO* __restrict__ Z, float* W_out, int T_all, int d, int chunk, int read_start,
+    const int* __restrict__ cu, int H, int total_T)
 {
     __shared__ float sWs[kRows][kPad];   // chunk-start state rows
     __shared__ float sM[kRows][kPad];    // running state rows
@@ -52,7 +53,9 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(
     const int r0 = (blockIdx.x % nrb) * kRows;
     const int R = min(kRows, d - r0);
 
-    const size_t tok0 = (size_t)slice * T;                 // first token row of the slice
+    size_t tok0;                                           // first token row of the slice
+    int T;
+    slice_span(cu, H, total_T, T_all, slice, tok0, T);
     const float* W0s = W0 + (size_t)slice * d * d;
     float* Wos = W_out + (size_t)slice * d * d;
 
@@ -184,12 +187,12 @@ hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s)
         hipLaunchKernelGGL(linear_generic_kernel<uint16_t>, grid, block, 0, s,
                            (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V,
                            a.eta, a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.T, a.d,
-                           a.chunk, a.read_start);
+                           a.chunk, a.read_start, a.cu, a.H, a.total_T);
     } else {
         hipLaunchKernelGGL(linear_generic_kernel<float>, grid, block, 0, s,
                            (const float*)a.K, (const float*)a.Q, (const float*)a.V,
                            a.eta, a.eta_scalar, a.W0, (float*)a.Z, a.W_out, a.T, a.d,
-                           a.chunk, a.read_start);
+                           a.chunk, a.read_start, a.cu, a.H, a.total_T);
     }
     return hipGetLastError();
 }

@@ -254,7 +254,8 @@ template <int D, int PF, int WPB, int RB, int ETA, bool FULL>
 __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
-    const float* W0, uint16_t* __restrict__ Z, float* W_out, int BH, int T, int chunk)
+    const float* W0, uint16_t* __restrict__ Z, float* W_out, int BH, int T_all, int chunk,
+    const int* __restrict__ cu, int H, int total_T)
 {
     constexpr int NB = D / 16;
     constexpr int NM = D / 32;
@@ -272,7 +273,22 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
     xcd_unit_part(blockIdx.x, NB / (WPB * RB), slice, bpart);
     if (slice >= BH) return;
     const int out0 = (bpart * WPB + wave) * RB * 16;
-    const size_t tok0 = (size_t)slice * T;
+    size_t tok0;
+    int T;
+    slice_span(cu, H, total_T, T_all, slice, tok0, T);
+    if (T == 0) {   // an empty document: the state passes through
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const float* w = W0 + (size_t)slice * D * D + (size_t)(out0 + 16 * r + c) * D;
+            float* wo = W_out + (size_t)slice * D * D + (size_t)(out0 + 16 * r + c) * D;
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+                *(f32x4*)(wo + 32 * m + 8 * g) = *(const f32x4*)(w + 32 * m + 8 * g);
+                *(f32x4*)(wo + 32 * m + 8 * g + 4) = *(const f32x4*)(w + 32 * m + 8 * g + 4);
+            }
+        }
+        return;
+    }
     const int step = chunk;                    // <= 16
     const int ntiles = (T + step - 1) / step;
 
@@ -438,7 +454,8 @@ void launch_chain(const LinearArgs& a, hipStream_t s)
     dim3 grid((unsigned)(units * (D / 16) / RB)), block(64);
     hipLaunchKernelGGL((linear_mfma_chain_kernel<D, PF, 1, RB, ETA, FULL>), grid, block, 0, s,
                        (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V, a.eta,
-                       a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.BH, a.T, a.chunk);
+                       a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.BH, a.T, a.chunk, a.cu,
+                       a.H, a.total_T);
 }
 
 template <int D, int ETA, bool FULL>
@@ -466,6 +483,11 @@ void launch_wpb(const LinearArgs& a, hipStream_t s)
 template <int D>
 hipError_t launch_d(const LinearArgs& a, hipStream_t s)
 {
+    if (a.cu) {   // packed documents: lengths known on the device only, chunk <= 16
+        if (!a.eta) launch_wpb<D, kEtaScalar, false>(a, s);
+        else launch_wpb<D, kEtaToken, false>(a, s);
+        return hipGetLastError();
+    }
     // every sub-tile holds 16 tokens: no padding logic at all
     const bool full = a.chunk % kStep == 0 && a.T % kStep == 0;
     const bool eta4 = a.eta && full && (reinterpret_cast<uintptr_t>(a.eta) % 16 == 0) &&
@@ -494,7 +516,8 @@ hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s)
     // and 128 go to one workgroup per head that fetches K and Q once for all of
     // its waves (8x12 heads at d = 64: 49 us vs 52 us; at 32 heads, where every
     // unit has a compute unit to itself, the single-wave kernel is faster).
-    if ((long)a.BH * (a.d / 16) > kComputeUnits && linear_coop_supported(a.d, a.chunk, a.bf16))
+    if (!a.cu && (long)a.BH * (a.d / 16) > kComputeUnits &&
+        linear_coop_supported(a.d, a.chunk, a.bf16))
         return launch_linear_coop(a, s);
     switch (a.d) {
     case 32: return launch_d<32>(a, s);

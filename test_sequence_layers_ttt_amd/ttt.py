@@ -22,6 +22,7 @@ READ_INCLUSIVE, READ_CHUNK_START = 0, 1
 EXPORTS = ("ttt_linear_workspace_bytes", "ttt_linear_select_plan", "ttt_linear_fwd",
            "ttt_linear_step", "ttt_linear_bwd_workspace_bytes", "ttt_linear_bwd",
            "ttt_linear_fwd_ex", "ttt_linear_select_plan_ex",
+           "ttt_linear_fwd_varlen", "ttt_linear_select_plan_varlen",
            "ttt_mlp_workspace_bytes", "ttt_mlp_select_plan", "ttt_mlp_fwd",
            "ttt_status_string", "ttt_plan_name")
 
@@ -53,6 +54,11 @@ def lib() -> ctypes.CDLL:
         L.ttt_linear_fwd_ex.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, i, i, i, i, i, i, vp, sz,
                                         vp, i, i]
         L.ttt_linear_fwd_ex.restype = i
+        L.ttt_linear_fwd_varlen.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, vp, i, i, i, i, i, i,
+                                            vp, i]
+        L.ttt_linear_fwd_varlen.restype = i
+        L.ttt_linear_select_plan_varlen.argtypes = [i] * 7
+        L.ttt_linear_select_plan_varlen.restype = i
         L.ttt_linear_select_plan_ex.argtypes = [i] * 8
         L.ttt_linear_select_plan_ex.restype = i
         L.ttt_linear_bwd_workspace_bytes.argtypes = [i] * 6
@@ -254,6 +260,41 @@ def linear_step(K, Q, V, eta, W_chunk, G, pos: int, chunk: int, eta_scalar: floa
     if rc != OK:
         raise TTTError(rc, "ttt_linear_step")
     return Z, (int(pos) + n) % int(chunk)
+
+
+def linear_select_plan_varlen(n_docs, H, total_T, d, chunk, io_dtype, plan=PLAN_AUTO) -> int:
+    return int(lib().ttt_linear_select_plan_varlen(n_docs, H, total_T, d, chunk, io_dtype, plan))
+
+
+def linear_fwd_varlen(K, Q, V, eta, W0, cu_seqlens, chunk: int, eta_scalar: float = 0.0, *,
+                      Z=None, W_out=None, plan: int = PLAN_AUTO, stream=None) -> Tuple:
+    """TTT-Linear over packed documents, each reset to its own initial state.
+    K, Q, V: [H, total_T, d]; eta: [H, total_T] or None; W0: [n_docs, H, d, d];
+    cu_seqlens: int32 device tensor [n_docs + 1].  Returns (Z, W_out)."""
+    import torch
+    H, total_T, d = K.shape
+    n_docs = cu_seqlens.numel() - 1
+    _check(K, "K", (H, total_T, d))
+    _check(Q, "Q", (H, total_T, d), K.dtype)
+    _check(V, "V", (H, total_T, d), K.dtype)
+    _check(W0, "W0", (n_docs, H, d, d), torch.float32)
+    _check(cu_seqlens, "cu_seqlens", (n_docs + 1,), torch.int32)
+    if eta is not None:
+        _check(eta, "eta", (H, total_T), torch.float32)
+    if Z is None:
+        Z = torch.zeros_like(K)
+    if W_out is None:
+        W_out = torch.empty_like(W0)
+    _check(Z, "Z", (H, total_T, d), K.dtype)
+    _check(W_out, "W_out", (n_docs, H, d, d), torch.float32)
+    rc = lib().ttt_linear_fwd_varlen(K.data_ptr(), Q.data_ptr(), V.data_ptr(), _ptr(eta),
+                                     float(eta_scalar), W0.data_ptr(), Z.data_ptr(),
+                                     W_out.data_ptr(), cu_seqlens.data_ptr(), n_docs, H, total_T,
+                                     d, int(chunk), _io_dtype(K), _stream(K.device, stream),
+                                     int(plan))
+    if rc != OK:
+        raise TTTError(rc, "ttt_linear_fwd_varlen")
+    return Z, W_out
 
 
 def mlp_fwd(K, Q, V, eta, W1, b1, W2, b2, chunk: int, eta_scalar: float = 0.0, *, Z=None,

@@ -228,6 +228,41 @@ def test_read_order_plan_selection():
     assert ttt.linear_select_plan(1, 1, 64, 64, 16, 1, 0, 7) == ttt.ERR_INVALID_ARG
 
 
+def _varlen(**kw):
+    a = dict(K=FAKE, Q=FAKE, V=FAKE, eta=None, eta_scalar=0.1, W0=FAKE, Z=FAKE, W=FAKE,
+             cu=FAKE, n_docs=3, H=2, total_T=40, d=64, chunk=16, io=1, stream=None, plan=0)
+    a.update(kw)
+    return ttt.lib().ttt_linear_fwd_varlen(a["K"], a["Q"], a["V"], a["eta"], a["eta_scalar"],
+                                           a["W0"], a["Z"], a["W"], a["cu"], a["n_docs"], a["H"],
+                                           a["total_T"], a["d"], a["chunk"], a["io"], a["stream"],
+                                           a["plan"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=None), ttt.ERR_INVALID_ARG),
+    (dict(cu=FAKE + 2), ttt.ERR_INVALID_ARG),
+    (dict(K=None), ttt.ERR_INVALID_ARG),
+    (dict(W0=FAKE + 4), ttt.ERR_INVALID_ARG),
+    (dict(n_docs=0), ttt.ERR_INVALID_ARG),
+    (dict(total_T=-1), ttt.ERR_INVALID_ARG),
+    (dict(H=0), ttt.ERR_INVALID_ARG),
+    (dict(chunk=0), ttt.ERR_INVALID_ARG),
+    (dict(eta_scalar=math.nan), ttt.ERR_INVALID_ARG),
+    (dict(d=48), ttt.ERR_UNSUPPORTED),
+    (dict(plan=ttt.PLAN_BIGCHUNK), ttt.ERR_UNSUPPORTED),
+    (dict(chunk=32, plan=ttt.PLAN_MFMA), ttt.ERR_UNSUPPORTED),
+])
+def test_varlen_rejects_bad_arguments(kw, status):
+    assert _varlen(**kw) == status
+
+
+def test_varlen_plan_selection():
+    assert ttt.linear_select_plan_varlen(3, 2, 40, 64, 16, 1) == ttt.PLAN_MFMA
+    assert ttt.linear_select_plan_varlen(3, 2, 40, 64, 32, 1) == ttt.PLAN_GENERIC
+    assert ttt.linear_select_plan_varlen(3, 2, 40, 64, 16, 0) == ttt.PLAN_GENERIC
+    assert ttt.linear_select_plan_varlen(3, 2, 0, 16, 16, 0) == ttt.PLAN_GENERIC
+
+
 def test_plan_selection_and_workspace_are_host_only():
     assert ttt.linear_select_plan(1, 1, 256, 16, 16, ttt.DTYPE_F32) == ttt.PLAN_GENERIC
     assert ttt.linear_select_plan(1, 1, 256, 16, 16, 0, ttt.PLAN_GENERIC) == ttt.PLAN_GENERIC
