@@ -31,6 +31,8 @@
 // No LDS, no barriers, no atomics.
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 #include "mfma_common.h"
@@ -331,11 +333,14 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
     // state) is done unconditionally: after the last chunk the next tile is a
     // valid re-read of this slice and its results are simply unused, so the
     // steady-state body has no branches for the scheduler to stop at.
-    auto chunk_step = [&](const Tile<D, RB>& cur, const Tile<D, RB>& nxt, int tau) {
+    // `whole` (a compile-time tag) marks a tile known to hold 16 tokens: no masks
+    // and no predicated store, so the step stays one basic block for the scheduler
+    auto chunk_step = [&](const Tile<D, RB>& cur, const Tile<D, RB>& nxt, int tau, auto whole) {
+        constexpr bool TF = FULL || decltype(whole)::value;
         const int s0 = tau * step;
         f32x4 et = ETA == kEtaScalar ? f32x4{eta_scalar, eta_scalar, eta_scalar, eta_scalar}
                                      : cur.eta;
-        if (!FULL) {
+        if (!TF) {
             et.x = (4 * g + 0 < cur.n) ? et.x : 0.f;
             et.y = (4 * g + 1 < cur.n) ? et.y : 0.f;
             et.z = (4 * g + 2 < cur.n) ? et.z : 0.f;
@@ -382,7 +387,7 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
 #pragma unroll
             for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[r][m], cur.q[m], Zt);
             Zt = mfma16(F[r], Sb, Zt);
-            if (FULL || c < cur.n) {
+            if (TF || c < cur.n) {
                 const u32x2 zb = pack_bf16x4(Zt);
                 *(u32x2*)(Z + (tok0 + s0 + c) * D + out0 + 16 * r + 4 * g) = zb;
             }
@@ -398,19 +403,44 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
         const int n = s1 < T ? min(step, T - s1) : 0;
         load_tile<D, ETA, FULL, RB>(slot, K, Q, V, eta, tok0, n > 0 ? s1 : 0, n, out0, lane);
     };
+    // a tile known to hold 16 tokens: unclamped loads
+    auto refill_whole = [&](Tile<D, RB>& slot, int tau) {
+        load_tile<D, ETA, true, RB>(slot, K, Q, V, eta, tok0, tau * step, 16, out0, lane);
+    };
 
+    const std::integral_constant<bool, true> whole;
+    const std::integral_constant<bool, false> ragged;
     int tau0 = 0;
+    if constexpr (!FULL) {
+        // ragged sequences of 16-token chunks: every tile before the last partial
+        // one is whole (loads stay clamped, as they may reach the partial tile)
+        const int nwhole = step == 16 ? T / 16 : 0;
+        for (; tau0 + 2 * PF <= nwhole; tau0 += PF) {   // the refills are whole too
+#pragma unroll
+            for (int p = 0; p < PF; ++p) {
+                chunk_step(buf[p], buf[(p + 1) % PF], tau0 + p, whole);
+                refill_whole(buf[p], tau0 + p + PF);
+            }
+        }
+        for (; tau0 + PF <= nwhole; tau0 += PF) {
+#pragma unroll
+            for (int p = 0; p < PF; ++p) {
+                chunk_step(buf[p], buf[(p + 1) % PF], tau0 + p, whole);
+                refill(buf[p], tau0 + p + PF);
+            }
+        }
+    }
     for (; tau0 + PF <= ntiles; tau0 += PF) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
-            chunk_step(buf[p], buf[(p + 1) % PF], tau0 + p);
+            chunk_step(buf[p], buf[(p + 1) % PF], tau0 + p, ragged);
             refill(buf[p], tau0 + p + PF);
         }
     }
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
         if (tau0 + p >= ntiles) break;
-        chunk_step(buf[p], buf[(p + 1) % PF], tau0 + p);
+        chunk_step(buf[p], buf[(p + 1) % PF], tau0 + p, ragged);
     }
 
 #pragma unroll
