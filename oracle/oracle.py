@@ -53,6 +53,11 @@ def _load():
                                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.ttt_oracle_linear_read.restype = ctypes.c_int
+        lib.ttt_oracle_linear_ln.argtypes = [P, P, P, P, ctypes.c_double, P, P, P, P,
+                                             ctypes.c_double, P, P, P,
+                                             ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int]
+        lib.ttt_oracle_linear_ln.restype = ctypes.c_int
         lib.ttt_oracle_linear_bwd.argtypes = [P, P, P, P, ctypes.c_double, P, P, P,
                                               P, P, P, P, P,
                                               ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -103,6 +108,27 @@ def linear(K, Q, V, eta, eta_scalar: float, W0, chunk: int,
     if rc <= 0:
         raise ValueError("ttt_oracle_linear rejected its arguments")
     return (Z, W, rc) if return_threads else (Z, W)
+
+
+def linear_ln(K, Q, V, eta, eta_scalar: float, W0, b0, ln_weight, ln_bias, eps: float,
+              chunk: int, nthreads: int = 0, return_threads: bool = False):
+    """TTT-Linear with the bias as state and f(x) = x + LN(W x + b) (LayerNorm and
+    residual inside f), or f(x) = W x + b when ln_weight and ln_bias are None.
+    b0, ln_weight, ln_bias: [n, d].  Returns (Z, W_T, b_T) in fp64."""
+    K, Q, V, W0, b0 = _f64(K), _f64(Q), _f64(V), _f64(W0), _f64(b0)
+    eta, lnw, lnb = _f64(eta), _f64(ln_weight), _f64(ln_bias)
+    n, T, d = K.shape
+    assert W0.shape == (n, d, d) and b0.shape == (n, d)
+    Z = np.empty((n, T, d), np.float64)
+    W = np.empty((n, d, d), np.float64)
+    b = np.empty((n, d), np.float64)
+    rc = _load().ttt_oracle_linear_ln(_ptr(K), _ptr(Q), _ptr(V), _ptr(eta), float(eta_scalar),
+                                      _ptr(W0), _ptr(b0), _ptr(lnw), _ptr(lnb), float(eps),
+                                      _ptr(Z), _ptr(W), _ptr(b), n, T, d, int(chunk),
+                                      int(nthreads))
+    if rc <= 0:
+        raise ValueError("ttt_oracle_linear_ln rejected its arguments")
+    return (Z, W, b, rc) if return_threads else (Z, W, b)
 
 
 def linear_bwd(K, Q, V, eta, eta_scalar: float, W0, chunk: int, dZ, dW_T=None,

@@ -70,6 +70,110 @@ static void linear_slice(const double* K, const double* Q, const double* V,
 }
 
 /* ------------------------------------------------------------------------ */
+/* TTT-Linear with a bias, and optionally LayerNorm and a residual inside f,  */
+/* one slice.  diosapp "Test-Time Training (TTT) guide" §3 gives the inner    */
+/* linear model as f(x) = W x + b; the ablation discussed in PaperTrace "5 ·  */
+/* TestingTime 训练与长上下文" (the section relating the three pages) adds LN  */
+/* and a residual inside f, read here as f(x) = x + LN(W x + b) with          */
+/* LN(u) = g * (u - mean(u)) / sqrt(var(u) + eps) + beta over the d features  */
+/* (g, beta fixed: they belong to the outer model).  W and b are the state:  */
+/* per token, at the chunk-start (Wc, bc),                                   */
+/*   u = Wc k + bc,  r = f(k) - v,  grad_u = dl/du (through LN when present), */
+/*   G += eta grad_u k^T,  gb += eta grad_u,  z = f_{Wc - G, bc - gb}(q),      */
+/* and at the chunk end W = Wc - G, b = bc - gb.  lnw == NULL: f(x) = W x + b. */
+/* ------------------------------------------------------------------------ */
+/* LN of u over d features: writes the normalised uhat and returns 1/sigma.  */
+static double ln_normalise(const double* u, double* uhat, int d, double eps)
+{
+    double mu = 0.0, var = 0.0;
+    for (int i = 0; i < d; ++i) mu += u[i];
+    mu /= d;
+    for (int i = 0; i < d; ++i) var += (u[i] - mu) * (u[i] - mu);
+    var /= d;
+    const double rs = 1.0 / sqrt(var + eps);
+    for (int i = 0; i < d; ++i) uhat[i] = (u[i] - mu) * rs;
+    return rs;
+}
+
+static void linear_ln_slice(const double* K, const double* Q, const double* V,
+                            const double* eta, double eta_scalar,
+                            const double* W0, const double* b0,
+                            const double* lnw, const double* lnb, double eps,
+                            double* Z, double* W_out, double* b_out, int T, int d, int chunk)
+{
+    double* W  = (double*)malloc(sizeof(double) * d * d);
+    double* Wc = (double*)malloc(sizeof(double) * d * d);
+    double* G  = (double*)malloc(sizeof(double) * d * d);
+    double* b  = (double*)malloc(sizeof(double) * d);
+    double* bc = (double*)malloc(sizeof(double) * d);
+    double* gb = (double*)malloc(sizeof(double) * d);
+    double* u  = (double*)malloc(sizeof(double) * d);
+    double* uh = (double*)malloc(sizeof(double) * d);
+    double* gu = (double*)malloc(sizeof(double) * d);
+    memcpy(W, W0, sizeof(double) * d * d);
+    memcpy(b, b0, sizeof(double) * d);
+
+    for (int c0 = 0; c0 < T; c0 += chunk) {
+        int c1 = c0 + chunk < T ? c0 + chunk : T;
+        memcpy(Wc, W, sizeof(double) * d * d);
+        memcpy(bc, b, sizeof(double) * d);
+        memset(G, 0, sizeof(double) * d * d);
+        memset(gb, 0, sizeof(double) * d);
+        for (int t = c0; t < c1; ++t) {
+            const double* k = K + (size_t)t * d;
+            const double* q = Q + (size_t)t * d;
+            const double* v = V + (size_t)t * d;
+            const double et = eta ? eta[t] : eta_scalar;
+            /* pre-activation at the chunk-start state */
+            for (int i = 0; i < d; ++i) {
+                double acc = bc[i];
+                for (int j = 0; j < d; ++j) acc += Wc[i * d + j] * k[j];
+                u[i] = acc;
+            }
+            if (lnw) {
+                /* r = k + LN(u) - v; dl/duhat = g * r; back through the normalisation:
+                 * dl/du = (1/sigma) (h - mean(h) - uhat mean(h uhat)), h = dl/duhat */
+                const double rs = ln_normalise(u, uh, d, eps);
+                double mh = 0.0, mhu = 0.0;
+                for (int i = 0; i < d; ++i) {
+                    const double r = k[i] + lnw[i] * uh[i] + lnb[i] - v[i];
+                    gu[i] = lnw[i] * r;
+                    mh += gu[i];
+                    mhu += gu[i] * uh[i];
+                }
+                mh /= d;
+                mhu /= d;
+                for (int i = 0; i < d; ++i) gu[i] = rs * (gu[i] - mh - uh[i] * mhu);
+            } else {
+                for (int i = 0; i < d; ++i) gu[i] = u[i] - v[i];
+            }
+            for (int i = 0; i < d; ++i) {
+                for (int j = 0; j < d; ++j) G[i * d + j] += et * gu[i] * k[j];
+                gb[i] += et * gu[i];
+            }
+            /* read with the chunk's updates up to and including this token */
+            for (int i = 0; i < d; ++i) {
+                double acc = bc[i] - gb[i];
+                for (int j = 0; j < d; ++j) acc += (Wc[i * d + j] - G[i * d + j]) * q[j];
+                u[i] = acc;
+            }
+            double* z = Z + (size_t)t * d;
+            if (lnw) {
+                ln_normalise(u, uh, d, eps);
+                for (int i = 0; i < d; ++i) z[i] = q[i] + lnw[i] * uh[i] + lnb[i];
+            } else {
+                for (int i = 0; i < d; ++i) z[i] = u[i];
+            }
+        }
+        for (int i = 0; i < d * d; ++i) W[i] = Wc[i] - G[i];
+        for (int i = 0; i < d; ++i) b[i] = bc[i] - gb[i];
+    }
+    memcpy(W_out, W, sizeof(double) * d * d);
+    memcpy(b_out, b, sizeof(double) * d);
+    free(W); free(Wc); free(G); free(b); free(bc); free(gb); free(u); free(uh); free(gu);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Vector-Jacobian product of the TTT-Linear scan, one slice: the gradient of */
 /* L = <dZ, Z> + <dW_T, W_T> with respect to K, Q, V, every token's eta and W0. */
 /* Reverse mode through the same per-token loop as linear_slice (PaperTrace   */
@@ -337,9 +441,9 @@ static void mlp_slice(const double* K, const double* Q, const double* V,
 /* Thread pool over (batch, head) slices.                                    */
 /* ------------------------------------------------------------------------ */
 typedef struct {
-    int is_mlp, is_bwd, read_start;
-    const double *K, *Q, *V, *eta, *W0, *W1, *b1, *W2, *b2, *dZ, *dWT;
-    double eta_scalar;
+    int is_mlp, is_bwd, read_start, is_ln;
+    const double *K, *Q, *V, *eta, *W0, *W1, *b1, *W2, *b2, *dZ, *dWT, *b0, *lnw, *lnb;
+    double eta_scalar, eps;
     double *Z, *W_out, *W1_o, *b1_o, *W2_o, *b2_o, *dK, *dQ, *dV, *deta, *dW0;
     int BH, T, d, hd, chunk, nthreads, tid;
 } job_t;
@@ -350,7 +454,15 @@ static void* worker(void* arg)
     size_t td = (size_t)j->T * j->d;
     for (int s = j->tid; s < j->BH; s += j->nthreads) {
         const double* eta = j->eta ? j->eta + (size_t)s * j->T : NULL;
-        if (j->is_bwd) {
+        if (j->is_ln) {
+            size_t dd = (size_t)j->d * j->d;
+            linear_ln_slice(j->K + s * td, j->Q + s * td, j->V + s * td, eta, j->eta_scalar,
+                            j->W0 + s * dd, j->b0 + (size_t)s * j->d,
+                            j->lnw ? j->lnw + (size_t)s * j->d : NULL,
+                            j->lnb ? j->lnb + (size_t)s * j->d : NULL, j->eps,
+                            j->Z + s * td, j->W_out + s * dd, j->b1_o + (size_t)s * j->d,
+                            j->T, j->d, j->chunk);
+        } else if (j->is_bwd) {
             size_t dd = (size_t)j->d * j->d;
             linear_bwd_slice(j->K + s * td, j->Q + s * td, j->V + s * td, eta, j->eta_scalar,
                              j->W0 + s * dd, j->dZ + s * td, j->dWT ? j->dWT + s * dd : NULL,
@@ -422,6 +534,27 @@ int ttt_oracle_linear_read(const double* K, const double* Q, const double* V,
     j.read_start = read_start;
     j.K = K; j.Q = Q; j.V = V; j.eta = eta; j.eta_scalar = eta_scalar; j.W0 = W0;
     j.Z = Z; j.W_out = W_out; j.BH = BH; j.T = T; j.d = d; j.chunk = chunk;
+    j.nthreads = nthreads;
+    return run_pool(&j);
+}
+
+int ttt_oracle_linear_ln(const double* K, const double* Q, const double* V,
+                         const double* eta, double eta_scalar,
+                         const double* W0, const double* b0,
+                         const double* ln_weight, const double* ln_bias, double eps,
+                         double* Z, double* W_out, double* b_out,
+                         int BH, int T, int d, int chunk, int nthreads)
+{
+    if (!K || !Q || !V || !W0 || !b0 || !Z || !W_out || !b_out) return -1;
+    if ((ln_weight == NULL) != (ln_bias == NULL)) return -1;
+    if (BH <= 0 || T <= 0 || d <= 0 || chunk <= 0 || !(eps > 0.0)) return -1;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.is_ln = 1;
+    j.K = K; j.Q = Q; j.V = V; j.eta = eta; j.eta_scalar = eta_scalar; j.W0 = W0; j.b0 = b0;
+    j.lnw = ln_weight; j.lnb = ln_bias; j.eps = eps;
+    j.Z = Z; j.W_out = W_out; j.b1_o = b_out;
+    j.BH = BH; j.T = T; j.d = d; j.chunk = chunk;
     j.nthreads = nthreads;
     return run_pool(&j);
 }

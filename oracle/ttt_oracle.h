@@ -61,6 +61,20 @@ int ttt_oracle_linear_read(const double* K, const double* Q, const double* V,
                            double* Z, double* W_out,
                            int BH, int T, int d, int chunk, int read_start, int nthreads);
 
+/* TTT-Linear with the inner bias as state and, when ln_weight is given,
+ * LayerNorm and a residual inside f: f(x) = x + LN(W x + b), LN(u) =
+ * ln_weight * (u - mean) / sqrt(var + eps) + ln_bias over the d features
+ * (ln_weight, ln_bias fixed).  ln_weight == ln_bias == NULL: f(x) = W x + b.
+ *   b0, b_out           : [BH, d]
+ *   ln_weight, ln_bias  : [BH, d] or both NULL
+ * Same chunking, read order and eta conventions as ttt_oracle_linear. */
+int ttt_oracle_linear_ln(const double* K, const double* Q, const double* V,
+                         const double* eta, double eta_scalar,
+                         const double* W0, const double* b0,
+                         const double* ln_weight, const double* ln_bias, double eps,
+                         double* Z, double* W_out, double* b_out,
+                         int BH, int T, int d, int chunk, int nthreads);
+
 /* Vector-Jacobian product of ttt_oracle_linear: for L = <dZ, Z> + <dW_T, W_T>
  * (dW_T may be NULL for zero), writes dK, dQ, dV : [BH, T, d], deta : [BH, T]
  * (the gradient for each token's eta, also when eta is NULL and eta_scalar

@@ -55,6 +55,23 @@ MUTANTS = {
     "chunk-start read includes the chunk's updates": (
         "for (int j = 0; j < d; ++j) s += Ws[i * d + j] * q[j];",
         "for (int j = 0; j < d; ++j) s += (Ws[i * d + j] - G[i * d + j]) * q[j];"),
+    # TTT-Linear with the inner bias, LayerNorm and residual inside f
+    "LN backward drops the mean term": (
+        "gu[i] = rs * (gu[i] - mh - uh[i] * mhu);", "gu[i] = rs * (gu[i] - uh[i] * mhu);"),
+    "LN backward drops the projection term": (
+        "gu[i] = rs * (gu[i] - mh - uh[i] * mhu);", "gu[i] = rs * (gu[i] - mh);"),
+    "LN loss without the residual": (
+        "const double r = k[i] + lnw[i] * uh[i] + lnb[i] - v[i];",
+        "const double r = lnw[i] * uh[i] + lnb[i] - v[i];"),
+    "inner bias never updated": (
+        "gb[i] += et * gu[i];", "gb[i] += 0.0 * gu[i];"),
+    "LN output without the residual": (
+        "for (int i = 0; i < d; ++i) z[i] = q[i] + lnw[i] * uh[i] + lnb[i];",
+        "for (int i = 0; i < d; ++i) z[i] = lnw[i] * uh[i] + lnb[i];"),
+    "LN without eps": (
+        "const double rs = 1.0 / sqrt(var + eps);", "const double rs = 1.0 / sqrt(var);"),
+    "bias read without the chunk's updates": (
+        "double acc = bc[i] - gb[i];", "double acc = bc[i];"),
     # the vector-Jacobian product of the TTT-Linear scan
     "VJP: dq read at the chunk-start state": (
         "acc += (Wc[i * d + j] - G[i * d + j]) * dz[i];", "acc += Wc[i * d + j] * dz[i];"),
@@ -97,6 +114,7 @@ def run_pins(lib):
     env = dict(os.environ, TTT_ORACLE_LIB=lib)
     return subprocess.run([sys.executable, "-m", "pytest", os.path.join(HERE, "test_oracle_pins.py"),
                            os.path.join(HERE, "test_oracle_bwd_pins.py"),
+                           os.path.join(HERE, "test_oracle_ln_pins.py"),
                            "-x", "-q", "-p", "no:cacheprovider", "-k", NOT_PINS],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
 
