@@ -42,10 +42,12 @@ KERNEL_SOURCES = {"linear": ["linear_mfma.hip", "linear_coop.hip", "linear_gener
                   "mlp": ["mlp_mfma.hip", "mlp_generic.hip", "mfma_common.h", "device_common.h",
                           "launch.h", "api.cpp"],
                   "step": ["linear_step.hip", "device_common.h", "launch.h", "api.cpp"],
+                  "ln": ["linear_ln.hip", "device_common.h", "launch.h", "api.cpp"],
                   "bwd": ["linear_bwd.hip", "mfma_common.h", "device_common.h", "launch.h",
                           "api.cpp"]}
 DECODE_METRIC = "TTT-Linear decode tokens/sec (all heads) + % of HBM roofline"
 BWD_METRIC = "TTT-Linear backward tokens/sec (all heads) + % of fp32 MFMA roofline"
+LN_METRIC = "TTT-Linear (bias, LayerNorm, residual) tokens/sec (all heads) + % of fp32 ALU roofline"
 FP32_PEAK_TFS = 157.3            # MI355X dense fp32 matrix
 
 
@@ -230,6 +232,102 @@ def bwd_main(args, wl, x, seed):
                    "heads": H, "seq_len": T, "head_dim": d, "chunk": wl.chunk, "io": wl.io,
                    "parallelism": "single_gpu"},
         "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": FP32_PEAK_TFS,
+                     "unit": "TFLOP/s", "frac": round(tfs / FP32_PEAK_TFS, 4), "traffic": None,
+                     "kernel_ms": round(ms_event, 5), "algorithmic_flops": flops},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "head_tokens_per_s": round(B * H * T / (ms_step * 1e-3), 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def ln_main(args, wl, x, seed):
+    """TTT-Linear with the inner bias and LayerNorm + residual inside f: one step
+    is one ttt_linear_ln_fwd call over the batch (seeded LN weight ~ 1 + 0.1 N,
+    LN bias and b0 ~ 0.1 N, W0 std 0.1, eps 1e-5)."""
+    import torch
+    from test_sequence_layers_ttt_amd import ttt
+    dev = torch.device("cuda:0")
+    B, H, T, d = wl.B, wl.H, wl.T, wl.d
+    rng = np.random.default_rng([seed, 55])
+    b0 = (0.1 * rng.standard_normal((B, H, d))).astype(np.float32)
+    lnw = (1.0 + 0.1 * rng.standard_normal((H, d))).astype(np.float32)
+    lnb = (0.1 * rng.standard_normal((H, d))).astype(np.float32)
+    W0 = (0.1 * rng.standard_normal((B, H, d, d))).astype(np.float32)
+    eps = 1e-5
+    io = torch.bfloat16 if wl.io == "bf16" else torch.float32
+    t = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+    K, Q, V = (t(x[k].reshape(B, H, T, d), io) for k in ("K", "Q", "V"))
+    eta = None if x["eta"] is None else t(x["eta"].reshape(B, H, T))
+    W0d, b0d, lnwd, lnbd = t(W0), t(b0), t(lnw), t(lnb)
+    Z = torch.empty_like(K)
+    Wo, bo = torch.empty_like(W0d), torch.empty_like(b0d)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ttt.linear_ln_fwd(K, Q, V, eta, W0d, b0d, lnwd, lnbd, wl.chunk, eps=eps,
+                          eta_scalar=x["eta_scalar"], Z=Z, W_out=Wo, b_out=bo, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_event = ev0.elapsed_time(ev1) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    log("timed %d LN calls: %.4f ms/call (events), %.4f ms/call (wall)" % (
+        args.steps, ms_event, ms_step))
+    # the dual form's products (as the plain scan) plus the bias terms; LN is O(d) per token
+    flops = algorithmic_flops(wl) + 4.0 * wl.BH * T * d
+    tfs = flops / (ms_event * 1e-3) / 1e12
+    cpu = parity = None
+    if not args.no_cpu_baseline:
+        import oracle
+        nsl = args.cpu_sample_slices or int(max(1, min(wl.BH, 2.0e10 * 16 // (4.0 * T * d * d))))
+        idx = np.unique(np.linspace(0, wl.BH - 1, nsl).round().astype(int))
+        heads = idx % H
+        t1 = time.perf_counter()
+        Zo, Wref, bref, nth = oracle.linear_ln(x["K"][idx], x["Q"][idx], x["V"][idx],
+                                               None if x["eta"] is None else x["eta"][idx],
+                                               x["eta_scalar"], W0.reshape(-1, d, d)[idx],
+                                               b0.reshape(-1, d)[idx], lnw[heads], lnb[heads],
+                                               eps, wl.chunk, return_threads=True)
+        tcpu = time.perf_counter() - t1
+        cpu = {"value": round(len(idx) * T / H / tcpu, 1), "unit": "tokens/s", "cores": int(nth),
+               "kind": "oracle",
+               "sample": "%d of %d (batch, head) slices, full T=%d, fp64 per-token primal "
+                         "loop with LayerNorm, %.2f s" % (len(idx), wl.BH, T, tcpu)}
+        errs = {}
+        for name, g, r in (("Z", Z, Zo), ("W", Wo, Wref), ("b", bo, bref)):
+            gg = g.float().cpu().numpy().reshape(wl.BH, -1)[idx]
+            rr = r.reshape(len(idx), -1)
+            den = np.maximum(np.abs(rr).max(axis=1), 1e-6)
+            errs[name] = float("%.3e" % (np.abs(gg - rr).max(axis=1) / den).max())
+        parity = {"max_rel_err": errs, "slices_checked": int(len(idx))}
+        log("oracle: %d slices in %.2f s; parity %s" % (len(idx), tcpu, parity))
+    rec = {
+        "metric": LN_METRIC,
+        "value": round(B * T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name + "_ln", "scan": "ttt_linear_ln_fwd", "batch": B,
+                   "heads": H, "seq_len": T, "head_dim": d, "chunk": wl.chunk, "io": wl.io,
+                   "parallelism": "single_gpu"},
+        "roofline": {"bound": "alu", "achieved": round(tfs, 3), "peak": FP32_PEAK_TFS,
                      "unit": "TFLOP/s", "frac": round(tfs / FP32_PEAK_TFS, 4), "traffic": None,
                      "kernel_ms": round(ms_event, 5), "algorithmic_flops": flops},
         "cpu_baseline": cpu,
@@ -444,6 +542,8 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0)
     ap.add_argument("--decode", type=int, default=0,
                     help="time ttt_linear_step continuing every sequence by N tokens")
+    ap.add_argument("--ln", action="store_true",
+                    help="TTT-Linear with the inner bias and LayerNorm + residual inside f")
     ap.add_argument("--varlen", action="store_true",
                     help="TTT-Linear over the workload's tokens packed as documents with resets")
     ap.add_argument("--read-start", action="store_true",
@@ -468,6 +568,11 @@ def main():
 
     wl = inputs.WORKLOADS[args.workload]
     seed = inputs.WORKLOAD_SEEDS[wl.name]
+    if args.ln:
+        if wl.model != "linear":
+            raise SystemExit("--ln needs a TTT-Linear workload")
+        ln_main(args, wl, inputs.make_inputs(wl, seed), seed)
+        return
     if args.varlen:
         if wl.model != "linear":
             raise SystemExit("--varlen needs a TTT-Linear workload")

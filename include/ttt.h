@@ -130,6 +130,27 @@ int ttt_linear_fwd(const void* K, const void* Q, const void* V,
                    void* workspace, size_t workspace_bytes,
                    void* stream, int plan);
 
+/* TTT-Linear with the inner bias as part of the state and, when ln_weight is
+ * given, LayerNorm and a residual inside the inner model:
+ *   f(x) = x + LN(W x + b),  LN(u) = ln_weight * (u - mean(u)) / sqrt(var(u) + eps)
+ *                                    + ln_bias   (over the d features),
+ * or f(x) = W x + b when ln_weight == ln_bias == NULL (diosapp "Test-Time
+ * Training (TTT) guide" §3 gives f(x) = W x + b; the LN-and-residual ablation
+ * is the one PaperTrace "5 · TestingTime 训练与长上下文" discusses).  W and b
+ * take the chunked gradient step of ttt_linear_fwd (loss 1/2 ||f(k) - v||^2,
+ * gradients at the chunk-start state, inclusive read); ln_weight and ln_bias
+ * are fixed (outer-model parameters).
+ *   b0, b_out            : [B, H, d] fp32 (b_out may alias b0; b0 may be zeros).
+ *   ln_weight, ln_bias   : [H, d] fp32, shared by the batch, or both NULL.
+ *   eps                  : > 0, finite.
+ *   Others as ttt_linear_fwd; d : 16, 32, 64 or 128; any chunk; fp32 arithmetic
+ *   on the vector ALUs, one workgroup per (batch, head); no workspace. */
+int ttt_linear_ln_fwd(const void* K, const void* Q, const void* V,
+                      const float* eta, float eta_scalar, const float* W0, const float* b0,
+                      const float* ln_weight, const float* ln_bias, float eps,
+                      void* Z, float* W_out, float* b_out,
+                      int B, int H, int T, int d, int chunk, int io_dtype, void* stream);
+
 /* Packed documents with a reset at every document (variable-length batches).
  * Each document of every head is its own TTT-Linear scan from its own initial
  * state: no state, gradient or output crosses a document boundary, and chunks

@@ -194,6 +194,33 @@ int ttt_linear_bwd(const void* K, const void* Q, const void* V,
     return launch_status(launch_linear_bwd(a, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int ttt_linear_ln_fwd(const void* K, const void* Q, const void* V,
+                      const float* eta, float eta_scalar, const float* W0, const float* b0,
+                      const float* ln_weight, const float* ln_bias, float eps,
+                      void* Z, float* W_out, float* b_out,
+                      int B, int H, int T, int d, int chunk, int io_dtype, void* stream)
+{
+    if (!K || !Q || !V || !W0 || !b0 || !Z || !W_out || !b_out) return TTT_ERR_INVALID_ARG;
+    if ((ln_weight == nullptr) != (ln_bias == nullptr)) return TTT_ERR_INVALID_ARG;
+    if (!aligned(K, 16) || !aligned(Q, 16) || !aligned(V, 16) || !aligned(Z, 16) ||
+        !aligned(W0, 16) || !aligned(W_out, 16) || !aligned(b0, 4) || !aligned(b_out, 4) ||
+        (ln_weight && (!aligned(ln_weight, 4) || !aligned(ln_bias, 4))))
+        return TTT_ERR_INVALID_ARG;
+    if (eta ? !aligned(eta, 4) : !std::isfinite(eta_scalar)) return TTT_ERR_INVALID_ARG;
+    if (!std::isfinite(eps) || !(eps > 0.f)) return TTT_ERR_INVALID_ARG;
+    if (!dims_ok(B, H, T, d, chunk)) return TTT_ERR_INVALID_ARG;
+    if (io_dtype != TTT_DTYPE_F32 && io_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARG;
+    if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
+
+    LinearLnArgs a;
+    a.K = K; a.Q = Q; a.V = V; a.eta = eta; a.eta_scalar = eta_scalar;
+    a.W0 = W0; a.b0 = b0; a.ln_weight = ln_weight; a.ln_bias = ln_bias; a.eps = eps;
+    a.Z = Z; a.W_out = W_out; a.b_out = b_out;
+    a.BH = B * H; a.H = H; a.T = T; a.d = d; a.chunk = chunk;
+    a.bf16 = io_dtype == TTT_DTYPE_BF16;
+    return launch_status(launch_linear_ln(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int ttt_linear_step(const void* K, const void* Q, const void* V,
                     const float* eta, float eta_scalar, float* W_chunk, float* G, int pos,
                     void* Z, int B, int H, int n, int d, int chunk, int io_dtype, void* stream)

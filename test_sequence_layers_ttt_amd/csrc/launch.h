@@ -83,6 +83,28 @@ bool linear_bigchunk_supported(int d, int chunk, int bf16);
 size_t linear_bigchunk_workspace(int BH, int T, int d, int chunk);
 hipError_t launch_linear_bigchunk(const LinearArgs& a, hipStream_t s);
 
+struct LinearLnArgs {
+    const void* K;
+    const void* Q;
+    const void* V;
+    const float* eta;
+    float eta_scalar;
+    const float* W0;         // [BH, d, d]
+    const float* b0;         // [BH, d]
+    const float* ln_weight;  // [H, d] or nullptr (no LayerNorm, no residual)
+    const float* ln_bias;    // [H, d] or nullptr
+    float eps;
+    void* Z;
+    float* W_out;
+    float* b_out;
+    int BH, H, T, d, chunk;
+    int bf16;
+};
+
+// TTT-Linear with the inner bias and optional LayerNorm + residual inside f:
+// fp32 vector ALU, one workgroup per (batch, head), any chunk, d <= 128.
+hipError_t launch_linear_ln(const LinearLnArgs& a, hipStream_t s);
+
 struct LinearBwdArgs {
     const void* K;
     const void* Q;

@@ -22,7 +22,7 @@ READ_INCLUSIVE, READ_CHUNK_START = 0, 1
 EXPORTS = ("ttt_linear_workspace_bytes", "ttt_linear_select_plan", "ttt_linear_fwd",
            "ttt_linear_step", "ttt_linear_bwd_workspace_bytes", "ttt_linear_bwd",
            "ttt_linear_fwd_ex", "ttt_linear_select_plan_ex",
-           "ttt_linear_fwd_varlen", "ttt_linear_select_plan_varlen",
+           "ttt_linear_fwd_varlen", "ttt_linear_select_plan_varlen", "ttt_linear_ln_fwd",
            "ttt_mlp_workspace_bytes", "ttt_mlp_select_plan", "ttt_mlp_fwd",
            "ttt_status_string", "ttt_plan_name")
 
@@ -54,6 +54,9 @@ def lib() -> ctypes.CDLL:
         L.ttt_linear_fwd_ex.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, i, i, i, i, i, i, vp, sz,
                                         vp, i, i]
         L.ttt_linear_fwd_ex.restype = i
+        L.ttt_linear_ln_fwd.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, vp, f, vp, vp, vp,
+                                        i, i, i, i, i, i, vp]
+        L.ttt_linear_ln_fwd.restype = i
         L.ttt_linear_fwd_varlen.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, vp, i, i, i, i, i, i,
                                             vp, i]
         L.ttt_linear_fwd_varlen.restype = i
@@ -260,6 +263,38 @@ def linear_step(K, Q, V, eta, W_chunk, G, pos: int, chunk: int, eta_scalar: floa
     if rc != OK:
         raise TTTError(rc, "ttt_linear_step")
     return Z, (int(pos) + n) % int(chunk)
+
+
+def linear_ln_fwd(K, Q, V, eta, W0, b0, ln_weight, ln_bias, chunk: int, eps: float = 1e-6,
+                  eta_scalar: float = 0.0, *, Z=None, W_out=None, b_out=None,
+                  stream=None) -> Tuple:
+    """TTT-Linear with f(x) = x + LN(W x + b) (ln_weight, ln_bias: [H, d]) or
+    f(x) = W x + b (both None).  b0: [B, H, d].  Returns (Z, W_out, b_out)."""
+    import torch
+    B, H, T, d = K.shape
+    _check(K, "K", (B, H, T, d))
+    _check(Q, "Q", (B, H, T, d), K.dtype)
+    _check(V, "V", (B, H, T, d), K.dtype)
+    _check(W0, "W0", (B, H, d, d), torch.float32)
+    _check(b0, "b0", (B, H, d), torch.float32)
+    if (ln_weight is None) != (ln_bias is None):
+        raise ValueError("ln_weight and ln_bias go together")
+    if ln_weight is not None:
+        _check(ln_weight, "ln_weight", (H, d), torch.float32)
+        _check(ln_bias, "ln_bias", (H, d), torch.float32)
+    if eta is not None:
+        _check(eta, "eta", (B, H, T), torch.float32)
+    Z = torch.empty_like(K) if Z is None else Z
+    W_out = torch.empty_like(W0) if W_out is None else W_out
+    b_out = torch.empty_like(b0) if b_out is None else b_out
+    rc = lib().ttt_linear_ln_fwd(K.data_ptr(), Q.data_ptr(), V.data_ptr(), _ptr(eta),
+                                 float(eta_scalar), W0.data_ptr(), b0.data_ptr(), _ptr(ln_weight),
+                                 _ptr(ln_bias), float(eps), Z.data_ptr(), W_out.data_ptr(),
+                                 b_out.data_ptr(), B, H, T, d, int(chunk), _io_dtype(K),
+                                 _stream(K.device, stream))
+    if rc != OK:
+        raise TTTError(rc, "ttt_linear_ln_fwd")
+    return Z, W_out, b_out
 
 
 def linear_select_plan_varlen(n_docs, H, total_T, d, chunk, io_dtype, plan=PLAN_AUTO) -> int:

@@ -263,6 +263,37 @@ def test_varlen_plan_selection():
     assert ttt.linear_select_plan_varlen(3, 2, 0, 16, 16, 0) == ttt.PLAN_GENERIC
 
 
+def _ln(**kw):
+    a = dict(K=FAKE, Q=FAKE, V=FAKE, eta=None, eta_scalar=0.1, W0=FAKE, b0=FAKE, lnw=FAKE,
+             lnb=FAKE, eps=1e-5, Z=FAKE, W=FAKE, b=FAKE, B=1, H=2, T=40, d=64, chunk=16, io=1,
+             stream=None)
+    a.update(kw)
+    return ttt.lib().ttt_linear_ln_fwd(a["K"], a["Q"], a["V"], a["eta"], a["eta_scalar"],
+                                       a["W0"], a["b0"], a["lnw"], a["lnb"], a["eps"], a["Z"],
+                                       a["W"], a["b"], a["B"], a["H"], a["T"], a["d"], a["chunk"],
+                                       a["io"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(b0=None), ttt.ERR_INVALID_ARG),
+    (dict(b=None), ttt.ERR_INVALID_ARG),
+    (dict(lnw=None), ttt.ERR_INVALID_ARG),          # weight and bias go together
+    (dict(lnb=None), ttt.ERR_INVALID_ARG),
+    (dict(lnw=FAKE + 2), ttt.ERR_INVALID_ARG),
+    (dict(b0=FAKE + 1), ttt.ERR_INVALID_ARG),
+    (dict(W0=FAKE + 4), ttt.ERR_INVALID_ARG),
+    (dict(eps=0.0), ttt.ERR_INVALID_ARG),
+    (dict(eps=-1.0), ttt.ERR_INVALID_ARG),
+    (dict(eps=math.inf), ttt.ERR_INVALID_ARG),
+    (dict(eta_scalar=math.nan), ttt.ERR_INVALID_ARG),
+    (dict(T=0), ttt.ERR_INVALID_ARG),
+    (dict(io=2), ttt.ERR_INVALID_ARG),
+    (dict(d=48), ttt.ERR_UNSUPPORTED),
+])
+def test_ln_rejects_bad_arguments(kw, status):
+    assert _ln(**kw) == status
+
+
 def test_plan_selection_and_workspace_are_host_only():
     assert ttt.linear_select_plan(1, 1, 256, 16, 16, ttt.DTYPE_F32) == ttt.PLAN_GENERIC
     assert ttt.linear_select_plan(1, 1, 256, 16, 16, 0, ttt.PLAN_GENERIC) == ttt.PLAN_GENERIC
