@@ -53,6 +53,11 @@ def _load():
                                                ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, ctypes.c_int, ctypes.c_int]
         lib.ttt_oracle_linear_read.restype = ctypes.c_int
+        lib.ttt_oracle_linear_momentum.argtypes = [P, P, P, P, ctypes.c_double, P, P,
+                                                   ctypes.c_double, P, P, P,
+                                                   ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                   ctypes.c_int, ctypes.c_int]
+        lib.ttt_oracle_linear_momentum.restype = ctypes.c_int
         lib.ttt_oracle_linear_ln.argtypes = [P, P, P, P, ctypes.c_double, P, P, P, P,
                                              ctypes.c_double, P, P, P,
                                              ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -108,6 +113,24 @@ def linear(K, Q, V, eta, eta_scalar: float, W0, chunk: int,
     if rc <= 0:
         raise ValueError("ttt_oracle_linear rejected its arguments")
     return (Z, W, rc) if return_threads else (Z, W)
+
+
+def linear_momentum(K, Q, V, eta, eta_scalar: float, W0, M0, beta: float, chunk: int,
+                    nthreads: int = 0, return_threads: bool = False):
+    """TTT-Linear with a momentum state (chunk-start reads).  M0: [n, d, d] or None.
+    Returns (Z, W_T, M_T) in fp64."""
+    K, Q, V, W0, M0, eta = _f64(K), _f64(Q), _f64(V), _f64(W0), _f64(M0), _f64(eta)
+    n, T, d = K.shape
+    Z = np.empty((n, T, d), np.float64)
+    W = np.empty((n, d, d), np.float64)
+    M = np.empty((n, d, d), np.float64)
+    rc = _load().ttt_oracle_linear_momentum(_ptr(K), _ptr(Q), _ptr(V), _ptr(eta),
+                                            float(eta_scalar), _ptr(W0), _ptr(M0), float(beta),
+                                            _ptr(Z), _ptr(W), _ptr(M), n, T, d, int(chunk),
+                                            int(nthreads))
+    if rc <= 0:
+        raise ValueError("ttt_oracle_linear_momentum rejected its arguments")
+    return (Z, W, M, rc) if return_threads else (Z, W, M)
 
 
 def linear_ln(K, Q, V, eta, eta_scalar: float, W0, b0, ln_weight, ln_bias, eps: float,

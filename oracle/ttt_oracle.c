@@ -70,6 +70,60 @@ static void linear_slice(const double* K, const double* Q, const double* V,
 }
 
 /* ------------------------------------------------------------------------ */
+/* TTT-Linear with a momentum state, one slice.  The E2-TTT passage of        */
+/* "Test-Time Training (TTT)" (§2.3, §5.1) keeps a momentum M next to the     */
+/* fast weights, updated per chunk from the chunk's gradient at the chunk     */
+/* start, M_{c+1} = beta M_c + (1 - beta) grad_c; the step it applies is read  */
+/* here as W_{c+1} = W_c - M_{c+1}, with grad_c the eta-weighted sum of the   */
+/* chunk's token gradients.  The pages give momentum at chunk level only, so  */
+/* every token reads with the chunk-start state: z_t = W_c q_t.  beta = 0 is   */
+/* the chunk-start scan.                                                     */
+/* ------------------------------------------------------------------------ */
+static void linear_momentum_slice(const double* K, const double* Q, const double* V,
+                                  const double* eta, double eta_scalar, const double* W0,
+                                  const double* M0, double beta, double* Z, double* W_out,
+                                  double* M_out, int T, int d, int chunk)
+{
+    double* W   = (double*)malloc(sizeof(double) * d * d);
+    double* Mom = (double*)malloc(sizeof(double) * d * d);
+    double* Gr  = (double*)malloc(sizeof(double) * d * d);   /* the chunk's gradient */
+    double* e   = (double*)malloc(sizeof(double) * d);
+    memcpy(W, W0, sizeof(double) * d * d);
+    if (M0) memcpy(Mom, M0, sizeof(double) * d * d);
+    else memset(Mom, 0, sizeof(double) * d * d);
+
+    for (int c0 = 0; c0 < T; c0 += chunk) {
+        int c1 = c0 + chunk < T ? c0 + chunk : T;
+        memset(Gr, 0, sizeof(double) * d * d);
+        for (int t = c0; t < c1; ++t) {
+            const double* k = K + (size_t)t * d;
+            const double* q = Q + (size_t)t * d;
+            const double* v = V + (size_t)t * d;
+            const double et = eta ? eta[t] : eta_scalar;
+            double* z = Z + (size_t)t * d;
+            for (int i = 0; i < d; ++i) {
+                double se = 0.0, sz = 0.0;
+                for (int j = 0; j < d; ++j) {
+                    se += W[i * d + j] * k[j];
+                    sz += W[i * d + j] * q[j];
+                }
+                e[i] = se - v[i];
+                z[i] = sz;
+            }
+            for (int i = 0; i < d; ++i)
+                for (int j = 0; j < d; ++j) Gr[i * d + j] += et * e[i] * k[j];
+        }
+        for (int i = 0; i < d * d; ++i) {
+            Mom[i] = beta * Mom[i] + (1.0 - beta) * Gr[i];
+            W[i] -= Mom[i];
+        }
+    }
+    memcpy(W_out, W, sizeof(double) * d * d);
+    memcpy(M_out, Mom, sizeof(double) * d * d);
+    free(W); free(Mom); free(Gr); free(e);
+}
+
+/* ------------------------------------------------------------------------ */
 /* TTT-Linear with a bias, and optionally LayerNorm and a residual inside f,  */
 /* one slice.  diosapp "Test-Time Training (TTT) guide" §3 gives the inner    */
 /* linear model as f(x) = W x + b; the ablation discussed in PaperTrace "5 ·  */
@@ -441,9 +495,9 @@ static void mlp_slice(const double* K, const double* Q, const double* V,
 /* Thread pool over (batch, head) slices.                                    */
 /* ------------------------------------------------------------------------ */
 typedef struct {
-    int is_mlp, is_bwd, read_start, is_ln;
-    const double *K, *Q, *V, *eta, *W0, *W1, *b1, *W2, *b2, *dZ, *dWT, *b0, *lnw, *lnb;
-    double eta_scalar, eps;
+    int is_mlp, is_bwd, read_start, is_ln, is_mom;
+    const double *K, *Q, *V, *eta, *W0, *W1, *b1, *W2, *b2, *dZ, *dWT, *b0, *lnw, *lnb, *M0;
+    double eta_scalar, eps, beta;
     double *Z, *W_out, *W1_o, *b1_o, *W2_o, *b2_o, *dK, *dQ, *dV, *deta, *dW0;
     int BH, T, d, hd, chunk, nthreads, tid;
 } job_t;
@@ -454,7 +508,13 @@ static void* worker(void* arg)
     size_t td = (size_t)j->T * j->d;
     for (int s = j->tid; s < j->BH; s += j->nthreads) {
         const double* eta = j->eta ? j->eta + (size_t)s * j->T : NULL;
-        if (j->is_ln) {
+        if (j->is_mom) {
+            size_t dd = (size_t)j->d * j->d;
+            linear_momentum_slice(j->K + s * td, j->Q + s * td, j->V + s * td, eta,
+                                  j->eta_scalar, j->W0 + s * dd, j->M0 ? j->M0 + s * dd : NULL,
+                                  j->beta, j->Z + s * td, j->W_out + s * dd, j->W1_o + s * dd,
+                                  j->T, j->d, j->chunk);
+        } else if (j->is_ln) {
             size_t dd = (size_t)j->d * j->d;
             linear_ln_slice(j->K + s * td, j->Q + s * td, j->V + s * td, eta, j->eta_scalar,
                             j->W0 + s * dd, j->b0 + (size_t)s * j->d,
@@ -534,6 +594,25 @@ int ttt_oracle_linear_read(const double* K, const double* Q, const double* V,
     j.read_start = read_start;
     j.K = K; j.Q = Q; j.V = V; j.eta = eta; j.eta_scalar = eta_scalar; j.W0 = W0;
     j.Z = Z; j.W_out = W_out; j.BH = BH; j.T = T; j.d = d; j.chunk = chunk;
+    j.nthreads = nthreads;
+    return run_pool(&j);
+}
+
+int ttt_oracle_linear_momentum(const double* K, const double* Q, const double* V,
+                               const double* eta, double eta_scalar, const double* W0,
+                               const double* M0, double beta,
+                               double* Z, double* W_out, double* M_out,
+                               int BH, int T, int d, int chunk, int nthreads)
+{
+    if (!K || !Q || !V || !W0 || !Z || !W_out || !M_out) return -1;
+    if (BH <= 0 || T <= 0 || d <= 0 || chunk <= 0 || !(beta >= 0.0 && beta < 1.0)) return -1;
+    job_t j;
+    memset(&j, 0, sizeof j);
+    j.is_mom = 1;
+    j.K = K; j.Q = Q; j.V = V; j.eta = eta; j.eta_scalar = eta_scalar; j.W0 = W0;
+    j.M0 = M0; j.beta = beta;
+    j.Z = Z; j.W_out = W_out; j.W1_o = M_out;
+    j.BH = BH; j.T = T; j.d = d; j.chunk = chunk;
     j.nthreads = nthreads;
     return run_pool(&j);
 }

@@ -75,6 +75,17 @@ int ttt_oracle_linear_ln(const double* K, const double* Q, const double* V,
                          double* Z, double* W_out, double* b_out,
                          int BH, int T, int d, int chunk, int nthreads);
 
+/* TTT-Linear with a momentum state M: per chunk, with grad_c the eta-weighted
+ * sum of the chunk's token gradients at the chunk-start state,
+ * M_{c+1} = beta M_c + (1 - beta) grad_c and W_{c+1} = W_c - M_{c+1}; every
+ * token reads with its chunk-start state (z_t = W_c q_t).  M0 may be NULL
+ * (zero); 0 <= beta < 1.  M_out : [BH, d, d]. */
+int ttt_oracle_linear_momentum(const double* K, const double* Q, const double* V,
+                               const double* eta, double eta_scalar, const double* W0,
+                               const double* M0, double beta,
+                               double* Z, double* W_out, double* M_out,
+                               int BH, int T, int d, int chunk, int nthreads);
+
 /* Vector-Jacobian product of ttt_oracle_linear: for L = <dZ, Z> + <dW_T, W_T>
  * (dW_T may be NULL for zero), writes dK, dQ, dV : [BH, T, d], deta : [BH, T]
  * (the gradient for each token's eta, also when eta is NULL and eta_scalar

@@ -55,6 +55,12 @@ MUTANTS = {
     "chunk-start read includes the chunk's updates": (
         "for (int j = 0; j < d; ++j) s += Ws[i * d + j] * q[j];",
         "for (int j = 0; j < d; ++j) s += (Ws[i * d + j] - G[i * d + j]) * q[j];"),
+    "momentum weights swapped": (
+        "Mom[i] = beta * Mom[i] + (1.0 - beta) * Gr[i];", "Mom[i] = (1.0 - beta) * Mom[i] + beta * Gr[i];"),
+    "momentum not carried": (
+        "Mom[i] = beta * Mom[i] + (1.0 - beta) * Gr[i];", "Mom[i] = (1.0 - beta) * Gr[i];"),
+    "momentum read with the running state": (
+        "sz += W[i * d + j] * q[j];", "sz += (W[i * d + j] - Gr[i * d + j]) * q[j];"),
     # TTT-Linear with the inner bias, LayerNorm and residual inside f
     "LN backward drops the mean term": (
         "gu[i] = rs * (gu[i] - mh - uh[i] * mhu);", "gu[i] = rs * (gu[i] - uh[i] * mhu);"),

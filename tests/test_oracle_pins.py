@@ -409,3 +409,56 @@ def test_read_start_zero_state_reads_zero():
     K, Q, V, eta, _ = rand_linear(rng, 2, 12, 4)
     Z, _ = oracle.linear(K, Q, V, eta, 0.0, np.zeros((2, 4, 4)), chunk=12, read_start=True)
     assert np.all(Z == 0)
+
+
+# ------------------------------------------------ TTT-Linear with a momentum state
+# M_{c+1} = beta M_c + (1 - beta) grad_c, W_{c+1} = W_c - M_{c+1}, chunk-start reads
+# (the E2-TTT passage of "Test-Time Training (TTT)" §2.3, §5.1).
+@pytest.mark.parametrize("chunk", [1, 5, 16])
+def test_momentum_zero_beta_is_the_chunk_start_scan(chunk):
+    rng = np.random.default_rng(81)
+    K, Q, V, eta, W0 = rand_linear(rng, 2, 37, 6)
+    Z, WT, MT = oracle.linear_momentum(K, Q, V, eta, 0.0, W0, None, 0.0, chunk)
+    Zs, Ws = oracle.linear(K, Q, V, eta, 0.0, W0, chunk, read_start=True)
+    np.testing.assert_allclose(Z, Zs, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(WT, Ws, rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("beta,chunk", [(0.5, 4), (0.9, 16), (0.3, 1)])
+def test_momentum_matches_the_chunk_matrix_form(beta, chunk):
+    """The same recurrence in chunk-matrix form: grad_c = (E diag(eta))^T K with
+    E = K W_c^T - V (token rows), M <- beta M + (1 - beta) grad_c, W <- W - M,
+    Z_c = Q_c W_c^T; with a nonzero initial momentum."""
+    rng = np.random.default_rng(82)
+    n, T, d = 2, 29, 5
+    K, Q, V, eta, W0 = rand_linear(rng, n, T, d)
+    M0 = rng.standard_normal((n, d, d)) * 0.05
+    Z, WT, MT = oracle.linear_momentum(K, Q, V, eta, 0.0, W0, M0, beta, chunk)
+    for s in range(n):
+        W, M = W0[s].copy(), M0[s].copy()
+        for c0 in range(0, T, chunk):
+            c1 = min(T, c0 + chunk)
+            E = K[s, c0:c1] @ W.T - V[s, c0:c1]
+            np.testing.assert_allclose(Z[s, c0:c1], Q[s, c0:c1] @ W.T, rtol=0, atol=1e-11)
+            grad = (eta[s, c0:c1, None] * E).T @ K[s, c0:c1]
+            M = beta * M + (1 - beta) * grad
+            W = W - M
+        np.testing.assert_allclose(WT[s], W, rtol=0, atol=1e-11)
+        np.testing.assert_allclose(MT[s], M, rtol=0, atol=1e-11)
+
+
+def test_momentum_without_gradient_decays_geometrically():
+    """Zero keys and values give a zero gradient: M_c = beta^c M_0 and
+    W_T = W_0 - M_0 (beta + ... + beta^C)."""
+    rng = np.random.default_rng(83)
+    n, T, d, chunk, beta = 1, 20, 4, 4, 0.7
+    K = np.zeros((n, T, d))
+    V = np.zeros((n, T, d))
+    Q = rng.standard_normal((n, T, d))
+    W0 = rng.standard_normal((n, d, d))
+    M0 = rng.standard_normal((n, d, d))
+    _, WT, MT = oracle.linear_momentum(K, Q, V, None, 0.1, W0, M0, beta, chunk)
+    C = T // chunk
+    np.testing.assert_allclose(MT[0], beta ** C * M0[0], rtol=1e-13)
+    np.testing.assert_allclose(WT[0], W0[0] - M0[0] * sum(beta ** i for i in range(1, C + 1)),
+                               rtol=1e-12, atol=1e-13)
