@@ -546,6 +546,8 @@ def main():
                     help="TTT-Linear with the inner bias and LayerNorm + residual inside f")
     ap.add_argument("--varlen", action="store_true",
                     help="TTT-Linear over the workload's tokens packed as documents with resets")
+    ap.add_argument("--momentum", type=float, default=None,
+                    help="TTT-Linear with a momentum state of this beta (chunk-start reads)")
     ap.add_argument("--read-start", action="store_true",
                     help="TTT-Linear with the chunk-start read order")
     ap.add_argument("--bwd", action="store_true",
@@ -593,6 +595,8 @@ def main():
     dev = torch.device("cuda:0")
     plan_req = PLANS[args.plan]
     io_code = ttt.DTYPE_BF16 if wl.io == "bf16" else ttt.DTYPE_F32
+    if args.momentum is not None:
+        args.read_start = True   # the momentum scan reads every chunk at its start state
     read_mode = ttt.READ_CHUNK_START if args.read_start else ttt.READ_INCLUSIVE
     if args.read_start and wl.model != "linear":
         raise SystemExit("--read-start applies to TTT-Linear")
@@ -649,9 +653,16 @@ def main():
         ncopies, set_bytes / 1e6, nbytes_ws / 1e6))
     stream = torch.cuda.current_stream(dev)
 
+    mom_out = torch.empty_like(base["W0"]) if args.momentum is not None else None
+
     def step(i):
         a, o = sets[i % ncopies]
-        if wl.model == "linear":
+        if args.momentum is not None:
+            ttt.linear_fwd_momentum(a["K"], a["Q"], a["V"], a["eta"], a["W0"], None,
+                                    args.momentum, wl.chunk, eta_scalar=x["eta_scalar"],
+                                    Z=o["Z"], W_out=o["W"], Mom_out=mom_out, workspace=ws,
+                                    plan=plan_req, stream=stream)
+        elif wl.model == "linear":
             ttt.linear_fwd(a["K"], a["Q"], a["V"], a["eta"], a["W0"], wl.chunk,
                            eta_scalar=x["eta_scalar"], Z=o["Z"], W_out=o["W"], workspace=ws,
                            plan=plan_req, stream=stream, read_mode=read_mode)
@@ -717,7 +728,12 @@ def main():
         idx = np.unique(idx)
         xo = {k: (v[idx] if isinstance(v, np.ndarray) else v) for k, v in x.items()}
         t1 = time.perf_counter()
-        if wl.model == "linear":
+        if args.momentum is not None:
+            Zo, Wo, _, nth = oracle.linear_momentum(xo["K"], xo["Q"], xo["V"], xo["eta"],
+                                                    xo["eta_scalar"], xo["W0"], None,
+                                                    args.momentum, wl.chunk, return_threads=True)
+            refs = {"Z": Zo, "W": Wo}
+        elif wl.model == "linear":
             Zo, Wo, nth = oracle.linear(xo["K"], xo["Q"], xo["V"], xo["eta"], xo["eta_scalar"],
                                         xo["W0"], wl.chunk, return_threads=True,
                                         read_start=args.read_start)
@@ -761,7 +777,8 @@ def main():
         "dtype": ("f32" if wl.io == "f32" or plan_name == "generic"
                   else ("f16" if wl.model == "mlp" else "bf16")),
         "data": "synthetic",
-        "config": {"workload": wl.name + ("_read_start" if args.read_start else ""),
+        "config": {"workload": wl.name + ("_momentum" if args.momentum is not None else
+                                          ("_read_start" if args.read_start else "")),
                    "scan": "ttt_" + wl.model, "batch": B, "heads": H,
                    "seq_len": T, "head_dim": d, "chunk": wl.chunk, "plan": plan_name,
                    "state_dtype": "f32", "parallelism": "single_gpu"},

@@ -130,6 +130,26 @@ int ttt_linear_fwd(const void* K, const void* Q, const void* V,
                    void* workspace, size_t workspace_bytes,
                    void* stream, int plan);
 
+/* TTT-Linear with a momentum state (the E2-TTT passage of "Test-Time Training
+ * (TTT)", §2.3 and §5.1: fast weights and a momentum evolve per chunk from the
+ * gradient at the chunk start).  With grad_c the eta-weighted sum of chunk c's
+ * token gradients at its start state W_c:
+ *   Mom_{c+1} = beta Mom_c + (1 - beta) grad_c,   W_{c+1} = W_c - Mom_{c+1},
+ * and every token of a chunk reads with W_c (z_t = W_c q_t), as the passage
+ * states the update per chunk only.  beta = 0 is ttt_linear_fwd_ex with
+ * TTT_READ_CHUNK_START.
+ *   Mom0     : [B, H, d, d] fp32 initial momentum, or NULL for zero.
+ *   Mom_out  : [B, H, d, d] fp32 final momentum (may alias Mom0).
+ *   beta     : 0 <= beta < 1.
+ *   Plans: GENERIC (any chunk) and BIGCHUNK (as ttt_linear_fwd; its workspace);
+ *   MFMA is TTT_ERR_UNSUPPORTED.  Other arguments as ttt_linear_fwd. */
+int ttt_linear_fwd_momentum(const void* K, const void* Q, const void* V,
+                            const float* eta, float eta_scalar, const float* W0,
+                            const float* Mom0, float beta,
+                            void* Z, float* W_out, float* Mom_out,
+                            int B, int H, int T, int d, int chunk, int io_dtype,
+                            void* workspace, size_t workspace_bytes, void* stream, int plan);
+
 /* TTT-Linear with the inner bias as part of the state and, when ln_weight is
  * given, LayerNorm and a residual inside the inner model:
  *   f(x) = x + LN(W x + b),  LN(u) = ln_weight * (u - mean(u)) / sqrt(var(u) + eps)

@@ -149,6 +149,7 @@ int ttt_linear_fwd_ex(const void* K, const void* Q, const void* V,
     a.read_start = read_mode == TTT_READ_CHUNK_START;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     a.cu = nullptr; a.H = H; a.total_T = T;
+    a.momentum = 0; a.beta = 0.f; a.mom0 = nullptr; a.mom_out = nullptr;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (p) {
     case TTT_PLAN_MFMA: return launch_status(launch_linear_mfma(a, s));
@@ -192,6 +193,39 @@ int ttt_linear_bwd(const void* K, const void* Q, const void* V,
     a.bf16 = io_dtype == TTT_DTYPE_BF16;
     a.workspace = workspace; a.workspace_bytes = workspace_bytes;
     return launch_status(launch_linear_bwd(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int ttt_linear_fwd_momentum(const void* K, const void* Q, const void* V,
+                            const float* eta, float eta_scalar, const float* W0,
+                            const float* Mom0, float beta,
+                            void* Z, float* W_out, float* Mom_out,
+                            int B, int H, int T, int d, int chunk, int io_dtype,
+                            void* workspace, size_t workspace_bytes, void* stream, int plan)
+{
+    if (!K || !Q || !V || !W0 || !Z || !W_out || !Mom_out) return TTT_ERR_INVALID_ARG;
+    if (!aligned(K, 16) || !aligned(Q, 16) || !aligned(V, 16) || !aligned(Z, 16) ||
+        !aligned(W0, 16) || !aligned(W_out, 16) || !aligned(Mom_out, 16) ||
+        (Mom0 && !aligned(Mom0, 16)))
+        return TTT_ERR_INVALID_ARG;
+    if (eta ? !aligned(eta, 4) : !std::isfinite(eta_scalar)) return TTT_ERR_INVALID_ARG;
+    if (!(beta >= 0.f && beta < 1.f)) return TTT_ERR_INVALID_ARG;
+    const int p = linear_plan(B, H, T, d, chunk, io_dtype, plan, TTT_READ_CHUNK_START);
+    if (p < 0) return p;
+    const size_t need = ttt_linear_workspace_bytes(B, H, T, d, chunk, io_dtype, p);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
+        return TTT_ERR_WORKSPACE;
+
+    LinearArgs a;
+    a.K = K; a.Q = Q; a.V = V; a.eta = eta; a.eta_scalar = eta_scalar; a.W0 = W0;
+    a.Z = Z; a.W_out = W_out; a.BH = B * H; a.T = T; a.d = d; a.chunk = chunk;
+    a.bf16 = io_dtype == TTT_DTYPE_BF16;
+    a.read_start = 1;
+    a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+    a.cu = nullptr; a.H = H; a.total_T = T;
+    a.momentum = 1; a.beta = beta; a.mom0 = Mom0; a.mom_out = Mom_out;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (p == TTT_PLAN_BIGCHUNK) return launch_status(launch_linear_bigchunk(a, s));
+    return launch_status(launch_linear_generic(a, s));
 }
 
 int ttt_linear_ln_fwd(const void* K, const void* Q, const void* V,
@@ -245,6 +279,7 @@ int ttt_linear_step(const void* K, const void* Q, const void* V,
     a.bf16 = io_dtype == TTT_DTYPE_BF16;
     a.read_start = 0;
     a.cu = nullptr; a.H = H; a.total_T = n;
+    a.momentum = 0; a.beta = 0.f; a.mom0 = nullptr; a.mom_out = nullptr;
     a.workspace = nullptr; a.workspace_bytes = 0;
     return launch_status(launch_linear_step(a, G, pos, reinterpret_cast<hipStream_t>(stream)));
 }
@@ -289,6 +324,7 @@ int ttt_linear_fwd_varlen(const void* K, const void* Q, const void* V,
     a.read_start = 0;
     a.workspace = nullptr; a.workspace_bytes = 0;
     a.cu = cu_seqlens; a.H = H; a.total_T = total_T;
+    a.momentum = 0; a.beta = 0.f; a.mom0 = nullptr; a.mom_out = nullptr;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (p == TTT_PLAN_MFMA) return launch_status(launch_linear_mfma(a, s));
     return launch_status(launch_linear_generic(a, s));

@@ -20,6 +20,12 @@ struct LinearArgs {
     int read_start;        // 1: every token reads with its chunk-start state
     void* workspace;
     size_t workspace_bytes;
+    // momentum state (chunk-start reads): M <- beta M + (1 - beta) grad_c,
+    // W <- W - M per chunk; mom0 may be null (zero)
+    int momentum;
+    float beta;
+    const float* mom0;     // [BH, d, d] or nullptr
+    float* mom_out;        // [BH, d, d]
     // packed documents: when cu is set, slice s = (document s / H, head s % H) reads
     // tokens [cu[doc], cu[doc + 1]) of head h's rows of [H, total_T, d] (clamped to
     // [0, total_T]); T is then unused

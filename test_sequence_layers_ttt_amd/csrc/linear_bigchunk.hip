@@ -170,10 +170,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void bigchunk_gram_kernel(
 // with P_c as the A operand (rows of P, 16-byte loads) and -W_c in bf16 as B.
 // The operands of the next two chunks are in flight while one is applied.
 // ---------------------------------------------------------------------------
-template <int D>
+//
+// With a momentum state (MOM) the chunk's negated gradient A = B_c^T - P_c W_c^T
+// feeds mom^T <- beta mom^T - (1 - beta) A and W_{c+1}^T = W_c^T - mom^T, the
+// momentum tiles kept in the state's layout.
+template <int D, bool MOM>
 __global__ __launch_bounds__(64) void bigchunk_chain_kernel(
     const float* W0, const uint16_t* __restrict__ P, const float* __restrict__ Bm,
-    float* __restrict__ Wc, float* W_out, int BH, int nchunks)
+    float* __restrict__ Wc, float* W_out, int BH, int nchunks, float beta,
+    const float* __restrict__ mom0, float* __restrict__ mom_out)
 {
     constexpr int NB = D / 16;
     constexpr int NM = D / 32;
@@ -184,13 +189,19 @@ __global__ __launch_bounds__(64) void bigchunk_chain_kernel(
     if (slice >= BH) return;
     const int out0 = 16 * ob;
 
-    f32x4 M[NB];
+    f32x4 M[NB], Mo[NB];
     {
         const float* w = W0 + (size_t)slice * D * D + (size_t)(out0 + c) * D;
+        const float* mo = mom0 ? mom0 + (size_t)slice * D * D + (size_t)(out0 + c) * D : nullptr;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
             M[2 * m] = *(const f32x4*)(w + 32 * m + 8 * g);
             M[2 * m + 1] = *(const f32x4*)(w + 32 * m + 8 * g + 4);
+            if constexpr (MOM) {
+                Mo[2 * m] = mo ? *(const f32x4*)(mo + 32 * m + 8 * g) : f32x4{0.f, 0.f, 0.f, 0.f};
+                Mo[2 * m + 1] =
+                    mo ? *(const f32x4*)(mo + 32 * m + 8 * g + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
     }
     // operands of chunk cc: rows pi(jb, c) of P_cc, and B_cc^T tiles
@@ -228,10 +239,18 @@ __global__ __launch_bounds__(64) void bigchunk_chain_kernel(
                     u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) {
-            f32x4 acc = M[jb] + bt[r][jb];
+            if constexpr (MOM) {
+                f32x4 acc = bt[r][jb];
 #pragma unroll
-            for (int m = 0; m < NM; ++m) acc = mfma32(pf[r][jb][m], Mn[m], acc);
-            M[jb] = acc;
+                for (int m = 0; m < NM; ++m) acc = mfma32(pf[r][jb][m], Mn[m], acc);
+                Mo[jb] = beta * Mo[jb] - (1.f - beta) * acc;
+                M[jb] -= Mo[jb];
+            } else {
+                f32x4 acc = M[jb] + bt[r][jb];
+#pragma unroll
+                for (int m = 0; m < NM; ++m) acc = mfma32(pf[r][jb][m], Mn[m], acc);
+                M[jb] = acc;
+            }
         }
         if (cc + 2 < nchunks) loadP(cc + 2, pf[r], bt[r]);
     };
@@ -246,6 +265,14 @@ __global__ __launch_bounds__(64) void bigchunk_chain_kernel(
     for (int m = 0; m < NM; ++m) {
         *(f32x4*)(w + 32 * m + 8 * g) = M[2 * m];
         *(f32x4*)(w + 32 * m + 8 * g + 4) = M[2 * m + 1];
+    }
+    if constexpr (MOM) {
+        float* mo = mom_out + (size_t)slice * D * D + (size_t)(out0 + c) * D;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            *(f32x4*)(mo + 32 * m + 8 * g) = Mo[2 * m];
+            *(f32x4*)(mo + 32 * m + 8 * g + 4) = Mo[2 * m + 1];
+        }
     }
 }
 
@@ -532,8 +559,14 @@ hipError_t launch_d(const LinearArgs& a, hipStream_t s)
     if (e != hipSuccess) return e;
 
     const int units = (a.BH + 7) / 8 * 8;
-    hipLaunchKernelGGL((bigchunk_chain_kernel<D>), dim3((unsigned)(units * (D / 16))), dim3(64), 0,
-                       s, a.W0, P, Bm, Wc, a.W_out, a.BH, nchunks);
+    if (a.momentum)
+        hipLaunchKernelGGL((bigchunk_chain_kernel<D, true>), dim3((unsigned)(units * (D / 16))),
+                           dim3(64), 0, s, a.W0, P, Bm, Wc, a.W_out, a.BH, nchunks, a.beta, a.mom0,
+                           a.mom_out);
+    else
+        hipLaunchKernelGGL((bigchunk_chain_kernel<D, false>), dim3((unsigned)(units * (D / 16))),
+                           dim3(64), 0, s, a.W0, P, Bm, Wc, a.W_out, a.BH, nchunks, 0.f, nullptr,
+                           nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 

@@ -15,7 +15,8 @@
 // M <- M - E_tau diag(eta) K_tau^T, and W_{c+1} = M at the chunk end.
 //
 // With the chunk-start read order every token of a chunk reads W_c: Z_tau = W_c Q_tau,
-// and the state moves exactly as above.
+// and the state moves exactly as above -- or, with a momentum state, through
+// mom <- beta mom + (1 - beta) (W_c - M), W_{c+1} = W_c - mom at each chunk end.
 //
 // Work split: one 256-thread workgroup per (batch*head, block of 16 output
 // rows).  Output row i of Z and of the state depends only on row i of W0 and
@@ -36,7 +37,8 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(
     const TIO* __restrict__ K, const TIO* __restrict__ Q, const TIO* __restrict__ V,
     const float* __restrict__ eta, float eta_scalar, const float* W0,
     TIO* __restrict__ Z, float* W_out, int T_all, int d, int chunk, int read_start,
-    const int* __restrict__ cu, int H, int total_T)
+    const int* __restrict__ cu, int H, int total_T, int momentum, float beta,
+    const float* __restrict__ mom0, float* __restrict__ mom_out)
 {
     __shared__ float sWs[kRows][kPad];   // chunk-start state rows
     __shared__ float sM[kRows][kPad];    // running state rows
@@ -46,6 +48,7 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(
     __shared__ float sE[kRows][kTile + 1];
     __shared__ float sS[kTile][kTile + 1];
     __shared__ float sEta[kTile];
+    __shared__ float sMom[kRows][kPad];  // momentum rows (momentum state only)
 
     const int tid = threadIdx.x;
     const int nrb = (d + kRows - 1) / kRows;
@@ -64,6 +67,8 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(
         float w = W0s[(size_t)(r0 + r) * d + j];
         sWs[r][j] = w;
         sM[r][j] = w;
+        if (momentum)
+            sMom[r][j] = mom0 ? mom0[(size_t)slice * d * d + (size_t)(r0 + r) * d + j] : 0.f;
     }
     __syncthreads();
 
@@ -160,9 +165,16 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(
             __syncthreads();
         }
         if (s0 + kTile >= c1) {
-            // chunk end: the running state becomes the next chunk-start state
+            // chunk end: the running state becomes the next chunk-start state.  With
+            // a momentum state the chunk's gradient g = W_c - M feeds
+            // mom <- beta mom + (1 - beta) g, and W_{c+1} = W_c - mom.
             for (int idx = tid; idx < R * d; idx += 256) {
                 int r = idx / d, j = idx % d;
+                if (momentum) {
+                    const float m = beta * sMom[r][j] + (1.f - beta) * (sWs[r][j] - sM[r][j]);
+                    sMom[r][j] = m;
+                    sM[r][j] = sWs[r][j] - m;
+                }
                 sWs[r][j] = sM[r][j];
             }
             __syncthreads();
@@ -174,6 +186,7 @@ __global__ __launch_bounds__(256) void linear_generic_kernel(
     for (int idx = tid; idx < R * d; idx += 256) {
         int r = idx / d, j = idx % d;
         Wos[(size_t)(r0 + r) * d + j] = sM[r][j];
+        if (momentum) mom_out[(size_t)slice * d * d + (size_t)(r0 + r) * d + j] = sMom[r][j];
     }
 }
 
@@ -187,12 +200,14 @@ hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s)
         hipLaunchKernelGGL(linear_generic_kernel<uint16_t>, grid, block, 0, s,
                            (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V,
                            a.eta, a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.T, a.d,
-                           a.chunk, a.read_start, a.cu, a.H, a.total_T);
+                           a.chunk, a.read_start, a.cu, a.H, a.total_T, a.momentum, a.beta,
+                           a.mom0, a.mom_out);
     } else {
         hipLaunchKernelGGL(linear_generic_kernel<float>, grid, block, 0, s,
                            (const float*)a.K, (const float*)a.Q, (const float*)a.V,
                            a.eta, a.eta_scalar, a.W0, (float*)a.Z, a.W_out, a.T, a.d,
-                           a.chunk, a.read_start, a.cu, a.H, a.total_T);
+                           a.chunk, a.read_start, a.cu, a.H, a.total_T, a.momentum, a.beta,
+                           a.mom0, a.mom_out);
     }
     return hipGetLastError();
 }

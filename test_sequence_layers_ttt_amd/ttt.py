@@ -23,6 +23,7 @@ EXPORTS = ("ttt_linear_workspace_bytes", "ttt_linear_select_plan", "ttt_linear_f
            "ttt_linear_step", "ttt_linear_bwd_workspace_bytes", "ttt_linear_bwd",
            "ttt_linear_fwd_ex", "ttt_linear_select_plan_ex",
            "ttt_linear_fwd_varlen", "ttt_linear_select_plan_varlen", "ttt_linear_ln_fwd",
+           "ttt_linear_fwd_momentum",
            "ttt_mlp_workspace_bytes", "ttt_mlp_select_plan", "ttt_mlp_fwd",
            "ttt_status_string", "ttt_plan_name")
 
@@ -54,6 +55,9 @@ def lib() -> ctypes.CDLL:
         L.ttt_linear_fwd_ex.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, i, i, i, i, i, i, vp, sz,
                                         vp, i, i]
         L.ttt_linear_fwd_ex.restype = i
+        L.ttt_linear_fwd_momentum.argtypes = [vp, vp, vp, vp, f, vp, vp, f, vp, vp, vp,
+                                              i, i, i, i, i, i, vp, sz, vp, i]
+        L.ttt_linear_fwd_momentum.restype = i
         L.ttt_linear_ln_fwd.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, vp, f, vp, vp, vp,
                                         i, i, i, i, i, i, vp]
         L.ttt_linear_ln_fwd.restype = i
@@ -263,6 +267,39 @@ def linear_step(K, Q, V, eta, W_chunk, G, pos: int, chunk: int, eta_scalar: floa
     if rc != OK:
         raise TTTError(rc, "ttt_linear_step")
     return Z, (int(pos) + n) % int(chunk)
+
+
+def linear_fwd_momentum(K, Q, V, eta, W0, Mom0, beta: float, chunk: int,
+                        eta_scalar: float = 0.0, *, Z=None, W_out=None, Mom_out=None,
+                        workspace=None, plan: int = PLAN_AUTO, stream=None) -> Tuple:
+    """TTT-Linear with a momentum state and chunk-start reads.  Mom0: [B, H, d, d]
+    fp32 or None (zero).  Returns (Z, W_out, Mom_out)."""
+    import torch
+    B, H, T, d = K.shape
+    _check(K, "K", (B, H, T, d))
+    _check(Q, "Q", (B, H, T, d), K.dtype)
+    _check(V, "V", (B, H, T, d), K.dtype)
+    _check(W0, "W0", (B, H, d, d), torch.float32)
+    if Mom0 is not None:
+        _check(Mom0, "Mom0", (B, H, d, d), torch.float32)
+    if eta is not None:
+        _check(eta, "eta", (B, H, T), torch.float32)
+    Z = torch.empty_like(K) if Z is None else Z
+    W_out = torch.empty_like(W0) if W_out is None else W_out
+    Mom_out = torch.empty_like(W0) if Mom_out is None else Mom_out
+    io = _io_dtype(K)
+    p = linear_select_plan(B, H, T, d, chunk, io, plan, READ_CHUNK_START)
+    nbytes = linear_workspace_bytes(B, H, T, d, chunk, io, p) if p > 0 else 0
+    ws = _workspace(nbytes, K.device, workspace)
+    rc = lib().ttt_linear_fwd_momentum(K.data_ptr(), Q.data_ptr(), V.data_ptr(), _ptr(eta),
+                                       float(eta_scalar), W0.data_ptr(), _ptr(Mom0), float(beta),
+                                       Z.data_ptr(), W_out.data_ptr(), Mom_out.data_ptr(),
+                                       B, H, T, d, int(chunk), io, _ptr(ws),
+                                       0 if ws is None else ws.numel(),
+                                       _stream(K.device, stream), int(plan))
+    if rc != OK:
+        raise TTTError(rc, "ttt_linear_fwd_momentum")
+    return Z, W_out, Mom_out
 
 
 def linear_ln_fwd(K, Q, V, eta, W0, b0, ln_weight, ln_bias, chunk: int, eps: float = 1e-6,

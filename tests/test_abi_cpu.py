@@ -294,6 +294,31 @@ def test_ln_rejects_bad_arguments(kw, status):
     assert _ln(**kw) == status
 
 
+def _mom(**kw):
+    a = dict(K=FAKE, Q=FAKE, V=FAKE, eta=None, eta_scalar=0.1, W0=FAKE, M0=None, beta=0.9,
+             Z=FAKE, W=FAKE, Mo=FAKE, B=1, H=2, T=40, d=64, chunk=16, io=1, ws=None, wsb=0,
+             stream=None, plan=0)
+    a.update(kw)
+    return ttt.lib().ttt_linear_fwd_momentum(a["K"], a["Q"], a["V"], a["eta"], a["eta_scalar"],
+                                             a["W0"], a["M0"], a["beta"], a["Z"], a["W"],
+                                             a["Mo"], a["B"], a["H"], a["T"], a["d"], a["chunk"],
+                                             a["io"], a["ws"], a["wsb"], a["stream"], a["plan"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Mo=None), ttt.ERR_INVALID_ARG),
+    (dict(M0=FAKE + 8), ttt.ERR_INVALID_ARG),
+    (dict(beta=1.0), ttt.ERR_INVALID_ARG),
+    (dict(beta=-0.1), ttt.ERR_INVALID_ARG),
+    (dict(beta=math.nan), ttt.ERR_INVALID_ARG),
+    (dict(plan=ttt.PLAN_MFMA), ttt.ERR_UNSUPPORTED),
+    (dict(d=40), ttt.ERR_UNSUPPORTED),
+    (dict(chunk=256, T=512, d=128), ttt.ERR_WORKSPACE),   # the large-chunk plan needs one
+])
+def test_momentum_rejects_bad_arguments(kw, status):
+    assert _mom(**kw) == status
+
+
 def test_plan_selection_and_workspace_are_host_only():
     assert ttt.linear_select_plan(1, 1, 256, 16, 16, ttt.DTYPE_F32) == ttt.PLAN_GENERIC
     assert ttt.linear_select_plan(1, 1, 256, 16, 16, 0, ttt.PLAN_GENERIC) == ttt.PLAN_GENERIC
