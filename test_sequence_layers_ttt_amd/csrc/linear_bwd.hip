@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
@@ -165,23 +166,73 @@ __device__ __forceinline__ void load_small(const TIO* p, float* out)
     }
 }
 
+// N consecutive elements of the I/O type kept as the raw 32-bit words a load
+// returns: widening to fp32 happens only when the words are consumed, so a load
+// issued a sub-tile ahead is not waited for (and, as stores share the same
+// counter, neither are the stores issued since).
+template <typename TIO, int N>
+struct RawRow {
+    static constexpr int BYTES = N * (int)sizeof(TIO);
+    static constexpr int WORDS = BYTES >= 4 ? BYTES / 4 : 1;
+    uint32_t w[WORDS];
+
+    __device__ __forceinline__ void load(const TIO* p)
+    {
+        if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+            for (int i = 0; i < WORDS; i += 4) {
+                const uint4 v = reinterpret_cast<const uint4*>(p)[i / 4];
+                w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+            }
+        } else if constexpr (BYTES == 8) {
+            const uint2 v = *reinterpret_cast<const uint2*>(p);
+            w[0] = v.x; w[1] = v.y;
+        } else if constexpr (BYTES == 4) {
+            w[0] = *reinterpret_cast<const uint32_t*>(p);
+        } else {
+            w[0] = *reinterpret_cast<const uint16_t*>(p);   // one bf16, zero-extended
+        }
+    }
+    __device__ __forceinline__ void zero()
+    {
+#pragma unroll
+        for (int i = 0; i < WORDS; ++i) w[i] = 0u;
+    }
+    __device__ __forceinline__ float at(int i) const
+    {
+        if constexpr (sizeof(TIO) == 4) {
+            return __uint_as_float(w[i]);
+        } else {
+            const uint32_t x = w[i >> 1];
+            return __uint_as_float((i & 1) ? (x & 0xffff0000u) : (x << 16));
+        }
+    }
+};
+
 // One sub-tile's inputs, loaded into registers one sub-tile ahead.  The 64*NW
 // threads share the K, Q (KP elements each) and V, dZ (VP elements each) tiles:
 // thread t takes row t / (4 NW); every lane holds eta of token l % 16, and each
 // wave the rows of its own column blocks of the chunk-start state (4 floats of
 // row l / 4 per block) when the sub-tile opens a chunk in the reverse pass.
-template <int D, int NW>
+template <typename TIO, int D, int NW>
 struct SubTile {
     static constexpr int KP = D / (4 * NW), VP = 4 / NW, NBW = D / 16 / NW;
-    float k[KP], q[KP], v[VP], dz[VP], w[NBW][4];
+    RawRow<TIO, KP> k, q;
+    RawRow<TIO, VP> v, dz;
+    RawRow<float, 4> w[NBW];
+    float h[NBW][4];   // CL tiles of the state after the chunk (chunks of several sub-tiles)
     float eta;
+    bool row_ok, eta_ok;   // rows and tokens past the sub-tile stage as zeros
 };
 
-template <typename TIO, int D>
+// MULTI: chunks span several 16-token sub-tiles (the running W - G_{<sigma} is
+// needed); a compile-time choice, so that chunks of at most 16 tokens carry no
+// trace of it.
+template <typename TIO, int D, bool MULTI>
 __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs a)
 {
     constexpr int NW = bwd_waves<D>(), NB = D / 16, NBW = NB / NW, S = D + 4;
-    constexpr int KP = SubTile<D, NW>::KP, VP = SubTile<D, NW>::VP;
+    constexpr int KP = SubTile<TIO, D, NW>::KP, VP = SubTile<TIO, D, NW>::VP;
     __shared__ BwdLds<D, NW> L;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -197,7 +248,6 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
     const int nch = (T + chunk - 1) / chunk;
     const int nsub = (chunk + kSub - 1) / kSub;            // sub-tiles of a full chunk
     const int last = (T - 1) / chunk * nsub + ((T - 1) % chunk) / kSub;   // last sub-tile
-    const bool multi = chunk > kSub;
     const TIO* Kg = static_cast<const TIO*>(a.K) + (size_t)slice * T * D;
     const TIO* Qg = static_cast<const TIO*>(a.Q) + (size_t)slice * T * D;
     const TIO* Vg = static_cast<const TIO*>(a.V) + (size_t)slice * T * D;
@@ -214,50 +264,55 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
         t0 = ch * chunk + si * kSub;
         len = min(kSub, min(ch * chunk + chunk, T) - t0);
     };
-    auto fetch = [&](SubTile<D, NW>& f, int j, bool rev, bool state) {
+    auto fetch = [&](SubTile<TIO, D, NW>& f, int j, bool rev, bool state) {
         int ch, si, t0, len;
         span(j, ch, si, t0, len);
-        if (srow < len) {
-            const size_t row = (size_t)(t0 + srow) * D;
-            load_vec<KP>(Kg + row + kcol, f.k);
-            load_small<VP>(Vg + row + r0 + vcol, f.v);
-            if (rev) {
-                load_vec<KP>(Qg + row + kcol, f.q);
-                load_small<VP>(dZg + row + r0 + vcol, f.dz);
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < KP; ++i) f.k[i] = f.q[i] = 0.f;
-#pragma unroll
-            for (int i = 0; i < VP; ++i) f.v[i] = f.dz[i] = 0.f;
+        // every load reads a row of the sub-tile (rows past its end re-read the
+        // last one), so no register is written on a divergent path
+        const size_t row = (size_t)(t0 + min(srow, len - 1)) * D;
+        f.row_ok = srow < len;
+        f.k.load(Kg + row + kcol);
+        f.v.load(Vg + row + r0 + vcol);
+        if (rev) {
+            f.q.load(Qg + row + kcol);
+            f.dz.load(dZg + row + r0 + vcol);
         }
-        f.eta = c < len ? (etag ? etag[t0 + c] : a.eta_scalar) : 0.f;
+        f.eta_ok = c < len;
+        f.eta = etag ? etag[t0 + min(c, len - 1)] : a.eta_scalar;
         if (state) {
             const float* src = states + (size_t)ch * D * D + (size_t)(r0 + wrow) * D + wcol;
 #pragma unroll
-            for (int bb = 0; bb < NBW; ++bb) load_vec<4>(src + 16 * blk(bb), f.w[bb]);
+            for (int bb = 0; bb < NBW; ++bb) f.w[bb].load(src + 16 * blk(bb));
+            if constexpr (MULTI) {
+                const float* hs = states + (size_t)(ch + 1) * D * D + (size_t)r0 * D;
+#pragma unroll
+                for (int bb = 0; bb < NBW; ++bb)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) f.h[bb][v] = hs[(4 * g + v) * D + 16 * blk(bb) + c];
+            }
         }
     };
-    auto put = [&](const SubTile<D, NW>& f, bool rev, bool state) {
+    auto put = [&](const SubTile<TIO, D, NW>& f, bool rev, bool state) {
+        const float ok = f.row_ok ? 1.f : 0.f;
 #pragma unroll
         for (int i = 0; i < KP; i += 4)
             *reinterpret_cast<f32x4*>(L.K + srow * S + kcol + i) =
-                f32x4{f.k[i], f.k[i + 1], f.k[i + 2], f.k[i + 3]};
+                f32x4{f.k.at(i), f.k.at(i + 1), f.k.at(i + 2), f.k.at(i + 3)} * ok;
 #pragma unroll
-        for (int i = 0; i < VP; ++i) L.V[srow * 20 + vcol + i] = f.v[i];
+        for (int i = 0; i < VP; ++i) L.V[srow * 20 + vcol + i] = f.v.at(i) * ok;
         if (rev) {
 #pragma unroll
             for (int i = 0; i < KP; i += 4)
                 *reinterpret_cast<f32x4*>(L.Q + srow * S + kcol + i) =
-                    f32x4{f.q[i], f.q[i + 1], f.q[i + 2], f.q[i + 3]};
+                    f32x4{f.q.at(i), f.q.at(i + 1), f.q.at(i + 2), f.q.at(i + 3)} * ok;
 #pragma unroll
-            for (int i = 0; i < VP; ++i) L.dZ[srow * 20 + vcol + i] = f.dz[i];
+            for (int i = 0; i < VP; ++i) L.dZ[srow * 20 + vcol + i] = f.dz.at(i) * ok;
         }
         if (state) {
 #pragma unroll
             for (int bb = 0; bb < NBW; ++bb)
                 *reinterpret_cast<f32x4*>(L.W + wrow * S + 16 * blk(bb) + wcol) =
-                    f32x4{f.w[bb][0], f.w[bb][1], f.w[bb][2], f.w[bb][3]};
+                    f32x4{f.w[bb].at(0), f.w[bb].at(1), f.w[bb].at(2), f.w[bb].at(3)};
         }
     };
     auto store_state = [&](int slot, const f32x4* Wr) {
@@ -275,7 +330,9 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
         return r;
     };
 
-    SubTile<D, NW> cur, nxt;
+    // two prefetch slots used alternately at compile-time positions: nothing is
+    // copied out of registers that loads may still be filling
+    SubTile<TIO, D, NW> bufs[2];
 
     // ------------------------------------------------ forward: chunk-start states
     f32x4 Wr[NBW];   // CL(W) of this wave's column blocks
@@ -284,8 +341,9 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
 #pragma unroll
         for (int v = 0; v < 4; ++v)
             Wr[bb][v] = a.W0[((size_t)slice * D + r0 + 4 * g + v) * D + 16 * blk(bb) + c];
-    fetch(cur, 0, false, false);
-    for (int j = 0; j <= last; ++j) {
+    auto fwd_step = [&](int j, auto slot) {
+        auto& cur = bufs[decltype(slot)::value];
+        auto& nxt = bufs[decltype(slot)::value ^ 1];
         int ch, si, t0, len;
         span(j, ch, si, t0, len);
         __syncthreads();   // the previous sub-tile's tiles are consumed
@@ -295,7 +353,7 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
             for (int bb = 0; bb < NBW; ++bb) put_cl<S>(L.W, 16 * blk(bb), lane, Wr[bb]);
         }
         put(cur, false, false);
-        const float et = cur.eta;
+        const float et = cur.eta_ok ? cur.eta : 0.f;
         __syncthreads();
         if (j < last) fetch(nxt, j + 1, false, false);
         // E = W K^T - V: this wave's part of the contraction over the state columns
@@ -316,9 +374,19 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
         const f32x4 Fa = rl<20>(L.F[wave], 0, lane);
 #pragma unroll
         for (int bb = 0; bb < NBW; ++bb) Wr[bb] = mm16(Fa, cl<S>(L.K, 16 * blk(bb), lane), Wr[bb]);
-        if (j < last) cur = nxt;
+    };
+    const std::integral_constant<int, 0> slot0;
+    const std::integral_constant<int, 1> slot1;
+    fetch(bufs[0], 0, false, false);
+    {
+        int j = 0;
+        for (; j + 1 <= last; j += 2) {
+            fwd_step(j, slot0);
+            fwd_step(j + 1, slot1);
+        }
+        if (j == last) fwd_step(j, slot0);
     }
-    if (multi) store_state(nch, Wr);
+    if constexpr (MULTI) store_state(nch, Wr);
     __threadfence();   // the states are read back below
     __syncthreads();
 
@@ -338,20 +406,22 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
         span(j, ch, si, t0, len);
         return j == last || si == nsub - 1;
     };
-    fetch(cur, last, true, true);
-    for (int j = last; j >= 0; --j) {
+    auto rev_step = [&](int j, auto slot) {
+        auto& cur = bufs[decltype(slot)::value];
+        auto& nxt = bufs[decltype(slot)::value ^ 1];
         int ch, si, t0, len;
         span(j, ch, si, t0, len);
         const bool first = opens(j);
         __syncthreads();   // the previous sub-tile's tiles are consumed
         put(cur, true, first);
-        const float et = cur.eta;
-        if (first && multi) {
-            const float* src = states + (size_t)(ch + 1) * D * D + (size_t)r0 * D;
+        const float et = cur.eta_ok ? cur.eta : 0.f;
+        if constexpr (MULTI) {
+            if (first) {
 #pragma unroll
-            for (int bb = 0; bb < NBW; ++bb)
+                for (int bb = 0; bb < NBW; ++bb)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) Hr[bb][v] = src[(4 * g + v) * D + 16 * blk(bb) + c];
+                    for (int v = 0; v < 4; ++v) Hr[bb][v] = cur.h[bb][v];
+            }
         }
 #pragma unroll
         for (int bb = 0; bb < NBW; ++bb) put_cl<S>(L.P, 16 * blk(bb), lane, P[bb]);
@@ -413,9 +483,9 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
         for (int v = 0; v < 4; ++v) dA[v] = (4 * g + v <= c) ? -dA[v] : 0.f;
         put_cl<20>(L.dA[wave], 0, lane, dA);
         put_cl<20>(L.dE[wave], 0, lane, dE);
-        if (multi) put_cl<20>(L.F[wave], 0, lane, F);
+        if constexpr (MULTI) put_cl<20>(L.F[wave], 0, lane, F);
         lds_order();
-        if (multi) {
+        if constexpr (MULTI) {
             // H = W - G_{<sigma}: add this sub-tile's update back
             const f32x4 Fa = rl<20>(L.F[wave], 0, lane);
 #pragma unroll
@@ -438,7 +508,9 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
             dK = mm16(dE, wc, dK);
             dK = mm16(dAa, qc, dK);
             // dQ (tokens x dims) = dZ^T H + dA^T K
-            f32x4 dQ = mm16(dZb, multi ? Hr[bb] : wc, f32x4{0.f, 0.f, 0.f, 0.f});
+            f32x4 dQ;
+            if constexpr (MULTI) dQ = mm16(dZb, Hr[bb], f32x4{0.f, 0.f, 0.f, 0.f});
+            else dQ = mm16(dZb, wc, f32x4{0.f, 0.f, 0.f, 0.f});
             dQ = mm16(dA, kc, dQ);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -459,7 +531,15 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
                 dWa[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
-        if (j > 0) cur = nxt;
+    };
+    fetch(bufs[0], last, true, true);
+    {
+        int j = last;
+        for (; j >= 1; j -= 2) {
+            rev_step(j, slot0);
+            rev_step(j - 1, slot1);
+        }
+        if (j == 0) rev_step(0, slot0);
     }
     float* dW0 = a.dW0 + ((size_t)slice * D + r0) * D;
 #pragma unroll
@@ -511,7 +591,12 @@ hipError_t launch_typed(const LinearBwdArgs& a, hipStream_t s)
     k.deta_part = reinterpret_cast<float*>(ws);
     k.BH = a.BH; k.T = a.T; k.chunk = a.chunk;
     const unsigned grid = (unsigned)(((a.BH + 7) / 8) * 8 * NB);
-    hipLaunchKernelGGL((linear_bwd_kernel<TIO, D>), dim3(grid), dim3(64 * bwd_waves<D>()), 0, s, k);
+    if (a.chunk > kSub)
+        hipLaunchKernelGGL((linear_bwd_kernel<TIO, D, true>), dim3(grid), dim3(64 * bwd_waves<D>()),
+                           0, s, k);
+    else
+        hipLaunchKernelGGL((linear_bwd_kernel<TIO, D, false>), dim3(grid),
+                           dim3(64 * bwd_waves<D>()), 0, s, k);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned rgrid = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
