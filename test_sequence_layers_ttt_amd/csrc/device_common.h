@@ -1,5 +1,5 @@
-// Device-side helpers shared by the TTT kernels: bf16 <-> fp32 conversion and
-// typed loads/stores of the I/O dtype.
+// Device-side helpers shared by the TTT kernels: bf16 <-> fp32 conversion,
+// typed loads/stores of the I/O dtype and raw-word prefetch registers.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -36,6 +36,44 @@ template <> struct io<uint16_t> {
     __device__ __forceinline__ static void store(uint16_t* p, size_t i, float v)
     {
         p[i] = f32_to_bf16_bits(v);
+    }
+};
+
+// N consecutive elements of the I/O type kept as the raw 32-bit words a load
+// returns: widening to fp32 happens only when the words are consumed, so a load
+// issued ahead of its use is not waited for at issue (and, as stores share the
+// same counter, neither are the stores issued since).
+template <typename TIO, int N>
+struct RawRow {
+    static constexpr int BYTES = N * (int)sizeof(TIO);
+    static constexpr int WORDS = BYTES >= 4 ? BYTES / 4 : 1;
+    uint32_t w[WORDS];
+
+    __device__ __forceinline__ void load(const TIO* p)
+    {
+        if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+            for (int i = 0; i < WORDS; i += 4) {
+                const uint4 v = reinterpret_cast<const uint4*>(p)[i / 4];
+                w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
+            }
+        } else if constexpr (BYTES == 8) {
+            const uint2 v = *reinterpret_cast<const uint2*>(p);
+            w[0] = v.x; w[1] = v.y;
+        } else if constexpr (BYTES == 4) {
+            w[0] = *reinterpret_cast<const uint32_t*>(p);
+        } else {
+            w[0] = *reinterpret_cast<const uint16_t*>(p);   // one bf16, zero-extended
+        }
+    }
+    __device__ __forceinline__ float at(int i) const
+    {
+        if constexpr (sizeof(TIO) == 4) {
+            return __uint_as_float(w[i]);
+        } else {
+            const uint32_t x = w[i >> 1];
+            return __uint_as_float((i & 1) ? (x & 0xffff0000u) : (x << 16));
+        }
     }
 };
 

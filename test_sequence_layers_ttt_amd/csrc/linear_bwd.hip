@@ -166,49 +166,6 @@ __device__ __forceinline__ void load_small(const TIO* p, float* out)
     }
 }
 
-// N consecutive elements of the I/O type kept as the raw 32-bit words a load
-// returns: widening to fp32 happens only when the words are consumed, so a load
-// issued a sub-tile ahead is not waited for (and, as stores share the same
-// counter, neither are the stores issued since).
-template <typename TIO, int N>
-struct RawRow {
-    static constexpr int BYTES = N * (int)sizeof(TIO);
-    static constexpr int WORDS = BYTES >= 4 ? BYTES / 4 : 1;
-    uint32_t w[WORDS];
-
-    __device__ __forceinline__ void load(const TIO* p)
-    {
-        if constexpr (BYTES % 16 == 0) {
-#pragma unroll
-            for (int i = 0; i < WORDS; i += 4) {
-                const uint4 v = reinterpret_cast<const uint4*>(p)[i / 4];
-                w[i] = v.x; w[i + 1] = v.y; w[i + 2] = v.z; w[i + 3] = v.w;
-            }
-        } else if constexpr (BYTES == 8) {
-            const uint2 v = *reinterpret_cast<const uint2*>(p);
-            w[0] = v.x; w[1] = v.y;
-        } else if constexpr (BYTES == 4) {
-            w[0] = *reinterpret_cast<const uint32_t*>(p);
-        } else {
-            w[0] = *reinterpret_cast<const uint16_t*>(p);   // one bf16, zero-extended
-        }
-    }
-    __device__ __forceinline__ void zero()
-    {
-#pragma unroll
-        for (int i = 0; i < WORDS; ++i) w[i] = 0u;
-    }
-    __device__ __forceinline__ float at(int i) const
-    {
-        if constexpr (sizeof(TIO) == 4) {
-            return __uint_as_float(w[i]);
-        } else {
-            const uint32_t x = w[i >> 1];
-            return __uint_as_float((i & 1) ? (x & 0xffff0000u) : (x << 16));
-        }
-    }
-};
-
 // One sub-tile's inputs, loaded into registers one sub-tile ahead.  The 64*NW
 // threads share the K, Q (KP elements each) and V, dZ (VP elements each) tiles:
 // thread t takes row t / (4 NW); every lane holds eta of token l % 16, and each
@@ -293,20 +250,23 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
         }
     };
     auto put = [&](const SubTile<TIO, D, NW>& f, bool rev, bool state) {
-        const float ok = f.row_ok ? 1.f : 0.f;
+        // a select, not a product: a re-read row may hold infinities
+        const bool ok = f.row_ok;
+        auto four = [&](const auto& r, int i) {
+            return ok ? f32x4{r.at(i), r.at(i + 1), r.at(i + 2), r.at(i + 3)}
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+        };
 #pragma unroll
         for (int i = 0; i < KP; i += 4)
-            *reinterpret_cast<f32x4*>(L.K + srow * S + kcol + i) =
-                f32x4{f.k.at(i), f.k.at(i + 1), f.k.at(i + 2), f.k.at(i + 3)} * ok;
+            *reinterpret_cast<f32x4*>(L.K + srow * S + kcol + i) = four(f.k, i);
 #pragma unroll
-        for (int i = 0; i < VP; ++i) L.V[srow * 20 + vcol + i] = f.v.at(i) * ok;
+        for (int i = 0; i < VP; ++i) L.V[srow * 20 + vcol + i] = ok ? f.v.at(i) : 0.f;
         if (rev) {
 #pragma unroll
             for (int i = 0; i < KP; i += 4)
-                *reinterpret_cast<f32x4*>(L.Q + srow * S + kcol + i) =
-                    f32x4{f.q.at(i), f.q.at(i + 1), f.q.at(i + 2), f.q.at(i + 3)} * ok;
+                *reinterpret_cast<f32x4*>(L.Q + srow * S + kcol + i) = four(f.q, i);
 #pragma unroll
-            for (int i = 0; i < VP; ++i) L.dZ[srow * 20 + vcol + i] = f.dz.at(i) * ok;
+            for (int i = 0; i < VP; ++i) L.dZ[srow * 20 + vcol + i] = ok ? f.dz.at(i) : 0.f;
         }
         if (state) {
 #pragma unroll

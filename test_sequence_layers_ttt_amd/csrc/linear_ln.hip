@@ -44,7 +44,8 @@ constexpr int ln_threads()
     return D == 128 ? 512 : 256;
 }
 
-template <typename TIO, int D>
+// ETA: per-token learning rates (else eta_scalar for every token)
+template <typename TIO, int D, bool ETA>
 __global__ __launch_bounds__(ln_threads<D>()) void linear_ln_kernel(
     const TIO* __restrict__ K, const TIO* __restrict__ Q, const TIO* __restrict__ V,
     const float* __restrict__ eta, float eta_scalar, const float* __restrict__ W0,
@@ -88,22 +89,20 @@ __global__ __launch_bounds__(ln_threads<D>()) void linear_ln_kernel(
         sbeta[i] = ln ? lnb[(size_t)h * D + i] : 0.f;
     }
 
-    // The next sub-tile's K, Q, V and eta are loaded into registers while the
-    // current one is computed (zeros past a chunk's last token).
-    float rk[PRE], rq[PRE], rv[PRE], re = 0.f;
+    // The next sub-tile's K, Q, V and eta are loaded into registers, as the
+    // loaded words, while the current one is computed.  Thread tid takes PRE
+    // consecutive features of token fs; tokens past the sub-tile's end re-read
+    // its last token and are staged as zeros, so every path issues the same
+    // loads and only the staging waits for them.
+    const int fs = tid * PRE / D, fj = tid * PRE % D;
+    RawRow<TIO, PRE> rk, rq, rv;
+    float re = eta_scalar;
     auto fetch = [&](int s0, int n) {
-#pragma unroll
-        for (int e = 0; e < PRE; ++e) {
-            const int idx = tid + NT * e, s = idx / D, j = idx % D;
-            rk[e] = rq[e] = rv[e] = 0.f;
-            if (s < n) {
-                const size_t off = (tok0 + s0 + s) * D + j;
-                rk[e] = io<TIO>::load(K, off);
-                rq[e] = io<TIO>::load(Q, off);
-                rv[e] = io<TIO>::load(V, off);
-            }
-        }
-        re = tid < n ? (eta ? eta[tok0 + s0 + tid] : eta_scalar) : 0.f;
+        const size_t off = (tok0 + s0 + min(fs, n - 1)) * D + fj;
+        rk.load(K + off);
+        rq.load(Q + off);
+        rv.load(V + off);
+        if constexpr (ETA) re = eta[tok0 + s0 + min(tid % kSub, n - 1)];
     };
     // sub-tile after the one at s0 (chunk starting at c0)
     auto next = [&](int c0, int s0, int& nc0, int& ns0) {
@@ -119,14 +118,16 @@ __global__ __launch_bounds__(ln_threads<D>()) void linear_ln_kernel(
             const int n = min(kSub, c1 - s0);
             __syncthreads();   // previous sub-tile done with the LDS tiles
             // ---- stage the prefetched K, Q, V and eta, then fetch the next ----
+            {
+                const bool ok = fs < n;
 #pragma unroll
-            for (int e = 0; e < PRE; ++e) {
-                const int idx = tid + NT * e, s = idx / D, j = idx % D;
-                sK[s][j] = rk[e];
-                sQ[s][j] = rq[e];
-                sV[s][j] = rv[e];
+                for (int i = 0; i < PRE; ++i) {
+                    sK[fs][fj + i] = ok ? rk.at(i) : 0.f;
+                    sQ[fs][fj + i] = ok ? rq.at(i) : 0.f;
+                    sV[fs][fj + i] = ok ? rv.at(i) : 0.f;
+                }
             }
-            if (tid < kSub) sEta[tid] = re;
+            if (tid < kSub) sEta[tid] = tid < n ? re : 0.f;
             {
                 int nc0, ns0;
                 next(c0, s0, nc0, ns0);
@@ -288,11 +289,15 @@ hipError_t launch_typed(const LinearLnArgs& a, hipStream_t s)
     const TIO* Q = static_cast<const TIO*>(a.Q);
     const TIO* V = static_cast<const TIO*>(a.V);
     TIO* Z = static_cast<TIO*>(a.Z);
-#define TTT_LN_LAUNCH(DD)                                                                       \
-    hipLaunchKernelGGL((linear_ln_kernel<TIO, DD>), grid, dim3(ln_threads<DD>()), 0, s, K, Q, \
-                       V, a.eta,                                                              \
-                       a.eta_scalar, a.W0, a.b0, a.ln_weight, a.ln_bias, a.eps, Z, a.W_out, \
-                       a.b_out, a.H, a.T, a.chunk)
+#define TTT_LN_LAUNCH(DD)                                                                      \
+    if (a.eta)                                                                                 \
+        hipLaunchKernelGGL((linear_ln_kernel<TIO, DD, true>), grid, dim3(ln_threads<DD>()), 0, \
+                           s, K, Q, V, a.eta, a.eta_scalar, a.W0, a.b0, a.ln_weight,            \
+                           a.ln_bias, a.eps, Z, a.W_out, a.b_out, a.H, a.T, a.chunk);           \
+    else                                                                                       \
+        hipLaunchKernelGGL((linear_ln_kernel<TIO, DD, false>), grid, dim3(ln_threads<DD>()),   \
+                           0, s, K, Q, V, a.eta, a.eta_scalar, a.W0, a.b0, a.ln_weight,         \
+                           a.ln_bias, a.eps, Z, a.W_out, a.b_out, a.H, a.T, a.chunk)
     switch (a.d) {
     case 16: TTT_LN_LAUNCH(16); break;
     case 32: TTT_LN_LAUNCH(32); break;

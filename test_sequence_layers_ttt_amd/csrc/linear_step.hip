@@ -15,6 +15,7 @@
 // inputs of the next few tokens are in flight while one is processed.
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 #include "device_common.h"
@@ -23,8 +24,8 @@
 namespace ttt {
 namespace {
 
-// n consecutive elements starting at p (aligned to their total size, up to 16
-// bytes), widened to fp32.
+// n consecutive fp32 elements starting at p (aligned to their total size, up to
+// 16 bytes)
 template <int N>
 __device__ __forceinline__ void load_row(const float* p, float (&out)[N])
 {
@@ -39,33 +40,6 @@ __device__ __forceinline__ void load_row(const float* p, float (&out)[N])
         out[0] = v.x; out[1] = v.y;
     } else {
         out[0] = *p;
-    }
-}
-
-template <int N>
-__device__ __forceinline__ void load_row(const uint16_t* p, float (&out)[N])
-{
-    // N bf16 values = N/2 dwords
-    if constexpr (N >= 8) {
-#pragma unroll
-        for (int i = 0; i < N; i += 8) {
-            const uint4 v = *reinterpret_cast<const uint4*>(p + i);
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                out[i + 2 * j] = __uint_as_float(w[j] << 16);
-                out[i + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-            }
-        }
-    } else if constexpr (N == 4) {
-        const uint2 v = *reinterpret_cast<const uint2*>(p);
-        out[0] = __uint_as_float(v.x << 16); out[1] = __uint_as_float(v.x & 0xffff0000u);
-        out[2] = __uint_as_float(v.y << 16); out[3] = __uint_as_float(v.y & 0xffff0000u);
-    } else if constexpr (N == 2) {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(p);
-        out[0] = __uint_as_float(v << 16); out[1] = __uint_as_float(v & 0xffff0000u);
-    } else {
-        out[0] = bf16_bits_to_f32(*p);
     }
 }
 
@@ -124,7 +98,8 @@ constexpr int kPrefetch = 4;
 // Lane (r, cg) of the workgroup holds state row 16*blockIdx + r, columns
 // [cg*C, cg*C + C), C = D/16: every state row is read and written as contiguous
 // 16-byte pieces and a key/query row as one contiguous segment per row group.
-template <typename TIO, int D>
+// ETA: per-token learning rates (else eta_scalar for every token).
+template <typename TIO, int D, bool ETA>
 __global__ __launch_bounds__(256) void linear_step_kernel(
     const TIO* __restrict__ K, const TIO* __restrict__ Q, const TIO* __restrict__ V,
     const float* __restrict__ eta, float eta_scalar, float* __restrict__ Wc,
@@ -143,60 +118,93 @@ __global__ __launch_bounds__(256) void linear_step_kernel(
     load_row(w, ws);
     load_row(gp, gg);
 
-    // inputs of the next kPrefetch tokens in a register ring (token t in slot
-    // t % kPrefetch; nothing is loaded past the last token)
-    float kr[kPrefetch][C], qr[kPrefetch][C], vr[kPrefetch], er[kPrefetch];
+    // Inputs of the next kPrefetch tokens in a register ring, token t in slot
+    // t % kPrefetch, kept as loaded words.  A slot is refilled right after its
+    // token is done.  Every path through the ring issues the same loads (a
+    // refill past the last token re-reads the last one), so the wait for a slot
+    // covers that slot's loads only, not the later loads and Z stores.
+    RawRow<TIO, C> kr[kPrefetch], qr[kPrefetch];
+    RawRow<TIO, 1> vr[kPrefetch];
+    float er[kPrefetch];
     auto load = [&](int t, auto slot) {
         constexpr int j = decltype(slot)::value;
-        if (t >= n) return;
         const size_t tok = tok0 + t;
-        load_row(K + tok * D + cg * C, kr[j]);
-        load_row(Q + tok * D + cg * C, qr[j]);
-        vr[j] = io<TIO>::load(V, tok * D + row);
-        er[j] = eta ? eta[tok] : eta_scalar;
+        kr[j].load(K + tok * D + cg * C);
+        qr[j].load(Q + tok * D + cg * C);
+        vr[j].load(V + tok * D + row);
+        if constexpr (ETA) er[j] = eta[tok];
+        else er[j] = eta_scalar;
     };
-    static_for<kPrefetch>([&](auto j) { load(decltype(j)::value, j); });
-
     int p = pos;
     bool folded = false;
-    for (int t0 = 0; t0 < n; t0 += kPrefetch) {
-        static_for<kPrefetch>([&](auto slot) {
-            constexpr int j = decltype(slot)::value;
-            const int t = t0 + j;
-            if (t >= n) return;
-            float k[C], q[C];
+    auto process = [&](int t, auto slot) {
+        constexpr int j = decltype(slot)::value;
+        // e = W_c k - v
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < C; ++i) s = fmaf(ws[i], kr[j].at(i), s);
+        const float e = row_sum16(s) - vr[j].at(0);
+        // G += eta e k^T;  z = (W_c - G) q
+        const float ee = er[j] * e;
+        float zs = 0.f;
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            gg[i] = fmaf(ee, kr[j].at(i), gg[i]);
+            zs = fmaf(ws[i] - gg[i], qr[j].at(i), zs);
+        }
+        const float z = row_sum16(zs);
+        if (cg == 0) io<TIO>::store(Z, (tok0 + t) * D + row, z);
+    };
+    // chunk complete: the updated state becomes the next chunk-start state
+    auto advance = [&]() {
+        if (++p == chunk) {
+            p = 0;
+            folded = true;
 #pragma unroll
             for (int i = 0; i < C; ++i) {
-                k[i] = kr[j][i];
-                q[i] = qr[j][i];
+                ws[i] -= gg[i];
+                gg[i] = 0.f;
             }
-            const float v = vr[j], et = er[j];
-            load(t + kPrefetch, slot);
-            // e = W_c k - v
-            float s = 0.f;
-#pragma unroll
-            for (int i = 0; i < C; ++i) s = fmaf(ws[i], k[i], s);
-            const float e = row_sum16(s) - v;
-            // G += eta e k^T;  z = (W_c - G) q
-            float zs = 0.f;
-#pragma unroll
-            for (int i = 0; i < C; ++i) {
-                gg[i] = fmaf(et * e, k[i], gg[i]);
-                zs = fmaf(ws[i] - gg[i], q[i], zs);
-            }
-            const float z = row_sum16(zs);
-            if (cg == 0) io<TIO>::store(Z, (tok0 + t) * D + row, z);
-            // chunk complete: the updated state becomes the next chunk-start state
-            if (++p == chunk) {
-                p = 0;
-                folded = true;
-#pragma unroll
-                for (int i = 0; i < C; ++i) {
-                    ws[i] -= gg[i];
-                    gg[i] = 0.f;
-                }
+        }
+    };
+    // token 0 (n >= 1) is fetched together with the state rows: a one-token
+    // call makes one memory round trip
+    const std::integral_constant<int, 0> slot0;
+    load(0, slot0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (n >= kPrefetch) {
+        // the other slots one by one, in the order the refills repeat (the
+        // scheduler would otherwise group the loads by tensor, and the first pass
+        // through the ring would then wait for every load of the ring at slot 0)
+        static_for<kPrefetch>([&](auto j) {
+            if constexpr (decltype(j)::value > 0) {
+                load(decltype(j)::value, j);
+                __builtin_amdgcn_sched_barrier(0);
             }
         });
+        int t0 = 0;
+        for (; t0 + kPrefetch <= n; t0 += kPrefetch) {
+            static_for<kPrefetch>([&](auto slot) {
+                const int t = t0 + decltype(slot)::value;
+                process(t, slot);
+                load(min(t + kPrefetch, n - 1), slot);
+                advance();
+            });
+        }
+        // the last n % kPrefetch tokens are already in slots 0, 1, ...
+        static_for<kPrefetch>([&](auto slot) {
+            const int t = t0 + decltype(slot)::value;
+            if (t < n) {
+                process(t, slot);
+                advance();
+            }
+        });
+    } else {
+        for (int t = 0; t < n; ++t) {
+            if (t > 0) load(t, slot0);
+            process(t, slot0);
+            advance();
+        }
     }
 
     // the chunk-start state changes only when a chunk completed in this call
@@ -204,32 +212,31 @@ __global__ __launch_bounds__(256) void linear_step_kernel(
     store_row(gp, gg);
 }
 
-template <typename TIO>
-hipError_t launch_typed(const LinearArgs& a, float* G, int pos, hipStream_t s)
+template <typename TIO, int D>
+void launch_d(const LinearArgs& a, float* G, int pos, hipStream_t s)
 {
-    dim3 grid((unsigned)(a.BH * (a.d / 16))), block(256);
+    dim3 grid((unsigned)(a.BH * (D / 16))), block(256);
     const TIO* K = (const TIO*)a.K;
     const TIO* Q = (const TIO*)a.Q;
     const TIO* V = (const TIO*)a.V;
     TIO* Z = (TIO*)a.Z;
     // the state is updated in place: W_out is the carried chunk-start state
+    if (a.eta)
+        hipLaunchKernelGGL((linear_step_kernel<TIO, D, true>), grid, block, 0, s, K, Q, V, a.eta,
+                           a.eta_scalar, a.W_out, G, Z, a.T, a.chunk, pos);
+    else
+        hipLaunchKernelGGL((linear_step_kernel<TIO, D, false>), grid, block, 0, s, K, Q, V,
+                           a.eta, a.eta_scalar, a.W_out, G, Z, a.T, a.chunk, pos);
+}
+
+template <typename TIO>
+hipError_t launch_typed(const LinearArgs& a, float* G, int pos, hipStream_t s)
+{
     switch (a.d) {
-    case 16:
-        hipLaunchKernelGGL((linear_step_kernel<TIO, 16>), grid, block, 0, s, K, Q, V, a.eta,
-                           a.eta_scalar, a.W_out, G, Z, a.T, a.chunk, pos);
-        break;
-    case 32:
-        hipLaunchKernelGGL((linear_step_kernel<TIO, 32>), grid, block, 0, s, K, Q, V, a.eta,
-                           a.eta_scalar, a.W_out, G, Z, a.T, a.chunk, pos);
-        break;
-    case 64:
-        hipLaunchKernelGGL((linear_step_kernel<TIO, 64>), grid, block, 0, s, K, Q, V, a.eta,
-                           a.eta_scalar, a.W_out, G, Z, a.T, a.chunk, pos);
-        break;
-    case 128:
-        hipLaunchKernelGGL((linear_step_kernel<TIO, 128>), grid, block, 0, s, K, Q, V, a.eta,
-                           a.eta_scalar, a.W_out, G, Z, a.T, a.chunk, pos);
-        break;
+    case 16: launch_d<TIO, 16>(a, G, pos, s); break;
+    case 32: launch_d<TIO, 32>(a, G, pos, s); break;
+    case 64: launch_d<TIO, 64>(a, G, pos, s); break;
+    case 128: launch_d<TIO, 128>(a, G, pos, s); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
