@@ -200,8 +200,8 @@ int ttt_linear_select_plan_varlen(int n_docs, int H, int total_T, int d, int chu
                                   int io_dtype, int plan);
 
 /* Bytes of workspace ttt_linear_bwd needs: the chunk-start states
- * (B*H*(ceil(T/chunk)+1)*d*d fp32) and per-16-row-block partial sums of dK, dQ
- * and deta.  0 for an unsupported shape. */
+ * (B*H*(ceil(T/chunk)+1)*d*d fp32) and, with bf16 I/O, fp32 sums of dK and dQ
+ * (2*B*H*T*d fp32).  0 for an unsupported shape. */
 size_t ttt_linear_bwd_workspace_bytes(int B, int H, int T, int d, int chunk, int io_dtype);
 
 /* Backward pass (vector-Jacobian product) of ttt_linear_fwd: for the scalar
@@ -221,8 +221,10 @@ size_t ttt_linear_bwd_workspace_bytes(int B, int H, int T, int d, int chunk, int
  *   d : 16, 32, 64 or 128;  chunk >= 1.
  *   workspace      : at least ttt_linear_bwd_workspace_bytes(...) bytes,
  *                    256-byte aligned.
- * Arithmetic is fp32 (inputs in bf16 are widened exactly).  Outputs must not
- * overlap inputs or each other. */
+ * Arithmetic is fp32 (inputs in bf16 are widened exactly).  dK, dQ and deta
+ * are sums over the state's 16-row blocks formed by atomic adds, so their
+ * last bits may differ between calls.  Outputs must not overlap inputs or each
+ * other. */
 int ttt_linear_bwd(const void* K, const void* Q, const void* V,
                    const float* eta, float eta_scalar, const float* W0,
                    const void* dZ, const float* dW_T,

@@ -163,7 +163,7 @@ size_t ttt_linear_bwd_workspace_bytes(int B, int H, int T, int d, int chunk, int
     if (!dims_ok(B, H, T, d, chunk)) return 0;
     if (io_dtype != TTT_DTYPE_F32 && io_dtype != TTT_DTYPE_BF16) return 0;
     if (d != 16 && d != 32 && d != 64 && d != 128) return 0;
-    return linear_bwd_workspace(B * H, T, d, chunk);
+    return linear_bwd_workspace(B * H, T, d, chunk, io_dtype == TTT_DTYPE_BF16);
 }
 
 int ttt_linear_bwd(const void* K, const void* Q, const void* V,
@@ -183,7 +183,7 @@ int ttt_linear_bwd(const void* K, const void* Q, const void* V,
     if (!dims_ok(B, H, T, d, chunk)) return TTT_ERR_INVALID_ARG;
     if (io_dtype != TTT_DTYPE_F32 && io_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARG;
     if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
-    const size_t need = linear_bwd_workspace(B * H, T, d, chunk);
+    const size_t need = linear_bwd_workspace(B * H, T, d, chunk, io_dtype == TTT_DTYPE_BF16);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return TTT_ERR_WORKSPACE;
 
     LinearBwdArgs a;

@@ -132,9 +132,10 @@ struct LinearBwdArgs {
 };
 
 // Backward pass of TTT-Linear (fp32 matrix cores), d in {16, 32, 64, 128}, any
-// chunk; the workspace holds the chunk-start states and the row-block partials.
+// chunk; the workspace holds the chunk-start states and, with bf16 I/O, the fp32
+// sums of dK and dQ.
 size_t linear_bwd_align(size_t bytes);
-size_t linear_bwd_workspace(int BH, int T, int d, int chunk);
+size_t linear_bwd_workspace(int BH, int T, int d, int chunk, bool bf16);
 hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s);
 
 // Streaming continuation from a carried (chunk-start state, in-chunk update) pair;

@@ -20,7 +20,8 @@
 // keeps its blocks of W, P, dW and H and computes its blocks of dK and dQ, and
 // the contractions over all columns (E, P K^T, K Q^T) are summed from per-wave
 // partial tiles in LDS.  Contributions to dK, dQ and deta (sums over the rows)
-// go to per-row-block partial buffers that a second kernel adds up.
+// are added by fp32 atomic adds into buffers cleared before the launch (the
+// outputs themselves with fp32 I/O; with bf16 I/O a last pass rounds the sums).
 //
 // All products run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32), operands
 // staged through LDS in row-major fp32 tiles with padded rows.  Register forms
@@ -148,9 +149,9 @@ struct BwdArgs {
     void* dV;
     float* dW0;
     float* states;        // [BH, nch + 1, d, d]
-    float* dK_part;       // [d/16, BH, T, d]
-    float* dQ_part;       // [d/16, BH, T, d]
-    float* deta_part;     // [d/16, BH, T]
+    float* dK_acc;        // [BH, T, d] fp32, zeroed before the launch
+    float* dQ_acc;        // [BH, T, d] fp32, zeroed before the launch
+    float* deta_acc;      // [BH, T] fp32, zeroed before the launch; may be null
     int BH, T, chunk;
 };
 
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
     const TIO* dZg = static_cast<const TIO*>(a.dZ) + (size_t)slice * T * D;
     const float* etag = a.eta ? a.eta + (size_t)slice * T : nullptr;
     float* states = a.states + (size_t)slice * (nch + 1) * D * D;
-    const size_t part = ((size_t)rb * a.BH + slice) * T;
+    const size_t tokb = (size_t)slice * T;   // the slice's first token
     auto blk = [&](int bb) { return wave + NW * bb; };   // column block of slot bb
 
     // sub-tile j: chunk j / nsub, tokens [t0, t0 + len)
@@ -430,7 +431,7 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
         de += __shfl_xor(de, 16);
         de += __shfl_xor(de, 32);
         if (wave == 0) {
-            if (g == 0 && c < len) a.deta_part[part + t0 + c] = de;
+            if (a.deta_acc && g == 0 && c < len) unsafeAtomicAdd(a.deta_acc + tokb + t0 + c, de);
             if (c < len) {
                 TIO* dv = static_cast<TIO*>(a.dV) + ((size_t)slice * T + t0 + c) * D + r0 + 4 * g;
 #pragma unroll
@@ -475,9 +476,9 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 if (4 * g + v < len) {
-                    const size_t o = (part + t0 + 4 * g + v) * D + 16 * b + c;
-                    a.dK_part[o] = dK[v];
-                    a.dQ_part[o] = dQ[v];
+                    const size_t o = (tokb + t0 + 4 * g + v) * D + 16 * b + c;
+                    unsafeAtomicAdd(a.dK_acc + o, dK[v]);
+                    unsafeAtomicAdd(a.dQ_acc + o, dQ[v]);
                 }
             }
             // P += dZ Q, dW += dE K
@@ -508,28 +509,43 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
         for (int v = 0; v < 4; ++v) dW0[(4 * g + v) * D + 16 * blk(bb) + c] = P[bb][v];
 }
 
-// dK, dQ = sum of the row blocks' partials (rounded to the I/O type), deta likewise
-template <typename TIO>
-__global__ __launch_bounds__(256) void linear_bwd_reduce_kernel(
-    const float* __restrict__ dK_part, const float* __restrict__ dQ_part,
-    const float* __restrict__ deta_part, TIO* __restrict__ dK, TIO* __restrict__ dQ,
-    float* __restrict__ deta, size_t n, size_t ntok, int nparts)
+// n floats set to zero: 16-byte stores (n a multiple of 4, p 16-byte aligned)
+// or, with VEC false, 4-byte ones
+template <bool VEC>
+__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, size_t n)
 {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        float k = 0.f, q = 0.f;
-        for (int p = 0; p < nparts; ++p) {
-            k += dK_part[(size_t)p * n + i];
-            q += dQ_part[(size_t)p * n + i];
-        }
-        io<TIO>::store(dK, i, k);
-        io<TIO>::store(dQ, i, q);
-        if (deta && i < ntok) {
-            float e = 0.f;
-            for (int p = 0; p < nparts; ++p) e += deta_part[(size_t)p * ntok + i];
-            deta[i] = e;
-        }
+    const size_t first = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if constexpr (VEC) {
+        for (size_t i = first; i < n / 4; i += stride)
+            reinterpret_cast<f32x4*>(p)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+        for (size_t i = first; i < n; i += stride) p[i] = 0.f;
     }
+}
+
+// the fp32 sums of dK and dQ rounded to bf16, four elements per thread
+__global__ __launch_bounds__(256) void round_bf16_kernel(const float* __restrict__ dK_acc,
+                                                         const float* __restrict__ dQ_acc,
+                                                         uint16_t* __restrict__ dK,
+                                                         uint16_t* __restrict__ dQ, size_t n)
+{
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    auto pack = [](f32x4 v) {
+        return uint2{f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
+                     f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16)};
+    };
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n / 4; i += stride) {
+        const f32x4 k = reinterpret_cast<const f32x4*>(dK_acc)[i];
+        const f32x4 q = reinterpret_cast<const f32x4*>(dQ_acc)[i];
+        reinterpret_cast<uint2*>(dK)[i] = pack(k);
+        reinterpret_cast<uint2*>(dQ)[i] = pack(q);
+    }
+}
+
+unsigned elementwise_grid(size_t n)
+{
+    return (unsigned)std::min<size_t>((n / 4 + 255) / 256, 4096);
 }
 
 template <typename TIO, int D>
@@ -544,12 +560,20 @@ hipError_t launch_typed(const LinearBwdArgs& a, hipStream_t s)
     k.W0 = a.W0; k.dZ = a.dZ; k.dWT = a.dW_T; k.dV = a.dV; k.dW0 = a.dW0;
     k.states = reinterpret_cast<float*>(ws);
     ws += linear_bwd_align((size_t)a.BH * (nch + 1) * D * D * sizeof(float));
-    k.dK_part = reinterpret_cast<float*>(ws);
-    ws += linear_bwd_align((size_t)NB * n * sizeof(float));
-    k.dQ_part = reinterpret_cast<float*>(ws);
-    ws += linear_bwd_align((size_t)NB * n * sizeof(float));
-    k.deta_part = reinterpret_cast<float*>(ws);
+    // dK, dQ and deta are sums over the d/16 row blocks, added into fp32 buffers
+    // by atomic adds (the outputs themselves with fp32 I/O; deta is fp32 always)
+    constexpr bool F32 = sizeof(TIO) == 4;
+    k.dK_acc = F32 ? static_cast<float*>(a.dK) : reinterpret_cast<float*>(ws);
+    ws += linear_bwd_align(n * sizeof(float));
+    k.dQ_acc = F32 ? static_cast<float*>(a.dQ) : reinterpret_cast<float*>(ws);
+    k.deta_acc = a.deta;
     k.BH = a.BH; k.T = a.T; k.chunk = a.chunk;
+    // (fill kernels rather than memsets, so that the call can be captured in a graph)
+    hipLaunchKernelGGL(zero_kernel<true>, dim3(elementwise_grid(n)), dim3(256), 0, s, k.dK_acc, n);
+    hipLaunchKernelGGL(zero_kernel<true>, dim3(elementwise_grid(n)), dim3(256), 0, s, k.dQ_acc, n);
+    if (a.deta)   // deta is only 4-byte aligned
+        hipLaunchKernelGGL(zero_kernel<false>, dim3(elementwise_grid(4 * ntok)), dim3(256), 0, s,
+                           a.deta, ntok);
     const unsigned grid = (unsigned)(((a.BH + 7) / 8) * 8 * NB);
     if (a.chunk > kSub)
         hipLaunchKernelGGL((linear_bwd_kernel<TIO, D, true>), dim3(grid), dim3(64 * bwd_waves<D>()),
@@ -557,12 +581,10 @@ hipError_t launch_typed(const LinearBwdArgs& a, hipStream_t s)
     else
         hipLaunchKernelGGL((linear_bwd_kernel<TIO, D, false>), dim3(grid),
                            dim3(64 * bwd_waves<D>()), 0, s, k);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const unsigned rgrid = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
-    hipLaunchKernelGGL(linear_bwd_reduce_kernel<TIO>, dim3(rgrid), dim3(256), 0, s,
-                       k.dK_part, k.dQ_part, k.deta_part, static_cast<TIO*>(a.dK),
-                       static_cast<TIO*>(a.dQ), a.deta, n, ntok, NB);
+    if constexpr (!F32)
+        hipLaunchKernelGGL(round_bf16_kernel, dim3(elementwise_grid(n)), dim3(256), 0, s,
+                           k.dK_acc, k.dQ_acc, static_cast<uint16_t*>(a.dK),
+                           static_cast<uint16_t*>(a.dQ), n);
     return hipGetLastError();
 }
 
@@ -582,13 +604,13 @@ hipError_t launch_dtype(const LinearBwdArgs& a, hipStream_t s)
 
 size_t linear_bwd_align(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
 
-size_t linear_bwd_workspace(int BH, int T, int d, int chunk)
+size_t linear_bwd_workspace(int BH, int T, int d, int chunk, bool bf16)
 {
     const size_t nch = (size_t)(T + chunk - 1) / chunk;
-    const size_t n = (size_t)BH * T * d, nb = (size_t)d / 16;
+    const size_t n = (size_t)BH * T * d;
+    // chunk-start states, then (bf16 I/O) the fp32 sums of dK and dQ
     return linear_bwd_align((size_t)BH * (nch + 1) * d * d * sizeof(float)) +
-           2 * linear_bwd_align(nb * n * sizeof(float)) +
-           linear_bwd_align(nb * (size_t)BH * T * sizeof(float));
+           (bf16 ? 2 * linear_bwd_align(n * sizeof(float)) : 0);
 }
 
 hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s)
