@@ -41,7 +41,16 @@
 #include "mfma_common.h"
 
 namespace ttt {
+
+// fp32 buffer atomic add (no-return form when the result is unused)
+__device__ float raw_buffer_atomic_fadd(float v, __amdgpu_buffer_rsrc_t rsrc, int voffset,
+                                        int soffset, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.atomic.fadd.f32");
+
 namespace {
+
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 constexpr int kSub = 16;   // tokens per sub-tile
 
@@ -90,6 +99,34 @@ __device__ __forceinline__ f32x4 mm16(f32x4 a, f32x4 b, f32x4 acc)
 }
 
 // ---------------------------------------------------------------- global I/O
+// Range-checked buffer accesses: a store or atomic add whose byte offset lies at
+// or past the resource's size is dropped by the memory unit.  Lanes outside a
+// sub-tile (or waves that must not write) point past the range instead of
+// branching, so every wave issues the same memory operations and a later wait
+// for prefetched loads need not cover them.
+constexpr int kBufferFlags = 0x00020000;   // dword 3 of a gfx9 buffer resource: raw 32-bit data
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_range(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes,
+                                            kBufferFlags);
+}
+
+// four consecutive values of the I/O type at byte offset `off`
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v,
+                                              float)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v,
+                                              uint16_t)
+{
+    const i32x2 w = {(int)(f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16)),
+                     (int)(f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16))};
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+}
+
 // N consecutive elements (N a multiple of 4) widened to fp32
 template <int N>
 __device__ __forceinline__ void load_vec(const float* p, float* out)
@@ -308,12 +345,14 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
         int ch, si, t0, len;
         span(j, ch, si, t0, len);
         __syncthreads();   // the previous sub-tile's tiles are consumed
+        put(cur, false, false);
+        // (after the staging, whose wait for the prefetched loads must not
+        // cover these stores)
         if (si == 0) {
             store_state(ch, Wr);
 #pragma unroll
             for (int bb = 0; bb < NBW; ++bb) put_cl<S>(L.W, 16 * blk(bb), lane, Wr[bb]);
         }
-        put(cur, false, false);
         const float et = cur.eta_ok ? cur.eta : 0.f;
         __syncthreads();
         if (j < last) fetch(nxt, j + 1, false, false);
@@ -427,16 +466,18 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
             de += E[v] * dF[v];
         }
         // deta: sum over the block's 16 rows (4 slots x 4 lane groups); every wave
-        // holds the same values, wave 0 writes them and dV
+        // holds the same values, wave 0's are written (with dV); token c of the
+        // sub-tile at byte 4c, dV row c at byte (c d + r0 + 4g) * size
         de += __shfl_xor(de, 16);
         de += __shfl_xor(de, 32);
-        if (wave == 0) {
-            if (a.deta_acc && g == 0 && c < len) unsafeAtomicAdd(a.deta_acc + tokb + t0 + c, de);
-            if (c < len) {
-                TIO* dv = static_cast<TIO*>(a.dV) + ((size_t)slice * T + t0 + c) * D + r0 + 4 * g;
-#pragma unroll
-                for (int v = 0; v < 4; ++v) io<TIO>::store(dv, v, -dE[v]);
-            }
+        {
+            const bool w0 = wave == 0;
+            const auto rde = buffer_range(a.deta_acc ? a.deta_acc + tokb + t0 : nullptr,
+                                          w0 && a.deta_acc ? 4u * len : 0u);
+            raw_buffer_atomic_fadd(de, rde, 4 * (g == 0 ? c : kSub), 0, 0);
+            const auto rdv = buffer_range(static_cast<TIO*>(a.dV) + (tokb + t0) * D,
+                                          w0 ? (uint32_t)(len * D * sizeof(TIO)) : 0u);
+            buffer_store4(rdv, (c * D + r0 + 4 * g) * (int)sizeof(TIO), -dE, TIO{});
         }
         // dA = -(F^T dZ) o U: A = RL(F^T) = CL(F) registers, B = CL(dZ_blk)
         f32x4 dA = mm16(F, dZb, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -458,6 +499,9 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
         f32x4 Fn;
 #pragma unroll
         for (int v = 0; v < 4; ++v) Fn[v] = -F[v];
+        const uint32_t tile_bytes = (uint32_t)(len * D * sizeof(float));
+        const auto rdk = buffer_range(a.dK_acc + (tokb + t0) * D, tile_bytes);
+        const auto rdq = buffer_range(a.dQ_acc + (tokb + t0) * D, tile_bytes);
 #pragma unroll
         for (int bb = 0; bb < NBW; ++bb) {
             const int b = blk(bb);
@@ -473,13 +517,12 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
             if constexpr (MULTI) dQ = mm16(dZb, Hr[bb], f32x4{0.f, 0.f, 0.f, 0.f});
             else dQ = mm16(dZb, wc, f32x4{0.f, 0.f, 0.f, 0.f});
             dQ = mm16(dA, kc, dQ);
+            // token 4g + v of the sub-tile, column 16b + c; rows past len dropped
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                if (4 * g + v < len) {
-                    const size_t o = (tokb + t0 + 4 * g + v) * D + 16 * b + c;
-                    unsafeAtomicAdd(a.dK_acc + o, dK[v]);
-                    unsafeAtomicAdd(a.dQ_acc + o, dQ[v]);
-                }
+                const int off = 4 * ((4 * g + v) * D + 16 * b + c);
+                raw_buffer_atomic_fadd(dK[v], rdk, off, 0, 0);
+                raw_buffer_atomic_fadd(dQ[v], rdq, off, 0, 0);
             }
             // P += dZ Q, dW += dE K
             P[bb] = mm16(dZa, qc, P[bb]);
