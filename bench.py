@@ -42,12 +42,13 @@ KERNEL_SOURCES = {"linear": ["linear_mfma.hip", "linear_coop.hip", "linear_gener
                   "mlp": ["mlp_mfma.hip", "mlp_generic.hip", "mfma_common.h", "device_common.h",
                           "launch.h", "api.cpp"],
                   "step": ["linear_step.hip", "device_common.h", "launch.h", "api.cpp"],
-                  "ln": ["linear_ln.hip", "device_common.h", "launch.h", "api.cpp"],
-                  "bwd": ["linear_bwd.hip", "mfma_common.h", "device_common.h", "launch.h",
-                          "api.cpp"]}
+                  "ln": ["linear_ln.hip", "mfma_f32.h", "mfma_common.h", "device_common.h",
+                         "launch.h", "api.cpp"],
+                  "bwd": ["linear_bwd.hip", "mfma_f32.h", "mfma_common.h", "device_common.h",
+                          "launch.h", "api.cpp"]}
 DECODE_METRIC = "TTT-Linear decode tokens/sec (all heads) + % of HBM roofline"
 BWD_METRIC = "TTT-Linear backward tokens/sec (all heads) + % of fp32 MFMA roofline"
-LN_METRIC = "TTT-Linear (bias, LayerNorm, residual) tokens/sec (all heads) + % of fp32 ALU roofline"
+LN_METRIC = "TTT-Linear (bias, LayerNorm, residual) tokens/sec (all heads) + % of fp32 MFMA roofline"
 FP32_PEAK_TFS = 157.3            # MI355X dense fp32 matrix
 
 
@@ -327,7 +328,7 @@ def ln_main(args, wl, x, seed):
         "config": {"workload": wl.name + "_ln", "scan": "ttt_linear_ln_fwd", "batch": B,
                    "heads": H, "seq_len": T, "head_dim": d, "chunk": wl.chunk, "io": wl.io,
                    "parallelism": "single_gpu"},
-        "roofline": {"bound": "alu", "achieved": round(tfs, 3), "peak": FP32_PEAK_TFS,
+        "roofline": {"bound": "mfma", "achieved": round(tfs, 3), "peak": FP32_PEAK_TFS,
                      "unit": "TFLOP/s", "frac": round(tfs / FP32_PEAK_TFS, 4), "traffic": None,
                      "kernel_ms": round(ms_event, 5), "algorithmic_flops": flops},
         "cpu_baseline": cpu,

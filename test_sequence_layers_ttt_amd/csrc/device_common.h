@@ -1,5 +1,6 @@
 // Device-side helpers shared by the TTT kernels: bf16 <-> fp32 conversion,
-// typed loads/stores of the I/O dtype and raw-word prefetch registers.
+// typed loads/stores of the I/O dtype, raw-word prefetch registers and 16-lane
+// row sums.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -76,5 +77,28 @@ struct RawRow {
         }
     }
 };
+
+// Sum over the 16 lanes of a DPP row (lanes 16m .. 16m+15); every lane of the row
+// receives the same sum, bit for bit (each lane adds the same pairs).  Swaps inside
+// each quad (lane ^ 1, lane ^ 2), then the half-row mirror (quad 0 <-> quad 1 of
+// each 8-lane half) and the row mirror (half 0 <-> half 1); no cross-row
+// movement, no LDS.
+__device__ __forceinline__ float dpp_add(float x, int y)
+{
+    return x + __int_as_float(y);
+}
+
+__device__ __forceinline__ float row_sum16(float x)
+{
+    constexpr int kQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
+    constexpr int kQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
+    constexpr int kRowHalfMirror = 0x141;
+    constexpr int kRowMirror = 0x140;
+    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kQuadXor1, 0xF, 0xF, false));
+    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kQuadXor2, 0xF, 0xF, false));
+    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kRowHalfMirror, 0xF, 0xF, false));
+    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kRowMirror, 0xF, 0xF, false));
+    return x;
+}
 
 }  // namespace ttt

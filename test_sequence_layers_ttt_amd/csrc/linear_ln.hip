@@ -13,272 +13,283 @@
 // in 16-token sub-tiles with M, b_m the running state (= W_c, b_c at a chunk
 // start); the "+1" carries the bias through the same causal products.
 //
-// LN needs all d features of a token, so one workgroup (256 threads, 512 at
-// d = 128) owns a whole (batch, head) state, fp32 on the vector ALUs.  Thread
-// (row i, part p) holds columns [p*C, (p+1)*C) of row i of W_c and M
-// (C = d*d/threads); row sums are butterfly reductions over the threads of a
-// row, and per-token statistics reductions over threads/16 lanes.
+// LN needs all d features of a token, so one workgroup owns a whole (batch,
+// head): d/16 waves, wave w holding state rows 16w .. 16w+15 (of W_c and M, all
+// columns, in registers).  Every product runs on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32, so results keep fp32 accuracy), in the transposed
+// orientation that leaves the state's rows in the lanes (see mfma_f32.h):
+//   U^T = K W_c^T,  P^T = Q M^T,  S = K Q^T,  Zpre^T = P^T - S^T (G diag(eta))^T,
+//   M^T <- M^T - K^T (G diag(eta))^T,
+// so that U, G, P and Zpre all sit as "lane = state row r0 + c, slots = tokens
+// 4g .. 4g+3" and the state update lands in the layout the products read.  A
+// token's LayerNorm statistics are 16-lane DPP sums inside each wave, combined
+// across the waves through LDS ((mean, M2) pairs merged by the parallel-variance
+// formula, so each statistic costs one barrier).  The next sub-tile's K, Q, V
+// and eta are loaded as raw words while the current one is computed.
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
+#include "mfma_f32.h"
 
 namespace ttt {
 namespace {
 
 constexpr int kSub = 16;
+constexpr int kBufferFlags = 0x00020000;   // dword 3 of a gfx9 buffer resource: raw 32-bit data
 
-// sum over the N consecutive lanes of a group (N a power of two <= 32); every
-// lane of the group receives the sum
-template <int N>
-__device__ __forceinline__ float group_sum(float x)
-{
-#pragma unroll
-    for (int o = N / 2; o >= 1; o /= 2) x += __shfl_xor(x, o, N);
-    return x;
-}
+// One sub-tile's inputs as loaded: thread t holds 4 consecutive features of one
+// token of K, Q and V, and eta of token t % 16.
+template <typename TIO>
+struct LnTile {
+    RawRow<TIO, 4> k, q, v;
+    float eta;
+};
 
 template <int D>
-constexpr int ln_threads()
+struct LnLds {
+    static constexpr int S = D + 4;   // row stride of the token x feature tiles
+    float K[kSub * S];
+    float Q[kSub * S];
+    float V[kSub * S];
+    float eta[kSub];
+    // per-wave partial statistics of each token: (mean, M2) of U, (sum g, sum g
+    // u-hat) for the LN backward, (mean, M2) of Zpre
+    f32x2 stat[3][D / 16][kSub];
+};
+
+// one element of the I/O type at byte offset `off` of a range-checked buffer
+// (an offset at or past the range's end is dropped by the memory unit)
+__device__ __forceinline__ void buffer_store1(__amdgpu_buffer_rsrc_t r, int off, float v, float)
 {
-    return D == 128 ? 512 : 256;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(v), r, off, 0, 0);
+}
+
+__device__ __forceinline__ void buffer_store1(__amdgpu_buffer_rsrc_t r, int off, float v,
+                                              uint16_t)
+{
+    __builtin_amdgcn_raw_buffer_store_b16((short)f32_to_bf16_bits(v), r, off, 0, 0);
 }
 
 // ETA: per-token learning rates (else eta_scalar for every token)
 template <typename TIO, int D, bool ETA>
-__global__ __launch_bounds__(ln_threads<D>()) void linear_ln_kernel(
+__global__ __launch_bounds__(4 * D) void linear_ln_kernel(
     const TIO* __restrict__ K, const TIO* __restrict__ Q, const TIO* __restrict__ V,
     const float* __restrict__ eta, float eta_scalar, const float* __restrict__ W0,
     const float* __restrict__ b0, const float* __restrict__ lnw, const float* __restrict__ lnb,
     float eps, TIO* __restrict__ Z, float* __restrict__ W_out, float* __restrict__ b_out,
     int H, int T, int chunk)
 {
-    constexpr int NT = ln_threads<D>();
-    constexpr int TPR = NT / D;           // threads per state row
-    constexpr int C = D / TPR;            // columns per thread
-    constexpr int SP = D + 4;             // LDS row pitch: 16-byte rows, columns on distinct banks
-    constexpr int PRE = kSub * D / NT;    // elements of each staged tile per thread
-    constexpr int LPT = NT / kSub;        // lanes per token in the per-token layout
-    constexpr int FPL = D / LPT;          // features per lane there
-    __shared__ __align__(16) float sK[kSub][SP];
-    __shared__ __align__(16) float sQ[kSub][SP];
-    __shared__ __align__(16) float sV[kSub][SP];
-    __shared__ float sU[kSub][SP];        // U, then G             [token][feature]
-    __shared__ float sP[kSub][SP];        // M Q + b_m, then Zpre  [token][feature]
-    __shared__ float sS[kSub][kSub + 1];  // k_s . q_t + 1 for s <= t, else 0
-    __shared__ float sEta[kSub];
-    __shared__ float sbc[D], sbm[D], sw[D], sbeta[D];
+    constexpr int NW = D / 16, NB = D / 16, S = LnLds<D>::S;
+    __shared__ __align__(16) LnLds<D> L;
 
     const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, c = lane & 15, g = lane >> 4;
+    const int r0 = 16 * wave;   // this wave's state rows
     const int slice = blockIdx.x;
-    const int row = tid / TPR, part = tid % TPR, col0 = part * C;
-    const int tt = tid / LPT, l16 = tid % LPT;   // per-token layout: token tt, lane l16
-    const bool ln = lnw != nullptr;
-    const size_t tok0 = (size_t)slice * T;
     const int h = slice % H;
+    const size_t tok0 = (size_t)slice * T;
+    const bool ln = lnw != nullptr;
+    const int fs = tid / (D / 4), fj = (tid % (D / 4)) * 4;   // staged token and features
 
-    float wc[C], wm[C];
+    // state rows r0 + c, columns 16b + 4g .. 16b + 4g + 3 of block b (RL form)
+    f32x4 Wc[NB], M[NB];
     {
-        const float* w = W0 + ((size_t)slice * D + row) * D + col0;
+        const float* w = W0 + ((size_t)slice * D + r0 + c) * D + 4 * g;
 #pragma unroll
-        for (int j = 0; j < C; ++j) wc[j] = wm[j] = w[j];
+        for (int b = 0; b < NB; ++b) Wc[b] = M[b] = *reinterpret_cast<const f32x4*>(w + 16 * b);
     }
-    for (int i = tid; i < D; i += NT) {
-        sbc[i] = sbm[i] = b0[(size_t)slice * D + i];
-        sw[i] = ln ? lnw[(size_t)h * D + i] : 0.f;
-        sbeta[i] = ln ? lnb[(size_t)h * D + i] : 0.f;
-    }
+    float bc = b0[(size_t)slice * D + r0 + c], bm = bc;
+    const float lw = ln ? lnw[(size_t)h * D + r0 + c] : 0.f;
+    const float lb = ln ? lnb[(size_t)h * D + r0 + c] : 0.f;
 
-    // The next sub-tile's K, Q, V and eta are loaded into registers, as the
-    // loaded words, while the current one is computed.  Thread tid takes PRE
-    // consecutive features of token fs; tokens past the sub-tile's end re-read
-    // its last token and are staged as zeros, so every path issues the same
-    // loads and only the staging waits for them.
-    const int fs = tid * PRE / D, fj = tid * PRE % D;
-    RawRow<TIO, PRE> rk, rq, rv;
-    float re = eta_scalar;
-    auto fetch = [&](int s0, int n) {
-        const size_t off = (tok0 + s0 + min(fs, n - 1)) * D + fj;
-        rk.load(K + off);
-        rq.load(Q + off);
-        rv.load(V + off);
-        if constexpr (ETA) re = eta[tok0 + s0 + min(tid % kSub, n - 1)];
+    const int nsub = (chunk + kSub - 1) / kSub;   // sub-tiles of a full chunk
+    const int last = (T - 1) / chunk * nsub + ((T - 1) % chunk) / kSub;
+    // sub-tile j: position si in its chunk, tokens [t0, t0 + len)
+    auto span = [&](int j, int& si, int& t0, int& len) {
+        const int ch = j / nsub;
+        si = j - ch * nsub;
+        t0 = ch * chunk + si * kSub;
+        len = min(kSub, min(ch * chunk + chunk, T) - t0);
     };
-    // sub-tile after the one at s0 (chunk starting at c0)
-    auto next = [&](int c0, int s0, int& nc0, int& ns0) {
-        const int c1 = min(T, c0 + chunk);
-        if (s0 + kSub < c1) { nc0 = c0; ns0 = s0 + kSub; }
-        else { nc0 = c1; ns0 = c1; }
+    // every load reads a token of the sub-tile (tokens past its end re-read the
+    // last one), so every path issues the same loads
+    auto fetch = [&](LnTile<TIO>& f, int j) {
+        int si, t0, len;
+        span(j, si, t0, len);
+        const size_t off = (tok0 + t0 + min(fs, len - 1)) * D + fj;
+        f.k.load(K + off);
+        f.q.load(Q + off);
+        f.v.load(V + off);
+        if constexpr (ETA) f.eta = eta[tok0 + t0 + min(c, len - 1)];
+        else f.eta = eta_scalar;
     };
-    fetch(0, min(kSub, min(T, chunk)));
-
-    for (int c0 = 0; c0 < T; c0 += chunk) {
-        const int c1 = min(T, c0 + chunk);
-        for (int s0 = c0; s0 < c1; s0 += kSub) {
-            const int n = min(kSub, c1 - s0);
-            __syncthreads();   // previous sub-tile done with the LDS tiles
-            // ---- stage the prefetched K, Q, V and eta, then fetch the next ----
-            {
-                const bool ok = fs < n;
+    auto put = [&](const LnTile<TIO>& f, int len) {
+        const bool ok = fs < len;   // tokens past the sub-tile's end stage as zeros
+        auto four = [&](const RawRow<TIO, 4>& r) {
+            return ok ? f32x4{r.at(0), r.at(1), r.at(2), r.at(3)} : f32x4{0.f, 0.f, 0.f, 0.f};
+        };
+        *reinterpret_cast<f32x4*>(L.K + fs * S + fj) = four(f.k);
+        *reinterpret_cast<f32x4*>(L.Q + fs * S + fj) = four(f.q);
+        *reinterpret_cast<f32x4*>(L.V + fs * S + fj) = four(f.v);
+        if (tid < kSub) L.eta[tid] = tid < len ? f.eta : 0.f;
+    };
+    // mean and 1/sqrt(var + eps) over the d features of tokens 4g + v, from this
+    // wave's 16 rows (lanes c) and the other waves' partials
+    auto ln_stats = [&](f32x4 x, int k, f32x4& mean, f32x4& rstd) {
 #pragma unroll
-                for (int i = 0; i < PRE; ++i) {
-                    sK[fs][fj + i] = ok ? rk.at(i) : 0.f;
-                    sQ[fs][fj + i] = ok ? rq.at(i) : 0.f;
-                    sV[fs][fj + i] = ok ? rv.at(i) : 0.f;
-                }
-            }
-            if (tid < kSub) sEta[tid] = tid < n ? re : 0.f;
-            {
-                int nc0, ns0;
-                next(c0, s0, nc0, ns0);
-                if (ns0 < T) fetch(ns0, min(kSub, min(T, nc0 + chunk) - ns0));
-            }
-            __syncthreads();
-            // ---- U = W_c K + b_c and P = M Q + b_m (row sums over the row's threads) ----
-#pragma unroll 2
-            for (int s = 0; s < kSub; ++s) {
-                float u = 0.f, p = 0.f;
-                if constexpr (C % 4 == 0) {
-#pragma unroll
-                    for (int j = 0; j < C; j += 4) {
-                        const float4 k4 = *reinterpret_cast<const float4*>(&sK[s][col0 + j]);
-                        const float4 q4 = *reinterpret_cast<const float4*>(&sQ[s][col0 + j]);
-                        u = fmaf(wc[j], k4.x, u); u = fmaf(wc[j + 1], k4.y, u);
-                        u = fmaf(wc[j + 2], k4.z, u); u = fmaf(wc[j + 3], k4.w, u);
-                        p = fmaf(wm[j], q4.x, p); p = fmaf(wm[j + 1], q4.y, p);
-                        p = fmaf(wm[j + 2], q4.z, p); p = fmaf(wm[j + 3], q4.w, p);
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < C; ++j) {
-                        u = fmaf(wc[j], sK[s][col0 + j], u);
-                        p = fmaf(wm[j], sQ[s][col0 + j], p);
-                    }
-                }
-                u = group_sum<TPR>(u);
-                p = group_sum<TPR>(p);
-                if (part == 0) {
-                    sU[s][row] = u + sbc[row];
-                    sP[s][row] = p + sbm[row];
-                }
-            }
-            // ---- causal scores (with the bias's +1) ----
-            if (tid < kSub * kSub) {
-                const int s = tid >> 4, t = tid & 15;
-                float acc = 0.f;
-                if (s <= t && t < n) {
-                    for (int j = 0; j < D; ++j) acc = fmaf(sK[s][j], sQ[t][j], acc);
-                    acc += 1.f;
-                }
-                sS[s][t] = acc;
-            }
-            __syncthreads();
-            // ---- G = dl/dU per token (token tt, features l16 + 16 m) ----
-            {
-                float u[FPL], g[FPL];
-                float mu = 0.f, var = 0.f;
-#pragma unroll
-                for (int m = 0; m < FPL; ++m) u[m] = sU[tt][l16 + LPT * m];
-                if (ln) {
-#pragma unroll
-                    for (int m = 0; m < FPL; ++m) mu += u[m];
-                    mu = group_sum<LPT>(mu) / D;
-#pragma unroll
-                    for (int m = 0; m < FPL; ++m) var += (u[m] - mu) * (u[m] - mu);
-                    var = group_sum<LPT>(var) / D;
-                    const float rs = rsqrtf(var + eps);
-                    float mh = 0.f, mhu = 0.f;
-#pragma unroll
-                    for (int m = 0; m < FPL; ++m) {
-                        const int i = l16 + LPT * m;
-                        const float uh = (u[m] - mu) * rs;
-                        const float r = sK[tt][i] + sw[i] * uh + sbeta[i] - sV[tt][i];
-                        g[m] = sw[i] * r;
-                        mh += g[m];
-                        mhu += g[m] * uh;
-                        u[m] = uh;
-                    }
-                    mh = group_sum<LPT>(mh) / D;
-                    mhu = group_sum<LPT>(mhu) / D;
-#pragma unroll
-                    for (int m = 0; m < FPL; ++m) g[m] = rs * (g[m] - mh - u[m] * mhu);
-                } else {
-#pragma unroll
-                    for (int m = 0; m < FPL; ++m) g[m] = u[m] - sV[tt][l16 + LPT * m];
-                }
-                __syncthreads();   // every lane has read U
-#pragma unroll
-                for (int m = 0; m < FPL; ++m) sU[tt][l16 + LPT * m] = tt < n ? g[m] : 0.f;
-            }
-            __syncthreads();
-            // ---- Zpre = P - G diag(eta) S, then Z = Q + LN(Zpre) (token tt) ----
-            {
-                float zp[FPL];
-                float mu = 0.f, var = 0.f;
-#pragma unroll
-                for (int m = 0; m < FPL; ++m) {
-                    const int i = l16 + LPT * m;
-                    float acc = sP[tt][i];
-                    for (int s = 0; s <= tt; ++s) acc = fmaf(-sEta[s] * sS[s][tt], sU[s][i], acc);
-                    zp[m] = acc;
-                    mu += acc;
-                }
-                if (ln) {
-                    mu = group_sum<LPT>(mu) / D;
-#pragma unroll
-                    for (int m = 0; m < FPL; ++m) var += (zp[m] - mu) * (zp[m] - mu);
-                    var = group_sum<LPT>(var) / D;
-                    const float rs = rsqrtf(var + eps);
-#pragma unroll
-                    for (int m = 0; m < FPL; ++m) {
-                        const int i = l16 + LPT * m;
-                        zp[m] = sQ[tt][i] + sw[i] * ((zp[m] - mu) * rs) + sbeta[i];
-                    }
-                }
-                if (tt < n) {
-#pragma unroll
-                    for (int m = 0; m < FPL; ++m)
-                        io<TIO>::store(Z, (tok0 + s0 + tt) * D + l16 + LPT * m, zp[m]);
-                }
-            }
-            // ---- M -= G diag(eta) K^T, b_m -= G eta ----
-#pragma unroll 2
-            for (int s = 0; s < kSub; ++s) {
-                const float f = sEta[s] * sU[s][row];
-                if constexpr (C % 4 == 0) {
-#pragma unroll
-                    for (int j = 0; j < C; j += 4) {
-                        const float4 k4 = *reinterpret_cast<const float4*>(&sK[s][col0 + j]);
-                        wm[j] = fmaf(-f, k4.x, wm[j]);
-                        wm[j + 1] = fmaf(-f, k4.y, wm[j + 1]);
-                        wm[j + 2] = fmaf(-f, k4.z, wm[j + 2]);
-                        wm[j + 3] = fmaf(-f, k4.w, wm[j + 3]);
-                    }
-                } else {
-#pragma unroll
-                    for (int j = 0; j < C; ++j) wm[j] = fmaf(-f, sK[s][col0 + j], wm[j]);
-                }
-            }
-            __syncthreads();   // every lane has read b_m through sP's producers
-            if (part == 0) {
-                float acc = 0.f;
-                for (int s = 0; s < kSub; ++s) acc = fmaf(sEta[s], sU[s][row], acc);
-                sbm[row] -= acc;
-            }
+        for (int v = 0; v < 4; ++v) {
+            const float mw = row_sum16(x[v]) * (1.f / 16.f);
+            const float dv = x[v] - mw;
+            const float m2 = row_sum16(dv * dv);
+            if (c == 0) L.stat[k][wave][4 * g + v] = f32x2{mw, m2};
         }
-        // chunk end: the running state becomes the next chunk-start state
-#pragma unroll
-        for (int j = 0; j < C; ++j) wc[j] = wm[j];
         __syncthreads();
-        for (int i = tid; i < D; i += NT) sbc[i] = sbm[i];
-    }
-    __syncthreads();
-    {
-        float* w = W_out + ((size_t)slice * D + row) * D + col0;
 #pragma unroll
-        for (int j = 0; j < C; ++j) w[j] = wm[j];
+        for (int v = 0; v < 4; ++v) {
+            float ms = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) ms += L.stat[k][w][4 * g + v].x;
+            const float mu = ms * (1.f / NW);
+            float m2 = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const f32x2 p = L.stat[k][w][4 * g + v];
+                const float dm = p.x - mu;
+                m2 += p.y + 16.f * dm * dm;
+            }
+            mean[v] = mu;
+            rstd[v] = rsqrtf(m2 * (1.f / D) + eps);
+        }
+    };
+    // sums over the d features of tokens 4g + v of two quantities
+    auto feature_sums = [&](f32x4 a, f32x4 b, int k, f32x4& sa, f32x4& sb) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float ra = row_sum16(a[v]), rb = row_sum16(b[v]);
+            if (c == 0) L.stat[k][wave][4 * g + v] = f32x2{ra, rb};
+        }
+        __syncthreads();
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            float x = 0.f, y = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                x += L.stat[k][w][4 * g + v].x;
+                y += L.stat[k][w][4 * g + v].y;
+            }
+            sa[v] = x;
+            sb[v] = y;
+        }
+    };
+
+    // two prefetch slots used alternately at compile-time positions
+    LnTile<TIO> bufs[2];
+    auto step = [&](int j, auto slot) {
+        auto& cur = bufs[decltype(slot)::value];
+        auto& nxt = bufs[decltype(slot)::value ^ 1];
+        int si, t0, len;
+        span(j, si, t0, len);
+        __syncthreads();   // the previous sub-tile is done with the tiles and statistics
+        put(cur, len);
+        __syncthreads();
+        if (j < last) fetch(nxt, j + 1);
+        // U^T = K W_c^T (+ b_c), P^T = Q M^T (+ b_m), S = K Q^T, over the features
+        f32x4 U = {bc, bc, bc, bc}, P = {bm, bm, bm, bm}, Sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const f32x4 kb = rl<S>(L.K, 16 * b, lane), qb = rl<S>(L.Q, 16 * b, lane);
+            U = mm16(kb, Wc[b], U);
+            P = mm16(qb, M[b], P);
+            Sc = mm16(kb, qb, Sc);
+        }
+        // causal scores with the bias's +1: writer s = 4g + v, reader t = c
+        f32x4 Sm;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Sm[v] = (4 * g + v <= c) ? Sc[v] + 1.f : 0.f;
+        // G = dl/dU: lane row r0 + c, tokens 4g + v
+        const f32x4 kc = cl<S>(L.K, r0, lane), vc = cl<S>(L.V, r0, lane);
+        f32x4 G;
+        if (ln) {
+            f32x4 mu, rs;
+            ln_stats(U, 0, mu, rs);
+            f32x4 uh, gg, ggu;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                uh[v] = (U[v] - mu[v]) * rs[v];
+                gg[v] = lw * (kc[v] + lw * uh[v] + lb - vc[v]);
+                ggu[v] = gg[v] * uh[v];
+            }
+            f32x4 mh, mhu;
+            feature_sums(gg, ggu, 1, mh, mhu);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                G[v] = rs[v] * (gg[v] - mh[v] * (1.f / D) - uh[v] * (mhu[v] * (1.f / D)));
+        } else {
+            G = U - vc;
+        }
+        // G diag(eta); tokens past the sub-tile's end contribute nothing
+        const f32x4 et = *reinterpret_cast<const f32x4*>(L.eta + 4 * g);
+        f32x4 Ge;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Ge[v] = (4 * g + v < len) ? G[v] * et[v] : 0.f;
+        // Zpre^T = P^T - S^T (G eta)^T: A = RL(S^T) = CL(S), B = CL((G eta)^T) = Ge
+        const f32x4 Zp = P - mm16(Sm, Ge, f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 Zo;
+        if (ln) {
+            f32x4 mu, rs;
+            ln_stats(Zp, 2, mu, rs);
+            const f32x4 qc = cl<S>(L.Q, r0, lane);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) Zo[v] = qc[v] + lw * ((Zp[v] - mu[v]) * rs[v]) + lb;
+        } else {
+            Zo = Zp;
+        }
+        // Z[t0 + 4g + v][r0 + c]; tokens past the sub-tile's end fall outside the range
+        {
+            const auto rz = __builtin_amdgcn_make_buffer_rsrc(
+                Z + (tok0 + t0) * D, 0, (int)(len * D * sizeof(TIO)), kBufferFlags);
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                buffer_store1(rz, ((4 * g + v) * D + r0 + c) * (int)sizeof(TIO), Zo[v], TIO{});
+        }
+        // M^T -= K^T (G eta)^T per column block: A = RL(K^T_b) = CL(K_b), B = -Ge
+        const f32x4 nGe = -Ge;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) M[b] = mm16(cl<S>(L.K, 16 * b, lane), nGe, M[b]);
+        // b_m -= G eta: over the tokens (slots, then lane groups)
+        float bs = (Ge[0] + Ge[1]) + (Ge[2] + Ge[3]);
+        bs += __shfl_xor(bs, 16);
+        bs += __shfl_xor(bs, 32);
+        bm -= bs;
+        // chunk end: the running state becomes the next chunk-start state
+        if (si == nsub - 1 || j == last) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) Wc[b] = M[b];
+            bc = bm;
+        }
+    };
+    const std::integral_constant<int, 0> slot0;
+    const std::integral_constant<int, 1> slot1;
+    fetch(bufs[0], 0);
+    {
+        int j = 0;
+        for (; j + 1 <= last; j += 2) {
+            step(j, slot0);
+            step(j + 1, slot1);
+        }
+        if (j == last) step(j, slot0);
     }
-    for (int i = tid; i < D; i += NT) b_out[(size_t)slice * D + i] = sbm[i];
+
+    {
+        float* w = W_out + ((size_t)slice * D + r0 + c) * D + 4 * g;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) *reinterpret_cast<f32x4*>(w + 16 * b) = M[b];
+    }
+    if (g == 0) b_out[(size_t)slice * D + r0 + c] = bm;
 }
 
 template <typename TIO>
@@ -289,15 +300,15 @@ hipError_t launch_typed(const LinearLnArgs& a, hipStream_t s)
     const TIO* Q = static_cast<const TIO*>(a.Q);
     const TIO* V = static_cast<const TIO*>(a.V);
     TIO* Z = static_cast<TIO*>(a.Z);
-#define TTT_LN_LAUNCH(DD)                                                                      \
-    if (a.eta)                                                                                 \
-        hipLaunchKernelGGL((linear_ln_kernel<TIO, DD, true>), grid, dim3(ln_threads<DD>()), 0, \
-                           s, K, Q, V, a.eta, a.eta_scalar, a.W0, a.b0, a.ln_weight,            \
-                           a.ln_bias, a.eps, Z, a.W_out, a.b_out, a.H, a.T, a.chunk);           \
-    else                                                                                       \
-        hipLaunchKernelGGL((linear_ln_kernel<TIO, DD, false>), grid, dim3(ln_threads<DD>()),   \
-                           0, s, K, Q, V, a.eta, a.eta_scalar, a.W0, a.b0, a.ln_weight,         \
-                           a.ln_bias, a.eps, Z, a.W_out, a.b_out, a.H, a.T, a.chunk)
+#define TTT_LN_LAUNCH(DD)                                                                    \
+    if (a.eta)                                                                               \
+        hipLaunchKernelGGL((linear_ln_kernel<TIO, DD, true>), grid, dim3(4 * DD), 0, s, K, Q, \
+                           V, a.eta, a.eta_scalar, a.W0, a.b0, a.ln_weight, a.ln_bias, a.eps, \
+                           Z, a.W_out, a.b_out, a.H, a.T, a.chunk);                           \
+    else                                                                                     \
+        hipLaunchKernelGGL((linear_ln_kernel<TIO, DD, false>), grid, dim3(4 * DD), 0, s, K,   \
+                           Q, V, a.eta, a.eta_scalar, a.W0, a.b0, a.ln_weight, a.ln_bias,     \
+                           a.eps, Z, a.W_out, a.b_out, a.H, a.T, a.chunk)
     switch (a.d) {
     case 16: TTT_LN_LAUNCH(16); break;
     case 32: TTT_LN_LAUNCH(32); break;

@@ -57,28 +57,6 @@ __device__ __forceinline__ void store_row(float* p, const float (&v)[N])
     }
 }
 
-// Sum over the 16 lanes of a DPP row (lanes 16m .. 16m+15); every lane of the row
-// receives the sum.  Swaps inside each quad (lane ^ 1, lane ^ 2), then the
-// half-row mirror (quad 0 <-> quad 1 of each 8-lane half) and the row mirror
-// (half 0 <-> half 1); no cross-row movement, no LDS.
-__device__ __forceinline__ float dpp_add(float x, int y)
-{
-    return x + __int_as_float(y);
-}
-
-__device__ __forceinline__ float row_sum16(float x)
-{
-    constexpr int kQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
-    constexpr int kQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
-    constexpr int kRowHalfMirror = 0x141;
-    constexpr int kRowMirror = 0x140;
-    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kQuadXor1, 0xF, 0xF, false));
-    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kQuadXor2, 0xF, 0xF, false));
-    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kRowHalfMirror, 0xF, 0xF, false));
-    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kRowMirror, 0xF, 0xF, false));
-    return x;
-}
-
 // f(integral_constant<0>), ..., f(integral_constant<N-1>): ring slots as constants
 template <typename F, int... I>
 __device__ __forceinline__ void static_for_seq(F& f, std::integer_sequence<int, I...>)
