@@ -164,7 +164,7 @@ int ttt_linear_fwd_momentum(const void* K, const void* Q, const void* V,
  *   ln_weight, ln_bias   : [H, d] fp32, shared by the batch, or both NULL.
  *   eps                  : > 0, finite.
  *   Others as ttt_linear_fwd; d : 16, 32, 64 or 128; any chunk; fp32 arithmetic
- *   on the vector ALUs, one workgroup per (batch, head); no workspace. */
+ *   on the fp32 matrix cores, one workgroup per (batch, head); no workspace. */
 int ttt_linear_ln_fwd(const void* K, const void* Q, const void* V,
                       const float* eta, float eta_scalar, const float* W0, const float* b0,
                       const float* ln_weight, const float* ln_bias, float eps,

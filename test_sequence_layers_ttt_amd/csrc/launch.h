@@ -108,7 +108,8 @@ struct LinearLnArgs {
 };
 
 // TTT-Linear with the inner bias and optional LayerNorm + residual inside f:
-// fp32 vector ALU, one workgroup per (batch, head), any chunk, d <= 128.
+// fp32 matrix cores, one workgroup of d/16 waves per (batch, head), any chunk,
+// d <= 128.
 hipError_t launch_linear_ln(const LinearLnArgs& a, hipStream_t s);
 
 struct LinearBwdArgs {
