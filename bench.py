@@ -47,7 +47,7 @@ KERNEL_SOURCES = {"linear": ["linear_mfma.hip", "linear_coop.hip", "linear_gener
                   "bwd": ["linear_bwd.hip", "mfma_f32.h", "mfma_common.h", "device_common.h",
                           "launch.h", "api.cpp"]}
 DECODE_METRIC = "TTT-Linear decode tokens/sec (all heads) + % of HBM roofline"
-BWD_METRIC = "TTT-Linear backward tokens/sec (all heads) + % of fp32 MFMA roofline"
+BWD_METRIC = "TTT-Linear backward tokens/sec (all heads) + % of MFMA roofline"
 LN_METRIC = "TTT-Linear (bias, LayerNorm, residual) tokens/sec (all heads) + % of fp32 MFMA roofline"
 FP32_PEAK_TFS = 157.3            # MI355X dense fp32 matrix
 
@@ -216,6 +216,7 @@ def bwd_main(args, wl, x, seed):
         parity = {"max_rel_err": errs, "slices_checked": int(len(idx))}
         log("oracle: %d slices in %.2f s on %d threads; parity %s" % (len(idx), tcpu, nth, parity))
 
+    peak = BF16_PEAK_TFS if wl.io == "bf16" else FP32_PEAK_TFS
     rec = {
         "metric": BWD_METRIC,
         "value": round(B * T / (ms_step * 1e-3), 1),
@@ -227,13 +228,15 @@ def bwd_main(args, wl, x, seed):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        # bf16 I/O: products on the bf16 matrix cores (fp32 operands split hi + lo),
+        # priced against the dense bf16 peak; fp32 I/O: the fp32 matrix peak
+        "dtype": "bf16x2" if wl.io == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name + "_bwd", "scan": "ttt_linear_bwd", "batch": B,
                    "heads": H, "seq_len": T, "head_dim": d, "chunk": wl.chunk, "io": wl.io,
                    "parallelism": "single_gpu"},
-        "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": FP32_PEAK_TFS,
-                     "unit": "TFLOP/s", "frac": round(tfs / FP32_PEAK_TFS, 4), "traffic": None,
+        "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(tfs / peak, 4), "traffic": None,
                      "kernel_ms": round(ms_event, 5), "algorithmic_flops": flops},
         "cpu_baseline": cpu,
         "parity": parity,

@@ -23,8 +23,11 @@
 // are added by fp32 atomic adds into buffers cleared before the launch (the
 // outputs themselves with fp32 I/O; with bf16 I/O a last pass rounds the sums).
 //
-// All products run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32), operands
-// staged through LDS in row-major fp32 tiles with padded rows.  Register forms
+// Every product is a 16 x 16 tile product, operands staged through LDS in
+// row-major fp32 tiles with padded rows.  With fp32 I/O it runs on the fp32
+// matrix cores (v_mfma_f32_16x16x4_f32); with bf16 I/O on the bf16 ones, the
+// fp32 operands split as hi + lo bf16 (mmt in mfma_f32.h: about 2^-17 relative
+// per product, against the bf16 rounding of the outputs).  Register forms
 // of a 16 x 16 tile X (lane l, c = l % 16, g = l / 16, slot v = 0..3):
 //   CL(X): lane holds X[4g + v][c]   (the MFMA result layout; a B operand whose
 //                                     contraction index is X's row)
@@ -184,6 +187,10 @@ template <typename TIO, int D, bool MULTI>
 __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs a)
 {
     constexpr int NW = bwd_waves<D>(), NB = D / 16, NBW = NB / NW, S = D + 4;
+    // bf16 I/O: K, Q, V and dZ values are exact in bf16 and the products run on
+    // the bf16 matrix cores (fp32 operands split as hi + lo); fp32 I/O keeps the
+    // fp32 form
+    constexpr bool BF = sizeof(TIO) == 2;
     constexpr int KP = SubTile<TIO, D, NW>::KP, VP = SubTile<TIO, D, NW>::VP;
     __shared__ BwdLds<D, NW> L;
     const int tid = threadIdx.x;
@@ -317,7 +324,7 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
         f32x4 Ew = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int bb = 0; bb < NBW; ++bb)
-            Ew = mm16(rl<S>(L.W, 16 * blk(bb), lane), rl<S>(L.K, 16 * blk(bb), lane), Ew);
+            Ew = mmt<BF, false, true>(rl<S>(L.W, 16 * blk(bb), lane), rl<S>(L.K, 16 * blk(bb), lane), Ew);
         put_cl<20>(L.part[wave][0], 0, lane, Ew);
         __syncthreads();
         const f32x4 E = reduce(0);
@@ -330,7 +337,8 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
         // W -= F K (contraction over the sub-tile's tokens), this wave's blocks
         const f32x4 Fa = rl<20>(L.F[wave], 0, lane);
 #pragma unroll
-        for (int bb = 0; bb < NBW; ++bb) Wr[bb] = mm16(Fa, cl<S>(L.K, 16 * blk(bb), lane), Wr[bb]);
+        for (int bb = 0; bb < NBW; ++bb)
+            Wr[bb] = mmt<BF, false, true>(Fa, cl<S>(L.K, 16 * blk(bb), lane), Wr[bb]);
     };
     const std::integral_constant<int, 0> slot0;
     const std::integral_constant<int, 1> slot1;
@@ -390,9 +398,9 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
         for (int bb = 0; bb < NBW; ++bb) {
             const int b = blk(bb);
             const f32x4 kb = rl<S>(L.K, 16 * b, lane);
-            Ew = mm16(rl<S>(L.W, 16 * b, lane), kb, Ew);
-            PKw = mm16(rl<S>(L.P, 16 * b, lane), kb, PKw);
-            Sw = mm16(kb, rl<S>(L.Q, 16 * b, lane), Sw);
+            Ew = mmt<BF, false, true>(rl<S>(L.W, 16 * b, lane), kb, Ew);
+            PKw = mmt<BF, false, true>(rl<S>(L.P, 16 * b, lane), kb, PKw);
+            Sw = mmt<BF, true, true>(kb, rl<S>(L.Q, 16 * b, lane), Sw);
         }
         put_cl<20>(L.part[wave][0], 0, lane, Ew);
         put_cl<20>(L.part[wave][1], 0, lane, PKw);
@@ -413,7 +421,7 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
         const f32x4 dZa = cl<20>(L.dZ, 0, lane);   // RL(dZ_blk): dZ[row c][token 4g + v]
         const f32x4 dZb = rl<20>(L.dZ, 0, lane);   // CL(dZ_blk): dZ[row 4g + v][token c]
         // dF = -dZ M^T - P K^T
-        f32x4 dF = mm16(dZa, rl<20>(L.M[wave], 0, lane), f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 dF = mmt<BF, true, false>(dZa, rl<20>(L.M[wave], 0, lane), f32x4{0.f, 0.f, 0.f, 0.f});
         f32x4 dE;
         float de = 0.f;
 #pragma unroll
@@ -437,7 +445,7 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
             buffer_store4(rdv, (c * D + r0 + 4 * g) * (int)sizeof(TIO), -dE, TIO{});
         }
         // dA = -(F^T dZ) o U: A = RL(F^T) = CL(F) registers, B = CL(dZ_blk)
-        f32x4 dA = mm16(F, dZb, f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 dA = mmt<BF, false, true>(F, dZb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int v = 0; v < 4; ++v) dA[v] = (4 * g + v <= c) ? -dA[v] : 0.f;
         put_cl<20>(L.dA[wave], 0, lane, dA);
@@ -449,7 +457,7 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
             const f32x4 Fa = rl<20>(L.F[wave], 0, lane);
 #pragma unroll
             for (int bb = 0; bb < NBW; ++bb)
-                Hr[bb] = mm16(Fa, cl<S>(L.K, 16 * blk(bb), lane), Hr[bb]);
+                Hr[bb] = mmt<BF, false, true>(Fa, cl<S>(L.K, 16 * blk(bb), lane), Hr[bb]);
         }
         const f32x4 dAa = rl<20>(L.dA[wave], 0, lane);   // RL(dA)
         const f32x4 dEa = rl<20>(L.dE[wave], 0, lane);   // RL(dE)
@@ -466,14 +474,14 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
             const f32x4 qc = cl<S>(L.Q, 16 * b, lane);
             const f32x4 wc = cl<S>(L.W, 16 * b, lane);
             // dK (tokens x dims) = -F^T P + dE^T W + dA Q   (P: this sub-tile's, CL)
-            f32x4 dK = mm16(Fn, P[bb], f32x4{0.f, 0.f, 0.f, 0.f});
-            dK = mm16(dE, wc, dK);
-            dK = mm16(dAa, qc, dK);
+            f32x4 dK = mmt<BF, false, false>(Fn, P[bb], f32x4{0.f, 0.f, 0.f, 0.f});
+            dK = mmt<BF, false, false>(dE, wc, dK);
+            dK = mmt<BF, false, true>(dAa, qc, dK);
             // dQ (tokens x dims) = dZ^T H + dA^T K
             f32x4 dQ;
-            if constexpr (MULTI) dQ = mm16(dZb, Hr[bb], f32x4{0.f, 0.f, 0.f, 0.f});
-            else dQ = mm16(dZb, wc, f32x4{0.f, 0.f, 0.f, 0.f});
-            dQ = mm16(dA, kc, dQ);
+            if constexpr (MULTI) dQ = mmt<BF, true, false>(dZb, Hr[bb], f32x4{0.f, 0.f, 0.f, 0.f});
+            else dQ = mmt<BF, true, false>(dZb, wc, f32x4{0.f, 0.f, 0.f, 0.f});
+            dQ = mmt<BF, false, true>(dA, kc, dQ);
             // token 4g + v of the sub-tile, column 16b + c; rows past len dropped
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
@@ -482,8 +490,8 @@ __global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs
                 raw_buffer_atomic_fadd(dQ[v], rdq, off, 0, 0);
             }
             // P += dZ Q, dW += dE K
-            P[bb] = mm16(dZa, qc, P[bb]);
-            dWa[bb] = mm16(dEa, kc, dWa[bb]);
+            P[bb] = mmt<BF, true, true>(dZa, qc, P[bb]);
+            dWa[bb] = mmt<BF, false, true>(dEa, kc, dWa[bb]);
         }
         if (si == 0) {   // the chunk is done: its dW is the previous chunk's dW_next
 #pragma unroll

@@ -56,4 +56,47 @@ __device__ __forceinline__ f32x4 mm16(f32x4 a, f32x4 b, f32x4 acc)
     return acc;
 }
 
+// The same tile product on the bf16 matrix cores (16x16x32 form, 16 cycles,
+// against 4 x 32 for the fp32 form), for operands of which AX / BX are exactly
+// representable in bf16 (values widened from bf16 inputs).  An operand that is
+// not is split as hi + lo, hi = bf16(x), lo = bf16(x - hi), which keeps about 17
+// significant bits: one exact operand takes one instruction (slots 0-3 hold hi,
+// 4-7 lo, against the exact operand in both halves), two split ones two (the
+// lo x lo term, below 2^-16 relative, is dropped).  Products are exact and sums
+// fp32, so the result is the fp32 product to about 2^-17 relative.  SPLIT false
+// keeps the fp32 form.
+__device__ __forceinline__ void split_bf16(f32x4 x, u32x2& hi, u32x2& lo)
+{
+    hi = pack_bf16x4(x);
+    const f32x4 h = {__uint_as_float(hi.x << 16), __uint_as_float(hi.x & 0xffff0000u),
+                     __uint_as_float(hi.y << 16), __uint_as_float(hi.y & 0xffff0000u)};
+    lo = pack_bf16x4(x - h);
+}
+
+template <bool SPLIT, bool AX, bool BX>
+__device__ __forceinline__ f32x4 mmt(f32x4 a, f32x4 b, f32x4 acc)
+{
+    if constexpr (!SPLIT) {
+        return mm16(a, b, acc);
+    } else if constexpr (AX && BX) {
+        return mfma16(pack_bf16x4(a), pack_bf16x4(b), acc);
+    } else if constexpr (BX) {
+        u32x2 ah, al;
+        split_bf16(a, ah, al);
+        const u32x2 bb = pack_bf16x4(b);
+        return mfma32(u32x4{ah.x, ah.y, al.x, al.y}, u32x4{bb.x, bb.y, bb.x, bb.y}, acc);
+    } else if constexpr (AX) {
+        u32x2 bh, bl;
+        split_bf16(b, bh, bl);
+        const u32x2 aa = pack_bf16x4(a);
+        return mfma32(u32x4{aa.x, aa.y, aa.x, aa.y}, u32x4{bh.x, bh.y, bl.x, bl.y}, acc);
+    } else {
+        u32x2 ah, al, bh, bl;
+        split_bf16(a, ah, al);
+        split_bf16(b, bh, bl);
+        acc = mfma32(u32x4{ah.x, ah.y, al.x, al.y}, u32x4{bh.x, bh.y, bh.x, bh.y}, acc);
+        return mfma16(ah, bl, acc);
+    }
+}
+
 }  // namespace ttt
