@@ -15,8 +15,9 @@
 //
 // LN needs all d features of a token, so one workgroup owns a whole (batch,
 // head): d/16 waves, wave w holding state rows 16w .. 16w+15 (of W_c and M, all
-// columns, in registers).  Every product runs on the fp32 matrix cores
-// (v_mfma_f32_16x16x4_f32, so results keep fp32 accuracy), in the transposed
+// columns, in registers).  Every product is a 16 x 16 tile product: on the fp32
+// matrix cores with fp32 I/O, on the bf16 ones with bf16 I/O (fp32 operands
+// split as hi + lo, about 2^-17 relative per product), in the transposed
 // orientation that leaves the state's rows in the lanes (see mfma_f32.h):
 //   U^T = K W_c^T,  P^T = Q M^T,  S = K Q^T,  Zpre^T = P^T - S^T (G diag(eta))^T,
 //   M^T <- M^T - K^T (G diag(eta))^T,
@@ -83,6 +84,9 @@ __global__ __launch_bounds__(4 * D) void linear_ln_kernel(
     int H, int T, int chunk)
 {
     constexpr int NW = D / 16, NB = D / 16, S = LnLds<D>::S;
+    // bf16 I/O: K and Q are exact in bf16 and the tile products run on the bf16
+    // matrix cores, fp32 operands split as hi + lo (mmt); fp32 I/O keeps fp32 ones
+    constexpr bool BF = sizeof(TIO) == 2;
     __shared__ __align__(16) LnLds<D> L;
 
     const int tid = threadIdx.x;
@@ -202,9 +206,9 @@ __global__ __launch_bounds__(4 * D) void linear_ln_kernel(
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             const f32x4 kb = rl<S>(L.K, 16 * b, lane), qb = rl<S>(L.Q, 16 * b, lane);
-            U = mm16(kb, Wc[b], U);
-            P = mm16(qb, M[b], P);
-            Sc = mm16(kb, qb, Sc);
+            U = mmt<BF, true, false>(kb, Wc[b], U);
+            P = mmt<BF, true, false>(qb, M[b], P);
+            Sc = mmt<BF, true, true>(kb, qb, Sc);
         }
         // causal scores with the bias's +1: writer s = 4g + v, reader t = c
         f32x4 Sm;
@@ -237,7 +241,7 @@ __global__ __launch_bounds__(4 * D) void linear_ln_kernel(
 #pragma unroll
         for (int v = 0; v < 4; ++v) Ge[v] = (4 * g + v < len) ? G[v] * et[v] : 0.f;
         // Zpre^T = P^T - S^T (G eta)^T: A = RL(S^T) = CL(S), B = CL((G eta)^T) = Ge
-        const f32x4 Zp = P - mm16(Sm, Ge, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 Zp = P - mmt<BF, false, false>(Sm, Ge, f32x4{0.f, 0.f, 0.f, 0.f});
         f32x4 Zo;
         if (ln) {
             f32x4 mu, rs;
@@ -259,7 +263,7 @@ __global__ __launch_bounds__(4 * D) void linear_ln_kernel(
         // M^T -= K^T (G eta)^T per column block: A = RL(K^T_b) = CL(K_b), B = -Ge
         const f32x4 nGe = -Ge;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) M[b] = mm16(cl<S>(L.K, 16 * b, lane), nGe, M[b]);
+        for (int b = 0; b < NB; ++b) M[b] = mmt<BF, true, false>(cl<S>(L.K, 16 * b, lane), nGe, M[b]);
         // b_m -= G eta: over the tokens (slots, then lane groups)
         float bs = (Ge[0] + Ge[1]) + (Ge[2] + Ge[3]);
         bs += __shfl_xor(bs, 16);
