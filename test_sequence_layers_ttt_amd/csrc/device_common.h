@@ -88,17 +88,40 @@ __device__ __forceinline__ float dpp_add(float x, int y)
     return x + __int_as_float(y);
 }
 
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
 __device__ __forceinline__ float row_sum16(float x)
 {
-    constexpr int kQuadXor1 = 0xB1;     // quad_perm [1, 0, 3, 2]
-    constexpr int kQuadXor2 = 0x4E;     // quad_perm [2, 3, 0, 1]
-    constexpr int kRowHalfMirror = 0x141;
-    constexpr int kRowMirror = 0x140;
-    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kQuadXor1, 0xF, 0xF, false));
-    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kQuadXor2, 0xF, 0xF, false));
-    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kRowHalfMirror, 0xF, 0xF, false));
-    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kRowMirror, 0xF, 0xF, false));
+    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kDppQuadXor1, 0xF, 0xF, false));
+    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kDppQuadXor2, 0xF, 0xF, false));
+    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kDppRowHalfMirror, 0xF, 0xF, false));
+    x = dpp_add(x, __builtin_amdgcn_mov_dpp(__float_as_int(x), kDppRowMirror, 0xF, 0xF, false));
     return x;
+}
+
+// one DPP stage of row_sum16 over N independent values: every move first, then
+// every add, so that each move's wait for the previous add is filled by the others
+template <int CTRL, int N>
+__device__ __forceinline__ void dpp_stage(float (&x)[N])
+{
+    int m[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) m[i] = __builtin_amdgcn_mov_dpp(__float_as_int(x[i]), CTRL, 0xF, 0xF, false);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = dpp_add(x[i], m[i]);
+}
+
+// row_sum16 of N independent values (the same sums, stage by stage)
+template <int N>
+__device__ __forceinline__ void row_sum16_n(float (&x)[N])
+{
+    dpp_stage<kDppQuadXor1>(x);
+    dpp_stage<kDppQuadXor2>(x);
+    dpp_stage<kDppRowHalfMirror>(x);
+    dpp_stage<kDppRowMirror>(x);
 }
 
 }  // namespace ttt

@@ -144,12 +144,18 @@ __global__ __launch_bounds__(4 * D) void linear_ln_kernel(
     // mean and 1/sqrt(var + eps) over the d features of tokens 4g + v, from this
     // wave's 16 rows (lanes c) and the other waves' partials
     auto ln_stats = [&](f32x4 x, int k, f32x4& mean, f32x4& rstd) {
+        float sx[4] = {x[0], x[1], x[2], x[3]};
+        row_sum16_n(sx);
+        float dd[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            const float mw = row_sum16(x[v]) * (1.f / 16.f);
-            const float dv = x[v] - mw;
-            const float m2 = row_sum16(dv * dv);
-            if (c == 0) L.stat[k][wave][4 * g + v] = f32x2{mw, m2};
+            const float dv = x[v] - sx[v] * (1.f / 16.f);
+            dd[v] = dv * dv;
+        }
+        row_sum16_n(dd);
+        if (c == 0) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) L.stat[k][wave][4 * g + v] = f32x2{sx[v] * (1.f / 16.f), dd[v]};
         }
         __syncthreads();
 #pragma unroll
@@ -171,10 +177,11 @@ __global__ __launch_bounds__(4 * D) void linear_ln_kernel(
     };
     // sums over the d features of tokens 4g + v of two quantities
     auto feature_sums = [&](f32x4 a, f32x4 b, int k, f32x4& sa, f32x4& sb) {
+        float r[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        row_sum16_n(r);
+        if (c == 0) {
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const float ra = row_sum16(a[v]), rb = row_sum16(b[v]);
-            if (c == 0) L.stat[k][wave][4 * g + v] = f32x2{ra, rb};
+            for (int v = 0; v < 4; ++v) L.stat[k][wave][4 * g + v] = f32x2{r[v], r[4 + v]};
         }
         __syncthreads();
 #pragma unroll
