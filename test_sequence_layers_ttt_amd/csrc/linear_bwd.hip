@@ -111,12 +111,18 @@ __device__ __forceinline__ void load_vec(const uint16_t* p, float* out)
     }
 }
 
-// Waves per workgroup: each owns NB / NW of the d/16 column blocks.
+// Waves per workgroup: each owns NB / NW of the d/16 column blocks.  With few
+// (sequence, 16-row block) units the waves split a unit's work across SIMDs;
+// once the units fill the compute units, one wave per unit (bf16 products, at
+// d = 64) avoids the cross-wave sums and barriers.  Measured on MI355X: 8x12
+// heads (384 units) 0.598 -> 0.563 ms with one wave; 1x32 heads (128 units)
+// 6.44 -> 7.32 ms, so there the four-wave split stays.
 template <int D>
 constexpr int bwd_waves()
 {
     return D == 128 ? 2 : (D >= 32 ? D / 16 : 1);
 }
+constexpr long kComputeUnits = 256;
 
 template <int D, int NW>
 struct BwdLds {
@@ -183,10 +189,10 @@ struct SubTile {
 // MULTI: chunks span several 16-token sub-tiles (the running W - G_{<sigma} is
 // needed); a compile-time choice, so that chunks of at most 16 tokens carry no
 // trace of it.
-template <typename TIO, int D, bool MULTI>
-__global__ __launch_bounds__(64 * bwd_waves<D>()) void linear_bwd_kernel(BwdArgs a)
+template <typename TIO, int D, int NW, bool MULTI>
+__global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
 {
-    constexpr int NW = bwd_waves<D>(), NB = D / 16, NBW = NB / NW, S = D + 4;
+    constexpr int NB = D / 16, NBW = NB / NW, S = D + 4;
     // bf16 I/O: K, Q, V and dZ values are exact in bf16 and the products run on
     // the bf16 matrix cores (fp32 operands split as hi + lo); fp32 I/O keeps the
     // fp32 form
@@ -583,12 +589,21 @@ hipError_t launch_typed(const LinearBwdArgs& a, hipStream_t s)
         hipLaunchKernelGGL(zero_kernel<false>, dim3(elementwise_grid(4 * ntok)), dim3(256), 0, s,
                            a.deta, ntok);
     const unsigned grid = (unsigned)(((a.BH + 7) / 8) * 8 * NB);
-    if (a.chunk > kSub)
-        hipLaunchKernelGGL((linear_bwd_kernel<TIO, D, true>), dim3(grid), dim3(64 * bwd_waves<D>()),
-                           0, s, k);
-    else
-        hipLaunchKernelGGL((linear_bwd_kernel<TIO, D, false>), dim3(grid),
-                           dim3(64 * bwd_waves<D>()), 0, s, k);
+    auto launch = [&](auto nw) {
+        constexpr int NW = decltype(nw)::value;
+        if (a.chunk > kSub)
+            hipLaunchKernelGGL((linear_bwd_kernel<TIO, D, NW, true>), dim3(grid), dim3(64 * NW), 0,
+                               s, k);
+        else
+            hipLaunchKernelGGL((linear_bwd_kernel<TIO, D, NW, false>), dim3(grid), dim3(64 * NW),
+                               0, s, k);
+    };
+    if constexpr (!F32 && D == 64) {
+        if ((long)a.BH * NB >= kComputeUnits) launch(std::integral_constant<int, 1>{});
+        else launch(std::integral_constant<int, bwd_waves<D>()>{});
+    } else {
+        launch(std::integral_constant<int, bwd_waves<D>()>{});
+    }
     if constexpr (!F32)
         hipLaunchKernelGGL(round_bf16_kernel, dim3(elementwise_grid(n)), dim3(256), 0, s,
                            k.dK_acc, k.dQ_acc, static_cast<uint16_t*>(a.dK),
