@@ -37,8 +37,8 @@ BF16_PEAK_TFS = 2500.0           # MI355X dense bf16 MFMA
 PLANS = {"auto": 0, "generic": 1, "mfma": 2, "bigchunk": 3}
 # sources whose change invalidates a stored counter profile (kernels and dispatch)
 KERNEL_SOURCES = {"linear": ["linear_mfma.hip", "linear_coop.hip", "linear_generic.hip",
-                             "linear_bigchunk.hip", "mfma_common.h", "device_common.h",
-                             "launch.h", "api.cpp"],
+                             "linear_bigchunk.hip", "linear_f32.hip", "mfma_common.h",
+                             "mfma_f32.h", "device_common.h", "launch.h", "api.cpp"],
                   "mlp": ["mlp_mfma.hip", "mlp_generic.hip", "mfma_common.h", "device_common.h",
                           "launch.h", "api.cpp"],
                   "step": ["linear_step.hip", "device_common.h", "launch.h", "api.cpp"],

@@ -82,8 +82,10 @@ typedef enum {
 typedef enum {
     TTT_PLAN_AUTO = 0,
     TTT_PLAN_GENERIC = 1,       /* fp32 vector ALU, any chunk, fp32 or bf16 I/O */
-    TTT_PLAN_MFMA = 2,          /* bf16 matrix cores, d in {32, 64, 128}, chunk <= 16 or a
-                                   multiple of 16 */
+    TTT_PLAN_MFMA = 2,          /* matrix cores, inclusive read.  bf16 I/O: bf16 matrix
+                                   cores, d in {32, 64, 128}, chunk <= 16 or a multiple
+                                   of 16.  fp32 I/O: fp32 matrix cores, d in {16, 32,
+                                   64, 128}, any chunk (not for packed documents) */
     TTT_PLAN_BIGCHUNK = 3       /* bf16 matrix cores, three stages, d in {64, 128}, chunk a
                                    multiple of 32 >= 128 */
 } ttt_plan;

@@ -35,8 +35,10 @@ int linear_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan,
         return TTT_ERR_INVALID_ARG;
     if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
     const int bf16 = io_dtype == TTT_DTYPE_BF16;
-    // the small-chunk matrix-core kernels implement the inclusive read only
-    const bool mfma = read_mode == TTT_READ_INCLUSIVE && linear_mfma_supported(d, chunk, bf16);
+    // the small-chunk matrix-core kernels implement the inclusive read only: bf16
+    // I/O on the bf16 matrix cores, fp32 I/O on the fp32 ones (any chunk)
+    const bool mfma = read_mode == TTT_READ_INCLUSIVE &&
+                      (bf16 ? linear_mfma_supported(d, chunk, bf16) : linear_f32_supported(d));
     const bool big = linear_bigchunk_supported(d, chunk, bf16);
     switch (plan) {
     case TTT_PLAN_GENERIC: return TTT_PLAN_GENERIC;
@@ -152,7 +154,8 @@ int ttt_linear_fwd_ex(const void* K, const void* Q, const void* V,
     a.momentum = 0; a.beta = 0.f; a.mom0 = nullptr; a.mom_out = nullptr;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     switch (p) {
-    case TTT_PLAN_MFMA: return launch_status(launch_linear_mfma(a, s));
+    case TTT_PLAN_MFMA:
+        return launch_status(a.bf16 ? launch_linear_mfma(a, s) : launch_linear_f32(a, s));
     case TTT_PLAN_BIGCHUNK: return launch_status(launch_linear_bigchunk(a, s));
     default: return launch_status(launch_linear_generic(a, s));
     }

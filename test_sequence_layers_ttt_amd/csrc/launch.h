@@ -78,6 +78,11 @@ hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
 bool linear_mfma_supported(int d, int chunk, int bf16);
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
 
+// fp32 I/O on the fp32 matrix cores: one wave per (batch*head, 16-row block), any
+// chunk, d in {16, 32, 64, 128}, the inclusive read; part of the MFMA plan.
+bool linear_f32_supported(int d);
+hipError_t launch_linear_f32(const LinearArgs& a, hipStream_t s);
+
 // Chunks of exactly 16 tokens, one workgroup of d/16 waves per (batch, head)
 // sharing each chunk's K/Q tile through LDS; part of the MFMA plan.
 bool linear_coop_supported(int d, int chunk, int bf16);

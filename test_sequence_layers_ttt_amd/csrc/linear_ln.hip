@@ -131,15 +131,18 @@ __global__ __launch_bounds__(4 * D) void linear_ln_kernel(
         if constexpr (ETA) f.eta = eta[tok0 + t0 + min(c, len - 1)];
         else f.eta = eta_scalar;
     };
-    auto put = [&](const LnTile<TIO>& f, int len) {
-        const bool ok = fs < len;   // tokens past the sub-tile's end stage as zeros
+    // Tokens past the sub-tile's end stage the re-read last token as it is: their
+    // statistics are their own, every contribution they make is scaled by the
+    // masked G diag(eta) (a finite value times zero), and their outputs are never
+    // stored.  (A select here would be hoisted onto the freshly loaded registers.)
+    auto put = [&](const LnTile<TIO>& f) {
         auto four = [&](const RawRow<TIO, 4>& r) {
-            return ok ? f32x4{r.at(0), r.at(1), r.at(2), r.at(3)} : f32x4{0.f, 0.f, 0.f, 0.f};
+            return f32x4{r.at(0), r.at(1), r.at(2), r.at(3)};
         };
         *reinterpret_cast<f32x4*>(L.K + fs * S + fj) = four(f.k);
         *reinterpret_cast<f32x4*>(L.Q + fs * S + fj) = four(f.q);
         *reinterpret_cast<f32x4*>(L.V + fs * S + fj) = four(f.v);
-        if (tid < kSub) L.eta[tid] = tid < len ? f.eta : 0.f;
+        if (tid < kSub) L.eta[tid] = f.eta;
     };
     // mean and 1/sqrt(var + eps) over the d features of tokens 4g + v, from this
     // wave's 16 rows (lanes c) and the other waves' partials
@@ -205,9 +208,12 @@ __global__ __launch_bounds__(4 * D) void linear_ln_kernel(
         int si, t0, len;
         span(j, si, t0, len);
         __syncthreads();   // the previous sub-tile is done with the tiles and statistics
-        put(cur, len);
+        put(cur);
         __syncthreads();
         if (j < last) fetch(nxt, j + 1);
+        // keep the loads here: sunk below this sub-tile's stores, they would make
+        // the next staging wait for those stores too
+        __builtin_amdgcn_sched_barrier(0);
         // U^T = K W_c^T (+ b_c), P^T = Q M^T (+ b_m), S = K Q^T, over the features
         f32x4 U = {bc, bc, bc, bc}, P = {bm, bm, bm, bm}, Sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -285,14 +291,18 @@ __global__ __launch_bounds__(4 * D) void linear_ln_kernel(
     };
     const std::integral_constant<int, 0> slot0;
     const std::integral_constant<int, 1> slot1;
+    // the first sub-tile runs before the loop, so that the loop is entered, as it
+    // is re-entered, with a sub-tile's stores behind the prefetched loads (the
+    // waits at the loop head then cover the loads only)
     fetch(bufs[0], 0);
+    step(0, slot0);
     {
-        int j = 0;
+        int j = 1;
         for (; j + 1 <= last; j += 2) {
-            step(j, slot0);
-            step(j + 1, slot1);
+            step(j, slot1);
+            step(j + 1, slot0);
         }
-        if (j == last) step(j, slot0);
+        if (j == last) step(j, slot1);
     }
 
     {

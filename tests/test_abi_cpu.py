@@ -321,8 +321,13 @@ def test_momentum_rejects_bad_arguments(kw, status):
 
 
 def test_plan_selection_and_workspace_are_host_only():
-    assert ttt.linear_select_plan(1, 1, 256, 16, 16, ttt.DTYPE_F32) == ttt.PLAN_GENERIC
+    # fp32 I/O runs on the fp32 matrix cores (any chunk) unless the generic plan
+    # is asked for or the read order is the chunk-start one
+    assert ttt.linear_select_plan(1, 1, 256, 16, 16, ttt.DTYPE_F32) == ttt.PLAN_MFMA
+    assert ttt.linear_select_plan(1, 1, 256, 16, 40, ttt.DTYPE_F32) == ttt.PLAN_MFMA
     assert ttt.linear_select_plan(1, 1, 256, 16, 16, 0, ttt.PLAN_GENERIC) == ttt.PLAN_GENERIC
+    assert ttt.linear_select_plan(1, 1, 256, 16, 16, 0, ttt.PLAN_AUTO,
+                                  ttt.READ_CHUNK_START) == ttt.PLAN_GENERIC
     assert ttt.linear_select_plan(1, 1, 256, 24, 16, 0) == ttt.ERR_UNSUPPORTED
     assert ttt.linear_workspace_bytes(8, 12, 2048, 64, 16, ttt.DTYPE_BF16) == 0
     assert ttt.mlp_workspace_bytes(1, 2, 64, 64, 16, 1, ttt.PLAN_GENERIC) == 0

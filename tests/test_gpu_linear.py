@@ -61,6 +61,23 @@ def test_edge_lengths(dev, T, chunk, d):
     check_linear(wl, seed, dev, ttt.PLAN_AUTO)
 
 
+# fp32 I/O on the fp32 matrix cores: lengths and chunks that leave ragged
+# sub-tiles, chunks of one token, chunks longer than T, many slices
+@pytest.mark.parametrize("d", [16, 64, 128])
+@pytest.mark.parametrize("T,chunk,per_token", [(1, 16, True), (5, 16, False), (16, 16, True),
+                                               (17, 16, True), (33, 1, True), (70, 24, False),
+                                               (300, 64, True), (40, 100, True)])
+def test_f32_matrix_core_lengths(dev, T, chunk, per_token, d):
+    wl, seed = small(d, chunk, "f32", per_token=per_token, T=T)
+    assert ttt.linear_select_plan(wl.B, wl.H, wl.T, d, chunk, 0) == ttt.PLAN_MFMA
+    check_linear(wl, seed, dev, ttt.PLAN_MFMA)
+
+
+def test_f32_matrix_core_many_slices(dev):
+    wl, seed = small(32, 16, "f32", per_token=True, T=50, B=9, H=15, seed=109)
+    check_linear(wl, seed, dev, ttt.PLAN_MFMA)
+
+
 # Many (batch, head) slices: shapes past the 256-unit threshold (units = B*H*d/16)
 # where chunk-16 heads share their K/Q tiles per workgroup, and the two-block
 # single-wave kernel for the shapes that cannot.
