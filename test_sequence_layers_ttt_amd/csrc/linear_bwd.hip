@@ -26,8 +26,9 @@
 // Every product is a 16 x 16 tile product, operands staged through LDS in
 // row-major fp32 tiles with padded rows.  With fp32 I/O it runs on the fp32
 // matrix cores (v_mfma_f32_16x16x4_f32); with bf16 I/O on the bf16 ones, the
-// fp32 operands split as hi + lo bf16 (mmt in mfma_f32.h: about 2^-17 relative
-// per product, against the bf16 rounding of the outputs).  Register forms
+// fp32 operands of the reverse recurrence split as hi + lo bf16 (mmt in
+// mfma_f32.h: about 2^-17 relative per product) and those of the dK and dQ
+// products rounded to bf16, the outputs' own precision.  Register forms
 // of a 16 x 16 tile X (lane l, c = l % 16, g = l / 16, slot v = 0..3):
 //   CL(X): lane holds X[4g + v][c]   (the MFMA result layout; a B operand whose
 //                                     contraction index is X's row)
@@ -194,8 +195,11 @@ __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
 {
     constexpr int NB = D / 16, NBW = NB / NW, S = D + 4;
     // bf16 I/O: K, Q, V and dZ values are exact in bf16 and the products run on
-    // the bf16 matrix cores (fp32 operands split as hi + lo); fp32 I/O keeps the
-    // fp32 form
+    // the bf16 matrix cores.  Products on the reverse recurrence (E, P K^T, the
+    // scores, dF, dW, H) split their fp32 operands as hi + lo (about 17 bits);
+    // those that only form the bf16 outputs dK and dQ (and dA, used only there)
+    // round their operands to bf16, the outputs' own precision.  fp32 I/O keeps
+    // fp32 products throughout.
     constexpr bool BF = sizeof(TIO) == 2;
     constexpr int KP = SubTile<TIO, D, NW>::KP, VP = SubTile<TIO, D, NW>::VP;
     __shared__ BwdLds<D, NW> L;
@@ -451,7 +455,7 @@ __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
             buffer_store4(rdv, (c * D + r0 + 4 * g) * (int)sizeof(TIO), -dE, TIO{});
         }
         // dA = -(F^T dZ) o U: A = RL(F^T) = CL(F) registers, B = CL(dZ_blk)
-        f32x4 dA = mmt<BF, false, true>(F, dZb, f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 dA = mmt<BF, true, true>(F, dZb, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int v = 0; v < 4; ++v) dA[v] = (4 * g + v <= c) ? -dA[v] : 0.f;
         put_cl<20>(L.dA[wave], 0, lane, dA);
@@ -480,14 +484,14 @@ __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
             const f32x4 qc = cl<S>(L.Q, 16 * b, lane);
             const f32x4 wc = cl<S>(L.W, 16 * b, lane);
             // dK (tokens x dims) = -F^T P + dE^T W + dA Q   (P: this sub-tile's, CL)
-            f32x4 dK = mmt<BF, false, false>(Fn, P[bb], f32x4{0.f, 0.f, 0.f, 0.f});
-            dK = mmt<BF, false, false>(dE, wc, dK);
-            dK = mmt<BF, false, true>(dAa, qc, dK);
+            f32x4 dK = mmt<BF, true, true>(Fn, P[bb], f32x4{0.f, 0.f, 0.f, 0.f});
+            dK = mmt<BF, true, true>(dE, wc, dK);
+            dK = mmt<BF, true, true>(dAa, qc, dK);
             // dQ (tokens x dims) = dZ^T H + dA^T K
             f32x4 dQ;
-            if constexpr (MULTI) dQ = mmt<BF, true, false>(dZb, Hr[bb], f32x4{0.f, 0.f, 0.f, 0.f});
-            else dQ = mmt<BF, true, false>(dZb, wc, f32x4{0.f, 0.f, 0.f, 0.f});
-            dQ = mmt<BF, false, true>(dA, kc, dQ);
+            if constexpr (MULTI) dQ = mmt<BF, true, true>(dZb, Hr[bb], f32x4{0.f, 0.f, 0.f, 0.f});
+            else dQ = mmt<BF, true, true>(dZb, wc, f32x4{0.f, 0.f, 0.f, 0.f});
+            dQ = mmt<BF, true, true>(dA, kc, dQ);
             // token 4g + v of the sub-tile, column 16b + c; rows past len dropped
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
