@@ -59,6 +59,22 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 constexpr int kSub = 16;   // tokens per sub-tile
 
+// A1 B1 + A2 B2 + C for two 16 x 16 tile products (RL / CL operands): with bf16
+// operands one 16x16x32 instruction holds both, the first product in slots 0-3
+// of each lane group and the second in slots 4-7 (operands rounded to bf16);
+// otherwise two fp32 products
+template <bool BF>
+__device__ __forceinline__ f32x4 mm2(f32x4 a1, f32x4 b1, f32x4 a2, f32x4 b2, f32x4 acc)
+{
+    if constexpr (!BF) {
+        return mm16(a2, b2, mm16(a1, b1, acc));
+    } else {
+        const u32x2 x1 = pack_bf16x4(a1), x2 = pack_bf16x4(a2);
+        const u32x2 y1 = pack_bf16x4(b1), y2 = pack_bf16x4(b2);
+        return mfma32(u32x4{x1.x, x1.y, x2.x, x2.y}, u32x4{y1.x, y1.y, y2.x, y2.y}, acc);
+    }
+}
+
 // ---------------------------------------------------------------- global I/O
 // Range-checked buffer accesses: a store or atomic add whose byte offset lies at
 // or past the resource's size is dropped by the memory unit.  Lanes outside a
@@ -484,14 +500,12 @@ __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
             const f32x4 qc = cl<S>(L.Q, 16 * b, lane);
             const f32x4 wc = cl<S>(L.W, 16 * b, lane);
             // dK (tokens x dims) = -F^T P + dE^T W + dA Q   (P: this sub-tile's, CL)
-            f32x4 dK = mmt<BF, true, true>(Fn, P[bb], f32x4{0.f, 0.f, 0.f, 0.f});
-            dK = mmt<BF, true, true>(dE, wc, dK);
+            f32x4 dK = mm2<BF>(Fn, P[bb], dE, wc, f32x4{0.f, 0.f, 0.f, 0.f});
             dK = mmt<BF, true, true>(dAa, qc, dK);
             // dQ (tokens x dims) = dZ^T H + dA^T K
             f32x4 dQ;
-            if constexpr (MULTI) dQ = mmt<BF, true, true>(dZb, Hr[bb], f32x4{0.f, 0.f, 0.f, 0.f});
-            else dQ = mmt<BF, true, true>(dZb, wc, f32x4{0.f, 0.f, 0.f, 0.f});
-            dQ = mmt<BF, true, true>(dA, kc, dQ);
+            if constexpr (MULTI) dQ = mm2<BF>(dZb, Hr[bb], dA, kc, f32x4{0.f, 0.f, 0.f, 0.f});
+            else dQ = mm2<BF>(dZb, wc, dA, kc, f32x4{0.f, 0.f, 0.f, 0.f});
             // token 4g + v of the sub-tile, column 16b + c; rows past len dropped
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
