@@ -85,7 +85,10 @@ __global__ __launch_bounds__(4 * D) void linear_ln_kernel(
 {
     constexpr int NW = D / 16, NB = D / 16, S = LnLds<D>::S;
     // bf16 I/O: K and Q are exact in bf16 and the tile products run on the bf16
-    // matrix cores, fp32 operands split as hi + lo (mmt); fp32 I/O keeps fp32 ones
+    // matrix cores: those on the state's recurrence (U, the update) split their
+    // fp32 operands as hi + lo (mmt), those that only form the bf16 output Z (the
+    // read Q M^T, the score-weighted correction) round them to bf16; fp32 I/O
+    // keeps fp32 products
     constexpr bool BF = sizeof(TIO) == 2;
     __shared__ __align__(16) LnLds<D> L;
 
@@ -220,7 +223,7 @@ __global__ __launch_bounds__(4 * D) void linear_ln_kernel(
         for (int b = 0; b < NB; ++b) {
             const f32x4 kb = rl<S>(L.K, 16 * b, lane), qb = rl<S>(L.Q, 16 * b, lane);
             U = mmt<BF, true, false>(kb, Wc[b], U);
-            P = mmt<BF, true, false>(qb, M[b], P);
+            P = mmt<BF, true, true>(qb, M[b], P);
             Sc = mmt<BF, true, true>(kb, qb, Sc);
         }
         // causal scores with the bias's +1: writer s = 4g + v, reader t = c
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(4 * D) void linear_ln_kernel(
 #pragma unroll
         for (int v = 0; v < 4; ++v) Ge[v] = (4 * g + v < len) ? G[v] * et[v] : 0.f;
         // Zpre^T = P^T - S^T (G eta)^T: A = RL(S^T) = CL(S), B = CL((G eta)^T) = Ge
-        const f32x4 Zp = P - mmt<BF, false, false>(Sm, Ge, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 Zp = P - mmt<BF, true, true>(Sm, Ge, f32x4{0.f, 0.f, 0.f, 0.f});
         f32x4 Zo;
         if (ln) {
             f32x4 mu, rs;
