@@ -169,8 +169,8 @@ def test_linear_step_replays_continue_the_state(dev):
     # the graph's call runs at the position of its first replay; chunk 3 = n makes
     # every call start a chunk, so each replay is the same call on the next state
     g = capture(lambda: ttt.linear_step(K, Q, V, eta, Wg, Gg, pos, n, Z=Zg))
-    # capture() ran the call twice (warm-up and capture do not both advance:
-    # the capture only records), so restart both states from W0
+    # capture() ran the call once eagerly (its warm-up) and only recorded it
+    # afterwards: restart both states from W0
     Wg.copy_(a["W0"])
     Gg.zero_()
     torch.cuda.synchronize()
@@ -180,3 +180,70 @@ def test_linear_step_replays_continue_the_state(dev):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(Zg, Ze) and torch.equal(Wg, We) and torch.equal(Gg, Ge), r
+
+
+def replay_equal(dev, call, outs):
+    """Eager call, then capture and three replays that must equal it bit for bit."""
+    import torch
+    call()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    g = capture(call)
+    for r in range(REPLAYS):
+        nan_fill(*outs)
+        eager_noise(dev)
+        g.replay()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, ref):
+            assert torch.equal(o, e), "replay %d differs" % r
+    return ref
+
+
+def test_mlp_fwd_replays(dev):
+    import torch
+    wl = inputs.workload("mlp_b16_4x16").with_(B=2, H=2, T=40)
+    x = inputs.make_inputs(wl, 905)
+    a = device_inputs(wl, x, dev)
+    Z = torch.empty_like(a["K"])
+    W1, W2 = torch.empty_like(a["W1"]), torch.empty_like(a["W2"])
+    b1, b2 = torch.empty_like(a["b1"]), torch.empty_like(a["b2"])
+    say("case", wl, "plan", ttt.plan_name(ttt.mlp_select_plan(wl.B, wl.H, wl.T, wl.d, wl.chunk, 1)))
+    replay_equal(dev, lambda: ttt.mlp_fwd(a["K"], a["Q"], a["V"], a["eta"], a["W1"], a["b1"],
+                                          a["W2"], a["b2"], wl.chunk,
+                                          eta_scalar=x["eta_scalar"], Z=Z, W1_out=W1,
+                                          b1_out=b1, W2_out=W2, b2_out=b2),
+                 [Z, W1, b1, W2, b2])
+
+
+def test_linear_fwd_varlen_replays(dev):
+    import torch
+    H, d, chunk = 3, 64, 16
+    lengths = [37, 5, 64, 20]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    total_T = int(cu[-1])
+    g = torch.Generator().manual_seed(906)
+    K, Q, V = (torch.randn(H, total_T, d, generator=g).to(torch.bfloat16).to(dev)
+               for _ in range(3))
+    eta = (0.05 * torch.rand(H, total_T, generator=g)).to(dev)
+    W0 = (0.02 * torch.randn(len(lengths), H, d, d, generator=g)).to(dev)
+    cu_d = torch.from_numpy(cu).to(dev)
+    Z, W = torch.zeros_like(K), torch.empty_like(W0)
+    replay_equal(dev, lambda: ttt.linear_fwd_varlen(K, Q, V, eta, W0, cu_d, chunk, Z=Z,
+                                                    W_out=W), [Z, W])
+
+
+def test_linear_fwd_momentum_replays(dev):
+    import torch
+    wl = wl_small(64, 128, "bf16", 300)
+    x = inputs.make_inputs(wl, 907)
+    a = device_inputs(wl, x, dev)
+    Mom0 = torch.zeros_like(a["W0"])
+    plan = ttt.linear_select_plan(wl.B, wl.H, wl.T, wl.d, wl.chunk, 1,
+                                  read_mode=ttt.READ_CHUNK_START)
+    nbytes = ttt.linear_workspace_bytes(wl.B, wl.H, wl.T, wl.d, wl.chunk, 1, plan)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    say("case", wl, "plan", ttt.plan_name(plan))
+    Z, W, M = torch.empty_like(a["K"]), torch.empty_like(a["W0"]), torch.empty_like(a["W0"])
+    replay_equal(dev, lambda: ttt.linear_fwd_momentum(a["K"], a["Q"], a["V"], a["eta"], a["W0"],
+                                                      Mom0, 0.9, wl.chunk, Z=Z, W_out=W,
+                                                      Mom_out=M, workspace=ws), [Z, W, M])
