@@ -26,7 +26,8 @@
 // the output features for D: the fp32 state keeps it with the output feature in
 // the lanes, and D takes the LDS transpose of its fp16 tiles each chunk.  Sums
 // over all 256 hidden units (E, A^T A', W2 A') are formed as per-wave partials
-// and added through LDS; two barriers per chunk.  A, A' and E change orientation
+// and added through LDS behind one barrier per chunk (the next chunk's H and E are
+// read beside this chunk's Z, see the main loop).  A, A' and E change orientation
 // through the LDS transpose read as well.  The next chunk's inputs are loaded
 // while the current one is processed.
 //
