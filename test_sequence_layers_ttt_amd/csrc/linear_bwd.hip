@@ -131,9 +131,9 @@ __device__ __forceinline__ void load_vec(const uint16_t* p, float* out)
 // Waves per workgroup: each owns NB / NW of the d/16 column blocks.  With few
 // (sequence, 16-row block) units the waves split a unit's work across SIMDs;
 // once the units fill the compute units, one wave per unit (bf16 products, at
-// d = 64) avoids the cross-wave sums and barriers.  Measured on MI355X: 8x12
-// heads (384 units) 0.598 -> 0.563 ms with one wave; 1x32 heads (128 units)
-// 6.44 -> 7.32 ms, so there the four-wave split stays.
+// d = 64) avoids the cross-wave sums and barriers.  Measured on MI355X with bf16
+// I/O at d = 64: 8x12 heads (384 units) 0.598 -> 0.563 ms with one wave instead
+// of four; 1x32 heads (128 units) 6.44 ms with four, 7.32 with one, 5.59 with two.
 template <int D>
 constexpr int bwd_waves()
 {
@@ -618,7 +618,7 @@ hipError_t launch_typed(const LinearBwdArgs& a, hipStream_t s)
     };
     if constexpr (!F32 && D == 64) {
         if ((long)a.BH * NB >= kComputeUnits) launch(std::integral_constant<int, 1>{});
-        else launch(std::integral_constant<int, bwd_waves<D>()>{});
+        else launch(std::integral_constant<int, 2>{});   // two waves per unit
     } else {
         launch(std::integral_constant<int, bwd_waves<D>()>{});
     }
