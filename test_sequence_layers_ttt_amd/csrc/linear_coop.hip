@@ -1,5 +1,6 @@
-// TTT-Linear forward scan, chunks of exactly 16 tokens, one workgroup per
-// (batch, head): d/16 waves, wave w owning state rows 16w .. 16w+15.
+// TTT-Linear forward scan, chunks of exactly 16 tokens: each (batch, head) is
+// split over d/16 / WPG workgroups of WPG waves, wave w of part p owning state
+// rows 16 (p WPG + w) .. + 15.
 //
 // Same chunk arithmetic as the single-wave chunk kernel (linear_mfma.hip): with
 // F_c = -diag(eta) E_c (token-row layout, PaperTrace "5 · TestingTime 训练与长上下文"
@@ -15,7 +16,9 @@
 // register ring eight chunks deep -- into a ring of four swizzled LDS tiles, and
 // every wave reads its operands from there (row reads; the transpose read gives K
 // with the feature in the lanes for the state update).  V and eta are loaded per
-// wave.
+// wave.  The parts of one head run on one XCD, so a tile fetched by one part is
+// served to the other from that XCD's L2 (the HBM traffic stays one fetch per
+// tile).
 //
 // Tiles are staged in groups of kGroup chunks into a ring three groups deep: a
 // chunk's tile is stored eight steps before it is needed, so one barrier per
@@ -33,20 +36,25 @@ namespace ttt {
 namespace {
 
 enum { kCoopEtaScalar = 0, kCoopEtaToken = 1, kCoopEtaToken4 = 2 };
+constexpr long kComputeUnits = 256;   // MI355X
 
-template <int D, int ETA, bool FULL>
-__global__ __launch_bounds__(4 * D) void linear_coop_kernel(
+template <int D, int WPG, int ETA, bool FULL>
+__global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
-    const float* W0, uint16_t* __restrict__ Z, float* W_out, int T)
+    const float* W0, uint16_t* __restrict__ Z, float* W_out, int BH, int T)
 {
     constexpr int NB = D / 16;
     constexpr int NM = D / 32;
-    constexpr int G = D / 8;     // 16-byte granules per row
-    // chunks per barrier (d = 128: eight waves per workgroup leave 256 registers
-    // per wave, so shorter rings)
-    constexpr int kGroup = D >= 128 ? 2 : 4;
-    constexpr int P = 2 * kGroup;   // chunks whose granule a thread holds in registers
+    constexpr int G = D / 8;           // 16-byte granules per row
+    constexpr int NT = 64 * WPG;       // threads per workgroup
+    constexpr int GPT = 32 * G / NT;   // granules of a chunk's K and Q tiles per thread
+    constexpr int PARTS = NB / WPG;    // workgroups per head
+    static_assert(NB % WPG == 0 && GPT >= 1 && GPT * NT == 32 * G, "tile split");
+    // chunks per barrier (eight waves per workgroup leave 256 registers per wave,
+    // so shorter rings)
+    constexpr int kGroup = WPG >= 8 ? 2 : 4;
+    constexpr int P = 2 * kGroup;   // chunks whose granules a thread holds in registers
     constexpr int kSlots = 3 * kGroup;
     __shared__ KQTile16<D> L[kSlots];
 
@@ -54,10 +62,17 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
-    const int slice = blockIdx.x;
+    int slice, part;
+    if constexpr (PARTS == 1) {
+        slice = blockIdx.x;
+        part = 0;
+    } else {
+        xcd_unit_part(blockIdx.x, PARTS, slice, part);
+        if (slice >= BH) return;
+    }
     const size_t tok0 = (size_t)slice * T;
     const int nch = (T + 15) / 16;
-    const int out0 = 16 * wave;
+    const int out0 = 16 * (part * WPG + wave);
     // token of row r of chunk ch, clamped into the sequence (a clamped row is a
     // re-read; its token gets eta = 0 and no store)
     auto tok = [&](int ch, int r) {
@@ -66,12 +81,17 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
         return FULL ? t : (t < T ? t : T - 1);
     };
 
-    // this thread's granule of each staged tile: K for the first half of the
-    // workgroup, Q for the second
-    const int which = tid / (16 * G);
-    const int grow = (tid / G) & 15, ggr = tid % G;
-    const uint16_t* src = which ? Q : K;
-    const int lpos = grow * G + (ggr ^ tile16_swizzle<D>(grow));
+    // this thread's granules of each staged tile: granule tid + i NT of the 32 G
+    // granules of K (the first 16 G) and Q
+    int which[GPT], grow[GPT], ggr[GPT], lpos[GPT];
+#pragma unroll
+    for (int i = 0; i < GPT; ++i) {
+        const int idx = tid + i * NT;
+        which[i] = idx / (16 * G);
+        grow[i] = (idx / G) & 15;
+        ggr[i] = idx % G;
+        lpos[i] = grow[i] * G + (ggr[i] ^ tile16_swizzle<D>(grow[i]));
+    }
     // first token of chunk ch (clamped), as a wave-uniform base; lanes add a
     // 32-bit offset within the chunk
     auto chunk_base = [&](int ch) {
@@ -83,9 +103,15 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
         const int cc = ch < nch ? ch : nch - 1;
         return 16 * cc + r < T ? r : T - 1 - 16 * cc;
     };
-    auto gload = [&](int ch) {
-        const uint16_t* b = src + chunk_base(ch) * D;
-        return *(const u32x4*)(b + (row_in(ch, grow) * D + 8 * ggr));
+    auto gload = [&](u32x4 (&r)[GPT], int ch) {
+        const size_t base = chunk_base(ch) * D;
+#pragma unroll
+        for (int i = 0; i < GPT; ++i)
+            r[i] = *(const u32x4*)((which[i] ? Q : K) + base + (row_in(ch, grow[i]) * D + 8 * ggr[i]));
+    };
+    auto gstore = [&](KQTile16<D>& t, const u32x4 (&r)[GPT]) {
+#pragma unroll
+        for (int i = 0; i < GPT; ++i) t.g[which[i]][lpos[i]] = r[i];
     };
     auto vload = [&](int ch) {
         const uint16_t* b = V + chunk_base(ch) * D;
@@ -127,19 +153,19 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
     // chunk X lives in LDS slot X % kSlots.  Tiles of chunks 0 .. 2*kGroup-1 are
     // stored up front; during chunk ch the tile of chunk ch + P is stored and the
     // granule of chunk ch + 2P loaded (into the register slot it came from).
-    u32x4 rg[P];
+    u32x4 rg[P][GPT];
     u32x2 rv[P];
     f32x4 re[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        rg[p] = gload(p);
+        gload(rg[p], p);
         rv[p] = vload(p);
         re[p] = eload(p);
     }
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        L[p].g[which][lpos] = rg[p];
-        rg[p] = gload(P + p);
+        gstore(L[p], rg[p]);
+        gload(rg[p], P + p);
     }
     __syncthreads();
 
@@ -156,8 +182,8 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
     auto step = [&](int ch, auto pc) {
         constexpr int p = decltype(pc)::value;
         // stage chunk ch + P, refill its register slot with chunk ch + 2P
-        if (ch + P < nch) L[(ch + P) % kSlots].g[which][lpos] = rg[p];
-        rg[p] = gload(ch + 2 * P);
+        if (ch + P < nch) gstore(L[(ch + P) % kSlots], rg[p]);
+        gload(rg[p], ch + 2 * P);
 
         const int sl = ch % kSlots;
         const u32x4* Kc = L[sl].g[0];
@@ -262,27 +288,41 @@ __global__ __launch_bounds__(4 * D) void linear_coop_kernel(
     }
 }
 
-template <int D, int ETA, bool FULL>
+template <int D, int WPG, int ETA, bool FULL>
 void launch_cfg(const LinearArgs& a, hipStream_t s)
 {
-    hipLaunchKernelGGL((linear_coop_kernel<D, ETA, FULL>), dim3((unsigned)a.BH), dim3(4 * D), 0,
+    constexpr int parts = D / 16 / WPG;
+    const unsigned grid = parts == 1 ? (unsigned)a.BH : (unsigned)((a.BH + 7) / 8 * 8 * parts);
+    hipLaunchKernelGGL((linear_coop_kernel<D, WPG, ETA, FULL>), dim3(grid), dim3(64 * WPG), 0,
                        s, (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V, a.eta,
-                       a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.T);
+                       a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.BH, a.T);
 }
 
-template <int D>
-hipError_t launch_d(const LinearArgs& a, hipStream_t s)
+template <int D, int WPG>
+void launch_eta(const LinearArgs& a, hipStream_t s)
 {
     const bool full = a.T % 16 == 0;
     const bool eta4 = a.eta && full && reinterpret_cast<uintptr_t>(a.eta) % 16 == 0;
     if (full) {
-        if (!a.eta) launch_cfg<D, kCoopEtaScalar, true>(a, s);
-        else if (eta4) launch_cfg<D, kCoopEtaToken4, true>(a, s);
-        else launch_cfg<D, kCoopEtaToken, true>(a, s);
+        if (!a.eta) launch_cfg<D, WPG, kCoopEtaScalar, true>(a, s);
+        else if (eta4) launch_cfg<D, WPG, kCoopEtaToken4, true>(a, s);
+        else launch_cfg<D, WPG, kCoopEtaToken, true>(a, s);
     } else {
-        if (!a.eta) launch_cfg<D, kCoopEtaScalar, false>(a, s);
-        else launch_cfg<D, kCoopEtaToken, false>(a, s);
+        if (!a.eta) launch_cfg<D, WPG, kCoopEtaScalar, false>(a, s);
+        else launch_cfg<D, WPG, kCoopEtaToken, false>(a, s);
     }
+}
+
+// Waves per workgroup, measured on MI355X at T = 2048: a d = 128 head runs as two
+// workgroups of four waves while they find a compute unit each (4x12 heads:
+// 71.8 us against 106.4 us with eight waves; 8x12: 84.8 against 113.2).  Four
+// waves is the floor: two-wave workgroups measured no faster at d = 64 (8x12
+// heads: 50.5 against 50.1 us) or d = 128 (4x12: 74.0 us).
+template <int D>
+hipError_t launch_d(const LinearArgs& a, hipStream_t s)
+{
+    if (D >= 128 && a.BH * 2 > kComputeUnits) launch_eta<D, D / 16>(a, s);
+    else launch_eta<D, 4>(a, s);
     return hipGetLastError();
 }
 
