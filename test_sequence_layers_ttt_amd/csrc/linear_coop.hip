@@ -20,13 +20,16 @@
 // served to the other from that XCD's L2 (the HBM traffic stays one fetch per
 // tile).
 //
-// Tiles are staged in groups of kGroup chunks into a ring three groups deep: a
-// chunk's tile is stored eight steps before it is needed, so one barrier per
-// group suffices, and the K rows of chunk c+2 are read into registers during
-// chunk c, keeping LDS latency off the chunk-to-chunk chain.
+// Tiles are staged P = 2 kGroup chunks ahead into a ring of 2P LDS slots, with
+// one barrier per kGroup chunks: a slot is rewritten only once every wave has
+// passed the chunks that read it.  The loop is unrolled over the whole ring, so
+// every slot address is a compile-time offset.  The K rows of chunk c+2 are read
+// into registers during chunk c, keeping LDS latency off the chunk-to-chunk
+// chain.
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 #include "launch.h"
@@ -36,6 +39,13 @@ namespace ttt {
 namespace {
 
 enum { kCoopEtaScalar = 0, kCoopEtaToken = 1, kCoopEtaToken4 = 2 };
+
+// f(integral_constant<int, I>) for I = 0, 1, ... in order
+template <typename F, int... I>
+__device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
 constexpr long kComputeUnits = 256;   // MI355X
 
 template <int D, int WPG, int ETA, bool FULL>
@@ -55,7 +65,7 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
     // so shorter rings)
     constexpr int kGroup = WPG >= 8 ? 2 : 4;
     constexpr int P = 2 * kGroup;   // chunks whose granules a thread holds in registers
-    constexpr int kSlots = 3 * kGroup;
+    constexpr int kSlots = 2 * P;   // > P + kGroup: chunks ch - kGroup .. ch + 2 stay
     __shared__ KQTile16<D> L[kSlots];
 
     const int tid = threadIdx.x;
@@ -150,7 +160,7 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
     for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
     const u32x2 I16 = identity_b16(lane);
 
-    // chunk X lives in LDS slot X % kSlots.  Tiles of chunks 0 .. 2*kGroup-1 are
+    // chunk X lives in LDS slot X % kSlots.  Tiles of chunks 0 .. P-1 are
     // stored up front; during chunk ch the tile of chunk ch + P is stored and the
     // granule of chunk ch + 2P loaded (into the register slot it came from).
     u32x4 rg[P][GPT];
@@ -179,13 +189,22 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
     for (int m = 0; m < NM; ++m) Et = mfma32(kb[0][m], Mf[m], Et);
 
     // one chunk; p = ch % P is a compile-time ring position
-    auto step = [&](int ch, auto pc) {
-        constexpr int p = decltype(pc)::value;
+    // 16-deep products as 32-deep ones whose lower half is zero in one operand
+    // (the other holds the identity there): these tuples live across the loop,
+    // their lower halves never written, so no zeros are moved in per product
+    u32x4 ktz[NB], smz = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) ktz[jb] = u32x4{0u, 0u, 0u, 0u};
+
+    // one chunk; k = ch % kSlots is a compile-time ring position
+    auto step = [&](int ch, auto kc_) {
+        constexpr int k = decltype(kc_)::value;
+        constexpr int p = k % P;
         // stage chunk ch + P, refill its register slot with chunk ch + 2P
-        if (ch + P < nch) gstore(L[(ch + P) % kSlots], rg[p]);
+        if (ch + P < nch) gstore(L[(k + P) % kSlots], rg[p]);
         gload(rg[p], ch + 2 * P);
 
-        const int sl = ch % kSlots;
+        constexpr int sl = k;
         const u32x4* Kc = L[sl].g[0];
         const u32x4* Qc = L[sl].g[1];
         constexpr int pe = p & 1;   // ch & 1 (the ring length is even)
@@ -193,8 +212,8 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
         u32x4 (&kn)[NM] = kb[pe ^ 1];
         u32x4 qc[NM];
         row_operand(Qc, qc);
-        // K_c with the feature in the lanes (A operand of the state update)
-        u32x2 kt[NB];
+        // K_c with the feature in the lanes (A operand of the state update), in
+        // the upper half of the zero-padded operands
         {
             const int r = (lane >> 2) & 3, q = lane & 3;
             const int row = 4 * g + r;
@@ -203,7 +222,9 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
             for (int jb = 0; jb < NB; ++jb) {
                 auto pt = (__attribute__((address_space(3))) s16x4*)(
                     base + 2 * ((4 * (jb >> 1) + q) ^ tile16_swizzle<D>(row)) + (jb & 1));
-                kt[jb] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(pt));
+                const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(pt));
+                ktz[jb].z = t.x;
+                ktz[jb].w = t.y;
             }
         }
         f32x4 et = re[p];
@@ -216,6 +237,7 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
         }
         // F_c = -diag(eta) E_c: the only value the next chunk waits for
         const u32x2 F = pack_bf16x4(-et * Et);
+        const u32x4 IF = {I16.x, I16.y, F.x, F.y};
         // E_{c+1} = K_{c+1} W_c^T + [-V_{c+1} | G_c] [I ; F_c]
         {
             f32x4 Gt = {0, 0, 0, 0};
@@ -226,11 +248,11 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
 #pragma unroll
             for (int m = 0; m < NM; ++m) Pt = mfma32(kn[m], Mf[m], Pt);
             const u32x2 vneg = rv[(p + 1) % P] ^ u32x2{0x80008000u, 0x80008000u};
-            Et = mfma32(u32x4{vneg.x, vneg.y, Gb.x, Gb.y}, u32x4{I16.x, I16.y, F.x, F.y}, Pt);
+            Et = mfma32(u32x4{vneg.x, vneg.y, Gb.x, Gb.y}, IF, Pt);
         }
-        // W_{c+1} = W_c + F_c^T K_c
+        // W_{c+1} = W_c + F_c^T K_c: [0 | K_c^T] [I ; F_c]
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) M[jb] = mfma16(kt[jb], F, M[jb]);
+        for (int jb = 0; jb < NB; ++jb) M[jb] = mfma32(ktz[jb], IF, M[jb]);
         // Z_c = Q_c W_c^T + causal scores times F_c
         f32x4 St = {0, 0, 0, 0};
 #pragma unroll
@@ -243,7 +265,12 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
         f32x4 Zt = {0, 0, 0, 0};
 #pragma unroll
         for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[m], qc[m], Zt);
-        Zt = mfma16(F, pack_bf16x4(Sm), Zt);
+        {   // + [I | F_c^T] [0 ; causal scores]
+            const u32x2 sb = pack_bf16x4(Sm);
+            smz.z = sb.x;
+            smz.w = sb.y;
+            Zt = mfma32(IF, smz, Zt);
+        }
         if (FULL || 16 * ch + c < T) {
             uint16_t* zb = Z + (tok0 + (size_t)16 * ch) * D;
             *(u32x2*)(zb + (c * D + out0 + 4 * g)) = pack_bf16x4(Zt);
@@ -251,34 +278,18 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
 #pragma unroll
         for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
         // K_{c+2} into the set K_c leaves (stale, unused, past the end)
-        row_operand(L[(ch + 2) % kSlots].g[0], kc);
+        row_operand(L[(k + 2) % kSlots].g[0], kc);
         rv[p] = vload(ch + P);
         re[p] = eload(ch + P);
         if (p % kGroup == kGroup - 1) __syncthreads();
     };
 
     int c0 = 0;
-    for (; c0 + P <= nch; c0 += P) {
-        step(c0 + 0, std::integral_constant<int, 0>{});
-        step(c0 + 1, std::integral_constant<int, 1>{});
-        step(c0 + 2, std::integral_constant<int, 2>{});
-        step(c0 + 3, std::integral_constant<int, 3>{});
-        if constexpr (P == 8) {
-            step(c0 + 4, std::integral_constant<int, 4 % P>{});
-            step(c0 + 5, std::integral_constant<int, 5 % P>{});
-            step(c0 + 6, std::integral_constant<int, 6 % P>{});
-            step(c0 + 7, std::integral_constant<int, 7 % P>{});
-        }
-    }
-    if (c0 + 0 < nch) step(c0 + 0, std::integral_constant<int, 0>{});
-    if (c0 + 1 < nch) step(c0 + 1, std::integral_constant<int, 1>{});
-    if (c0 + 2 < nch) step(c0 + 2, std::integral_constant<int, 2>{});
-    if constexpr (P == 8) {
-        if (c0 + 3 < nch) step(c0 + 3, std::integral_constant<int, 3>{});
-        if (c0 + 4 < nch) step(c0 + 4, std::integral_constant<int, 4 % P>{});
-        if (c0 + 5 < nch) step(c0 + 5, std::integral_constant<int, 5 % P>{});
-        if (c0 + 6 < nch) step(c0 + 6, std::integral_constant<int, 6 % P>{});
-    }
+    for (; c0 + kSlots <= nch; c0 += kSlots)
+        unroll_seq([&](auto k) { step(c0 + k, k); }, std::make_integer_sequence<int, kSlots>{});
+    unroll_seq([&](auto k) {
+        if (c0 + k < nch) step(c0 + k, k);
+    }, std::make_integer_sequence<int, kSlots - 1>{});
 
     float* w = W_out + (size_t)slice * D * D + (size_t)(out0 + c) * D;
 #pragma unroll
