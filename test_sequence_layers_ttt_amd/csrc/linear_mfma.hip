@@ -88,6 +88,67 @@ __device__ __forceinline__ void load_tile(Tile<D, RB>& t, const uint16_t* __rest
     }
 }
 
+// One slice's K, Q, V, eta and Z as buffer resources, with this lane's byte
+// offset within a 16-token tile: K and Q row c at features 8g (+ 32m), V and Z row
+// c at the wave's features out0 + 4g (+ 16r), eta 4g.  Loads and stores of whole
+// tiles then put the tile's start in the scalar offset and need no vector address
+// arithmetic.  The scalar offset is not part of the buffer's range check, so
+// only tiles inside the slice are addressed this way, and the slice must span
+// less than 2^31 bytes (T d 2).
+struct SliceBuffers {
+    __amdgpu_buffer_rsrc_t k, q, v, e, z;
+    int kq, vo, eo;
+};
+
+constexpr int kRawBufferFlags = 0x00020000;   // dword 3 of a gfx9 buffer resource: raw 32-bit data
+
+template <int D>
+__device__ __forceinline__ SliceBuffers slice_buffers(const uint16_t* K, const uint16_t* Q,
+                                                      const uint16_t* V, const float* eta,
+                                                      uint16_t* Z, size_t tok0, int T, int out0,
+                                                      int lane)
+{
+    const int c = lane & 15, g = lane >> 4;
+    const int bytes = (int)min((long long)T * D * 2, 0x7fffffffLL);
+    SliceBuffers b;
+    b.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(K + tok0 * D), 0, bytes,
+                                            kRawBufferFlags);
+    b.q = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Q + tok0 * D), 0, bytes,
+                                            kRawBufferFlags);
+    b.v = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(V + tok0 * D), 0, bytes,
+                                            kRawBufferFlags);
+    b.z = __builtin_amdgcn_make_buffer_rsrc(Z + tok0 * D, 0, bytes, kRawBufferFlags);
+    b.e = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(eta ? eta + tok0 : nullptr), 0,
+                                            eta ? T * 4 : 0, kRawBufferFlags);
+    b.kq = (c * D + 8 * g) * 2;
+    b.vo = (c * D + out0 + 4 * g) * 2;
+    b.eo = 16 * g;
+    return b;
+}
+
+// load_tile for a whole tile starting at token s0 of the slice (inside it)
+template <int D, int ETA, int RB>
+__device__ __forceinline__ void load_tile_full(Tile<D, RB>& t, const SliceBuffers& b, int s0)
+{
+    const int so = s0 * D * 2;
+    t.n = 16;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) {
+        t.k[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b.k, b.kq + 64 * m, so, 0));
+        t.q[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b.q, b.kq + 64 * m, so, 0));
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+        t.v[r] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(b.v, b.vo + 32 * r, so, 0));
+    if (ETA == kEtaToken4) {
+        t.eta = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(b.e, b.eo, s0 * 4, 0));
+    } else if (ETA == kEtaToken) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            t.eta[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(b.e, b.eo + 4 * i, s0 * 4, 0));
+    }
+}
+
 // K of one sub-tile, re-laid out in LDS as d/16 row-major 16 x 16 bf16 blocks
 // (block jb holds K[token][pi(jb, 0..15)], 512 bytes), then read back with the
 // gfx950 transpose read: in each 16-lane group, lanes 4r..4r+3 supply row r
@@ -111,6 +172,22 @@ __device__ __forceinline__ void transpose_k(u32x2 (&kt)[D / 16], const Tile<D, R
         kt[jb] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
     }
     asm volatile("" ::: "memory");
+}
+
+// The same transpose into the upper halves of 32-deep operands whose lower halves
+// stay zero: [0 | K^T] [I ; F] is the 16-deep product K^T F, and tuples that live
+// across the loop keep their zeros without a move per product.
+template <int D, int RB>
+__device__ __forceinline__ void transpose_k_hi(u32x4 (&ktz)[D / 16], const Tile<D, RB>& t,
+                                               u32x2* lds, int lane)
+{
+    u32x2 kt[D / 16];
+    transpose_k<D>(kt, t, lds, lane);
+#pragma unroll
+    for (int jb = 0; jb < D / 16; ++jb) {
+        ktz[jb].z = kt[jb].x;
+        ktz[jb].w = kt[jb].y;
+    }
 }
 
 // The unit is one (batch, head) sequence and one 16-row block of its state.
@@ -306,12 +383,14 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
     }
     const u32x2 I16 = identity_b16(lane);
 
+    const SliceBuffers sres = slice_buffers<D>(K, Q, V, eta, Z, tok0, T, out0, lane);
     Tile<D, RB> buf[PF];
 #pragma unroll
     for (int p = 0; p < PF; ++p) {
         const int s0 = p * step;
         const int n = s0 < T ? min(step, T - s0) : 0;
-        load_tile<D, ETA, FULL, RB>(buf[p], K, Q, V, eta, tok0, n > 0 ? s0 : 0, n, out0, lane);
+        if constexpr (FULL) load_tile_full<D, ETA, RB>(buf[p], sres, n > 0 ? s0 : 0);
+        else load_tile<D, ETA, FULL, RB>(buf[p], K, Q, V, eta, tok0, n > 0 ? s0 : 0, n, out0, lane);
     }
 
     // prologue: E_0 = K_0 W_0^T - V_0 directly
@@ -326,8 +405,11 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
 #pragma unroll
         for (int m = 0; m < NM; ++m) Et[r] = mfma32(buf[0].k[m], Mf[r][m], Et[r]);
     }
-    u32x2 kt[NB];
-    transpose_k<D>(kt, buf[0], lds_kt, lane);
+    u32x4 ktz[NB];
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) ktz[jb] = u32x4{0u, 0u, 0u, 0u};
+    transpose_k_hi<D>(ktz, buf[0], lds_kt, lane);
+    u32x4 smz = {0u, 0u, 0u, 0u};   // causal scores in the upper half
 
     // One chunk.  Work for the next chunk (Gram term, bracket, transposed K, bf16
     // state) is done unconditionally: after the last chunk the next tile is a
@@ -347,9 +429,12 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
             et.w = (4 * g + 3 < cur.n) ? et.w : 0.f;
         }
         // F_c = -diag(eta) E_c (bf16): the only value the next chunk waits for
-        u32x2 F[RB];
+        u32x4 IF[RB];   // [I ; F_c]
 #pragma unroll
-        for (int r = 0; r < RB; ++r) F[r] = pack_bf16x4(-et * Et[r]);
+        for (int r = 0; r < RB; ++r) {
+            const u32x2 F = pack_bf16x4(-et * Et[r]);
+            IF[r] = u32x4{I16.x, I16.y, F.x, F.y};
+        }
         // E_{c+1} = K_{c+1} W_c^T + [-V_{c+1} | G_c] [I ; F_c]
         {
             f32x4 Gt = {0, 0, 0, 0};
@@ -362,15 +447,14 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
 #pragma unroll
                 for (int m = 0; m < NM; ++m) P = mfma32(nxt.k[m], Mf[r][m], P);
                 const u32x2 vneg = nxt.v[r] ^ u32x2{0x80008000u, 0x80008000u};
-                Et[r] = mfma32(u32x4{vneg.x, vneg.y, G.x, G.y}, u32x4{I16.x, I16.y, F[r].x, F[r].y},
-                               P);
+                Et[r] = mfma32(u32x4{vneg.x, vneg.y, G.x, G.y}, IF[r], P);
             }
         }
         // W_{c+1} = W_c + F_c^T K_c, block by block
 #pragma unroll
         for (int r = 0; r < RB; ++r)
 #pragma unroll
-            for (int jb = 0; jb < NB; ++jb) M[r][jb] = mfma16(kt[jb], F[r], M[r][jb]);
+            for (int jb = 0; jb < NB; ++jb) M[r][jb] = mfma32(ktz[jb], IF[r], M[r][jb]);
         // Z_c = Q_c W_c^T - causal (eta-weighted) scores times E_c
         f32x4 St = {0, 0, 0, 0};
 #pragma unroll
@@ -380,19 +464,26 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
         Sm.y = (4 * g + 1 <= c) ? St.y : 0.f;
         Sm.z = (4 * g + 2 <= c) ? St.z : 0.f;
         Sm.w = (4 * g + 3 <= c) ? St.w : 0.f;
-        const u32x2 Sb = pack_bf16x4(Sm);
+        {
+            const u32x2 Sb = pack_bf16x4(Sm);
+            smz.z = Sb.x;
+            smz.w = Sb.y;
+        }
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             f32x4 Zt = {0, 0, 0, 0};
 #pragma unroll
             for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[r][m], cur.q[m], Zt);
-            Zt = mfma16(F[r], Sb, Zt);
-            if (TF || c < cur.n) {
+            Zt = mfma32(IF[r], smz, Zt);   // + [I | F_c^T] [0 ; scores]
+            if constexpr (FULL) {
+                __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(Zt), sres.z, sres.vo + 32 * r,
+                                                      s0 * D * 2, 0);
+            } else if (TF || c < cur.n) {
                 const u32x2 zb = pack_bf16x4(Zt);
                 *(u32x2*)(Z + (tok0 + s0 + c) * D + out0 + 16 * r + 4 * g) = zb;
             }
         }
-        transpose_k<D>(kt, nxt, lds_kt, lane);
+        transpose_k_hi<D>(ktz, nxt, lds_kt, lane);
 #pragma unroll
         for (int r = 0; r < RB; ++r)
 #pragma unroll
@@ -401,7 +492,8 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
     auto refill = [&](Tile<D, RB>& slot, int tau) {
         const int s1 = tau * step;
         const int n = s1 < T ? min(step, T - s1) : 0;
-        load_tile<D, ETA, FULL, RB>(slot, K, Q, V, eta, tok0, n > 0 ? s1 : 0, n, out0, lane);
+        if constexpr (FULL) load_tile_full<D, ETA, RB>(slot, sres, n > 0 ? s1 : 0);
+        else load_tile<D, ETA, FULL, RB>(slot, K, Q, V, eta, tok0, n > 0 ? s1 : 0, n, out0, lane);
     };
     // a tile known to hold 16 tokens: unclamped loads
     auto refill_whole = [&](Tile<D, RB>& slot, int tau) {
@@ -519,7 +611,9 @@ hipError_t launch_d(const LinearArgs& a, hipStream_t s)
         return hipGetLastError();
     }
     // every sub-tile holds 16 tokens: no padding logic at all
-    const bool full = a.chunk % kStep == 0 && a.T % kStep == 0;
+    // (whole-tile loads address a slice through 32-bit byte offsets)
+    const bool full = a.chunk % kStep == 0 && a.T % kStep == 0 &&
+                      (long long)a.T * a.d * 2 <= 0x7fffffffLL;
     const bool eta4 = a.eta && full && (reinterpret_cast<uintptr_t>(a.eta) % 16 == 0) &&
                       a.T % 4 == 0;
     if (full) {
