@@ -404,11 +404,20 @@ __global__ __launch_bounds__(4 * D / RB) void bigchunk_seg_kernel(
     }
     __syncthreads();
 
-    // one sub-tile; p = tau % P is a compile-time ring position
+    // 16-deep products as 32-deep ones whose upper half is zero in one operand
+    // and finite in the other: these tuples live across the loop with their zero
+    // halves never written, so no zeros are moved in per product
+    u32x4 ktz[NB], smz = {0u, 0u, 0u, 0u}, vz = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) ktz[jb] = u32x4{0u, 0u, 0u, 0u};
+    const u32x4 II = {I16.x, I16.y, I16.x, I16.y};
+
+    // one sub-tile; p = tau % P is a compile-time ring position (tau - p is a
+    // multiple of the even P, so the LDS slot tau & 1 is p & 1)
     auto step = [&](int tau, auto pc) {
         constexpr int p = decltype(pc)::value;
         constexpr int p1 = (p + 1) % P;
-        const int sl = tau & 1;
+        constexpr int sl = p & 1;
         // stage the next sub-tile, refill its register slots
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
@@ -442,7 +451,7 @@ __global__ __launch_bounds__(4 * D / RB) void bigchunk_seg_kernel(
         }
         // K with the feature in the lanes: supplying lane (r, q) of group g reads
         // the 8 bytes K[4g + r][32m + 8q + 4h .. +3] of block jb = 2m + h
-        u32x2 kt[NB];
+        // (upper halves of ktz: [0 | K^T] [I ; F] = K^T F)
         {
             const int r = (lane >> 2) & 3, q = lane & 3;
             const int row = 4 * g + r;
@@ -452,7 +461,9 @@ __global__ __launch_bounds__(4 * D / RB) void bigchunk_seg_kernel(
                 const int m = jb >> 1, h = jb & 1;
                 auto pt = (__attribute__((address_space(3))) s16x4*)(
                     base + 2 * ((4 * m + q) ^ tile16_swizzle<D>(row)) + h);
-                kt[jb] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(pt));
+                const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(pt));
+                ktz[jb].z = t.x;
+                ktz[jb].w = t.y;
             }
         }
         const int n = FULL ? 16 : min(16, nc - 16 * tau);
@@ -472,26 +483,35 @@ __global__ __launch_bounds__(4 * D / RB) void bigchunk_seg_kernel(
         Sm.y = (4 * g + 1 <= c) ? St.y : 0.f;
         Sm.z = (4 * g + 2 <= c) ? St.z : 0.f;
         Sm.w = (4 * g + 3 <= c) ? St.w : 0.f;
-        const u32x2 Sb = pack_bf16x4(Sm);
+        {
+            const u32x2 Sb = pack_bf16x4(Sm);
+            smz.z = Sb.x;
+            smz.w = Sb.y;
+        }
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
             // E = K W_c^T - V (tokens in the rows, this block's outputs in the lanes)
-            f32x4 Et = mfma16(rv[p][rb] ^ u32x2{0x80008000u, 0x80008000u}, I16,
-                              f32x4{0, 0, 0, 0});
+            {
+                const u32x2 vneg = rv[p][rb] ^ u32x2{0x80008000u, 0x80008000u};
+                vz.x = vneg.x;
+                vz.y = vneg.y;
+            }
+            f32x4 Et = mfma32(vz, II, f32x4{0, 0, 0, 0});   // [-V | 0] [I ; I]
 #pragma unroll
             for (int m = 0; m < NM; ++m) Et = mfma32(kop[m], Wf[rb][m], Et);
             const u32x2 F = pack_bf16x4(-et * Et);
+            const u32x4 IF = {I16.x, I16.y, F.x, F.y};
             // Z = Q M^T + S^T-weighted F (outputs in the rows, tokens in the lanes)
             f32x4 Zt = {0, 0, 0, 0};
 #pragma unroll
             for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[rb][m], qop[m], Zt);
-            Zt = mfma16(F, Sb, Zt);
+            Zt = mfma32(IF, smz, Zt);   // + [I | F^T] [0 ; scores]
             if (FULL || c < n)
                 *(u32x2*)(Z + (tok0 + 16 * tau + c) * D + out0 + 16 * rb + 4 * g) =
                     pack_bf16x4(Zt);
             // M += F^T K
 #pragma unroll
-            for (int jb = 0; jb < NB; ++jb) M[rb][jb] = mfma16(kt[jb], F, M[rb][jb]);
+            for (int jb = 0; jb < NB; ++jb) M[rb][jb] = mfma32(ktz[jb], IF, M[rb][jb]);
 #pragma unroll
             for (int m = 0; m < NM; ++m) Mf[rb][m] = pack_bf16x8(M[rb][2 * m], M[rb][2 * m + 1]);
             rv[p][rb] = vload(tau + P, rb);
