@@ -99,9 +99,8 @@ __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int off,
 __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int off, f32x4 v,
                                               uint16_t)
 {
-    const i32x2 w = {(int)(f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16)),
-                     (int)(f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16))};
-    __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+    // hardware convert (round to nearest even): no branch for the NaN case
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, pack_bf16x4(v)), r, off, 0, 0);
 }
 
 // N consecutive elements (N a multiple of 4) widened to fp32
@@ -203,6 +202,19 @@ struct SubTile {
     bool row_ok, eta_ok;   // rows and tokens past the sub-tile stage as zeros
 };
 
+// Element i of a raw row with its storage word ANDed with m (all ones or zero):
+// zero bits widen to +0.0 in either I/O type.
+template <typename TIO, int N>
+__device__ __forceinline__ float masked_at(const RawRow<TIO, N>& r, int i, uint32_t m)
+{
+    if constexpr (sizeof(TIO) == 4) {
+        return __uint_as_float(r.w[i] & m);
+    } else {
+        const uint32_t x = r.w[i >> 1] & m;
+        return __uint_as_float((i & 1) ? (x & 0xffff0000u) : (x << 16));
+    }
+}
+
 // MULTI: chunks span several 16-token sub-tiles (the running W - G_{<sigma} is
 // needed); a compile-time choice, so that chunks of at most 16 tokens carry no
 // trace of it.
@@ -278,23 +290,25 @@ __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
         }
     };
     auto put = [&](const SubTile<TIO, D, NW>& f, bool rev, bool state) {
-        // a select, not a product: a re-read row may hold infinities
-        const bool ok = f.row_ok;
+        // Rows past the sub-tile stage as zeros through a mask on the raw words:
+        // not a product (a re-read row may hold infinities) and not a select on
+        // the values (that is compiled into a branch around the stores).
+        const uint32_t m = f.row_ok ? 0xffffffffu : 0u;
         auto four = [&](const auto& r, int i) {
-            return ok ? f32x4{r.at(i), r.at(i + 1), r.at(i + 2), r.at(i + 3)}
-                      : f32x4{0.f, 0.f, 0.f, 0.f};
+            return f32x4{masked_at(r, i, m), masked_at(r, i + 1, m), masked_at(r, i + 2, m),
+                         masked_at(r, i + 3, m)};
         };
 #pragma unroll
         for (int i = 0; i < KP; i += 4)
             *reinterpret_cast<f32x4*>(L.K + srow * S + kcol + i) = four(f.k, i);
 #pragma unroll
-        for (int i = 0; i < VP; ++i) L.V[srow * 20 + vcol + i] = ok ? f.v.at(i) : 0.f;
+        for (int i = 0; i < VP; ++i) L.V[srow * 20 + vcol + i] = masked_at(f.v, i, m);
         if (rev) {
 #pragma unroll
             for (int i = 0; i < KP; i += 4)
                 *reinterpret_cast<f32x4*>(L.Q + srow * S + kcol + i) = four(f.q, i);
 #pragma unroll
-            for (int i = 0; i < VP; ++i) L.dZ[srow * 20 + vcol + i] = ok ? f.dz.at(i) : 0.f;
+            for (int i = 0; i < VP; ++i) L.dZ[srow * 20 + vcol + i] = masked_at(f.dz, i, m);
         }
         if (state) {
 #pragma unroll
@@ -564,8 +578,8 @@ __global__ __launch_bounds__(256) void round_bf16_kernel(const float* __restrict
 {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     auto pack = [](f32x4 v) {
-        return uint2{f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16),
-                     f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16)};
+        const u32x2 p = pack_bf16x4(v);
+        return uint2{p.x, p.y};
     };
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n / 4; i += stride) {
         const f32x4 k = reinterpret_cast<const f32x4*>(dK_acc)[i];
