@@ -13,7 +13,7 @@
 // each wave fetching them (d/16 copies through the compute unit's vector-memory
 // path, which saturates once several waves share a compute unit), the workgroup
 // fetches each tile once -- one coalesced 16-byte granule per thread, through a
-// register ring eight chunks deep -- into a ring of four swizzled LDS tiles, and
+// register ring -- into a ring of swizzled LDS tiles (below), and
 // every wave reads its operands from there (row reads; the transpose read gives K
 // with the feature in the lanes for the state update).  V and eta are loaded per
 // wave.  The parts of one head run on one XCD, so a tile fetched by one part is
@@ -188,7 +188,6 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
 #pragma unroll
     for (int m = 0; m < NM; ++m) Et = mfma32(kb[0][m], Mf[m], Et);
 
-    // one chunk; p = ch % P is a compile-time ring position
     // 16-deep products as 32-deep ones whose lower half is zero in one operand
     // (the other holds the identity there): these tuples live across the loop,
     // their lower halves never written, so no zeros are moved in per product

@@ -92,9 +92,9 @@ __device__ __forceinline__ void load_tile(Tile<D, RB>& t, const uint16_t* __rest
 // offset within a 16-token tile: K and Q row c at features 8g (+ 32m), V and Z row
 // c at the wave's features out0 + 4g (+ 16r), eta 4g.  Loads and stores of whole
 // tiles then put the tile's start in the scalar offset and need no vector address
-// arithmetic.  The scalar offset is not part of the buffer's range check, so
-// only tiles inside the slice are addressed this way, and the slice must span
-// less than 2^31 bytes (T d 2).
+// arithmetic.  The buffer's range check is not relied on (on gfx9 it covers the
+// vector offset only): only tiles inside the slice are addressed this way, and
+// the slice must span less than 2^31 bytes (T d 2) so that offsets fit.
 struct SliceBuffers {
     __amdgpu_buffer_rsrc_t k, q, v, e, z;
     int kq, vo, eo;
