@@ -323,16 +323,17 @@ void launch_eta(const LinearArgs& a, hipStream_t s)
     }
 }
 
-// Waves per workgroup, measured on MI355X at T = 2048: a d = 128 head runs as two
-// workgroups of four waves while they find a compute unit each (4x12 heads:
-// 71.8 us against 106.4 us with eight waves; 8x12: 84.8 against 113.2).  Four
-// waves is the floor: two-wave workgroups measured no faster at d = 64 (8x12
-// heads: 50.5 against 50.1 us) or d = 128 (4x12: 74.0 us).
+// Waves per workgroup, measured on MI355X at T = 2048: a head is split over
+// workgroups while they find a compute unit each.  d = 64: two workgroups of two
+// waves (8x12 heads: 39.0 us against 48.9 with one of four; 8x12 heads at
+// T = 8192: 130 against 173 us).  d = 128: two workgroups of four waves (4x12
+// heads: 71.8 us against 106.4 with eight waves; 8x12: 84.8 against 113.2); two
+// waves measured no faster there (4x12: 74.0 us).
 template <int D>
 hipError_t launch_d(const LinearArgs& a, hipStream_t s)
 {
-    if (D >= 128 && a.BH * 2 > kComputeUnits) launch_eta<D, D / 16>(a, s);
-    else launch_eta<D, 4>(a, s);
+    if (a.BH * 2 > kComputeUnits) launch_eta<D, D / 16>(a, s);
+    else launch_eta<D, D == 64 ? 2 : 4>(a, s);
     return hipGetLastError();
 }
 

@@ -80,13 +80,15 @@ def test_f32_matrix_core_many_slices(dev):
 
 # Many (batch, head) slices: shapes past the 256-unit threshold (units = B*H*d/16)
 # where chunk-16 heads share their K/Q tiles per workgroup, and the two-block
-# single-wave kernel for the shapes that cannot.  At d = 128 the shared-tile
-# kernel splits a head over two workgroups of four waves up to 128 heads (the
-# grid rounded up to whole rounds of the 8 XCDs), and keeps eight waves past that.
+# single-wave kernel for the shapes that cannot.  Up to 128 heads the shared-tile
+# kernel splits a head over two workgroups (two waves each at d = 64, four at
+# d = 128; the grid rounded up to whole rounds of the 8 XCDs), and keeps one
+# workgroup of d/16 waves per head past that.
 @pytest.mark.parametrize("d,B,H,T,chunk,per_token", [
-    (64, 9, 8, 100, 16, True),     # shared-tile kernel, ragged last chunk
-    (64, 5, 16, 64, 16, False),    # shared-tile kernel, scalar eta
-    (64, 9, 16, 64, 16, True),     # 144 heads, 16-byte eta loads
+    (64, 9, 8, 100, 16, True),     # shared-tile kernel, ragged last chunk, two workgroups
+    (64, 5, 16, 64, 16, False),    # shared-tile kernel, scalar eta, two workgroups
+    (64, 7, 11, 80, 16, True),     # 77 heads: two workgroups, grid rounded up
+    (64, 9, 16, 64, 16, True),     # 144 heads: one workgroup, 16-byte eta loads
     (128, 3, 11, 48, 16, True),    # d = 128, 33 heads: two workgroups per head
     (128, 5, 14, 48, 16, True),    # d = 128, 70 heads: two workgroups per head
     (128, 9, 15, 33, 16, False),   # d = 128, 135 heads: one, ragged, scalar eta
