@@ -35,17 +35,37 @@ METRIC = "TTT scan tokens/sec (all heads) + % of HBM/MFMA roofline, b=16 d=64"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFS = 2500.0           # MI355X dense bf16 MFMA
 PLANS = {"auto": 0, "generic": 1, "mfma": 2, "bigchunk": 3}
-# sources whose change invalidates a stored counter profile (kernels and dispatch)
-KERNEL_SOURCES = {"linear": ["linear_mfma.hip", "linear_coop.hip", "linear_generic.hip",
-                             "linear_bigchunk.hip", "linear_f32.hip", "mfma_common.h",
-                             "mfma_f32.h", "device_common.h", "launch.h", "api.cpp"],
+# sources whose change invalidates a stored counter profile, per kernel family (the
+# host-side api.cpp only validates and dispatches; the plan is part of a profile's
+# file name)
+KERNEL_SOURCES = {"linear_b16": ["linear_mfma.hip", "linear_coop.hip", "mfma_common.h",
+                                 "device_common.h", "launch.h"],
+                  "linear_f32": ["linear_f32.hip", "mfma_f32.h", "mfma_common.h",
+                                 "device_common.h", "launch.h"],
+                  "linear_generic": ["linear_generic.hip", "device_common.h", "launch.h"],
+                  "bigchunk": ["linear_bigchunk.hip", "mfma_common.h", "device_common.h",
+                               "launch.h"],
                   "mlp": ["mlp_mfma.hip", "mlp_generic.hip", "mfma_common.h", "device_common.h",
-                          "launch.h", "api.cpp"],
-                  "step": ["linear_step.hip", "device_common.h", "launch.h", "api.cpp"],
+                          "launch.h"],
+                  "step": ["linear_step.hip", "device_common.h", "launch.h"],
                   "ln": ["linear_ln.hip", "mfma_f32.h", "mfma_common.h", "device_common.h",
-                         "launch.h", "api.cpp"],
+                         "launch.h"],
                   "bwd": ["linear_bwd.hip", "mfma_f32.h", "mfma_common.h", "device_common.h",
-                          "launch.h", "api.cpp"]}
+                          "launch.h"]}
+HOST_ONLY_SOURCES = {"api.cpp"}
+
+
+def kernel_family(wl, plan_name: str) -> str:
+    """Which kernel sources a workload's plan runs."""
+    if wl.model == "mlp":
+        return "mlp"
+    if plan_name == "bigchunk":
+        return "bigchunk"
+    if plan_name == "generic":
+        return "linear_generic"
+    return "linear_f32" if wl.io == "f32" else "linear_b16"
+
+
 DECODE_METRIC = "TTT-Linear decode tokens/sec (all heads) + % of HBM roofline"
 BWD_METRIC = "TTT-Linear backward tokens/sec (all heads) + % of MFMA roofline"
 LN_METRIC = "TTT-Linear (bias, LayerNorm, residual) tokens/sec (all heads) + % of fp32 MFMA roofline"
@@ -84,13 +104,28 @@ def algorithmic_flops(wl, read_start: bool = False) -> float:
     return total * wl.BH
 
 
-def kernel_hash(model: str) -> str:
+def kernel_hash(family: str) -> str:
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES[model]:
+    for name in KERNEL_SOURCES[family]:
         p = os.path.join(ROOT, "test_sequence_layers_ttt_amd", "csrc", name)
         if os.path.exists(p):
             h.update(open(p, "rb").read())
     return h.hexdigest()[:16]
+
+
+def executed_flops_from_profiles(wl, plan_name):
+    """Matrix-core flops one call executes (sum over its kernels) from the committed
+    counter summary, or None when there is none or the kernel sources changed."""
+    path = os.path.join(ROOT, "profiles", "mfma_%s_%s.json" % (wl.name, plan_name))
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    if rec.get("kernel_hash") != kernel_hash(kernel_family(wl, plan_name)):
+        return None
+    return rec.get("mfma_flops_per_call")
 
 
 def traffic_from_profiles(wl, plan_name):
@@ -103,7 +138,7 @@ def traffic_from_profiles(wl, plan_name):
         rec = json.load(open(path))
     except Exception:
         return None
-    if rec.get("kernel_hash") != kernel_hash(wl.model):
+    if rec.get("kernel_hash") != kernel_hash(kernel_family(wl, plan_name)):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -558,7 +593,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="linear_b16_8x12")
+    ap.add_argument("--workload", default="linear_b16_1x32")
     ap.add_argument("--plan", default="auto", choices=sorted(PLANS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-slices", type=int, default=0,
@@ -754,6 +789,12 @@ def main():
         roof["frac_of_copy"] = round(achieved_gbs / copy_gbs, 4)
     roof["algorithmic_bytes"] = abytes
     roof["algorithmic_flops"] = aflops
+    # matrix-core flops the kernels execute (counter summary), which can differ from
+    # the method's count: the fraction of peak they reach in the same time
+    xfl = None if args.read_start else executed_flops_from_profiles(wl, plan_name)
+    if xfl is not None:
+        roof["executed_flops"] = xfl
+        roof["frac_executed"] = round(xfl / (ms_event * 1e-3) / 1e12 / BF16_PEAK_TFS, 4)
 
     # parity of the first output set against the oracle, and the CPU baseline
     cpu = None

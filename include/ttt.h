@@ -42,9 +42,13 @@
  *    The library allocates no device memory, keeps no state between calls and
  *    may be called from several host threads at once.
  *  - Streams: all work is enqueued on `stream` (a hipStream_t; NULL = the
- *    default stream).  The call returns before the work completes; outputs are
+ *    default stream).  It is declared `void*` so that this header compiles
+ *    without the HIP headers; the calling convention is that of the pointer
+ *    hipStream_t is.  The call returns before the work completes; outputs are
  *    valid once the stream has been synchronised.  The library never
  *    synchronises.
+ *  - `io_dtype` and `plan` take the ttt_dtype and ttt_plan values (passed as
+ *    int, the enums' own calling convention).
  *  - Aliasing: the final-state outputs may alias the matching initial-state
  *    inputs (W_out == W0 updates in place).  Z must not overlap any input.
  *  - Errors: arguments are checked on the host before any HIP call; a failed
@@ -94,9 +98,9 @@ typedef enum {
  * updates up to and including its own (the dual form above).  CHUNK_START:
  * every token of a chunk reads with the chunk-start state, z_t = W_c q_t (apply,
  * then update: the large-chunk ordering that leaves in-chunk dependencies to
- * window attention, PaperTrace "5 · TestingTime 训练与长上下文" §1.1 and the
- * read/write-order discussion after its §3.1; with chunk == 1 the
- * read-before-write delta rule).  The state update is the same in both. */
+ * window attention, PaperTrace "5 · TestingTime 训练与长上下文" §1.1, and the
+ * read/write-order passage of its §2.4; with chunk == 1 the read-before-write
+ * delta rule).  The state update is the same in both. */
 typedef enum {
     TTT_READ_INCLUSIVE = 0,
     TTT_READ_CHUNK_START = 1
@@ -106,22 +110,29 @@ typedef enum {
 /* TTT-Linear                                                                */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of workspace ttt_linear_fwd needs for this shape and plan (0 when none).
- * Returns 0 as well for shapes the plan cannot run. */
-size_t ttt_linear_workspace_bytes(int B, int H, int T, int d, int chunk,
-                                  int io_dtype, int plan);
+/* Bytes of workspace ttt_linear_fwd needs for this shape: the largest size any
+ * plan needs for either I/O dtype (0 when none does).  A workspace of this size
+ * serves ttt_linear_fwd and ttt_linear_fwd_ex for the shape whatever their
+ * dtype and plan. */
+size_t ttt_linear_workspace_bytes(int B, int H, int T, int d, int chunk);
+
+/* Bytes of workspace for this shape, dtype and plan exactly (0 when none, and
+ * for shapes the plan cannot run). */
+size_t ttt_linear_workspace_bytes_ex(int B, int H, int T, int d, int chunk,
+                                     int io_dtype, int plan);
 
 /* Plan that ttt_linear_fwd would run for this shape (never TTT_PLAN_AUTO), or a
  * negative ttt_status if no plan supports it. */
 int ttt_linear_select_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan);
 
-/* Forward scan of TTT-Linear.
+/* Forward scan of TTT-Linear (plan AUTO, inclusive read).
  *   W0    : [B, H, d, d] fp32 initial state.
  *   W_out : [B, H, d, d] fp32 state after the last token (may alias W0).
  *   d     : 16, 32, 64 or 128.   chunk : >= 1.
  *   workspace / workspace_bytes : device scratch of at least
- *           ttt_linear_workspace_bytes(...) bytes, 256-byte aligned (may be NULL
- *           when that is 0).
+ *           ttt_linear_workspace_bytes_ex(..., io_dtype, TTT_PLAN_AUTO) bytes
+ *           (ttt_linear_workspace_bytes(...) always suffices), 256-byte aligned
+ *           (may be NULL when that is 0).
  * The state update follows PaperTrace "5 · TestingTime 训练与长上下文" §1.1/§2.3;
  * with chunk == 1 it is the delta rule of the same page §2.1. */
 int ttt_linear_fwd(const void* K, const void* Q, const void* V,
@@ -130,7 +141,7 @@ int ttt_linear_fwd(const void* K, const void* Q, const void* V,
                    void* Z, float* W_out,
                    int B, int H, int T, int d, int chunk, int io_dtype,
                    void* workspace, size_t workspace_bytes,
-                   void* stream, int plan);
+                   void* stream);
 
 /* TTT-Linear with a momentum state (the E2-TTT passage of "Test-Time Training
  * (TTT)", §2.3 and §5.1: fast weights and a momentum evolve per chunk from the
@@ -158,7 +169,7 @@ int ttt_linear_fwd_momentum(const void* K, const void* Q, const void* V,
  *                                    + ln_bias   (over the d features),
  * or f(x) = W x + b when ln_weight == ln_bias == NULL (diosapp "Test-Time
  * Training (TTT) guide" §3 gives f(x) = W x + b; the LN-and-residual ablation
- * is the one PaperTrace "5 · TestingTime 训练与长上下文" discusses).  W and b
+ * is the one of PaperTrace "5 · TestingTime 训练与长上下文" §3.1).  W and b
  * take the chunked gradient step of ttt_linear_fwd (loss 1/2 ||f(k) - v||^2,
  * gradients at the chunk-start state, inclusive read); ln_weight and ln_bias
  * are fixed (outer-model parameters).
@@ -177,8 +188,8 @@ int ttt_linear_ln_fwd(const void* K, const void* Q, const void* V,
  * Each document of every head is its own TTT-Linear scan from its own initial
  * state: no state, gradient or output crosses a document boundary, and chunks
  * are counted from the document's first token (PaperTrace "5 · TestingTime
- * 训练与长上下文", the discussion of cross-sequence reset after §3.1: each
- * independent document needs its own W0 and state).
+ * 训练与长上下文" §2.4, the cross-sequence reset passage: each independent
+ * document needs its own W0 and state).
  *   K, Q, V, Z  : [H, total_T, d] in io_dtype, head-major: document n of head h is
  *                 rows cu_seqlens[n] .. cu_seqlens[n+1]-1 of head h's block.
  *   eta         : [H, total_T] fp32 or NULL (eta_scalar).
@@ -261,11 +272,11 @@ int ttt_linear_step(const void* K, const void* Q, const void* V,
                     void* Z, int B, int H, int n, int d, int chunk, int io_dtype,
                     void* stream);
 
-/* ttt_linear_fwd with a choice of read order (ttt_read_mode); ttt_linear_fwd is
- * this call with TTT_READ_INCLUSIVE.  CHUNK_START runs on the GENERIC and
- * BIGCHUNK plans (MFMA: TTT_ERR_UNSUPPORTED); an unknown read_mode is
- * TTT_ERR_INVALID_ARG.  Workspace sizes are those of ttt_linear_workspace_bytes
- * for the plan that runs. */
+/* ttt_linear_fwd with a kernel plan (ttt_plan) and a choice of read order
+ * (ttt_read_mode); ttt_linear_fwd is this call with TTT_PLAN_AUTO and
+ * TTT_READ_INCLUSIVE.  CHUNK_START runs on the GENERIC and BIGCHUNK plans (MFMA:
+ * TTT_ERR_UNSUPPORTED); an unknown read_mode is TTT_ERR_INVALID_ARG.  Workspace
+ * sizes are those of ttt_linear_workspace_bytes_ex for the plan that runs. */
 int ttt_linear_fwd_ex(const void* K, const void* Q, const void* V,
                       const float* eta, float eta_scalar,
                       const float* W0,
@@ -282,18 +293,31 @@ int ttt_linear_select_plan_ex(int B, int H, int T, int d, int chunk, int io_dtyp
 /* TTT-MLP (hidden width 4d)                                                 */
 /* ------------------------------------------------------------------------ */
 
-size_t ttt_mlp_workspace_bytes(int B, int H, int T, int d, int chunk, int io_dtype, int plan);
+/* Bytes of workspace ttt_mlp_fwd needs for this shape: the largest size any plan
+ * needs for either I/O dtype (0 when none does). */
+size_t ttt_mlp_workspace_bytes(int B, int H, int T, int d, int chunk);
+
+/* Bytes of workspace for this shape, dtype and plan exactly. */
+size_t ttt_mlp_workspace_bytes_ex(int B, int H, int T, int d, int chunk, int io_dtype, int plan);
 
 int ttt_mlp_select_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan);
 
-/* Forward scan of TTT-MLP, f(k) = W2 gelu(W1 k + b1) + b2.
+/* Forward scan of TTT-MLP, f(k) = W2 gelu(W1 k + b1) + b2 (plan AUTO).
  *   W1_0 : [B, H, 4d, d]   b1_0 : [B, H, 4d] or NULL (model without b1)
  *   W2_0 : [B, H, d, 4d]   b2_0 : [B, H, d]  or NULL (model without b2)
  *   W1_out, W2_out : final states (may alias W1_0, W2_0);
  *   b1_out / b2_out: final biases, NULL exactly when b1_0 / b2_0 is NULL.
- *   d : 64 (hidden 256).  chunk : >= 1.
+ *   d : 16, 32 or 64 (hidden 4d).  chunk : >= 1.
+ *   workspace : at least ttt_mlp_workspace_bytes(...) bytes, 256-byte aligned.
  * A present bias is part of the state and takes the same gradient step; an
- * absent one is a model without that bias. */
+ * absent one is a model without that bias.
+ * Operand range of the matrix-core plan (bf16 I/O, d = 64, chunk <= 16, which
+ * AUTO picks): its products take fp16 operands with fp32 accumulation.  Inputs,
+ * state and intermediate values of magnitude up to 65504 keep their bf16 value
+ * exactly when it is at least 2^-14 in magnitude; smaller ones are rounded to
+ * fp16's subnormal spacing of 2^-24, and values past 65504 overflow.  For data
+ * outside that range, call ttt_mlp_fwd_ex with TTT_PLAN_GENERIC (fp32 vector
+ * ALU, any magnitude). */
 int ttt_mlp_fwd(const void* K, const void* Q, const void* V,
                 const float* eta, float eta_scalar,
                 const float* W1_0, const float* b1_0,
@@ -301,7 +325,18 @@ int ttt_mlp_fwd(const void* K, const void* Q, const void* V,
                 void* Z, float* W1_out, float* b1_out, float* W2_out, float* b2_out,
                 int B, int H, int T, int d, int chunk, int io_dtype,
                 void* workspace, size_t workspace_bytes,
-                void* stream, int plan);
+                void* stream);
+
+/* ttt_mlp_fwd with a kernel plan (ttt_plan); the workspace is
+ * ttt_mlp_workspace_bytes_ex for the plan that runs. */
+int ttt_mlp_fwd_ex(const void* K, const void* Q, const void* V,
+                   const float* eta, float eta_scalar,
+                   const float* W1_0, const float* b1_0,
+                   const float* W2_0, const float* b2_0,
+                   void* Z, float* W1_out, float* b1_out, float* W2_out, float* b2_out,
+                   int B, int H, int T, int d, int chunk, int io_dtype,
+                   void* workspace, size_t workspace_bytes,
+                   void* stream, int plan);
 
 /* Static string for a ttt_status value (or "unknown status"). */
 const char* ttt_status_string(int status);

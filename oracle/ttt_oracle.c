@@ -126,8 +126,8 @@ static void linear_momentum_slice(const double* K, const double* Q, const double
 /* ------------------------------------------------------------------------ */
 /* TTT-Linear with a bias, and optionally LayerNorm and a residual inside f,  */
 /* one slice.  diosapp "Test-Time Training (TTT) guide" §3 gives the inner    */
-/* linear model as f(x) = W x + b; the ablation discussed in PaperTrace "5 ·  */
-/* TestingTime 训练与长上下文" (the section relating the three pages) adds LN  */
+/* linear model as f(x) = W x + b; the 125M ablation of PaperTrace "5 ·      */
+/* TestingTime 训练与长上下文" §3.1 adds LN                                   */
 /* and a residual inside f, read here as f(x) = x + LN(W x + b) with          */
 /* LN(u) = g * (u - mean(u)) / sqrt(var(u) + eps) + beta over the d features  */
 /* (g, beta fixed: they belong to the outer model).  W and b are the state:  */

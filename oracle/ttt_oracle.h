@@ -23,7 +23,7 @@
  *   - token t reads with every in-chunk update up to and including its own
  *     (ttt_oracle_linear_read also offers the chunk-start read, the
  *     apply-then-update order of large-chunk TTT: PaperTrace "5 · TestingTime
- *     训练与长上下文" §1.1 and the read/write-order discussion after §3.1);
+ *     训练与长上下文" §1.1, and the read/write-order passage of its §2.4);
  *   - eta_t belongs to the writing token (it scales token t's gradient);
  *   - TTT-Linear has no bias; TTT-MLP biases b1, b2 are part of the state and
  *     are updated by the same step, or are absent (frozen zero) when NULL;

@@ -108,21 +108,34 @@ int ttt_linear_select_plan_ex(int B, int H, int T, int d, int chunk, int io_dtyp
     return linear_plan(B, H, T, d, chunk, io_dtype, plan, read_mode);
 }
 
-size_t ttt_linear_workspace_bytes(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
+size_t ttt_linear_workspace_bytes_ex(int B, int H, int T, int d, int chunk, int io_dtype,
+                                     int plan)
 {
     int p = linear_plan(B, H, T, d, chunk, io_dtype, plan);
     if (p == TTT_PLAN_BIGCHUNK) return linear_bigchunk_workspace(B * H, T, d, chunk);
     return 0;
 }
 
+// The size-only query: enough for whatever plan either I/O type selects.
+size_t ttt_linear_workspace_bytes(int B, int H, int T, int d, int chunk)
+{
+    size_t n = 0;
+    for (int io : {(int)TTT_DTYPE_F32, (int)TTT_DTYPE_BF16})
+        for (int plan = TTT_PLAN_AUTO; plan <= TTT_PLAN_BIGCHUNK; ++plan) {
+            const size_t m = ttt_linear_workspace_bytes_ex(B, H, T, d, chunk, io, plan);
+            n = m > n ? m : n;
+        }
+    return n;
+}
+
 int ttt_linear_fwd(const void* K, const void* Q, const void* V,
                    const float* eta, float eta_scalar, const float* W0,
                    void* Z, float* W_out,
                    int B, int H, int T, int d, int chunk, int io_dtype,
-                   void* workspace, size_t workspace_bytes, void* stream, int plan)
+                   void* workspace, size_t workspace_bytes, void* stream)
 {
     return ttt_linear_fwd_ex(K, Q, V, eta, eta_scalar, W0, Z, W_out, B, H, T, d, chunk,
-                             io_dtype, workspace, workspace_bytes, stream, plan,
+                             io_dtype, workspace, workspace_bytes, stream, TTT_PLAN_AUTO,
                              TTT_READ_INCLUSIVE);
 }
 
@@ -140,7 +153,7 @@ int ttt_linear_fwd_ex(const void* K, const void* Q, const void* V,
     if (eta ? !aligned(eta, 4) : !std::isfinite(eta_scalar)) return TTT_ERR_INVALID_ARG;
     const int p = linear_plan(B, H, T, d, chunk, io_dtype, plan, read_mode);
     if (p < 0) return p;
-    const size_t need = ttt_linear_workspace_bytes(B, H, T, d, chunk, io_dtype, p);
+    const size_t need = ttt_linear_workspace_bytes_ex(B, H, T, d, chunk, io_dtype, p);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
         return TTT_ERR_WORKSPACE;
 
@@ -214,7 +227,7 @@ int ttt_linear_fwd_momentum(const void* K, const void* Q, const void* V,
     if (!(beta >= 0.f && beta < 1.f)) return TTT_ERR_INVALID_ARG;
     const int p = linear_plan(B, H, T, d, chunk, io_dtype, plan, TTT_READ_CHUNK_START);
     if (p < 0) return p;
-    const size_t need = ttt_linear_workspace_bytes(B, H, T, d, chunk, io_dtype, p);
+    const size_t need = ttt_linear_workspace_bytes_ex(B, H, T, d, chunk, io_dtype, p);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
         return TTT_ERR_WORKSPACE;
 
@@ -338,11 +351,22 @@ int ttt_mlp_select_plan(int B, int H, int T, int d, int chunk, int io_dtype, int
     return mlp_plan(B, H, T, d, chunk, io_dtype, plan);
 }
 
-size_t ttt_mlp_workspace_bytes(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
+size_t ttt_mlp_workspace_bytes_ex(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
 {
     int p = mlp_plan(B, H, T, d, chunk, io_dtype, plan);
     if (p == TTT_PLAN_GENERIC) return mlp_generic_workspace(B * H, T, d, chunk);
     return 0;
+}
+
+size_t ttt_mlp_workspace_bytes(int B, int H, int T, int d, int chunk)
+{
+    size_t n = 0;
+    for (int io : {(int)TTT_DTYPE_F32, (int)TTT_DTYPE_BF16})
+        for (int plan = TTT_PLAN_AUTO; plan <= TTT_PLAN_BIGCHUNK; ++plan) {
+            const size_t m = ttt_mlp_workspace_bytes_ex(B, H, T, d, chunk, io, plan);
+            n = m > n ? m : n;
+        }
+    return n;
 }
 
 int ttt_mlp_fwd(const void* K, const void* Q, const void* V,
@@ -350,7 +374,19 @@ int ttt_mlp_fwd(const void* K, const void* Q, const void* V,
                 const float* W1_0, const float* b1_0, const float* W2_0, const float* b2_0,
                 void* Z, float* W1_out, float* b1_out, float* W2_out, float* b2_out,
                 int B, int H, int T, int d, int chunk, int io_dtype,
-                void* workspace, size_t workspace_bytes, void* stream, int plan)
+                void* workspace, size_t workspace_bytes, void* stream)
+{
+    return ttt_mlp_fwd_ex(K, Q, V, eta, eta_scalar, W1_0, b1_0, W2_0, b2_0, Z, W1_out, b1_out,
+                          W2_out, b2_out, B, H, T, d, chunk, io_dtype, workspace,
+                          workspace_bytes, stream, TTT_PLAN_AUTO);
+}
+
+int ttt_mlp_fwd_ex(const void* K, const void* Q, const void* V,
+                   const float* eta, float eta_scalar,
+                   const float* W1_0, const float* b1_0, const float* W2_0, const float* b2_0,
+                   void* Z, float* W1_out, float* b1_out, float* W2_out, float* b2_out,
+                   int B, int H, int T, int d, int chunk, int io_dtype,
+                   void* workspace, size_t workspace_bytes, void* stream, int plan)
 {
     if (!K || !Q || !V || !W1_0 || !W2_0 || !Z || !W1_out || !W2_out) return TTT_ERR_INVALID_ARG;
     if ((b1_0 == nullptr) != (b1_out == nullptr) || (b2_0 == nullptr) != (b2_out == nullptr))
@@ -365,7 +401,7 @@ int ttt_mlp_fwd(const void* K, const void* Q, const void* V,
     if (eta ? !aligned(eta, 4) : !std::isfinite(eta_scalar)) return TTT_ERR_INVALID_ARG;
     const int p = mlp_plan(B, H, T, d, chunk, io_dtype, plan);
     if (p < 0) return p;
-    const size_t need = ttt_mlp_workspace_bytes(B, H, T, d, chunk, io_dtype, p);
+    const size_t need = ttt_mlp_workspace_bytes_ex(B, H, T, d, chunk, io_dtype, p);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256)))
         return TTT_ERR_WORKSPACE;
 

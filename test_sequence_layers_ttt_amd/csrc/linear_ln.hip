@@ -2,8 +2,8 @@
 // residual inside the inner model: f(x) = x + LN(W x + b), LN(u) =
 // w * (u - mean(u)) / sqrt(var(u) + eps) + beta over the d features, w and beta
 // fixed (diosapp "Test-Time Training (TTT) guide" §3 for f(x) = W x + b; the
-// LN-and-residual ablation discussed in PaperTrace "5 · TestingTime
-// 训练与长上下文").  Without LN, f(x) = W x + b.
+// LN-and-residual ablation of PaperTrace "5 · TestingTime 训练与长上下文"
+// §3.1).  Without LN, f(x) = W x + b.
 //
 // Chunked dual form (same page §1.1): every gradient of a chunk is taken at the
 // chunk-start (W_c, b_c).  For tokens as columns,

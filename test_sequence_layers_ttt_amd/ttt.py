@@ -19,12 +19,14 @@ PLAN_AUTO, PLAN_GENERIC, PLAN_MFMA, PLAN_BIGCHUNK = 0, 1, 2, 3
 READ_INCLUSIVE, READ_CHUNK_START = 0, 1
 
 # every symbol include/ttt.h declares
-EXPORTS = ("ttt_linear_workspace_bytes", "ttt_linear_select_plan", "ttt_linear_fwd",
+EXPORTS = ("ttt_linear_workspace_bytes", "ttt_linear_workspace_bytes_ex",
+           "ttt_linear_select_plan", "ttt_linear_fwd",
            "ttt_linear_step", "ttt_linear_bwd_workspace_bytes", "ttt_linear_bwd",
            "ttt_linear_fwd_ex", "ttt_linear_select_plan_ex",
            "ttt_linear_fwd_varlen", "ttt_linear_select_plan_varlen", "ttt_linear_ln_fwd",
            "ttt_linear_fwd_momentum",
-           "ttt_mlp_workspace_bytes", "ttt_mlp_select_plan", "ttt_mlp_fwd",
+           "ttt_mlp_workspace_bytes", "ttt_mlp_workspace_bytes_ex", "ttt_mlp_select_plan",
+           "ttt_mlp_fwd", "ttt_mlp_fwd_ex",
            "ttt_status_string", "ttt_plan_name")
 
 
@@ -46,11 +48,13 @@ def lib() -> ctypes.CDLL:
                                "the TTT scan has no CPU fallback")
         L = ctypes.CDLL(LIB_PATH)
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-        L.ttt_linear_workspace_bytes.argtypes = [i] * 7
+        L.ttt_linear_workspace_bytes.argtypes = [i] * 5
         L.ttt_linear_workspace_bytes.restype = sz
+        L.ttt_linear_workspace_bytes_ex.argtypes = [i] * 7
+        L.ttt_linear_workspace_bytes_ex.restype = sz
         L.ttt_linear_select_plan.argtypes = [i] * 7
         L.ttt_linear_select_plan.restype = i
-        L.ttt_linear_fwd.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp, i]
+        L.ttt_linear_fwd.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, i, i, i, i, i, i, vp, sz, vp]
         L.ttt_linear_fwd.restype = i
         L.ttt_linear_fwd_ex.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, i, i, i, i, i, i, vp, sz,
                                         vp, i, i]
@@ -75,13 +79,18 @@ def lib() -> ctypes.CDLL:
         L.ttt_linear_bwd.restype = i
         L.ttt_linear_step.argtypes = [vp, vp, vp, vp, f, vp, vp, i, vp, i, i, i, i, i, i, vp]
         L.ttt_linear_step.restype = i
-        L.ttt_mlp_workspace_bytes.argtypes = [i] * 7
+        L.ttt_mlp_workspace_bytes.argtypes = [i] * 5
         L.ttt_mlp_workspace_bytes.restype = sz
+        L.ttt_mlp_workspace_bytes_ex.argtypes = [i] * 7
+        L.ttt_mlp_workspace_bytes_ex.restype = sz
         L.ttt_mlp_select_plan.argtypes = [i] * 7
         L.ttt_mlp_select_plan.restype = i
         L.ttt_mlp_fwd.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                  i, i, i, i, i, i, vp, sz, vp, i]
+                                  i, i, i, i, i, i, vp, sz, vp]
         L.ttt_mlp_fwd.restype = i
+        L.ttt_mlp_fwd_ex.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                     i, i, i, i, i, i, vp, sz, vp, i]
+        L.ttt_mlp_fwd_ex.restype = i
         L.ttt_status_string.argtypes = [i]
         L.ttt_status_string.restype = ctypes.c_char_p
         L.ttt_plan_name.argtypes = [i]
@@ -132,8 +141,11 @@ def _check(t, name, shape, dtype=None):
         raise ValueError("%s must be %s" % (name, dtype))
 
 
-def linear_workspace_bytes(B, H, T, d, chunk, io_dtype, plan=PLAN_AUTO) -> int:
-    return int(lib().ttt_linear_workspace_bytes(B, H, T, d, chunk, io_dtype, plan))
+def linear_workspace_bytes(B, H, T, d, chunk, io_dtype=None, plan=PLAN_AUTO) -> int:
+    """Workspace bytes for the shape; with io_dtype, for that dtype and plan exactly."""
+    if io_dtype is None:
+        return int(lib().ttt_linear_workspace_bytes(B, H, T, d, chunk))
+    return int(lib().ttt_linear_workspace_bytes_ex(B, H, T, d, chunk, io_dtype, plan))
 
 
 def linear_select_plan(B, H, T, d, chunk, io_dtype, plan=PLAN_AUTO,
@@ -143,8 +155,11 @@ def linear_select_plan(B, H, T, d, chunk, io_dtype, plan=PLAN_AUTO,
     return int(lib().ttt_linear_select_plan_ex(B, H, T, d, chunk, io_dtype, plan, read_mode))
 
 
-def mlp_workspace_bytes(B, H, T, d, chunk, io_dtype, plan=PLAN_AUTO) -> int:
-    return int(lib().ttt_mlp_workspace_bytes(B, H, T, d, chunk, io_dtype, plan))
+def mlp_workspace_bytes(B, H, T, d, chunk, io_dtype=None, plan=PLAN_AUTO) -> int:
+    """Workspace bytes for the shape; with io_dtype, for that dtype and plan exactly."""
+    if io_dtype is None:
+        return int(lib().ttt_mlp_workspace_bytes(B, H, T, d, chunk))
+    return int(lib().ttt_mlp_workspace_bytes_ex(B, H, T, d, chunk, io_dtype, plan))
 
 
 def mlp_select_plan(B, H, T, d, chunk, io_dtype, plan=PLAN_AUTO) -> int:
@@ -398,11 +413,12 @@ def mlp_fwd(K, Q, V, eta, W1, b1, W2, b2, chunk: int, eta_scalar: float = 0.0, *
     io = _io_dtype(K)
     nbytes = mlp_workspace_bytes(B, H, T, d, chunk, io, plan)
     ws = _workspace(nbytes, K.device, workspace)
-    rc = lib().ttt_mlp_fwd(K.data_ptr(), Q.data_ptr(), V.data_ptr(), _ptr(eta), float(eta_scalar),
-                           W1.data_ptr(), _ptr(b1), W2.data_ptr(), _ptr(b2),
-                           Z.data_ptr(), W1_out.data_ptr(), _ptr(b1_out), W2_out.data_ptr(),
-                           _ptr(b2_out), B, H, T, d, int(chunk), io, _ptr(ws),
-                           0 if ws is None else ws.numel(), _stream(K.device, stream), int(plan))
+    rc = lib().ttt_mlp_fwd_ex(K.data_ptr(), Q.data_ptr(), V.data_ptr(), _ptr(eta),
+                              float(eta_scalar), W1.data_ptr(), _ptr(b1), W2.data_ptr(), _ptr(b2),
+                              Z.data_ptr(), W1_out.data_ptr(), _ptr(b1_out), W2_out.data_ptr(),
+                              _ptr(b2_out), B, H, T, d, int(chunk), io, _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream(K.device, stream),
+                              int(plan))
     if rc != OK:
         raise TTTError(rc, "ttt_mlp_fwd")
     return Z, W1_out, b1_out, W2_out, b2_out

@@ -52,9 +52,10 @@ def _linear(**kw):
     a = dict(K=FAKE, Q=FAKE, V=FAKE, eta=FAKE, eta_scalar=0.1, W0=FAKE, Z=FAKE, W=FAKE,
              B=1, H=1, T=16, d=16, chunk=16, io=0, ws=None, wsb=0, stream=None, plan=0)
     a.update(kw)
-    return ttt.lib().ttt_linear_fwd(a["K"], a["Q"], a["V"], a["eta"], a["eta_scalar"], a["W0"],
-                                    a["Z"], a["W"], a["B"], a["H"], a["T"], a["d"], a["chunk"],
-                                    a["io"], a["ws"], a["wsb"], a["stream"], a["plan"])
+    return ttt.lib().ttt_linear_fwd_ex(a["K"], a["Q"], a["V"], a["eta"], a["eta_scalar"],
+                                       a["W0"], a["Z"], a["W"], a["B"], a["H"], a["T"], a["d"],
+                                       a["chunk"], a["io"], a["ws"], a["wsb"], a["stream"],
+                                       a["plan"], ttt.READ_INCLUSIVE)
 
 
 def _mlp(**kw):
@@ -62,10 +63,87 @@ def _mlp(**kw):
              b2=FAKE, Z=FAKE, W1o=FAKE, b1o=FAKE, W2o=FAKE, b2o=FAKE, B=1, H=1, T=16, d=64,
              chunk=16, io=1, ws=None, wsb=0, stream=None, plan=0)
     a.update(kw)
-    return ttt.lib().ttt_mlp_fwd(a["K"], a["Q"], a["V"], a["eta"], a["eta_scalar"], a["W1"],
-                                 a["b1"], a["W2"], a["b2"], a["Z"], a["W1o"], a["b1o"], a["W2o"],
-                                 a["b2o"], a["B"], a["H"], a["T"], a["d"], a["chunk"], a["io"],
-                                 a["ws"], a["wsb"], a["stream"], a["plan"])
+    return ttt.lib().ttt_mlp_fwd_ex(a["K"], a["Q"], a["V"], a["eta"], a["eta_scalar"], a["W1"],
+                                    a["b1"], a["W2"], a["b2"], a["Z"], a["W1o"], a["b1o"],
+                                    a["W2o"], a["b2o"], a["B"], a["H"], a["T"], a["d"],
+                                    a["chunk"], a["io"], a["ws"], a["wsb"], a["stream"],
+                                    a["plan"])
+
+
+def _c_prototypes(src):
+    """name -> list of parameter declarations, from a C header."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(?:int|size_t|const char\*)\s+(ttt_[a-z0-9_]+)\s*\(([^)]*)\)\s*;",
+                         src):
+        out[m.group(1)] = [p.strip() for p in m.group(2).split(",") if p.strip()]
+    return out
+
+
+# The boundary's signatures as the hot-path scope table fixes them: the calls a C
+# caller written to that interface makes.  Extensions (plan choice, read order)
+# live in the _ex entry points, so these keep exactly this argument list.
+SCOPE_SIGNATURES = {
+    "ttt_linear_workspace_bytes": ["int", "int", "int", "int", "int"],
+    "ttt_linear_fwd": ["void*", "void*", "void*", "float*", "float", "float*", "void*",
+                       "float*", "int", "int", "int", "int", "int", "int", "void*", "size_t",
+                       "void*"],
+    "ttt_mlp_workspace_bytes": ["int", "int", "int", "int", "int"],
+    "ttt_mlp_fwd": ["void*", "void*", "void*", "float*", "float", "float*", "float*",
+                    "float*", "float*", "void*", "float*", "float*", "float*", "float*",
+                    "int", "int", "int", "int", "int", "int", "void*", "size_t", "void*"],
+    "ttt_status_string": ["int"],
+}
+
+
+def _param_type(decl):
+    decl = decl.replace("const ", "").strip()
+    t = re.sub(r"\s*\b[A-Za-z_][A-Za-z0-9_]*$", "", decl)   # drop the parameter name
+    return t.replace(" ", "")
+
+
+def test_scope_table_signatures():
+    protos = _c_prototypes(open(HEADER).read())
+    for name, types in SCOPE_SIGNATURES.items():
+        assert name in protos, name
+        assert [_param_type(p) for p in protos[name]] == types, (name, protos[name])
+
+
+def test_scope_table_argument_lists_reach_validation():
+    """Calls with exactly the scope table's argument lists (no plan, no read
+    order) go through the host validation; each carries one refused argument."""
+    L = ttt.lib()
+    assert L.ttt_linear_fwd(None, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, FAKE, 1, 1, 16, 16, 16, 0,
+                            None, 0, None) == ttt.ERR_INVALID_ARG
+    assert L.ttt_linear_fwd(FAKE, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, FAKE, 1, 1, 16, 48, 16, 0,
+                            None, 0, None) == ttt.ERR_UNSUPPORTED
+    # the large-chunk shape needs its workspace under AUTO
+    assert L.ttt_linear_fwd(FAKE, FAKE, FAKE, None, 1.0 / 256, FAKE, FAKE, FAKE, 1, 2, 512, 64,
+                            256, 1, None, 0, None) == ttt.ERR_WORKSPACE
+    assert L.ttt_mlp_fwd(FAKE, FAKE, FAKE, None, 0.05, FAKE, None, FAKE, None, FAKE, FAKE,
+                         None, FAKE, None, 1, 1, 16, 128, 16, 1, None, 0,
+                         None) == ttt.ERR_UNSUPPORTED
+    assert L.ttt_mlp_fwd(None, FAKE, FAKE, None, 0.05, FAKE, None, FAKE, None, FAKE, FAKE,
+                         None, FAKE, None, 1, 1, 16, 64, 16, 1, None, 0,
+                         None) == ttt.ERR_INVALID_ARG
+
+
+def test_size_only_workspace_queries_cover_every_plan():
+    for shape in [(1, 2, 512, 64, 256), (1, 16, 131072, 128, 2048), (8, 12, 2048, 64, 16),
+                  (2, 3, 100, 32, 40)]:
+        n = ttt.linear_workspace_bytes(*shape)
+        for io in (ttt.DTYPE_F32, ttt.DTYPE_BF16):
+            for plan in range(4):
+                assert ttt.linear_workspace_bytes(*shape, io, plan) <= n
+    assert ttt.linear_workspace_bytes(1, 2, 512, 64, 256) == \
+        ttt.linear_workspace_bytes(1, 2, 512, 64, 256, ttt.DTYPE_BF16, ttt.PLAN_BIGCHUNK) > 0
+    assert ttt.linear_workspace_bytes(8, 12, 2048, 64, 16) == 0
+    for shape in [(1, 2, 64, 64, 16), (1, 2, 64, 64, 32), (3, 1, 50, 16, 5)]:
+        n = ttt.mlp_workspace_bytes(*shape)
+        for io in (ttt.DTYPE_F32, ttt.DTYPE_BF16):
+            for plan in range(4):
+                assert ttt.mlp_workspace_bytes(*shape, io, plan) <= n
+    assert ttt.mlp_workspace_bytes(1, 2, 64, 64, 32) == 2 * (2 * 256 * 64 + 256 + 64) * 4
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -350,5 +428,5 @@ def test_profile_hash_covers_every_kernel_source():
     csrc = os.path.join(ROOT, "test_sequence_layers_ttt_amd", "csrc")
     files = {os.path.basename(p) for p in glob.glob(os.path.join(csrc, "*"))
              if p.endswith((".hip", ".h", ".cpp"))}
-    hashed = set().union(*bench.KERNEL_SOURCES.values())
+    hashed = set().union(*bench.KERNEL_SOURCES.values()) | bench.HOST_ONLY_SOURCES
     assert files <= hashed, sorted(files - hashed)

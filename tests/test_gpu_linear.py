@@ -94,6 +94,9 @@ def test_f32_matrix_core_many_slices(dev):
     (128, 9, 15, 33, 16, False),   # d = 128, 135 heads: one, ragged, scalar eta
     (32, 9, 15, 40, 16, True),     # two 16-row blocks per wave at d = 32
     (64, 2, 40, 56, 8, True),      # two blocks per wave, chunk 8
+    (64, 5, 13, 48, 16, True),     # 65 heads: the smallest head count past 256 units
+    (64, 8, 16, 64, 16, False),    # 128 heads: the largest with two workgroups per head
+    (64, 3, 43, 61, 16, True),     # 129 heads: one workgroup per head, ragged T
 ])
 def test_many_slices(dev, d, B, H, T, chunk, per_token):
     wl, seed = small(d, chunk, "bf16", per_token=per_token, T=T, B=B, H=H, seed=107)
@@ -132,7 +135,32 @@ def test_linear_b16_1x32_full(dev):
 
 def test_linear_b2048_1x16_full(dev):
     wl = inputs.WORKLOADS["linear_b2048_1x16"]
-    check_linear(wl, inputs.WORKLOAD_SEEDS[wl.name], dev, ttt.PLAN_AUTO, slices=[0, 3, 9, 15])
+    check_linear(wl, inputs.WORKLOAD_SEEDS[wl.name], dev, ttt.PLAN_AUTO)   # all 16 slices
+
+
+def test_scope_table_entry_point(dev):
+    """ttt_linear_fwd called through ctypes with exactly the boundary's argument
+    list (no plan, no read order), against the oracle."""
+    import ctypes
+    import torch
+    from gpu_helpers import device_inputs, host
+    wl, seed = small(64, 16, "bf16", per_token=True, T=200, B=2, H=5)
+    x = inputs.make_inputs(wl, seed)
+    a = device_inputs(wl, x, dev)
+    Z = torch.empty_like(a["K"])
+    W = torch.empty_like(a["W0"])
+    n = ttt.lib().ttt_linear_workspace_bytes(wl.B, wl.H, wl.T, wl.d, wl.chunk)
+    assert n == 0
+    rc = ttt.lib().ttt_linear_fwd(
+        a["K"].data_ptr(), a["Q"].data_ptr(), a["V"].data_ptr(), a["eta"].data_ptr(),
+        ctypes.c_float(0.0), a["W0"].data_ptr(), Z.data_ptr(), W.data_ptr(), wl.B, wl.H, wl.T,
+        wl.d, wl.chunk, ttt.DTYPE_BF16, None, 0, torch.cuda.current_stream(dev).cuda_stream)
+    assert rc == ttt.OK
+    torch.cuda.synchronize()
+    Zo, Wo = oracle.linear(x["K"], x["Q"], x["V"], x["eta"], x["eta_scalar"], x["W0"], wl.chunk)
+    ez, ew = rel_err(host(Z, wl.BH), Zo), rel_err(host(W, wl.BH), Wo)
+    say("  scope-table call: max rel err Z %.3e  W %.3e" % (ez, ew))
+    assert ez < TOL["bf16"] and ew < TOL["bf16"]
 
 
 def test_state_may_alias_initial_state(dev):

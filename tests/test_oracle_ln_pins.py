@@ -1,7 +1,7 @@
 """Pins for the oracle's TTT-Linear with the inner bias and, optionally,
 LayerNorm and a residual inside f: f(x) = x + LN(W x + b) (diosapp "Test-Time
 Training (TTT) guide" §3 for W x + b; the LN-and-residual ablation discussed in
-PaperTrace "5 · TestingTime 训练与长上下文").
+PaperTrace "5 · TestingTime 训练与长上下文" §3.1).
 
   - bias only: the model equals the plain TTT-Linear oracle on inputs with an
     appended constant-1 feature (the bias as an extra column of W);

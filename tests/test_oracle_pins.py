@@ -351,7 +351,7 @@ def test_golden_fixtures_unchanged():
 # Every token of a chunk reads with the chunk-start state (apply, then update):
 # the large-chunk ordering whose in-chunk dependencies are left to window
 # attention (PaperTrace "5 · TestingTime 训练与长上下文" §1.1, and the
-# read/write-order discussion after its §3.1).
+# read/write-order passage of its §2.4).
 def test_read_start_keeps_the_state_update():
     """The read order changes the outputs only: the final state is identical."""
     rng = np.random.default_rng(41)
