@@ -285,6 +285,36 @@ int ttt_linear_fwd_ex(const void* K, const void* Q, const void* V,
                       void* workspace, size_t workspace_bytes,
                       void* stream, int plan, int read_mode);
 
+/* ttt_linear_fwd for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments as ttt_linear_fwd without the workspace: the plan
+ * that needs one (TTT_PLAN_BIGCHUNK, chunks of 128+ tokens) runs in a static
+ * device array of the library, TTT_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU.  The
+ * array is part of the library's code object: each GPU holds it from the
+ * library's first use there until the process ends.  The call allocates
+ * nothing and frees nothing.
+ *   - Shapes whose workspace (ttt_linear_workspace_bytes_ex for the AUTO plan)
+ *     exceeds 64 MiB return TTT_ERR_WORKSPACE before any HIP call (for example
+ *     16 heads x 131072 tokens at d = 128, chunk 2048, which needs 160 MiB: use
+ *     ttt_linear_fwd with a caller workspace there).
+ *   - The scratch of the caller's current device is used; `stream` must belong
+ *     to that device.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in time
+ *     on one GPU (other streams, other host threads) race and give wrong
+ *     results.  Calls serialised on one stream are safe; each call writes every
+ *     scratch byte it reads, so nothing depends on what an earlier call left.
+ *   - A failure to find the array's device address returns TTT_ERR_LAUNCH. */
+#define TTT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ttt_linear_fwd_noalloc(const void* K, const void* Q, const void* V,
+                           const float* eta, float eta_scalar,
+                           const float* W0,
+                           void* Z, float* W_out,
+                           int B, int H, int T, int d, int chunk, int io_dtype,
+                           void* stream);
+
+/* Size in bytes of ttt_linear_fwd_noalloc's per-GPU scratch array. */
+size_t ttt_linear_noalloc_scratch_bytes(void);
+
 /* Plan that ttt_linear_fwd_ex would run for this shape and read order. */
 int ttt_linear_select_plan_ex(int B, int H, int T, int d, int chunk, int io_dtype, int plan,
                               int read_mode);

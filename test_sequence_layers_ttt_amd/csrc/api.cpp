@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "ttt.h"
 #include "launch.h"
@@ -69,6 +70,31 @@ int mlp_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_LAUNCH; }
+
+// Workspace of ttt_linear_fwd_noalloc: one static array per GPU, held until the
+// process ends.  Host code never passes `scratch` itself to a kernel (on the host
+// the name is only a stand-in for the symbol); it passes the device address
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+constexpr size_t kScratchBytes = TTT_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of this device's scratch array (nullptr on failure, with the
+// HIP error in *err).
+void* scratch_address(int device, hipError_t* err)
+{
+    std::call_once(g_scratch_once[device], [device] {
+        void* p = nullptr;
+        g_scratch_err[device] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[device] = g_scratch_err[device] == hipSuccess ? p : nullptr;
+    });
+    *err = g_scratch_err[device];
+    return g_scratch_ptr[device];
+}
 
 }  // namespace
 
@@ -173,6 +199,38 @@ int ttt_linear_fwd_ex(const void* K, const void* Q, const void* V,
     default: return launch_status(launch_linear_generic(a, s));
     }
 }
+
+int ttt_linear_fwd_noalloc(const void* K, const void* Q, const void* V,
+                           const float* eta, float eta_scalar, const float* W0,
+                           void* Z, float* W_out,
+                           int B, int H, int T, int d, int chunk, int io_dtype, void* stream)
+{
+    // the same host checks as ttt_linear_fwd, then the workspace size against the
+    // static scratch, before any HIP call
+    if (!K || !Q || !V || !W0 || !Z || !W_out) return TTT_ERR_INVALID_ARG;
+    if (!aligned(K, 16) || !aligned(Q, 16) || !aligned(V, 16) || !aligned(Z, 16) ||
+        !aligned(W0, 16) || !aligned(W_out, 16))
+        return TTT_ERR_INVALID_ARG;
+    if (eta ? !aligned(eta, 4) : !std::isfinite(eta_scalar)) return TTT_ERR_INVALID_ARG;
+    const int p = linear_plan(B, H, T, d, chunk, io_dtype, TTT_PLAN_AUTO);
+    if (p < 0) return p;
+    const size_t need = ttt_linear_workspace_bytes_ex(B, H, T, d, chunk, io_dtype, p);
+    if (need > kScratchBytes) return TTT_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+            return TTT_ERR_LAUNCH;
+        hipError_t err;
+        ws = scratch_address(dev, &err);
+        if (!ws) return TTT_ERR_LAUNCH;
+    }
+    return ttt_linear_fwd_ex(K, Q, V, eta, eta_scalar, W0, Z, W_out, B, H, T, d, chunk,
+                             io_dtype, ws, ws ? kScratchBytes : 0, stream, p,
+                             TTT_READ_INCLUSIVE);
+}
+
+size_t ttt_linear_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 size_t ttt_linear_bwd_workspace_bytes(int B, int H, int T, int d, int chunk, int io_dtype)
 {

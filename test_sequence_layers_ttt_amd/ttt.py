@@ -24,7 +24,8 @@ EXPORTS = ("ttt_linear_workspace_bytes", "ttt_linear_workspace_bytes_ex",
            "ttt_linear_step", "ttt_linear_bwd_workspace_bytes", "ttt_linear_bwd",
            "ttt_linear_fwd_ex", "ttt_linear_select_plan_ex",
            "ttt_linear_fwd_varlen", "ttt_linear_select_plan_varlen", "ttt_linear_ln_fwd",
-           "ttt_linear_fwd_momentum",
+           "ttt_linear_fwd_momentum", "ttt_linear_fwd_noalloc",
+           "ttt_linear_noalloc_scratch_bytes",
            "ttt_mlp_workspace_bytes", "ttt_mlp_workspace_bytes_ex", "ttt_mlp_select_plan",
            "ttt_mlp_fwd", "ttt_mlp_fwd_ex",
            "ttt_status_string", "ttt_plan_name")
@@ -59,6 +60,10 @@ def lib() -> ctypes.CDLL:
         L.ttt_linear_fwd_ex.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, i, i, i, i, i, i, vp, sz,
                                         vp, i, i]
         L.ttt_linear_fwd_ex.restype = i
+        L.ttt_linear_fwd_noalloc.argtypes = [vp, vp, vp, vp, f, vp, vp, vp, i, i, i, i, i, i, vp]
+        L.ttt_linear_fwd_noalloc.restype = i
+        L.ttt_linear_noalloc_scratch_bytes.argtypes = []
+        L.ttt_linear_noalloc_scratch_bytes.restype = sz
         L.ttt_linear_fwd_momentum.argtypes = [vp, vp, vp, vp, f, vp, vp, f, vp, vp, vp,
                                               i, i, i, i, i, i, vp, sz, vp, i]
         L.ttt_linear_fwd_momentum.restype = i
@@ -207,6 +212,34 @@ def linear_fwd(K, Q, V, eta, W0, chunk: int, eta_scalar: float = 0.0, *, Z=None,
     if rc != OK:
         raise TTTError(rc, "ttt_linear_fwd")
     return Z, W_out
+
+
+def linear_fwd_noalloc(K, Q, V, eta, W0, chunk: int, eta_scalar: float = 0.0, *, Z, W_out,
+                       stream=None) -> Tuple:
+    """ttt_linear_fwd_noalloc: the AUTO-plan scan with any workspace taken from the
+    library's static per-GPU scratch.  Z and W_out are caller-given (this call
+    allocates nothing).  Returns (Z, W_out)."""
+    import torch
+    B, H, T, d = K.shape
+    _check(K, "K", (B, H, T, d))
+    _check(Q, "Q", (B, H, T, d), K.dtype)
+    _check(V, "V", (B, H, T, d), K.dtype)
+    _check(W0, "W0", (B, H, d, d), torch.float32)
+    if eta is not None:
+        _check(eta, "eta", (B, H, T), torch.float32)
+    _check(Z, "Z", (B, H, T, d), K.dtype)
+    _check(W_out, "W_out", (B, H, d, d), torch.float32)
+    rc = lib().ttt_linear_fwd_noalloc(K.data_ptr(), Q.data_ptr(), V.data_ptr(), _ptr(eta),
+                                      float(eta_scalar), W0.data_ptr(), Z.data_ptr(),
+                                      W_out.data_ptr(), B, H, T, d, int(chunk), _io_dtype(K),
+                                      _stream(K.device, stream))
+    if rc != OK:
+        raise TTTError(rc, "ttt_linear_fwd_noalloc")
+    return Z, W_out
+
+
+def linear_noalloc_scratch_bytes() -> int:
+    return int(lib().ttt_linear_noalloc_scratch_bytes())
 
 
 def linear_bwd_workspace_bytes(B, H, T, d, chunk, io_dtype) -> int:

@@ -413,6 +413,36 @@ def test_plan_selection_and_workspace_are_host_only():
         2 * (2 * 256 * 64 + 256 + 64) * 4
 
 
+def _noalloc(**kw):
+    a = dict(K=FAKE, Q=FAKE, V=FAKE, eta=None, eta_scalar=1.0 / 2048, W0=FAKE, Z=FAKE, W=FAKE,
+             B=1, H=16, T=131072, d=128, chunk=2048, io=1, stream=None)
+    a.update(kw)
+    return ttt.lib().ttt_linear_fwd_noalloc(a["K"], a["Q"], a["V"], a["eta"], a["eta_scalar"],
+                                            a["W0"], a["Z"], a["W"], a["B"], a["H"], a["T"],
+                                            a["d"], a["chunk"], a["io"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), ttt.ERR_WORKSPACE),            # 160 MiB of workspace > the 64 MiB scratch
+    (dict(H=7), ttt.ERR_WORKSPACE),         # 70 MiB
+    (dict(K=None), ttt.ERR_INVALID_ARG),
+    (dict(Z=MISALIGNED), ttt.ERR_INVALID_ARG),
+    (dict(eta_scalar=math.nan), ttt.ERR_INVALID_ARG),
+    (dict(d=48), ttt.ERR_UNSUPPORTED),
+    (dict(T=0), ttt.ERR_INVALID_ARG),
+])
+def test_noalloc_rejects_before_any_hip_call(kw, status):
+    assert _noalloc(**kw) == status
+
+
+def test_noalloc_scratch_size():
+    n = ttt.linear_noalloc_scratch_bytes()
+    assert n == 64 << 20
+    # the largest large-chunk shapes that fit: 6 heads x 131072 tokens at d = 128
+    assert ttt.linear_workspace_bytes(1, 6, 131072, 128, 2048, ttt.DTYPE_BF16) <= n
+    assert ttt.linear_workspace_bytes(1, 7, 131072, 128, 2048, ttt.DTYPE_BF16) > n
+
+
 def test_binding_refuses_host_tensors():
     torch = pytest.importorskip("torch")
     K = torch.zeros(1, 1, 16, 16)
