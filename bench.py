@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "TTT scan tokens/sec (all heads) + % of HBM/MFMA roofline, b=16 d=64"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFS = 2500.0           # MI355X dense bf16 MFMA
-PLANS = {"auto": 0, "generic": 1, "mfma": 2, "bigchunk": 3}
+PLANS = {"auto": 0, "generic": 1, "mfma": 2, "bigchunk": 3, "split": 4}
 # sources whose change invalidates a stored counter profile, per kernel family (the
 # host-side api.cpp only validates and dispatches; the plan is part of a profile's
 # file name)

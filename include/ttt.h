@@ -90,8 +90,14 @@ typedef enum {
                                    cores, d in {32, 64, 128}, chunk <= 16 or a multiple
                                    of 16.  fp32 I/O: fp32 matrix cores, d in {16, 32,
                                    64, 128}, any chunk (not for packed documents) */
-    TTT_PLAN_BIGCHUNK = 3       /* bf16 matrix cores, three stages, d in {64, 128}, chunk a
+    TTT_PLAN_BIGCHUNK = 3,      /* bf16 matrix cores, three stages, d in {64, 128}, chunk a
                                    multiple of 32 >= 128 */
+    TTT_PLAN_SPLIT = 4          /* bf16 matrix cores, inclusive read, d = 64, chunk 16, T a
+                                   multiple of 16 and >= 2048, at most 32 (batch, head)
+                                   slices: the sequence in two segments scanned at once,
+                                   the second from zero and from the identity, joined by
+                                   a fix-up pass (workspace: (T - T1) d bf16 + 3 d^2
+                                   fp32 per slice, T1 ~ 0.64 T) */
 } ttt_plan;
 
 /* Read order of a chunk's tokens.  INCLUSIVE: token t reads with the chunk's
@@ -287,16 +293,18 @@ int ttt_linear_fwd_ex(const void* K, const void* Q, const void* V,
 
 /* ttt_linear_fwd for callers that cannot allocate device memory: code being
  * captured into a HIP graph, tight serving loops, harnesses that forbid
- * hipMalloc.  Same arguments as ttt_linear_fwd without the workspace: the plan
- * that needs one (TTT_PLAN_BIGCHUNK, chunks of 128+ tokens) runs in a static
- * device array of the library, TTT_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU.  The
- * array is part of the library's code object: each GPU holds it from the
- * library's first use there until the process ends.  The call allocates
- * nothing and frees nothing.
- *   - Shapes whose workspace (ttt_linear_workspace_bytes_ex for the AUTO plan)
- *     exceeds 64 MiB return TTT_ERR_WORKSPACE before any HIP call (for example
- *     16 heads x 131072 tokens at d = 128, chunk 2048, which needs 160 MiB: use
- *     ttt_linear_fwd with a caller workspace there).
+ * hipMalloc.  Same arguments as ttt_linear_fwd without the workspace: the plans
+ * that need one (TTT_PLAN_BIGCHUNK for chunks of 128+ tokens, TTT_PLAN_SPLIT for
+ * a few long chunk-16 heads) run in a static device array of the library,
+ * TTT_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU.  The array is part of the library's
+ * code object: each GPU holds it from the library's first use there until the
+ * process ends.  The call allocates nothing and frees nothing.
+ *   - The plan is AUTO's, except that a TTT_PLAN_SPLIT shape whose workspace
+ *     exceeds 64 MiB runs TTT_PLAN_MFMA, which needs none.
+ *   - Other shapes whose workspace (ttt_linear_workspace_bytes_ex for the AUTO
+ *     plan) exceeds 64 MiB return TTT_ERR_WORKSPACE before any HIP call (for
+ *     example 16 heads x 131072 tokens at d = 128, chunk 2048, which needs
+ *     160 MiB: use ttt_linear_fwd with a caller workspace there).
  *   - The scratch of the caller's current device is used; `stream` must belong
  *     to that device.
  *   - Every call on one GPU shares that GPU's array: calls that overlap in time
@@ -342,12 +350,15 @@ int ttt_mlp_select_plan(int B, int H, int T, int d, int chunk, int io_dtype, int
  * A present bias is part of the state and takes the same gradient step; an
  * absent one is a model without that bias.
  * Operand range of the matrix-core plan (bf16 I/O, d = 64, chunk <= 16, which
- * AUTO picks): its products take fp16 operands with fp32 accumulation.  Inputs,
- * state and intermediate values of magnitude up to 65504 keep their bf16 value
- * exactly when it is at least 2^-14 in magnitude; smaller ones are rounded to
- * fp16's subnormal spacing of 2^-24, and values past 65504 overflow.  For data
- * outside that range, call ttt_mlp_fwd_ex with TTT_PLAN_GENERIC (fp32 vector
- * ALU, any magnitude). */
+ * AUTO picks): its products take fp16 operands with fp32 accumulation.  The fp16
+ * operands are K, Q, the states W1 and W2, the activations gelu(W1 k + b1), the
+ * prediction error E = f(k) - v, the eta-scaled gradients eta E and
+ * eta (W2^T E) * gelu', and the token scores k_s . q_t.  Each of them must stay
+ * below 65504 in magnitude: past it the operand overflows and the outputs turn
+ * non-finite.  Values of at least 2^-14 keep their bf16 value exactly; smaller
+ * ones are rounded to fp16's subnormal spacing of 2^-24 (so a tiny eta with a
+ * tiny error loses precision).  For data outside that range, call ttt_mlp_fwd_ex
+ * with TTT_PLAN_GENERIC (fp32 vector ALU, any magnitude). */
 int ttt_mlp_fwd(const void* K, const void* Q, const void* V,
                 const float* eta, float eta_scalar,
                 const float* W1_0, const float* b1_0,

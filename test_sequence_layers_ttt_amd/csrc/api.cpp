@@ -31,7 +31,7 @@ int linear_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan,
 {
     if (!dims_ok(B, H, T, d, chunk)) return TTT_ERR_INVALID_ARG;
     if (io_dtype != TTT_DTYPE_F32 && io_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARG;
-    if (plan < TTT_PLAN_AUTO || plan > TTT_PLAN_BIGCHUNK) return TTT_ERR_INVALID_ARG;
+    if (plan < TTT_PLAN_AUTO || plan > TTT_PLAN_SPLIT) return TTT_ERR_INVALID_ARG;
     if (read_mode != TTT_READ_INCLUSIVE && read_mode != TTT_READ_CHUNK_START)
         return TTT_ERR_INVALID_ARG;
     if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
@@ -41,14 +41,19 @@ int linear_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan,
     const bool mfma = read_mode == TTT_READ_INCLUSIVE &&
                       (bf16 ? linear_mfma_supported(d, chunk, bf16) : linear_f32_supported(d));
     const bool big = linear_bigchunk_supported(d, chunk, bf16);
+    const bool split = read_mode == TTT_READ_INCLUSIVE &&
+                       linear_split_supported(B * H, T, d, chunk, bf16);
     switch (plan) {
     case TTT_PLAN_GENERIC: return TTT_PLAN_GENERIC;
     case TTT_PLAN_MFMA: return mfma ? TTT_PLAN_MFMA : TTT_ERR_UNSUPPORTED;
     case TTT_PLAN_BIGCHUNK: return big ? TTT_PLAN_BIGCHUNK : TTT_ERR_UNSUPPORTED;
+    case TTT_PLAN_SPLIT: return split ? TTT_PLAN_SPLIT : TTT_ERR_UNSUPPORTED;
     default: break;
     }
     // chunks of 128+ tokens: the three-stage path spreads the chunks over the GPU
     if (big) return TTT_PLAN_BIGCHUNK;
+    // few heads: two segments along T use the compute units the heads leave idle
+    if (split) return TTT_PLAN_SPLIT;
     if (mfma) return TTT_PLAN_MFMA;
     return TTT_PLAN_GENERIC;
 }
@@ -57,13 +62,14 @@ int mlp_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan)
 {
     if (!dims_ok(B, H, T, d, chunk)) return TTT_ERR_INVALID_ARG;
     if (io_dtype != TTT_DTYPE_F32 && io_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARG;
-    if (plan < TTT_PLAN_AUTO || plan > TTT_PLAN_BIGCHUNK) return TTT_ERR_INVALID_ARG;
+    if (plan < TTT_PLAN_AUTO || plan > TTT_PLAN_SPLIT) return TTT_ERR_INVALID_ARG;
     if (d != 16 && d != 32 && d != 64) return TTT_ERR_UNSUPPORTED;
     const bool mfma = mlp_mfma_supported(d, chunk, io_dtype == TTT_DTYPE_BF16);
     switch (plan) {
     case TTT_PLAN_GENERIC: return TTT_PLAN_GENERIC;
     case TTT_PLAN_MFMA: return mfma ? TTT_PLAN_MFMA : TTT_ERR_UNSUPPORTED;
-    case TTT_PLAN_BIGCHUNK: return TTT_ERR_UNSUPPORTED;
+    case TTT_PLAN_BIGCHUNK:
+    case TTT_PLAN_SPLIT: return TTT_ERR_UNSUPPORTED;
     default: break;
     }
     return mfma ? TTT_PLAN_MFMA : TTT_PLAN_GENERIC;
@@ -119,6 +125,7 @@ const char* ttt_plan_name(int plan)
     case TTT_PLAN_GENERIC: return "generic";
     case TTT_PLAN_MFMA: return "mfma";
     case TTT_PLAN_BIGCHUNK: return "bigchunk";
+    case TTT_PLAN_SPLIT: return "split";
     default: return "unknown plan";
     }
 }
@@ -139,6 +146,7 @@ size_t ttt_linear_workspace_bytes_ex(int B, int H, int T, int d, int chunk, int 
 {
     int p = linear_plan(B, H, T, d, chunk, io_dtype, plan);
     if (p == TTT_PLAN_BIGCHUNK) return linear_bigchunk_workspace(B * H, T, d, chunk);
+    if (p == TTT_PLAN_SPLIT) return linear_split_workspace(B * H, T, d);
     return 0;
 }
 
@@ -147,7 +155,7 @@ size_t ttt_linear_workspace_bytes(int B, int H, int T, int d, int chunk)
 {
     size_t n = 0;
     for (int io : {(int)TTT_DTYPE_F32, (int)TTT_DTYPE_BF16})
-        for (int plan = TTT_PLAN_AUTO; plan <= TTT_PLAN_BIGCHUNK; ++plan) {
+        for (int plan = TTT_PLAN_AUTO; plan <= TTT_PLAN_SPLIT; ++plan) {
             const size_t m = ttt_linear_workspace_bytes_ex(B, H, T, d, chunk, io, plan);
             n = m > n ? m : n;
         }
@@ -196,6 +204,7 @@ int ttt_linear_fwd_ex(const void* K, const void* Q, const void* V,
     case TTT_PLAN_MFMA:
         return launch_status(a.bf16 ? launch_linear_mfma(a, s) : launch_linear_f32(a, s));
     case TTT_PLAN_BIGCHUNK: return launch_status(launch_linear_bigchunk(a, s));
+    case TTT_PLAN_SPLIT: return launch_status(launch_linear_split(a, s));
     default: return launch_status(launch_linear_generic(a, s));
     }
 }
@@ -212,9 +221,15 @@ int ttt_linear_fwd_noalloc(const void* K, const void* Q, const void* V,
         !aligned(W0, 16) || !aligned(W_out, 16))
         return TTT_ERR_INVALID_ARG;
     if (eta ? !aligned(eta, 4) : !std::isfinite(eta_scalar)) return TTT_ERR_INVALID_ARG;
-    const int p = linear_plan(B, H, T, d, chunk, io_dtype, TTT_PLAN_AUTO);
+    int p = linear_plan(B, H, T, d, chunk, io_dtype, TTT_PLAN_AUTO);
     if (p < 0) return p;
-    const size_t need = ttt_linear_workspace_bytes_ex(B, H, T, d, chunk, io_dtype, p);
+    size_t need = ttt_linear_workspace_bytes_ex(B, H, T, d, chunk, io_dtype, p);
+    if (p == TTT_PLAN_SPLIT && need > kScratchBytes) {
+        // too long for the two-segment plan's workspace: the chunk-by-chunk plan
+        // runs the same shape without one
+        p = TTT_PLAN_MFMA;
+        need = ttt_linear_workspace_bytes_ex(B, H, T, d, chunk, io_dtype, p);
+    }
     if (need > kScratchBytes) return TTT_ERR_WORKSPACE;
     void* ws = nullptr;
     if (need > 0) {
@@ -366,13 +381,14 @@ int ttt_linear_select_plan_varlen(int n_docs, int H, int total_T, int d, int chu
         (long double)n_docs * H * 64 >= 2.0e9L)
         return TTT_ERR_INVALID_ARG;
     if (io_dtype != TTT_DTYPE_F32 && io_dtype != TTT_DTYPE_BF16) return TTT_ERR_INVALID_ARG;
-    if (plan < TTT_PLAN_AUTO || plan > TTT_PLAN_BIGCHUNK) return TTT_ERR_INVALID_ARG;
+    if (plan < TTT_PLAN_AUTO || plan > TTT_PLAN_SPLIT) return TTT_ERR_INVALID_ARG;
     if (d != 16 && d != 32 && d != 64 && d != 128) return TTT_ERR_UNSUPPORTED;
     const bool mfma = chunk <= 16 && linear_mfma_supported(d, chunk, io_dtype == TTT_DTYPE_BF16);
     switch (plan) {
     case TTT_PLAN_GENERIC: return TTT_PLAN_GENERIC;
     case TTT_PLAN_MFMA: return mfma ? TTT_PLAN_MFMA : TTT_ERR_UNSUPPORTED;
-    case TTT_PLAN_BIGCHUNK: return TTT_ERR_UNSUPPORTED;
+    case TTT_PLAN_BIGCHUNK:
+    case TTT_PLAN_SPLIT: return TTT_ERR_UNSUPPORTED;
     default: return mfma ? TTT_PLAN_MFMA : TTT_PLAN_GENERIC;
     }
 }
@@ -420,7 +436,7 @@ size_t ttt_mlp_workspace_bytes(int B, int H, int T, int d, int chunk)
 {
     size_t n = 0;
     for (int io : {(int)TTT_DTYPE_F32, (int)TTT_DTYPE_BF16})
-        for (int plan = TTT_PLAN_AUTO; plan <= TTT_PLAN_BIGCHUNK; ++plan) {
+        for (int plan = TTT_PLAN_AUTO; plan <= TTT_PLAN_SPLIT; ++plan) {
             const size_t m = ttt_mlp_workspace_bytes_ex(B, H, T, d, chunk, io, plan);
             n = m > n ? m : n;
         }

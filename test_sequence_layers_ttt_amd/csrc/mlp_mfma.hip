@@ -17,7 +17,10 @@
 // rounded to nearest): the state takes about 500 updates per sequence at the
 // reference sizes and bf16's 8-bit significand let their rounding errors
 // accumulate to ~2% of the state; fp16's 11 bits keep it ~8x smaller at the
-// same matrix-core rate.  Values must stay inside fp16 range (|x| < 65504).
+// same matrix-core rate.  The fp16 operands are K, Q, W1, W2, A and A', E, the
+// token scores and the eta-scaled gradients (-eta E and -eta D: D itself, a sum of
+// |W2| |E| over the output features, can pass fp16's range where eta D does not);
+// each must stay below 65504 in magnitude, or the outputs turn non-finite.
 //
 // One workgroup of four waves per (batch, head); wave w owns hidden units
 // 64w .. 64w+63, i.e. rows of W1 and columns of W2.  Each product keeps one
@@ -303,7 +306,7 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
         u32x4 Ef[kNB / 2];
 #pragma unroll
         for (int m = 0; m < kNB / 2; ++m) Ef[m] = pack_f16x8(E[2 * m], E[2 * m + 1]);
-        u32x2 Db[kUB], DSb[kUB];
+        u32x2 DSb[kUB];     // -eta D_c: the scaled gradient stays small where D may not
         f32x4 db1 = {0, 0, 0, 0};
 #pragma unroll
         for (int ub = 0; ub < kUB; ++ub) {
@@ -318,12 +321,11 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
                 d = mfma32h(Ef[m], u32x4{w2t[2 * m].x, w2t[2 * m].y, w2t[2 * m + 1].x,
                                          w2t[2 * m + 1].y}, d);
             d = d * G[ub];
-            Db[ub] = pack_f16x4(d);
             const f32x4 ds = -er * d;
             DSb[ub] = pack_f16x4(ds);
             if (HAS_B1) db1[ub] = ds[0] + ds[1] + ds[2] + ds[3];
         }
-        // ---- scores of K_c against Q_c (causal) and K_{c+1} (all), scaled by -eta_s ----
+        // ---- scores of K_c against Q_c (causal) and K_{c+1} (all); -eta rides on D ----
         u32x2 S1q, S1k;
         {
             f32x4 sq = {0, 0, 0, 0}, sk = {0, 0, 0, 0};
@@ -335,8 +337,8 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
             f32x4 mq, mk;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                mq[r] = (4 * g + r <= c) ? -er[r] * (sq[r] + (HAS_B1 ? 1.f : 0.f)) : 0.f;
-                mk[r] = -er[r] * (sk[r] + (HAS_B1 ? 1.f : 0.f));
+                mq[r] = (4 * g + r <= c) ? sq[r] + (HAS_B1 ? 1.f : 0.f) : 0.f;
+                mk[r] = sk[r] + (HAS_B1 ? 1.f : 0.f);
             }
             S1q = pack_f16x4(mq);
             S1k = pack_f16x4(mk);
@@ -353,8 +355,8 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
                 hq = mfma32h(Qf[m], W1f[ub][m], hq);
                 hk = mfma32h(Kn[m], W1f[ub][m], hk);
             }
-            hq = mfma16h(S1q, Db[ub], hq);
-            hk = mfma16h(S1k, Db[ub], hk);
+            hq = mfma16h(S1q, DSb[ub], hq);
+            hk = mfma16h(S1k, DSb[ub], hk);
             A2b[ub] = pack_f16x4(gelu4(hq));
             f32x4 a;
             gelu_pair(hk, a, Gn[ub]);

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libttt_amd.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = 0, -1, -2, -3, -4
 DTYPE_F32, DTYPE_BF16 = 0, 1
-PLAN_AUTO, PLAN_GENERIC, PLAN_MFMA, PLAN_BIGCHUNK = 0, 1, 2, 3
+PLAN_AUTO, PLAN_GENERIC, PLAN_MFMA, PLAN_BIGCHUNK, PLAN_SPLIT = 0, 1, 2, 3, 4
 READ_INCLUSIVE, READ_CHUNK_START = 0, 1
 
 # every symbol include/ttt.h declares

@@ -45,7 +45,9 @@ def test_status_and_plan_strings():
     for s in (-1, -2, -3, -4):
         assert ttt.status_string(s) not in ("ok", "unknown status")
     assert ttt.status_string(17) == "unknown status"
-    assert [ttt.plan_name(p) for p in range(4)] == ["auto", "generic", "mfma", "bigchunk"]
+    assert [ttt.plan_name(p) for p in range(5)] == ["auto", "generic", "mfma", "bigchunk",
+                                                    "split"]
+    assert ttt.plan_name(5) == "unknown plan"
 
 
 def _linear(**kw):
@@ -133,7 +135,7 @@ def test_size_only_workspace_queries_cover_every_plan():
                   (2, 3, 100, 32, 40)]:
         n = ttt.linear_workspace_bytes(*shape)
         for io in (ttt.DTYPE_F32, ttt.DTYPE_BF16):
-            for plan in range(4):
+            for plan in range(5):
                 assert ttt.linear_workspace_bytes(*shape, io, plan) <= n
     assert ttt.linear_workspace_bytes(1, 2, 512, 64, 256) == \
         ttt.linear_workspace_bytes(1, 2, 512, 64, 256, ttt.DTYPE_BF16, ttt.PLAN_BIGCHUNK) > 0
@@ -141,7 +143,7 @@ def test_size_only_workspace_queries_cover_every_plan():
     for shape in [(1, 2, 64, 64, 16), (1, 2, 64, 64, 32), (3, 1, 50, 16, 5)]:
         n = ttt.mlp_workspace_bytes(*shape)
         for io in (ttt.DTYPE_F32, ttt.DTYPE_BF16):
-            for plan in range(4):
+            for plan in range(5):
                 assert ttt.mlp_workspace_bytes(*shape, io, plan) <= n
     assert ttt.mlp_workspace_bytes(1, 2, 64, 64, 32) == 2 * (2 * 256 * 64 + 256 + 64) * 4
 
@@ -166,6 +168,12 @@ def test_size_only_workspace_queries_cover_every_plan():
     (dict(d=0), ttt.ERR_INVALID_ARG),
     (dict(io=2), ttt.ERR_INVALID_ARG),
     (dict(plan=7), ttt.ERR_INVALID_ARG),
+    (dict(plan=5), ttt.ERR_INVALID_ARG),
+    (dict(d=64, io=1, T=4096, plan=ttt.PLAN_SPLIT), ttt.ERR_WORKSPACE),
+    (dict(d=64, io=0, T=4096, plan=ttt.PLAN_SPLIT), ttt.ERR_UNSUPPORTED),   # fp32 I/O
+    (dict(d=64, io=1, T=1024, plan=ttt.PLAN_SPLIT), ttt.ERR_UNSUPPORTED),   # too short
+    (dict(d=64, io=1, T=4100, plan=ttt.PLAN_SPLIT), ttt.ERR_UNSUPPORTED),   # T % 16
+    (dict(d=64, io=1, T=4096, B=4, H=9, plan=ttt.PLAN_SPLIT), ttt.ERR_UNSUPPORTED),  # 36 heads
     (dict(d=48), ttt.ERR_UNSUPPORTED),
     (dict(d=256), ttt.ERR_UNSUPPORTED),
     (dict(d=16, io=1, plan=ttt.PLAN_MFMA), ttt.ERR_UNSUPPORTED),
