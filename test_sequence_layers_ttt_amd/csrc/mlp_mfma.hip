@@ -22,17 +22,25 @@
 // |W2| |E| over the output features, can pass fp16's range where eta D does not);
 // each must stay below 65504 in magnitude, or the outputs turn non-finite.
 //
-// One workgroup of four waves per (batch, head); wave w owns hidden units
-// 64w .. 64w+63, i.e. rows of W1 and columns of W2.  Each product keeps one
-// index in the lanes and the contracted one in the register slots (see
-// mfma_common.h).  W2 is contracted over the hidden units for E and Z but over
-// the output features for D: the fp32 state keeps it with the output feature in
-// the lanes, and D takes the LDS transpose of its fp16 tiles each chunk.  Sums
-// over all 256 hidden units (E, A^T A', W2 A') are formed as per-wave partials
-// and added through LDS behind one barrier per chunk (the next chunk's H and E are
-// read beside this chunk's Z, see the main loop).  A, A' and E change orientation
-// through the LDS transpose read as well.  The next chunk's inputs are loaded
-// while the current one is processed.
+// One workgroup of eight waves per (batch, head), two per SIMD so that one
+// wave's waits on the matrix cores, LDS and transcendentals are filled by the
+// other's work; wave w owns hidden units 32w .. 32w+31, i.e. rows of W1 and
+// columns of W2.  Each product keeps one index in the lanes and the contracted
+// one in the register slots (see mfma_common.h).  W2 is contracted over the
+// hidden units for E and Z but over the output features for D: the fp32 state
+// keeps it with the output feature in the lanes, and D takes the LDS transpose of
+// its fp16 tiles each chunk.
+//
+// Per chunk each wave forms its partials of Z_c and E_{c+1} over its own units,
+// each with its share of the eta-weighted correction already added (the
+// correction E diag(eta) (U * (A^T A' + 1)) is linear in the per-wave sums of
+// A^T A'), and writes them to LDS.  After a barrier all 512 threads reduce the
+// eight partials, two values each: the Z values go to memory with b2 added, the
+// E values get b2 - V and are written back as the fp16 operands the next chunk
+// reads (E and -eta E); the thread that owns an output feature also keeps that
+// bias.  A second barrier publishes them.  K and Q of each chunk are staged once
+// per workgroup in LDS as fp16 rows (two chunks ahead), and both the row operand
+// and the transposed K come from that tile.
 //
 // GELU: gelu(x) = x Phi(x), gelu'(x) = Phi(x) + x phi(x), with erf from
 // Abramowitz & Stegun, Handbook of Mathematical Functions, eq. 7.1.26
@@ -48,9 +56,12 @@ namespace {
 
 constexpr int kD = 64;
 constexpr int kH = 256;
-constexpr int kWaves = 4;
-constexpr int kUB = 4;          // 16-unit hidden blocks per wave
+constexpr int kWaves = 8;
+constexpr int kUB = 2;          // 16-unit hidden blocks per wave
+constexpr int kUW = 16 * kUB;   // hidden units per wave
 constexpr int kNB = kD / 16;    // 16-feature blocks of d (input i and output o)
+constexpr int kRing = 3;        // staged chunks: the current, the next, the one arriving
+static_assert(kWaves * kUW == kH, "the waves cover the hidden units");
 
 __device__ __forceinline__ float phi_erf(float x, float& e)
 {
@@ -89,40 +100,22 @@ __device__ __forceinline__ f32x4 gelu4(f32x4 h)
     return g;
 }
 
-__device__ __forceinline__ f32x4 bf16x4_to_f32(u32x2 v)
-{
-    return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
-                 __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
-}
-
-// shared LDS layout (bytes): per-wave private areas, then the partial sums
+// LDS layout: staged inputs, per-wave transpose buffers, the shared fp16 E
+// operands and the per-wave partial sums
 struct Lds {
-    // private, per wave
-    u32x2 tA[kWaves][kUB * 64];     // A (fp16) for the transpose
-    u32x2 tA2[kWaves][kUB * 64];    // A'
-    u32x2 tE[kWaves][kNB * 64];     // -eta E
-    u32x2 tK[kWaves][kNB * 64];     // K tile for the W1 update operand
-    u32x2 tW2[kWaves][kUB * kNB * 64];  // fp16 W2 tiles for the transpose to (u, o)
-    float b2d[kWaves][kD];          // b2 update staging
-    // shared partial sums (fp32, C/D layout, one f32x4 per lane), double-buffered
-    // by chunk parity: a wave may write chunk c+1's partials while another still
-    // reads chunk c's
-    f32x4 Ep[2][kWaves][kNB][64];   // W2 A_{c+1}  (+ b2 - V_{c+1} from wave 0)
-    f32x4 S3p[2][kWaves][64];       // A_c^T A_{c+1}
-    f32x4 Zp[2][kWaves][kNB][64];   // W2 A'_c     (+ b2 from wave 0)
-    f32x4 S2p[2][kWaves][64];       // A_c^T A'_c
-};
-
-// One chunk's inputs as loaded (bf16), one chunk ahead of their use.
-struct ChunkIn {
-    u32x4 k[kNB / 2], q[kNB / 2];   // K, Q rows (lane = token), pieces at 32m + 8g
-    u32x2 v[kNB];                   // V[token][16ob + 4g ..], loaded by wave 0 only
-    f32x4 er;                       // eta of tokens 4g + r
-    float ec;                       // eta of token c
+    KQTile16<kD> kq[kRing];             // fp16 K and Q rows of three staged chunks
+    float eta[kRing][16];               // their tokens' eta (0 past a short chunk's end)
+    u32x2 tW2[kWaves][kUB * kNB * 64];  // per wave: fp16 W2 tiles for the transpose to (u, o)
+    u32x2 tA[kWaves][kUB * 64];         // per wave: A (fp16) for the transpose
+    u32x2 tA2[kWaves][kUB * 64];        // per wave: A'
+    u32x2 tE[kNB * 64];                 // -eta E (fp16), the transpose read's source layout
+    u32x4 Ef[2 * 64];                   // E (fp16) as the A operand of the D product
+    f32x4 Ep[kWaves][kNB][64];          // per wave: W2 A_{c+1} - E diag(eta) (A_c^T A_{c+1} [+ 1])
+    f32x4 Zp[kWaves][kNB][64];          // per wave: W2 A'_c  - E diag(eta) (U * (A_c^T A'_c [+ 1]))
 };
 
 template <bool FULL, bool ETA_TOKEN, bool HAS_B1, bool HAS_B2>
-__global__ __launch_bounds__(256) void mlp_mfma_kernel(
+__global__ __launch_bounds__(64 * kWaves) void mlp_mfma_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
     const float* W1_0, const float* b1_0, const float* W2_0, const float* b2_0,
@@ -132,23 +125,24 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
     extern __shared__ __align__(16) unsigned char lds_raw[];
     Lds& L = *reinterpret_cast<Lds*>(lds_raw);
 
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int c = lane & 15, g = lane >> 4;
     const int slice = blockIdx.x;
     const size_t tok0 = (size_t)slice * T;
     const float* W1s = W1_0 + (size_t)slice * kH * kD;
     const float* W2s = W2_0 + (size_t)slice * kD * kH;
-    const int ubase = 64 * w;   // first hidden unit of this wave
+    const int ubase = kUW * w;   // first hidden unit of this wave
+    const int step = chunk;      // <= 16
+    const int nchunks = (T + step - 1) / step;
 
     // ---- state in C/D tiles ----
-    // W1t[ub][ib]: lane (u, g), value r = W1[u][pi(ib, 4g + r)], u = ubase + 16ub + c
+    // W1t[ub][ib]: lane (u, g), value r = W1[u][pi(ib, 4g + r)], u = ubase + 16ub + c,
+    //              pi(2m + h, 4g + r) = 32m + 8g + 4h + r
     // W2o[ob][ub]: lane (o, g), value r = W2[o][ubase + 16ub + 4g + r], o = 16ob + c
-    // (W2 with the hidden unit in the lanes, needed for D, is the LDS transpose of
-    // W2o's fp16 tiles, formed per chunk)
     f32x4 W1t[kUB][kNB], W2o[kNB][kUB];
-    f32x4 b1r;      // b1[ubase + 16ub + c] for ub = 0..3
-    f32x4 b2r[kNB]; // b2[16ob + 4g + r]
+    float b1r[kUB];   // b1[ubase + 16ub + c]
 #pragma unroll
     for (int ub = 0; ub < kUB; ++ub) {
         const float* row = W1s + (size_t)(ubase + 16 * ub + c) * kD;
@@ -162,47 +156,70 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
             W2o[ob][ub] = *(const f32x4*)(W2s + (size_t)(16 * ob + c) * kH + ubase + 16 * ub + 4 * g);
         b1r[ub] = HAS_B1 ? b1_0[(size_t)slice * kH + ubase + 16 * ub + c] : 0.f;
     }
-#pragma unroll
-    for (int ob = 0; ob < kNB; ++ob)
-        b2r[ob] = HAS_B2 ? *(const f32x4*)(b2_0 + (size_t)slice * kD + 16 * ob + 4 * g)
-                         : f32x4{0, 0, 0, 0};
 
-    const int step = chunk;   // <= 16
-    const int nchunks = (T + step - 1) / step;
-    // Loads one chunk's inputs; chunks past the end re-read the last one (their
-    // values are never used).  Rows past a short chunk's end re-read row 0 of it;
-    // their tokens are neutralised with eta = 0 where the chunk is used.
-    auto load_in = [&](ChunkIn& t, int ci) {
+    // ---- the reduction's share: two values of each 16 x 64 (token, output) tile ----
+    // value pair p = tid of the C/D layout [ob][lane'][r]: ob = p / 128,
+    // lane' = (p / 2) % 64, r = 2 (p % 2) + {0, 1}
+    const int rv = 2 * tid;                    // first float of the pair in a partial
+    const int rob = tid >> 7, rln = (tid >> 1) & 63, rrp = tid & 1;
+    const int rtok = rln & 15;                 // token within the chunk
+    const int rout = 16 * rob + 4 * (rln >> 4) + 2 * rrp;   // first output feature
+    f32x2 b2v = {0.f, 0.f};
+    if (HAS_B2) b2v = *(const f32x2*)(b2_0 + (size_t)slice * kD + rout);
+    f32x2 eprev = {0.f, 0.f};                  // this pair of E_c (for the b2 step)
+
+    // ---- staging: thread t < 256 carries granule t % 128 of K (t < 128) or Q,
+    // threads 256..271 the eta of one token ----
+    const bool ld_kq = tid < 256;
+    const int lwhich = (tid >> 7) & 1, lrow = (tid >> 3) & 15, lgr = tid & 7;
+    const int lpos = lrow * (kD / 8) + (lgr ^ tile16_swizzle<kD>(lrow));
+    const bool ld_eta = tid >= 256 && tid < 272;
+    const int etok = tid - 256;
+    auto chunk_n = [&](int cc) { return FULL ? 16 : min(step, T - cc * step); };
+    auto stage_load = [&](int ci, u32x4& r, float& e) {
         const int cc = ci < nchunks ? ci : nchunks - 1;
-        const int s0 = cc * step;
-        const int n = FULL ? 16 : min(step, T - s0);
-        const size_t row = (tok0 + s0 + ((FULL || c < n) ? c : 0)) * kD;
-#pragma unroll
-        for (int m = 0; m < kNB / 2; ++m) {
-            t.k[m] = *(const u32x4*)(K + row + 32 * m + 8 * g);
-            t.q[m] = *(const u32x4*)(Q + row + 32 * m + 8 * g);
+        const int s0 = cc * step, n = chunk_n(cc);
+        if (ld_kq) {
+            const int row = (FULL || lrow < n) ? lrow : 0;
+            r = *(const u32x4*)((lwhich ? Q : K) + (tok0 + s0 + row) * kD + 8 * lgr);
         }
-        if (w == 0) {
-#pragma unroll
-            for (int ob = 0; ob < kNB; ++ob) t.v[ob] = *(const u32x2*)(V + row + 16 * ob + 4 * g);
-        } else {
-#pragma unroll
-            for (int ob = 0; ob < kNB; ++ob) t.v[ob] = u32x2{0u, 0u};
-        }
-        if (ETA_TOKEN) {
-            const float* e = eta + tok0 + s0;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) t.er[r] = e[(FULL || 4 * g + r < n) ? 4 * g + r : 0];
-            t.ec = e[(FULL || c < n) ? c : 0];
-        } else {
-            t.er = f32x4{eta_scalar, eta_scalar, eta_scalar, eta_scalar};
-            t.ec = eta_scalar;
+        if (ld_eta) {
+            if (ETA_TOKEN) e = (FULL || etok < n) ? eta[tok0 + s0 + etok] : 0.f;
+            else e = (FULL || etok < n) ? eta_scalar : 0.f;
         }
     };
-    auto to_f16 = [&](const u32x4 (&x)[kNB / 2], u32x4 (&y)[kNB / 2]) {
-#pragma unroll
-        for (int m = 0; m < kNB / 2; ++m) y[m] = bf16x8_to_f16x8(x[m]);
+    auto stage_store = [&](int ci, const u32x4& r, float e) {
+        const int sl = ci % kRing;
+        if (ld_kq) L.kq[sl].g[lwhich][lpos] = bf16x8_to_f16x8(r);
+        if (ld_eta) L.eta[sl][etok] = e;
     };
+    // V of the reduction's pair for the chunk ci (clamped rows as above)
+    auto v_load = [&](int ci) {
+        const int cc = ci < nchunks ? ci : nchunks - 1;
+        const int s0 = cc * step, n = chunk_n(cc);
+        const int row = (FULL || rtok < n) ? rtok : 0;
+        return *(const unsigned*)(V + (tok0 + s0 + row) * kD + rout);
+    };
+
+    // row operand of a staged tile: lane (c, g) gets granules 4m + g of row c
+    auto row_operand = [&](const u32x4* t, u32x4 (&op)[kNB / 2]) {
+#pragma unroll
+        for (int m = 0; m < kNB / 2; ++m) op[m] = t[c * (kD / 8) + ((4 * m + g) ^ tile16_swizzle<kD>(c))];
+    };
+    // K with the input feature in the lanes and tokens 4g..4g+3 in the slots, for
+    // the feature blocks ib of the W1t layout (transpose read of the staged rows)
+    auto k_transposed = [&](const u32x4* t, u32x2 (&kt)[kNB]) {
+        const int r = (lane >> 2) & 3, q = lane & 3;
+        const int row = 4 * g + r;
+        const u32x2* base = reinterpret_cast<const u32x2*>(t) + row * (2 * (kD / 8));
+#pragma unroll
+        for (int ib = 0; ib < kNB; ++ib) {
+            auto pt = (__attribute__((address_space(3))) s16x4*)(
+                base + 2 * ((4 * (ib >> 1) + q) ^ tile16_swizzle<kD>(row)) + (ib & 1));
+            kt[ib] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(pt));
+        }
+    };
+
     // fp16 state operands: W1 rows (B operand over the input features) and W2o tiles
     u32x4 W1f[kUB][kNB / 2];
     u32x2 W2f[kNB][kUB];
@@ -217,37 +234,55 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
 #pragma unroll
             for (int ub = 0; ub < kUB; ++ub) W2f[ob][ub] = pack_f16x4(W2o[ob][ub]);
     };
-    auto w2pair = [&](int ob, int m) {
-        return u32x4{W2f[ob][2 * m].x, W2f[ob][2 * m].y, W2f[ob][2 * m + 1].x, W2f[ob][2 * m + 1].y};
-    };
     // A (fp16, lane = hidden unit) -> tokens in the lanes, hidden units in the slots
-    auto transpose_a = [&](u32x2* buf, const u32x2 (&ab)[kUB], u32x4 (&ta)[kUB / 2]) {
+    auto transpose_a = [&](u32x2* buf, const u32x2 (&ab)[kUB], u32x4& ta) {
         u32x2 t[kUB];
 #pragma unroll
         for (int ub = 0; ub < kUB; ++ub) t[ub] = lds_transpose16(buf + ub * 64, ab[ub], lane);
-#pragma unroll
-        for (int m = 0; m < kUB / 2; ++m) ta[m] = u32x4{t[2 * m].x, t[2 * m].y, t[2 * m + 1].x, t[2 * m + 1].y};
+        ta = u32x4{t[0].x, t[0].y, t[1].x, t[1].y};
     };
-    // partial of W2 X (o x t) over this wave's units, plus `base` on wave 0
-    auto w2_partial = [&](const u32x4 (&tx)[kUB / 2], int ob, f32x4 base) {
-        f32x4 e = (w == 0) ? base : f32x4{0, 0, 0, 0};
+    // W2 X (o x t) over this wave's 32 units
+    auto w2_partial = [&](const u32x4& tx, int ob) {
+        const u32x4 a = {W2f[ob][0].x, W2f[ob][0].y, W2f[ob][1].x, W2f[ob][1].y};
+        return mfma32h(a, tx, f32x4{0, 0, 0, 0});
+    };
+    // the reduction of one partial set: this thread's pair, summed over the waves
+    auto reduce_pair = [&](const f32x4 (*P)[kNB][64]) {
+        const float* base = reinterpret_cast<const float*>(P) + rv;
+        f32x2 s = *(const f32x2*)base;
 #pragma unroll
-        for (int m = 0; m < kUB / 2; ++m) e = mfma32h(w2pair(ob, m), tx[m], e);
-        return e;
+        for (int v = 1; v < kWaves; ++v) s += *(const f32x2*)(base + v * (kNB * 64 * 4));
+        return s;
+    };
+    // publish E (this thread's pair, token rtok of the chunk whose eta sits in
+    // slot sl): as fp16 for the D product and, times -eta, for the transposes
+    auto publish_e = [&](f32x2 e, int sl) {
+        const float et = L.eta[sl][rtok];
+        unsigned* ef = reinterpret_cast<unsigned*>(L.Ef);
+        ef[((rob >> 1) * 64 + rln) * 4 + (rob & 1) * 2 + rrp] = pack_f16x2(e.x, e.y);
+        unsigned* te = reinterpret_cast<unsigned*>(L.tE);
+        te[(rob * 64 + 4 * rtok + (rln >> 4)) * 2 + rrp] = pack_f16x2(-et * e.x, -et * e.y);
     };
 
-    // ---- chunk 0's forward at the initial state: H, A, gelu'(H), E ----
-    ChunkIn cur, nx, nx2;
-    load_in(cur, 0);
-    load_in(nx, 1);
+    // ---- prologue: stage chunks 0 and 1, hold chunk 2 ----
+    u32x4 sr = {0u, 0u, 0u, 0u};
+    float se = 0.f;
+    stage_load(0, sr, se);
+    stage_store(0, sr, se);
+    stage_load(1, sr, se);
+    stage_store(1, sr, se);
+    stage_load(2, sr, se);
+    unsigned vnext = v_load(0);
     pack_state();
-    u32x4 Kc[kNB / 2];          // K of the current chunk (fp16, lane = token)
-    to_f16(cur.k, Kc);
-    f32x4 G[kUB];               // gelu'(H_c)
-    u32x2 Ab[kUB];              // A_c (fp16, lane = hidden unit, rows = tokens)
-    u32x4 tAf[kUB / 2];         // A_c with tokens in the lanes
-    f32x4 E[kNB];               // E_c (lanes = tokens, rows = output features)
+    __syncthreads();
+
+    // ---- chunk 0's forward at the initial state: H, A, gelu'(H), E ----
+    f32x4 G[kUB];      // gelu'(H_c) of this wave's units
+    u32x2 Ab[kUB];     // A_c (fp16, lane = hidden unit, rows = tokens)
+    u32x4 tAf;         // A_c with tokens in the lanes
     {
+        u32x4 Kc[kNB / 2];
+        row_operand(L.kq[0].g[0], Kc);
 #pragma unroll
         for (int ub = 0; ub < kUB; ++ub) {
             f32x4 h = {b1r[ub], b1r[ub], b1r[ub], b1r[ub]};
@@ -259,55 +294,53 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
         }
         transpose_a(L.tA[w], Ab, tAf);
 #pragma unroll
-        for (int ob = 0; ob < kNB; ++ob)
-            L.Ep[1][w][ob][lane] = w2_partial(tAf, ob, b2r[ob] - bf16x4_to_f32(cur.v[ob]));
-        __syncthreads();
-#pragma unroll
-        for (int ob = 0; ob < kNB; ++ob) {
-            f32x4 e = L.Ep[1][0][ob][lane];
-#pragma unroll
-            for (int v = 1; v < kWaves; ++v) e += L.Ep[1][v][ob][lane];
-            E[ob] = e;
-        }
+        for (int ob = 0; ob < kNB; ++ob) L.Ep[w][ob][lane] = w2_partial(tAf, ob);
     }
+    __syncthreads();
+    {
+        f32x2 e = reduce_pair(L.Ep);
+        const unsigned v = vnext;
+        e.x += b2v.x - __uint_as_float(v << 16);
+        e.y += b2v.y - __uint_as_float(v & 0xffff0000u);
+        eprev = e;
+        publish_e(e, 0);
+        vnext = v_load(1);
+    }
+    __syncthreads();
 
     // Chunk c, from its start state and its forward (H_c, A_c, E_c): the backward
     // D_c, then two reads of the chunk's updated model -- Q_c (the output, causal
     // and inclusive) and K_{c+1} (the next chunk's forward; every token of chunk c
-    // precedes it) -- and one barrier for all the sums over hidden units:
+    // precedes it):
     //   H'      = W1 Q_c     + b1 - D_c diag(eta) (U * (K_c^T Q_c + 1))
     //   H_{c+1} = W1 K_{c+1} + b1 - D_c diag(eta) (K_c^T K_{c+1} + 1)
     //   Z_c     = W2 A'      + b2 - E_c diag(eta) (U * (A_c^T A' + 1))
     //   E_{c+1} = W2 A_{c+1} + b2 - V_{c+1} - E_c diag(eta) (A_c^T A_{c+1} + 1)
-    // The state update itself is off the chain: only the next chunk's operands
-    // need it.
     for (int ci = 0; ci < nchunks; ++ci) {
         const int s0 = ci * step;
-        const int n = FULL ? 16 : min(step, T - s0);
-        const int pb = ci & 1;
-        load_in(nx2, ci + 2);
-        u32x4 Qf[kNB / 2], Kn[kNB / 2];
-        to_f16(cur.q, Qf);
-        to_f16(nx.k, Kn);
-        f32x4 er = cur.er;   // zero for padding tokens
-        float ec = cur.ec;
-        if (!FULL) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) er[r] = (4 * g + r < n) ? er[r] : 0.f;
-            ec = (c < n) ? ec : 0.f;
-        }
+        const int n = chunk_n(ci);
+        const int sl = ci % kRing, sn = (ci + 1) % kRing;
 
-        // -eta E_c with o in the lanes and tokens in the slots
-        u32x2 tE[kNB];
-#pragma unroll
-        for (int ob = 0; ob < kNB; ++ob)
-            tE[ob] = lds_transpose16(&L.tE[w][ob * 64], pack_f16x4(-ec * E[ob]), lane);
-        // ---- D^T (t x u) = (E^T W2) * gelu'(H) ----
+        // the staged chunk ci + 2 goes to the slot chunk ci - 1 left (read before the
+        // last barrier); chunk ci + 3 is fetched
+        stage_store(ci + 2, sr, se);
+        stage_load(ci + 3, sr, se);
+
+        // E_c (fp16) and -eta E_c with o in the lanes and tokens in the slots
         u32x4 Ef[kNB / 2];
 #pragma unroll
-        for (int m = 0; m < kNB / 2; ++m) Ef[m] = pack_f16x8(E[2 * m], E[2 * m + 1]);
-        u32x2 DSb[kUB];     // -eta D_c: the scaled gradient stays small where D may not
-        f32x4 db1 = {0, 0, 0, 0};
+        for (int m = 0; m < kNB / 2; ++m) Ef[m] = L.Ef[m * 64 + lane];
+        u32x2 tE[kNB];
+#pragma unroll
+        for (int ob = 0; ob < kNB; ++ob) {
+            auto p = (__attribute__((address_space(3))) s16x4*)(&L.tE[ob * 64] + lane);
+            tE[ob] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+        }
+        const f32x4 er = *(const f32x4*)&L.eta[sl][4 * g];   // zero for padding tokens
+
+        // ---- D^T (t x u) = (E^T W2) * gelu'(H), scaled by -eta ----
+        u32x2 DSb[kUB];
+        float db1[kUB];
 #pragma unroll
         for (int ub = 0; ub < kUB; ++ub) {
             // W2 with lanes = hidden unit u, slots = output features (transpose read)
@@ -320,12 +353,15 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
             for (int m = 0; m < kNB / 2; ++m)
                 d = mfma32h(Ef[m], u32x4{w2t[2 * m].x, w2t[2 * m].y, w2t[2 * m + 1].x,
                                          w2t[2 * m + 1].y}, d);
-            d = d * G[ub];
-            const f32x4 ds = -er * d;
+            const f32x4 ds = -er * (d * G[ub]);
             DSb[ub] = pack_f16x4(ds);
-            if (HAS_B1) db1[ub] = ds[0] + ds[1] + ds[2] + ds[3];
+            db1[ub] = ds[0] + ds[1] + ds[2] + ds[3];
         }
         // ---- scores of K_c against Q_c (causal) and K_{c+1} (all); -eta rides on D ----
+        u32x4 Kc[kNB / 2], Qf[kNB / 2], Kn[kNB / 2];
+        row_operand(L.kq[sl].g[0], Kc);
+        row_operand(L.kq[sl].g[1], Qf);
+        row_operand(L.kq[sn].g[0], Kn);
         u32x2 S1q, S1k;
         {
             f32x4 sq = {0, 0, 0, 0}, sk = {0, 0, 0, 0};
@@ -362,73 +398,30 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
             gelu_pair(hk, a, Gn[ub]);
             An[ub] = pack_f16x4(a);
         }
-        u32x4 tA2f[kUB / 2], tAn[kUB / 2];
+        u32x4 tA2f, tAn;
         transpose_a(L.tA2[w], A2b, tA2f);
         transpose_a(L.tA[w], An, tAn);
-        // ---- per-wave partials of Z_c and E_{c+1} ----
+        // ---- this wave's partials of Z_c and E_{c+1}, corrections included (the
+        // bias "+1" terms once, on wave 0) ----
         {
-            f32x4 s2 = {0, 0, 0, 0}, s3 = {0, 0, 0, 0};
-#pragma unroll
-            for (int m = 0; m < kUB / 2; ++m) {
-                s2 = mfma32h(tAf[m], tA2f[m], s2);
-                s3 = mfma32h(tAf[m], tAn[m], s3);
-            }
-            L.S2p[pb][w][lane] = s2;
-            L.S3p[pb][w][lane] = s3;
-#pragma unroll
-            for (int ob = 0; ob < kNB; ++ob) {
-                L.Zp[pb][w][ob][lane] = w2_partial(tA2f, ob, b2r[ob]);
-                L.Ep[pb][w][ob][lane] = w2_partial(tAn, ob, b2r[ob] - bf16x4_to_f32(nx.v[ob]));
-            }
-        }
-        __syncthreads();
-
-        // ---- Z_c: wave w finishes output block w ----
-        {
-            f32x4 s2 = L.S2p[pb][0][lane];
-#pragma unroll
-            for (int v = 1; v < kWaves; ++v) s2 += L.S2p[pb][v][lane];
+            const f32x4 s2 = mfma32h(tAf, tA2f, f32x4{0, 0, 0, 0});
+            const f32x4 s3 = mfma32h(tAf, tAn, f32x4{0, 0, 0, 0});
+            const float one = (HAS_B2 && w == 0) ? 1.f : 0.f;
             f32x4 sm;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sm[r] = (4 * g + r <= c) ? s2[r] + (HAS_B2 ? 1.f : 0.f) : 0.f;
-            f32x4 z = L.Zp[pb][0][w][lane];
-#pragma unroll
-            for (int v = 1; v < kWaves; ++v) z += L.Zp[pb][v][w][lane];
-            z = mfma16h(tE[w], pack_f16x4(sm), z);
-            if (FULL || c < n) *(u32x2*)(Z + (tok0 + s0 + c) * kD + 16 * w + 4 * g) = pack_bf16x4(z);
-        }
-        // ---- E_{c+1} (every wave, every output block) ----
-        {
-            f32x4 s3 = L.S3p[pb][0][lane];
-#pragma unroll
-            for (int v = 1; v < kWaves; ++v) s3 += L.S3p[pb][v][lane];
-            const u32x2 s3b = pack_f16x4(s3 + (HAS_B2 ? 1.f : 0.f));
+            for (int r = 0; r < 4; ++r) sm[r] = (4 * g + r <= c) ? s2[r] + one : 0.f;
+            const u32x2 smb = pack_f16x4(sm);
+            const u32x2 s3b = pack_f16x4(s3 + one);
 #pragma unroll
             for (int ob = 0; ob < kNB; ++ob) {
-                f32x4 e = L.Ep[pb][0][ob][lane];
-#pragma unroll
-                for (int v = 1; v < kWaves; ++v) e += L.Ep[pb][v][ob][lane];
-                E[ob] = mfma16h(tE[ob], s3b, e);
+                L.Zp[w][ob][lane] = mfma16h(tE[ob], smb, w2_partial(tA2f, ob));
+                L.Ep[w][ob][lane] = mfma16h(tE[ob], s3b, w2_partial(tAn, ob));
             }
         }
-
-        // ---- state updates (needed from the next chunk's operands on) ----
+        // ---- state updates (this wave's units; needed from the next chunk on) ----
         {
-            // K_c with input features in the lanes and tokens in the slots
-            // (block ib holds K[token][pi(ib, 0..15)] row by row, 512 bytes)
             u32x2 Kt[kNB];
-#pragma unroll
-            for (int m = 0; m < kNB / 2; ++m) {
-                L.tK[w][(2 * m) * 64 + 4 * c + g] = lo_half(Kc[m]);
-                L.tK[w][(2 * m + 1) * 64 + 4 * c + g] = hi_half(Kc[m]);
-            }
-            asm volatile("" ::: "memory");
-#pragma unroll
-            for (int ib = 0; ib < kNB; ++ib) {
-                auto p = (__attribute__((address_space(3))) s16x4*)(&L.tK[w][ib * 64] + lane);
-                Kt[ib] = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
-            }
-            asm volatile("" ::: "memory");
+            k_transposed(L.kq[sl].g[0], Kt);
 #pragma unroll
             for (int ub = 0; ub < kUB; ++ub)
 #pragma unroll
@@ -446,36 +439,44 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
                     b1r[ub] += v;
                 }
             }
-            if (HAS_B2) {
-                // b2 -= sum_s eta_s E[o][s]: sum tE's four token slots and the four
-                // lane groups, stage through LDS, read back in the rows-of-o layout
-#pragma unroll
-                for (int ob = 0; ob < kNB; ++ob) {
-                    const f32x4 t = f16x4_to_f32(tE[ob]);
-                    float v = t[0] + t[1] + t[2] + t[3];
-                    v += __shfl_xor(v, 16);
-                    v += __shfl_xor(v, 32);
-                    if (g == 0) L.b2d[w][16 * ob + c] = v;
-                }
-                asm volatile("" ::: "memory");
-#pragma unroll
-                for (int ob = 0; ob < kNB; ++ob) b2r[ob] += *(const f32x4*)&L.b2d[w][16 * ob + 4 * g];
-                asm volatile("" ::: "memory");
+        }
+        __syncthreads();
+
+        // ---- reduction: Z_c to memory, E_{c+1} published, b2 stepped ----
+        {
+            f32x2 z = reduce_pair(L.Zp) + b2v;
+            if (FULL || rtok < n) {
+                unsigned* zp = reinterpret_cast<unsigned*>(Z + (tok0 + s0 + rtok) * kD + rout);
+                *zp = pack_bf16x2(z.x, z.y);
             }
+            f32x2 e = reduce_pair(L.Ep);
+            const unsigned v = vnext;
+            e.x += b2v.x - __uint_as_float(v << 16);
+            e.y += b2v.y - __uint_as_float(v & 0xffff0000u);
+            if (HAS_B2) {
+                // b2 -= sum_s eta_s E_c[o][s]: the 16 tokens of an output pair sit in
+                // lanes 2 apart within 32 consecutive lanes
+                const float et = L.eta[sl][rtok];
+                f32x2 t = {et * eprev.x, et * eprev.y};
+#pragma unroll
+                for (int k = 2; k <= 16; k *= 2) {
+                    t.x += __shfl_xor(t.x, k);
+                    t.y += __shfl_xor(t.y, k);
+                }
+                b2v -= t;
+            }
+            eprev = e;
+            publish_e(e, sn);
+            vnext = v_load(ci + 2);
         }
         pack_state();
-        // ---- move to the next chunk ----
 #pragma unroll
         for (int ub = 0; ub < kUB; ++ub) {
             G[ub] = Gn[ub];
             Ab[ub] = An[ub];
         }
-#pragma unroll
-        for (int m = 0; m < kUB / 2; ++m) tAf[m] = tAn[m];
-#pragma unroll
-        for (int m = 0; m < kNB / 2; ++m) Kc[m] = Kn[m];
-        cur = nx;
-        nx = nx2;
+        tAf = tAn;
+        __syncthreads();
     }
 
     // ---- final state ----
@@ -494,11 +495,7 @@ __global__ __launch_bounds__(256) void mlp_mfma_kernel(
             *(f32x4*)(W2o_ + (size_t)(16 * ob + c) * kH + ubase + 16 * ub + 4 * g) = W2o[ob][ub];
         if (HAS_B1 && g == 0) b1_out[(size_t)slice * kH + ubase + 16 * ub + c] = b1r[ub];
     }
-    if (HAS_B2 && w == 0 && c == 0) {
-#pragma unroll
-        for (int ob = 0; ob < kNB; ++ob)
-            *(f32x4*)(b2_out + (size_t)slice * kD + 16 * ob + 4 * g) = b2r[ob];
-    }
+    if (HAS_B2 && rtok == 0) *(f32x2*)(b2_out + (size_t)slice * kD + rout) = b2v;
 }
 
 template <bool FULL, bool ETA_TOKEN, bool HAS_B1, bool HAS_B2>
