@@ -23,13 +23,14 @@
 // each must stay below 65504 in magnitude, or the outputs turn non-finite.
 //
 // One workgroup of eight waves per (batch, head), two per SIMD so that one
-// wave's waits on the matrix cores, LDS and transcendentals are filled by the
-// other's work; wave w owns hidden units 32w .. 32w+31, i.e. rows of W1 and
-// columns of W2.  Each product keeps one index in the lanes and the contracted
-// one in the register slots (see mfma_common.h).  W2 is contracted over the
-// hidden units for E and Z but over the output features for D: the fp32 state
-// keeps it with the output feature in the lanes, and D takes the LDS transpose of
-// its fp16 tiles each chunk.
+// wave's waits on the matrix cores and LDS are filled by the other's work; wave w
+// owns hidden units 32w .. 32w+31, i.e. rows of W1 and columns of W2.  Each
+// product keeps one index in the lanes and the contracted one in the register
+// slots (see mfma_common.h).  W2 is contracted over the hidden units for E and Z
+// but over the output features for D: the fp32 state keeps it with the output
+// feature in the lanes, and D takes the LDS transpose of its fp16 tiles each
+// chunk.  (Transposing on the matrix cores instead, as a product with the
+// identity, measured 11% slower: it lengthens each wave's dependent chain.)
 //
 // Per chunk each wave forms its partials of Z_c and E_{c+1} over its own units,
 // each with its share of the eta-weighted correction already added (the
@@ -42,9 +43,14 @@
 // per workgroup in LDS as fp16 rows (two chunks ahead), and both the row operand
 // and the transposed K come from that tile.
 //
-// GELU: gelu(x) = x Phi(x), gelu'(x) = Phi(x) + x phi(x), with erf from
-// Abramowitz & Stegun, Handbook of Mathematical Functions, eq. 7.1.26
-// (|error| <= 1.5e-7), using the hardware exp2 and reciprocal.
+// GELU: gelu(x) = x Phi(x), gelu'(x) = Phi(x) + x phi(x).  Each workgroup first
+// tabulates Phi and gelu' at 1024 points on [-8, 8) (step 1/64; erf from
+// Abramowitz & Stegun, Handbook of Mathematical Functions, eq. 7.1.26, |error| <=
+// 1.5e-7, with the hardware exp2 and reciprocal) and then interpolates linearly:
+// |error| <= 7.4e-6 in Phi and 2.4e-5 in gelu' (beyond +-8 the end values, where
+// Phi is 0 or 1 to 6e-16).  That is far below the fp16 rounding of the
+// activations, and it replaces a reciprocal, an exponential and about fifteen
+// other operations per element by an LDS read and five operations.
 #include <stdint.h>
 
 #include "device_common.h"
@@ -78,24 +84,48 @@ __device__ __forceinline__ float phi_erf(float x, float& e)
     return 0.5f + copysignf(0.5f * erf_abs, x);
 }
 
-__device__ __forceinline__ void gelu_pair(f32x4 h, f32x4& g, f32x4& gp)
+// Table of Phi and gelu' at x_i = -8 + i / 64: entry i holds (Phi(x_i),
+// Phi(x_{i+1}) - Phi(x_i), gelu'(x_i), gelu'(x_{i+1}) - gelu'(x_i)).
+constexpr int kTab = 1024;
+
+__device__ __forceinline__ f32x4 gelu_tab_entry(int i)
+{
+    float e0, e1;
+    const float x0 = -8.f + (float)i * (1.f / 64.f), x1 = x0 + 1.f / 64.f;
+    const float p0 = phi_erf(x0, e0), p1 = phi_erf(x1, e1);
+    const float g0 = fmaf(x0 * 0.39894228040143268f, e0, p0);
+    const float g1 = fmaf(x1 * 0.39894228040143268f, e1, p1);
+    return f32x4{p0, p1 - p0, g0, g1 - g0};
+}
+
+// table position of x: entry index (clamped to the table, 0 for a NaN) and the
+// fraction of the step past it
+__device__ __forceinline__ int gelu_tab_pos(float x, float& fr)
+{
+    const float t = __builtin_amdgcn_fmed3f(fmaf(x, 64.f, 512.f), 0.f, 1023.999f);
+    fr = __builtin_amdgcn_fractf(t);
+    return min(max((int)t, 0), kTab - 1);
+}
+
+__device__ __forceinline__ void gelu_pair(const f32x4* tab, f32x4 h, f32x4& g, f32x4& gp)
 {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        float e;
-        const float P = phi_erf(h[r], e);
-        g[r] = h[r] * P;
-        gp[r] = fmaf(h[r] * 0.39894228040143268f, e, P);
+        float fr;
+        const f32x4 e = tab[gelu_tab_pos(h[r], fr)];
+        g[r] = h[r] * fmaf(e.y, fr, e.x);
+        gp[r] = fmaf(e.w, fr, e.z);
     }
 }
 
-__device__ __forceinline__ f32x4 gelu4(f32x4 h)
+__device__ __forceinline__ f32x4 gelu4(const f32x4* tab, f32x4 h)
 {
     f32x4 g;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        float e;
-        g[r] = h[r] * phi_erf(h[r], e);
+        float fr;
+        const f32x2 e = *reinterpret_cast<const f32x2*>(&tab[gelu_tab_pos(h[r], fr)]);
+        g[r] = h[r] * fmaf(e.y, fr, e.x);
     }
     return g;
 }
@@ -103,6 +133,7 @@ __device__ __forceinline__ f32x4 gelu4(f32x4 h)
 // LDS layout: staged inputs, per-wave transpose buffers, the shared fp16 E
 // operands and the per-wave partial sums
 struct Lds {
+    f32x4 gtab[kTab];                   // Phi and gelu' for interpolation
     KQTile16<kD> kq[kRing];             // fp16 K and Q rows of three staged chunks
     float eta[kRing][16];               // their tokens' eta (0 past a short chunk's end)
     u32x2 tW2[kWaves][kUB * kNB * 64];  // per wave: fp16 W2 tiles for the transpose to (u, o)
@@ -264,7 +295,8 @@ __global__ __launch_bounds__(64 * kWaves) void mlp_mfma_kernel(
         te[(rob * 64 + 4 * rtok + (rln >> 4)) * 2 + rrp] = pack_f16x2(-et * e.x, -et * e.y);
     };
 
-    // ---- prologue: stage chunks 0 and 1, hold chunk 2 ----
+    // ---- prologue: the GELU table; stage chunks 0 and 1, hold chunk 2 ----
+    for (int i = tid; i < kTab; i += 64 * kWaves) L.gtab[i] = gelu_tab_entry(i);
     u32x4 sr = {0u, 0u, 0u, 0u};
     float se = 0.f;
     stage_load(0, sr, se);
@@ -289,7 +321,7 @@ __global__ __launch_bounds__(64 * kWaves) void mlp_mfma_kernel(
 #pragma unroll
             for (int m = 0; m < kNB / 2; ++m) h = mfma32h(Kc[m], W1f[ub][m], h);
             f32x4 a;
-            gelu_pair(h, a, G[ub]);
+            gelu_pair(L.gtab, h, a, G[ub]);
             Ab[ub] = pack_f16x4(a);
         }
         transpose_a(L.tA[w], Ab, tAf);
@@ -393,9 +425,9 @@ __global__ __launch_bounds__(64 * kWaves) void mlp_mfma_kernel(
             }
             hq = mfma16h(S1q, DSb[ub], hq);
             hk = mfma16h(S1k, DSb[ub], hk);
-            A2b[ub] = pack_f16x4(gelu4(hq));
+            A2b[ub] = pack_f16x4(gelu4(L.gtab, hq));
             f32x4 a;
-            gelu_pair(hk, a, Gn[ub]);
+            gelu_pair(L.gtab, hk, a, Gn[ub]);
             An[ub] = pack_f16x4(a);
         }
         u32x4 tA2f, tAn;
