@@ -45,6 +45,7 @@ KERNEL_SOURCES = {"linear_b16": ["linear_mfma.hip", "linear_coop.hip", "mfma_com
                   "linear_generic": ["linear_generic.hip", "device_common.h", "launch.h"],
                   "bigchunk": ["linear_bigchunk.hip", "mfma_common.h", "device_common.h",
                                "launch.h"],
+                  "seg": ["linear_seg.hip", "mfma_common.h", "device_common.h", "launch.h"],
                   "mlp": ["mlp_mfma.hip", "mlp_generic.hip", "mfma_common.h", "device_common.h",
                           "launch.h"],
                   "step": ["linear_step.hip", "device_common.h", "launch.h"],
@@ -61,6 +62,8 @@ def kernel_family(wl, plan_name: str) -> str:
         return "mlp"
     if plan_name == "bigchunk":
         return "bigchunk"
+    if plan_name == "split":
+        return "seg"
     if plan_name == "generic":
         return "linear_generic"
     return "linear_f32" if wl.io == "f32" else "linear_b16"

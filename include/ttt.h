@@ -94,10 +94,12 @@ typedef enum {
                                    multiple of 32 >= 128 */
     TTT_PLAN_SPLIT = 4          /* bf16 matrix cores, inclusive read, d = 64, chunk 16, T a
                                    multiple of 16 and >= 2048, at most 32 (batch, head)
-                                   slices: the sequence in two segments scanned at once,
-                                   the second from zero and from the identity, joined by
-                                   a fix-up pass (workspace: (T - T1) d bf16 + 3 d^2
-                                   fp32 per slice, T1 ~ 0.64 T) */
+                                   slices: each sequence in S ~ 256 / slices segments;
+                                   segment 0 scans while the others form their affine
+                                   maps (scans from zero and from the identity), a
+                                   combine gives every segment its start state, and
+                                   segments 1 .. S-1 scan again from it (workspace:
+                                   3 S d^2 fp32 per slice) */
 } ttt_plan;
 
 /* Read order of a chunk's tokens.  INCLUSIVE: token t reads with the chunk's
@@ -295,16 +297,14 @@ int ttt_linear_fwd_ex(const void* K, const void* Q, const void* V,
  * captured into a HIP graph, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments as ttt_linear_fwd without the workspace: the plans
  * that need one (TTT_PLAN_BIGCHUNK for chunks of 128+ tokens, TTT_PLAN_SPLIT for
- * a few long chunk-16 heads) run in a static device array of the library,
- * TTT_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU.  The array is part of the library's
- * code object: each GPU holds it from the library's first use there until the
- * process ends.  The call allocates nothing and frees nothing.
- *   - The plan is AUTO's, except that a TTT_PLAN_SPLIT shape whose workspace
- *     exceeds 64 MiB runs TTT_PLAN_MFMA, which needs none.
- *   - Other shapes whose workspace (ttt_linear_workspace_bytes_ex for the AUTO
- *     plan) exceeds 64 MiB return TTT_ERR_WORKSPACE before any HIP call (for
- *     example 16 heads x 131072 tokens at d = 128, chunk 2048, which needs
- *     160 MiB: use ttt_linear_fwd with a caller workspace there).
+ * a few long chunk-16 heads, at most 12 MiB) run in a static device array of the
+ * library, TTT_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU.  The array is part of the
+ * library's code object: each GPU holds it from the library's first use there
+ * until the process ends.  The call allocates nothing and frees nothing.
+ *   - Shapes whose workspace (ttt_linear_workspace_bytes_ex for the AUTO plan)
+ *     exceeds 64 MiB return TTT_ERR_WORKSPACE before any HIP call (for example
+ *     16 heads x 131072 tokens at d = 128, chunk 2048, which needs 160 MiB: use
+ *     ttt_linear_fwd with a caller workspace there).
  *   - The scratch of the caller's current device is used; `stream` must belong
  *     to that device.
  *   - Every call on one GPU shares that GPU's array: calls that overlap in time

@@ -42,7 +42,7 @@ int linear_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan,
                       (bf16 ? linear_mfma_supported(d, chunk, bf16) : linear_f32_supported(d));
     const bool big = linear_bigchunk_supported(d, chunk, bf16);
     const bool split = read_mode == TTT_READ_INCLUSIVE &&
-                       linear_split_supported(B * H, T, d, chunk, bf16);
+                       linear_seg_supported(B * H, T, d, chunk, bf16);
     switch (plan) {
     case TTT_PLAN_GENERIC: return TTT_PLAN_GENERIC;
     case TTT_PLAN_MFMA: return mfma ? TTT_PLAN_MFMA : TTT_ERR_UNSUPPORTED;
@@ -52,7 +52,7 @@ int linear_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan,
     }
     // chunks of 128+ tokens: the three-stage path spreads the chunks over the GPU
     if (big) return TTT_PLAN_BIGCHUNK;
-    // few heads: two segments along T use the compute units the heads leave idle
+    // few heads: segments along T use the compute units the heads leave idle
     if (split) return TTT_PLAN_SPLIT;
     if (mfma) return TTT_PLAN_MFMA;
     return TTT_PLAN_GENERIC;
@@ -146,7 +146,7 @@ size_t ttt_linear_workspace_bytes_ex(int B, int H, int T, int d, int chunk, int 
 {
     int p = linear_plan(B, H, T, d, chunk, io_dtype, plan);
     if (p == TTT_PLAN_BIGCHUNK) return linear_bigchunk_workspace(B * H, T, d, chunk);
-    if (p == TTT_PLAN_SPLIT) return linear_split_workspace(B * H, T, d);
+    if (p == TTT_PLAN_SPLIT) return linear_seg_workspace(B * H, T, d);
     return 0;
 }
 
@@ -204,7 +204,7 @@ int ttt_linear_fwd_ex(const void* K, const void* Q, const void* V,
     case TTT_PLAN_MFMA:
         return launch_status(a.bf16 ? launch_linear_mfma(a, s) : launch_linear_f32(a, s));
     case TTT_PLAN_BIGCHUNK: return launch_status(launch_linear_bigchunk(a, s));
-    case TTT_PLAN_SPLIT: return launch_status(launch_linear_split(a, s));
+    case TTT_PLAN_SPLIT: return launch_status(launch_linear_seg(a, s));
     default: return launch_status(launch_linear_generic(a, s));
     }
 }
@@ -221,15 +221,9 @@ int ttt_linear_fwd_noalloc(const void* K, const void* Q, const void* V,
         !aligned(W0, 16) || !aligned(W_out, 16))
         return TTT_ERR_INVALID_ARG;
     if (eta ? !aligned(eta, 4) : !std::isfinite(eta_scalar)) return TTT_ERR_INVALID_ARG;
-    int p = linear_plan(B, H, T, d, chunk, io_dtype, TTT_PLAN_AUTO);
+    const int p = linear_plan(B, H, T, d, chunk, io_dtype, TTT_PLAN_AUTO);
     if (p < 0) return p;
-    size_t need = ttt_linear_workspace_bytes_ex(B, H, T, d, chunk, io_dtype, p);
-    if (p == TTT_PLAN_SPLIT && need > kScratchBytes) {
-        // too long for the two-segment plan's workspace: the chunk-by-chunk plan
-        // runs the same shape without one
-        p = TTT_PLAN_MFMA;
-        need = ttt_linear_workspace_bytes_ex(B, H, T, d, chunk, io_dtype, p);
-    }
+    const size_t need = ttt_linear_workspace_bytes_ex(B, H, T, d, chunk, io_dtype, p);
     if (need > kScratchBytes) return TTT_ERR_WORKSPACE;
     void* ws = nullptr;
     if (need > 0) {

@@ -78,13 +78,14 @@ hipError_t launch_linear_generic(const LinearArgs& a, hipStream_t s);
 bool linear_mfma_supported(int d, int chunk, int bf16);
 hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
 
-// Two segments along T for chunk-16 heads at d = 64 that fill at most half the
-// compute units: both segments scan at once (the second as the sum of a scan from
-// zero and one from the identity), then a fix-up pass adds W_mid's contribution.
-// The workspace holds U [BH, T - T1, d] bf16 and W_mid, W_B, A [BH, d, d] fp32.
-bool linear_split_supported(int BH, int T, int d, int chunk, int bf16);
-size_t linear_split_workspace(int BH, int T, int d);
-hipError_t launch_linear_split(const LinearArgs& a, hipStream_t s);
+// Segments along T for chunk-16 heads at d = 64 that leave compute units idle:
+// each slice's sequence in S segments (S * slices workgroups of four waves);
+// segment 0 scans while the others form their affine maps, a combine gives every
+// segment its start state, and segments 1 .. S-1 scan again from it.  The
+// workspace holds W_B, A and W_start [BH, S, d, d] fp32.
+bool linear_seg_supported(int BH, int T, int d, int chunk, int bf16);
+size_t linear_seg_workspace(int BH, int T, int d);
+hipError_t launch_linear_seg(const LinearArgs& a, hipStream_t s);
 
 // fp32 I/O on the fp32 matrix cores: one wave per (batch*head, 16-row block), any
 // chunk, d in {16, 32, 64, 128}, the inclusive read; part of the MFMA plan.

@@ -546,352 +546,6 @@ __global__ __launch_bounds__(64 * WPB) void linear_mfma_chain_kernel(
     }
 }
 
-// Two segments along T.  The chunk map is affine in the state,
-// W -> W (I - P_c) + B_c with P_c = K_c diag(eta) K_c^T, B_c = V_c diag(eta) K_c^T
-// (PaperTrace "5 · TestingTime 训练与长上下文" §1.1/§2.3), and so is every read
-// z_t = W_t q_t.  Split the tokens at T1 (a chunk boundary): the first segment is
-// the scan from W0, ending at W_mid; the second is the sum of two scans that do
-// not need W_mid,
-//     from 0 with V           -> Z_B, W_B      (row block 0 of the unit's wave)
-//     from the identity, V=0  -> U,   A        (row block 1)
-// with Z_2 = Z_B + U W_mid^T (split_fixup_kernel) and W_T = W_B + W_mid A
-// (split_state_kernel).  Both segments start at once, so a head's chain is T1
-// chunks long instead of T.
-enum { kSegFirst = 0, kSegSecond = 1 };
-
-// Block r of a wave scans with V when bit r of VMASK is set (a compile-time
-// choice: a select on loaded V would make the loop wait for every load).
-template <int RB>
-struct SplitBlocks {
-    const float* w0[RB];   // initial state [D, D]; nullptr: zero with V, the identity without
-    uint16_t* z[RB];       // outputs [tokens, D]: token s0 + c of the segment at row
-    size_t z_tok0[RB];     //   z_tok0 + s0 + c
-    float* w_out[RB];      // [D, D] final state of the segment's scan
-};
-
-template <int D, int PF, int ETA, int RB, int VMASK>
-__device__ __forceinline__ void split_chain(const uint16_t* __restrict__ K,
-                                            const uint16_t* __restrict__ Q,
-                                            const uint16_t* __restrict__ V,
-                                            const float* __restrict__ eta, float eta_scalar,
-                                            const SplitBlocks<RB>& blk, size_t tok0, int n,
-                                            int out0, u32x2* lds_kt, int lane)
-{
-    constexpr int NB = D / 16;
-    constexpr int NM = D / 32;
-    const int c = lane & 15, g = lane >> 4;
-    // state rows out0 + c of each block's problem, columns pi(jb, 4g + i)
-    f32x4 M[RB][NB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-        if (blk.w0[r]) {
-            const float* w = blk.w0[r] + (size_t)(out0 + c) * D;
-#pragma unroll
-            for (int m = 0; m < NM; ++m) {
-                M[r][2 * m] = *(const f32x4*)(w + 32 * m + 8 * g);
-                M[r][2 * m + 1] = *(const f32x4*)(w + 32 * m + 8 * g + 4);
-            }
-        } else {
-#pragma unroll
-            for (int jb = 0; jb < NB; ++jb) {
-                // zero, or the identity row out0 + c: column pi(jb, 4g + i)
-                f32x4 e = {0, 0, 0, 0};
-                if (!((VMASK >> r) & 1)) {
-                    const int base = 32 * (jb >> 1) + 8 * g + 4 * (jb & 1);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) e[i] = (base + i == out0 + c) ? 1.f : 0.f;
-                }
-                M[r][jb] = e;
-            }
-        }
-    }
-    const u32x2 I16 = identity_b16(lane);
-    const SliceBuffers sres = slice_buffers<D>(K, Q, V, eta, blk.z[0], tok0, n, out0, lane);
-    const int ntiles = n / 16;
-    auto load = [&](Tile<D, RB>& t, int tau) {
-        const int so = min(tau, ntiles - 1) * 16 * D * 2;   // past the end: re-read the last tile
-        t.n = 16;
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            t.k[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sres.k, sres.kq + 64 * m, so, 0));
-            t.q[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(sres.q, sres.kq + 64 * m, so, 0));
-        }
-        t.v[0] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(sres.v, sres.vo, so, 0));
-        const int eo = min(tau, ntiles - 1) * 16 * 4;
-        if (ETA == kEtaToken4) {
-            t.eta = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(sres.e, sres.eo, eo, 0));
-        } else if (ETA == kEtaToken) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                t.eta[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sres.e, sres.eo + 4 * i, eo, 0));
-        }
-    };
-    // -V^T of a block (zero for the identity scan)
-    auto vneg_of = [&](const Tile<D, RB>& t, int r) {
-        return ((VMASK >> r) & 1) ? t.v[0] ^ u32x2{0x80008000u, 0x80008000u} : u32x2{0u, 0u};
-    };
-    // outputs through buffer stores: the tile start as the scalar offset
-    __amdgpu_buffer_rsrc_t zr[RB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r)
-        zr[r] = __builtin_amdgcn_make_buffer_rsrc(blk.z[r] + blk.z_tok0[r] * D, 0,
-                                                  (int)min((long long)n * D * 2, 0x7fffffffLL),
-                                                  kRawBufferFlags);
-    Tile<D, RB> buf[PF];
-#pragma unroll
-    for (int p = 0; p < PF; ++p) load(buf[p], p);
-
-    u32x4 Mf[RB][NM];
-    f32x4 Et[RB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-#pragma unroll
-        for (int m = 0; m < NM; ++m) Mf[r][m] = pack_bf16x8(M[r][2 * m], M[r][2 * m + 1]);
-        Et[r] = mfma16(vneg_of(buf[0], r), I16, f32x4{0, 0, 0, 0});
-#pragma unroll
-        for (int m = 0; m < NM; ++m) Et[r] = mfma32(buf[0].k[m], Mf[r][m], Et[r]);
-    }
-    u32x4 ktz[NB];
-#pragma unroll
-    for (int jb = 0; jb < NB; ++jb) ktz[jb] = u32x4{0u, 0u, 0u, 0u};
-    transpose_k_hi<D>(ktz, buf[0], lds_kt, lane);
-    u32x4 smz = {0u, 0u, 0u, 0u};
-
-    // one chunk, as in linear_mfma_chain_kernel (every tile whole)
-    auto chunk_step = [&](const Tile<D, RB>& cur, const Tile<D, RB>& nxt, int tau) {
-        const int s0 = tau * 16;
-        const f32x4 et = ETA == kEtaScalar ? f32x4{eta_scalar, eta_scalar, eta_scalar, eta_scalar}
-                                           : cur.eta;
-        u32x4 IF[RB];
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            const u32x2 F = pack_bf16x4(-et * Et[r]);
-            IF[r] = u32x4{I16.x, I16.y, F.x, F.y};
-        }
-        {
-            f32x4 Gt = {0, 0, 0, 0};
-#pragma unroll
-            for (int m = 0; m < NM; ++m) Gt = mfma32(cur.k[m], nxt.k[m], Gt);
-            const u32x2 G = pack_bf16x4(Gt);
-#pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                f32x4 P = {0, 0, 0, 0};
-#pragma unroll
-                for (int m = 0; m < NM; ++m) P = mfma32(nxt.k[m], Mf[r][m], P);
-                const u32x2 vneg = vneg_of(nxt, r);
-                Et[r] = mfma32(u32x4{vneg.x, vneg.y, G.x, G.y}, IF[r], P);
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int jb = 0; jb < NB; ++jb) M[r][jb] = mfma32(ktz[jb], IF[r], M[r][jb]);
-        f32x4 St = {0, 0, 0, 0};
-#pragma unroll
-        for (int m = 0; m < NM; ++m) St = mfma32(cur.k[m], cur.q[m], St);
-        f32x4 Sm;
-        Sm.x = (4 * g + 0 <= c) ? St.x : 0.f;
-        Sm.y = (4 * g + 1 <= c) ? St.y : 0.f;
-        Sm.z = (4 * g + 2 <= c) ? St.z : 0.f;
-        Sm.w = (4 * g + 3 <= c) ? St.w : 0.f;
-        {
-            const u32x2 Sb = pack_bf16x4(Sm);
-            smz.z = Sb.x;
-            smz.w = Sb.y;
-        }
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            f32x4 Zt = {0, 0, 0, 0};
-#pragma unroll
-            for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[r][m], cur.q[m], Zt);
-            Zt = mfma32(IF[r], smz, Zt);
-            __builtin_amdgcn_raw_buffer_store_b64(pack_bf16x4(Zt), zr[r], sres.vo, s0 * D * 2, 0);
-        }
-        transpose_k_hi<D>(ktz, nxt, lds_kt, lane);
-#pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int m = 0; m < NM; ++m) Mf[r][m] = pack_bf16x8(M[r][2 * m], M[r][2 * m + 1]);
-    };
-    int tau0 = 0;
-    for (; tau0 + PF <= ntiles; tau0 += PF) {
-#pragma unroll
-        for (int p = 0; p < PF; ++p) {
-            chunk_step(buf[p], buf[(p + 1) % PF], tau0 + p);
-            load(buf[p], tau0 + p + PF);
-        }
-    }
-#pragma unroll
-    for (int p = 0; p < PF; ++p) {
-        if (tau0 + p >= ntiles) break;
-        chunk_step(buf[p], buf[(p + 1) % PF], tau0 + p);
-    }
-#pragma unroll
-    for (int r = 0; r < RB; ++r) {
-        float* w = blk.w_out[r] + (size_t)(out0 + c) * D;
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            *(f32x4*)(w + 32 * m + 8 * g) = M[r][2 * m];
-            *(f32x4*)(w + 32 * m + 8 * g + 4) = M[r][2 * m + 1];
-        }
-    }
-}
-
-// Workspace of the two-segment scan, per (batch, head): U [T - T1, D] bf16, then
-// W_mid, W_B, A [D, D] fp32 each.
-struct SplitWorkspace {
-    uint16_t* u;
-    float* wmid;
-    float* wb;
-    float* amap;
-};
-
-template <int D>
-__host__ __device__ inline SplitWorkspace split_workspace(void* base, int BH, int T2)
-{
-    SplitWorkspace w;
-    const size_t ubytes = ((size_t)BH * T2 * D * 2 + 255) / 256 * 256;
-    w.u = reinterpret_cast<uint16_t*>(base);
-    w.wmid = reinterpret_cast<float*>(reinterpret_cast<char*>(base) + ubytes);
-    w.wb = w.wmid + (size_t)BH * D * D;
-    w.amap = w.wb + (size_t)BH * D * D;
-    return w;
-}
-
-// Grid: 2 * units_r workgroups of one wave; the first units_r run the first
-// segment (one row block each), the rest the second (the scans from zero and from
-// the identity of one row block, as the two row blocks of one wave, which share
-// its K/Q loads, transposes, Gram matrices and scores).
-// units_r = round_up(BH, 8) * D / 16.
-
-template <int D, int PF1, int PF2, int ETA>
-__global__ __launch_bounds__(64) void linear_split_kernel(
-    const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
-    const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
-    const float* W0, uint16_t* __restrict__ Z, void* ws, int BH, int T, int T1)
-{
-    constexpr int NB = D / 16;
-    __shared__ u32x2 lds_kt[NB * 64];
-    const int lane = threadIdx.x;
-    const int units_r = (BH + 7) / 8 * 8 * NB;
-    const int seg = (int)blockIdx.x >= units_r ? kSegSecond : kSegFirst;
-    int slice, rb;
-    xcd_unit_part((int)blockIdx.x - seg * units_r, NB, slice, rb);
-    if (slice >= BH) return;
-    const int out0 = 16 * rb;
-    const SplitWorkspace w = split_workspace<D>(ws, BH, T - T1);
-    const size_t dd = (size_t)D * D;
-    if (seg == kSegFirst) {
-        const size_t t0 = (size_t)slice * T;
-        SplitBlocks<1> b;
-        b.w0[0] = W0 + slice * dd;
-        b.z[0] = Z;
-        b.z_tok0[0] = t0;
-        b.w_out[0] = w.wmid + slice * dd;
-        split_chain<D, PF1, ETA, 1, 1>(K, Q, V, eta, eta_scalar, b, t0, T1, out0, lds_kt, lane);
-    } else {
-        // tokens T1 .. T-1 of the slice; U is [slice, T - T1, D]
-        const size_t t0 = (size_t)slice * T + T1;
-        SplitBlocks<2> b;
-        b.w0[0] = nullptr;   // zero, with V
-        b.z[0] = Z;
-        b.z_tok0[0] = t0;
-        b.w_out[0] = w.wb + slice * dd;
-        b.w0[1] = nullptr;   // the identity, without V
-        b.z[1] = w.u;
-        b.z_tok0[1] = (size_t)slice * (T - T1);
-        b.w_out[1] = w.amap + slice * dd;
-        split_chain<D, PF2, ETA, 2, 1>(K, Q, V, eta, eta_scalar, b, t0, T - T1, out0, lds_kt,
-                                       lane);
-    }
-}
-
-// W_T = W_B + W_mid A in fp32: one workgroup per (slice, 16 rows); thread
-// (row i, columns 4q..4q+3) with W_mid's rows and A in LDS.
-template <int D>
-__global__ __launch_bounds__(256) void split_state_kernel(float* __restrict__ W_out, void* ws,
-                                                          int BH, int T, int T1)
-{
-    static_assert(D == 64, "16 rows x 16 column quads per workgroup");
-    __shared__ f32x4 al[D * D / 4];
-    __shared__ float wl[16 * D];
-    const SplitWorkspace w = split_workspace<D>(ws, BH, T - T1);
-    const size_t dd = (size_t)D * D;
-    const int slice = blockIdx.x, i0 = 16 * blockIdx.y;
-    for (int e = threadIdx.x; e < D * D / 4; e += blockDim.x)
-        al[e] = *(const f32x4*)(w.amap + slice * dd + 4 * e);
-    for (int e = threadIdx.x; e < 16 * D; e += blockDim.x)
-        wl[e] = w.wmid[slice * dd + (size_t)i0 * D + e];
-    __syncthreads();
-    const int i = threadIdx.x >> 4, q = threadIdx.x & 15;
-    f32x4 o = *(const f32x4*)(w.wb + slice * dd + (size_t)(i0 + i) * D + 4 * q);
-    for (int k = 0; k < D; ++k) {
-        const float a = wl[i * D + k];
-        const f32x4 r = al[k * (D / 4) + q];
-        o.x = fmaf(a, r.x, o.x);
-        o.y = fmaf(a, r.y, o.y);
-        o.z = fmaf(a, r.z, o.z);
-        o.w = fmaf(a, r.w, o.w);
-    }
-    *(f32x4*)(W_out + slice * dd + (size_t)(i0 + i) * D + 4 * q) = o;
-}
-
-// Z[T1..T) += U W_mid^T.  A wave takes kFixTiles 16-token tiles and all D output
-// rows (bf16 products of U, exact as stored, and W_mid rounded to bf16, added in
-// fp32 onto the stored Z); every load of a wave's tiles is issued before the
-// first product.  Tiles past the end read the last one (in range) and store
-// nothing.
-constexpr int kFixTiles = 4;
-
-template <int D>
-__global__ __launch_bounds__(256) void split_fixup_kernel(uint16_t* __restrict__ Z, void* ws,
-                                                          int BH, int T, int T1)
-{
-    constexpr int NM = D / 32, NB = D / 16;
-    const int T2 = T - T1;
-    const int ntiles = T2 / 16;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int c = lane & 15, g = lane >> 4;
-    const int slice = blockIdx.y;
-    const SplitWorkspace w = split_workspace<D>(ws, BH, T2);
-    const size_t dd = (size_t)D * D;
-    const int tile0 = ((int)blockIdx.x * 4 + wave) * kFixTiles;
-    u32x2 zb[kFixTiles][NB];
-    u32x4 ub[kFixTiles][NM];
-    size_t zrow[kFixTiles];
-#pragma unroll
-    for (int i = 0; i < kFixTiles; ++i) {
-        const size_t tok = (size_t)min(tile0 + i, ntiles - 1) * 16 + c;
-        zrow[i] = ((size_t)slice * T + T1 + tok) * D;
-        const uint16_t* u = w.u + ((size_t)slice * T2 + tok) * D;
-#pragma unroll
-        for (int m = 0; m < NM; ++m) ub[i][m] = *(const u32x4*)(u + 32 * m + 8 * g);
-#pragma unroll
-        for (int ob = 0; ob < NB; ++ob) zb[i][ob] = *(const u32x2*)(Z + zrow[i] + 16 * ob + 4 * g);
-    }
-    // W_mid rows 16 ob + c, columns 32m + 8g .. +7 (A operand)
-    u32x4 wmb[NB][NM];
-#pragma unroll
-    for (int ob = 0; ob < NB; ++ob) {
-        const float* wm = w.wmid + slice * dd + (size_t)(16 * ob + c) * D;
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-            wmb[ob][m] = pack_bf16x8(*(const f32x4*)(wm + 32 * m + 8 * g),
-                                     *(const f32x4*)(wm + 32 * m + 8 * g + 4));
-    }
-#pragma unroll
-    for (int i = 0; i < kFixTiles; ++i)
-#pragma unroll
-        for (int ob = 0; ob < NB; ++ob) {
-            const u32x2 z = zb[i][ob];
-            f32x4 acc = {__uint_as_float(z.x << 16), __uint_as_float(z.x & 0xffff0000u),
-                         __uint_as_float(z.y << 16), __uint_as_float(z.y & 0xffff0000u)};
-#pragma unroll
-            for (int m = 0; m < NM; ++m) acc = mfma32(wmb[ob][m], ub[i][m], acc);
-            if (tile0 + i < ntiles) *(u32x2*)(Z + zrow[i] + 16 * ob + 4 * g) = pack_bf16x4(acc);
-        }
-}
-
 // Launch choices, all measured on MI355X (256 compute units):
 //  - prefetch depth of the chunk-16 kernel: 8 chunks (1x32 heads x 32768 tokens:
 //    605 -> 438 us against 4), 4 where the registers do not allow 8;
@@ -924,37 +578,6 @@ void launch_chain(const LinearArgs& a, hipStream_t s)
                        (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V, a.eta,
                        a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.BH, a.T, a.chunk, a.cu,
                        a.H, a.total_T);
-}
-
-// Two segments: the first takes this fraction of the tokens.  Its one-block waves
-// run a chunk in ~190 ns, the second segment's two-block waves in ~1.5-2 times
-// that; of 0.60, 0.64, 0.68 and 0.72 the call is fastest at 0.64 (32 heads of
-// 32768 tokens).
-constexpr double kSplitFirst = 0.64;
-
-int split_point(int T)
-{
-    int t1 = (int)(kSplitFirst * T) / 16 * 16;
-    return t1 < 16 ? 16 : (t1 > T - 16 ? T - 16 : t1);
-}
-
-template <int ETA>
-hipError_t launch_split_eta(const LinearArgs& a, hipStream_t s)
-{
-    constexpr int D = 64;
-    const int T1 = split_point(a.T);
-    const unsigned units_r = (unsigned)((a.BH + 7) / 8 * 8 * (D / 16));
-    hipLaunchKernelGGL((linear_split_kernel<D, kChainPrefetch, kChainPrefetchWide, ETA>),
-                       dim3(2 * units_r), dim3(64), 0, s, (const uint16_t*)a.K,
-                       (const uint16_t*)a.Q, (const uint16_t*)a.V, a.eta, a.eta_scalar, a.W0,
-                       (uint16_t*)a.Z, a.workspace, a.BH, a.T, T1);
-    const int tiles = (a.T - T1) / 16;
-    dim3 fgrid((unsigned)((tiles + 4 * kFixTiles - 1) / (4 * kFixTiles)), (unsigned)a.BH);
-    hipLaunchKernelGGL((split_fixup_kernel<D>), fgrid, dim3(256), 0, s, (uint16_t*)a.Z,
-                       a.workspace, a.BH, a.T, T1);
-    hipLaunchKernelGGL((split_state_kernel<D>), dim3((unsigned)a.BH, D / 16), dim3(256), 0, s,
-                       a.W_out, a.workspace, a.BH, a.T, T1);
-    return hipGetLastError();
 }
 
 template <int D, int ETA, bool FULL>
@@ -1005,29 +628,6 @@ hipError_t launch_d(const LinearArgs& a, hipStream_t s)
 }
 
 }  // namespace
-
-bool linear_split_supported(int BH, int T, int d, int chunk, int bf16)
-{
-    // chunk-16 heads at d = 64 whose row blocks fill at most half the compute
-    // units, long enough to split; whole-tile loads use 32-bit byte offsets
-    return bf16 && d == 64 && chunk == 16 && T % 16 == 0 && T >= 2048 &&
-           (long)BH * (d / 16) <= kComputeUnits / 2 && (long long)T * d * 2 <= 0x7fffffffLL;
-}
-
-size_t linear_split_workspace(int BH, int T, int d)
-{
-    const int T2 = T - split_point(T);
-    const size_t ubytes = ((size_t)BH * T2 * d * 2 + 255) / 256 * 256;
-    return ubytes + 3 * (size_t)BH * d * d * sizeof(float);
-}
-
-hipError_t launch_linear_split(const LinearArgs& a, hipStream_t s)
-{
-    const bool eta4 = a.eta && reinterpret_cast<uintptr_t>(a.eta) % 16 == 0;
-    if (!a.eta) return launch_split_eta<kEtaScalar>(a, s);
-    if (eta4) return launch_split_eta<kEtaToken4>(a, s);
-    return launch_split_eta<kEtaToken>(a, s);
-}
 
 bool linear_mfma_supported(int d, int chunk, int bf16)
 {

@@ -1,0 +1,479 @@
+// TTT-Linear forward scan, chunks of 16 tokens, for few (batch, head) slices
+// with long sequences: the sequence of every slice is cut into S segments so
+// that S * slices workgroups fill the compute units.
+//
+// The chunk map is affine in the state: W -> W (I - P_c) + B_c with
+// P_c = K_c^T diag(eta) K_c, B_c = V_c^T diag(eta) K_c (PaperTrace "5 · TestingTime
+// 训练与长上下文" §1.1/§2.3; the dual form of diosapp "Test-Time Training (TTT)
+// guide" §3 inside a chunk), so the end state of segment k is W_B,k + W_start,k A_k,
+// where (W_B,k, A_k) is the scan of the segment from zero with V and from the
+// identity without V.  Three launches:
+//   pass 1   segment 0 scans from W0 (Z written, end state kept); segments
+//            1 .. S-1 form their maps (W_B, A) -- two chains per wave, no Z;
+//   combine  W_start,1 = end of segment 0, W_start,k+1 = W_B,k + W_start,k A_k;
+//   pass 2   segments 1 .. S-1 scan again from W_start,k (Z written; the last
+//            one's end state is W_T).
+// Every token is read twice past segment 0 (once for the map, once for the
+// replay), but no chain is longer than the longest segment.
+//
+// A workgroup is one (slice, segment) on one compute unit: four waves, wave w
+// owning state rows 16w .. 16w+15, sharing each chunk's K (and Q) tile through a
+// ring of swizzled LDS tiles, as the many-head kernel does (linear_coop.hip): one
+// unit's vector-memory path, not the matrix cores, bounds a chunk step, and the
+// shared tile cuts a chunk's fetch from 4 (K, Q) + 1 (V) KB per row block to
+// 4 KB per head plus 1 KB per row block.
+#include <stdint.h>
+
+#include <type_traits>
+#include <utility>
+
+#include "device_common.h"
+#include "launch.h"
+#include "mfma_common.h"
+
+namespace ttt {
+namespace {
+
+enum { kSegScan = 0, kSegMap = 1 };
+enum { kSegEtaScalar = 0, kSegEtaToken = 1, kSegEtaToken4 = 2 };
+
+constexpr int kSegD = 64;
+constexpr int kSegWaves = kSegD / 16;
+
+template <typename F, int... I>
+__device__ __forceinline__ void seg_unroll(F&& f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+// Where the segments of a slice start: segment 0 holds n0 chunks, the others n1
+// each (the last one takes what is left), all whole 16-token chunks.
+struct SegPlan {
+    int S;       // segments per slice
+    int n0, n1;  // chunks of segment 0 and of the middle segments
+    int nch;     // chunks of the whole sequence
+};
+
+__host__ __device__ inline int seg_first_chunk(const SegPlan& p, int k)
+{
+    return k == 0 ? 0 : p.n0 + (k - 1) * p.n1;
+}
+
+__host__ __device__ inline int seg_chunks(const SegPlan& p, int k)
+{
+    return k == 0 ? p.n0 : (k == p.S - 1 ? p.nch - p.n0 - (p.S - 2) * p.n1 : p.n1);
+}
+
+// Workspace, per slice: W_B, A and W_start of every segment (index 0 of W_start
+// holding segment 0's end state), [D, D] fp32 each.
+struct SegWorkspace {
+    float* wb;      // [BH, S, D, D]
+    float* amap;    // [BH, S, D, D]
+    float* wstart;  // [BH, S, D, D]
+};
+
+__host__ __device__ inline SegWorkspace seg_workspace(void* base, int BH, int S)
+{
+    SegWorkspace w;
+    const size_t n = (size_t)BH * S * kSegD * kSegD;
+    w.wb = reinterpret_cast<float*>(base);
+    w.amap = w.wb + n;
+    w.wstart = w.amap + n;
+    return w;
+}
+
+// chunks per barrier, chunks staged ahead, LDS ring slots (as the many-head
+// kernel with four waves)
+constexpr int kSegGroup = 4;
+constexpr int kSegAhead = 2 * kSegGroup;
+constexpr int kSegSlots = 2 * kSegAhead;
+
+// One (slice, segment) on a workgroup of four waves.
+//   SCAN: from the segment's start state (W0 for segment 0, else W_start), Z
+//         written; the end state goes to W_out for the last segment, to
+//         W_start[0] for segment 0.
+//   MAP:  the scans from zero with V (-> W_B) and from the identity without V
+//         (-> A), two chains per wave sharing its operands.
+template <int MODE, int ETA>
+__device__ __forceinline__ void seg_body(
+    KQTile16<kSegD>* L, const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
+    const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
+    const float* W0, uint16_t* __restrict__ Z, float* W_out, void* ws, int BH, int T,
+    const SegPlan& plan, int slice, int seg)
+{
+    constexpr int D = kSegD;
+    constexpr int NB = D / 16;
+    constexpr int NM = D / 32;
+    constexpr int G = D / 8;           // 16-byte granules per row
+    constexpr int RB = MODE == kSegMap ? 2 : 1;
+    constexpr int kGroup = kSegGroup;
+    constexpr int P = kSegAhead;
+    constexpr int kSlots = kSegSlots;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
+    const int ch0 = seg_first_chunk(plan, seg);
+    const int nch = seg_chunks(plan, seg);
+    const size_t tok0 = (size_t)slice * T + (size_t)16 * ch0;
+    const int out0 = 16 * wave;
+    const SegWorkspace w = seg_workspace(ws, BH, plan.S);
+    const size_t dd = (size_t)D * D;
+    const size_t sw = ((size_t)slice * plan.S + seg) * dd;   // this segment's [D, D] block
+
+    // this thread's granule of each staged tile: K (threads 0..127) or Q
+    const int which = tid / (16 * G);
+    const int grow = (tid / G) & 15;
+    const int ggr = tid % G;
+    const int lpos = grow * G + (ggr ^ tile16_swizzle<D>(grow));
+    const bool loads = MODE == kSegScan || which == 0;   // the map reads no Q
+    auto chunk_base = [&](int ch) {   // first token of chunk ch (clamped)
+        const int cc = ch < nch ? ch : nch - 1;
+        return tok0 + (size_t)16 * cc;
+    };
+    auto gload = [&](u32x4& r, int ch) {
+        if (loads) r = *(const u32x4*)((which ? Q : K) + chunk_base(ch) * D + (grow * D + 8 * ggr));
+    };
+    auto gstore = [&](KQTile16<D>& t, const u32x4& r) {
+        if (loads) t.g[which][lpos] = r;
+    };
+    auto vload = [&](int ch) {
+        return *(const u32x2*)(V + chunk_base(ch) * D + (c * D + out0 + 4 * g));
+    };
+    auto eload = [&](int ch) {
+        if (ETA == kSegEtaToken4) {
+            return *(const f32x4*)(eta + chunk_base(ch) + 4 * g);
+        } else if (ETA == kSegEtaToken) {
+            f32x4 e;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) e[r] = eta[chunk_base(ch) + 4 * g + r];
+            return e;
+        } else {
+            return f32x4{eta_scalar, eta_scalar, eta_scalar, eta_scalar};
+        }
+    };
+    auto row_operand = [&](const u32x4* t, u32x4 (&op)[NM]) {
+#pragma unroll
+        for (int m = 0; m < NM; ++m) op[m] = t[c * G + ((4 * m + g) ^ tile16_swizzle<D>(c))];
+    };
+
+    // state rows out0 + c, columns pi(jb, 4g + i) = 32 (jb / 2) + 8g + 4 (jb % 2) + i
+    f32x4 M[RB][NB];
+    if constexpr (MODE == kSegMap) {
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+            const int base = 32 * (jb >> 1) + 8 * g + 4 * (jb & 1);
+            M[0][jb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) M[1][jb][i] = (base + i == out0 + c) ? 1.f : 0.f;
+        }
+    } else {
+        const float* w0 = seg == 0 ? W0 + (size_t)slice * dd : w.wstart + sw;
+        const float* wr = w0 + (size_t)(out0 + c) * D;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            M[0][2 * m] = *(const f32x4*)(wr + 32 * m + 8 * g);
+            M[0][2 * m + 1] = *(const f32x4*)(wr + 32 * m + 8 * g + 4);
+        }
+    }
+    u32x4 Mf[RB][NM];
+#pragma unroll
+    for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) Mf[r][m] = pack_bf16x8(M[r][2 * m], M[r][2 * m + 1]);
+    const u32x2 I16 = identity_b16(lane);
+    // -V of chunk data for chain r (the identity chain has no V)
+    auto vneg_of = [&](u32x2 v, int r) {
+        return r == 0 ? v ^ u32x2{0x80008000u, 0x80008000u} : u32x2{0u, 0u};
+    };
+
+    // chunk X lives in LDS slot X % kSlots; tiles of chunks 0 .. P-1 are stored up
+    // front, and during chunk ch the tile of chunk ch + P is stored and the
+    // granule of chunk ch + 2P loaded (into the register slot it came from)
+    u32x4 rg[P];
+    u32x2 rv[P];
+    f32x4 re[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        gload(rg[p], p);
+        rv[p] = vload(p);
+        re[p] = eload(p);
+    }
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        gstore(L[p], rg[p]);
+        gload(rg[p], P + p);
+    }
+    __syncthreads();
+
+    // E_0 = K_0 W^T - V_0 for each chain; kb[ch & 1] holds K_ch as row operand, the
+    // other set K_{ch+1}
+    u32x4 kb[2][NM];
+    row_operand(L[0].g[0], kb[0]);
+    row_operand(L[1].g[0], kb[1]);
+    f32x4 Et[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        Et[r] = mfma16(vneg_of(rv[0], r), I16, f32x4{0, 0, 0, 0});
+#pragma unroll
+        for (int m = 0; m < NM; ++m) Et[r] = mfma32(kb[0][m], Mf[r][m], Et[r]);
+    }
+    // 16-deep products as 32-deep ones whose lower half is zero in one operand
+    u32x4 ktz[NB], smz = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) ktz[jb] = u32x4{0u, 0u, 0u, 0u};
+
+    auto step = [&](int ch, auto kc_) {
+        constexpr int k = decltype(kc_)::value;
+        constexpr int p = k % P;
+        if (ch + P < nch) gstore(L[(k + P) % kSlots], rg[p]);
+        gload(rg[p], ch + 2 * P);
+
+        const u32x4* Kc = L[k].g[0];
+        constexpr int pe = p & 1;
+        u32x4 (&kc)[NM] = kb[pe];
+        u32x4 (&kn)[NM] = kb[pe ^ 1];
+        // K_c with the feature in the lanes (A operand of the state update)
+        {
+            const int r = (lane >> 2) & 3, q = lane & 3;
+            const int row = 4 * g + r;
+            const u32x2* base = reinterpret_cast<const u32x2*>(Kc) + row * (2 * G);
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) {
+                auto pt = (__attribute__((address_space(3))) s16x4*)(
+                    base + 2 * ((4 * (jb >> 1) + q) ^ tile16_swizzle<D>(row)) + (jb & 1));
+                const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(pt));
+                ktz[jb].z = t.x;
+                ktz[jb].w = t.y;
+            }
+        }
+        const f32x4 et = re[p];
+        // F_c = -diag(eta) E_c per chain
+        u32x4 IF[RB];
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const u32x2 F = pack_bf16x4(-et * Et[r]);
+            IF[r] = u32x4{I16.x, I16.y, F.x, F.y};
+        }
+        // E_{c+1} = K_{c+1} W_c^T + [-V_{c+1} | G_c] [I ; F_c]
+        {
+            f32x4 Gt = {0, 0, 0, 0};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) Gt = mfma32(kc[m], kn[m], Gt);
+            const u32x2 Gb = pack_bf16x4(Gt);
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                f32x4 Pt = {0, 0, 0, 0};
+#pragma unroll
+                for (int m = 0; m < NM; ++m) Pt = mfma32(kn[m], Mf[r][m], Pt);
+                const u32x2 vneg = vneg_of(rv[(p + 1) % P], r);
+                Et[r] = mfma32(u32x4{vneg.x, vneg.y, Gb.x, Gb.y}, IF[r], Pt);
+            }
+        }
+        // W_{c+1} = W_c + F_c^T K_c
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int jb = 0; jb < NB; ++jb) M[r][jb] = mfma32(ktz[jb], IF[r], M[r][jb]);
+        if constexpr (MODE == kSegScan) {
+            // Z_c = Q_c W_c^T + causal scores times F_c
+            u32x4 qc[NM];
+            row_operand(L[k].g[1], qc);
+            f32x4 St = {0, 0, 0, 0};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) St = mfma32(kc[m], qc[m], St);
+            f32x4 Sm;
+            Sm.x = (4 * g + 0 <= c) ? St.x : 0.f;
+            Sm.y = (4 * g + 1 <= c) ? St.y : 0.f;
+            Sm.z = (4 * g + 2 <= c) ? St.z : 0.f;
+            Sm.w = (4 * g + 3 <= c) ? St.w : 0.f;
+            f32x4 Zt = {0, 0, 0, 0};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[0][m], qc[m], Zt);
+            const u32x2 sb = pack_bf16x4(Sm);
+            smz.z = sb.x;
+            smz.w = sb.y;
+            Zt = mfma32(IF[0], smz, Zt);
+            uint16_t* zb = Z + (tok0 + (size_t)16 * ch) * D;
+            *(u32x2*)(zb + (c * D + out0 + 4 * g)) = pack_bf16x4(Zt);
+        }
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int m = 0; m < NM; ++m) Mf[r][m] = pack_bf16x8(M[r][2 * m], M[r][2 * m + 1]);
+        row_operand(L[(k + 2) % kSlots].g[0], kc);   // K_{c+2} (stale past the end)
+        rv[p] = vload(ch + P);
+        re[p] = eload(ch + P);
+        if (p % kGroup == kGroup - 1) __syncthreads();
+    };
+
+    int c0 = 0;
+    for (; c0 + kSlots <= nch; c0 += kSlots)
+        seg_unroll([&](auto k) { step(c0 + k, k); }, std::make_integer_sequence<int, kSlots>{});
+    seg_unroll([&](auto k) {
+        if (c0 + k < nch) step(c0 + k, k);
+    }, std::make_integer_sequence<int, kSlots - 1>{});
+
+    // end states
+    float* dst[RB];
+    if constexpr (MODE == kSegMap) {
+        dst[0] = w.wb + sw;
+        dst[1] = w.amap + sw;
+    } else {
+        dst[0] = seg == plan.S - 1 ? W_out + (size_t)slice * dd
+                                   : w.wstart + ((size_t)slice * plan.S) * dd;   // segment 0
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        float* wr = dst[r] + (size_t)(out0 + c) * D;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            *(f32x4*)(wr + 32 * m + 8 * g) = M[r][2 * m];
+            *(f32x4*)(wr + 32 * m + 8 * g + 4) = M[r][2 * m + 1];
+        }
+    }
+}
+
+// Pass 1: workgroup (slice, segment), segment 0 scanning and the others forming
+// their maps, all at once.  Pass 2: segments 1 .. S-1 scanning from their start
+// states.  The segments of a slice are adjacent workgroups.
+template <int ETA>
+__global__ __launch_bounds__(256) void linear_seg_pass1_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
+    const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
+    const float* W0, uint16_t* __restrict__ Z, float* W_out, void* ws, int BH, int T,
+    SegPlan plan)
+{
+    __shared__ KQTile16<kSegD> L[kSegSlots];
+    const int slice = (int)blockIdx.x / plan.S, seg = (int)blockIdx.x % plan.S;
+    if (seg == 0)
+        seg_body<kSegScan, ETA>(L, K, Q, V, eta, eta_scalar, W0, Z, W_out, ws, BH, T, plan, slice, 0);
+    else
+        seg_body<kSegMap, ETA>(L, K, Q, V, eta, eta_scalar, W0, Z, W_out, ws, BH, T, plan, slice, seg);
+}
+
+template <int ETA>
+__global__ __launch_bounds__(256) void linear_seg_pass2_kernel(
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
+    const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
+    const float* W0, uint16_t* __restrict__ Z, float* W_out, void* ws, int BH, int T,
+    SegPlan plan)
+{
+    __shared__ KQTile16<kSegD> L[kSegSlots];
+    const int slice = (int)blockIdx.x / (plan.S - 1), seg = 1 + (int)blockIdx.x % (plan.S - 1);
+    seg_body<kSegScan, ETA>(L, K, Q, V, eta, eta_scalar, W0, Z, W_out, ws, BH, T, plan, slice, seg);
+}
+
+// W_start,k+1 = W_B,k + W_start,k A_k for k = 1 .. S-2 (W_start,1 = the end of
+// segment 0, left in W_start[0] by pass 1), in fp32: one workgroup per (slice,
+// 16 rows), thread (row i, column quad q).  A_k and the current rows sit in LDS,
+// double-buffered by k's parity; A_{k+1} and W_B,k+1 are fetched while step k
+// computes, so the chain of S - 2 steps waits on memory once.
+__global__ __launch_bounds__(256) void seg_combine_kernel(void* ws, int BH, int S)
+{
+    constexpr int D = kSegD;
+    constexpr int NQ = D * D / 4 / 256;   // f32x4 of A per thread
+    __shared__ f32x4 al[2][D * D / 4];
+    __shared__ float wl[2][16 * D];
+    const SegWorkspace w = seg_workspace(ws, BH, S);
+    const size_t dd = (size_t)D * D;
+    const int slice = blockIdx.x, i0 = 16 * blockIdx.y;
+    const int tid = threadIdx.x;
+    const int i = tid >> 4, q = tid & 15;
+    const size_t row = (size_t)(i0 + i) * D + 4 * q;
+    float* base = w.wstart + (size_t)slice * S * dd;
+    f32x4 cur = *(const f32x4*)(base + row);
+    *(f32x4*)(base + dd + row) = cur;
+    f32x4 ar[NQ], wbr = {0, 0, 0, 0};
+    auto fetch = [&](int k) {
+        const size_t sk = ((size_t)slice * S + k) * dd;
+#pragma unroll
+        for (int e = 0; e < NQ; ++e) ar[e] = *(const f32x4*)(w.amap + sk + 4 * (tid + 256 * e));
+        wbr = *(const f32x4*)(w.wb + sk + row);
+    };
+    if (S > 2) fetch(1);
+    for (int k = 1; k + 1 < S; ++k) {
+        const int b = k & 1;
+#pragma unroll
+        for (int e = 0; e < NQ; ++e) al[b][tid + 256 * e] = ar[e];
+        wl[b][i * D + 4 * q + 0] = cur.x;
+        wl[b][i * D + 4 * q + 1] = cur.y;
+        wl[b][i * D + 4 * q + 2] = cur.z;
+        wl[b][i * D + 4 * q + 3] = cur.w;
+        f32x4 o = wbr;
+        __syncthreads();
+        if (k + 2 < S) fetch(k + 1);
+        for (int j = 0; j < D; ++j) {
+            const float a = wl[b][i * D + j];
+            const f32x4 r = al[b][j * (D / 4) + q];
+            o.x = fmaf(a, r.x, o.x);
+            o.y = fmaf(a, r.y, o.y);
+            o.z = fmaf(a, r.z, o.z);
+            o.w = fmaf(a, r.w, o.w);
+        }
+        cur = o;
+        *(f32x4*)(base + (k + 1) * dd + row) = cur;
+    }
+}
+
+// Segment lengths: n0 = kSegFirstRatio n1.  Measured per call (32 heads of 32768
+// tokens): 0.5 -> 0.229 ms, 0.7 -> 0.226, 0.85 -> 0.219, 1.0 -> 0.233, 1.2 -> 0.240,
+// 1.4 -> 0.250; 16 and 8 heads change by under 5% across 0.5 .. 1.0.
+constexpr double kSegFirstRatio = 0.85;
+constexpr int kSegMinChunks = 32;     // shortest middle segment
+constexpr int kSegUnits = 256;        // MI355X compute units
+
+SegPlan seg_plan(int BH, int T)
+{
+    SegPlan p;
+    p.nch = T / 16;
+    int S = kSegUnits / (BH > 0 ? BH : 1);
+    S = S > 64 ? 64 : S;
+    while (S > 2 && p.nch < (int)((S - 1 + kSegFirstRatio) * kSegMinChunks)) --S;
+    p.S = S < 2 ? 2 : S;
+    p.n1 = (int)(p.nch / (p.S - 1 + kSegFirstRatio));
+    p.n0 = p.nch - (p.S - 1) * p.n1;   // the remainder goes to segment 0
+    return p;
+}
+
+template <int ETA>
+hipError_t launch_seg_eta(const LinearArgs& a, hipStream_t s)
+{
+    const SegPlan p = seg_plan(a.BH, a.T);
+    const unsigned bh = (unsigned)a.BH;
+    hipLaunchKernelGGL((linear_seg_pass1_kernel<ETA>), dim3(bh * p.S), dim3(256), 0, s,
+                       (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V, a.eta,
+                       a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.workspace, a.BH, a.T, p);
+    hipLaunchKernelGGL(seg_combine_kernel, dim3(bh, kSegD / 16), dim3(256), 0, s, a.workspace,
+                       a.BH, p.S);
+    hipLaunchKernelGGL((linear_seg_pass2_kernel<ETA>), dim3(bh * (p.S - 1)), dim3(256), 0, s,
+                       (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V, a.eta,
+                       a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.workspace, a.BH, a.T, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool linear_seg_supported(int BH, int T, int d, int chunk, int bf16)
+{
+    return bf16 && d == kSegD && chunk == 16 && T % 16 == 0 && T >= 2048 && BH >= 1 &&
+           (long)BH * 8 <= kSegUnits && (long long)BH * T * d * 2 <= 0x7fffffffffffLL;
+}
+
+size_t linear_seg_workspace(int BH, int T, int d)
+{
+    (void)d;
+    const SegPlan p = seg_plan(BH, T);
+    return 3 * (size_t)BH * p.S * kSegD * kSegD * sizeof(float);
+}
+
+hipError_t launch_linear_seg(const LinearArgs& a, hipStream_t s)
+{
+    const bool eta4 = a.eta && reinterpret_cast<uintptr_t>(a.eta) % 16 == 0;
+    if (!a.eta) return launch_seg_eta<kSegEtaScalar>(a, s);
+    if (eta4) return launch_seg_eta<kSegEtaToken4>(a, s);
+    return launch_seg_eta<kSegEtaToken>(a, s);
+}
+
+}  // namespace ttt

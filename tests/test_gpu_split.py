@@ -1,7 +1,9 @@
-"""GPU parity of the two-segment plan (chunk-16 TTT-Linear at d = 64 with few
-(batch, head) slices: both segments of the sequence scanned at once, the second
-from zero and from the identity, joined by a fix-up pass) against the fp64
-oracle, element by element: max relative error per slice below 2e-2 (bf16)."""
+"""GPU parity of the segmented plan (chunk-16 TTT-Linear at d = 64 with few
+(batch, head) slices: each sequence cut into S ~ 256 / slices segments; segment 0
+scans while the others form their affine maps from zero and from the identity, a
+combine gives every segment its start state, and the segments after the first
+scan again from it) against the fp64 oracle, element by element: max relative
+error per slice below 2e-2 (bf16)."""
 import numpy as np
 import pytest
 
@@ -41,8 +43,8 @@ def check(wl, seed, dev, plan=ttt.PLAN_SPLIT, slices=None, eta_offset=0):
     assert ez < TOL["bf16"] and ew < TOL["bf16"], (ez, ew)
 
 
-# lengths: the shortest taken, split points that are and are not multiples of the
-# prefetch ring, a second segment of a few tiles
+# lengths: the shortest taken, and segment lengths that are and are not multiples
+# of the LDS ring (16 chunks)
 @pytest.mark.parametrize("T", [2048, 2064, 3008, 4096, 5120])
 @pytest.mark.parametrize("per_token", [True, False])
 def test_lengths(dev, T, per_token):
@@ -50,12 +52,19 @@ def test_lengths(dev, T, per_token):
     check(wl, seed, dev)
 
 
-# slice counts up to the 32 (128 row blocks) the plan takes; grids not a multiple
-# of the 8 XCDs
+# slice counts up to the 32 the plan takes (8 to 64 segments each)
 @pytest.mark.parametrize("B,H", [(1, 1), (1, 7), (2, 9), (4, 8)])
 def test_slice_counts(dev, B, H):
     wl, seed = case(2080, B=B, H=H)
     check(wl, seed, dev)
+
+
+# long chains of segment maps: one slice in 32 segments (30 combine steps), two in
+# 16, sixteen in 8
+@pytest.mark.parametrize("B,H,T", [(1, 1, 16384), (1, 2, 8192), (2, 8, 4096)])
+def test_many_segments(dev, B, H, T):
+    wl, seed = case(T, B=B, H=H, seed=157)
+    check(wl, seed, dev, slices=[0, wl.BH - 1])
 
 
 def test_unaligned_eta(dev):
@@ -114,7 +123,7 @@ def test_nan_stays_in_its_slice(dev):
     wl, seed = case(2048, B=2, H=3)
     x = inputs.make_inputs(wl, seed)
     a = device_inputs(wl, x, dev)
-    a["V"][1, 2, 1900, 5] = float("nan")    # in the second segment
+    a["V"][1, 2, 1900, 5] = float("nan")    # in the last segment
     a["K"][0, 1, 100, 7] = float("nan")     # in the first segment
     Z, W = ttt.linear_fwd(a["K"], a["Q"], a["V"], a["eta"], a["W0"], 16, plan=ttt.PLAN_SPLIT)
     torch.cuda.synchronize()

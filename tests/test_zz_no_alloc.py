@@ -29,10 +29,10 @@ def shape_case(B, H, T, d, chunk, per_token, seed):
 
 
 # Calls in a row on one stream, each smaller than the one before: the large-chunk
-# plan in the scratch, the two-segment plan over a smaller part of it, the
+# plan in the scratch, the segmented chunk-16 plan over a smaller part of it, the
 # large-chunk plan again, and a shape that needs no workspace at all.
 CALLS = [(1, 4, 8192, 128, 2048, False, 301),      # 10.0 MiB of scratch
-         (1, 4, 4096, 64, 16, True, 304),           # 0.9 MiB, two segments
+         (1, 4, 4096, 64, 16, True, 304),           # 1.5 MiB, eight segments
          (2, 3, 1000, 64, 256, True, 302),          # 0.7 MiB, ragged last chunk
          (1, 2, 300, 64, 16, True, 303)]            # chunk-16 plan, no workspace
 
@@ -76,34 +76,3 @@ def test_noalloc_rejects_oversized_workspace(dev):
                                           1, 7, 131072, 128, 2048, ttt.DTYPE_BF16, None)
     assert rc == ttt.ERR_WORKSPACE
 
-
-def test_noalloc_long_two_segment_shape_runs_chunk_by_chunk(dev):
-    """32 heads x 49152 tokens: the two-segment plan would need 72 MiB of workspace,
-    more than the scratch holds, so the entry point runs the chunk-by-chunk plan,
-    which needs none (bit-identical to ttt_linear_fwd_ex with that plan)."""
-    import torch
-    B, H, T, d, chunk = 1, 32, 49152, 64, 16
-    assert ttt.linear_select_plan(B, H, T, d, chunk, ttt.DTYPE_BF16) == ttt.PLAN_SPLIT
-    assert (ttt.linear_workspace_bytes(B, H, T, d, chunk, ttt.DTYPE_BF16, ttt.PLAN_SPLIT)
-            > ttt.linear_noalloc_scratch_bytes())
-    wl, seed = shape_case(B, H, T, d, chunk, True, 305)
-    say("case", wl, "two-segment workspace too large: chunk-by-chunk plan")
-    x = inputs.make_inputs(wl, seed)
-    a = device_inputs(wl, x, dev)
-    Z1, W1 = ttt.linear_fwd(a["K"], a["Q"], a["V"], a["eta"], a["W0"], chunk,
-                            eta_scalar=x["eta_scalar"], plan=ttt.PLAN_MFMA)
-    Z2 = torch.full_like(Z1, float("nan"))
-    W2 = torch.full_like(W1, float("nan"))
-    torch.cuda.synchronize()
-    ttt.linear_fwd_noalloc(a["K"], a["Q"], a["V"], a["eta"], a["W0"], chunk,
-                           eta_scalar=x["eta_scalar"], Z=Z2, W_out=W2)
-    torch.cuda.synchronize()
-    assert torch.equal(Z1, Z2) and torch.equal(W1, W2)
-    idx = np.array([0, wl.BH - 1])
-    xo = take(x, idx)
-    Zo, Wo = oracle.linear(xo["K"], xo["Q"], xo["V"], xo["eta"], xo["eta_scalar"],
-                           xo["W0"], chunk)
-    ez = rel_err(host(Z2, wl.BH)[idx], Zo)
-    ew = rel_err(host(W2, wl.BH)[idx], Wo)
-    say("  max rel err Z %.3e  W %.3e" % (ez, ew))
-    assert ez < TOL["bf16"] and ew < TOL["bf16"]
