@@ -243,9 +243,10 @@ size_t ttt_linear_bwd_workspace_bytes(int B, int H, int T, int d, int chunk, int
  *   workspace      : at least ttt_linear_bwd_workspace_bytes(...) bytes,
  *                    256-byte aligned.
  * Arithmetic is fp32 (inputs in bf16 are widened exactly).  dK, dQ and deta
- * are sums over the state's 16-row blocks formed by atomic adds, so their
- * last bits may differ between calls.  Outputs must not overlap inputs or each
- * other. */
+ * are sums over the state's 16-row blocks, each block's terms kept in its own
+ * fp32 plane of the workspace and the planes added in a fixed order: every
+ * output is the same bits on every call.  Outputs must not overlap inputs or
+ * each other. */
 int ttt_linear_bwd(const void* K, const void* Q, const void* V,
                    const float* eta, float eta_scalar, const float* W0,
                    const void* dZ, const float* dW_T,

@@ -20,8 +20,9 @@
 // keeps its blocks of W, P, dW and H and computes its blocks of dK and dQ, and
 // the contractions over all columns (E, P K^T, K Q^T) are summed from per-wave
 // partial tiles in LDS.  Contributions to dK, dQ and deta (sums over the rows)
-// are added by fp32 atomic adds into buffers cleared before the launch (the
-// outputs themselves with fp32 I/O; with bf16 I/O a last pass rounds the sums).
+// go to one fp32 plane per row block, each element written once; a last pass
+// adds the planes in row-block order (and rounds to bf16 with bf16 I/O), so the
+// results are the same bits on every call.
 //
 // Every product is a 16 x 16 tile product, operands staged through LDS in
 // row-major fp32 tiles with padded rows.  With fp32 I/O it runs on the fp32
@@ -46,11 +47,6 @@
 #include "mfma_f32.h"
 
 namespace ttt {
-
-// fp32 buffer atomic add (no-return form when the result is unused)
-__device__ float raw_buffer_atomic_fadd(float v, __amdgpu_buffer_rsrc_t rsrc, int voffset,
-                                        int soffset, int aux)
-    __asm("llvm.amdgcn.raw.ptr.buffer.atomic.fadd.f32");
 
 namespace {
 
@@ -168,9 +164,11 @@ struct BwdArgs {
     void* dV;
     float* dW0;
     float* states;        // [BH, nch + 1, d, d]
-    float* dK_acc;        // [BH, T, d] fp32, zeroed before the launch
-    float* dQ_acc;        // [BH, T, d] fp32, zeroed before the launch
-    float* deta_acc;      // [BH, T] fp32, zeroed before the launch; may be null
+    float* dK_part;       // [d/16, BH, T, d] fp32: this row block's terms of dK
+    float* dQ_part;       // [d/16, BH, T, d] fp32
+    float* deta_part;     // [d/16, BH, T] fp32; null when deta is not wanted
+    size_t plane;         // BH T d: elements of one dK / dQ plane
+    size_t tplane;        // BH T: elements of one deta plane
     int BH, T, chunk;
 };
 
@@ -477,9 +475,11 @@ __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
         de += __shfl_xor(de, 32);
         {
             const bool w0 = wave == 0;
-            const auto rde = buffer_range(a.deta_acc ? a.deta_acc + tokb + t0 : nullptr,
-                                          w0 && a.deta_acc ? 4u * len : 0u);
-            raw_buffer_atomic_fadd(de, rde, 4 * (g == 0 ? c : kSub), 0, 0);
+            const auto rde = buffer_range(a.deta_part ? a.deta_part + rb * a.tplane + tokb + t0
+                                                      : nullptr,
+                                          w0 && a.deta_part ? 4u * len : 0u);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(de), rde,
+                                                  4 * (g == 0 ? c : kSub), 0, 0);
             const auto rdv = buffer_range(static_cast<TIO*>(a.dV) + (tokb + t0) * D,
                                           w0 ? (uint32_t)(len * D * sizeof(TIO)) : 0u);
             buffer_store4(rdv, (c * D + r0 + 4 * g) * (int)sizeof(TIO), -dE, TIO{});
@@ -505,8 +505,8 @@ __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
 #pragma unroll
         for (int v = 0; v < 4; ++v) Fn[v] = -F[v];
         const uint32_t tile_bytes = (uint32_t)(len * D * sizeof(float));
-        const auto rdk = buffer_range(a.dK_acc + (tokb + t0) * D, tile_bytes);
-        const auto rdq = buffer_range(a.dQ_acc + (tokb + t0) * D, tile_bytes);
+        const auto rdk = buffer_range(a.dK_part + rb * a.plane + (tokb + t0) * D, tile_bytes);
+        const auto rdq = buffer_range(a.dQ_part + rb * a.plane + (tokb + t0) * D, tile_bytes);
 #pragma unroll
         for (int bb = 0; bb < NBW; ++bb) {
             const int b = blk(bb);
@@ -524,8 +524,8 @@ __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int off = 4 * ((4 * g + v) * D + 16 * b + c);
-                raw_buffer_atomic_fadd(dK[v], rdk, off, 0, 0);
-                raw_buffer_atomic_fadd(dQ[v], rdq, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(dK[v]), rdk, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(dQ[v]), rdq, off, 0, 0);
             }
             // P += dZ Q, dW += dE K
             P[bb] = mmt<BF, true, true>(dZa, qc, P[bb]);
@@ -557,35 +557,47 @@ __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
 
 // n floats set to zero: 16-byte stores (n a multiple of 4, p 16-byte aligned)
 // or, with VEC false, 4-byte ones
-template <bool VEC>
-__global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, size_t n)
+// dK and dQ: the row-block planes added in order, four elements per thread,
+// written in the I/O type
+template <typename TIO, int NB>
+__global__ __launch_bounds__(256) void sum_planes_kernel(const float* __restrict__ dK_part,
+                                                         const float* __restrict__ dQ_part,
+                                                         TIO* __restrict__ dK, TIO* __restrict__ dQ,
+                                                         size_t n)
 {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
-    const size_t first = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if constexpr (VEC) {
-        for (size_t i = first; i < n / 4; i += stride)
-            reinterpret_cast<f32x4*>(p)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    } else {
-        for (size_t i = first; i < n; i += stride) p[i] = 0.f;
+    auto put = [](TIO* out, size_t i, f32x4 v) {
+        if constexpr (sizeof(TIO) == 4) {
+            reinterpret_cast<f32x4*>(out)[i] = v;
+        } else {
+            const u32x2 p = pack_bf16x4(v);
+            reinterpret_cast<uint2*>(out)[i] = uint2{p.x, p.y};
+        }
+    };
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n / 4; i += stride) {
+        f32x4 k = reinterpret_cast<const f32x4*>(dK_part)[i];
+        f32x4 q = reinterpret_cast<const f32x4*>(dQ_part)[i];
+#pragma unroll
+        for (int r = 1; r < NB; ++r) {
+            k += reinterpret_cast<const f32x4*>(dK_part + r * n)[i];
+            q += reinterpret_cast<const f32x4*>(dQ_part + r * n)[i];
+        }
+        put(dK, i, k);
+        put(dQ, i, q);
     }
 }
 
-// the fp32 sums of dK and dQ rounded to bf16, four elements per thread
-__global__ __launch_bounds__(256) void round_bf16_kernel(const float* __restrict__ dK_acc,
-                                                         const float* __restrict__ dQ_acc,
-                                                         uint16_t* __restrict__ dK,
-                                                         uint16_t* __restrict__ dQ, size_t n)
+// deta: the row-block planes added in order (deta is only 4-byte aligned)
+template <int NB>
+__global__ __launch_bounds__(256) void sum_deta_kernel(const float* __restrict__ part,
+                                                       float* __restrict__ deta, size_t n)
 {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
-    auto pack = [](f32x4 v) {
-        const u32x2 p = pack_bf16x4(v);
-        return uint2{p.x, p.y};
-    };
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n / 4; i += stride) {
-        const f32x4 k = reinterpret_cast<const f32x4*>(dK_acc)[i];
-        const f32x4 q = reinterpret_cast<const f32x4*>(dQ_acc)[i];
-        reinterpret_cast<uint2*>(dK)[i] = pack(k);
-        reinterpret_cast<uint2*>(dQ)[i] = pack(q);
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        float v = part[i];
+#pragma unroll
+        for (int r = 1; r < NB; ++r) v += part[r * n + i];
+        deta[i] = v;
     }
 }
 
@@ -606,20 +618,16 @@ hipError_t launch_typed(const LinearBwdArgs& a, hipStream_t s)
     k.W0 = a.W0; k.dZ = a.dZ; k.dWT = a.dW_T; k.dV = a.dV; k.dW0 = a.dW0;
     k.states = reinterpret_cast<float*>(ws);
     ws += linear_bwd_align((size_t)a.BH * (nch + 1) * D * D * sizeof(float));
-    // dK, dQ and deta are sums over the d/16 row blocks, added into fp32 buffers
-    // by atomic adds (the outputs themselves with fp32 I/O; deta is fp32 always)
-    constexpr bool F32 = sizeof(TIO) == 4;
-    k.dK_acc = F32 ? static_cast<float*>(a.dK) : reinterpret_cast<float*>(ws);
-    ws += linear_bwd_align(n * sizeof(float));
-    k.dQ_acc = F32 ? static_cast<float*>(a.dQ) : reinterpret_cast<float*>(ws);
-    k.deta_acc = a.deta;
+    // dK, dQ and deta are sums over the d/16 row blocks: one fp32 plane each per row
+    // block, added in order after the scan
+    k.plane = n;
+    k.tplane = ntok;
+    k.dK_part = reinterpret_cast<float*>(ws);
+    ws += linear_bwd_align(NB * n * sizeof(float));
+    k.dQ_part = reinterpret_cast<float*>(ws);
+    ws += linear_bwd_align(NB * n * sizeof(float));
+    k.deta_part = a.deta ? reinterpret_cast<float*>(ws) : nullptr;
     k.BH = a.BH; k.T = a.T; k.chunk = a.chunk;
-    // (fill kernels rather than memsets, so that the call can be captured in a graph)
-    hipLaunchKernelGGL(zero_kernel<true>, dim3(elementwise_grid(n)), dim3(256), 0, s, k.dK_acc, n);
-    hipLaunchKernelGGL(zero_kernel<true>, dim3(elementwise_grid(n)), dim3(256), 0, s, k.dQ_acc, n);
-    if (a.deta)   // deta is only 4-byte aligned
-        hipLaunchKernelGGL(zero_kernel<false>, dim3(elementwise_grid(4 * ntok)), dim3(256), 0, s,
-                           a.deta, ntok);
     const unsigned grid = (unsigned)(((a.BH + 7) / 8) * 8 * NB);
     auto launch = [&](auto nw) {
         constexpr int NW = decltype(nw)::value;
@@ -630,16 +638,19 @@ hipError_t launch_typed(const LinearBwdArgs& a, hipStream_t s)
             hipLaunchKernelGGL((linear_bwd_kernel<TIO, D, NW, false>), dim3(grid), dim3(64 * NW),
                                0, s, k);
     };
+    constexpr bool F32 = sizeof(TIO) == 4;
     if constexpr (!F32 && D == 64) {
         if ((long)a.BH * NB >= kComputeUnits) launch(std::integral_constant<int, 1>{});
         else launch(std::integral_constant<int, 2>{});   // two waves per unit
     } else {
         launch(std::integral_constant<int, bwd_waves<D>()>{});
     }
-    if constexpr (!F32)
-        hipLaunchKernelGGL(round_bf16_kernel, dim3(elementwise_grid(n)), dim3(256), 0, s,
-                           k.dK_acc, k.dQ_acc, static_cast<uint16_t*>(a.dK),
-                           static_cast<uint16_t*>(a.dQ), n);
+    hipLaunchKernelGGL((sum_planes_kernel<TIO, NB>), dim3(elementwise_grid(n)), dim3(256), 0, s,
+                       (const float*)k.dK_part, (const float*)k.dQ_part, static_cast<TIO*>(a.dK),
+                       static_cast<TIO*>(a.dQ), n);
+    if (a.deta)
+        hipLaunchKernelGGL((sum_deta_kernel<NB>), dim3(elementwise_grid(4 * ntok)), dim3(256), 0,
+                           s, (const float*)k.deta_part, a.deta, ntok);
     return hipGetLastError();
 }
 
@@ -661,11 +672,13 @@ size_t linear_bwd_align(size_t bytes) { return (bytes + 255) & ~(size_t)255; }
 
 size_t linear_bwd_workspace(int BH, int T, int d, int chunk, bool bf16)
 {
+    (void)bf16;
     const size_t nch = (size_t)(T + chunk - 1) / chunk;
-    const size_t n = (size_t)BH * T * d;
-    // chunk-start states, then (bf16 I/O) the fp32 sums of dK and dQ
+    const size_t n = (size_t)BH * T * d, nb = (size_t)d / 16;
+    // chunk-start states, then the row blocks' fp32 planes of dK, dQ and deta
     return linear_bwd_align((size_t)BH * (nch + 1) * d * d * sizeof(float)) +
-           (bf16 ? 2 * linear_bwd_align(n * sizeof(float)) : 0);
+           2 * linear_bwd_align(nb * n * sizeof(float)) +
+           linear_bwd_align(nb * (size_t)BH * T * sizeof(float));
 }
 
 hipError_t launch_linear_bwd(const LinearBwdArgs& a, hipStream_t s)

@@ -102,3 +102,22 @@ def test_full_size_sampled(dev, name, slices):
     checked against the oracle."""
     wl = inputs.WORKLOADS[name]
     check_bwd(wl, inputs.WORKLOAD_SEEDS[name], dev, slices=slices)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_bitwise_deterministic(dev, io):
+    """dK, dQ and deta are sums over the state's row blocks: they come out the same
+    bits on every call (planes added in a fixed order, no atomics)."""
+    import torch
+    wl = case(64, 16, io, True, 300, B=2, H=5)
+    x = inputs.make_inputs(wl, 419)
+    dZ, dWT = cotangents(wl, 419)
+    a = device_inputs(wl, x, dev)
+    t = torch.bfloat16 if io == "bf16" else torch.float32
+    dZ_d = torch.from_numpy(dZ).to(dev).reshape(wl.B, wl.H, wl.T, wl.d).to(t).contiguous()
+    dWT_d = torch.from_numpy(dWT).to(dev).reshape(wl.B, wl.H, wl.d, wl.d)
+    runs = [ttt.linear_bwd(a["K"], a["Q"], a["V"], a["eta"], a["W0"], dZ_d, wl.chunk,
+                           eta_scalar=x["eta_scalar"], dW_T=dWT_d) for _ in range(3)]
+    torch.cuda.synchronize()
+    for r in runs[1:]:
+        assert all(torch.equal(u, v) for u, v in zip(runs[0], r))
