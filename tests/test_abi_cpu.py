@@ -271,14 +271,15 @@ def test_bwd_rejects_bad_arguments(kw, status):
 
 
 def test_bwd_workspace_size():
-    # chunk-start states (ceil(T/b) + 1 per slice), then, with bf16 I/O, fp32
-    # sums of dK and dQ; each piece rounded up to 256 bytes
+    # chunk-start states (ceil(T/b) + 1 per slice), then one fp32 plane of dK, of
+    # dQ and of deta per 16-row block (d/16 of each); each piece rounded up to 256
+    # bytes; the same for either I/O type
     B, H, T, d, b = 1, 2, 40, 64, 16
     up = lambda x: (x + 255) // 256 * 256
     states = up(B * H * (3 + 1) * d * d * 4)
-    sums = 2 * up(B * H * T * d * 4)
-    assert ttt.linear_bwd_workspace_bytes(B, H, T, d, b, 1) == states + sums
-    assert ttt.linear_bwd_workspace_bytes(B, H, T, d, b, 0) == states
+    planes = 2 * up(d // 16 * B * H * T * d * 4) + up(d // 16 * B * H * T * 4)
+    assert ttt.linear_bwd_workspace_bytes(B, H, T, d, b, 1) == states + planes
+    assert ttt.linear_bwd_workspace_bytes(B, H, T, d, b, 0) == states + planes
     assert ttt.linear_bwd_workspace_bytes(B, H, T, 48, b, 1) == 0
 
 
