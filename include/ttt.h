@@ -221,8 +221,9 @@ int ttt_linear_select_plan_varlen(int n_docs, int H, int total_T, int d, int chu
                                   int io_dtype, int plan);
 
 /* Bytes of workspace ttt_linear_bwd needs: the chunk-start states
- * (B*H*(ceil(T/chunk)+1)*d*d fp32) and, with bf16 I/O, fp32 sums of dK and dQ
- * (2*B*H*T*d fp32).  0 for an unsupported shape. */
+ * (B*H*(ceil(T/chunk)+1)*d*d fp32) and one fp32 plane of dK, dQ and deta per
+ * 16-row block of the state ((d/16)*B*H*T*(2d+1) fp32), each piece rounded up
+ * to 256 bytes; the same for either I/O type.  0 for an unsupported shape. */
 size_t ttt_linear_bwd_workspace_bytes(int B, int H, int T, int d, int chunk, int io_dtype);
 
 /* Backward pass (vector-Jacobian product) of ttt_linear_fwd: for the scalar
