@@ -39,7 +39,7 @@
 // eight partials, two values each: the Z values go to memory with b2 added, the
 // E values get b2 - V and are written back as the fp16 operands the next chunk
 // reads (E and -eta E); the thread that owns an output feature also keeps that
-// bias.  A second barrier publishes them.  K and Q of each chunk are staged once
+// bias and adds the chunk's step, which wave 0 forms as -eta E times ones.  A second barrier publishes them.  K and Q of each chunk are staged once
 // per workgroup in LDS as fp16 rows (two chunks ahead), and both the row operand
 // and the transposed K come from that tile.
 //
@@ -141,6 +141,7 @@ struct Lds {
     u32x2 tA2[kWaves][kUB * 64];        // per wave: A'
     u32x2 tE[kNB * 64];                 // -eta E (fp16), the transpose read's source layout
     u32x4 Ef[2 * 64];                   // E (fp16) as the A operand of the D product
+    float b2d[kD];                      // the chunk's b2 step, -sum_s eta_s E[o][s]
     f32x4 Ep[kWaves][kNB][64];          // per wave: W2 A_{c+1} - E diag(eta) (A_c^T A_{c+1} [+ 1])
     f32x4 Zp[kWaves][kNB][64];          // per wave: W2 A'_c  - E diag(eta) (U * (A_c^T A'_c [+ 1]))
 };
@@ -197,7 +198,6 @@ __global__ __launch_bounds__(64 * kWaves) void mlp_mfma_kernel(
     const int rout = 16 * rob + 4 * (rln >> 4) + 2 * rrp;   // first output feature
     f32x2 b2v = {0.f, 0.f};
     if (HAS_B2) b2v = *(const f32x2*)(b2_0 + (size_t)slice * kD + rout);
-    f32x2 eprev = {0.f, 0.f};                  // this pair of E_c (for the b2 step)
 
     // ---- staging: thread t < 256 carries granule t % 128 of K (t < 128) or Q,
     // threads 256..271 the eta of one token ----
@@ -334,7 +334,6 @@ __global__ __launch_bounds__(64 * kWaves) void mlp_mfma_kernel(
         const unsigned v = vnext;
         e.x += b2v.x - __uint_as_float(v << 16);
         e.y += b2v.y - __uint_as_float(v & 0xffff0000u);
-        eprev = e;
         publish_e(e, 0);
         vnext = v_load(1);
     }
@@ -449,6 +448,16 @@ __global__ __launch_bounds__(64 * kWaves) void mlp_mfma_kernel(
                 L.Zp[w][ob][lane] = mfma16h(tE[ob], smb, w2_partial(tA2f, ob));
                 L.Ep[w][ob][lane] = mfma16h(tE[ob], s3b, w2_partial(tAn, ob));
             }
+            if (HAS_B2 && w == 0) {
+                // the b2 step: -eta E summed over the chunk's tokens, as a product
+                // with ones (every token column of the result holds it)
+                const u32x2 ones = {0x3C003C00u, 0x3C003C00u};
+#pragma unroll
+                for (int ob = 0; ob < kNB; ++ob) {
+                    const f32x4 dl = mfma16h(tE[ob], ones, f32x4{0, 0, 0, 0});
+                    if (c == 0) *(f32x4*)&L.b2d[16 * ob + 4 * g] = dl;
+                }
+            }
         }
         // ---- state updates (this wave's units; needed from the next chunk on) ----
         {
@@ -485,19 +494,7 @@ __global__ __launch_bounds__(64 * kWaves) void mlp_mfma_kernel(
             const unsigned v = vnext;
             e.x += b2v.x - __uint_as_float(v << 16);
             e.y += b2v.y - __uint_as_float(v & 0xffff0000u);
-            if (HAS_B2) {
-                // b2 -= sum_s eta_s E_c[o][s]: the 16 tokens of an output pair sit in
-                // lanes 2 apart within 32 consecutive lanes
-                const float et = L.eta[sl][rtok];
-                f32x2 t = {et * eprev.x, et * eprev.y};
-#pragma unroll
-                for (int k = 2; k <= 16; k *= 2) {
-                    t.x += __shfl_xor(t.x, k);
-                    t.y += __shfl_xor(t.y, k);
-                }
-                b2v -= t;
-            }
-            eprev = e;
+            if (HAS_B2) b2v += *(const f32x2*)&L.b2d[rout];   // wave 0's sum over the tokens
             publish_e(e, sn);
             vnext = v_load(ci + 2);
         }
