@@ -371,7 +371,6 @@ __global__ __launch_bounds__(64 * kWaves) void mlp_mfma_kernel(
 
         // ---- D^T (t x u) = (E^T W2) * gelu'(H), scaled by -eta ----
         u32x2 DSb[kUB];
-        float db1[kUB];
 #pragma unroll
         for (int ub = 0; ub < kUB; ++ub) {
             // W2 with lanes = hidden unit u, slots = output features (transpose read)
@@ -386,7 +385,6 @@ __global__ __launch_bounds__(64 * kWaves) void mlp_mfma_kernel(
                                          w2t[2 * m + 1].y}, d);
             const f32x4 ds = -er * (d * G[ub]);
             DSb[ub] = pack_f16x4(ds);
-            db1[ub] = ds[0] + ds[1] + ds[2] + ds[3];
         }
         // ---- scores of K_c against Q_c (causal) and K_{c+1} (all); -eta rides on D ----
         u32x4 Kc[kNB / 2], Qf[kNB / 2], Kn[kNB / 2];
@@ -472,13 +470,12 @@ __global__ __launch_bounds__(64 * kWaves) void mlp_mfma_kernel(
 #pragma unroll
                 for (int ub = 0; ub < kUB; ++ub) W2o[ob][ub] = mfma16h(Ab[ub], tE[ob], W2o[ob][ub]);
             if (HAS_B1) {
+                // the b1 step, -eta D summed over the chunk's tokens: ones times
+                // the same operand the W1 update takes (every row holds the sum)
+                const u32x2 ones = {0x3C003C00u, 0x3C003C00u};
 #pragma unroll
-                for (int ub = 0; ub < kUB; ++ub) {
-                    float v = db1[ub];
-                    v += __shfl_xor(v, 16);
-                    v += __shfl_xor(v, 32);
-                    b1r[ub] += v;
-                }
+                for (int ub = 0; ub < kUB; ++ub)
+                    b1r[ub] += mfma16h(ones, DSb[ub], f32x4{0, 0, 0, 0})[0];
             }
         }
         __syncthreads();
