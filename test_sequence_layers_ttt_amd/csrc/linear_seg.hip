@@ -17,11 +17,15 @@
 // replay), but no chain is longer than the longest segment.
 //
 // A workgroup is one (slice, segment) on one compute unit: four waves, wave w
-// owning state rows 16w .. 16w+15, sharing each chunk's K (and Q) tile through a
-// ring of swizzled LDS tiles, as the many-head kernel does (linear_coop.hip): one
-// unit's vector-memory path, not the matrix cores, bounds a chunk step, and the
-// shared tile cuts a chunk's fetch from 4 (K, Q) + 1 (V) KB per row block to
-// 4 KB per head plus 1 KB per row block.
+// owning state rows 16w .. 16w+15, sharing each chunk's K, Q and V through a
+// ring of LDS tiles.  One unit's vector-memory path, not the matrix cores, bounds
+// a chunk step, and its cost follows the cache lines an instruction touches more
+// than the bytes: every global access is a contiguous piece per wave (K and Q in
+// 16-byte granules, V and Z in 8-byte pieces, 512 bytes per wave), never the
+// 16-row stripe of one wave's features.  Z goes out through LDS one group of
+// chunks later, after the barrier that makes all four waves' parts visible.
+// Per-token eta is read per lane (the four tokens of its rows, one 16-byte load
+// with few distinct lines); staging it through LDS measured slower.
 #include <stdint.h>
 
 #include <type_traits>
@@ -37,8 +41,9 @@ namespace {
 enum { kSegScan = 0, kSegMap = 1 };
 enum { kSegEtaScalar = 0, kSegEtaToken = 1, kSegEtaToken4 = 2 };
 
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+
 constexpr int kSegD = 64;
-constexpr int kSegWaves = kSegD / 16;
 
 template <typename F, int... I>
 __device__ __forceinline__ void seg_unroll(F&& f, std::integer_sequence<int, I...>)
@@ -88,6 +93,25 @@ constexpr int kSegGroup = 4;
 constexpr int kSegAhead = 2 * kSegGroup;
 constexpr int kSegSlots = 2 * kSegAhead;
 
+// One chunk's inputs in LDS.  K and Q as swizzled 16-byte granules (row operand
+// and transposed reads conflict-free within a 16-lane group).  V as 8-byte units
+// (four features), unit u of token r at r * 16 + (u ^ seg_vswz(r)): the 16 tokens
+// a lane group reads at one unit then fall on distinct banks.
+struct SegTile {
+    u32x4 g[2][16 * (kSegD / 8)];
+    u32x2 v[16 * 16];
+};
+
+__device__ __forceinline__ int seg_vswz(int r) { return (r >> 1) & 7; }
+
+// Z of a group of chunks waits in LDS (same unit layout as V) until the barrier
+// that ends the group; two groups alternate.
+typedef u32x2 SegZStage[2 * kSegGroup][16 * 16];
+
+// A raw buffer store at or past the resource's size is dropped by the memory unit.
+constexpr int kSegBufferFlags = 0x00020000;   // dword 3 of a gfx9 buffer resource: raw 32-bit data
+constexpr int kSegDropOffset = 0x7ffffff0;
+
 // One (slice, segment) on a workgroup of four waves.
 //   SCAN: from the segment's start state (W0 for segment 0, else W_start), Z
 //         written; the end state goes to W_out for the last segment, to
@@ -96,7 +120,7 @@ constexpr int kSegSlots = 2 * kSegAhead;
 //         (-> A), two chains per wave sharing its operands.
 template <int MODE, int ETA>
 __device__ __forceinline__ void seg_body(
-    KQTile16<kSegD>* L, const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
+    SegTile* L, SegZStage& Zs, const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
     const float* W0, uint16_t* __restrict__ Z, float* W_out, void* ws, int BH, int T,
     const SegPlan& plan, int slice, int seg)
@@ -122,29 +146,34 @@ __device__ __forceinline__ void seg_body(
     const size_t dd = (size_t)D * D;
     const size_t sw = ((size_t)slice * plan.S + seg) * dd;   // this segment's [D, D] block
 
-    // this thread's granule of each staged tile: K (threads 0..127) or Q
+    // Every wave issues the same loads (a wave-dependent load count would make the
+    // compiler wait on the prefetch ring early).  Threads 0..127 load a 16-byte
+    // granule of K, threads 128..255 one of Q (scan) or of V (map: no Q); a scan
+    // also loads V as one 8-byte piece per thread.
+    constexpr bool kV8 = MODE == kSegScan;
     const int which = tid / (16 * G);
     const int grow = (tid / G) & 15;
     const int ggr = tid % G;
     const int lpos = grow * G + (ggr ^ tile16_swizzle<D>(grow));
-    const bool loads = MODE == kSegScan || which == 0;   // the map reads no Q
     auto chunk_base = [&](int ch) {   // first token of chunk ch (clamped)
         const int cc = ch < nch ? ch : nch - 1;
         return tok0 + (size_t)16 * cc;
     };
+    // thread t's 8-byte piece of a V (or Z) tile: token t / 16, unit t % 16
+    const int vrow = tid >> 4;
+    const int vpos = vrow * 16 + ((tid & 15) ^ seg_vswz(vrow));
+    // this lane's unit of a V (or Z) tile: token c, features out0 + 4g .. out0 + 4g + 3
+    const int opos = c * 16 + ((4 * wave + g) ^ seg_vswz(c));
     auto gload = [&](u32x4& r, int ch) {
-        if (loads) r = *(const u32x4*)((which ? Q : K) + chunk_base(ch) * D + (grow * D + 8 * ggr));
+        const uint16_t* src = which ? (MODE == kSegMap ? V : Q) : K;
+        r = *(const u32x4*)(src + chunk_base(ch) * D + (grow * D + 8 * ggr));
     };
-    auto gstore = [&](KQTile16<D>& t, const u32x4& r) {
-        if (loads) t.g[which][lpos] = r;
-    };
-    auto vload = [&](int ch) {
-        return *(const u32x2*)(V + chunk_base(ch) * D + (c * D + out0 + 4 * g));
-    };
+    auto vload = [&](int ch) { return *(const u32x2*)(V + chunk_base(ch) * D + 4 * tid); };
+    // eta of tokens 4g .. 4g + 3 (the rows of this lane's E tile)
     auto eload = [&](int ch) {
-        if (ETA == kSegEtaToken4) {
+        if constexpr (ETA == kSegEtaToken4) {
             return *(const f32x4*)(eta + chunk_base(ch) + 4 * g);
-        } else if (ETA == kSegEtaToken) {
+        } else if constexpr (ETA == kSegEtaToken) {
             f32x4 e;
 #pragma unroll
             for (int r = 0; r < 4; ++r) e[r] = eta[chunk_base(ch) + 4 * g + r];
@@ -152,6 +181,23 @@ __device__ __forceinline__ void seg_body(
         } else {
             return f32x4{eta_scalar, eta_scalar, eta_scalar, eta_scalar};
         }
+    };
+    auto stage = [&](SegTile& t, const u32x4& r, const u32x2& v) {
+        if (MODE == kSegMap && which) {   // a V granule: two 8-byte units of row grow
+            t.v[grow * 16 + ((2 * ggr) ^ seg_vswz(grow))] = u32x2{r.x, r.y};
+            t.v[grow * 16 + ((2 * ggr + 1) ^ seg_vswz(grow))] = u32x2{r.z, r.w};
+        } else {
+            t.g[which][lpos] = r;
+        }
+        if constexpr (kV8) t.v[vpos] = v;
+    };
+    auto vread = [&](const SegTile& t) { return t.v[opos]; };
+    // Z of chunk ch as thread tid's piece, dropped for ch < 0
+    const auto rz = __builtin_amdgcn_make_buffer_rsrc(Z + tok0 * D, 0, nch * 16 * D * 2,
+                                                      kSegBufferFlags);
+    auto zstore = [&](const u32x2& v, int ch) {
+        const int off = ch >= 0 ? (ch * 16 * D + 4 * tid) * 2 : kSegDropOffset;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), rz, off, 0, 0);
     };
     auto row_operand = [&](const u32x4* t, u32x4 (&op)[NM]) {
 #pragma unroll
@@ -183,27 +229,31 @@ __device__ __forceinline__ void seg_body(
 #pragma unroll
         for (int m = 0; m < NM; ++m) Mf[r][m] = pack_bf16x8(M[r][2 * m], M[r][2 * m + 1]);
     const u32x2 I16 = identity_b16(lane);
-    // -V of chunk data for chain r (the identity chain has no V)
+    // -V of a chunk for chain r (the identity chain has no V)
     auto vneg_of = [&](u32x2 v, int r) {
         return r == 0 ? v ^ u32x2{0x80008000u, 0x80008000u} : u32x2{0u, 0u};
     };
 
     // chunk X lives in LDS slot X % kSlots; tiles of chunks 0 .. P-1 are stored up
     // front, and during chunk ch the tile of chunk ch + P is stored and the
-    // granule of chunk ch + 2P loaded (into the register slot it came from)
+    // pieces of chunk ch + 2P loaded (into the register slots they came from).
+    // re[] holds eta of chunks ch .. ch + P - 1.
     u32x4 rg[P];
-    u32x2 rv[P];
+    u32x2 rv[kV8 ? P : 1] = {};
     f32x4 re[P];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         gload(rg[p], p);
-        rv[p] = vload(p);
-        re[p] = eload(p);
+        if constexpr (kV8) rv[p] = vload(p);
     }
+    // the loads that stay in flight into the loop, in the order a chunk step issues
+    // them, so that the loop's waits count them as in the steady state
 #pragma unroll
     for (int p = 0; p < P; ++p) {
-        gstore(L[p], rg[p]);
+        stage(L[p], rg[p], rv[kV8 ? p : 0]);
         gload(rg[p], P + p);
+        if constexpr (kV8) rv[p] = vload(P + p);
+        re[p] = eload(p);
     }
     __syncthreads();
 
@@ -215,7 +265,7 @@ __device__ __forceinline__ void seg_body(
     f32x4 Et[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-        Et[r] = mfma16(vneg_of(rv[0], r), I16, f32x4{0, 0, 0, 0});
+        Et[r] = mfma16(vneg_of(vread(L[0]), r), I16, f32x4{0, 0, 0, 0});
 #pragma unroll
         for (int m = 0; m < NM; ++m) Et[r] = mfma32(kb[0][m], Mf[r][m], Et[r]);
     }
@@ -227,8 +277,17 @@ __device__ __forceinline__ void seg_body(
     auto step = [&](int ch, auto kc_) {
         constexpr int k = decltype(kc_)::value;
         constexpr int p = k % P;
-        if (ch + P < nch) gstore(L[(k + P) % kSlots], rg[p]);
+        constexpr int j = k % kGroup;              // chunk within its group
+        constexpr int zb = (k / kGroup) & 1;       // group parity (c0 is a multiple of 16)
+        // staged unconditionally: past the end the slot receives a re-read of the last
+        // chunk (read only by the unused lookahead), and a conditional use would let
+        // the compiler sink the prefetch loads into the branch
+        stage(L[(k + P) % kSlots], rg[p], rv[kV8 ? p : 0]);
         gload(rg[p], ch + 2 * P);
+        if constexpr (kV8) rv[p] = vload(ch + 2 * P);
+        // the previous group's Z, complete since the last barrier
+        u32x2 zprev = {0u, 0u};
+        if constexpr (MODE == kSegScan) zprev = Zs[(zb ^ 1) * kGroup + j][vpos];
 
         const u32x4* Kc = L[k].g[0];
         constexpr int pe = p & 1;
@@ -267,7 +326,7 @@ __device__ __forceinline__ void seg_body(
                 f32x4 Pt = {0, 0, 0, 0};
 #pragma unroll
                 for (int m = 0; m < NM; ++m) Pt = mfma32(kn[m], Mf[r][m], Pt);
-                const u32x2 vneg = vneg_of(rv[(p + 1) % P], r);
+                const u32x2 vneg = vneg_of(vread(L[(k + 1) % kSlots]), r);
                 Et[r] = mfma32(u32x4{vneg.x, vneg.y, Gb.x, Gb.y}, IF[r], Pt);
             }
         }
@@ -295,17 +354,16 @@ __device__ __forceinline__ void seg_body(
             smz.z = sb.x;
             smz.w = sb.y;
             Zt = mfma32(IF[0], smz, Zt);
-            uint16_t* zb = Z + (tok0 + (size_t)16 * ch) * D;
-            *(u32x2*)(zb + (c * D + out0 + 4 * g)) = pack_bf16x4(Zt);
+            Zs[zb * kGroup + j][opos] = pack_bf16x4(Zt);
+            zstore(zprev, ch - kGroup);
         }
 #pragma unroll
         for (int r = 0; r < RB; ++r)
 #pragma unroll
             for (int m = 0; m < NM; ++m) Mf[r][m] = pack_bf16x8(M[r][2 * m], M[r][2 * m + 1]);
         row_operand(L[(k + 2) % kSlots].g[0], kc);   // K_{c+2} (stale past the end)
-        rv[p] = vload(ch + P);
         re[p] = eload(ch + P);
-        if (p % kGroup == kGroup - 1) __syncthreads();
+        if (j == kGroup - 1) __syncthreads();
     };
 
     int c0 = 0;
@@ -314,6 +372,16 @@ __device__ __forceinline__ void seg_body(
     seg_unroll([&](auto k) {
         if (c0 + k < nch) step(c0 + k, k);
     }, std::make_integer_sequence<int, kSlots - 1>{});
+
+    if constexpr (MODE == kSegScan) {
+        // Z of the last group and the rest of the group before it
+        __syncthreads();
+        const int gl = (nch - 1) / kGroup, m = nch - gl * kGroup;
+        if (gl > 0)
+            for (int jj = m; jj < kGroup; ++jj)
+                zstore(Zs[((gl - 1) & 1) * kGroup + jj][vpos], (gl - 1) * kGroup + jj);
+        for (int jj = 0; jj < m; ++jj) zstore(Zs[(gl & 1) * kGroup + jj][vpos], gl * kGroup + jj);
+    }
 
     // end states
     float* dst[RB];
@@ -345,12 +413,15 @@ __global__ __launch_bounds__(256) void linear_seg_pass1_kernel(
     const float* W0, uint16_t* __restrict__ Z, float* W_out, void* ws, int BH, int T,
     SegPlan plan)
 {
-    __shared__ KQTile16<kSegD> L[kSegSlots];
+    __shared__ SegTile L[kSegSlots];
+    __shared__ SegZStage Zs;
     const int slice = (int)blockIdx.x / plan.S, seg = (int)blockIdx.x % plan.S;
     if (seg == 0)
-        seg_body<kSegScan, ETA>(L, K, Q, V, eta, eta_scalar, W0, Z, W_out, ws, BH, T, plan, slice, 0);
+        seg_body<kSegScan, ETA>(L, Zs, K, Q, V, eta, eta_scalar, W0, Z, W_out, ws, BH, T, plan,
+                                slice, 0);
     else
-        seg_body<kSegMap, ETA>(L, K, Q, V, eta, eta_scalar, W0, Z, W_out, ws, BH, T, plan, slice, seg);
+        seg_body<kSegMap, ETA>(L, Zs, K, Q, V, eta, eta_scalar, W0, Z, W_out, ws, BH, T, plan,
+                               slice, seg);
 }
 
 template <int ETA>
@@ -360,9 +431,11 @@ __global__ __launch_bounds__(256) void linear_seg_pass2_kernel(
     const float* W0, uint16_t* __restrict__ Z, float* W_out, void* ws, int BH, int T,
     SegPlan plan)
 {
-    __shared__ KQTile16<kSegD> L[kSegSlots];
+    __shared__ SegTile L[kSegSlots];
+    __shared__ SegZStage Zs;
     const int slice = (int)blockIdx.x / (plan.S - 1), seg = 1 + (int)blockIdx.x % (plan.S - 1);
-    seg_body<kSegScan, ETA>(L, K, Q, V, eta, eta_scalar, W0, Z, W_out, ws, BH, T, plan, slice, seg);
+    seg_body<kSegScan, ETA>(L, Zs, K, Q, V, eta, eta_scalar, W0, Z, W_out, ws, BH, T, plan, slice,
+                            seg);
 }
 
 // W_start,k+1 = W_B,k + W_start,k A_k for k = 1 .. S-2 (W_start,1 = the end of
@@ -457,8 +530,10 @@ hipError_t launch_seg_eta(const LinearArgs& a, hipStream_t s)
 
 bool linear_seg_supported(int BH, int T, int d, int chunk, int bf16)
 {
+    // Z of one segment is addressed by a 32-bit byte offset
     return bf16 && d == kSegD && chunk == 16 && T % 16 == 0 && T >= 2048 && BH >= 1 &&
-           (long)BH * 8 <= kSegUnits && (long long)BH * T * d * 2 <= 0x7fffffffffffLL;
+           (long)BH * 8 <= kSegUnits && (long long)T * d * 2 < 0x7fffffffLL &&
+           (long long)BH * T * d * 2 <= 0x7fffffffffffLL;
 }
 
 size_t linear_seg_workspace(int BH, int T, int d)
@@ -470,9 +545,8 @@ size_t linear_seg_workspace(int BH, int T, int d)
 
 hipError_t launch_linear_seg(const LinearArgs& a, hipStream_t s)
 {
-    const bool eta4 = a.eta && reinterpret_cast<uintptr_t>(a.eta) % 16 == 0;
     if (!a.eta) return launch_seg_eta<kSegEtaScalar>(a, s);
-    if (eta4) return launch_seg_eta<kSegEtaToken4>(a, s);
+    if (reinterpret_cast<uintptr_t>(a.eta) % 16 == 0) return launch_seg_eta<kSegEtaToken4>(a, s);
     return launch_seg_eta<kSegEtaToken>(a, s);
 }
 
