@@ -15,10 +15,23 @@
 // fetches each tile once -- one coalesced 16-byte granule per thread, through a
 // register ring -- into a ring of swizzled LDS tiles (below), and
 // every wave reads its operands from there (row reads; the transpose read gives K
-// with the feature in the lanes for the state update).  V and eta are loaded per
-// wave.  The parts of one head run on one XCD, so a tile fetched by one part is
-// served to the other from that XCD's L2 (the HBM traffic stays one fetch per
-// tile).
+// with the feature in the lanes for the state update).  The parts of one head run
+// on one XCD, so a tile fetched by one part is served to the other from that
+// XCD's L2 (the HBM traffic stays one fetch per tile).
+//
+// A compute unit's vector-memory path pays per cache line an instruction touches
+// more than per byte, so with four waves at d = 64 V and Z also move as contiguous
+// pieces: the workgroup's
+// feature stripe of a chunk (16 tokens x 16 WPG features) is loaded as one 8-byte
+// piece per thread into the LDS tile, and Z leaves through an LDS stage one group
+// of chunks later, after the barrier that makes every wave's part visible, one
+// 8-byte piece per thread (a range-checked buffer store drops rows past T).  Each
+// wave reads its 16 x 16 block of V from LDS.  eta stays a per-lane load (the
+// four tokens of the lane's rows).  Elsewhere each wave loads its V block and
+// stores its Z block itself: at d = 128 the extra LDS and registers do not fit
+// beside the K and Q rings, and two-wave workgroups at d = 64 (a 64-byte stripe
+// per token) measured slower staged (8x12 heads, T = 2048: 37.5 us against 36.3;
+// four-wave workgroups at 64x12 heads, T = 1024: 94.0 against 99.7).
 //
 // Tiles are staged P = 2 kGroup chunks ahead into a ring of 2P LDS slots, with
 // one barrier per kGroup chunks: a slot is rewritten only once every wave has
@@ -48,6 +61,22 @@ __device__ __forceinline__ void unroll_seq(F&& f, std::integer_sequence<int, I..
 }
 constexpr long kComputeUnits = 256;   // MI355X
 
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+
+// K and Q as swizzled 16-byte granules; V as 8-byte units (four features) of the
+// workgroup's stripe, unit u of token r at r U + (u ^ coop_vswz(r)) with U = 4 WPG
+// units per token: the 16 tokens a lane group reads at one unit fall on distinct
+// banks.
+template <int D, int WPG>
+struct CoopTile {
+    u32x4 g[2][16 * (D / 8)];
+    u32x2 v[D == 64 && WPG >= 4 ? 16 * 4 * WPG : 1];
+};
+
+__device__ __forceinline__ int coop_vswz(int r) { return (r >> 1) & 7; }
+
+constexpr int kCoopBufferFlags = 0x00020000;   // dword 3 of a gfx9 buffer resource: raw 32-bit data
+
 template <int D, int WPG, int ETA, bool FULL>
 __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
@@ -66,7 +95,10 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
     constexpr int kGroup = WPG >= 8 ? 2 : 4;
     constexpr int P = 2 * kGroup;   // chunks whose granules a thread holds in registers
     constexpr int kSlots = 2 * P;   // > P + kGroup: chunks ch - kGroup .. ch + 2 stay
-    __shared__ KQTile16<D> L[kSlots];
+    constexpr bool SV = D == 64 && WPG >= 4;   // V and Z staged through LDS
+    constexpr int U = 4 * WPG;      // 8-byte units of the stripe per token
+    __shared__ CoopTile<D, WPG> L[kSlots];
+    __shared__ u32x2 Zs[SV ? 2 * kGroup : 1][SV ? 16 * U : 1];   // Z of two groups of chunks
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -83,6 +115,12 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
     const size_t tok0 = (size_t)slice * T;
     const int nch = (T + 15) / 16;
     const int out0 = 16 * (part * WPG + wave);
+    const int sbase = 16 * WPG * part;   // first feature of the workgroup's stripe
+    // thread tid's piece of a stripe tile: token vrow, unit vunit; this lane's
+    // unit of one (token c, features out0 + 4g .. + 3)
+    const int vrow = tid / U, vunit = tid % U;
+    const int vpos = vrow * U + (vunit ^ coop_vswz(vrow));
+    const int opos = c * U + ((4 * wave + g) ^ coop_vswz(c));
     // token of row r of chunk ch, clamped into the sequence (a clamped row is a
     // re-read; its token gets eta = 0 and no store)
     auto tok = [&](int ch, int r) {
@@ -119,13 +157,25 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
         for (int i = 0; i < GPT; ++i)
             r[i] = *(const u32x4*)((which[i] ? Q : K) + base + (row_in(ch, grow[i]) * D + 8 * ggr[i]));
     };
-    auto gstore = [&](KQTile16<D>& t, const u32x4 (&r)[GPT]) {
+    auto stage = [&](CoopTile<D, WPG>& t, const u32x4 (&r)[GPT], const u32x2& v) {
 #pragma unroll
         for (int i = 0; i < GPT; ++i) t.g[which[i]][lpos[i]] = r[i];
+        if constexpr (SV) t.v[vpos] = v;
     };
+    // SV: thread tid's piece of the stripe; else this lane's unit
     auto vload = [&](int ch) {
         const uint16_t* b = V + chunk_base(ch) * D;
-        return *(const u32x2*)(b + (row_in(ch, c) * D + out0 + 4 * g));
+        if constexpr (SV) return *(const u32x2*)(b + (row_in(ch, vrow) * D + sbase + 4 * vunit));
+        else return *(const u32x2*)(b + (row_in(ch, c) * D + out0 + 4 * g));
+    };
+    // Z of chunk ch as thread tid's piece: rows past T (and chunks ch < 0) fall
+    // outside the resource and are dropped
+    auto zstore = [&](const u32x2& v, int ch) {
+        const int rows = ch < 0 ? 0 : min(16, T - 16 * ch);
+        const auto rz = __builtin_amdgcn_make_buffer_rsrc(
+            Z + (tok0 + (size_t)16 * (ch < 0 ? 0 : ch)) * D, 0, rows * D * 2, kCoopBufferFlags);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), rz,
+                                              (vrow * D + sbase + 4 * vunit) * 2, 0, 0);
     };
     auto eload = [&](int ch) {
         if (ETA == kCoopEtaToken4) {
@@ -162,29 +212,55 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
 
     // chunk X lives in LDS slot X % kSlots.  Tiles of chunks 0 .. P-1 are
     // stored up front; during chunk ch the tile of chunk ch + P is stored and the
-    // granule of chunk ch + 2P loaded (into the register slot it came from).
+    // pieces of chunk ch + 2P loaded (into the register slots they came from).
+    // re[] holds eta of chunks ch .. ch + P - 1, and so does rv[] when V is not
+    // staged.
     u32x4 rg[P][GPT];
     u32x2 rv[P];
     f32x4 re[P];
+    if constexpr (SV) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-        gload(rg[p], p);
-        rv[p] = vload(p);
-        re[p] = eload(p);
-    }
+        for (int p = 0; p < P; ++p) {
+            gload(rg[p], p);
+            rv[p] = vload(p);
+        }
+        // the loads that stay in flight into the loop, in the order a chunk step
+        // issues them, so that the loop's waits count them as in the steady state
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-        gstore(L[p], rg[p]);
-        gload(rg[p], P + p);
+        for (int p = 0; p < P; ++p) {
+            stage(L[p], rg[p], rv[p]);
+            gload(rg[p], P + p);
+            rv[p] = vload(P + p);
+            re[p] = eload(p);
+        }
+    } else {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            gload(rg[p], p);
+            rv[p] = vload(p);
+            re[p] = eload(p);
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            stage(L[p], rg[p], rv[p]);
+            gload(rg[p], P + p);
+        }
     }
     __syncthreads();
+    // -V of chunk ch + 1 for the lookahead, ch at ring position k
+    auto vneg_next = [&](auto kc_) {
+        constexpr int k = decltype(kc_)::value;
+        if constexpr (SV) return L[(k + 1) % kSlots].v[opos] ^ u32x2{0x80008000u, 0x80008000u};
+        else return rv[(k % P + 1) % P] ^ u32x2{0x80008000u, 0x80008000u};
+    };
 
     // E_0 = K_0 W_0^T - V_0 directly.  kb[ch & 1] holds K_ch as row operand; the
     // other set holds K_{ch+1}.
     u32x4 kb[2][NM];
     row_operand(L[0].g[0], kb[0]);
     row_operand(L[1].g[0], kb[1]);
-    f32x4 Et = mfma16(rv[0] ^ u32x2{0x80008000u, 0x80008000u}, I16, f32x4{0, 0, 0, 0});
+    const u32x2 v0 = SV ? L[0].v[opos] : rv[0];
+    f32x4 Et = mfma16(v0 ^ u32x2{0x80008000u, 0x80008000u}, I16, f32x4{0, 0, 0, 0});
 #pragma unroll
     for (int m = 0; m < NM; ++m) Et = mfma32(kb[0][m], Mf[m], Et);
 
@@ -199,9 +275,20 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
     auto step = [&](int ch, auto kc_) {
         constexpr int k = decltype(kc_)::value;
         constexpr int p = k % P;
-        // stage chunk ch + P, refill its register slot with chunk ch + 2P
-        if (ch + P < nch) gstore(L[(k + P) % kSlots], rg[p]);
+        constexpr int j = k % kGroup;              // chunk within its group
+        constexpr int zb = (k / kGroup) & 1;       // group parity (kSlots is a multiple of 2 kGroup)
+        // stage chunk ch + P, refill its register slots with chunk ch + 2P.  With V
+        // staged this is unconditional: past the end the slot receives a re-read of
+        // the last chunk (read only by the unused lookahead), and a conditional use
+        // would let the compiler sink the prefetch loads into the branch.
+        // Otherwise the conditional form, which keeps d = 128 under the register
+        // limit.
+        if (SV || ch + P < nch) stage(L[(k + P) % kSlots], rg[p], rv[p]);
         gload(rg[p], ch + 2 * P);
+        if constexpr (SV) rv[p] = vload(ch + 2 * P);
+        // the previous group's Z, complete since the last barrier
+        u32x2 zprev = {0u, 0u};
+        if constexpr (SV) zprev = Zs[(zb ^ 1) * kGroup + j][vpos];
 
         constexpr int sl = k;
         const u32x4* Kc = L[sl].g[0];
@@ -246,7 +333,7 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
             f32x4 Pt = {0, 0, 0, 0};
 #pragma unroll
             for (int m = 0; m < NM; ++m) Pt = mfma32(kn[m], Mf[m], Pt);
-            const u32x2 vneg = rv[(p + 1) % P] ^ u32x2{0x80008000u, 0x80008000u};
+            const u32x2 vneg = vneg_next(kc_);
             Et = mfma32(u32x4{vneg.x, vneg.y, Gb.x, Gb.y}, IF, Pt);
         }
         // W_{c+1} = W_c + F_c^T K_c: [0 | K_c^T] [I ; F_c]
@@ -270,17 +357,20 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
             smz.w = sb.y;
             Zt = mfma32(IF, smz, Zt);
         }
-        if (FULL || 16 * ch + c < T) {
-            uint16_t* zb = Z + (tok0 + (size_t)16 * ch) * D;
-            *(u32x2*)(zb + (c * D + out0 + 4 * g)) = pack_bf16x4(Zt);
+        if constexpr (SV) {
+            Zs[zb * kGroup + j][opos] = pack_bf16x4(Zt);
+            zstore(zprev, ch - kGroup);
+        } else if (FULL || 16 * ch + c < T) {
+            uint16_t* zp = Z + (tok0 + (size_t)16 * ch) * D;
+            *(u32x2*)(zp + (c * D + out0 + 4 * g)) = pack_bf16x4(Zt);
         }
 #pragma unroll
         for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
         // K_{c+2} into the set K_c leaves (stale, unused, past the end)
         row_operand(L[(k + 2) % kSlots].g[0], kc);
-        rv[p] = vload(ch + P);
+        if constexpr (!SV) rv[p] = vload(ch + P);
         re[p] = eload(ch + P);
-        if (p % kGroup == kGroup - 1) __syncthreads();
+        if (j == kGroup - 1) __syncthreads();
     };
 
     int c0 = 0;
@@ -289,6 +379,15 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
     unroll_seq([&](auto k) {
         if (c0 + k < nch) step(c0 + k, k);
     }, std::make_integer_sequence<int, kSlots - 1>{});
+
+    if constexpr (SV) {   // Z of the last group and the rest of the group before it
+        __syncthreads();
+        const int gl = (nch - 1) / kGroup, m = nch - gl * kGroup;
+        if (gl > 0)
+            for (int jj = m; jj < kGroup; ++jj)
+                zstore(Zs[((gl - 1) & 1) * kGroup + jj][vpos], (gl - 1) * kGroup + jj);
+        for (int jj = 0; jj < m; ++jj) zstore(Zs[(gl & 1) * kGroup + jj][vpos], gl * kGroup + jj);
+    }
 
     float* w = W_out + (size_t)slice * D * D + (size_t)(out0 + c) * D;
 #pragma unroll
