@@ -6,10 +6,11 @@
 // P_c = K_c^T diag(eta) K_c, B_c = V_c^T diag(eta) K_c (PaperTrace "5 · TestingTime
 // 训练与长上下文" §1.1/§2.3; the dual form of diosapp "Test-Time Training (TTT)
 // guide" §3 inside a chunk), so the end state of segment k is W_B,k + W_start,k A_k,
-// where (W_B,k, A_k) is the scan of the segment from zero with V and from the
-// identity without V.  Three launches:
+// where A_k is the product of the segment's (I - P_c) and W_B,k its end state
+// from zero.  Three launches:
 //   pass 1   segment 0 scans from W0 (Z written, end state kept); segments
-//            1 .. S-1 form their maps (W_B, A) -- two chains per wave, no Z;
+//            1 .. S-1 form their maps (W_B, A), reading their chunks backwards:
+//            one chain per wave (A^T) and W_B accumulated beside it, no Z;
 //   combine  W_start,1 = end of segment 0, W_start,k+1 = W_B,k + W_start,k A_k;
 //   pass 2   segments 1 .. S-1 scan again from W_start,k (Z written; the last
 //            one's end state is W_T).
@@ -116,8 +117,14 @@ constexpr int kSegDropOffset = 0x7ffffff0;
 //   SCAN: from the segment's start state (W0 for segment 0, else W_start), Z
 //         written; the end state goes to W_out for the last segment, to
 //         W_start[0] for segment 0.
-//   MAP:  the scans from zero with V (-> W_B) and from the identity without V
-//         (-> A), two chains per wave sharing its operands.
+//   MAP:  the segment's chunks in reverse order.  P_c is symmetric, so the
+//         suffix products R_c = (I - P_c) R_{c+1} (R_{n+1} = I, R_1 = A) satisfy
+//         R_c^T = R_{c+1}^T (I - P_c): the scan recurrence without V, run on the
+//         rows of R^T from the identity.  Beside it, with no feedback into the
+//         chain, W_B = sum_c B_c R_{c+1} = sum_c V_c^T diag(eta) (K_c R_{c+1}),
+//         K_c R_{c+1} being the chain's own E for chunk c.  Both leave transposed
+//         back through LDS.  Reading the segment backwards also means its first
+//         chunks are the last ones pass 1 reads, the first ones pass 2 replays.
 template <int MODE, int ETA>
 __device__ __forceinline__ void seg_body(
     SegTile* L, SegZStage& Zs, const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
@@ -125,11 +132,11 @@ __device__ __forceinline__ void seg_body(
     const float* W0, uint16_t* __restrict__ Z, float* W_out, void* ws, int BH, int T,
     const SegPlan& plan, int slice, int seg)
 {
+    constexpr bool MAP = MODE == kSegMap;
     constexpr int D = kSegD;
     constexpr int NB = D / 16;
     constexpr int NM = D / 32;
     constexpr int G = D / 8;           // 16-byte granules per row
-    constexpr int RB = MODE == kSegMap ? 2 : 1;
     constexpr int kGroup = kSegGroup;
     constexpr int P = kSegAhead;
     constexpr int kSlots = kSegSlots;
@@ -148,16 +155,18 @@ __device__ __forceinline__ void seg_body(
 
     // Every wave issues the same loads (a wave-dependent load count would make the
     // compiler wait on the prefetch ring early).  Threads 0..127 load a 16-byte
-    // granule of K, threads 128..255 one of Q (scan) or of V (map: no Q); a scan
-    // also loads V as one 8-byte piece per thread.
-    constexpr bool kV8 = MODE == kSegScan;
+    // granule of K, threads 128..255 one of Q (scan) or of V (map), into the tile's
+    // second granule array; a scan also loads V as one 8-byte piece per thread.
+    constexpr bool kV8 = !MAP;
     const int which = tid / (16 * G);
     const int grow = (tid / G) & 15;
     const int ggr = tid % G;
     const int lpos = grow * G + (ggr ^ tile16_swizzle<D>(grow));
-    auto chunk_base = [&](int ch) {   // first token of chunk ch (clamped)
+    // first token of the chunk that step ch processes (steps past the end re-read
+    // the last one)
+    auto chunk_base = [&](int ch) {
         const int cc = ch < nch ? ch : nch - 1;
-        return tok0 + (size_t)16 * cc;
+        return tok0 + (size_t)16 * (MAP ? nch - 1 - cc : cc);
     };
     // thread t's 8-byte piece of a V (or Z) tile: token t / 16, unit t % 16
     const int vrow = tid >> 4;
@@ -165,7 +174,7 @@ __device__ __forceinline__ void seg_body(
     // this lane's unit of a V (or Z) tile: token c, features out0 + 4g .. out0 + 4g + 3
     const int opos = c * 16 + ((4 * wave + g) ^ seg_vswz(c));
     auto gload = [&](u32x4& r, int ch) {
-        const uint16_t* src = which ? (MODE == kSegMap ? V : Q) : K;
+        const uint16_t* src = which ? (MAP ? V : Q) : K;
         r = *(const u32x4*)(src + chunk_base(ch) * D + (grow * D + 8 * ggr));
     };
     auto vload = [&](int ch) { return *(const u32x2*)(V + chunk_base(ch) * D + 4 * tid); };
@@ -183,15 +192,14 @@ __device__ __forceinline__ void seg_body(
         }
     };
     auto stage = [&](SegTile& t, const u32x4& r, const u32x2& v) {
-        if (MODE == kSegMap && which) {   // a V granule: two 8-byte units of row grow
-            t.v[grow * 16 + ((2 * ggr) ^ seg_vswz(grow))] = u32x2{r.x, r.y};
-            t.v[grow * 16 + ((2 * ggr + 1) ^ seg_vswz(grow))] = u32x2{r.z, r.w};
-        } else {
-            t.g[which][lpos] = r;
-        }
+        t.g[which][lpos] = r;
         if constexpr (kV8) t.v[vpos] = v;
     };
-    auto vread = [&](const SegTile& t) { return t.v[opos]; };
+    // -V of the chunk in slot t for the scan's E (the map's chain has no V)
+    auto vneg = [&](const SegTile& t) {
+        if constexpr (MAP) return u32x2{0u, 0u};
+        else return t.v[opos] ^ u32x2{0x80008000u, 0x80008000u};
+    };
     // Z of chunk ch as thread tid's piece, dropped for ch < 0
     const auto rz = __builtin_amdgcn_make_buffer_rsrc(Z + tok0 * D, 0, nch * 16 * D * 2,
                                                       kSegBufferFlags);
@@ -203,41 +211,54 @@ __device__ __forceinline__ void seg_body(
 #pragma unroll
         for (int m = 0; m < NM; ++m) op[m] = t[c * G + ((4 * m + g) ^ tile16_swizzle<D>(c))];
     };
+    // the tile's transpose, features 16 jb .. 16 jb + 15 in the lanes and the
+    // chunk's tokens in the upper half of zero-padded operands
+    auto trans_operand = [&](const u32x4* t, u32x4 (&op)[NB]) {
+        const int r = (lane >> 2) & 3, q = lane & 3;
+        const int row = 4 * g + r;
+        const u32x2* base = reinterpret_cast<const u32x2*>(t) + row * (2 * G);
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+            auto pt = (__attribute__((address_space(3))) s16x4*)(
+                base + 2 * ((4 * (jb >> 1) + q) ^ tile16_swizzle<D>(row)) + (jb & 1));
+            const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(pt));
+            op[jb].z = v.x;
+            op[jb].w = v.y;
+        }
+    };
 
     // state rows out0 + c, columns pi(jb, 4g + i) = 32 (jb / 2) + 8g + 4 (jb % 2) + i
-    f32x4 M[RB][NB];
-    if constexpr (MODE == kSegMap) {
+    f32x4 M[NB];
+    if constexpr (MAP) {
 #pragma unroll
         for (int jb = 0; jb < NB; ++jb) {
             const int base = 32 * (jb >> 1) + 8 * g + 4 * (jb & 1);
-            M[0][jb] = f32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) M[1][jb][i] = (base + i == out0 + c) ? 1.f : 0.f;
+            for (int i = 0; i < 4; ++i) M[jb][i] = (base + i == out0 + c) ? 1.f : 0.f;
         }
     } else {
         const float* w0 = seg == 0 ? W0 + (size_t)slice * dd : w.wstart + sw;
         const float* wr = w0 + (size_t)(out0 + c) * D;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-            M[0][2 * m] = *(const f32x4*)(wr + 32 * m + 8 * g);
-            M[0][2 * m + 1] = *(const f32x4*)(wr + 32 * m + 8 * g + 4);
+            M[2 * m] = *(const f32x4*)(wr + 32 * m + 8 * g);
+            M[2 * m + 1] = *(const f32x4*)(wr + 32 * m + 8 * g + 4);
         }
     }
-    u32x4 Mf[RB][NM];
+    u32x4 Mf[NM];
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
-#pragma unroll
-        for (int m = 0; m < NM; ++m) Mf[r][m] = pack_bf16x8(M[r][2 * m], M[r][2 * m + 1]);
+    for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
     const u32x2 I16 = identity_b16(lane);
-    // -V of a chunk for chain r (the identity chain has no V)
-    auto vneg_of = [&](u32x2 v, int r) {
-        return r == 0 ? v ^ u32x2{0x80008000u, 0x80008000u} : u32x2{0u, 0u};
-    };
+    // map: minus W_B, output features pi(ob, 4g + i), columns out0 + c (the
+    // transposed V operand orders its features as the state's columns)
+    f32x4 Sb[MAP ? NB : 1];
+#pragma unroll
+    for (int ob = 0; ob < (MAP ? NB : 1); ++ob) Sb[ob] = f32x4{0, 0, 0, 0};
 
-    // chunk X lives in LDS slot X % kSlots; tiles of chunks 0 .. P-1 are stored up
-    // front, and during chunk ch the tile of chunk ch + P is stored and the
-    // pieces of chunk ch + 2P loaded (into the register slots they came from).
-    // re[] holds eta of chunks ch .. ch + P - 1.
+    // step X uses LDS slot X % kSlots; tiles of steps 0 .. P-1 are stored up
+    // front, and during step ch the tile of step ch + P is stored and the pieces
+    // of step ch + 2P loaded (into the register slots they came from).  re[]
+    // holds eta of steps ch .. ch + P - 1.
     u32x4 rg[P];
     u32x2 rv[kV8 ? P : 1] = {};
     f32x4 re[P];
@@ -246,7 +267,7 @@ __device__ __forceinline__ void seg_body(
         gload(rg[p], p);
         if constexpr (kV8) rv[p] = vload(p);
     }
-    // the loads that stay in flight into the loop, in the order a chunk step issues
+    // the loads that stay in flight into the loop, in the order a step issues
     // them, so that the loop's waits count them as in the steady state
 #pragma unroll
     for (int p = 0; p < P; ++p) {
@@ -257,27 +278,25 @@ __device__ __forceinline__ void seg_body(
     }
     __syncthreads();
 
-    // E_0 = K_0 W^T - V_0 for each chain; kb[ch & 1] holds K_ch as row operand, the
-    // other set K_{ch+1}
+    // E of the first step = K W^T (- V); kb[ch & 1] holds K of step ch as row
+    // operand, the other set K of step ch + 1
     u32x4 kb[2][NM];
     row_operand(L[0].g[0], kb[0]);
     row_operand(L[1].g[0], kb[1]);
-    f32x4 Et[RB];
+    f32x4 Et = mfma16(vneg(L[0]), I16, f32x4{0, 0, 0, 0});
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-        Et[r] = mfma16(vneg_of(vread(L[0]), r), I16, f32x4{0, 0, 0, 0});
-#pragma unroll
-        for (int m = 0; m < NM; ++m) Et[r] = mfma32(kb[0][m], Mf[r][m], Et[r]);
-    }
+    for (int m = 0; m < NM; ++m) Et = mfma32(kb[0][m], Mf[m], Et);
     // 16-deep products as 32-deep ones whose lower half is zero in one operand
-    u32x4 ktz[NB], smz = {0u, 0u, 0u, 0u};
+    u32x4 ktz[NB], vtz[MAP ? NB : 1], smz = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) ktz[jb] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int jb = 0; jb < (MAP ? NB : 1); ++jb) vtz[jb] = u32x4{0u, 0u, 0u, 0u};
 
     auto step = [&](int ch, auto kc_) {
         constexpr int k = decltype(kc_)::value;
         constexpr int p = k % P;
-        constexpr int j = k % kGroup;              // chunk within its group
+        constexpr int j = k % kGroup;              // step within its group
         constexpr int zb = (k / kGroup) & 1;       // group parity (c0 is a multiple of 16)
         // staged unconditionally: past the end the slot receives a re-read of the last
         // chunk (read only by the unused lookahead), and a conditional use would let
@@ -287,56 +306,39 @@ __device__ __forceinline__ void seg_body(
         if constexpr (kV8) rv[p] = vload(ch + 2 * P);
         // the previous group's Z, complete since the last barrier
         u32x2 zprev = {0u, 0u};
-        if constexpr (MODE == kSegScan) zprev = Zs[(zb ^ 1) * kGroup + j][vpos];
+        if constexpr (!MAP) zprev = Zs[(zb ^ 1) * kGroup + j][vpos];
 
-        const u32x4* Kc = L[k].g[0];
         constexpr int pe = p & 1;
         u32x4 (&kc)[NM] = kb[pe];
         u32x4 (&kn)[NM] = kb[pe ^ 1];
-        // K_c with the feature in the lanes (A operand of the state update)
-        {
-            const int r = (lane >> 2) & 3, q = lane & 3;
-            const int row = 4 * g + r;
-            const u32x2* base = reinterpret_cast<const u32x2*>(Kc) + row * (2 * G);
-#pragma unroll
-            for (int jb = 0; jb < NB; ++jb) {
-                auto pt = (__attribute__((address_space(3))) s16x4*)(
-                    base + 2 * ((4 * (jb >> 1) + q) ^ tile16_swizzle<D>(row)) + (jb & 1));
-                const u32x2 t = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(pt));
-                ktz[jb].z = t.x;
-                ktz[jb].w = t.y;
-            }
-        }
+        // K with the feature in the lanes (A operand of the state update)
+        trans_operand(L[k].g[0], ktz);
         const f32x4 et = re[p];
-        // F_c = -diag(eta) E_c per chain
-        u32x4 IF[RB];
-#pragma unroll
-        for (int r = 0; r < RB; ++r) {
-            const u32x2 F = pack_bf16x4(-et * Et[r]);
-            IF[r] = u32x4{I16.x, I16.y, F.x, F.y};
-        }
-        // E_{c+1} = K_{c+1} W_c^T + [-V_{c+1} | G_c] [I ; F_c]
+        // F = -diag(eta) E
+        const u32x2 F = pack_bf16x4(-et * Et);
+        const u32x4 IF = {I16.x, I16.y, F.x, F.y};
+        // E of the next step = K' W^T + [-V' | G] [I ; F]  (G = K' K^T)
         {
             f32x4 Gt = {0, 0, 0, 0};
 #pragma unroll
             for (int m = 0; m < NM; ++m) Gt = mfma32(kc[m], kn[m], Gt);
             const u32x2 Gb = pack_bf16x4(Gt);
+            f32x4 Pt = {0, 0, 0, 0};
 #pragma unroll
-            for (int r = 0; r < RB; ++r) {
-                f32x4 Pt = {0, 0, 0, 0};
-#pragma unroll
-                for (int m = 0; m < NM; ++m) Pt = mfma32(kn[m], Mf[r][m], Pt);
-                const u32x2 vneg = vneg_of(vread(L[(k + 1) % kSlots]), r);
-                Et[r] = mfma32(u32x4{vneg.x, vneg.y, Gb.x, Gb.y}, IF[r], Pt);
-            }
+            for (int m = 0; m < NM; ++m) Pt = mfma32(kn[m], Mf[m], Pt);
+            const u32x2 vn = vneg(L[(k + 1) % kSlots]);
+            Et = mfma32(u32x4{vn.x, vn.y, Gb.x, Gb.y}, IF, Pt);
         }
-        // W_{c+1} = W_c + F_c^T K_c
+        // W += F^T K
 #pragma unroll
-        for (int r = 0; r < RB; ++r)
+        for (int jb = 0; jb < NB; ++jb) M[jb] = mfma32(ktz[jb], IF, M[jb]);
+        if constexpr (MAP) {
+            // -W_B += V^T F  (V with the feature in the lanes)
+            trans_operand(L[k].g[1], vtz);
 #pragma unroll
-            for (int jb = 0; jb < NB; ++jb) M[r][jb] = mfma32(ktz[jb], IF[r], M[r][jb]);
-        if constexpr (MODE == kSegScan) {
-            // Z_c = Q_c W_c^T + causal scores times F_c
+            for (int ob = 0; ob < NB; ++ob) Sb[ob] = mfma32(vtz[ob], IF, Sb[ob]);
+        } else {
+            // Z = Q W^T + causal scores times F
             u32x4 qc[NM];
             row_operand(L[k].g[1], qc);
             f32x4 St = {0, 0, 0, 0};
@@ -349,19 +351,17 @@ __device__ __forceinline__ void seg_body(
             Sm.w = (4 * g + 3 <= c) ? St.w : 0.f;
             f32x4 Zt = {0, 0, 0, 0};
 #pragma unroll
-            for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[0][m], qc[m], Zt);
+            for (int m = 0; m < NM; ++m) Zt = mfma32(Mf[m], qc[m], Zt);
             const u32x2 sb = pack_bf16x4(Sm);
             smz.z = sb.x;
             smz.w = sb.y;
-            Zt = mfma32(IF[0], smz, Zt);
+            Zt = mfma32(IF, smz, Zt);
             Zs[zb * kGroup + j][opos] = pack_bf16x4(Zt);
             zstore(zprev, ch - kGroup);
         }
 #pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int m = 0; m < NM; ++m) Mf[r][m] = pack_bf16x8(M[r][2 * m], M[r][2 * m + 1]);
-        row_operand(L[(k + 2) % kSlots].g[0], kc);   // K_{c+2} (stale past the end)
+        for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
+        row_operand(L[(k + 2) % kSlots].g[0], kc);   // K of step ch + 2 (stale past the end)
         re[p] = eload(ch + P);
         if (j == kGroup - 1) __syncthreads();
     };
@@ -373,7 +373,35 @@ __device__ __forceinline__ void seg_body(
         if (c0 + k < nch) step(c0 + k, k);
     }, std::make_integer_sequence<int, kSlots - 1>{});
 
-    if constexpr (MODE == kSegScan) {
+    if constexpr (MAP) {
+        // A (= R_1, from the rows of R_1^T held here) and W_B, transposed through
+        // LDS (row stride D + 1) and stored row-major
+        __syncthreads();   // every wave is done with the ring
+        float* ta = reinterpret_cast<float*>(L);
+        float* tb = ta + D * (D + 1);
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+            const int base = 32 * (jb >> 1) + 8 * g + 4 * (jb & 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ta[(base + i) * (D + 1) + out0 + c] = M[jb][i];
+                tb[(base + i) * (D + 1) + out0 + c] = -Sb[jb][i];
+            }
+        }
+        __syncthreads();
+        const int r = tid >> 2, cb = 16 * (tid & 3);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            f32x4 a, b;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a[i] = ta[r * (D + 1) + cb + 4 * q + i];
+                b[i] = tb[r * (D + 1) + cb + 4 * q + i];
+            }
+            *(f32x4*)(w.amap + sw + (size_t)r * D + cb + 4 * q) = a;
+            *(f32x4*)(w.wb + sw + (size_t)r * D + cb + 4 * q) = b;
+        }
+    } else {
         // Z of the last group and the rest of the group before it
         __syncthreads();
         const int gl = (nch - 1) / kGroup, m = nch - gl * kGroup;
@@ -381,24 +409,14 @@ __device__ __forceinline__ void seg_body(
             for (int jj = m; jj < kGroup; ++jj)
                 zstore(Zs[((gl - 1) & 1) * kGroup + jj][vpos], (gl - 1) * kGroup + jj);
         for (int jj = 0; jj < m; ++jj) zstore(Zs[(gl & 1) * kGroup + jj][vpos], gl * kGroup + jj);
-    }
-
-    // end states
-    float* dst[RB];
-    if constexpr (MODE == kSegMap) {
-        dst[0] = w.wb + sw;
-        dst[1] = w.amap + sw;
-    } else {
-        dst[0] = seg == plan.S - 1 ? W_out + (size_t)slice * dd
-                                   : w.wstart + ((size_t)slice * plan.S) * dd;   // segment 0
-    }
+        // end state
+        float* dst = seg == plan.S - 1 ? W_out + (size_t)slice * dd
+                                       : w.wstart + ((size_t)slice * plan.S) * dd;   // segment 0
+        float* wr = dst + (size_t)(out0 + c) * D;
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-        float* wr = dst[r] + (size_t)(out0 + c) * D;
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-            *(f32x4*)(wr + 32 * m + 8 * g) = M[r][2 * m];
-            *(f32x4*)(wr + 32 * m + 8 * g + 4) = M[r][2 * m + 1];
+        for (int m2 = 0; m2 < NM; ++m2) {
+            *(f32x4*)(wr + 32 * m2 + 8 * g) = M[2 * m2];
+            *(f32x4*)(wr + 32 * m2 + 8 * g + 4) = M[2 * m2 + 1];
         }
     }
 }
@@ -490,10 +508,12 @@ __global__ __launch_bounds__(256) void seg_combine_kernel(void* ws, int BH, int 
     }
 }
 
-// Segment lengths: n0 = kSegFirstRatio n1.  Measured per call (32 heads of 32768
-// tokens): 0.5 -> 0.229 ms, 0.7 -> 0.226, 0.85 -> 0.219, 1.0 -> 0.233, 1.2 -> 0.240,
-// 1.4 -> 0.250; 16 and 8 heads change by under 5% across 0.5 .. 1.0.
-constexpr double kSegFirstRatio = 0.85;
+// Segment lengths: n0 = kSegFirstRatio n1.  Segment 0 scans while the others form
+// their maps, so the ratio balances a scan step against a map step.  Measured per
+// call (32 heads of 32768 tokens, same inputs repeated): 0.3 -> 0.181 ms, 0.4 ->
+// 0.176, 0.55 -> 0.172-0.176, 0.7 -> 0.174, 0.85 -> 0.180; 16 heads: 0.55 -> 0.103,
+// 0.85 -> 0.108; 8 heads of 65536: flat from 0.4 to 0.7 (0.126-0.127 ms).
+constexpr double kSegFirstRatio = 0.55;
 constexpr int kSegMinChunks = 32;     // shortest middle segment
 constexpr int kSegUnits = 256;        // MI355X compute units
 
