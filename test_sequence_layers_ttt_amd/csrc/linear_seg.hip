@@ -35,6 +35,7 @@
 #include "device_common.h"
 #include "launch.h"
 #include "mfma_common.h"
+#include "mfma_f32.h"
 
 namespace ttt {
 namespace {
@@ -457,54 +458,57 @@ __global__ __launch_bounds__(256) void linear_seg_pass2_kernel(
 }
 
 // W_start,k+1 = W_B,k + W_start,k A_k for k = 1 .. S-2 (W_start,1 = the end of
-// segment 0, left in W_start[0] by pass 1), in fp32: one workgroup per (slice,
-// 16 rows), thread (row i, column quad q).  A_k and the current rows sit in LDS,
-// double-buffered by k's parity; A_{k+1} and W_B,k+1 are fetched while step k
-// computes, so the chain of S - 2 steps waits on memory once.
+// segment 0, left in W_start[0] by pass 1), in fp32 on the fp32 matrix cores
+// (16x16x4 products of fp32 operands): one workgroup per (slice, 16 rows), wave w
+// computing columns 16w .. 16w + 15.  The current rows sit in LDS; the next map's
+// A block and W_B rows load while a step computes, so the chain of S - 2 steps
+// waits on memory once.  (The FMA loop over LDS this replaces took 12-13 us at
+// 32 heads of 8 segments.)
 __global__ __launch_bounds__(256) void seg_combine_kernel(void* ws, int BH, int S)
 {
     constexpr int D = kSegD;
-    constexpr int NQ = D * D / 4 / 256;   // f32x4 of A per thread
-    __shared__ f32x4 al[2][D * D / 4];
-    __shared__ float wl[2][16 * D];
+    constexpr int STRIDE = D + 4;   // RL reads of 16 lanes on distinct banks
+    __shared__ __align__(16) float cur[16 * STRIDE];
     const SegWorkspace w = seg_workspace(ws, BH, S);
     const size_t dd = (size_t)D * D;
     const int slice = blockIdx.x, i0 = 16 * blockIdx.y;
     const int tid = threadIdx.x;
-    const int i = tid >> 4, q = tid & 15;
-    const size_t row = (size_t)(i0 + i) * D + 4 * q;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int c = lane & 15, g = lane >> 4;
     float* base = w.wstart + (size_t)slice * S * dd;
-    f32x4 cur = *(const f32x4*)(base + row);
-    *(f32x4*)(base + dd + row) = cur;
-    f32x4 ar[NQ], wbr = {0, 0, 0, 0};
+    {   // W_start,1: thread tid copies 4 values of the 16 rows
+        const int r = tid >> 4, q = tid & 15;
+        const size_t off = (size_t)(i0 + r) * D + 4 * q;
+        const f32x4 v = *(const f32x4*)(base + off);
+        *(f32x4*)(base + dd + off) = v;
+        *(f32x4*)(cur + r * STRIDE + 4 * q) = v;
+    }
+    // CL forms: a[kb] of A_k rows 16 kb .. + 15, columns 16w .. + 15; wb of W_B,k
+    // rows i0 .. i0 + 15, the same columns
+    f32x4 a[4], wb;
     auto fetch = [&](int k) {
-        const size_t sk = ((size_t)slice * S + k) * dd;
+        const float* ak = w.amap + ((size_t)slice * S + k) * dd;
+        const float* bk = w.wb + ((size_t)slice * S + k) * dd;
 #pragma unroll
-        for (int e = 0; e < NQ; ++e) ar[e] = *(const f32x4*)(w.amap + sk + 4 * (tid + 256 * e));
-        wbr = *(const f32x4*)(w.wb + sk + row);
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) a[kb][v] = ak[(size_t)(16 * kb + 4 * g + v) * D + 16 * wave + c];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) wb[v] = bk[(size_t)(i0 + 4 * g + v) * D + 16 * wave + c];
     };
     if (S > 2) fetch(1);
+    __syncthreads();
     for (int k = 1; k + 1 < S; ++k) {
-        const int b = k & 1;
+        f32x4 acc = wb;
 #pragma unroll
-        for (int e = 0; e < NQ; ++e) al[b][tid + 256 * e] = ar[e];
-        wl[b][i * D + 4 * q + 0] = cur.x;
-        wl[b][i * D + 4 * q + 1] = cur.y;
-        wl[b][i * D + 4 * q + 2] = cur.z;
-        wl[b][i * D + 4 * q + 3] = cur.w;
-        f32x4 o = wbr;
-        __syncthreads();
+        for (int kb = 0; kb < 4; ++kb) acc = mm16(rl<STRIDE>(cur, 16 * kb, lane), a[kb], acc);
         if (k + 2 < S) fetch(k + 1);
-        for (int j = 0; j < D; ++j) {
-            const float a = wl[b][i * D + j];
-            const f32x4 r = al[b][j * (D / 4) + q];
-            o.x = fmaf(a, r.x, o.x);
-            o.y = fmaf(a, r.y, o.y);
-            o.z = fmaf(a, r.z, o.z);
-            o.w = fmaf(a, r.w, o.w);
-        }
-        cur = o;
-        *(f32x4*)(base + (k + 1) * dd + row) = cur;
+        __syncthreads();   // every wave has read the current rows
+        put_cl<STRIDE>(cur, 16 * wave, lane, acc);
+        float* dst = base + (size_t)(k + 1) * dd + (size_t)(i0 + 4 * g) * D + 16 * wave + c;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) dst[(size_t)v * D] = acc[v];
+        __syncthreads();
     }
 }
 
