@@ -28,10 +28,16 @@ typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
 typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
 
 // D = A(16x16) B(16x16) + C, bf16 operands (4 per lane), fp32 accumulate.
-// Issued as the 16x16x32 form with the upper four slots of both operands zero:
-// with this toolchain the 16x16x16 bf16 form returned stale accumulator values
-// under some instruction schedules (seen with d = 128 kernels), while the
-// 16x16x32 form was exact in every schedule tested.  The zero slots add nothing.
+// Issued as the 16x16x32 form with the upper four slots of both operands zero.
+// The 16-deep forms (bf16 and fp16) read a stale accumulator when C is the result
+// of a 16x16x32 MFMA issued just before them: a one-wave probe on gfx950 gives
+// garbage for that pair back to back and the exact sum with 24 wait cycles
+// between, and this toolchain emits no wait states for it (an accumulator
+// written by the same 16-deep form, or the 16-deep product overwriting the
+// 32-deep one's accumulator register, are fine).  Mixing the two depths in one
+// dependent chain is what returned wrong results in the d = 128 kernels and, with
+// the fp16 form, in the TTT-MLP kernel.  One depth everywhere avoids the pair; the
+// zero slots add nothing.
 __device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c)
 {
     const u32x4 a8 = {a.x, a.y, 0u, 0u}, b8 = {b.x, b.y, 0u, 0u};
@@ -53,6 +59,7 @@ __device__ __forceinline__ f32x4 mfma32h(u32x4 a, u32x4 b, f32x4 c)
                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+// (zero-padded 32-deep form, for the reason given at mfma16)
 __device__ __forceinline__ f32x4 mfma16h(u32x2 a, u32x2 b, f32x4 c)
 {
     const u32x4 a8 = {a.x, a.y, 0u, 0u}, b8 = {b.x, b.y, 0u, 0u};
