@@ -102,9 +102,10 @@ __device__ __forceinline__ f32x4 gelu_tab_entry(int i)
 // fraction of the step past it
 __device__ __forceinline__ int gelu_tab_pos(float x, float& fr)
 {
+    // t in [0, 1023.999] (a NaN converts to 0), so the index needs no clamp
     const float t = __builtin_amdgcn_fmed3f(fmaf(x, 64.f, 512.f), 0.f, 1023.999f);
     fr = __builtin_amdgcn_fractf(t);
-    return min(max((int)t, 0), kTab - 1);
+    return (int)t;
 }
 
 __device__ __forceinline__ void gelu_pair(const f32x4* tab, f32x4 h, f32x4& g, f32x4& gp)
