@@ -95,10 +95,11 @@ constexpr int kSegGroup = 4;
 constexpr int kSegAhead = 2 * kSegGroup;
 constexpr int kSegSlots = 2 * kSegAhead;
 
-// One chunk's inputs in LDS.  K and Q as swizzled 16-byte granules (row operand
-// and transposed reads conflict-free within a 16-lane group).  V as 8-byte units
-// (four features), unit u of token r at r * 16 + (u ^ seg_vswz(r)): the 16 tokens
-// a lane group reads at one unit then fall on distinct banks.
+// One chunk's inputs in LDS.  K and Q (a map: K and V) as swizzled 16-byte
+// granules (row operand and transposed reads conflict-free within a 16-lane
+// group).  A scan's V as 8-byte units (four features), unit u of token r at
+// r * 16 + (u ^ seg_vswz(r)): the 16 tokens a lane group reads at one unit then
+// fall on distinct banks.
 struct SegTile {
     u32x4 g[2][16 * (kSegD / 8)];
     u32x2 v[16 * 16];
