@@ -31,7 +31,9 @@
 // stores its Z block itself: at d = 128 the extra LDS and registers do not fit
 // beside the K and Q rings, and two-wave workgroups at d = 64 (a 64-byte stripe
 // per token) measured slower staged (8x12 heads, T = 2048: 37.5 us against 36.3;
-// four-wave workgroups at 64x12 heads, T = 1024: 94.0 against 99.7).
+// four-wave workgroups at 64x12 heads, T = 1024: 94.0 against 99.7).  Two-wave
+// workgroups with a ragged last chunk still stage Z, whose per-lane row check
+// otherwise branches (8x12 heads, T = 2047: 48.5 us against 54.1).
 //
 // Tiles are staged P = 2 kGroup chunks ahead into a ring of 2P LDS slots, with
 // one barrier per kGroup chunks: a slot is rewritten only once every wave has
@@ -95,10 +97,11 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
     constexpr int kGroup = WPG >= 8 ? 2 : 4;
     constexpr int P = 2 * kGroup;   // chunks whose granules a thread holds in registers
     constexpr int kSlots = 2 * P;   // > P + kGroup: chunks ch - kGroup .. ch + 2 stay
-    constexpr bool SV = D == 64 && WPG >= 4;   // V and Z staged through LDS
+    constexpr bool SV = D == 64 && WPG >= 4;   // V staged through LDS
+    constexpr bool SZ = D == 64 && (WPG >= 4 || !FULL);   // Z staged through LDS
     constexpr int U = 4 * WPG;      // 8-byte units of the stripe per token
     __shared__ CoopTile<D, WPG> L[kSlots];
-    __shared__ u32x2 Zs[SV ? 2 * kGroup : 1][SV ? 16 * U : 1];   // Z of two groups of chunks
+    __shared__ u32x2 Zs[SZ ? 2 * kGroup : 1][SZ ? 16 * U : 1];   // Z of two groups of chunks
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
         if constexpr (SV) rv[p] = vload(ch + 2 * P);
         // the previous group's Z, complete since the last barrier
         u32x2 zprev = {0u, 0u};
-        if constexpr (SV) zprev = Zs[(zb ^ 1) * kGroup + j][vpos];
+        if constexpr (SZ) zprev = Zs[(zb ^ 1) * kGroup + j][vpos];
 
         constexpr int sl = k;
         const u32x4* Kc = L[sl].g[0];
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
             smz.w = sb.y;
             Zt = mfma32(IF, smz, Zt);
         }
-        if constexpr (SV) {
+        if constexpr (SZ) {
             Zs[zb * kGroup + j][opos] = pack_bf16x4(Zt);
             zstore(zprev, ch - kGroup);
         } else if (FULL || 16 * ch + c < T) {
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
         if (c0 + k < nch) step(c0 + k, k);
     }, std::make_integer_sequence<int, kSlots - 1>{});
 
-    if constexpr (SV) {   // Z of the last group and the rest of the group before it
+    if constexpr (SZ) {   // Z of the last group and the rest of the group before it
         __syncthreads();
         const int gl = (nch - 1) / kGroup, m = nch - gl * kGroup;
         if (gl > 0)
