@@ -1,6 +1,8 @@
 // TTT-Linear forward scan, chunks of exactly 16 tokens: each (batch, head) is
 // split over d/16 / WPG workgroups of WPG waves, wave w of part p owning state
-// rows 16 (p WPG + w) .. + 15.
+// rows 16 (p WPG + w) .. + 15.  Packed documents take the ragged-chunk form
+// (FULL false) with one slice per (document, head): its tokens come from the
+// offset table, and an empty document copies its start state through.
 //
 // Same chunk arithmetic as the single-wave chunk kernel (linear_mfma.hip): with
 // F_c = -diag(eta) E_c (token-row layout, PaperTrace "5 · TestingTime 训练与长上下文"
@@ -31,9 +33,15 @@
 // stores its Z block itself: at d = 128 the extra LDS and registers do not fit
 // beside the K and Q rings, and two-wave workgroups at d = 64 (a 64-byte stripe
 // per token) measured slower staged (8x12 heads, T = 2048: 37.5 us against 36.3;
-// four-wave workgroups at 64x12 heads, T = 1024: 94.0 against 99.7).  Two-wave
-// workgroups with a ragged last chunk still stage Z, whose per-lane row check
-// otherwise branches (8x12 heads, T = 2047: 48.5 us against 54.1).
+// four-wave workgroups at 64x12 heads, T = 1024: 94.0 against 99.7).
+//
+// A sequence whose length is not a multiple of 16 (and every packed document)
+// takes the ragged form: its loads and stores go through range-checked buffer
+// resources over the slice's rows, so rows past the end read as zero and are not
+// written, and a zero row of K and V contributes nothing to the scan.  The loop
+// then has no per-lane clamps, masks or branches and runs at the whole-chunk rate
+// (8x12 heads, T = 2047: 36.8 us, against 48.3 with clamped loads and masked eta;
+// 8 packed documents of 8x12 heads' tokens: 58.6 against 78.0).
 //
 // Tiles are staged P = 2 kGroup chunks ahead into a ring of 2P LDS slots, with
 // one barrier per kGroup chunks: a slot is rewritten only once every wave has
@@ -83,7 +91,8 @@ template <int D, int WPG, int ETA, bool FULL>
 __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
-    const float* W0, uint16_t* __restrict__ Z, float* W_out, int BH, int T)
+    const float* W0, uint16_t* __restrict__ Z, float* W_out, int BH, int T_all,
+    const int* __restrict__ cu, int H, int total_T)
 {
     constexpr int NB = D / 16;
     constexpr int NM = D / 32;
@@ -98,7 +107,7 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
     constexpr int P = 2 * kGroup;   // chunks whose granules a thread holds in registers
     constexpr int kSlots = 2 * P;   // > P + kGroup: chunks ch - kGroup .. ch + 2 stay
     constexpr bool SV = D == 64 && WPG >= 4;   // V staged through LDS
-    constexpr bool SZ = D == 64 && (WPG >= 4 || !FULL);   // Z staged through LDS
+    constexpr bool SZ = D == 64 && WPG >= 4;   // Z staged through LDS
     constexpr int U = 4 * WPG;      // 8-byte units of the stripe per token
     __shared__ CoopTile<D, WPG> L[kSlots];
     __shared__ u32x2 Zs[SZ ? 2 * kGroup : 1][SZ ? 16 * U : 1];   // Z of two groups of chunks
@@ -115,25 +124,44 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
         xcd_unit_part(blockIdx.x, PARTS, slice, part);
         if (slice >= BH) return;
     }
-    const size_t tok0 = (size_t)slice * T;
+    // the slice's first row and length T (packed documents: only with a ragged
+    // last chunk, FULL false)
+    size_t tok0;
+    int T;
+    if constexpr (FULL) {
+        tok0 = (size_t)slice * T_all;
+        T = T_all;
+    } else {
+        slice_span(cu, H, total_T, T_all, slice, tok0, T);
+    }
     const int nch = (T + 15) / 16;
     const int out0 = 16 * (part * WPG + wave);
+    // Ragged form: K, Q, V, eta and Z go through range-checked buffer resources
+    // over the slice's rows, the whole offset in the vector offset (the part the
+    // check covers; T d 2 < 2^31 - 2^20, so that offsets past the end still fit):
+    // rows past T and chunks past the end read as zero, and Z rows past T are
+    // dropped.  A zero row of K and V gives a zero row of E, so such a token
+    // contributes nothing (F row zero) whatever its eta: no clamps, masks or
+    // per-lane branches.
+    auto rsrc = [](const void* base, int bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kCoopBufferFlags);
+    };
+    const int sbytes = FULL ? 0 : T * D * 2;
+    const auto bK = rsrc(K + tok0 * D, sbytes), bQ = rsrc(Q + tok0 * D, sbytes);
+    const auto bV = rsrc(V + tok0 * D, sbytes), bZ = rsrc(Z + tok0 * D, sbytes);
+    const auto bE = rsrc(eta ? eta + tok0 : nullptr, eta && !FULL ? T * 4 : 0);
     const int sbase = 16 * WPG * part;   // first feature of the workgroup's stripe
     // thread tid's piece of a stripe tile: token vrow, unit vunit; this lane's
     // unit of one (token c, features out0 + 4g .. + 3)
     const int vrow = tid / U, vunit = tid % U;
     const int vpos = vrow * U + (vunit ^ coop_vswz(vrow));
     const int opos = c * U + ((4 * wave + g) ^ coop_vswz(c));
-    // token of row r of chunk ch, clamped into the sequence (a clamped row is a
-    // re-read; its token gets eta = 0 and no store)
-    auto tok = [&](int ch, int r) {
-        const int cc = ch < nch ? ch : nch - 1;
-        const int t = 16 * cc + r;
-        return FULL ? t : (t < T ? t : T - 1);
-    };
 
     // this thread's granules of each staged tile: granule tid + i NT of the 32 G
     // granules of K (the first 16 G) and Q
+    // (a wave's granules all come from one of the two: which[i] is also
+    // (64 wave + i NT) / 16 G, uniform)
+    static_assert(16 * G % 64 == 0, "a wave's granules lie in one tile");
     int which[GPT], grow[GPT], ggr[GPT], lpos[GPT];
 #pragma unroll
     for (int i = 0; i < GPT; ++i) {
@@ -143,22 +171,25 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
         ggr[i] = idx % G;
         lpos[i] = grow[i] * G + (ggr[i] ^ tile16_swizzle<D>(grow[i]));
     }
-    // first token of chunk ch (clamped), as a wave-uniform base; lanes add a
-    // 32-bit offset within the chunk
+    // whole-chunk form: first token of chunk ch (a chunk past the end re-reads the
+    // last one), as a wave-uniform base; lanes add a 32-bit offset within the chunk
     auto chunk_base = [&](int ch) {
         const int cc = ch < nch ? ch : nch - 1;
         return tok0 + (size_t)16 * cc;
     };
-    auto row_in = [&](int ch, int r) {   // row r of chunk ch, clamped into the sequence
-        if (FULL) return r;
-        const int cc = ch < nch ? ch : nch - 1;
-        return 16 * cc + r < T ? r : T - 1 - 16 * cc;
-    };
     auto gload = [&](u32x4 (&r)[GPT], int ch) {
-        const size_t base = chunk_base(ch) * D;
+        if constexpr (FULL) {
+            const size_t base = chunk_base(ch) * D;
 #pragma unroll
-        for (int i = 0; i < GPT; ++i)
-            r[i] = *(const u32x4*)((which[i] ? Q : K) + base + (row_in(ch, grow[i]) * D + 8 * ggr[i]));
+            for (int i = 0; i < GPT; ++i)
+                r[i] = *(const u32x4*)((which[i] ? Q : K) + base + (grow[i] * D + 8 * ggr[i]));
+        } else {
+#pragma unroll
+            for (int i = 0; i < GPT; ++i)
+                r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                    (64 * wave + i * NT) / (16 * G) ? bQ : bK,
+                    (16 * ch + grow[i]) * (2 * D) + 16 * ggr[i], 0, 0));
+        }
     };
     auto stage = [&](CoopTile<D, WPG>& t, const u32x4 (&r)[GPT], const u32x2& v) {
 #pragma unroll
@@ -167,9 +198,13 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
     };
     // SV: thread tid's piece of the stripe; else this lane's unit
     auto vload = [&](int ch) {
-        const uint16_t* b = V + chunk_base(ch) * D;
-        if constexpr (SV) return *(const u32x2*)(b + (row_in(ch, vrow) * D + sbase + 4 * vunit));
-        else return *(const u32x2*)(b + (row_in(ch, c) * D + out0 + 4 * g));
+        const int r = SV ? vrow : c, f = SV ? sbase + 4 * vunit : out0 + 4 * g;
+        if constexpr (FULL) {
+            return *(const u32x2*)(V + chunk_base(ch) * D + (r * D + f));
+        } else {
+            return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                bV, ((16 * ch + r) * D + f) * 2, 0, 0));
+        }
     };
     // Z of chunk ch as thread tid's piece: rows past T (and chunks ch < 0) fall
     // outside the resource and are dropped
@@ -186,8 +221,16 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
             return *(const f32x4*)(eta + tok0 + 16 * cc + 4 * g);
         } else if (ETA == kCoopEtaToken) {
             f32x4 e;
+            if constexpr (FULL) {
+                const int cc = ch < nch ? ch : nch - 1;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) e[r] = eta[tok0 + tok(ch, 4 * g + r)];
+                for (int r = 0; r < 4; ++r) e[r] = eta[tok0 + 16 * cc + 4 * g + r];
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    e[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                        bE, (16 * ch + 4 * g + r) * 4, 0, 0));
+            }
             return e;
         } else {
             return f32x4{eta_scalar, eta_scalar, eta_scalar, eta_scalar};
@@ -207,6 +250,19 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
             M[2 * m] = *(const f32x4*)(w + 32 * m + 8 * g);
             M[2 * m + 1] = *(const f32x4*)(w + 32 * m + 8 * g + 4);
         }
+    }
+    // this wave's rows of the state to W_out
+    auto store_state = [&]() {
+        float* w = W_out + (size_t)slice * D * D + (size_t)(out0 + c) * D;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            *(f32x4*)(w + 32 * m + 8 * g) = M[2 * m];
+            *(f32x4*)(w + 32 * m + 8 * g + 4) = M[2 * m + 1];
+        }
+    };
+    if (!FULL && T == 0) {   // an empty document (uniform over the workgroup): the state passes through
+        store_state();
+        return;
     }
     u32x4 Mf[NM];
 #pragma unroll
@@ -316,14 +372,7 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
                 ktz[jb].w = t.y;
             }
         }
-        f32x4 et = re[p];
-        if (!FULL) {
-            const int n = min(16, T - 16 * ch);
-            et.x = (4 * g + 0 < n) ? et.x : 0.f;
-            et.y = (4 * g + 1 < n) ? et.y : 0.f;
-            et.z = (4 * g + 2 < n) ? et.z : 0.f;
-            et.w = (4 * g + 3 < n) ? et.w : 0.f;
-        }
+        const f32x4 et = re[p];
         // F_c = -diag(eta) E_c: the only value the next chunk waits for
         const u32x2 F = pack_bf16x4(-et * Et);
         const u32x4 IF = {I16.x, I16.y, F.x, F.y};
@@ -363,9 +412,12 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
         if constexpr (SZ) {
             Zs[zb * kGroup + j][opos] = pack_bf16x4(Zt);
             zstore(zprev, ch - kGroup);
-        } else if (FULL || 16 * ch + c < T) {
+        } else if constexpr (FULL) {
             uint16_t* zp = Z + (tok0 + (size_t)16 * ch) * D;
             *(u32x2*)(zp + (c * D + out0 + 4 * g)) = pack_bf16x4(Zt);
+        } else {
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, pack_bf16x4(Zt)), bZ,
+                                                  ((16 * ch + c) * D + out0 + 4 * g) * 2, 0, 0);
         }
 #pragma unroll
         for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
@@ -392,12 +444,7 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
         for (int jj = 0; jj < m; ++jj) zstore(Zs[(gl & 1) * kGroup + jj][vpos], gl * kGroup + jj);
     }
 
-    float* w = W_out + (size_t)slice * D * D + (size_t)(out0 + c) * D;
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-        *(f32x4*)(w + 32 * m + 8 * g) = M[2 * m];
-        *(f32x4*)(w + 32 * m + 8 * g + 4) = M[2 * m + 1];
-    }
+    store_state();
 }
 
 template <int D, int WPG, int ETA, bool FULL>
@@ -407,13 +454,14 @@ void launch_cfg(const LinearArgs& a, hipStream_t s)
     const unsigned grid = parts == 1 ? (unsigned)a.BH : (unsigned)((a.BH + 7) / 8 * 8 * parts);
     hipLaunchKernelGGL((linear_coop_kernel<D, WPG, ETA, FULL>), dim3(grid), dim3(64 * WPG), 0,
                        s, (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V, a.eta,
-                       a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.BH, a.T);
+                       a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.BH, a.T, a.cu, a.H,
+                       a.total_T);
 }
 
 template <int D, int WPG>
 void launch_eta(const LinearArgs& a, hipStream_t s)
 {
-    const bool full = a.T % 16 == 0;
+    const bool full = !a.cu && a.T % 16 == 0;
     const bool eta4 = a.eta && full && reinterpret_cast<uintptr_t>(a.eta) % 16 == 0;
     if (full) {
         if (!a.eta) launch_cfg<D, WPG, kCoopEtaScalar, true>(a, s);
@@ -448,6 +496,11 @@ bool linear_coop_supported(int d, int chunk, int bf16)
 
 hipError_t launch_linear_coop(const LinearArgs& a, hipStream_t s)
 {
+    // the ragged form (packed documents, or T not a multiple of 16) addresses a
+    // slice through 32-bit buffer offsets
+    const long long span = a.cu ? a.total_T : a.T;
+    if (!(!a.cu && a.T % 16 == 0) && span * a.d * 2 >= (1LL << 31) - (1LL << 20))
+        return hipErrorInvalidValue;
     switch (a.d) {
     case 64: return launch_d<64>(a, s);
     case 128: return launch_d<128>(a, s);

@@ -639,8 +639,14 @@ hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s)
     // Once the 16-row units outnumber the compute units, chunk-16 heads at d = 64
     // and 128 go to one workgroup per head that fetches K and Q once for all of
     // its waves (8x12 heads at d = 64: 49 us vs 52 us; at 32 heads, where every
-    // unit has a compute unit to itself, the single-wave kernel is faster).
-    if (!a.cu && (long)a.BH * (a.d / 16) > kComputeUnits &&
+    // unit has a compute unit to itself, the single-wave kernel is faster).  Packed
+    // documents count one slice per (document, head).  That kernel's ragged form
+    // (packed documents, or T not a multiple of 16) addresses a slice through 32-bit
+    // buffer offsets, so it takes slices of fewer than 2^31 - 2^20 bytes.
+    const long long span = a.cu ? a.total_T : a.T;
+    const bool offsets_fit =
+        (!a.cu && a.T % 16 == 0) || span * a.d * 2 < (1LL << 31) - (1LL << 20);
+    if ((long)a.BH * (a.d / 16) > kComputeUnits && offsets_fit &&
         linear_coop_supported(a.d, a.chunk, a.bf16))
         return launch_linear_coop(a, s);
     switch (a.d) {

@@ -102,11 +102,28 @@ def test_generic_plan_matches(dev):
 
 
 def test_many_documents(dev):
-    """48 documents x 12 heads: past 256 (document, head, row block) units the
-    matrix-core kernel takes two row blocks per wave."""
+    """48 documents x 12 heads: past 256 (document, head, 16-row block) units the
+    (document, head) slices go to the many-head kernel (four-wave workgroups)."""
     rng = np.random.default_rng(603)
     lengths = [int(v) for v in rng.integers(0, 90, size=48)]
     check(lengths, 12, 64, 16, "bf16", True, 603, dev, expect_plan=ttt.PLAN_MFMA)
+
+
+@pytest.mark.parametrize("d,H,n_docs,per_token", [
+    (64, 12, 24, True),     # 288 slices: one four-wave workgroup per slice
+    (64, 12, 8, False),     # 96 slices: two two-wave workgroups per slice
+    (128, 8, 8, True),      # 64 slices: two four-wave workgroups per slice
+    (128, 12, 12, False),   # 144 slices: one eight-wave workgroup per slice
+])
+def test_many_head_kernel_documents(dev, d, H, n_docs, per_token):
+    """Packed documents on every workgroup shape of the many-head kernel: empty,
+    one-token, ragged and whole-chunk documents, rows past the last document
+    untouched."""
+    rng = np.random.default_rng(604 + d + n_docs)
+    edge = [0, 1, 15, 16, 17, 64, 0, 33]
+    lengths = edge + [int(v) for v in rng.integers(0, 70, size=n_docs - len(edge))]
+    check(lengths, H, d, 16, "bf16", per_token, 604 + n_docs, dev, gap=3,
+          expect_plan=ttt.PLAN_MFMA)
 
 
 def test_malformed_offsets_stay_in_bounds(dev):
@@ -119,4 +136,23 @@ def test_malformed_offsets_stay_in_bounds(dev):
     Z, Wo = ttt.linear_fwd_varlen(K, K, K, None, W0, cu, 16, eta_scalar=0.05)
     torch.cuda.synchronize()
     assert torch.equal(Wo[1], W0[1])            # [25, 10) clamps to empty
+    assert torch.isfinite(Z).all() and torch.isfinite(Wo).all()
+
+
+def test_malformed_offsets_many_head_kernel(dev):
+    """The same clamping with enough (document, head) slices for the many-head
+    kernel: decreasing offsets give empty documents, offsets past total_T end at
+    total_T."""
+    import torch
+    H, d, T = 12, 64, 100
+    g = torch.Generator(device="cpu").manual_seed(605)
+    K = (torch.randn(H, T, d, generator=g) * 0.2).to(torch.bfloat16).to(dev)
+    cu_h = [0, 30, 12, 12, 50, 99, 1 << 30, 40, 60]
+    n_docs = len(cu_h) - 1
+    W0 = (torch.randn(n_docs, H, d, d, generator=g) * 0.02).to(dev)
+    cu = torch.tensor(cu_h, dtype=torch.int32, device=dev)
+    Z, Wo = ttt.linear_fwd_varlen(K, K, K, None, W0, cu, 16, eta_scalar=0.05)
+    torch.cuda.synchronize()
+    for n in (1, 2, 6):                         # [30, 12), [12, 12), [T, 40) clamp to empty
+        assert torch.equal(Wo[n], W0[n]), n
     assert torch.isfinite(Z).all() and torch.isfinite(Wo).all()
