@@ -94,12 +94,12 @@ typedef enum {
                                    multiple of 32 >= 128 */
     TTT_PLAN_SPLIT = 4          /* bf16 matrix cores, inclusive read, d = 64, chunk 16, T a
                                    multiple of 16 and >= 2048, at most 32 (batch, head)
-                                   slices: each sequence in S ~ 256 / slices segments;
-                                   segment 0 scans while the others form their affine
-                                   maps (scans from zero and from the identity), a
-                                   combine gives every segment its start state, and
-                                   segments 1 .. S-1 scan again from it (workspace:
-                                   3 S d^2 fp32 per slice) */
+                                   slices: each sequence in S ~ 256 / slices + 1
+                                   segments; segment 0 scans while segments 1 .. S-2
+                                   form their affine maps, a combine gives every
+                                   segment its start state, and segments 1 .. S-1
+                                   scan again from it (workspace: 3 S d^2 fp32 per
+                                   slice) */
 } ttt_plan;
 
 /* Read order of a chunk's tokens.  INCLUSIVE: token t reads with the chunk's

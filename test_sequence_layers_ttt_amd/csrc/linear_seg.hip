@@ -423,9 +423,11 @@ __device__ __forceinline__ void seg_body(
     }
 }
 
-// Pass 1: workgroup (slice, segment), segment 0 scanning and the others forming
-// their maps, all at once.  Pass 2: segments 1 .. S-1 scanning from their start
-// states.  The segments of a slice are adjacent workgroups.
+// Pass 1: workgroup (slice, segment) for segments 0 .. S-2, segment 0 scanning
+// and the others forming their maps, all at once (no start state depends on the
+// last segment's map, so it is never formed).  Pass 2: segments 1 .. S-1 scanning
+// from their start states.  Either pass runs S - 1 workgroups per slice, and the
+// segments of a slice are adjacent workgroups.
 template <int ETA>
 __global__ __launch_bounds__(256) void linear_seg_pass1_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
@@ -435,7 +437,7 @@ __global__ __launch_bounds__(256) void linear_seg_pass1_kernel(
 {
     __shared__ SegTile L[kSegSlots];
     __shared__ SegZStage Zs;
-    const int slice = (int)blockIdx.x / plan.S, seg = (int)blockIdx.x % plan.S;
+    const int slice = (int)blockIdx.x / (plan.S - 1), seg = (int)blockIdx.x % (plan.S - 1);
     if (seg == 0)
         seg_body<kSegScan, ETA>(L, Zs, K, Q, V, eta, eta_scalar, W0, Z, W_out, ws, BH, T, plan,
                                 slice, 0);
@@ -526,7 +528,8 @@ SegPlan seg_plan(int BH, int T)
 {
     SegPlan p;
     p.nch = T / 16;
-    int S = kSegUnits / (BH > 0 ? BH : 1);
+    // S - 1 workgroups per slice in either pass, one per compute unit
+    int S = kSegUnits / (BH > 0 ? BH : 1) + 1;
     S = S > 64 ? 64 : S;
     while (S > 2 && p.nch < (int)((S - 1 + kSegFirstRatio) * kSegMinChunks)) --S;
     p.S = S < 2 ? 2 : S;
@@ -540,7 +543,7 @@ hipError_t launch_seg_eta(const LinearArgs& a, hipStream_t s)
 {
     const SegPlan p = seg_plan(a.BH, a.T);
     const unsigned bh = (unsigned)a.BH;
-    hipLaunchKernelGGL((linear_seg_pass1_kernel<ETA>), dim3(bh * p.S), dim3(256), 0, s,
+    hipLaunchKernelGGL((linear_seg_pass1_kernel<ETA>), dim3(bh * (p.S - 1)), dim3(256), 0, s,
                        (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V, a.eta,
                        a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.workspace, a.BH, a.T, p);
     hipLaunchKernelGGL(seg_combine_kernel, dim3(bh, kSegD / 16), dim3(256), 0, s, a.workspace,

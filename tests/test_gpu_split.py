@@ -1,9 +1,9 @@
 """GPU parity of the segmented plan (chunk-16 TTT-Linear at d = 64 with few
-(batch, head) slices: each sequence cut into S ~ 256 / slices segments; segment 0
-scans while the others form their affine maps from zero and from the identity, a
-combine gives every segment its start state, and the segments after the first
-scan again from it) against the fp64 oracle, element by element: max relative
-error per slice below 2e-2 (bf16)."""
+(batch, head) slices: each sequence cut into S ~ 256 / slices + 1 segments;
+segment 0 scans while segments 1 .. S-2 form their affine maps, a combine gives
+every segment its start state, and the segments after the first scan again from
+it) against the fp64 oracle, element by element: max relative error per slice
+below 2e-2 (bf16)."""
 import numpy as np
 import pytest
 
