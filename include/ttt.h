@@ -92,8 +92,8 @@ typedef enum {
                                    64, 128}, any chunk (not for packed documents) */
     TTT_PLAN_BIGCHUNK = 3,      /* bf16 matrix cores, three stages, d in {64, 128}, chunk a
                                    multiple of 32 >= 128 */
-    TTT_PLAN_SPLIT = 4          /* bf16 matrix cores, inclusive read, d = 64, chunk 16, T a
-                                   multiple of 16 and >= 2048, at most 32 (batch, head)
+    TTT_PLAN_SPLIT = 4          /* bf16 matrix cores, inclusive read, d = 64, chunk 16,
+                                   T >= 2048, at most 32 (batch, head)
                                    slices: each sequence in S ~ 256 / slices + 1
                                    segments; segment 0 scans while segments 1 .. S-2
                                    form their affine maps, a combine gives every

@@ -127,7 +127,13 @@ constexpr int kSegDropOffset = 0x7ffffff0;
 //         K_c R_{c+1} being the chain's own E for chunk c.  Both leave transposed
 //         back through LDS.  Reading the segment backwards also means its first
 //         chunks are the last ones pass 1 reads, the first ones pass 2 replays.
-template <int MODE, int ETA>
+// RAG: the last segment of a sequence whose length is not a multiple of 16 (a
+// scan, pass 2 only).  Its K, Q, V and eta come through range-checked buffer
+// resources over the segment's rows (the whole offset in the vector offset, the
+// part the check covers), so rows past T, and steps past the end, read as zero;
+// a zero row of K and V gives a zero row of E, hence of F, so such a token adds
+// nothing, whatever its eta.  Z rows past T fall outside Z's resource.
+template <int MODE, int ETA, bool RAG = false>
 __device__ __forceinline__ void seg_body(
     SegTile* L, SegZStage& Zs, const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
@@ -175,19 +181,49 @@ __device__ __forceinline__ void seg_body(
     const int vpos = vrow * 16 + ((tid & 15) ^ seg_vswz(vrow));
     // this lane's unit of a V (or Z) tile: token c, features out0 + 4g .. out0 + 4g + 3
     const int opos = c * 16 + ((4 * wave + g) ^ seg_vswz(c));
-    auto gload = [&](u32x4& r, int ch) {
-        const uint16_t* src = which ? (MAP ? V : Q) : K;
-        r = *(const u32x4*)(src + chunk_base(ch) * D + (grow * D + 8 * ggr));
+    // RAG: the segment's rows [tok0, slice start + T) as buffer resources
+    static_assert(!(RAG && MAP), "only a scan takes the ragged form");
+    const int rows = RAG ? T - 16 * ch0 : 0;
+    auto rsrc = [](const void* base, int bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kSegBufferFlags);
     };
-    auto vload = [&](int ch) { return *(const u32x2*)(V + chunk_base(ch) * D + 4 * tid); };
+    const auto bK = rsrc(K + tok0 * D, rows * D * 2), bQ = rsrc(Q + tok0 * D, rows * D * 2);
+    const auto bV = rsrc(V + tok0 * D, rows * D * 2);
+    const auto bE = rsrc(eta ? eta + tok0 : nullptr, eta ? rows * 4 : 0);
+    auto gload = [&](u32x4& r, int ch) {
+        if constexpr (RAG) {   // wave >> 1 == which, uniform
+            r = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                (wave >> 1) ? bQ : bK, (16 * ch + grow) * (2 * D) + 16 * ggr, 0, 0));
+        } else {
+            const uint16_t* src = which ? (MAP ? V : Q) : K;
+            r = *(const u32x4*)(src + chunk_base(ch) * D + (grow * D + 8 * ggr));
+        }
+    };
+    auto vload = [&](int ch) {
+        if constexpr (RAG)
+            return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                bV, (16 * ch * D + 4 * tid) * 2, 0, 0));
+        else
+            return *(const u32x2*)(V + chunk_base(ch) * D + 4 * tid);
+    };
     // eta of tokens 4g .. 4g + 3 (the rows of this lane's E tile)
     auto eload = [&](int ch) {
-        if constexpr (ETA == kSegEtaToken4) {
+        if constexpr (ETA == kSegEtaToken4 && RAG) {
+            return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                bE, (16 * ch + 4 * g) * 4, 0, 0));
+        } else if constexpr (ETA == kSegEtaToken4) {
             return *(const f32x4*)(eta + chunk_base(ch) + 4 * g);
         } else if constexpr (ETA == kSegEtaToken) {
             f32x4 e;
+            if constexpr (RAG) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) e[r] = eta[chunk_base(ch) + 4 * g + r];
+                for (int r = 0; r < 4; ++r)
+                    e[r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                        bE, (16 * ch + 4 * g + r) * 4, 0, 0));
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) e[r] = eta[chunk_base(ch) + 4 * g + r];
+            }
             return e;
         } else {
             return f32x4{eta_scalar, eta_scalar, eta_scalar, eta_scalar};
@@ -202,8 +238,9 @@ __device__ __forceinline__ void seg_body(
         if constexpr (MAP) return u32x2{0u, 0u};
         else return t.v[opos] ^ u32x2{0x80008000u, 0x80008000u};
     };
-    // Z of chunk ch as thread tid's piece, dropped for ch < 0
-    const auto rz = __builtin_amdgcn_make_buffer_rsrc(Z + tok0 * D, 0, nch * 16 * D * 2,
+    // Z of chunk ch as thread tid's piece, dropped for ch < 0 (and rows past T)
+    const auto rz = __builtin_amdgcn_make_buffer_rsrc(Z + tok0 * D, 0,
+                                                      (RAG ? rows : nch * 16) * D * 2,
                                                       kSegBufferFlags);
     auto zstore = [&](const u32x2& v, int ch) {
         const int off = ch >= 0 ? (ch * 16 * D + 4 * tid) * 2 : kSegDropOffset;
@@ -446,7 +483,7 @@ __global__ __launch_bounds__(256) void linear_seg_pass1_kernel(
                                slice, seg);
 }
 
-template <int ETA>
+template <int ETA, bool RAGGED>
 __global__ __launch_bounds__(256) void linear_seg_pass2_kernel(
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Q,
     const uint16_t* __restrict__ V, const float* __restrict__ eta, float eta_scalar,
@@ -456,8 +493,12 @@ __global__ __launch_bounds__(256) void linear_seg_pass2_kernel(
     __shared__ SegTile L[kSegSlots];
     __shared__ SegZStage Zs;
     const int slice = (int)blockIdx.x / (plan.S - 1), seg = 1 + (int)blockIdx.x % (plan.S - 1);
-    seg_body<kSegScan, ETA>(L, Zs, K, Q, V, eta, eta_scalar, W0, Z, W_out, ws, BH, T, plan, slice,
-                            seg);
+    if (RAGGED && seg == plan.S - 1)
+        seg_body<kSegScan, ETA, RAGGED>(L, Zs, K, Q, V, eta, eta_scalar, W0, Z, W_out, ws, BH, T,
+                                        plan, slice, seg);
+    else
+        seg_body<kSegScan, ETA>(L, Zs, K, Q, V, eta, eta_scalar, W0, Z, W_out, ws, BH, T, plan,
+                                slice, seg);
 }
 
 // W_start,k+1 = W_B,k + W_start,k A_k for k = 1 .. S-2 (W_start,1 = the end of
@@ -527,7 +568,7 @@ constexpr int kSegUnits = 256;        // MI355X compute units
 SegPlan seg_plan(int BH, int T)
 {
     SegPlan p;
-    p.nch = T / 16;
+    p.nch = (T + 15) / 16;   // the last segment holds a partial chunk
     // S - 1 workgroups per slice in either pass, one per compute unit
     int S = kSegUnits / (BH > 0 ? BH : 1) + 1;
     S = S > 64 ? 64 : S;
@@ -548,9 +589,16 @@ hipError_t launch_seg_eta(const LinearArgs& a, hipStream_t s)
                        a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.workspace, a.BH, a.T, p);
     hipLaunchKernelGGL(seg_combine_kernel, dim3(bh, kSegD / 16), dim3(256), 0, s, a.workspace,
                        a.BH, p.S);
-    hipLaunchKernelGGL((linear_seg_pass2_kernel<ETA>), dim3(bh * (p.S - 1)), dim3(256), 0, s,
-                       (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V, a.eta,
-                       a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.workspace, a.BH, a.T, p);
+    if (a.T % 16 == 0)
+        hipLaunchKernelGGL((linear_seg_pass2_kernel<ETA, false>), dim3(bh * (p.S - 1)), dim3(256),
+                           0, s, (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V,
+                           a.eta, a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.workspace, a.BH,
+                           a.T, p);
+    else
+        hipLaunchKernelGGL((linear_seg_pass2_kernel<ETA, true>), dim3(bh * (p.S - 1)), dim3(256),
+                           0, s, (const uint16_t*)a.K, (const uint16_t*)a.Q, (const uint16_t*)a.V,
+                           a.eta, a.eta_scalar, a.W0, (uint16_t*)a.Z, a.W_out, a.workspace, a.BH,
+                           a.T, p);
     return hipGetLastError();
 }
 
@@ -559,7 +607,7 @@ hipError_t launch_seg_eta(const LinearArgs& a, hipStream_t s)
 bool linear_seg_supported(int BH, int T, int d, int chunk, int bf16)
 {
     // Z of one segment is addressed by a 32-bit byte offset
-    return bf16 && d == kSegD && chunk == 16 && T % 16 == 0 && T >= 2048 && BH >= 1 &&
+    return bf16 && d == kSegD && chunk == 16 && T >= 2048 && BH >= 1 &&
            (long)BH * 8 <= kSegUnits && (long long)T * d * 2 < 0x7fffffffLL &&
            (long long)BH * T * d * 2 <= 0x7fffffffffffLL;
 }
@@ -574,7 +622,9 @@ size_t linear_seg_workspace(int BH, int T, int d)
 hipError_t launch_linear_seg(const LinearArgs& a, hipStream_t s)
 {
     if (!a.eta) return launch_seg_eta<kSegEtaScalar>(a, s);
-    if (reinterpret_cast<uintptr_t>(a.eta) % 16 == 0) return launch_seg_eta<kSegEtaToken4>(a, s);
+    // 16-byte eta loads need every slice's rows 16-byte aligned
+    if (reinterpret_cast<uintptr_t>(a.eta) % 16 == 0 && a.T % 4 == 0)
+        return launch_seg_eta<kSegEtaToken4>(a, s);
     return launch_seg_eta<kSegEtaToken>(a, s);
 }
 

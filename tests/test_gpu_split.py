@@ -43,9 +43,10 @@ def check(wl, seed, dev, plan=ttt.PLAN_SPLIT, slices=None, eta_offset=0):
     assert ez < TOL["bf16"] and ew < TOL["bf16"], (ez, ew)
 
 
-# lengths: the shortest taken, and segment lengths that are and are not multiples
-# of the LDS ring (16 chunks)
-@pytest.mark.parametrize("T", [2048, 2064, 3008, 4096, 5120])
+# lengths: the shortest taken, segment lengths that are and are not multiples of
+# the LDS ring (16 chunks), and lengths that are not multiples of 16 (the last
+# segment's ragged form; 2052 and 3004 with 16-byte eta loads)
+@pytest.mark.parametrize("T", [2048, 2064, 3008, 4096, 5120, 2049, 2052, 3001, 3004, 5117])
 @pytest.mark.parametrize("per_token", [True, False])
 def test_lengths(dev, T, per_token):
     wl, seed = case(T, per_token=per_token)
@@ -72,9 +73,23 @@ def test_unaligned_eta(dev):
     check(wl, seed, dev, eta_offset=1)
 
 
+def test_unaligned_eta_ragged(dev):
+    wl, seed = case(2060, B=2, H=2, seed=158)
+    check(wl, seed, dev, eta_offset=1)
+
+
+def test_linear_b16_1x32_ragged(dev):
+    """The headline shape one token short of a whole chunk: 1x32 heads at
+    T = 32767 on the segmented plan, sampled slices against the oracle."""
+    wl = inputs.WORKLOADS["linear_b16_1x32"].with_(T=32767)
+    check(wl, inputs.WORKLOAD_SEEDS["linear_b16_1x32"], dev, plan=ttt.PLAN_AUTO,
+          slices=[0, 13, 31])
+
+
 def test_auto_picks_split_at_1x32_heads(dev):
     wl = inputs.WORKLOADS["linear_b16_1x32"]
     assert ttt.linear_select_plan(wl.B, wl.H, wl.T, wl.d, wl.chunk, 1) == ttt.PLAN_SPLIT
+    assert ttt.linear_select_plan(wl.B, wl.H, wl.T - 1, wl.d, wl.chunk, 1) == ttt.PLAN_SPLIT
     wl2 = inputs.WORKLOADS["linear_b16_8x12"]
     assert ttt.linear_select_plan(wl2.B, wl2.H, wl2.T, wl2.d, wl2.chunk, 1) == ttt.PLAN_MFMA
 
