@@ -5,8 +5,8 @@ One step = one ttt_linear_fwd (or ttt_mlp_fwd) call over the whole batch: every
 region; successive steps rotate over enough input/output copies (>= 1 GiB) that
 the 256 MB last-level cache cannot serve them.
 
-Default workload: TTT-Linear, 8 x 12 heads, d = 64, T = 2048, chunk b = 16, bf16
-K/Q/V, per-token eta, fp32 state.  Prints ONE JSON line on stdout; diagnostics go
+Default workload: TTT-Linear, 1 x 32 heads, d = 64, T = 32768, chunk b = 16, bf16
+K/Q/V, per-token eta, fp32 state (the segmented plan).  Prints ONE JSON line on stdout; diagnostics go
 to stderr.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--plan auto|generic|mfma|bigchunk]

@@ -86,6 +86,12 @@ struct CoopTile {
 __device__ __forceinline__ int coop_vswz(int r) { return (r >> 1) & 7; }
 
 constexpr int kCoopBufferFlags = 0x00020000;   // dword 3 of a gfx9 buffer resource: raw 32-bit data
+// K, Q and V bytes are read once per workgroup and Z bytes written once, so they
+// go with the non-temporal bit of gfx950's cache-policy operand (for pointer
+// accesses, the nontemporal builtins).  The second workgroup of a split head still
+// finds the K and Q tiles in L2.  eta keeps the default policy: every wave reads
+// each of its lines.  8 x 12 heads, T = 2048: 36.9 -> 36.2 us per call.
+constexpr int kCoopStream = 2;
 
 template <int D, int WPG, int ETA, bool FULL>
 __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
@@ -182,13 +188,14 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
             const size_t base = chunk_base(ch) * D;
 #pragma unroll
             for (int i = 0; i < GPT; ++i)
-                r[i] = *(const u32x4*)((which[i] ? Q : K) + base + (grow[i] * D + 8 * ggr[i]));
+                r[i] = __builtin_nontemporal_load(
+                    (const u32x4*)((which[i] ? Q : K) + base + (grow[i] * D + 8 * ggr[i])));
         } else {
 #pragma unroll
             for (int i = 0; i < GPT; ++i)
                 r[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                     (64 * wave + i * NT) / (16 * G) ? bQ : bK,
-                    (16 * ch + grow[i]) * (2 * D) + 16 * ggr[i], 0, 0));
+                    (16 * ch + grow[i]) * (2 * D) + 16 * ggr[i], 0, kCoopStream));
         }
     };
     auto stage = [&](CoopTile<D, WPG>& t, const u32x4 (&r)[GPT], const u32x2& v) {
@@ -200,10 +207,10 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
     auto vload = [&](int ch) {
         const int r = SV ? vrow : c, f = SV ? sbase + 4 * vunit : out0 + 4 * g;
         if constexpr (FULL) {
-            return *(const u32x2*)(V + chunk_base(ch) * D + (r * D + f));
+            return __builtin_nontemporal_load((const u32x2*)(V + chunk_base(ch) * D + (r * D + f)));
         } else {
             return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                bV, ((16 * ch + r) * D + f) * 2, 0, 0));
+                bV, ((16 * ch + r) * D + f) * 2, 0, kCoopStream));
         }
     };
     // Z of chunk ch as thread tid's piece: rows past T (and chunks ch < 0) fall
@@ -213,7 +220,7 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
         const auto rz = __builtin_amdgcn_make_buffer_rsrc(
             Z + (tok0 + (size_t)16 * (ch < 0 ? 0 : ch)) * D, 0, rows * D * 2, kCoopBufferFlags);
         __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, v), rz,
-                                              (vrow * D + sbase + 4 * vunit) * 2, 0, 0);
+                                              (vrow * D + sbase + 4 * vunit) * 2, 0, kCoopStream);
     };
     auto eload = [&](int ch) {
         if (ETA == kCoopEtaToken4) {
@@ -414,10 +421,11 @@ __global__ __launch_bounds__(64 * WPG) void linear_coop_kernel(
             zstore(zprev, ch - kGroup);
         } else if constexpr (FULL) {
             uint16_t* zp = Z + (tok0 + (size_t)16 * ch) * D;
-            *(u32x2*)(zp + (c * D + out0 + 4 * g)) = pack_bf16x4(Zt);
+            __builtin_nontemporal_store(pack_bf16x4(Zt), (u32x2*)(zp + (c * D + out0 + 4 * g)));
         } else {
             __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, pack_bf16x4(Zt)), bZ,
-                                                  ((16 * ch + c) * D + out0 + 4 * g) * 2, 0, 0);
+                                                  ((16 * ch + c) * D + out0 + 4 * g) * 2, 0,
+                                                  kCoopStream);
         }
 #pragma unroll
         for (int m = 0; m < NM; ++m) Mf[m] = pack_bf16x8(M[2 * m], M[2 * m + 1]);
