@@ -1,13 +1,14 @@
 """Summarise rocprofv3 output for the TTT kernels.
 
-  python -m test_sequence_layers_ttt_amd.rocprof_summary stats  <dir>   # kernel-trace --stats
+  python -m test_sequence_layers_ttt_amd.rocprof_summary stats  <dir> [--last N]   # kernel-trace --stats
   python -m test_sequence_layers_ttt_amd.rocprof_summary traffic \
         --fetch <dir> --write <dir> --copy-fetch <dir> --copy-write <dir> \
         --copy-bytes N --kernel SUBSTR[,SUBSTR...] [--json OUT --workload NAME --plan PLAN --model FAMILY]
   python -m test_sequence_layers_ttt_amd.rocprof_summary mfma <dir> [--kernel SUBSTR]
 
 `stats` prints the per-kernel table of a `--kernel-trace --stats --output-format csv`
-run.  `traffic` averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the
+run (with `--last N`, also each kernel's mean over its last N dispatches: a bench
+run's timed steps come last).  `traffic` averages FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the
 kernels whose name contains each SUBSTR, sums them over the substrings (one
 library call launches each kernel once), scales each by bytes / counter-reading
 of a plain device copy of known size, and optionally writes the JSON that bench.py
@@ -35,6 +36,23 @@ def _csv(d, suffix):
         with open(f) as fh:
             rows += list(csv.DictReader(fh))
     return rows
+
+
+def last_dispatches(d, n):
+    """Per kernel name, the mean and min duration of its last n dispatches in the
+    kernel trace (the timed steps of a bench run, which come last)."""
+    rows = _csv(d, "kernel_trace.csv")
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    by = {}
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | dispatches (last) | avg us | min us |")
+    print("|---|---|---|---|")
+    for name, ds in sorted(by.items(), key=lambda kv: -sum(kv[1][-n:])):
+        tail = ds[-n:]
+        short = name if len(name) <= 90 else name[:87] + "..."
+        print("| %s | %d | %.2f | %.2f |" % (short, len(tail), sum(tail) / len(tail), min(tail)))
 
 
 def stats(d):
@@ -149,6 +167,8 @@ def main():
     sub = ap.add_subparsers(dest="cmd", required=True)
     s = sub.add_parser("stats")
     s.add_argument("dir")
+    s.add_argument("--last", type=int, default=0,
+                   help="also average each kernel's last N dispatches from the kernel trace")
     t = sub.add_parser("traffic")
     for k in ("fetch", "write", "copy_fetch", "copy_write"):
         t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
@@ -173,6 +193,9 @@ def main():
     a = ap.parse_args()
     if a.cmd == "stats":
         stats(a.dir)
+        if a.last:
+            print()
+            last_dispatches(a.dir, a.last)
     elif a.cmd == "mfma":
         mfma(a)
     else:
