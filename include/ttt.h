@@ -93,8 +93,9 @@ typedef enum {
     TTT_PLAN_BIGCHUNK = 3,      /* bf16 matrix cores, three stages, d in {64, 128}, chunk a
                                    multiple of 32 >= 128 */
     TTT_PLAN_SPLIT = 4          /* bf16 matrix cores, inclusive read, d = 64, chunk 16,
-                                   T >= 2048, at most 32 (batch, head)
-                                   slices: each sequence in S ~ 256 / slices + 1
+                                   T >= 2048, at most 64 (batch, head) slices (AUTO
+                                   takes it up to 32 slices, and from 33 to 64 when
+                                   T >= 4096): each sequence in S ~ 256 / slices + 1
                                    segments; segment 0 scans while segments 1 .. S-2
                                    form their affine maps, a combine gives every
                                    segment its start state, and segments 1 .. S-1

@@ -53,7 +53,7 @@ int linear_plan(int B, int H, int T, int d, int chunk, int io_dtype, int plan,
     // chunks of 128+ tokens: the three-stage path spreads the chunks over the GPU
     if (big) return TTT_PLAN_BIGCHUNK;
     // few heads: segments along T use the compute units the heads leave idle
-    if (split) return TTT_PLAN_SPLIT;
+    if (split && linear_seg_preferred(B * H, T)) return TTT_PLAN_SPLIT;
     if (mfma) return TTT_PLAN_MFMA;
     return TTT_PLAN_GENERIC;
 }

@@ -84,6 +84,7 @@ hipError_t launch_linear_mfma(const LinearArgs& a, hipStream_t s);
 // segment its start state, and segments 1 .. S-1 scan again from it.  The
 // workspace holds W_B, A and W_start [BH, S, d, d] fp32.
 bool linear_seg_supported(int BH, int T, int d, int chunk, int bf16);
+bool linear_seg_preferred(int BH, int T);
 size_t linear_seg_workspace(int BH, int T, int d);
 hipError_t launch_linear_seg(const LinearArgs& a, hipStream_t s);
 

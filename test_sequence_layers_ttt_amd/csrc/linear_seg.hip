@@ -615,10 +615,21 @@ hipError_t launch_seg_eta(const LinearArgs& a, hipStream_t s)
 
 bool linear_seg_supported(int BH, int T, int d, int chunk, int bf16)
 {
-    // Z of one segment is addressed by a 32-bit byte offset
+    // at least four workgroups per slice in each pass; Z of one segment is
+    // addressed by a 32-bit byte offset
     return bf16 && d == kSegD && chunk == 16 && T >= 2048 && BH >= 1 &&
-           (long)BH * 8 <= kSegUnits && (long long)T * d * 2 < 0x7fffffffLL &&
+           (long)BH * 4 <= kSegUnits && (long long)T * d * 2 < 0x7fffffffLL &&
            (long long)BH * T * d * 2 <= 0x7fffffffffffLL;
+}
+
+// Whether the plan beats the one-segment chain kernel.  Up to 32 slices (at least
+// eight segments each) it does from T = 2048 on.  From 33 to 64 slices, five to
+// eight segments: measured per call, 1 x 40 heads T = 4096 43.7 against 52.0 us,
+// 1 x 48 heads T = 8192 70.0 against 98.8 us, 2 x 32 heads T = 32768 305.5
+// against 410.0 us, but 2 x 32 heads T = 2048 36.7 against 29.0 us.
+bool linear_seg_preferred(int BH, int T)
+{
+    return BH <= kSegUnits / 8 || T >= 4096;
 }
 
 size_t linear_seg_workspace(int BH, int T, int d)

@@ -173,7 +173,8 @@ def test_size_only_workspace_queries_cover_every_plan():
     (dict(d=64, io=0, T=4096, plan=ttt.PLAN_SPLIT), ttt.ERR_UNSUPPORTED),   # fp32 I/O
     (dict(d=64, io=1, T=1024, plan=ttt.PLAN_SPLIT), ttt.ERR_UNSUPPORTED),   # too short
     (dict(d=64, io=1, T=4100, plan=ttt.PLAN_SPLIT), ttt.ERR_WORKSPACE),   # ragged T: taken
-    (dict(d=64, io=1, T=4096, B=4, H=9, plan=ttt.PLAN_SPLIT), ttt.ERR_UNSUPPORTED),  # 36 heads
+    (dict(d=64, io=1, T=4096, B=4, H=9, plan=ttt.PLAN_SPLIT), ttt.ERR_WORKSPACE),  # 36 heads
+    (dict(d=64, io=1, T=4096, B=5, H=13, plan=ttt.PLAN_SPLIT), ttt.ERR_UNSUPPORTED),  # 65 heads
     (dict(d=48), ttt.ERR_UNSUPPORTED),
     (dict(d=256), ttt.ERR_UNSUPPORTED),
     (dict(d=16, io=1, plan=ttt.PLAN_MFMA), ttt.ERR_UNSUPPORTED),
@@ -310,6 +311,13 @@ def test_read_order_plan_selection():
     # small chunks: the matrix-core kernels read inclusively only
     assert ttt.linear_select_plan(8, 12, 2048, 64, 16, 1) == ttt.PLAN_MFMA
     assert ttt.linear_select_plan(1, 32, 32767, 64, 16, 1) == ttt.PLAN_SPLIT   # ragged T
+    # 33 to 64 slices: the segmented plan from T = 4096 on, the chain kernel below
+    assert ttt.linear_select_plan(2, 32, 4096, 64, 16, 1) == ttt.PLAN_SPLIT
+    assert ttt.linear_select_plan(1, 40, 32768, 64, 16, 1) == ttt.PLAN_SPLIT
+    assert ttt.linear_select_plan(2, 32, 4095, 64, 16, 1) == ttt.PLAN_MFMA
+    assert ttt.linear_select_plan(2, 32, 2048, 64, 16, 1, ttt.PLAN_SPLIT) == ttt.PLAN_SPLIT
+    assert ttt.linear_select_plan(1, 65, 8192, 64, 16, 1, ttt.PLAN_SPLIT) == ttt.ERR_UNSUPPORTED
+    assert ttt.linear_select_plan(1, 65, 8192, 64, 16, 1) == ttt.PLAN_MFMA
     assert ttt.linear_select_plan(8, 12, 2048, 64, 16, 1, read_mode=R) == ttt.PLAN_GENERIC
     assert ttt.linear_select_plan(8, 12, 2048, 64, 16, 1, ttt.PLAN_MFMA, R) == ttt.ERR_UNSUPPORTED
     # large chunks: the three-stage plan in both orders

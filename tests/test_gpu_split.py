@@ -53,11 +53,20 @@ def test_lengths(dev, T, per_token):
     check(wl, seed, dev)
 
 
-# slice counts up to the 32 the plan takes (8 to 64 segments each)
-@pytest.mark.parametrize("B,H", [(1, 1), (1, 7), (2, 9), (4, 8)])
+# slice counts up to the 64 the plan takes (64 down to 5 segments each)
+@pytest.mark.parametrize("B,H", [(1, 1), (1, 7), (2, 9), (4, 8), (1, 33), (5, 10), (2, 32)])
 def test_slice_counts(dev, B, H):
     wl, seed = case(2080, B=B, H=H)
     check(wl, seed, dev)
+
+
+# 33 to 64 slices, long and ragged, where AUTO takes the plan (T >= 4096); sampled
+@pytest.mark.parametrize("B,H,T", [(1, 40, 4096), (2, 32, 8195), (1, 48, 6000)])
+def test_many_slices_auto(dev, B, H, T):
+    wl, seed = case(T, B=B, H=H, seed=159)
+    assert ttt.linear_select_plan(wl.B, wl.H, wl.T, wl.d, wl.chunk, 1) == ttt.PLAN_SPLIT
+    check(wl, seed, dev, plan=ttt.PLAN_AUTO, slices=[0, 17, wl.BH - 1])
+
 
 
 # long chains of segment maps: one slice in 32 segments (30 combine steps), two in
