@@ -135,6 +135,7 @@ constexpr int bwd_waves()
     return D == 128 ? 2 : (D >= 32 ? D / 16 : 1);
 }
 constexpr long kComputeUnits = 256;
+constexpr int kMaxBwdSeg = 8;
 
 template <int D, int NW>
 struct BwdLds {
@@ -170,6 +171,10 @@ struct BwdArgs {
     size_t plane;         // BH T d: elements of one dK / dQ plane
     size_t tplane;        // BH T: elements of one deta plane
     int BH, T, chunk;
+    // segments along T (chunks of at most one sub-tile only): segment k owns
+    // sub-tiles bound[k] .. bound[k + 1] - 1
+    int nseg;
+    int bound[kMaxBwdSeg + 1];
 };
 
 // N consecutive elements (N = 1, 2 or 4) widened to fp32
@@ -216,7 +221,9 @@ __device__ __forceinline__ float masked_at(const RawRow<TIO, N>& r, int i, uint3
 // MULTI: chunks span several 16-token sub-tiles (the running W - G_{<sigma} is
 // needed); a compile-time choice, so that chunks of at most 16 tokens carry no
 // trace of it.
-template <typename TIO, int D, int NW, bool MULTI>
+// SEG: segments along T (a.nseg > 1; MULTI false), a compile-time choice so that
+// the one-segment pass carries no trace of them.
+template <typename TIO, int D, int NW, bool MULTI, bool SEG = false>
 __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
 {
     constexpr int NB = D / 16, NBW = NB / NW, S = D + 4;
@@ -235,14 +242,27 @@ __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
     const int c = lane & 15, g = lane >> 4;
     const int srow = tid / (4 * NW), kcol = (tid % (4 * NW)) * KP, vcol = (tid % (4 * NW)) * VP;
     const int wrow = lane >> 2, wcol = (lane & 3) * 4;
-    int slice, rb;
-    xcd_unit_part(blockIdx.x, NB, slice, rb);
+    static_assert(!(SEG && MULTI), "segments take chunks of one sub-tile");
+    int slice, part;
+    xcd_unit_part(blockIdx.x, SEG ? NB * a.nseg : NB, slice, part);
     if (slice >= a.BH) return;
+    const int rb = part % NB, seg = part / NB;
     const int r0 = 16 * rb;
     const int T = a.T, chunk = a.chunk;
     const int nch = (T + chunk - 1) / chunk;
     const int nsub = (chunk + kSub - 1) / kSub;            // sub-tiles of a full chunk
     const int last = (T - 1) / chunk * nsub + ((T - 1) % chunk) / kSub;   // last sub-tile
+    // this unit's segment: sub-tiles j_lo .. j_hi (the whole sequence when nseg = 1)
+    int j_lo = 0, j_hi = last;
+    if constexpr (SEG) {
+#pragma unroll
+        for (int k = 0; k < kMaxBwdSeg; ++k) {
+            if (k == seg) {
+                j_lo = a.bound[k];
+                j_hi = a.bound[k + 1] - 1;
+            }
+        }
+    }
     const TIO* Kg = static_cast<const TIO*>(a.K) + (size_t)slice * T * D;
     const TIO* Qg = static_cast<const TIO*>(a.Q) + (size_t)slice * T * D;
     const TIO* Vg = static_cast<const TIO*>(a.V) + (size_t)slice * T * D;
@@ -351,13 +371,13 @@ __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
         // (after the staging, whose wait for the prefetched loads must not
         // cover these stores)
         if (si == 0) {
-            store_state(ch, Wr);
+            if (j >= j_lo) store_state(ch, Wr);   // the segment's own chunk-start states
 #pragma unroll
             for (int bb = 0; bb < NBW; ++bb) put_cl<S>(L.W, 16 * blk(bb), lane, Wr[bb]);
         }
         const float et = cur.eta_ok ? cur.eta : 0.f;
         __syncthreads();
-        if (j < last) fetch(nxt, j + 1, false, false);
+        if (j < j_hi) fetch(nxt, j + 1, false, false);
         // E = W K^T - V: this wave's part of the contraction over the state columns
         f32x4 Ew = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -383,11 +403,11 @@ __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
     fetch(bufs[0], 0, false, false);
     {
         int j = 0;
-        for (; j + 1 <= last; j += 2) {
+        for (; j + 1 <= j_hi; j += 2) {
             fwd_step(j, slot0);
             fwd_step(j + 1, slot1);
         }
-        if (j == last) fwd_step(j, slot0);
+        if (j == j_hi) fwd_step(j, slot0);
     }
     if constexpr (MULTI) store_state(nch, Wr);
     __threadfence();   // the states are read back below
@@ -429,7 +449,7 @@ __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
 #pragma unroll
         for (int bb = 0; bb < NBW; ++bb) put_cl<S>(L.P, 16 * blk(bb), lane, P[bb]);
         __syncthreads();
-        if (j > 0) fetch(nxt, j - 1, true, opens(j - 1));
+        if (j > j_lo) fetch(nxt, j - 1, true, opens(j - 1));
         // partial E = W K^T, PK = P K^T, S = K Q^T over this wave's columns
         f32x4 Ew = {0.f, 0.f, 0.f, 0.f}, PKw = Ew, Sw = Ew;
 #pragma unroll
@@ -539,20 +559,86 @@ __global__ __launch_bounds__(64 * NW) void linear_bwd_kernel(BwdArgs a)
             }
         }
     };
-    fetch(bufs[0], last, true, true);
-    {
+    // The sub-tiles after the segment only carry the state's cotangent back to the
+    // segment's end, dW_c = dW_{c+1} (I - K diag(eta) K^T) + dZ U^T: the P chain of
+    // the full step below, the same operations in the same order (so the result has
+    // the bits the unsegmented pass reaches there), without E, the gradients of
+    // K, Q, V, eta or the state.  One sub-tile per chunk (nseg > 1 only then).
+    auto cot_step = [&](int j, auto slot) {
+        auto& cur = bufs[decltype(slot)::value];
+        auto& nxt = bufs[decltype(slot)::value ^ 1];
+        __syncthreads();   // the previous sub-tile's tiles are consumed
+        put(cur, true, false);
+        const float et = cur.eta_ok ? cur.eta : 0.f;
+#pragma unroll
+        for (int bb = 0; bb < NBW; ++bb) put_cl<S>(L.P, 16 * blk(bb), lane, P[bb]);
+        __syncthreads();
+        fetch(nxt, j - 1, true, j - 1 <= j_hi);   // j > j_hi >= j_lo
+        f32x4 PKw = {0.f, 0.f, 0.f, 0.f}, Sw = PKw;
+#pragma unroll
+        for (int bb = 0; bb < NBW; ++bb) {
+            const int b = blk(bb);
+            const f32x4 kb = rl<S>(L.K, 16 * b, lane);
+            PKw = mmt<BF, false, true>(rl<S>(L.P, 16 * b, lane), kb, PKw);
+            Sw = mmt<BF, true, true>(kb, rl<S>(L.Q, 16 * b, lane), Sw);
+        }
+        put_cl<20>(L.part[wave][1], 0, lane, PKw);
+        put_cl<20>(L.part[wave][2], 0, lane, Sw);
+        __syncthreads();
+        const f32x4 PK = reduce(1), Sm = reduce(2);
+        f32x4 Mk;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Mk[v] = (4 * g + v <= c) ? Sm[v] : 0.f;
+        put_cl<20>(L.M[wave], 0, lane, Mk);
+        lds_order();
+        const f32x4 dZa = cl<20>(L.dZ, 0, lane);
+        f32x4 dF = mmt<BF, true, false>(dZa, rl<20>(L.M[wave], 0, lane), f32x4{0.f, 0.f, 0.f, 0.f});
+        f32x4 dE;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            dF[v] = -dF[v] - PK[v];
+            dE[v] = dF[v] * et;
+        }
+        put_cl<20>(L.dE[wave], 0, lane, dE);
+        lds_order();
+        const f32x4 dEa = rl<20>(L.dE[wave], 0, lane);
+#pragma unroll
+        for (int bb = 0; bb < NBW; ++bb) {
+            const int b = blk(bb);
+            P[bb] = mmt<BF, true, true>(dZa, cl<S>(L.Q, 16 * b, lane), P[bb]);
+            dWa[bb] = mmt<BF, false, true>(dEa, cl<S>(L.K, 16 * b, lane), dWa[bb]);
+        }
+#pragma unroll
+        for (int bb = 0; bb < NBW; ++bb) {
+            P[bb] += dWa[bb];
+            dWa[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    };
+    fetch(bufs[0], last, true, last <= j_hi && opens(last));
+    if constexpr (!SEG) {   // one segment
         int j = last;
         for (; j >= 1; j -= 2) {
             rev_step(j, slot0);
             rev_step(j - 1, slot1);
         }
         if (j == 0) rev_step(0, slot0);
+    } else {
+        int j = last;
+        for (; j >= j_lo + 1; j -= 2) {
+            if (j > j_hi) cot_step(j, slot0);
+            else rev_step(j, slot0);
+            if (j - 1 > j_hi) cot_step(j - 1, slot1);
+            else rev_step(j - 1, slot1);
+        }
+        if (j == j_lo) rev_step(j_lo, slot0);
     }
-    float* dW0 = a.dW0 + ((size_t)slice * D + r0) * D;
+    if (j_lo == 0) {
+        float* dW0 = a.dW0 + ((size_t)slice * D + r0) * D;
 #pragma unroll
-    for (int bb = 0; bb < NBW; ++bb)
+        for (int bb = 0; bb < NBW; ++bb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) dW0[(4 * g + v) * D + 16 * blk(bb) + c] = P[bb][v];
+            for (int v = 0; v < 4; ++v) dW0[(4 * g + v) * D + 16 * blk(bb) + c] = P[bb][v];
+    }
 }
 
 // n floats set to zero: 16-byte stores (n a multiple of 4, p 16-byte aligned)
@@ -606,6 +692,41 @@ unsigned elementwise_grid(size_t n)
     return (unsigned)std::min<size_t>((n / 4 + 255) / 256, 4096);
 }
 
+// Segments along T for chunks of at most one sub-tile when the (sequence, row
+// block) units leave compute units idle.  Segment k (sub-tiles b_k .. b_{k+1}-1 of
+// N) recomputes the forward over b_{k+1} sub-tiles, carries the cotangent back over
+// N - b_{k+1} and runs the full reverse over its own b_{k+1} - b_k, at relative
+// costs kFwd, kCot and kRev per sub-tile.  Equal costs give b_{k+1} = N s_k /
+// s_{S-1}, s_k = sum_{i <= k} r^i, r = kRev / (kFwd - kCot + kRev).  The ratios are
+// fitted to where the two-segment split of 1 x 32 heads, T = 32768 (bf16, d = 64)
+// is fastest: b_1 / N = 0.23, 0.41, 0.47, 0.535, 0.59 measured 5.00, 4.33, 4.12,
+// 4.32 and 4.50 ms per call (one segment: 5.00 ms; every split gives the same bits).
+constexpr double kFwd = 0.15, kCot = 0.25, kRev = 1.0;
+constexpr int kMinBwdSegSub = 64;   // shortest segment, in sub-tiles
+
+void bwd_segments(long units, int nsubtiles, int& nseg, int* bound)
+{
+    for (int i = 0; i <= kMaxBwdSeg; ++i) bound[i] = 0;
+    long S = std::min<long>(kMaxBwdSeg, kComputeUnits / std::max<long>(units, 1));
+    S = std::min<long>(S, nsubtiles / kMinBwdSegSub);
+    nseg = S > 1 ? (int)S : 1;
+    if (nseg == 1) return;
+    const double r = kRev / (kFwd - kCot + kRev);
+    double sk[kMaxBwdSeg];
+    double acc = 0.0, term = 1.0;
+    for (int k = 0; k < nseg; ++k) {
+        acc += term;
+        sk[k] = acc;
+        term *= r;
+    }
+    bound[0] = 0;
+    for (int k = 0; k + 1 < nseg; ++k) {
+        const int e = (int)(nsubtiles * sk[k] / sk[nseg - 1] + 0.5);
+        bound[k + 1] = std::max(bound[k] + 1, std::min(e, nsubtiles - (nseg - 1 - k)));
+    }
+    bound[nseg] = nsubtiles;
+}
+
 template <typename TIO, int D>
 hipError_t launch_typed(const LinearBwdArgs& a, hipStream_t s)
 {
@@ -628,12 +749,16 @@ hipError_t launch_typed(const LinearBwdArgs& a, hipStream_t s)
     ws += linear_bwd_align(NB * n * sizeof(float));
     k.deta_part = a.deta ? reinterpret_cast<float*>(ws) : nullptr;
     k.BH = a.BH; k.T = a.T; k.chunk = a.chunk;
-    const unsigned grid = (unsigned)(((a.BH + 7) / 8) * 8 * NB);
+    bwd_segments(a.BH * NB, a.chunk <= kSub ? nch : 0, k.nseg, k.bound);
+    const unsigned grid = (unsigned)(((a.BH + 7) / 8) * 8 * NB * k.nseg);
     auto launch = [&](auto nw) {
         constexpr int NW = decltype(nw)::value;
         if (a.chunk > kSub)
             hipLaunchKernelGGL((linear_bwd_kernel<TIO, D, NW, true>), dim3(grid), dim3(64 * NW), 0,
                                s, k);
+        else if (k.nseg > 1)
+            hipLaunchKernelGGL((linear_bwd_kernel<TIO, D, NW, false, true>), dim3(grid),
+                               dim3(64 * NW), 0, s, k);
         else
             hipLaunchKernelGGL((linear_bwd_kernel<TIO, D, NW, false>), dim3(grid), dim3(64 * NW),
                                0, s, k);

@@ -104,6 +104,45 @@ def test_full_size_sampled(dev, name, slices):
     check_bwd(wl, inputs.WORKLOAD_SEEDS[name], dev, slices=slices)
 
 
+# Segments along T: with chunks of at most 16 tokens and fewer (sequence, row
+# block) units than compute units, each sequence is cut into segments whose units
+# recompute the forward up to their end and carry the state's cotangent back from
+# the sequence end; these shapes take 2 to 4 segments.
+@pytest.mark.parametrize("d,io,chunk,H,T", [
+    (64, "bf16", 16, 20, 3072),    # 80 units: 3 segments
+    (64, "bf16", 16, 20, 3001),    # ragged last sub-tile
+    (128, "bf16", 16, 8, 4096),    # 64 units: 4 segments
+    (32, "f32", 16, 10, 2048),     # 20 units: 2 segments
+    (64, "bf16", 8, 12, 2048),     # chunks of 8 tokens: 256 sub-tiles, 4 segments
+])
+def test_segments(dev, d, io, chunk, H, T):
+    wl = case(d, chunk, io, per_token=True, T=T, B=1, H=H)
+    check_bwd(wl, 421, dev, slices=[0, H - 1])
+
+
+@pytest.mark.parametrize("io,T", [("bf16", 3072), ("bf16", 3001), ("f32", 2050)])
+def test_segments_bitwise(dev, io, T):
+    """A segmented pass gives the bits of the one-segment pass: the first 20 heads
+    of a 40-head call (160 row-block units, one segment) against a 20-head call of
+    the same inputs (80 units, three segments; two with fp32 I/O)."""
+    import torch
+    wl = case(64, 16, io, True, T, B=1, H=40)
+    x = inputs.make_inputs(wl, 422)
+    dZ, dWT = cotangents(wl, 422)
+    a = device_inputs(wl, x, dev)
+    t = torch.bfloat16 if io == "bf16" else torch.float32
+    dZ_d = torch.from_numpy(dZ).to(dev).reshape(1, 40, T, 64).to(t).contiguous()
+    dWT_d = torch.from_numpy(dWT).to(dev).reshape(1, 40, 64, 64)
+    full = ttt.linear_bwd(a["K"], a["Q"], a["V"], a["eta"], a["W0"], dZ_d, wl.chunk,
+                          eta_scalar=x["eta_scalar"], dW_T=dWT_d)
+    h = lambda u: u[:, :20].contiguous()   # noqa: E731
+    part = ttt.linear_bwd(h(a["K"]), h(a["Q"]), h(a["V"]), h(a["eta"]), h(a["W0"]), h(dZ_d),
+                          wl.chunk, eta_scalar=x["eta_scalar"], dW_T=h(dWT_d))
+    torch.cuda.synchronize()
+    for name, u, v in zip(("dK", "dQ", "dV", "deta", "dW0"), full, part):
+        assert torch.equal(h(u), v), name
+
+
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 def test_bitwise_deterministic(dev, io):
     """dK, dQ and deta are sums over the state's row blocks: they come out the same
