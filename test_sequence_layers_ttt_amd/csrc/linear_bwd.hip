@@ -700,14 +700,18 @@ unsigned elementwise_grid(size_t n)
 // s_{S-1}, s_k = sum_{i <= k} r^i, r = kRev / (kFwd - kCot + kRev).  The ratios are
 // fitted to where the two-segment split of 1 x 32 heads, T = 32768 (bf16, d = 64)
 // is fastest: b_1 / N = 0.23, 0.41, 0.47, 0.535, 0.59 measured 5.00, 4.33, 4.12,
-// 4.32 and 4.50 ms per call (one segment: 5.00 ms; every split gives the same bits).
+// 4.32 and 4.50 ms per call (one segment: 5.00 ms; every split gives the same bits);
+// with four segments the same ratios stay best (3.82 ms; kCot = 0, 0.5, 0.7: 4.18,
+// 4.23, 4.88).  Segments per sequence at 128 units: 2 -> 4.12, 4 -> 3.85,
+// 6 -> 3.91, 8 -> 4.22 ms; one wave per unit instead of two: 4.96 (2), 4.26 (4).
 constexpr double kFwd = 0.15, kCot = 0.25, kRev = 1.0;
 constexpr int kMinBwdSegSub = 64;   // shortest segment, in sub-tiles
 
 void bwd_segments(long units, int nsubtiles, int& nseg, int* bound)
 {
     for (int i = 0; i <= kMaxBwdSeg; ++i) bound[i] = 0;
-    long S = std::min<long>(kMaxBwdSeg, kComputeUnits / std::max<long>(units, 1));
+    // two segment units per compute unit (their LDS and registers fit)
+    long S = std::min<long>(kMaxBwdSeg, 2 * kComputeUnits / std::max<long>(units, 1));
     S = std::min<long>(S, nsubtiles / kMinBwdSegSub);
     nseg = S > 1 ? (int)S : 1;
     if (nseg == 1) return;
