@@ -24,6 +24,13 @@
 // adds the planes in row-block order (and rounds to bf16 with bf16 I/O), so the
 // results are the same bits on every call.
 //
+// With chunks of at most 16 tokens and fewer units than compute units, each
+// sequence is also cut into segments along T, one unit per (sequence, row block,
+// segment): the unit recomputes the forward up to its segment's end, carries the
+// state's cotangent back from dW_T over the later segments (the affine reverse
+// recurrence, from K, Q, dZ and eta only) and runs the full reverse over its own
+// segment, with the bits of the one-segment pass.
+//
 // Every product is a 16 x 16 tile product, operands staged through LDS in
 // row-major fp32 tiles with padded rows.  With fp32 I/O it runs on the fp32
 // matrix cores (v_mfma_f32_16x16x4_f32); with bf16 I/O on the bf16 ones, the
