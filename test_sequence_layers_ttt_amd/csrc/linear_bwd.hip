@@ -714,11 +714,13 @@ unsigned elementwise_grid(size_t n)
 constexpr double kFwd = 0.15, kCot = 0.25, kRev = 1.0;
 constexpr int kMinBwdSegSub = 64;   // shortest segment, in sub-tiles
 
-void bwd_segments(long units, int nsubtiles, int& nseg, int* bound)
+void bwd_segments(long wave_units, int nsubtiles, int& nseg, int* bound)
 {
     for (int i = 0; i <= kMaxBwdSeg; ++i) bound[i] = 0;
-    // two segment units per compute unit (their LDS and registers fit)
-    long S = std::min<long>(kMaxBwdSeg, 2 * kComputeUnits / std::max<long>(units, 1));
+    // at most four waves of segment units per compute unit (wave_units: units times
+    // waves per unit): 1 x 32 heads (128 two-wave units) takes four segments, 8 x 12
+    // heads (384 one-wave units) two (0.515 -> 0.497 ms)
+    long S = std::min<long>(kMaxBwdSeg, 4 * kComputeUnits / std::max<long>(wave_units, 1));
     S = std::min<long>(S, nsubtiles / kMinBwdSegSub);
     nseg = S > 1 ? (int)S : 1;
     if (nseg == 1) return;
@@ -760,7 +762,11 @@ hipError_t launch_typed(const LinearBwdArgs& a, hipStream_t s)
     ws += linear_bwd_align(NB * n * sizeof(float));
     k.deta_part = a.deta ? reinterpret_cast<float*>(ws) : nullptr;
     k.BH = a.BH; k.T = a.T; k.chunk = a.chunk;
-    bwd_segments(a.BH * NB, a.chunk <= kSub ? nch : 0, k.nseg, k.bound);
+    constexpr bool F32 = sizeof(TIO) == 4;
+    // waves per unit: at d = 64 with bf16 I/O two while the units leave compute
+    // units idle, else one; otherwise fixed per d
+    const int nw = (!F32 && D == 64) ? ((long)a.BH * NB >= kComputeUnits ? 1 : 2) : bwd_waves<D>();
+    bwd_segments((long)a.BH * NB * nw, a.chunk <= kSub ? nch : 0, k.nseg, k.bound);
     const unsigned grid = (unsigned)(((a.BH + 7) / 8) * 8 * NB * k.nseg);
     auto launch = [&](auto nw) {
         constexpr int NW = decltype(nw)::value;
@@ -774,9 +780,8 @@ hipError_t launch_typed(const LinearBwdArgs& a, hipStream_t s)
             hipLaunchKernelGGL((linear_bwd_kernel<TIO, D, NW, false>), dim3(grid), dim3(64 * NW),
                                0, s, k);
     };
-    constexpr bool F32 = sizeof(TIO) == 4;
     if constexpr (!F32 && D == 64) {
-        if ((long)a.BH * NB >= kComputeUnits) launch(std::integral_constant<int, 1>{});
+        if (nw == 1) launch(std::integral_constant<int, 1>{});
         else launch(std::integral_constant<int, 2>{});   // two waves per unit
     } else {
         launch(std::integral_constant<int, bwd_waves<D>()>{});

@@ -106,7 +106,7 @@ def test_full_size_sampled(dev, name, slices):
 
 # Segments along T: with chunks of at most 16 tokens and fewer (sequence, row
 # block) units than compute units, each sequence is cut into up to 8 segments (at
-# least 64 sub-tiles each, at most two units per compute unit) whose units
+# least 64 sub-tiles each, at most four waves of units per compute unit) whose units
 # recompute the forward up to their end and carry the state's cotangent back from
 # the sequence end; these shapes take 2 to 8 segments.
 @pytest.mark.parametrize("d,io,chunk,H,T", [
@@ -125,9 +125,10 @@ def test_segments(dev, d, io, chunk, H, T):
 @pytest.mark.parametrize("io,T", [("bf16", 4096), ("bf16", 5000), ("f32", 4096)])
 def test_segments_bitwise(dev, io, T):
     """The segment count does not change a bit of the result: the first 20 heads of
-    a 40-head call (160 row-block units, three segments) against a 20-head call of
-    the same inputs (80 units, four segments).  (A split of the same shape at five
-    points, and one segment against two, gave the same bits on the GPU too.)"""
+    a 40-head call (160 row-block units: three segments with bf16 I/O, one with
+    fp32 I/O) against a 20-head call of the same inputs (80 units: four segments
+    with bf16 I/O, three with fp32 I/O).  (Five split points of one shape, and one
+    segment against two and four, gave the same bits on the GPU too.)"""
     import torch
     wl = case(64, 16, io, True, T, B=1, H=40)
     x = inputs.make_inputs(wl, 422)
