@@ -116,6 +116,10 @@ def test_full_size_sampled(dev, name, slices):
     (32, "f32", 16, 10, 2048),     # 20 units: 2 segments
     (64, "bf16", 8, 12, 2048),     # chunks of 8 tokens: 256 sub-tiles, 4 segments
     (64, "bf16", 16, 4, 8192),     # 16 units: 8 segments
+    (16, "f32", 16, 40, 2048),     # 40 one-wave units: 2 segments
+    (128, "f32", 16, 6, 4096),     # 48 two-wave units: 4 segments
+    (16, "bf16", 16, 24, 3000),    # 24 one-wave units: 2 segments, ragged
+    (32, "bf16", 16, 30, 4096),    # 60 two-wave units: 4 segments
 ])
 def test_segments(dev, d, io, chunk, H, T):
     wl = case(d, chunk, io, per_token=True, T=T, B=1, H=H)
